@@ -1,0 +1,93 @@
+"""CPU tests: the oracle against its pins, and planted mistakes against the pins.
+
+The second half copies the oracle's source, plants one plausible mistake in
+the copy (on the CPU, never in the product) and shows that at least one pin
+rejects it.
+"""
+import os
+import types
+
+import pytest
+
+import oracle
+import oracle_pins as P
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                          "oracle", "awq_oracle.py")
+
+
+@pytest.mark.parametrize("check", P.ALL_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_pin(check):
+    check(oracle.awq_oracle)
+
+
+# (what is broken, text in the oracle, replacement, pins expected to catch it)
+MUTATIONS = [
+    ("stats without |x|", "np.abs(x).sum(axis=0)", "x.sum(axis=0)", [P.check_stats_closed_form]),
+    ("stats sum, not mean", "(S / F64(T))", "(S)", [P.check_stats_closed_form]),
+    ("stats over the wrong axis", "np.abs(x).sum(axis=0)", "np.abs(x).sum(axis=1)",
+     [P.check_stats_closed_form]),
+    ("scale not normalised", "s = p / np.sqrt(p.max() * p.min())", "s = p",
+     [P.check_scale_closed_form]),
+    ("scale normalised by its max", "s = p / np.sqrt(p.max() * p.min())", "s = p / p.max()",
+     [P.check_scale_closed_form]),
+    ("exponent applied to the reciprocal", "p = a ** F64(F32(alpha))", "p = a ** (-F64(F32(alpha)))",
+     [P.check_scale_closed_form]),
+    ("2^b levels instead of 2^b-1 intervals", "qmax = F32(2 ** bits - 1)\n    mx",
+     "qmax = F32(2 ** bits)\n    mx", [P.check_quant_worked_examples]),
+    ("zero point with the wrong sign", "np.rint((-mn) / step)", "np.rint(mn / step)",
+     [P.check_quant_worked_examples]),
+    ("codes truncated instead of rounded", "np.rint(wg / step[:, :, None])",
+     "np.floor(wg / step[:, :, None])", [P.check_codes_nearest_bruteforce]),
+    ("range not widened to contain 0", "np.maximum(wp_groups.max(axis=2), F32(0))",
+     "wp_groups.max(axis=2)", [P.check_codes_nearest_bruteforce]),
+    ("clip ratio applied to the max only", "mn = (r * mn).astype(F32)", "mn = mn.astype(F32)",
+     [P.check_quant_worked_examples]),
+    ("symmetric step over 2^(b-1)", "amax / F32(2 ** (bits - 1) - 1)", "amax / F32(2 ** (bits - 1))",
+     [P.check_quant_worked_examples, P.check_codes_nearest_bruteforce]),
+    ("dequantise without the zero point", "(qg - zero.astype(F64)[:, :, None])", "(qg - 0)",
+     [P.check_quant_worked_examples]),
+    ("fold multiplies by s", "return wp_hat / np.asarray(s32", "return wp_hat * np.asarray(s32",
+     [P.check_fold_invariance, P.check_quant_worked_examples]),
+    ("error of the weights, not of the output",
+     "E = np.asarray(w_hat, dtype=F64) - np.asarray(w32, dtype=F64)",
+     "E = np.asarray(w_hat, dtype=F64)", [P.check_output_error_bruteforce]),
+    ("absolute instead of squared error", "M += (Y * Y).sum(axis=0)", "M += np.abs(Y).sum(axis=0)",
+     [P.check_output_error_bruteforce]),
+    ("sum over output channels instead of tokens", "M += (Y * Y).sum(axis=0)",
+     "M += (Y * Y).sum(axis=1)",
+     [P.check_output_error_bruteforce]),
+    ("argmax instead of argmin", "best = int(np.argmin(mse))", "best = int(np.argmax(mse))",
+     [P.check_search_scale_bruteforce]),
+    ("curve divided by T only", "mse = row_sums.sum(axis=1) / F64(T * R)",
+     "mse = row_sums.sum(axis=1) / F64(T)", [P.check_search_scale_bruteforce,
+                                            P.check_monotone_and_separable]),
+    ("clip picks the worst ratio", "idx = np.argmin(row_sums, axis=0)",
+     "idx = np.argmax(row_sums, axis=0)", [P.check_search_clip_bruteforce]),
+    ("nibbles in reverse order", "word |= c[:, :, i] << np.uint32(4 * i)",
+     "word |= c[:, :, i] << np.uint32(28 - 4 * i)", [P.check_pack_layout]),
+    ("codes packed along the input dim", "pack_nibbles(np.ascontiguousarray(q.T))",
+     "pack_nibbles(np.ascontiguousarray(q))", [P.check_pack_layout]),
+]
+
+
+def _mutant(old, new):
+    with open(ORACLE_SRC) as f:
+        src = f.read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    mod = types.ModuleType("awq_oracle_mutant")
+    exec(compile(src.replace(old, new, 1), "awq_oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("desc,old,new,checks", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(desc, old, new, checks):
+    mod = _mutant(old, new)
+    caught = False
+    for chk in checks:
+        try:
+            chk(mod)
+        except Exception:
+            caught = True
+            break
+    assert caught, f"no pin caught: {desc}"
