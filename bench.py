@@ -1,0 +1,210 @@
+"""Benchmark: AWQ per-layer search throughput on one MI355X.
+
+A step is one pass of the whole per-layer path over one synthetic layer
+already resident in HBM: activation statistics, the scale table and the
+α-grid search (quantise / dequantise / fold candidates, the search GEMM with
+its squared-error epilogue, reductions, argmin), the clip search when the
+workload has one, and INT4 packing. The default workload is a Llama-7B-shaped
+attention projection: W [4096, 4096] bf16, X [65536, 4096] bf16 with 41
+outlier channels, INT4 asymmetric g128, 20 α values, then pack.
+
+Prints one JSON line. ``value`` is α-candidates evaluated per second over the
+timed steps (whole job). ``roofline`` covers the dominant kernel, the search
+GEMM, timed with HIP events on its launch stream inside the timed region.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "search_gemm_traffic.json")
+GEMM_SRC = os.path.join(ROOT, "post_weight_quantization_26_amd", "csrc", "gemm.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--config", default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=16)
+    return p.parse_args()
+
+
+def gemm_traffic(cfg_name: str, launches_per_step: int):
+    """HBM bytes per search-GEMM launch from committed rocprofv3 counter runs,
+    or None when the kernel source changed since they were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    src_hash = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
+    if rec.get("gemm_source_sha256") != src_hash or rec.get("workload") != cfg_name:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, X, W, alphas, rows_n: int):
+    """The CPU oracle, as it stands, on a bounded sample of one step: stats over
+    the full X, the α search over ``rows_n`` evenly spaced output rows (all
+    tokens, all α; extrapolated linearly to N rows, since every row costs the
+    same), and packing of the full W."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    rows = np.unique(np.linspace(0, cfg.N - 1, rows_n).round().astype(np.int64))
+    t0 = time.perf_counter()
+    ab = O.act_stats(X, cfg.dtype)
+    t1 = time.perf_counter()
+    O.search_scale(X, W, cfg.dtype, ab, alphas, cfg.bits, 128, cfg.zero_point, rows=rows)
+    t2 = time.perf_counter()
+    pack_t = 0.0
+    if cfg.pack:
+        O.quantize_pack(W, cfg.dtype, np.ones(cfg.K, np.float32), None, 4, 128, cfg.zero_point)
+        pack_t = time.perf_counter() - t2
+    step = (t1 - t0) + (t2 - t1) * cfg.N / len(rows) + pack_t
+    return {"value": len(alphas) / step, "unit": "alpha-candidates/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"stats over all {cfg.T} tokens; alpha search over {len(rows)} of {cfg.N} "
+                       f"output rows (all {len(alphas)} alphas, all tokens) extrapolated x"
+                       f"{cfg.N / len(rows):.0f}; pack of the full W"),
+            "sample_seconds": round(time.perf_counter() - t0, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from post_weight_quantization_26_amd import build_lib, synth
+    if not os.path.exists(build_lib.LIB_PATH):
+        build_lib.build()
+    from post_weight_quantization_26_amd import _lib, api
+
+    name = args.config or synth.BENCH_CONFIG
+    cfg = synth.CONFIGS[name]
+    dev = torch.device("cuda:0")
+    X, W = synth.make_layer(cfg)
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+
+    def up(a):
+        if cfg.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    Xd, Wd = up(X), up(W)
+    alphas = synth.alpha_grid(cfg.n_alpha)
+    ratios = synth.ratio_grid(cfg.n_ratio) if cfg.n_ratio else None
+    T, N, K = cfg.T, cfg.N, cfg.K
+    ws_stats = torch.empty(api.workspace_bytes(_lib.AWQ_OP_STATS, T, 1, K, 1, tdt),
+                           dtype=torch.uint8, device=dev)
+    n_grid = max(cfg.n_alpha, cfg.n_ratio)
+    ws_search = torch.empty(api.workspace_bytes(_lib.AWQ_OP_SEARCH_SCALE, T, N, K, n_grid, tdt),
+                            dtype=torch.uint8, device=dev)
+    ws_pack = torch.empty(256, dtype=torch.uint8, device=dev)
+    abar = torch.empty(K, dtype=torch.float32, device=dev)
+    pack_out = (torch.empty((K, N // 8), dtype=torch.int32, device=dev),
+                torch.empty((K // 128, N // 8), dtype=torch.int32, device=dev),
+                torch.empty((K // 128, N), dtype=torch.float16, device=dev))
+    zp = cfg.zero_point
+
+    def step():
+        api.act_stats(Xd, ws=ws_stats, out=abar)
+        res = api.search_scale(Xd, Wd, abar, alphas, bits=cfg.bits, zero_point=zp, ws=ws_search)
+        ratio = None
+        if ratios is not None:
+            ratio = api.search_clip(Xd, Wd, res["s_best"], ratios, bits=cfg.bits, zero_point=zp,
+                                    ws=ws_search)["ratio_best"]
+        if cfg.pack:
+            api.quantize_pack(Wd, res["s_best"], ratio, zero_point=zp, ws=ws_pack, out=pack_out)
+        return res
+
+    for _ in range(args.warmup):
+        res = step()
+    torch.cuda.synchronize()
+    api.profile_enable(True)
+    api.profile_reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        res = step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = {k: api.profile_read(k) for k in _lib.KERNEL_KINDS}
+    api.profile_enable(False)
+
+    elapsed = t1 - t0
+    cands_per_step = cfg.n_alpha + (cfg.n_ratio or 0)
+    value = cfg.n_alpha * args.steps / elapsed
+    gemm_ms, gemm_n = prof["gemm"]
+    gemm_avg_s = gemm_ms / 1e3 / max(gemm_n, 1)
+    launches_per_step = gemm_n // args.steps if args.steps else 0
+    flops_per_launch = 2.0 * T * N * K * cands_per_step / max(launches_per_step, 1)
+    achieved = flops_per_launch / gemm_avg_s / 1e12
+    traffic = gemm_traffic(name, launches_per_step)
+    kernels = {k: {"avg_us": round(ms * 1e3 / n, 2) if n else None, "launches": n,
+                   "share_of_step": round(ms / (elapsed * 1e3), 4)}
+               for k, (ms, n) in prof.items()}
+    stats_ms, stats_n = prof["stats"]
+    stats_gbs = (T * K * X.itemsize) / (stats_ms / 1e3 / max(stats_n, 1)) / 1e9 if stats_n else None
+    pack_ms, pack_n = prof["pack"]
+    pack_bytes = N * K * W.itemsize + N * K // 2 + (N * K // 128) * (2 + 0.5) + K * 4
+    pack_gbs = pack_bytes / (pack_ms / 1e3 / max(pack_n, 1)) / 1e9 if pack_n else None
+
+    out = {
+        "metric": "AWQ alpha-candidates evaluated/sec (4096x4096, 64K tok, g128) + MFMA util %",
+        "value": round(value, 3),
+        "unit": "alpha-candidates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": name, "T": T, "N": N, "K": K, "group": 128, "bits": cfg.bits,
+                   "zero_point": zp, "n_alpha": cfg.n_alpha, "n_ratio": cfg.n_ratio,
+                   "pack": cfg.pack},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "search_gemm_bf16_kernel",
+                     "avg_launch_us": round(gemm_avg_s * 1e6, 1),
+                     "algorithmic_flops_per_launch": flops_per_launch},
+        "mfma_util_pct": round(100 * achieved / MFMA_BF16_PEAK_TFLOPS, 2),
+        "hbm": {"stats_GBps": None if stats_gbs is None else round(stats_gbs, 1),
+                "pack_GBps": None if pack_gbs is None else round(pack_gbs, 1),
+                "peak_GBps": HBM_PEAK_GBS},
+        "kernels": kernels,
+        "alpha_best": float(res["alpha_best"]),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, X, W, alphas, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

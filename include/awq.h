@@ -1,0 +1,168 @@
+/*
+ * awq.h — C ABI of the AWQ per-layer activation-aware scale search on MI355X.
+ *
+ * For one linear layer Y = X·Wᵀ (X [T, K] calibration activations, W [N, K]
+ * weights, K input channels, N output channels) the library computes:
+ *
+ *   awq_act_stats      ā_j = mean_t |x_tj|                       (step 1)
+ *   awq_scale_table    s_j(α) = ā_j^α / sqrt(max ā^α · min ā^α)  (step 2)
+ *   awq_search_scale   for each α of a grid: quantise W·diag(s) group-wise,
+ *                      fold diag(s)^-1 back, measure the output MSE against
+ *                      the unquantised product; return the curve and argmin
+ *   awq_search_clip    per-output-channel clip ratio search with s fixed
+ *   awq_quantize_pack  INT4 codes, packed zeros and fp16 scales
+ *
+ * Sources (page titles and sections):
+ *   "AWQ and Activation-Aware Scaling", section "Scaling instead of
+ *   protecting" — s = ā^α with α in [0, 1] found by a per-layer grid search
+ *   minimising reconstruction error; α = 0 is plain quantisation.
+ *   "05 — AWQ: Activation-Aware Weight Scaling": section 3 "The scaling
+ *   trick" (the invariance X·W = (X·diag(s)^-1)(diag(s)·W)); section 4 "How
+ *   to find s — the grid search" (~20 α values in [0, 1], output MSE, pick
+ *   the best) and "Optional: per-channel clipping" (ratios 0.5–1.0 of the
+ *   max after α is chosen); section 5 "Bit-level output format" (qweight,
+ *   qzeros, scales layout); section 9 option A (zero point, group 128, 4 bit).
+ *   Anthology record SOTA-356, "What to do" (collect per-input-channel
+ *   activation statistics, scale, round uniformly).
+ *
+ * Conventions for every entry point:
+ *   - Arrays are DEVICE pointers unless marked [host]. Matrices are dense and
+ *     row-major. The caller owns and allocates every buffer; the library
+ *     keeps no device memory between calls (workspaces are passed in).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All device work is enqueued on it in order. Functions with [host]
+ *     outputs synchronise `stream` before returning; the others do not.
+ *   - Arguments are validated on the host before anything is enqueued. A
+ *     failed check returns a negative status and launches nothing.
+ *     X and W must be 16-byte aligned; K must be a multiple of the group
+ *     size (128); grids hold 1..64 values.
+ *   - Quantiser arithmetic is IEEE float32 with round-to-nearest-even, one
+ *     rounding per operation (no contraction, no flush of denormals):
+ *       w' = w·s_j; mx = r·max(0, max_G w'); mn = r·min(0, min_G w')
+ *       asymmetric: step = max((mx-mn)/(2^b-1), 1e-5);
+ *                   zero = clamp(rint(-mn/step), 0, 2^b-1)
+ *       symmetric:  step = max(max(mx,-mn)/(2^(b-1)-1), 1e-5); zero = 2^(b-1)
+ *       code = clamp(rint(w'/step) + zero, 0, 2^b-1)
+ *     Groups are 128 consecutive input channels of one output row.
+ *   - Errors never abort: a non-zero status is returned and
+ *     awq_last_error() describes it (per calling thread).
+ *   - Calls are thread-compatible: concurrent calls must use distinct
+ *     workspaces.
+ */
+#ifndef AWQ_MI355X_AWQ_H
+#define AWQ_MI355X_AWQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AWQ_OK = 0,
+  AWQ_E_INVALID = -1,     /* bad argument: shape, NULL, alignment, grid value */
+  AWQ_E_UNSUPPORTED = -2, /* valid but not implemented (dtype, bits, group) */
+  AWQ_E_WORKSPACE = -3,   /* workspace smaller than the minimum */
+  AWQ_E_RANGE = -4,       /* an fp16 scale overflowed in awq_quantize_pack */
+  AWQ_E_HIP = -5          /* a HIP runtime call failed (message in awq_last_error) */
+} awq_status;
+
+typedef enum { AWQ_F32 = 0, AWQ_BF16 = 1, AWQ_F16 = 2 } awq_dtype;
+
+/* Quantiser parameters. w_bit: 4 or 3 (packing: 4 only). group_size: 128.
+ * zero_point: 1 = asymmetric min-max with an integer zero point,
+ * 0 = symmetric (zero point fixed at 2^(w_bit-1)). */
+typedef struct {
+  int32_t w_bit;
+  int32_t group_size;
+  int32_t zero_point;
+} awq_qconfig;
+
+enum { AWQ_OP_STATS = 0, AWQ_OP_SEARCH_SCALE = 1, AWQ_OP_SEARCH_CLIP = 2, AWQ_OP_PACK = 3 };
+
+/* Workspace bytes that let `op` process all `n_grid` candidates in one
+ * batch (the fastest configuration). Returns 0 for invalid sizes. Pure host
+ * arithmetic. */
+size_t awq_workspace_bytes(int op, int64_t T, int64_t N, int64_t K, int32_t n_grid,
+                           awq_dtype dtype);
+
+/* Workspace bytes for a search (AWQ_OP_SEARCH_SCALE / AWQ_OP_SEARCH_CLIP)
+ * that works through its `n_grid` candidates in batches of at most `batch`
+ * (1 <= batch <= n_grid; batch 1 is the minimum any search call accepts).
+ * A search call picks the largest batch its workspace allows; results do not
+ * depend on the batch. Returns 0 for invalid arguments. */
+size_t awq_workspace_bytes_batch(int op, int64_t T, int64_t N, int64_t K, int32_t n_grid,
+                                 int32_t batch, awq_dtype dtype);
+
+/* Step 1 — per-input-channel mean activation magnitude.
+ * X [T, K] (bf16, f16 or f32) -> abar [K] f32 with abar_j = fl32(Σ_t |x_tj| / T),
+ * the sum taken in float64. K must be a multiple of 8 (f32: of 4).
+ * Does not synchronise. */
+awq_status awq_act_stats(const void* X, awq_dtype x_dtype, int64_t T, int64_t K, float* abar,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Step 2 — scale table s[a][j] = ā_j^α_a / sqrt(max_k ā_k^α_a · min_k ā_k^α_a),
+ * computed in float64 and rounded once to f32; ā is floored at 1e-8.
+ * abar [K] f32; alphas [host] n_alpha values in [0, 1]; s_table [n_alpha, K].
+ * Does not synchronise. */
+awq_status awq_scale_table(const float* abar, int64_t K, const float* alphas, int32_t n_alpha,
+                           float* s_table, void* stream);
+
+/* Steps 2-6 — α grid search for one layer.
+ * X [T, K], W [N, K] of `dtype` (bf16 or f32); abar [K] from awq_act_stats;
+ * alphas [host] n_alpha values in [0, 1].
+ * Outputs: s_best [K] f32 = the scale row of the best α;
+ *          alpha_best [host] 1 f32; mse [host] n_alpha f64, mse[a] =
+ *          Σ_{t,n} (Y_a - Y)_{tn}² / (T·N) where Y_a uses the quantised,
+ *          folded weights; row_sums [n_alpha, N] f64 (per output channel
+ *          Σ_t, optional: may be NULL). Ties go to the lowest index.
+ * Synchronises `stream`. */
+awq_status awq_search_scale(const void* X, const void* W, awq_dtype dtype, int64_t T, int64_t N,
+                            int64_t K, const float* abar, const float* alphas, int32_t n_alpha,
+                            awq_qconfig qc, float* s_best, float* alpha_best, double* mse,
+                            double* row_sums, void* ws, size_t ws_bytes, void* stream);
+
+/* Step 7 — per-output-channel clip-ratio search with s fixed.
+ * s [K] f32 (normally s_best); ratios [host] n_ratio values in (0, 1].
+ * Every group of row n uses ratio r_n. Outputs: ratio_best [N] f32 (argmin
+ * per row, lowest index on ties); mse_clip [host] 1 f64 = Σ_n min_r M_n(r) / (T·N);
+ * row_sums [n_ratio, N] f64 = M_n(r) (optional: may be NULL).
+ * Synchronises `stream`. */
+awq_status awq_search_clip(const void* X, const void* W, awq_dtype dtype, int64_t T, int64_t N,
+                           int64_t K, const float* s, const float* ratios, int32_t n_ratio,
+                           awq_qconfig qc, float* ratio_best, double* mse_clip, double* row_sums,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* Step 8 — quantise W·diag(s) (rows clipped by `ratio`, NULL = 1) and pack.
+ * W [N, K] (bf16, f16 or f32), N a multiple of 8, w_bit 4.
+ * qweight [K, N/8] int32: word (k, j) holds the codes of rows 8j..8j+7 at
+ * column k, row 8j+i in bits 4i..4i+3. qzeros [K/128, N/8] int32 packed the
+ * same way. scales [K/128, N] IEEE fp16 bits (RNE of the f32 step).
+ * The codes represent W·diag(s); the caller folds diag(s)^-1 into the
+ * operation that produces X. ws: at least awq_workspace_bytes(AWQ_OP_PACK,...).
+ * Synchronises `stream`; returns AWQ_E_RANGE if a scale overflowed fp16. */
+awq_status awq_quantize_pack(const void* W, awq_dtype w_dtype, int64_t N, int64_t K,
+                             const float* s, const float* ratio, awq_qconfig qc, int32_t* qweight,
+                             int32_t* qzeros, uint16_t* scales, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* Message for the last non-OK status returned on the calling thread. */
+const char* awq_last_error(void);
+
+/* Kernel timing. When enabled, every kernel launch of the library is
+ * bracketed by HIP events recorded on the stream it is launched on;
+ * awq_profile_read synchronises those events and returns the summed
+ * duration (ms) and launch count of one kernel kind since the last reset.
+ * Kinds: 0 stats, 1 scale table, 2 transform (quantise/dequantise
+ * candidates), 3 search GEMM, 4 reductions, 5 pack. */
+enum { AWQ_K_STATS = 0, AWQ_K_SCALE = 1, AWQ_K_TRANSFORM = 2, AWQ_K_GEMM = 3, AWQ_K_REDUCE = 4,
+       AWQ_K_PACK = 5, AWQ_K_COUNT = 6 };
+void awq_profile_enable(int on);
+void awq_profile_reset(void);
+awq_status awq_profile_read(int kind, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AWQ_MI355X_AWQ_H */

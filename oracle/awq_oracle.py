@@ -49,10 +49,12 @@ F64 = np.float64
 # ----------------------------------------------------------------------------
 
 def decode(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact float32 values of an input tensor given as bf16 bit patterns
-    (``uint16``) or as float32."""
+    """Exact float32 values of an input tensor given as bf16 or fp16 bit
+    patterns (``uint16``) or as float32."""
     if dtype == "bf16":
         return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(F32)
+    if dtype == "f16":
+        return np.asarray(a, dtype=np.uint16).view(np.float16).astype(F32)
     if dtype == "f32":
         return np.asarray(a, dtype=F32)
     raise ValueError(f"unsupported dtype {dtype!r}")

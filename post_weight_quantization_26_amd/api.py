@@ -1,0 +1,175 @@
+"""Torch-facing wrappers of the C ABI: AWQ per-layer search on one MI355X.
+
+PyTorch provides device memory and the current HIP stream; every computation
+runs in the HIP library through the C ABI. Tensors must live on the GPU and be
+contiguous. Defaults follow the AutoAWQ configuration the roadmap page prints
+in section 9 (zero point on, group 128, 4 bits).
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+_DT = {torch.float32: L.AWQ_F32, torch.bfloat16: L.AWQ_BF16, torch.float16: L.AWQ_F16}
+
+DEFAULT_BITS = 4
+DEFAULT_GROUP = 128
+DEFAULT_ZERO_POINT = True
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def workspace_bytes(op: int, T: int, N: int, K: int, n_grid: int, dtype: torch.dtype) -> int:
+    return int(L.lib().awq_workspace_bytes(op, T, N, K, n_grid, _DT[dtype]))
+
+
+def workspace_bytes_batch(op: int, T: int, N: int, K: int, n_grid: int, batch: int,
+                          dtype: torch.dtype) -> int:
+    return int(L.lib().awq_workspace_bytes_batch(op, T, N, K, n_grid, batch, _DT[dtype]))
+
+
+def _workspace(ws: Optional[torch.Tensor], need: int, device) -> torch.Tensor:
+    if ws is not None:
+        return ws
+    return torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+
+
+def qconfig(bits=DEFAULT_BITS, group=DEFAULT_GROUP, zero_point=DEFAULT_ZERO_POINT) -> L.QConfig:
+    return L.QConfig(int(bits), int(group), int(bool(zero_point)))
+
+
+def act_stats(X: torch.Tensor, ws: Optional[torch.Tensor] = None,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-input-channel mean |x| over tokens: X [T, K] -> abar [K] float32."""
+    _dev(X, "X")
+    T, K = X.shape
+    abar = out if out is not None else torch.empty(K, dtype=torch.float32, device=X.device)
+    ws = _workspace(ws, workspace_bytes(L.AWQ_OP_STATS, T, 1, K, 1, X.dtype), X.device)
+    L.check(L.lib().awq_act_stats(_ptr(X), _dtype(X), T, K, _ptr(abar), _ptr(ws), ws.numel(),
+                                  _stream()))
+    return abar
+
+
+def scale_table(abar: torch.Tensor, alphas: Sequence[float]) -> torch.Tensor:
+    """s[a][j] = abar_j^alpha_a / sqrt(max abar^alpha_a * min abar^alpha_a), float32."""
+    _dev(abar, "abar")
+    n = len(alphas)
+    out = torch.empty((n, abar.numel()), dtype=torch.float32, device=abar.device)
+    L.check(L.lib().awq_scale_table(_ptr(abar), abar.numel(), L.float_array(alphas), n, _ptr(out),
+                                    _stream()))
+    return out
+
+
+def search_scale(X: torch.Tensor, W: torch.Tensor, abar: torch.Tensor, alphas: Sequence[float],
+                 bits: int = DEFAULT_BITS, group: int = DEFAULT_GROUP,
+                 zero_point: bool = DEFAULT_ZERO_POINT, want_row_sums: bool = False,
+                 ws: Optional[torch.Tensor] = None) -> dict:
+    """Grid search over alpha. Returns alpha_best, index, s_best [K], mse (numpy
+    [n_alpha]) and, if asked, row_sums [n_alpha, N] float64 on the GPU."""
+    _dev(X, "X"), _dev(W, "W"), _dev(abar, "abar")
+    if X.dtype != W.dtype:
+        raise ValueError("X and W must share a dtype")
+    T, K = X.shape
+    N = W.shape[0]
+    n = len(alphas)
+    ws = _workspace(ws, workspace_bytes(L.AWQ_OP_SEARCH_SCALE, T, N, K, n, X.dtype), X.device)
+    s_best = torch.empty(K, dtype=torch.float32, device=X.device)
+    rows = torch.empty((n, N), dtype=torch.float64, device=X.device) if want_row_sums else None
+    a_best = ctypes.c_float(0.0)
+    mse = (ctypes.c_double * n)()
+    grid = L.float_array(alphas)
+    L.check(L.lib().awq_search_scale(_ptr(X), _ptr(W), _dtype(X), T, N, K, _ptr(abar), grid, n,
+                                     qconfig(bits, group, zero_point), _ptr(s_best),
+                                     ctypes.byref(a_best), mse, _ptr(rows), _ptr(ws), ws.numel(),
+                                     _stream()))
+    mse_np = np.array(mse[:], dtype=np.float64)
+    g32 = np.asarray(alphas, dtype=np.float32)
+    idx = int(np.flatnonzero(g32 == np.float32(a_best.value))[0])
+    return dict(alpha_best=np.float32(a_best.value), index=idx, s_best=s_best, mse=mse_np,
+                row_sums=rows)
+
+
+def search_clip(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor, ratios: Sequence[float],
+                bits: int = DEFAULT_BITS, group: int = DEFAULT_GROUP,
+                zero_point: bool = DEFAULT_ZERO_POINT, want_row_sums: bool = False,
+                ws: Optional[torch.Tensor] = None) -> dict:
+    """Per-output-channel clip-ratio search with s fixed. Returns ratio_best [N]
+    (GPU), mse_clip (float) and optionally row_sums [n_ratio, N]."""
+    _dev(X, "X"), _dev(W, "W"), _dev(s, "s")
+    if X.dtype != W.dtype:
+        raise ValueError("X and W must share a dtype")
+    T, K = X.shape
+    N = W.shape[0]
+    n = len(ratios)
+    ws = _workspace(ws, workspace_bytes(L.AWQ_OP_SEARCH_CLIP, T, N, K, n, X.dtype), X.device)
+    r_best = torch.empty(N, dtype=torch.float32, device=X.device)
+    rows = torch.empty((n, N), dtype=torch.float64, device=X.device) if want_row_sums else None
+    mse_clip = ctypes.c_double(0.0)
+    L.check(L.lib().awq_search_clip(_ptr(X), _ptr(W), _dtype(X), T, N, K, _ptr(s),
+                                    L.float_array(ratios), n, qconfig(bits, group, zero_point),
+                                    _ptr(r_best), ctypes.byref(mse_clip), _ptr(rows), _ptr(ws),
+                                    ws.numel(), _stream()))
+    return dict(ratio_best=r_best, mse_clip=float(mse_clip.value), row_sums=rows)
+
+
+def quantize_pack(W: torch.Tensor, s: torch.Tensor, ratio: Optional[torch.Tensor] = None,
+                  bits: int = DEFAULT_BITS, group: int = DEFAULT_GROUP,
+                  zero_point: bool = DEFAULT_ZERO_POINT, ws: Optional[torch.Tensor] = None,
+                  out=None):
+    """Packed layer: qweight [K, N/8] int32, qzeros [K/g, N/8] int32, scales [K/g, N] float16."""
+    _dev(W, "W"), _dev(s, "s")
+    if ratio is not None:
+        _dev(ratio, "ratio")
+    N, K = W.shape
+    if out is None:
+        qweight = torch.empty((K, N // 8), dtype=torch.int32, device=W.device)
+        qzeros = torch.empty((K // group, N // 8), dtype=torch.int32, device=W.device)
+        scales = torch.empty((K // group, N), dtype=torch.float16, device=W.device)
+    else:
+        qweight, qzeros, scales = out
+    ws = _workspace(ws, workspace_bytes(L.AWQ_OP_PACK, 1, N, K, 1, W.dtype), W.device)
+    L.check(L.lib().awq_quantize_pack(_ptr(W), _dtype(W), N, K, _ptr(s), _ptr(ratio),
+                                      qconfig(bits, group, zero_point), _ptr(qweight),
+                                      _ptr(qzeros), _ptr(scales), _ptr(ws), ws.numel(), _stream()))
+    return qweight, qzeros, scales
+
+
+def profile_enable(on: bool = True) -> None:
+    L.lib().awq_profile_enable(1 if on else 0)
+
+
+def profile_reset() -> None:
+    L.lib().awq_profile_reset()
+
+
+def profile_read(kind: str):
+    """(total milliseconds, launches) of one kernel kind since the last reset."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    L.check(L.lib().awq_profile_read(L.KERNEL_KINDS[kind], ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

@@ -1,0 +1,300 @@
+// The C ABI entry points: validate on the host, then enqueue the HIP kernels
+// on the caller's stream. See include/awq.h for the contract of each call.
+#include <hip/hip_runtime_api.h>
+
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "awq_internal.h"
+
+namespace awq {
+// Launchers (HIP translation units).
+hipError_t launch_stats(const void* X, int dtype, int64_t T, int64_t K, int64_t chunks,
+                        double* partial, float* abar, hipStream_t st);
+hipError_t launch_scale_table(const float* abar, int64_t K, const float* alphas_host, int n,
+                              float* s_table, hipStream_t st);
+hipError_t launch_transform(const void* W, int dtype, int64_t N, int64_t K, const float* s_rows,
+                            int64_t s_stride, const float* ratios_host, int nc, int bits,
+                            int zero_point, void* E, hipStream_t st);
+hipError_t launch_search_gemm(const void* X, int dtype, const void* E, int64_t M, int64_t Nc,
+                              int64_t K, float* partials, hipStream_t st);
+hipError_t launch_reduce_rows(const float* partials, int64_t MT, int64_t Nc, double* row_sums,
+                              hipStream_t st);
+hipError_t launch_curve(const double* row_sums, int n_cand, int64_t N, double denom,
+                        double* mse, hipStream_t st);
+hipError_t launch_clip_select(const double* row_sums, int n_ratio, int64_t N,
+                              const float* ratios_host, double denom, float* ratio_best,
+                              double* best, double* mse_clip, hipStream_t st);
+hipError_t launch_pack(const void* W, int dtype, int64_t N, int64_t K, const float* s,
+                       const float* ratio, int zero_point, int32_t* qweight, int32_t* qzeros,
+                       uint16_t* scales, int* overflow, hipStream_t st);
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Optional kernel timing with HIP events on the launch stream.
+// ---------------------------------------------------------------------------
+struct Pending {
+  int kind;
+  hipEvent_t a, b;
+};
+
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> spare;
+  double ms[AWQ_K_COUNT] = {};
+  int64_t n[AWQ_K_COUNT] = {};
+};
+
+Profiler& prof() {
+  static Profiler p;
+  return p;
+}
+
+hipEvent_t take_event() {
+  Profiler& p = prof();
+  if (!p.spare.empty()) {
+    hipEvent_t e = p.spare.back();
+    p.spare.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+hipError_t timed(int kind, hipStream_t st, F&& launch) {
+  Profiler& p = prof();
+  std::unique_lock<std::mutex> lk(p.mu);
+  if (!p.on) {
+    lk.unlock();
+    return launch();
+  }
+  hipEvent_t a = take_event(), b = take_event();
+  if (a && b) hipEventRecord(a, st);
+  hipError_t e = launch();
+  if (a && b) {
+    hipEventRecord(b, st);
+    p.pending.push_back({kind, a, b});
+  }
+  return e;
+}
+
+awq_status hip_fail(hipError_t e, const char* where) {
+  return set_error(AWQ_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define AWQ_HIP(call, where)                     \
+  do {                                           \
+    hipError_t e__ = (call);                     \
+    if (e__ != hipSuccess) return hip_fail(e__, where); \
+  } while (0)
+
+int dt(awq_dtype d) { return d == AWQ_F32 ? 0 : d == AWQ_BF16 ? 1 : 2; }
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// Runs transform -> GEMM -> row reduction for candidates [c0, c0+cb).
+awq_status run_batch(const void* X, const void* W, awq_dtype d, int64_t T, int64_t N, int64_t K,
+                     const float* s_rows, int64_t s_stride, const float* ratios_host, int cb,
+                     awq_qconfig qc, const SearchLayout& L, void* ws, double* row_sums_out,
+                     hipStream_t st) {
+  void* E = at<void>(ws, L.E);
+  float* partials = at<float>(ws, L.partials);
+  AWQ_HIP(timed(AWQ_K_TRANSFORM, st,
+                [&] {
+                  return launch_transform(W, dt(d), N, K, s_rows, s_stride, ratios_host, cb,
+                                          qc.w_bit, qc.zero_point, E, st);
+                }),
+          "transform");
+  AWQ_HIP(timed(AWQ_K_GEMM, st,
+                [&] { return launch_search_gemm(X, dt(d), E, T, int64_t(cb) * N, K, partials, st); }),
+          "search_gemm");
+  AWQ_HIP(timed(AWQ_K_REDUCE, st,
+                [&] { return launch_reduce_rows(partials, L.MT, int64_t(cb) * N, row_sums_out, st); }),
+          "reduce_rows");
+  return AWQ_OK;
+}
+
+}  // namespace
+}  // namespace awq
+
+using namespace awq;
+
+extern "C" awq_status awq_act_stats(const void* X, awq_dtype x_dtype, int64_t T, int64_t K,
+                                    float* abar, void* ws, size_t ws_bytes, void* stream) {
+  awq_status s = check_stats(X, x_dtype, T, K, abar, ws, ws_bytes);
+  if (s != AWQ_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t chunks = stats_chunks(T, K, x_dtype);
+  AWQ_HIP(timed(AWQ_K_STATS, st,
+                [&] {
+                  return launch_stats(X, dt(x_dtype), T, K, chunks, static_cast<double*>(ws), abar,
+                                      st);
+                }),
+          "act_stats");
+  return AWQ_OK;
+}
+
+extern "C" awq_status awq_scale_table(const float* abar, int64_t K, const float* alphas,
+                                      int32_t n_alpha, float* s_table, void* stream) {
+  awq_status s = check_scale_table(abar, K, alphas, n_alpha, s_table);
+  if (s != AWQ_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  AWQ_HIP(timed(AWQ_K_SCALE, st,
+                [&] { return launch_scale_table(abar, K, alphas, n_alpha, s_table, st); }),
+          "scale_table");
+  return AWQ_OK;
+}
+
+extern "C" awq_status awq_search_scale(const void* X, const void* W, awq_dtype dtype, int64_t T,
+                                       int64_t N, int64_t K, const float* abar,
+                                       const float* alphas, int32_t n_alpha, awq_qconfig qc,
+                                       float* s_best, float* alpha_best, double* mse,
+                                       double* row_sums, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  int32_t nb = 0;
+  awq_status s = check_search(AWQ_OP_SEARCH_SCALE, X, W, dtype, T, N, K, abar, alphas, n_alpha,
+                              qc, s_best, alpha_best, mse, ws, ws_bytes, &nb);
+  if (s != AWQ_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const SearchLayout L = search_layout(AWQ_OP_SEARCH_SCALE, T, N, K, n_alpha, nb, dtype);
+  float* s_table = at<float>(ws, L.s_table);
+  double* rs = at<double>(ws, L.row_sums);
+  double* mse_dev = at<double>(ws, L.mse);
+
+  AWQ_HIP(timed(AWQ_K_SCALE, st,
+                [&] { return launch_scale_table(abar, K, alphas, n_alpha, s_table, st); }),
+          "scale_table");
+  for (int c0 = 0; c0 < n_alpha; c0 += nb) {
+    const int cb = n_alpha - c0 < nb ? n_alpha - c0 : nb;
+    s = run_batch(X, W, dtype, T, N, K, s_table + int64_t(c0) * K, K, nullptr, cb, qc, L, ws,
+                  rs + int64_t(c0) * N, st);
+    if (s != AWQ_OK) return s;
+  }
+  AWQ_HIP(timed(AWQ_K_REDUCE, st,
+                [&] { return launch_curve(rs, n_alpha, N, double(T) * double(N), mse_dev, st); }),
+          "curve");
+  AWQ_HIP(hipMemcpyAsync(mse, mse_dev, sizeof(double) * size_t(n_alpha), hipMemcpyDeviceToHost, st),
+          "copy mse");
+  AWQ_HIP(hipStreamSynchronize(st), "synchronize");
+  int best = 0;
+  for (int i = 1; i < n_alpha; ++i)
+    if (mse[i] < mse[best]) best = i;
+  *alpha_best = alphas[best];
+  AWQ_HIP(hipMemcpyAsync(s_best, s_table + int64_t(best) * K, sizeof(float) * size_t(K),
+                         hipMemcpyDeviceToDevice, st),
+          "copy s_best");
+  if (row_sums)
+    AWQ_HIP(hipMemcpyAsync(row_sums, rs, sizeof(double) * size_t(n_alpha) * size_t(N),
+                           hipMemcpyDeviceToDevice, st),
+            "copy row_sums");
+  AWQ_HIP(hipStreamSynchronize(st), "synchronize");
+  return AWQ_OK;
+}
+
+extern "C" awq_status awq_search_clip(const void* X, const void* W, awq_dtype dtype, int64_t T,
+                                      int64_t N, int64_t K, const float* s, const float* ratios,
+                                      int32_t n_ratio, awq_qconfig qc, float* ratio_best,
+                                      double* mse_clip, double* row_sums, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  int32_t nb = 0;
+  awq_status st_ = check_search(AWQ_OP_SEARCH_CLIP, X, W, dtype, T, N, K, s, ratios, n_ratio, qc,
+                                ratio_best, mse_clip, nullptr, ws, ws_bytes, &nb);
+  if (st_ != AWQ_OK) return st_;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const SearchLayout L = search_layout(AWQ_OP_SEARCH_CLIP, T, N, K, n_ratio, nb, dtype);
+  double* rs = at<double>(ws, L.row_sums);
+  double* best = at<double>(ws, L.best);
+  double* mc = at<double>(ws, L.scalar);
+  for (int c0 = 0; c0 < n_ratio; c0 += nb) {
+    const int cb = n_ratio - c0 < nb ? n_ratio - c0 : nb;
+    st_ = run_batch(X, W, dtype, T, N, K, s, 0, ratios + c0, cb, qc, L, ws, rs + int64_t(c0) * N,
+                    st);
+    if (st_ != AWQ_OK) return st_;
+  }
+  AWQ_HIP(timed(AWQ_K_REDUCE, st,
+                [&] {
+                  return launch_clip_select(rs, n_ratio, N, ratios, double(T) * double(N),
+                                            ratio_best, best, mc, st);
+                }),
+          "clip_select");
+  if (row_sums)
+    AWQ_HIP(hipMemcpyAsync(row_sums, rs, sizeof(double) * size_t(n_ratio) * size_t(N),
+                           hipMemcpyDeviceToDevice, st),
+            "copy row_sums");
+  AWQ_HIP(hipMemcpyAsync(mse_clip, mc, sizeof(double), hipMemcpyDeviceToHost, st), "copy mse_clip");
+  AWQ_HIP(hipStreamSynchronize(st), "synchronize");
+  return AWQ_OK;
+}
+
+extern "C" awq_status awq_quantize_pack(const void* W, awq_dtype w_dtype, int64_t N, int64_t K,
+                                        const float* s, const float* ratio, awq_qconfig qc,
+                                        int32_t* qweight, int32_t* qzeros, uint16_t* scales,
+                                        void* ws, size_t ws_bytes, void* stream) {
+  awq_status s_ = check_pack(W, w_dtype, N, K, s, qc, qweight, qzeros, scales, ws, ws_bytes);
+  if (s_ != AWQ_OK) return s_;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int* flag = static_cast<int*>(ws);
+  AWQ_HIP(hipMemsetAsync(flag, 0, sizeof(int), st), "clear overflow flag");
+  AWQ_HIP(timed(AWQ_K_PACK, st,
+                [&] {
+                  return launch_pack(W, dt(w_dtype), N, K, s, ratio, qc.zero_point, qweight,
+                                     qzeros, scales, flag, st);
+                }),
+          "pack");
+  int host_flag = 0;
+  AWQ_HIP(hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, st), "copy flag");
+  AWQ_HIP(hipStreamSynchronize(st), "synchronize");
+  if (host_flag) return set_error(AWQ_E_RANGE, "quantize_pack: a group step overflows fp16");
+  return AWQ_OK;
+}
+
+extern "C" void awq_profile_enable(int on) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  p.on = on != 0;
+}
+
+extern "C" void awq_profile_reset(void) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  for (auto& q : p.pending) {
+    hipEventSynchronize(q.b);
+    p.spare.push_back(q.a);
+    p.spare.push_back(q.b);
+  }
+  p.pending.clear();
+  for (int i = 0; i < AWQ_K_COUNT; ++i) {
+    p.ms[i] = 0.0;
+    p.n[i] = 0;
+  }
+}
+
+extern "C" awq_status awq_profile_read(int kind, double* total_ms, int64_t* launches) {
+  if (kind < 0 || kind >= AWQ_K_COUNT || !total_ms || !launches)
+    return set_error(AWQ_E_INVALID, "profile_read: bad kind or NULL output");
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  for (auto& q : p.pending) {
+    hipError_t e = hipEventSynchronize(q.b);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, q.a, q.b);
+    if (e != hipSuccess) return hip_fail(e, "profile_read");
+    p.ms[q.kind] += double(ms);
+    p.n[q.kind] += 1;
+    p.spare.push_back(q.a);
+    p.spare.push_back(q.b);
+  }
+  p.pending.clear();
+  *total_ms = p.ms[kind];
+  *launches = p.n[kind];
+  return AWQ_OK;
+}

@@ -1,0 +1,60 @@
+// Internal declarations shared by the C ABI and the HIP kernels. Host-only
+// types: nothing here needs the HIP headers, so the argument checks and the
+// workspace arithmetic can be compiled and tested without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "awq.h"
+
+namespace awq {
+
+constexpr int kGroup = 128;
+constexpr int kMaxGrid = 64;
+constexpr int kGemmBM_bf16 = 256;  // token rows per search-GEMM tile (bf16 MFMA path)
+constexpr int kGemmBM_f32 = 64;    // token rows per tile on the fp32 path
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline size_t dtype_bytes(awq_dtype d) { return d == AWQ_F32 ? 4 : 2; }
+
+// Number of token chunks the stats kernel splits T into (one float64 partial
+// row per chunk); chosen so the launch has ~2048 workgroups.
+int64_t stats_chunks(int64_t T, int64_t K, awq_dtype d);
+
+// Byte offsets of the regions of a search workspace for a batch of `nb`
+// candidates out of `n_grid`.
+struct SearchLayout {
+  size_t s_table;   // [n_grid, K] f32 (scale search only)
+  size_t E;         // [nb, N, K] candidate error weights (bf16 or f32)
+  size_t partials;  // [MT, nb*N] f32 per-tile column sums of squares
+  size_t row_sums;  // [n_grid, N] f64
+  size_t mse;       // [n_grid] f64
+  size_t best;      // [N] f64 best per-row sums (clip search)
+  size_t scalar;    // [8] f64
+  size_t total;
+  int64_t MT;
+};
+SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_grid, int32_t nb,
+                           awq_dtype dtype);
+
+// Host-side argument checks. Return AWQ_OK or an error (message via set_error).
+awq_status check_stats(const void* X, awq_dtype d, int64_t T, int64_t K, const float* abar,
+                       const void* ws, size_t ws_bytes);
+awq_status check_scale_table(const float* abar, int64_t K, const float* alphas, int32_t n,
+                             const float* s_table);
+awq_status check_search(int op, const void* X, const void* W, awq_dtype d, int64_t T, int64_t N,
+                        int64_t K, const float* vec, const float* grid, int32_t n_grid,
+                        awq_qconfig qc, const void* out_dev, const void* out_host,
+                        const void* out_host2, const void* ws, size_t ws_bytes, int32_t* nb);
+awq_status check_pack(const void* W, awq_dtype d, int64_t N, int64_t K, const float* s,
+                      awq_qconfig qc, const int32_t* qweight, const int32_t* qzeros,
+                      const uint16_t* scales, const void* ws, size_t ws_bytes);
+
+awq_status set_error(awq_status st, const char* fmt, ...);
+
+}  // namespace awq

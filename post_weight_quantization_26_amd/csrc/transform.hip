@@ -1,0 +1,111 @@
+// Steps 3-4 — quantise W·diag(s_c) group-wise, dequantise, fold diag(s_c)^-1
+// back and subtract W, for every candidate c of a batch:
+//
+//   E_c[n][k] = (q - zero)·step / s_c[k] - W[n][k]
+//
+// so that X·E_cᵀ = Y_c - Y, the output error of candidate c ("05 — AWQ",
+// section 3 "The scaling trick" for the fold; section 4 for quantise then
+// measure the output error; "Optional: per-channel clipping" for the ratio).
+//
+// One lane owns 8 consecutive input channels of one row; the 16 lanes of a
+// 128-wide group find its min/max with xor-shuffles, so every lane holds the
+// group's step and zero point. W is read once per batch and each candidate's
+// E row segment is written with one 16-byte store per lane (bf16) — the
+// kernel is bound by the E write stream. Codes use exact IEEE float32
+// division and rint, as in the packed output.
+#include "device_common.h"
+
+namespace awq {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int DT>
+__device__ __forceinline__ void store8(void* E, int64_t idx, const float (&e)[8]);
+
+template <>
+__device__ __forceinline__ void store8<1>(void* E, int64_t idx, const float (&e)[8]) {
+  uint4 q;
+  q.x = uint32_t(f32_to_bf16_rne(e[0])) | (uint32_t(f32_to_bf16_rne(e[1])) << 16);
+  q.y = uint32_t(f32_to_bf16_rne(e[2])) | (uint32_t(f32_to_bf16_rne(e[3])) << 16);
+  q.z = uint32_t(f32_to_bf16_rne(e[4])) | (uint32_t(f32_to_bf16_rne(e[5])) << 16);
+  q.w = uint32_t(f32_to_bf16_rne(e[6])) | (uint32_t(f32_to_bf16_rne(e[7])) << 16);
+  *reinterpret_cast<uint4*>(static_cast<uint16_t*>(E) + idx) = q;
+}
+
+template <>
+__device__ __forceinline__ void store8<0>(void* E, int64_t idx, const float (&e)[8]) {
+  float4* p = reinterpret_cast<float4*>(static_cast<float*>(E) + idx);
+  p[0] = make_float4(e[0], e[1], e[2], e[3]);
+  p[1] = make_float4(e[4], e[5], e[6], e[7]);
+}
+
+// DT: 0 = f32 (E in f32), 1 = bf16 (E in bf16).
+template <int DT>
+__global__ __launch_bounds__(kThreads) void transform_kernel(
+    const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s_rows,
+    int64_t s_stride, GridArgs ratios, int has_ratio, int nc, int bits, int zero_point,
+    void* __restrict__ E) {
+#pragma clang fp contract(off)
+  const int64_t NK = N * K;
+  const int64_t e0 = (int64_t(blockIdx.x) * kThreads + threadIdx.x) * 8;  // flat n*K + k
+  // NK is a multiple of 128, so the 16 lanes of a group are all in range or all out.
+  const bool active = e0 < NK;
+  const int64_t k = active ? e0 % K : 0;
+
+  float w[8];
+  if (active) {
+    load8<DT>(W, e0, w);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = 0.f;
+  }
+
+  for (int c = 0; c < nc; ++c) {
+    const float* s = s_rows + int64_t(c) * s_stride + k;
+    float sv[8], wp[8];
+    float mx = 0.f, mn = 0.f;  // range widened to contain 0
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      sv[i] = active ? s[i] : 1.f;
+      wp[i] = w[i] * sv[i];
+      mx = fmaxf(mx, wp[i]);
+      mn = fminf(mn, wp[i]);
+    }
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      mx = fmaxf(mx, __shfl_xor(mx, off));
+      mn = fminf(mn, __shfl_xor(mn, off));
+    }
+    const float r = has_ratio ? ratios.v[c] : 1.f;
+    const QParams p = group_qparams(mx, mn, r, bits, zero_point);
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float q = quant_code(wp[i], p);
+      e[i] = ((q - p.zero) * p.step) / sv[i] - w[i];
+    }
+    if (active) store8<DT>(E, int64_t(c) * NK + e0, e);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_transform(const void* W, int dtype, int64_t N, int64_t K, const float* s_rows,
+                            int64_t s_stride, const float* ratios_host, int nc, int bits,
+                            int zero_point, void* E, hipStream_t st) {
+  GridArgs g{};
+  const int has_ratio = ratios_host != nullptr;
+  for (int i = 0; i < nc && i < 64; ++i) g.v[i] = has_ratio ? ratios_host[i] : 1.f;
+  const int64_t lanes = N * K / 8;
+  const unsigned blocks = unsigned((lanes + kThreads - 1) / kThreads);
+  if (dtype == 1)
+    transform_kernel<1><<<blocks, kThreads, 0, st>>>(W, N, K, s_rows, s_stride, g, has_ratio, nc,
+                                                     bits, zero_point, E);
+  else
+    transform_kernel<0><<<blocks, kThreads, 0, st>>>(W, N, K, s_rows, s_stride, g, has_ratio, nc,
+                                                     bits, zero_point, E);
+  return hipGetLastError();
+}
+
+}  // namespace awq

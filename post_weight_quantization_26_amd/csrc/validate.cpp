@@ -1,0 +1,199 @@
+// Argument checks and workspace arithmetic of the C ABI. Plain C++: no HIP
+// headers and no HIP calls, so every rejection path runs on a machine
+// without a GPU.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "awq_internal.h"
+
+namespace awq {
+
+static thread_local char g_err[512] = "";
+
+awq_status set_error(awq_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+static bool dtype_ok(awq_dtype d) { return d == AWQ_F32 || d == AWQ_BF16 || d == AWQ_F16; }
+
+// Upper bound on any single dimension; keeps every index product in int64.
+static constexpr int64_t kMaxDim = int64_t(1) << 31;
+
+int64_t stats_chunks(int64_t T, int64_t K, awq_dtype d) {
+  const int64_t vec = 16 / int64_t(dtype_bytes(d));
+  const int64_t col_blocks = ceil_div(K, 64 * vec);
+  int64_t chunks = ceil_div(2048, col_blocks);
+  const int64_t max_chunks = ceil_div(T, 64);  // at least 64 rows (16 per row lane) per chunk
+  if (chunks > max_chunks) chunks = max_chunks;
+  if (chunks < 1) chunks = 1;
+  return chunks;
+}
+
+SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_grid, int32_t nb,
+                           awq_dtype dtype) {
+  SearchLayout L{};
+  const int64_t bm = dtype == AWQ_F32 ? kGemmBM_f32 : kGemmBM_bf16;
+  L.MT = ceil_div(T, bm);
+  size_t off = 0;
+  L.s_table = off;
+  if (op == AWQ_OP_SEARCH_SCALE) off += align_up(size_t(n_grid) * size_t(K) * 4);
+  L.E = off;
+  off += align_up(size_t(nb) * size_t(N) * size_t(K) * dtype_bytes(dtype));
+  L.partials = off;
+  off += align_up(size_t(L.MT) * size_t(nb) * size_t(N) * 4);
+  L.row_sums = off;
+  off += align_up(size_t(n_grid) * size_t(N) * 8);
+  L.mse = off;
+  off += align_up(size_t(n_grid) * 8);
+  L.best = off;
+  off += align_up(size_t(N) * 8);
+  L.scalar = off;
+  off += align_up(64);
+  L.total = off;
+  return L;
+}
+
+awq_status check_stats(const void* X, awq_dtype d, int64_t T, int64_t K, const float* abar,
+                       const void* ws, size_t ws_bytes) {
+  if (!X || !abar) return set_error(AWQ_E_INVALID, "act_stats: NULL X or abar");
+  if (!dtype_ok(d)) return set_error(AWQ_E_INVALID, "act_stats: unknown dtype %d", int(d));
+  if (T < 1 || K < 1 || T > kMaxDim || K > kMaxDim)
+    return set_error(AWQ_E_INVALID, "act_stats: bad shape T=%lld K=%lld", (long long)T,
+                     (long long)K);
+  const int64_t vec = 16 / int64_t(dtype_bytes(d));
+  if (K % vec) return set_error(AWQ_E_INVALID, "act_stats: K=%lld must be a multiple of %lld",
+                                (long long)K, (long long)vec);
+  if (!aligned16(X) || !aligned4(abar))
+    return set_error(AWQ_E_INVALID, "act_stats: X must be 16-byte aligned");
+  const size_t need = awq_workspace_bytes(AWQ_OP_STATS, T, 1, K, 1, d);
+  if (!ws || !aligned16(ws) || ws_bytes < need)
+    return set_error(AWQ_E_WORKSPACE, "act_stats: workspace needs %zu bytes (16-byte aligned)",
+                     need);
+  return AWQ_OK;
+}
+
+awq_status check_scale_table(const float* abar, int64_t K, const float* alphas, int32_t n,
+                             const float* s_table) {
+  if (!abar || !alphas || !s_table) return set_error(AWQ_E_INVALID, "scale_table: NULL pointer");
+  if (K < 1 || K > kMaxDim) return set_error(AWQ_E_INVALID, "scale_table: bad K");
+  if (n < 1 || n > kMaxGrid)
+    return set_error(AWQ_E_INVALID, "scale_table: n_alpha=%d outside 1..%d", n, kMaxGrid);
+  for (int i = 0; i < n; ++i)
+    if (!(alphas[i] >= 0.f && alphas[i] <= 1.f))
+      return set_error(AWQ_E_INVALID, "scale_table: alpha[%d] outside [0, 1]", i);
+  return AWQ_OK;
+}
+
+static awq_status check_qconfig(awq_qconfig qc, bool pack) {
+  if (qc.group_size != kGroup)
+    return set_error(AWQ_E_UNSUPPORTED, "group_size %d not supported (128 only)", qc.group_size);
+  if (pack ? qc.w_bit != 4 : (qc.w_bit != 3 && qc.w_bit != 4))
+    return set_error(AWQ_E_UNSUPPORTED, "w_bit %d not supported here (%s)", qc.w_bit,
+                     pack ? "pack: 4" : "search: 3 or 4");
+  if (qc.zero_point != 0 && qc.zero_point != 1)
+    return set_error(AWQ_E_INVALID, "zero_point must be 0 or 1");
+  return AWQ_OK;
+}
+
+awq_status check_search(int op, const void* X, const void* W, awq_dtype d, int64_t T, int64_t N,
+                        int64_t K, const float* vec, const float* grid, int32_t n_grid,
+                        awq_qconfig qc, const void* out_dev, const void* out_host,
+                        const void* out_host2, const void* ws, size_t ws_bytes, int32_t* nb) {
+  const char* nm = op == AWQ_OP_SEARCH_SCALE ? "search_scale" : "search_clip";
+  if (!X || !W || !vec || !grid || !out_dev || !out_host || (op == AWQ_OP_SEARCH_SCALE && !out_host2))
+    return set_error(AWQ_E_INVALID, "%s: NULL pointer argument", nm);
+  if (!dtype_ok(d)) return set_error(AWQ_E_INVALID, "%s: unknown dtype %d", nm, int(d));
+  if (d == AWQ_F16)
+    return set_error(AWQ_E_UNSUPPORTED, "%s: fp16 inputs are not supported (bf16 or f32)", nm);
+  if (T < 1 || N < 1 || K < 1 || T > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return set_error(AWQ_E_INVALID, "%s: bad shape T=%lld N=%lld K=%lld", nm, (long long)T,
+                     (long long)N, (long long)K);
+  awq_status st = check_qconfig(qc, false);
+  if (st != AWQ_OK) return st;
+  if (K % qc.group_size)
+    return set_error(AWQ_E_INVALID, "%s: K=%lld is not a multiple of the group size", nm,
+                     (long long)K);
+  if (n_grid < 1 || n_grid > kMaxGrid)
+    return set_error(AWQ_E_INVALID, "%s: grid size %d outside 1..%d", nm, n_grid, kMaxGrid);
+  for (int i = 0; i < n_grid; ++i) {
+    const float g = grid[i];
+    const bool ok = op == AWQ_OP_SEARCH_SCALE ? (g >= 0.f && g <= 1.f) : (g > 0.f && g <= 1.f);
+    if (!ok) return set_error(AWQ_E_INVALID, "%s: grid[%d]=%g out of range", nm, i, double(g));
+  }
+  if (!aligned16(X) || !aligned16(W) || !aligned4(vec) || !aligned4(out_dev))
+    return set_error(AWQ_E_INVALID, "%s: X and W must be 16-byte aligned", nm);
+  const size_t need1 = search_layout(op, T, N, K, n_grid, 1, d).total;
+  if (!ws || !aligned16(ws) || ws_bytes < need1)
+    return set_error(AWQ_E_WORKSPACE, "%s: workspace needs at least %zu bytes (16-byte aligned)",
+                     nm, need1);
+  int32_t b = n_grid;
+  while (b > 1 && search_layout(op, T, N, K, n_grid, b, d).total > ws_bytes) --b;
+  *nb = b;
+  return AWQ_OK;
+}
+
+awq_status check_pack(const void* W, awq_dtype d, int64_t N, int64_t K, const float* s,
+                      awq_qconfig qc, const int32_t* qweight, const int32_t* qzeros,
+                      const uint16_t* scales, const void* ws, size_t ws_bytes) {
+  if (!W || !s || !qweight || !qzeros || !scales)
+    return set_error(AWQ_E_INVALID, "quantize_pack: NULL pointer argument");
+  if (!dtype_ok(d)) return set_error(AWQ_E_INVALID, "quantize_pack: unknown dtype %d", int(d));
+  if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim)
+    return set_error(AWQ_E_INVALID, "quantize_pack: bad shape N=%lld K=%lld", (long long)N,
+                     (long long)K);
+  awq_status st = check_qconfig(qc, true);
+  if (st != AWQ_OK) return st;
+  if (N % 8) return set_error(AWQ_E_INVALID, "quantize_pack: N=%lld not a multiple of 8",
+                              (long long)N);
+  if (K % qc.group_size)
+    return set_error(AWQ_E_INVALID, "quantize_pack: K=%lld not a multiple of the group size",
+                     (long long)K);
+  if (!aligned16(W) || !aligned4(qweight) || !aligned4(qzeros) || !aligned4(scales) ||
+      !aligned4(s))
+    return set_error(AWQ_E_INVALID, "quantize_pack: W must be 16-byte aligned, outputs 4-byte");
+  const size_t need = awq_workspace_bytes(AWQ_OP_PACK, 1, N, K, 1, d);
+  if (!ws || !aligned8(ws) || ws_bytes < need)
+    return set_error(AWQ_E_WORKSPACE, "quantize_pack: workspace needs %zu bytes", need);
+  return AWQ_OK;
+}
+
+}  // namespace awq
+
+extern "C" size_t awq_workspace_bytes(int op, int64_t T, int64_t N, int64_t K, int32_t n_grid,
+                                      awq_dtype dtype) {
+  using namespace awq;
+  if (T < 1 || N < 1 || K < 1 || n_grid < 1 || n_grid > kMaxGrid) return 0;
+  if (T > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+  if (!(dtype == AWQ_F32 || dtype == AWQ_BF16 || dtype == AWQ_F16)) return 0;
+  switch (op) {
+    case AWQ_OP_STATS:
+      return align_up(size_t(stats_chunks(T, K, dtype)) * size_t(K) * 8);
+    case AWQ_OP_SEARCH_SCALE:
+    case AWQ_OP_SEARCH_CLIP:
+      return search_layout(op, T, N, K, n_grid, n_grid, dtype).total;
+    case AWQ_OP_PACK:
+      return kAlign;
+    default:
+      return 0;
+  }
+}
+
+extern "C" size_t awq_workspace_bytes_batch(int op, int64_t T, int64_t N, int64_t K,
+                                            int32_t n_grid, int32_t batch, awq_dtype dtype) {
+  using namespace awq;
+  if (op != AWQ_OP_SEARCH_SCALE && op != AWQ_OP_SEARCH_CLIP) return 0;
+  if (batch < 1 || batch > n_grid) return 0;
+  if (awq_workspace_bytes(op, T, N, K, n_grid, dtype) == 0) return 0;
+  return search_layout(op, T, N, K, n_grid, batch, dtype).total;
+}
+
+extern "C" const char* awq_last_error(void) { return awq::g_err; }

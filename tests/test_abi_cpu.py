@@ -1,0 +1,180 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+sizes workspaces, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from post_weight_quantization_26_amd import build_lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "awq.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(build_lib.LIB_PATH):
+        build_lib.build()
+    from post_weight_quantization_26_amd import _lib
+    _lib.lib()
+    return _lib
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(awq_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("awq_act_stats", "awq_search_scale", "awq_search_clip", "awq_quantize_pack",
+              "awq_workspace_bytes", "awq_last_error", "awq_scale_table"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    lib = ctypes.CDLL(build_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in L.SIGNATURES, f"binding lacks {name}"
+
+
+def test_workspace_sizes(L):
+    lib = L.lib()
+    ws = lib.awq_workspace_bytes
+    # search: s table + E batch + per-tile partials + row sums + curve
+    full = ws(L.AWQ_OP_SEARCH_SCALE, 65536, 4096, 4096, 20, L.AWQ_BF16)
+    e_bytes = 20 * 4096 * 4096 * 2
+    part = 256 * 20 * 4096 * 4
+    assert full >= e_bytes + part and full < e_bytes + part + (1 << 20)
+    one = lib.awq_workspace_bytes_batch(L.AWQ_OP_SEARCH_SCALE, 65536, 4096, 4096, 20, 1, L.AWQ_BF16)
+    assert one < full / 10
+    assert lib.awq_workspace_bytes_batch(L.AWQ_OP_SEARCH_SCALE, 65536, 4096, 4096, 20, 20,
+                                         L.AWQ_BF16) == full
+    assert lib.awq_workspace_bytes_batch(L.AWQ_OP_SEARCH_SCALE, 65536, 4096, 4096, 20, 21,
+                                         L.AWQ_BF16) == 0
+    assert lib.awq_workspace_bytes_batch(L.AWQ_OP_PACK, 1, 64, 128, 1, 1, L.AWQ_BF16) == 0
+    # the minimum a search accepts is batch 1: one byte less is rejected
+    FAKEW = ctypes.c_void_p(0x10000)
+    mse = (ctypes.c_double * 20)()
+    a_best = ctypes.c_float()
+    st = lib.awq_search_scale(FAKEW, FAKEW, L.AWQ_BF16, 65536, 4096, 4096, FAKEW,
+                              L.float_array([0.5] * 20), 20, L.QConfig(4, 128, 1), FAKEW,
+                              ctypes.byref(a_best), mse, None, FAKEW, one - 1, None)
+    assert st == L.AWQ_E_WORKSPACE
+    assert ws(L.AWQ_OP_PACK, 1, 4096, 4096, 1, L.AWQ_BF16) > 0
+    assert ws(L.AWQ_OP_STATS, 65536, 1, 4096, 1, L.AWQ_BF16) >= 4096 * 8
+    for bad in ((9, 1, 1, 1, 1, 1), (1, 0, 1, 1, 1, 1), (1, 1, 1, 1, 0, 1), (1, 1, 1, 1, 65, 1),
+                (1, 1, 1, 1, 1, 7)):
+        assert ws(*bad) == 0
+
+
+FAKE = ctypes.c_void_p(0x10000)       # aligned, never dereferenced: validation fails first
+MIS = ctypes.c_void_p(0x10002)        # misaligned
+
+
+def _search(L, op, **kw):
+    a = dict(X=FAKE, W=FAKE, dtype=L.AWQ_BF16, T=256, N=256, K=256, vec=FAKE,
+             grid=[0.25, 0.5, 1.0], qc=L.QConfig(4, 128, 1), out=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    lib = L.lib()
+    grid = L.float_array(a["grid"])
+    n = kw.get("n", len(a["grid"]))
+    if op == "scale":
+        a_best = ctypes.c_float()
+        mse = (ctypes.c_double * 64)()
+        return lib.awq_search_scale(a["X"], a["W"], a["dtype"], a["T"], a["N"], a["K"], a["vec"],
+                                    grid, n, a["qc"], a["out"], ctypes.byref(a_best), mse, None,
+                                    a["ws"], a["ws_bytes"], None)
+    mc = ctypes.c_double()
+    return lib.awq_search_clip(a["X"], a["W"], a["dtype"], a["T"], a["N"], a["K"], a["vec"], grid,
+                               n, a["qc"], a["out"], ctypes.byref(mc), None, a["ws"],
+                               a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), -1), (dict(W=None), -1), (dict(vec=None), -1), (dict(out=None), -1),
+    (dict(T=0), -1), (dict(N=-3), -1), (dict(K=200), -1), (dict(K=0), -1),
+    (dict(dtype=7), -1), (dict(dtype=2), -2),
+    (dict(qc=None), -2),
+    (dict(grid=[0.5, 1.5]), -1), (dict(grid=[-0.1]), -1), (dict(grid=[float("nan")]), -1),
+    (dict(grid=[0.5] * 65), -1), (dict(grid=[]), -1),
+    (dict(X=MIS), -1), (dict(W=MIS), -1),
+    (dict(ws=None), -3), (dict(ws_bytes=1000), -3), (dict(ws=MIS), -3),
+])
+@pytest.mark.parametrize("op", ["scale", "clip"])
+def test_search_rejects(L, kw, status, op):
+    if kw.get("qc", 0) is None:
+        kw = dict(kw, qc=L.QConfig(4, 64, 1))
+    assert _search(L, op, **kw) == status
+    assert L.last_error()
+
+
+@pytest.mark.parametrize("qc,status", [((5, 128, 1), -2), ((2, 128, 1), -2), ((4, 32, 1), -2),
+                                       ((4, 128, 2), -1)])
+def test_search_rejects_qconfig(L, qc, status):
+    assert _search(L, "scale", qc=L.QConfig(*qc)) == status
+
+
+def test_clip_grid_excludes_zero(L):
+    assert _search(L, "clip", grid=[0.0, 1.0]) == -1
+    assert "out of range" in L.last_error()
+
+
+def test_stats_rejects(L):
+    lib = L.lib()
+    f = lib.awq_act_stats
+    assert f(None, 1, 16, 64, FAKE, FAKE, 1 << 30, None) == -1
+    assert f(FAKE, 1, 0, 64, FAKE, FAKE, 1 << 30, None) == -1
+    assert f(FAKE, 1, 16, 60, FAKE, FAKE, 1 << 30, None) == -1     # K not a multiple of 8
+    assert f(FAKE, 0, 16, 62, FAKE, FAKE, 1 << 30, None) == -1     # f32: multiple of 4
+    assert f(MIS, 1, 16, 64, FAKE, FAKE, 1 << 30, None) == -1
+    assert f(FAKE, 1, 16, 64, FAKE, FAKE, 8, None) == -3
+    assert f(FAKE, 9, 16, 64, FAKE, FAKE, 1 << 30, None) == -1
+
+
+def test_scale_table_rejects(L):
+    lib = L.lib()
+    assert lib.awq_scale_table(FAKE, 16, L.float_array([0.5, 2.0]), 2, FAKE, None) == -1
+    assert lib.awq_scale_table(FAKE, 0, L.float_array([0.5]), 1, FAKE, None) == -1
+    assert lib.awq_scale_table(None, 16, L.float_array([0.5]), 1, FAKE, None) == -1
+
+
+def test_pack_rejects(L):
+    lib = L.lib()
+    f = lib.awq_quantize_pack
+    qc = L.QConfig(4, 128, 1)
+    args = lambda **k: [k.get("W", FAKE), k.get("dt", 1), k.get("N", 64), k.get("K", 256),
+                        FAKE, None, k.get("qc", qc), FAKE, FAKE, FAKE, k.get("ws", FAKE),
+                        k.get("wsb", 4096), None]
+    assert f(*args(N=12)) == -1                     # N % 8
+    assert f(*args(K=200)) == -1                    # K % 128
+    assert f(*args(qc=L.QConfig(3, 128, 1))) == -2  # pack is 4-bit only
+    assert f(*args(W=None)) == -1
+    assert f(*args(W=MIS)) == -1
+    assert f(*args(wsb=0)) == -3
+    assert f(*args(dt=5)) == -1
+
+
+def test_profile_read_rejects_bad_kind(L):
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    assert L.lib().awq_profile_read(99, ctypes.byref(ms), ctypes.byref(n)) == -1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, L):
+    from post_weight_quantization_26_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libawq_mi355x.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()
+
+
+def test_autoawq_defaults():
+    import json
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "quant_config_autoawq.json")))
+    src = open(os.path.join(ROOT, "post_weight_quantization_26_amd", "api.py")).read()
+    assert f"DEFAULT_BITS = {gold['w_bit']}" in src
+    assert f"DEFAULT_GROUP = {gold['q_group_size']}" in src
+    assert f"DEFAULT_ZERO_POINT = {gold['zero_point']}" in src
