@@ -4,23 +4,34 @@
 //
 // E stacks the candidates' error weights [n_cand·N, K], so one launch covers
 // the whole grid and every X tile is reused across all candidates ("05 —
-// AWQ", section 4: for each α, scale, quantise and measure the output MSE;
-// the product X·E_cᵀ is Y_c - Y). No output tile is ever written: the
-// epilogue squares the fp32 accumulators and sums them per output column.
+// AWQ: Activation-Aware Weight Scaling", section 4: for each α, scale,
+// quantise and measure the output MSE; the product X·E_cᵀ is Y_c - Y). No
+// output tile is ever written: the epilogue squares the fp32 accumulators and
+// sums them per output column.
 //
-// bf16 path (gfx950 MFMA): 256x256 block tile, BK = 64, four wavefronts in a
-// 2x2 arrangement, each owning a 128x128 sub-tile held as 4x4
-// v_mfma_f32_32x32x16_bf16 accumulators (256 AGPRs). Both operands are
-// K-contiguous, so one 16-byte LDS read per lane feeds an MFMA operand.
-// Tiles are double-buffered in LDS with an XOR swizzle on 16-byte chunks
-// (conflict-free ds_read_b128 for the 32 rows of a fragment). Workgroups are
-// mapped so each XCD works on 4 token tiles x 8 candidate tiles at a time
-// while all XCDs share the same 8 candidate tiles (one HBM read of each E
-// panel per group of 32 token tiles, X panels reused from the last-level
-// cache).
+// bf16 path (gfx950 MFMA):
+//  * 256x256 block tile, four wavefronts (one per SIMD) in a 2x2 arrangement,
+//    each owning 128x128 outputs as 4x4 v_mfma_f32_32x32x16_bf16 accumulators
+//    (256 AGPRs).
+//  * K advances in 32-wide k-tiles through a 4-stage LDS ring (4 x 32 KiB).
+//    Tiles are copied global -> LDS by buffer_load_dwordx4 ... lds (no
+//    staging registers), three k-tiles ahead of the MFMAs. Loads go through a
+//    buffer resource per tile, so rows past the end of X or E read as zero.
+//  * One k-tile per barrier-delimited region; inside it the MFMAs of the
+//    previous k-step run while this k-tile's fragments are read and the DMA
+//    for k-tile kt+3 is issued, one memory instruction per MFMA slot.
+//  * LDS rows are 64 bytes (4 chunks of 16 B) with the chunk index XORed by
+//    (row >> 2) & 3: gfx950 serves ds_read_b128 sixteen lanes at a time over
+//    64 banks, and this swizzle keeps both the fragment reads and the DMA
+//    writes free of bank conflicts.
+//  * Each LDS stage is its own __shared__ array and the k-loop is unrolled
+//    over the 4 stages, so the compiler can tell the stage being read from the
+//    stages the DMA writes and does not serialise LDS reads behind the DMA.
+//  * Workgroups are mapped so each XCD runs 4 token tiles x 8 candidate tiles
+//    at a time while all XCDs share the same 8 candidate tiles (one E panel
+//    fetch per group of 32 token tiles; X panels stay in the last-level cache).
 //
-// fp32 path: a plain LDS-tiled FMA kernel (64x64 tiles), used for float32
-// layers, where exact-ish float32 products are wanted and the work is small.
+// fp32 path: a plain LDS-tiled FMA kernel (64x64 tiles) for float32 layers.
 #include "device_common.h"
 
 namespace awq {
@@ -29,13 +40,49 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
+#define AWQ_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 64;
+constexpr int BK = 32;       // k per stage / region
 constexpr int NT = 256;
-constexpr int CHUNKS = BK / 8;  // 16-byte chunks per tile row
+constexpr int CH = BK / 8;   // 16-byte chunks per tile row per stage
+constexpr int STAGE = 256 * CH;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * CHUNKS + (chunk ^ (row & 7)); }
+__shared__ uint4 sA0[STAGE], sA1[STAGE], sA2[STAGE], sA3[STAGE];
+__shared__ uint4 sB0[STAGE], sB1[STAGE], sB2[STAGE], sB3[STAGE];
+
+template <int S>
+__device__ __forceinline__ uint4* stage_a() {
+  return S == 0 ? sA0 : S == 1 ? sA1 : S == 2 ? sA2 : sA3;
+}
+template <int S>
+__device__ __forceinline__ uint4* stage_b() {
+  return S == 0 ? sB0 : S == 1 ? sB1 : S == 2 ? sB2 : sB3;
+}
+
+// 16-byte slot of (row, chunk) inside a stage.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * CH + (chunk ^ ((row >> 2) & 3));
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int wait_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int kWaitLgkm0 = 0xF | (3 << 14) | (0x7 << 4);
+
+// Masks for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100;
+
+// Workgroup barrier that neither the compiler nor the scheduler may move a
+// memory operation or any instruction across. Unlike __syncthreads() it adds
+// no vmcnt(0), so DMA copies stay in flight across it.
+__device__ __forceinline__ void region_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // Block id -> (token tile, candidate-column tile). Returns false for padding blocks.
 __device__ __forceinline__ bool tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -53,57 +100,127 @@ __device__ __forceinline__ bool tile_of(int bid, int tiles_m, int tiles_n, int& 
   return tm < tiles_m && tn < tiles_n;
 }
 
+// Buffer resource over `rows` rows of K bf16 starting at `base` (dword 3 =
+// raw 32-bit data format, the gfx9-family default). Offsets past the end
+// read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int64_t rows,
+                                                           int64_t K) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0,
+                                           int(rows * K * 2), 0x00020000);
+}
+
+struct GemmCtx {
+  __amdgpu_buffer_rsrc_t rsA, rsB;
+  int voff[4];  // byte offset (k-tile 0) of the chunk this lane copies in DMA instruction j
+  int wave, KT, oob;
+  int rdA[2], rdB[2];  // fragment slot for k-step 0/1 (sub-tile i adds 128 i)
+};
+
+// Copy k-tile kt into stage S: 4 instructions per operand per wave, each
+// filling 1 KiB (16 rows) of the stage; lane l fills slot base + l. Past the
+// last k-tile the offset leaves the resource, so the copy writes zeros
+// without touching memory and the vmcnt bookkeeping stays uniform.
+template <int S>
+__device__ __forceinline__ void dma_tile(const GemmCtx& c, int kt) {
+  const int kofs = kt < c.KT ? kt * (BK * 2) : c.oob;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsA, AWQ_LDS(stage_a<S>() + (c.wave * 4 + j) * 64),
+                                             16, c.voff[j] + kofs, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsB, AWQ_LDS(stage_b<S>() + (c.wave * 4 + j) * 64),
+                                             16, c.voff[j] + kofs, 0, 0, 0);
+  }
+}
+
+template <int S>
+__device__ __forceinline__ void read_frags(const GemmCtx& c, int ks, bf16x8_t (&fa)[4],
+                                           bf16x8_t (&fb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    fa[i] = __builtin_bit_cast(bf16x8_t, stage_a<S>()[c.rdA[ks] + i * 128]);
+    fb[i] = __builtin_bit_cast(bf16x8_t, stage_b<S>()[c.rdB[ks] + i * 128]);
+  }
+}
+
+__device__ __forceinline__ void mfma_4x4(floatx16 (&acc)[4][4], const bf16x8_t (&fa)[4],
+                                         const bf16x8_t (&fb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+}
+
+// Region kt (stage S = kt % 4), between two barriers:
+//   DMA of k-tile kt+3 into stage (kt+3) % 4 (last read before this region),
+//   MFMAs of (kt-1, k-step 1) from F1 while F0 <- (kt, k-step 0) is read,
+//   MFMAs of (kt, k-step 0) from F0 while F1 <- (kt, k-step 1) is read,
+//   then wait for this wave's LDS reads and for its DMA of k-tile kt+1
+//   (two k-tiles = 16 copies may stay in flight) and meet at the barrier.
+template <int S, bool PREV>
+__device__ __forceinline__ void region(const GemmCtx& c, int kt, floatx16 (&acc)[4][4],
+                                       bf16x8_t (&f0a)[4], bf16x8_t (&f0b)[4],
+                                       bf16x8_t (&f1a)[4], bf16x8_t (&f1b)[4]) {
+  dma_tile<(S + 3) & 3>(c, kt + 3);
+  if (PREV) mfma_4x4(acc, f1a, f1b);
+  read_frags<S>(c, 0, f0a, f0b);
+  mfma_4x4(acc, f0a, f0b);
+  read_frags<S>(c, 1, f1a, f1b);
+  if (PREV) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSgMfma, 8, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_waitcnt(wait_vm(16));
+  region_barrier();
+}
+
+// K must be a multiple of 128 (so the number of 32-wide k-tiles is a multiple of 4).
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void search_gemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ E,
                              int64_t M, int64_t Nc, int64_t K, int tiles_m, int tiles_n,
                              float* __restrict__ partials) {
-  extern __shared__ uint4 smem[];
-  // LDS: A buffers [2][BM*CHUNKS] then B buffers [2][BN*CHUNKS].
-  uint4* const As0 = smem;
-  uint4* const Bs0 = smem + 2 * BM * CHUNKS;
-
   int tm, tn;
   if (!tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  // Global -> register staging: thread loads chunk (tid & 7) of rows tid/8 + 32 i.
-  const int ld_chunk = tid & 7;
-  const int ld_row = tid >> 3;
-  const uint4* gA[8];
-  const uint4* gB[8];
-  bool okA[8], okB[8];
+  const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
+  const int64_t rows_b = Nc - n0 < BN ? Nc - n0 : BN;
+  GemmCtx c;
+  c.rsA = tile_rsrc(X + m0 * K, rows_a, K);
+  c.rsB = tile_rsrc(E + n0 * K, rows_b, K);
+  const int tid = threadIdx.x, lane = tid & 63;
+  c.wave = tid >> 6;
+  c.KT = int(K / BK);
+  c.oob = BM * int(K) * 2;  // beyond every row of the tile
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t ra = m0 + ld_row + 32 * i, rb = n0 + ld_row + 32 * i;
-    okA[i] = ra < M;
-    okB[i] = rb < Nc;
-    gA[i] = reinterpret_cast<const uint4*>(X + (okA[i] ? ra : 0) * K) + ld_chunk;
-    gB[i] = reinterpret_cast<const uint4*>(E + (okB[i] ? rb : 0) * K) + ld_chunk;
+  for (int j = 0; j < 4; ++j) {
+    // Slot p of a stage holds chunk (p & 3) ^ ((row >> 2) & 3) of row p >> 2.
+    const int p = (c.wave * 4 + j) * 64 + lane;
+    const int row = p >> 2;
+    const int chunk = (p & 3) ^ ((row >> 2) & 3);
+    c.voff[j] = (row * int(K) + chunk * 8) * 2;
   }
-  const uint4 zero4 = make_uint4(0, 0, 0, 0);
-  uint4 ra[8], rb[8];
-
-  auto load_tile = [&](int64_t kt) {
-    const int64_t off = kt * CHUNKS;  // in uint4 units
+  const int wm = c.wave >> 1, wn = c.wave & 1;
+  const int fr = lane & 31, fh = lane >> 5;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ra[i] = okA[i] ? gA[i][off] : zero4;
-      rb[i] = okB[i] ? gB[i][off] : zero4;
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = ld_row + 32 * i;
-      As0[buf * BM * CHUNKS + swz(row, ld_chunk)] = ra[i];
-      Bs0[buf * BN * CHUNKS + swz(row, ld_chunk)] = rb[i];
-    }
-  };
-
+  for (int ks = 0; ks < 2; ++ks) {
+    c.rdA[ks] = swz(wm * 128 + fr, 2 * ks + fh);
+    c.rdB[ks] = swz(wn * 128 + fr, 2 * ks + fh);
+  }
   floatx16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -112,40 +229,30 @@ void search_gemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __r
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int64_t KT = K / BK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  const int frag_row = lane & 31;
-  const int frag_half = lane >> 5;
-  for (int64_t kt = 0; kt < KT; ++kt) {
-    const int buf = int(kt & 1);
-    if (kt + 1 < KT) load_tile(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int ch = 2 * ks + frag_half;
-      bf16x8_t a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = __builtin_bit_cast(bf16x8_t,
-                                  As0[buf * BM * CHUNKS + swz(wm * 128 + i * 32 + frag_row, ch)]);
-        b[i] = __builtin_bit_cast(bf16x8_t,
-                                  Bs0[buf * BN * CHUNKS + swz(wn * 128 + i * 32 + frag_row, ch)]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < KT) store_tile(buf ^ 1);
-    __syncthreads();
+  dma_tile<0>(c, 0);
+  dma_tile<1>(c, 1);
+  dma_tile<2>(c, 2);
+  __builtin_amdgcn_s_waitcnt(wait_vm(16));  // k-tile 0 landed; 1 and 2 in flight
+  region_barrier();
+  bf16x8_t f0a[4], f0b[4], f1a[4], f1b[4];
+  region<0, false>(c, 0, acc, f0a, f0b, f1a, f1b);
+  int kt = 1;
+  for (; kt + 4 < c.KT; kt += 4) {
+    region<1, true>(c, kt, acc, f0a, f0b, f1a, f1b);
+    region<2, true>(c, kt + 1, acc, f0a, f0b, f1a, f1b);
+    region<3, true>(c, kt + 2, acc, f0a, f0b, f1a, f1b);
+    region<0, true>(c, kt + 3, acc, f0a, f0b, f1a, f1b);
   }
+  region<1, true>(c, kt, acc, f0a, f0b, f1a, f1b);
+  region<2, true>(c, kt + 1, acc, f0a, f0b, f1a, f1b);
+  region<3, true>(c, kt + 2, acc, f0a, f0b, f1a, f1b);
+  mfma_4x4(acc, f1a, f1b);
 
   // Epilogue: each lane's 16 accumulators of sub-tile (i, j) all lie in output
   // column j*32 + lane%32 of the wave's range; lanes l and l^32 share it.
-  float* red = reinterpret_cast<float*>(smem);  // [2][BN]
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(sA0);  // [2][BN]
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float s = 0.f;
@@ -157,8 +264,8 @@ void search_gemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __r
     if (lane < 32) red[wm * BN + wn * 128 + j * 32 + lane] = s;
   }
   __syncthreads();
-  const int64_t c = n0 + tid;
-  if (c < Nc) partials[int64_t(tm) * Nc + c] = red[tid] + red[BN + tid];
+  const int64_t col = n0 + tid;
+  if (col < Nc) partials[int64_t(tm) * Nc + col] = red[tid] + red[BN + tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -225,17 +332,14 @@ __global__ __launch_bounds__(256) void search_gemm_f32_kernel(const float* __res
 hipError_t launch_search_gemm(const void* X, int dtype, const void* E, int64_t M, int64_t Nc,
                               int64_t K, float* partials, hipStream_t st) {
   if (dtype == 1) {
+    if (K % 128) return hipErrorInvalidValue;
     const int tiles_m = int((M + BM - 1) / BM), tiles_n = int((Nc + BN - 1) / BN);
     int64_t blocks;
     if (tiles_m >= 32)
       blocks = int64_t((tiles_m + 31) / 32) * 32 * (int64_t((tiles_n + 7) / 8) * 8);
     else
       blocks = int64_t(tiles_m) * tiles_n;
-    const size_t lds = size_t(2) * (BM + BN) * CHUNKS * sizeof(uint4);  // 128 KiB
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(search_gemm_bf16_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    if (e != hipSuccess) return e;
-    search_gemm_bf16_kernel<<<unsigned(blocks), NT, lds, st>>>(
+    search_gemm_bf16_kernel<<<unsigned(blocks), NT, 0, st>>>(
         static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(E), M, Nc, K, tiles_m,
         tiles_n, partials);
   } else {
