@@ -13,10 +13,12 @@ namespace awq {
 hipError_t launch_stats(const void* X, int dtype, int64_t T, int64_t K, int64_t chunks,
                         double* partial, float* abar, hipStream_t st);
 hipError_t launch_scale_table(const float* abar, int64_t K, const float* alphas_host, int n,
-                              float* s_table, hipStream_t st);
+                              float* s_table, float* inv_table, hipStream_t st);
+hipError_t launch_reciprocal(const float* s, int64_t n, float* s_copy, float* inv,
+                             hipStream_t st);
 hipError_t launch_transform(const void* W, int dtype, int64_t N, int64_t K, const float* s_rows,
-                            int64_t s_stride, const float* ratios_host, int nc, int bits,
-                            int zero_point, void* E, hipStream_t st);
+                            const float* inv_rows, int64_t s_stride, const float* ratios_host,
+                            int nc, int bits, int zero_point, void* E, hipStream_t st);
 hipError_t launch_search_gemm(const void* X, int dtype, const void* E, int64_t M, int64_t Nc,
                               int64_t K, float* partials, hipStream_t st);
 hipError_t launch_reduce_rows(const float* partials, int64_t MT, int64_t Nc, double* row_sums,
@@ -103,15 +105,16 @@ T* at(void* ws, size_t off) {
 
 // Runs transform -> GEMM -> row reduction for candidates [c0, c0+cb).
 awq_status run_batch(const void* X, const void* W, awq_dtype d, int64_t T, int64_t N, int64_t K,
-                     const float* s_rows, int64_t s_stride, const float* ratios_host, int cb,
+                     const float* s_rows, const float* inv_rows, int64_t s_stride,
+                     const float* ratios_host, int cb,
                      awq_qconfig qc, const SearchLayout& L, void* ws, double* row_sums_out,
                      hipStream_t st) {
   void* E = at<void>(ws, L.E);
   float* partials = at<float>(ws, L.partials);
   AWQ_HIP(timed(AWQ_K_TRANSFORM, st,
                 [&] {
-                  return launch_transform(W, dt(d), N, K, s_rows, s_stride, ratios_host, cb,
-                                          qc.w_bit, qc.zero_point, E, st);
+                  return launch_transform(W, dt(d), N, K, s_rows, inv_rows, s_stride, ratios_host,
+                                          cb, qc.w_bit, qc.zero_point, E, st);
                 }),
           "transform");
   AWQ_HIP(timed(AWQ_K_GEMM, st,
@@ -149,7 +152,7 @@ extern "C" awq_status awq_scale_table(const float* abar, int64_t K, const float*
   if (s != AWQ_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   AWQ_HIP(timed(AWQ_K_SCALE, st,
-                [&] { return launch_scale_table(abar, K, alphas, n_alpha, s_table, st); }),
+                [&] { return launch_scale_table(abar, K, alphas, n_alpha, s_table, nullptr, st); }),
           "scale_table");
   return AWQ_OK;
 }
@@ -167,16 +170,19 @@ extern "C" awq_status awq_search_scale(const void* X, const void* W, awq_dtype d
   hipStream_t st = static_cast<hipStream_t>(stream);
   const SearchLayout L = search_layout(AWQ_OP_SEARCH_SCALE, T, N, K, n_alpha, nb, dtype);
   float* s_table = at<float>(ws, L.s_table);
+  float* inv_table = at<float>(ws, L.inv);
   double* rs = at<double>(ws, L.row_sums);
   double* mse_dev = at<double>(ws, L.mse);
 
   AWQ_HIP(timed(AWQ_K_SCALE, st,
-                [&] { return launch_scale_table(abar, K, alphas, n_alpha, s_table, st); }),
+                [&] {
+                  return launch_scale_table(abar, K, alphas, n_alpha, s_table, inv_table, st);
+                }),
           "scale_table");
   for (int c0 = 0; c0 < n_alpha; c0 += nb) {
     const int cb = n_alpha - c0 < nb ? n_alpha - c0 : nb;
-    s = run_batch(X, W, dtype, T, N, K, s_table + int64_t(c0) * K, K, nullptr, cb, qc, L, ws,
-                  rs + int64_t(c0) * N, st);
+    s = run_batch(X, W, dtype, T, N, K, s_table + int64_t(c0) * K, inv_table + int64_t(c0) * K,
+                  K, nullptr, cb, qc, L, ws, rs + int64_t(c0) * N, st);
     if (s != AWQ_OK) return s;
   }
   AWQ_HIP(timed(AWQ_K_REDUCE, st,
@@ -214,10 +220,14 @@ extern "C" awq_status awq_search_clip(const void* X, const void* W, awq_dtype dt
   double* rs = at<double>(ws, L.row_sums);
   double* best = at<double>(ws, L.best);
   double* mc = at<double>(ws, L.scalar);
+  float* inv = at<float>(ws, L.inv);
+  float* s_copy = at<float>(ws, L.s_table);
+  AWQ_HIP(timed(AWQ_K_SCALE, st, [&] { return launch_reciprocal(s, K, s_copy, inv, st); }),
+          "reciprocal");
   for (int c0 = 0; c0 < n_ratio; c0 += nb) {
     const int cb = n_ratio - c0 < nb ? n_ratio - c0 : nb;
-    st_ = run_batch(X, W, dtype, T, N, K, s, 0, ratios + c0, cb, qc, L, ws, rs + int64_t(c0) * N,
-                    st);
+    st_ = run_batch(X, W, dtype, T, N, K, s_copy, inv, 0, ratios + c0, cb, qc, L, ws,
+                    rs + int64_t(c0) * N, st);
     if (st_ != AWQ_OK) return st_;
   }
   AWQ_HIP(timed(AWQ_K_REDUCE, st,

@@ -23,13 +23,14 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t dtype_bytes(awq_dtype d) { return d == AWQ_F32 ? 4 : 2; }
 
 // Number of token chunks the stats kernel splits T into (one float64 partial
-// row per chunk); chosen so the launch has ~2048 workgroups.
+// row per chunk); chosen so the launch has ~1024 workgroups.
 int64_t stats_chunks(int64_t T, int64_t K, awq_dtype d);
 
 // Byte offsets of the regions of a search workspace for a batch of `nb`
 // candidates out of `n_grid`.
 struct SearchLayout {
-  size_t s_table;   // [n_grid, K] f32 (scale search only)
+  size_t s_table;   // [n_grid, K] f32 scale table (clip search: aligned copy of s, [K])
+  size_t inv;       // [n_grid, K] f32 reciprocal scales (clip search: [K])
   size_t E;         // [nb, N, K] candidate error weights (bf16 or f32)
   size_t partials;  // [MT, nb*N] f32 per-tile column sums of squares
   size_t row_sums;  // [n_grid, N] f64

@@ -11,13 +11,15 @@ namespace awq {
 hipError_t launch_stats(const void* X, int dtype, int64_t T, int64_t K, int64_t chunks,
                         double* partial, float* abar, hipStream_t st);
 hipError_t launch_scale_table(const float* abar, int64_t K, const float* alphas_host, int n,
-                              float* s_table, hipStream_t st);
+                              float* s_table, float* inv_table, hipStream_t st);
+hipError_t launch_reciprocal(const float* s, int64_t n, float* s_copy, float* inv,
+                             hipStream_t st);
 // Candidate error weights E[c] = fold(dequant(quant(W·diag(s_c), r_c))) - W for
 // c in [0, nc): scale rows `s_rows` (s_stride 0 = one shared row) and clip
 // ratios `ratios_host` (NULL = all 1).
 hipError_t launch_transform(const void* W, int dtype, int64_t N, int64_t K, const float* s_rows,
-                            int64_t s_stride, const float* ratios_host, int nc, int bits,
-                            int zero_point, void* E, hipStream_t st);
+                            const float* inv_rows, int64_t s_stride, const float* ratios_host,
+                            int nc, int bits, int zero_point, void* E, hipStream_t st);
 // partials[mt][c] = Σ_{t in tile mt} (X·Eᵀ)[t][c]² for c in [0, Nc).
 hipError_t launch_search_gemm(const void* X, int dtype, const void* E, int64_t M, int64_t Nc,
                               int64_t K, float* partials, hipStream_t st);

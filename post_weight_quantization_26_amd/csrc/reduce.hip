@@ -15,14 +15,23 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// 64 columns per workgroup, 4 lanes per column: lane group g adds token
+// tiles g, g+4, ... in order (8 loads in flight), then the four sums are
+// added in a fixed order.
 __global__ __launch_bounds__(kThreads) void reduce_rows_kernel(const float* __restrict__ partials,
                                                                int64_t MT, int64_t Nc,
                                                                double* __restrict__ row_sums) {
-  const int64_t c = int64_t(blockIdx.x) * kThreads + threadIdx.x;
-  if (c >= Nc) return;
+  __shared__ double red[4][64];
+  const int cl = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int64_t c = int64_t(blockIdx.x) * 64 + cl;
   double s = 0.0;
-  for (int64_t m = 0; m < MT; ++m) s += double(partials[m * Nc + c]);
-  row_sums[c] = s;
+  if (c < Nc) {
+#pragma unroll 8
+    for (int64_t m = g; m < MT; m += 4) s += double(partials[m * Nc + c]);
+  }
+  red[g][cl] = s;
+  __syncthreads();
+  if (g == 0 && c < Nc) row_sums[c] = ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
 }
 
 // Fixed-shape block sum: thread i adds elements i, i+256, ...; then a tree.
@@ -70,8 +79,7 @@ __global__ __launch_bounds__(kThreads) void clip_argmin_kernel(const double* __r
 
 hipError_t launch_reduce_rows(const float* partials, int64_t MT, int64_t Nc, double* row_sums,
                               hipStream_t st) {
-  reduce_rows_kernel<<<unsigned((Nc + kThreads - 1) / kThreads), kThreads, 0, st>>>(partials, MT,
-                                                                                    Nc, row_sums);
+  reduce_rows_kernel<<<unsigned((Nc + 63) / 64), kThreads, 0, st>>>(partials, MT, Nc, row_sums);
   return hipGetLastError();
 }
 

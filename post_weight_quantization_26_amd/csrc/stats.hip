@@ -111,13 +111,22 @@ __global__ __launch_bounds__(kColThreads* kRowLanes) void stats_partial_kernel(
   }
 }
 
-__global__ void stats_finalize_kernel(const double* __restrict__ partial, int64_t chunks,
-                                      int64_t T, int64_t K, float* __restrict__ abar) {
-  const int64_t j = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (j >= K) return;
+// Finalise: 64 columns per workgroup, 4 lanes per column each adding every
+// 4th chunk in order, then the 4 sums in a fixed order; one rounding to f32.
+__global__ __launch_bounds__(256) void stats_finalize_kernel(const double* __restrict__ partial,
+                                                             int64_t chunks, int64_t T, int64_t K,
+                                                             float* __restrict__ abar) {
+  __shared__ double red[4][64];
+  const int cl = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int64_t j = int64_t(blockIdx.x) * 64 + cl;
   double s = 0.0;
-  for (int64_t c = 0; c < chunks; ++c) s += partial[c * K + j];
-  abar[j] = float(s / double(T));
+  if (j < K) {
+#pragma unroll 4
+    for (int64_t c = g; c < chunks; c += 4) s += partial[c * K + j];
+  }
+  red[g][cl] = s;
+  __syncthreads();
+  if (g == 0 && j < K) abar[j] = float((((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl]) / double(T));
 }
 
 }  // namespace
@@ -138,7 +147,7 @@ hipError_t launch_stats(const void* X, int dtype, int64_t T, int64_t K, int64_t 
     stats_partial_kernel<2><<<grid, block, 0, st>>>(x, T, K, rows_per_chunk, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  stats_finalize_kernel<<<unsigned((K + 255) / 256), 256, 0, st>>>(partial, chunks, T, K, abar);
+  stats_finalize_kernel<<<unsigned((K + 63) / 64), 256, 0, st>>>(partial, chunks, T, K, abar);
   return hipGetLastError();
 }
 

@@ -10,9 +10,15 @@
 // One lane owns 8 consecutive input channels of one row; the 16 lanes of a
 // 128-wide group find its min/max with xor-shuffles, so every lane holds the
 // group's step and zero point. W is read once per batch and each candidate's
-// E row segment is written with one 16-byte store per lane (bf16) — the
-// kernel is bound by the E write stream. Codes use exact IEEE float32
-// division and rint, as in the packed output.
+// E row segment is written with one 16-byte store per lane.
+//
+// Arithmetic per element: w' = w·s; the quotient w'/step comes from the
+// group's IEEE reciprocal r = 1/step and one FMA correction step
+// (q0 = w'·r, q = q0 + (w' - q0·step)·r), which reproduces the correctly
+// rounded quotient except in vanishingly rare cases at a rounding midpoint;
+// only the error energy of the search depends on these codes (the packed
+// output uses exact IEEE division). The fold multiplies by a precomputed
+// table 1/s instead of dividing by s.
 #include "device_common.h"
 
 namespace awq {
@@ -23,13 +29,17 @@ constexpr int kThreads = 256;
 template <int DT>
 __device__ __forceinline__ void store8(void* E, int64_t idx, const float (&e)[8]);
 
+// bf16 output: gfx950 converts float32 to bf16 in hardware with round-to-nearest-even.
 template <>
 __device__ __forceinline__ void store8<1>(void* E, int64_t idx, const float (&e)[8]) {
+  uint16_t h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(e[i]));
   uint4 q;
-  q.x = uint32_t(f32_to_bf16_rne(e[0])) | (uint32_t(f32_to_bf16_rne(e[1])) << 16);
-  q.y = uint32_t(f32_to_bf16_rne(e[2])) | (uint32_t(f32_to_bf16_rne(e[3])) << 16);
-  q.z = uint32_t(f32_to_bf16_rne(e[4])) | (uint32_t(f32_to_bf16_rne(e[5])) << 16);
-  q.w = uint32_t(f32_to_bf16_rne(e[6])) | (uint32_t(f32_to_bf16_rne(e[7])) << 16);
+  q.x = uint32_t(h[0]) | (uint32_t(h[1]) << 16);
+  q.y = uint32_t(h[2]) | (uint32_t(h[3]) << 16);
+  q.z = uint32_t(h[4]) | (uint32_t(h[5]) << 16);
+  q.w = uint32_t(h[6]) | (uint32_t(h[7]) << 16);
   *reinterpret_cast<uint4*>(static_cast<uint16_t*>(E) + idx) = q;
 }
 
@@ -44,8 +54,8 @@ __device__ __forceinline__ void store8<0>(void* E, int64_t idx, const float (&e)
 template <int DT>
 __global__ __launch_bounds__(kThreads) void transform_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s_rows,
-    int64_t s_stride, GridArgs ratios, int has_ratio, int nc, int bits, int zero_point,
-    void* __restrict__ E) {
+    const float* __restrict__ inv_rows, int64_t s_stride, GridArgs ratios, int has_ratio, int nc,
+    int bits, int zero_point, void* __restrict__ E) {
 #pragma clang fp contract(off)
   const int64_t NK = N * K;
   const int64_t e0 = (int64_t(blockIdx.x) * kThreads + threadIdx.x) * 8;  // flat n*K + k
@@ -62,12 +72,16 @@ __global__ __launch_bounds__(kThreads) void transform_kernel(
   }
 
   for (int c = 0; c < nc; ++c) {
-    const float* s = s_rows + int64_t(c) * s_stride + k;
-    float sv[8], wp[8];
+    // 16-byte aligned rows (k is a multiple of 8); idle lanes read column 0.
+    const float4* s4 = reinterpret_cast<const float4*>(s_rows + int64_t(c) * s_stride + k);
+    const float4* i4 = reinterpret_cast<const float4*>(inv_rows + int64_t(c) * s_stride + k);
+    const float4 sa = s4[0], sb = s4[1], ia = i4[0], ib = i4[1];
+    const float sv[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+    const float iv[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
+    float wp[8];
     float mx = 0.f, mn = 0.f;  // range widened to contain 0
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      sv[i] = active ? s[i] : 1.f;
       wp[i] = w[i] * sv[i];
       mx = fmaxf(mx, wp[i]);
       mn = fminf(mn, wp[i]);
@@ -79,11 +93,14 @@ __global__ __launch_bounds__(kThreads) void transform_kernel(
     }
     const float r = has_ratio ? ratios.v[c] : 1.f;
     const QParams p = group_qparams(mx, mn, r, bits, zero_point);
+    const float rstep = 1.0f / p.step;
     float e[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float q = quant_code(wp[i], p);
-      e[i] = ((q - p.zero) * p.step) / sv[i] - w[i];
+      const float q0 = wp[i] * rstep;
+      const float quo = __builtin_fmaf(__builtin_fmaf(-q0, p.step, wp[i]), rstep, q0);
+      const float q = fminf(fmaxf(__builtin_rintf(quo) + p.zero, 0.f), p.qmax);
+      e[i] = ((q - p.zero) * p.step) * iv[i] - w[i];
     }
     if (active) store8<DT>(E, int64_t(c) * NK + e0, e);
   }
@@ -92,19 +109,19 @@ __global__ __launch_bounds__(kThreads) void transform_kernel(
 }  // namespace
 
 hipError_t launch_transform(const void* W, int dtype, int64_t N, int64_t K, const float* s_rows,
-                            int64_t s_stride, const float* ratios_host, int nc, int bits,
-                            int zero_point, void* E, hipStream_t st) {
+                            const float* inv_rows, int64_t s_stride, const float* ratios_host,
+                            int nc, int bits, int zero_point, void* E, hipStream_t st) {
   GridArgs g{};
   const int has_ratio = ratios_host != nullptr;
   for (int i = 0; i < nc && i < 64; ++i) g.v[i] = has_ratio ? ratios_host[i] : 1.f;
   const int64_t lanes = N * K / 8;
   const unsigned blocks = unsigned((lanes + kThreads - 1) / kThreads);
   if (dtype == 1)
-    transform_kernel<1><<<blocks, kThreads, 0, st>>>(W, N, K, s_rows, s_stride, g, has_ratio, nc,
-                                                     bits, zero_point, E);
+    transform_kernel<1><<<blocks, kThreads, 0, st>>>(W, N, K, s_rows, inv_rows, s_stride, g,
+                                                     has_ratio, nc, bits, zero_point, E);
   else
-    transform_kernel<0><<<blocks, kThreads, 0, st>>>(W, N, K, s_rows, s_stride, g, has_ratio, nc,
-                                                     bits, zero_point, E);
+    transform_kernel<0><<<blocks, kThreads, 0, st>>>(W, N, K, s_rows, inv_rows, s_stride, g,
+                                                     has_ratio, nc, bits, zero_point, E);
   return hipGetLastError();
 }
 

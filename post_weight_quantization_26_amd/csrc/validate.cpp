@@ -31,7 +31,7 @@ static constexpr int64_t kMaxDim = int64_t(1) << 31;
 int64_t stats_chunks(int64_t T, int64_t K, awq_dtype d) {
   const int64_t vec = 16 / int64_t(dtype_bytes(d));
   const int64_t col_blocks = ceil_div(K, 64 * vec);
-  int64_t chunks = ceil_div(2048, col_blocks);
+  int64_t chunks = ceil_div(1024, col_blocks);
   const int64_t max_chunks = ceil_div(T, 64);  // at least 64 rows (16 per row lane) per chunk
   if (chunks > max_chunks) chunks = max_chunks;
   if (chunks < 1) chunks = 1;
@@ -45,7 +45,9 @@ SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_gr
   L.MT = ceil_div(T, bm);
   size_t off = 0;
   L.s_table = off;
-  if (op == AWQ_OP_SEARCH_SCALE) off += align_up(size_t(n_grid) * size_t(K) * 4);
+  off += align_up(size_t(op == AWQ_OP_SEARCH_SCALE ? n_grid : 1) * size_t(K) * 4);
+  L.inv = off;
+  off += align_up(size_t(op == AWQ_OP_SEARCH_SCALE ? n_grid : 1) * size_t(K) * 4);
   L.E = off;
   off += align_up(size_t(nb) * size_t(N) * size_t(K) * dtype_bytes(dtype));
   L.partials = off;

@@ -64,13 +64,15 @@ def assert_alpha_rule(gpu_idx, ref_mse):
 
 
 def model_E(w32, s32, ratio, bits, zp, dtype):
-    """Error weights as the search GEMM consumes them, from the oracle's codes:
-    fl32(fl32(fl32((q - zero)·step) / s) - w), then one RNE rounding to the
-    MFMA operand type (bf16; float32 inputs stay float32)."""
+    """Error weights as the search GEMM consumes them, from the oracle's codes
+    and the kernel's float32 arithmetic: fl32(fl32(fl32((q - zero)·step) ·
+    fl32(1/s)) - w), then one RNE rounding to the MFMA operand type (bf16;
+    float32 inputs stay float32)."""
     q, step, zero = O.quantize(w32, s32, ratio, bits, 128, zp)
     N, K = w32.shape
     d = ((q.reshape(N, K // 128, 128).astype(np.float32) - zero[:, :, None]) * step[:, :, None])
-    e = (d.reshape(N, K) / s32[None, :].astype(np.float32)) - w32
+    inv_s = (np.float32(1.0) / s32.astype(np.float32)).astype(np.float32)
+    e = (d.reshape(N, K) * inv_s[None, :]) - w32
     e = e.astype(np.float32)
     if dtype == "f32":
         return e.astype(np.float64)
