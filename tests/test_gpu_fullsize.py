@@ -56,3 +56,18 @@ def run_config(api, name, variants=None, pack_check=True):
 
 def test_llama7b_attn_4096_full(api):
     run_config(api, "llama7b_attn_4096")
+
+
+def test_llama7b_mlp_up_full(api):
+    # 11008 x 4096, 20 alphas then 20 clip ratios per output channel, then pack
+    run_config(api, "llama7b_mlp_up")
+
+
+def test_llama7b_mlp_down_int3_full(api):
+    # 4096 x 11008, heavy-tailed inputs, INT3 search and clip (no pack at 3 bits)
+    run_config(api, "llama7b_mlp_down_int3")
+
+
+def test_llama70b_mlp_full(api):
+    # 28672 x 8192 over 32768 tokens, asymmetric and symmetric INT4, search + clip + pack
+    run_config(api, "llama70b_mlp")

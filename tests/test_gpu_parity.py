@@ -110,7 +110,7 @@ def compare_rows(gpu_rows, M64, Mm, tol, what):
     worst = (err / tol).max()
     assert worst <= 1.0, f"{what}: GPU vs model exceeds the float32 bound ({worst:.2f}x)"
     gap = (np.abs(Mm - M64) / M64).max()
-    print(f"{what}: |gpu-model|/bound max {worst:.3f}; bf16 operand gap max {gap:.2e}; "
+    print(f"{what}: |gpu-model|/bound max {worst:.2e}; bf16 operand gap max {gap:.2e}; "
           f"|gpu-oracle|/oracle max {(np.abs(gpu_rows - M64) / M64).max():.2e}")
 
 
