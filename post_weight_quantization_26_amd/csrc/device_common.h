@@ -116,9 +116,15 @@ __device__ __forceinline__ QParams group_qparams(float mx, float mn, float ratio
   return p;
 }
 
-__device__ __forceinline__ float quant_code(float wp, const QParams& p) {
-#pragma clang fp contract(off)
-  return fminf(fmaxf(__builtin_rintf(wp / p.step) + p.zero, 0.f), p.qmax);
+// Code of a scaled weight. The quotient w'/step comes from the group's IEEE
+// reciprocal `rstep` = 1/step and one FMA correction step, which gives the
+// correctly rounded quotient up to at most one ulp in rare cases; a code can
+// differ from exact division only when the quotient lies within one ulp of a
+// .5 rounding boundary.
+__device__ __forceinline__ float quant_code(float wp, const QParams& p, float rstep) {
+  const float q0 = wp * rstep;
+  const float quo = __builtin_fmaf(__builtin_fmaf(-q0, p.step, wp), rstep, q0);
+  return fminf(fmaxf(__builtin_rintf(quo) + p.zero, 0.f), p.qmax);
 }
 
 }  // namespace awq

@@ -12,7 +12,8 @@
 // range with xor-shuffles over those 16 lanes, and packs its 8x8 codes into 8
 // words in registers. Words are transposed through LDS so every qweight row
 // segment is written with consecutive 4-byte stores. One pass over W: HBM
-// bound. Codes use exact IEEE float32 division and rint.
+// bound. Codes: IEEE float32 group parameters, quotient from the group's
+// reciprocal with one FMA correction, rint.
 #include "device_common.h"
 
 namespace awq {
@@ -72,8 +73,9 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(
       }
       const float r = (ratio != nullptr && valid) ? ratio[n] : 1.f;
       const QParams p = group_qparams(mx, mn, r, 4, zero_point);
+      const float rstep = 1.0f / p.step;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) wd[i] |= uint32_t(quant_code(wp[i], p)) << (4 * r8);
+      for (int i = 0; i < 8; ++i) wd[i] |= uint32_t(quant_code(wp[i], p, rstep)) << (4 * r8);
       if (c == 0) {
         const _Float16 h = _Float16(p.step);
         const uint16_t hb = __builtin_bit_cast(uint16_t, h);

@@ -12,13 +12,10 @@
 // group's step and zero point. W is read once per batch and each candidate's
 // E row segment is written with one 16-byte store per lane.
 //
-// Arithmetic per element: w' = w·s; the quotient w'/step comes from the
-// group's IEEE reciprocal r = 1/step and one FMA correction step
-// (q0 = w'·r, q = q0 + (w' - q0·step)·r), which reproduces the correctly
-// rounded quotient except in vanishingly rare cases at a rounding midpoint;
-// only the error energy of the search depends on these codes (the packed
-// output uses exact IEEE division). The fold multiplies by a precomputed
-// table 1/s instead of dividing by s.
+// Arithmetic per element: w' = w·s; the code quotient w'/step comes from the
+// group's IEEE reciprocal and one FMA correction (quant_code), as in the
+// packed output. The fold multiplies by a precomputed table 1/s instead of
+// dividing by s.
 #include "device_common.h"
 
 namespace awq {
@@ -97,9 +94,7 @@ __global__ __launch_bounds__(kThreads) void transform_kernel(
     float e[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float q0 = wp[i] * rstep;
-      const float quo = __builtin_fmaf(__builtin_fmaf(-q0, p.step, wp[i]), rstep, q0);
-      const float q = fminf(fmaxf(__builtin_rintf(quo) + p.zero, 0.f), p.qmax);
+      const float q = quant_code(wp[i], p, rstep);
       e[i] = ((q - p.zero) * p.step) * iv[i] - w[i];
     }
     if (active) store8<DT>(E, int64_t(c) * NK + e0, e);

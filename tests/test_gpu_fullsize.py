@@ -13,7 +13,7 @@ import torch
 
 import oracle as O
 from post_weight_quantization_26_amd import synth
-from test_gpu_parity import check_clip, check_scale_search, bits32
+from test_gpu_parity import assert_pack_parity, check_clip, check_scale_search
 
 pytestmark = pytest.mark.gpu
 
@@ -46,10 +46,7 @@ def run_config(api, name, variants=None, pack_check=True):
         if cfg.pack and pack_check:
             qw, qz, sc = api.quantize_pack(Wd, res["s_best"], ratio, zero_point=zp)
             r_np = None if ratio is None else ratio.cpu().numpy()
-            rqw, rqz, rsc, _ = O.quantize_pack(W, cfg.dtype, s, r_np, 4, 128, zp)
-            assert np.array_equal(qw.cpu().numpy(), rqw)
-            assert np.array_equal(qz.cpu().numpy(), rqz)
-            assert np.array_equal(sc.cpu().numpy().view(np.uint16), rsc)
+            assert_pack_parity(qw, qz, sc, W, cfg.dtype, s, r_np, zp)
         del Xd, Wd
         torch.cuda.empty_cache()
 

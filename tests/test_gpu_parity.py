@@ -1,7 +1,11 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
 Tolerances:
-  * ā, the scale table, codes, zeros and fp16 scales: bit-exact.
+  * ā, the scale table, zeros and fp16 scales: bit-exact. Codes: bit-exact
+    except elements whose pre-round value fl32(w'/step) lies within 1e-6 of a
+    .5 boundary (the kernels form the quotient from the group's reciprocal
+    with one FMA correction, at most one ulp from IEEE division); such
+    elements are counted and may differ by one code.
   * Per-candidate MSE (the curve) against the float64 oracle: 1e-3 relative.
   * Chosen α: identical unless the oracle's two best MSEs are within 1e-4
     relative.
@@ -285,6 +289,39 @@ def test_search_clip_small_ragged(api, bits, zp):
 # step 8: pack
 # ---------------------------------------------------------------------------
 
+def unpack_nibbles(words, cols):
+    u = np.ascontiguousarray(words).view(np.uint32)
+    out = np.zeros((u.shape[0], cols), dtype=np.int64)
+    for i in range(8):
+        out[:, i::8] = (u >> np.uint32(4 * i)) & np.uint32(0xF)
+    return out
+
+
+def assert_pack_parity(qw, qz, sc, W, dtype, s, ratio, zp):
+    """GPU packed output against the oracle's; returns the number of near-tie codes."""
+    rqw, rqz, rsc, ovf = O.quantize_pack(W, dtype, s, ratio, 4, 128, zp)
+    assert not ovf
+    qw, qz, sc = qw.cpu().numpy(), qz.cpu().numpy(), sc.cpu().numpy().view(np.uint16)
+    assert np.array_equal(qz, rqz), "qzeros differ"
+    assert np.array_equal(sc, rsc), "scales differ"
+    if np.array_equal(qw, rqw):
+        return 0
+    N = W.shape[0]
+    gq, rq = unpack_nibbles(qw, N), unpack_nibbles(rqw, N)      # [K, N]
+    kk, nn = np.nonzero(gq != rq)
+    w32 = O.decode(W, dtype)
+    r = np.ones(N, np.float32) if ratio is None else np.asarray(ratio, np.float32)
+    _, step, _ = O.quantize(w32[np.unique(nn)], s, r[np.unique(nn)], 4, 128, zp)
+    row_of = {n: i for i, n in enumerate(np.unique(nn))}
+    for k, n in zip(kk, nn):
+        wp = np.float32(w32[n, k] * np.float32(s[k]))
+        v = float(np.float32(wp / step[row_of[n], k // 128]))
+        assert abs(v - np.floor(v) - 0.5) < 1e-6, f"code ({k},{n}) differs away from a tie"
+        assert abs(int(gq[k, n]) - int(rq[k, n])) == 1
+    print(f"pack: {len(kk)} near-tie codes differ")
+    return len(kk)
+
+
 def _pack_case(api, N, K, dtype, zp, with_ratio, seed):
     rng = np.random.default_rng(seed)
     w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
@@ -299,11 +336,7 @@ def _pack_case(api, N, K, dtype, zp, with_ratio, seed):
     qw, qz, sc = api.quantize_pack(to_dev(W, dtype), torch.from_numpy(s).to("cuda:0"),
                                    None if ratio is None else torch.from_numpy(ratio).to("cuda:0"),
                                    zero_point=zp)
-    rqw, rqz, rsc, ovf = O.quantize_pack(W, dtype, s, ratio, 4, 128, zp)
-    assert not ovf
-    assert np.array_equal(qw.cpu().numpy(), rqw), "qweight differs"
-    assert np.array_equal(qz.cpu().numpy(), rqz), "qzeros differs"
-    assert np.array_equal(sc.cpu().numpy().view(np.uint16), rsc), "scales differ"
+    assert_pack_parity(qw, qz, sc, W, dtype, s, ratio, zp)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
