@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--config", default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=512)
+    p.add_argument("--cpu-rows", type=int, default=2048)
     return p.parse_args()
 
 

@@ -166,16 +166,20 @@ __device__ __forceinline__ void region(const GemmCtx& c, int kt, floatx16 (&acc)
   read_frags<S>(c, 0, f0a, f0b);
   mfma_4x4(acc, f0a, f0b);
   read_frags<S>(c, 1, f1a, f1b);
+  // The 8 copies are spread one per two MFMAs over the 16 MFMAs of (kt-1, 1)
+  // so that the LDS writes they cause interleave with the fragment reads
+  // instead of arriving in one burst.
   if (PREV) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      if (i & 1) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      if (i & 1) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
     }
   }
 #pragma unroll
