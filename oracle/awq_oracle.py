@@ -35,6 +35,12 @@ project's design notes):
   * Ties in every argmin go to the lowest grid index.
   * Packing: 8 four-bit codes per 32-bit word along the output dimension,
     element 8j+i in bits 4i..4i+3; zeros packed the same way; scales fp16.
+  * Linears that read the same input share one preceding operation, so they
+    get one s: their weights are searched as one layer with the outputs
+    concatenated, and the error is the mean over all of those outputs.
+  * The fold divides the preceding normalisation's per-channel weight (and
+    bias, if any), or the preceding linear's output rows and bias, by s:
+    one IEEE float32 division per element, rounded once to the storage type.
 """
 from __future__ import annotations
 
@@ -318,3 +324,83 @@ def storage_bits_per_weight(N: int, K: int, bits: int = 4, group: int = 128) -> 
     """Bits per weight of the packed layout: codes + fp16 scales + packed zeros."""
     total = N * K * bits + (N * K // group) * (16 + bits)
     return total / (N * K)
+
+
+# ----------------------------------------------------------------------------
+# Linears sharing one input, and the fold of diag(s)^-1 into the op before
+# ([concept] "Scaling instead of protecting": the division of the activation
+# channel goes into the preceding layer, usually the normalisation's scale;
+# "When it breaks": that op must be a norm or a linear with per-channel
+# weights)
+# ----------------------------------------------------------------------------
+
+def search_scale_group(X, Ws, dtype, abar, alphas, bits=4, group=128, zero_point=True, rows=None):
+    """α search for several linears that read the same X (for example the
+    query, key and value projections after one normalisation).
+
+    Only one op precedes them, so one s must serve them all. Their outputs,
+    side by side, are the group's output; its error is measured over all of
+    them, which is the single-layer search of the weights stacked along the
+    output dimension. ``rows`` index the stacked rows. Same result dict as
+    ``search_scale``.
+    """
+    W = np.concatenate([np.asarray(w) for w in Ws], axis=0)
+    return search_scale(X, W, dtype, abar, alphas, bits, group, zero_point, rows=rows)
+
+
+def encode(v32: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values -> storage of ``dtype`` (bf16/f16 as uint16 bit
+    patterns), rounded to the nearest representable value, ties to the even
+    significand; values past the largest finite one round to infinity as
+    IEEE rounding prescribes."""
+    v = np.ascontiguousarray(v32, dtype=F32)
+    if dtype == "f32":
+        return v.copy()
+    if dtype == "f16":
+        with np.errstate(over="ignore"):
+            return v.astype(np.float16).view(np.uint16)      # IEEE conversion, ties to even
+    if dtype != "bf16":
+        raise ValueError(f"unsupported dtype {dtype!r}")
+    u = v.view(np.uint32)
+    lo = (u >> np.uint32(16)).astype(np.uint32)              # same sign, magnitude truncated
+    exp = (lo >> np.uint32(7)) & np.uint32(0xFF)
+    # one unit in the last place of a bf16 with this exponent field (8 significand bits)
+    ulp = np.ldexp(1.0, np.maximum(exp.astype(np.int64), 1) - 127 - 7)
+    x = np.abs(v.astype(F64))
+    x_lo = np.abs((lo << np.uint32(16)).view(F32).astype(F64))
+    finite = np.isfinite(v)
+    with np.errstate(invalid="ignore"):
+        d_lo = x - x_lo
+        d_hi = (x_lo + ulp) - x
+    up = finite & ((d_hi < d_lo) | ((d_hi == d_lo) & ((lo & np.uint32(1)) == 1)))
+    out = np.where(up, lo + np.uint32(1), lo)
+    nan = np.isnan(v)
+    out = np.where(nan, out | np.uint32(0x0040), out)         # keep NaN a (quiet) NaN
+    return out.astype(np.uint16)
+
+
+def _divide_stored(a, dtype, d32):
+    """fl32(a / d) elementwise (numpy's float32 division is IEEE's correctly
+    rounded quotient), stored back as ``dtype``."""
+    q = decode(a, dtype) / np.asarray(d32, dtype=F32)
+    return encode(q.astype(F32), dtype)
+
+
+def fold_norm(gamma, beta, dtype, s32):
+    """Normalisation before the layer: y_j = γ_j·x̂_j (+ β_j). Dividing
+    activation channel j by s_j is γ_j / s_j (and β_j / s_j). Returns
+    (γ', β' or None) in the storage ``dtype``."""
+    s = np.asarray(s32, dtype=F32)
+    g = _divide_stored(gamma, dtype, s)
+    b = None if beta is None else _divide_stored(beta, dtype, s)
+    return g, b
+
+
+def fold_linear(W_prev, b_prev, dtype, s32):
+    """Linear before the layer: h = x·W_prevᵀ + b_prev with W_prev [K, K_prev];
+    output channel j of h is input channel j of the layer, so row j of W_prev
+    and b_prev[j] are divided by s_j. Returns (W_prev', b_prev' or None)."""
+    s = np.asarray(s32, dtype=F32)
+    W = _divide_stored(W_prev, dtype, s[:, None])
+    b = None if b_prev is None else _divide_stored(b_prev, dtype, s)
+    return W, b

@@ -402,6 +402,148 @@ def check_pack_overflow_flag(O):
     _, _, _, ovf = O.quantize_pack(W, "f32", np.full(128, 1e6, F32))
     assert ovf
 
+# ----------------------------------------------------------------------------
+# layer groups sharing one input, storage rounding, and the fold
+# ----------------------------------------------------------------------------
+
+def check_search_group(O):
+    """A group's curve is the row-count-weighted mean of its members' curves
+    (its error is averaged over all concatenated outputs); its row sums are
+    the members' row sums side by side; the member order does not matter; a
+    group of one is the single-layer search."""
+    T, K = 12, 256
+    X, _ = synth.make_custom(T, 8, K, "bf16", n_out=3, seed=21)
+    Ws = [synth.make_weight(n, K, 0.02, "bf16", seed=21, cid=c)
+          for n, c in ((4, 1), (2, 2), (6, 3))]
+    alphas = np.array([0.0, 0.3, 0.6, 1.0], F32)
+    ab = O.act_stats(X, "bf16")
+    g = O.search_scale_group(X, Ws, "bf16", ab, alphas)
+    singles = [O.search_scale(X, W, "bf16", ab, alphas) for W in Ws]
+    Ns = [W.shape[0] for W in Ws]
+    weighted = sum(n * r["mse"] for n, r in zip(Ns, singles)) / sum(Ns)
+    assert np.allclose(g["mse"], weighted, rtol=1e-12, atol=0), (g["mse"], weighted)
+    assert np.array_equal(g["row_sums"], np.concatenate([r["row_sums"] for r in singles], axis=1))
+    assert g["index"] == int(np.argmin(weighted))
+    assert np.array_equal(g["s_best"], O.scale_for_alpha(ab, alphas[g["index"]]))
+    perm = O.search_scale_group(X, [Ws[2], Ws[0], Ws[1]], "bf16", ab, alphas)
+    assert np.allclose(perm["mse"], g["mse"], rtol=1e-12, atol=0)
+    one = O.search_scale_group(X, [Ws[0]], "bf16", ab, alphas)
+    assert np.array_equal(one["mse"], singles[0]["mse"])
+
+
+def _bf16_value(p):
+    return float(synth.bf16_bits_to_f32(np.array([p], np.uint16))[0])
+
+
+def check_encode_bf16_exhaustive(O):
+    """Every finite bf16 value encodes to itself; every midpoint of two
+    neighbouring finite values goes to the one with the even significand;
+    one float32 ulp either side of a midpoint goes to the nearer value; the
+    largest finite value plus half its ulp overflows to infinity; signed
+    zero, infinity and NaN keep their kind."""
+    pos = np.arange(0x0000, 0x7F80, dtype=np.uint32).astype(np.uint16)     # 0 .. max finite
+    allp = np.concatenate([pos, pos | np.uint16(0x8000)])
+    assert np.array_equal(O.encode(synth.bf16_bits_to_f32(allp), "bf16"), allp)
+    lo = np.arange(0x0000, 0x7F7F, dtype=np.uint32)                          # lo, lo+1 both finite
+    for sign in (0, 0x8000):
+        vlo = synth.bf16_bits_to_f32((lo | sign).astype(np.uint16)).astype(np.float64)
+        vhi = synth.bf16_bits_to_f32(((lo + 1) | sign).astype(np.uint16)).astype(np.float64)
+        mid = ((vlo + vhi) / 2).astype(F32)
+        assert np.array_equal(mid.astype(np.float64), (vlo + vhi) / 2)     # midpoints exact in f32
+        even = np.where(lo % 2 == 0, lo, lo + 1) | sign
+        assert np.array_equal(O.encode(mid, "bf16"), even.astype(np.uint16))
+        toward = np.float32(np.inf) if sign == 0 else np.float32(-np.inf)
+        away_from_lo = np.nextafter(mid, toward)
+        assert np.array_equal(O.encode(away_from_lo, "bf16"), ((lo + 1) | sign).astype(np.uint16))
+        toward_lo = np.nextafter(mid, -toward)
+        assert np.array_equal(O.encode(toward_lo, "bf16"), (lo | sign).astype(np.uint16))
+    vmax = _bf16_value(0x7F7F)
+    half_ulp = 2.0 ** (254 - 127 - 8)
+    edge = np.array([vmax + half_ulp, np.nextafter(F32(vmax + half_ulp), F32(0))], F32)
+    assert list(O.encode(edge, "bf16")) == [0x7F80, 0x7F7F]
+    special = O.encode(np.array([-0.0, np.inf, -np.inf, np.nan], F32), "bf16")
+    assert list(special[:3]) == [0x8000, 0x7F80, 0xFF80]
+    assert (special[3] & 0x7F80) == 0x7F80 and (special[3] & 0x007F) != 0
+    assert O.encode(np.array([1 / 3], F32), "bf16")[0] == 0x3EAB   # 0x3EAAAAAB rounds up
+
+
+def check_encode_f16_examples(O):
+    """IEEE half: ties to even at 1 + 2^-11 and 1 + 3·2^-11; 65519 -> 65504;
+    the midpoint 65520 above the largest finite value overflows."""
+    v = np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, 65519.0, 65520.0, -2.0], F32)
+    assert list(O.encode(v, "f16")) == [0x3C00, 0x3C02, 0x7BFF, 0x7C00, 0xC000]
+
+
+def _norm_rows(x, eps=1e-6):
+    x = x.astype(np.float64)
+    return x / np.sqrt((x * x).mean(axis=1, keepdims=True) + eps)
+
+
+def check_fold_norm(O):
+    """Norm then layer: with γ' = γ/s, β' = β/s and the layer's weights
+    W·diag(s), every output equals the original one up to the two float32
+    roundings of the quotients (bound u·Σ_j (|x̂_j γ_j| + |β_j|)|w_nj|,
+    u = 2^-24); division by s = 2^k is exact in bf16; γ = 1 with s = 3 stores
+    0x3EAB in bf16 (worked by hand: fl32(1/3) = 0x3EAAAAAB)."""
+    rng = _rng(31)
+    T, K, N = 5, 96, 7
+    x = rng.standard_normal((T, K)).astype(F32)
+    gamma = (1 + 0.3 * rng.standard_normal(K)).astype(F32)
+    beta = (0.5 * rng.standard_normal(K)).astype(F32)
+    w = (0.05 * rng.standard_normal((N, K))).astype(F32)
+    ab = np.abs(rng.standard_normal(K)).astype(F32) + F32(0.01)
+    ab[[3, 40]] = 50.0
+    s = O.scale_for_alpha(ab, 0.8)
+    assert s.max() / s.min() > 10
+    xh = _norm_rows(x)
+    for b in (None, beta):
+        g2, b2 = O.fold_norm(gamma, b, "f32", s)
+        assert (b2 is None) == (b is None)
+        y = xh * gamma.astype(np.float64) + (0 if b is None else b.astype(np.float64))
+        y2 = xh * g2.astype(np.float64) + (0 if b2 is None else b2.astype(np.float64))
+        w2 = w.astype(np.float64) * s.astype(np.float64)[None, :]
+        out, out2 = y @ w.astype(np.float64).T, y2 @ w2.T
+        mag = np.abs(xh * gamma.astype(np.float64)) + (0 if b is None else np.abs(b))
+        bound = 2.0 ** -24 * (mag @ np.abs(w.astype(np.float64)).T) * (1 + 1e-6) + 1e-15
+        assert np.all(np.abs(out2 - out) <= bound), np.max(np.abs(out2 - out) / bound)
+    gb = synth.f32_to_bf16_bits((1 + 0.3 * rng.standard_normal(K)).astype(F32))
+    for k in (-3, -1, 1, 4):
+        g2, _ = O.fold_norm(gb, None, "bf16", np.full(K, 2.0 ** k, F32))
+        assert np.array_equal(synth.bf16_bits_to_f32(g2), synth.bf16_bits_to_f32(gb) * F32(2.0 ** -k))
+    g3, b3 = O.fold_norm(np.array([0x3F80], np.uint16), np.array([0xC040], np.uint16), "bf16",
+                         np.array([3.0], F32))
+    assert g3[0] == 0x3EAB and b3[0] == 0xBF80                        # -3 / 3 = -1 exactly
+
+
+def check_fold_linear(O):
+    """Linear then layer: dividing row j of W_prev and b_prev[j] by s_j and
+    scaling the layer's input channel j by s_j leaves every output unchanged
+    up to the float32 roundings of the quotients. W_prev is square here, so
+    dividing its columns instead of its rows would be shape-valid and must fail."""
+    rng = _rng(32)
+    T, K, N = 6, 64, 5
+    xp = rng.standard_normal((T, K)).astype(F32)
+    wp = (0.1 * rng.standard_normal((K, K))).astype(F32)
+    bp = (0.2 * rng.standard_normal(K)).astype(F32)
+    w = (0.05 * rng.standard_normal((N, K))).astype(F32)
+    ab = np.abs(rng.standard_normal(K)).astype(F32) + F32(0.01)
+    ab[[5, 17, 60]] = 40.0
+    s = O.scale_for_alpha(ab, 0.7)
+    assert s.max() / s.min() > 10
+    for b in (None, bp):
+        wp2, bp2 = O.fold_linear(wp, b, "f32", s)
+        x64, wp64 = xp.astype(np.float64), wp.astype(np.float64)
+        h = x64 @ wp64.T + (0 if b is None else b.astype(np.float64))
+        h2 = x64 @ wp2.astype(np.float64).T + (0 if bp2 is None else bp2.astype(np.float64))
+        out = h @ w.astype(np.float64).T
+        out2 = h2 @ (w.astype(np.float64) * s.astype(np.float64)[None, :]).T
+        mag = np.abs(x64) @ np.abs(wp64).T + (0 if b is None else np.abs(b))
+        bound = 2.0 ** -24 * (mag @ np.abs(w.astype(np.float64)).T) * (1 + 1e-6) + 1e-15
+        assert np.all(np.abs(out2 - out) <= bound), np.max(np.abs(out2 - out) / bound)
+    wb = synth.f32_to_bf16_bits(wp)
+    wb2, _ = O.fold_linear(wb, None, "bf16", np.full(K, 0.5, F32))
+    assert np.array_equal(synth.bf16_bits_to_f32(wb2), synth.bf16_bits_to_f32(wb) * F32(2))
+
 
 ALL_CHECKS = [
     check_stats_closed_form, check_stats_exact_sum, check_scale_closed_form,
@@ -409,5 +551,6 @@ ALL_CHECKS = [
     check_power_of_two_rescale, check_output_error_bruteforce, check_fold_invariance,
     check_gram_identity, check_search_scale_bruteforce, check_search_clip_bruteforce,
     check_monotone_and_separable, check_outlier_behaviour, check_pack_layout,
-    check_pack_overflow_flag,
+    check_pack_overflow_flag, check_search_group, check_encode_bf16_exhaustive,
+    check_encode_f16_examples, check_fold_norm, check_fold_linear,
 ]

@@ -68,6 +68,19 @@ MUTATIONS = [
      "word |= c[:, :, i] << np.uint32(28 - 4 * i)", [P.check_pack_layout]),
     ("codes packed along the input dim", "pack_nibbles(np.ascontiguousarray(q.T))",
      "pack_nibbles(np.ascontiguousarray(q))", [P.check_pack_layout]),
+    ("group searched on its first layer only",
+     "W = np.concatenate([np.asarray(w) for w in Ws], axis=0)", "W = np.asarray(Ws[0])",
+     [P.check_search_group]),
+    ("bf16 ties rounded away from zero", "((d_hi == d_lo) & ((lo & np.uint32(1)) == 1))",
+     "(d_hi == d_lo)", [P.check_encode_bf16_exhaustive]),
+    ("bf16 truncated", "up = finite & ((d_hi < d_lo)", "up = finite & ((d_hi < -1.0)",
+     [P.check_encode_bf16_exhaustive]),
+    ("fold multiplies by s", "q = decode(a, dtype) / np.asarray(d32", "q = decode(a, dtype) * np.asarray(d32",
+     [P.check_fold_norm, P.check_fold_linear]),
+    ("norm bias not folded", "b = None if beta is None else _divide_stored(beta, dtype, s)",
+     "b = None if beta is None else np.asarray(beta)", [P.check_fold_norm]),
+    ("previous linear folded along its input dim", "_divide_stored(W_prev, dtype, s[:, None])",
+     "_divide_stored(W_prev, dtype, s[None, :])", [P.check_fold_linear]),
 ]
 
 
