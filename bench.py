@@ -56,11 +56,13 @@ def gemm_traffic(cfg_name: str, launches_per_step: int):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, X, W, alphas, rows_n: int):
+def cpu_baseline(cfg, X, Ws, alphas, rows_n: int):
     """The CPU oracle, as it stands, on a bounded sample of one step: stats over
     the full X, the α search over ``rows_n`` evenly spaced output rows (all
     tokens, all α; extrapolated linearly to N rows, since every row costs the
-    same), and packing of the full W."""
+    same), and packing of every full W. ``Ws`` holds one layer, or the layers
+    of a group that share X (searched together, with the fold into the
+    normalisation timed too)."""
     import numpy as np
     import oracle as O
     try:
@@ -73,18 +75,25 @@ def cpu_baseline(cfg, X, W, alphas, rows_n: int):
     t0 = time.perf_counter()
     ab = O.act_stats(X, cfg.dtype)
     t1 = time.perf_counter()
-    O.search_scale(X, W, cfg.dtype, ab, alphas, cfg.bits, 128, cfg.zero_point, rows=rows)
+    res = O.search_scale_group(X, Ws, cfg.dtype, ab, alphas, cfg.bits, 128, cfg.zero_point,
+                               rows=rows)
     t2 = time.perf_counter()
-    pack_t = 0.0
+    if cfg.layers:
+        from post_weight_quantization_26_amd import synth
+        O.fold_norm(synth.make_norm_weight(cfg.K, cfg.dtype, cid=cfg.cid)[0], None, cfg.dtype,
+                    res["s_best"])
     if cfg.pack:
-        O.quantize_pack(W, cfg.dtype, np.ones(cfg.K, np.float32), None, 4, 128, cfg.zero_point)
-        pack_t = time.perf_counter() - t2
+        for W in Ws:
+            O.quantize_pack(W, cfg.dtype, res["s_best"], None, 4, 128, cfg.zero_point)
+    pack_t = time.perf_counter() - t2
     step = (t1 - t0) + (t2 - t1) * cfg.N / len(rows) + pack_t
     return {"value": len(alphas) / step, "unit": "alpha-candidates/s", "cores": int(threads),
             "kind": "oracle",
             "sample": (f"stats over all {cfg.T} tokens; alpha search over {len(rows)} of {cfg.N} "
                        f"output rows (all {len(alphas)} alphas, all tokens) extrapolated x"
-                       f"{cfg.N / len(rows):.0f}; pack of the full W"),
+                       f"{cfg.N / len(rows):.0f}" + ("; fold into the norm weight" if cfg.layers
+                                                     else "")
+                       + ("; pack of every full W" if cfg.pack else "")),
             "sample_seconds": round(time.perf_counter() - t0, 2)}
 
 
@@ -105,7 +114,11 @@ def main():
     name = args.config or synth.BENCH_CONFIG
     cfg = synth.CONFIGS[name]
     dev = torch.device("cuda:0")
-    X, W = synth.make_layer(cfg)
+    if cfg.layers:
+        X, Ws = synth.make_group(cfg)
+    else:
+        X, W = synth.make_layer(cfg)
+        Ws = [W]
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
 
     def up(a):
@@ -113,7 +126,9 @@ def main():
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
 
-    Xd, Wd = up(X), up(W)
+    Xd = up(X)
+    Wds = [up(W) for W in Ws]
+    gamma = up(synth.make_norm_weight(cfg.K, cfg.dtype, cid=cfg.cid)[0]) if cfg.layers else None
     alphas = synth.alpha_grid(cfg.n_alpha)
     ratios = synth.ratio_grid(cfg.n_ratio) if cfg.n_ratio else None
     T, N, K = cfg.T, cfg.N, cfg.K
@@ -124,20 +139,30 @@ def main():
                             dtype=torch.uint8, device=dev)
     ws_pack = torch.empty(256, dtype=torch.uint8, device=dev)
     abar = torch.empty(K, dtype=torch.float32, device=dev)
-    pack_out = (torch.empty((K, N // 8), dtype=torch.int32, device=dev),
-                torch.empty((K // 128, N // 8), dtype=torch.int32, device=dev),
-                torch.empty((K // 128, N), dtype=torch.float16, device=dev))
+    pack_out = [(torch.empty((K, Wd.shape[0] // 8), dtype=torch.int32, device=dev),
+                 torch.empty((K // 128, Wd.shape[0] // 8), dtype=torch.int32, device=dev),
+                 torch.empty((K // 128, Wd.shape[0]), dtype=torch.float16, device=dev))
+                for Wd in Wds]
     zp = cfg.zero_point
 
     def step():
         api.act_stats(Xd, ws=ws_stats, out=abar)
-        res = api.search_scale(Xd, Wd, abar, alphas, bits=cfg.bits, zero_point=zp, ws=ws_search)
-        ratio = None
-        if ratios is not None:
-            ratio = api.search_clip(Xd, Wd, res["s_best"], ratios, bits=cfg.bits, zero_point=zp,
-                                    ws=ws_search)["ratio_best"]
-        if cfg.pack:
-            api.quantize_pack(Wd, res["s_best"], ratio, zero_point=zp, ws=ws_pack, out=pack_out)
+        if cfg.layers:
+            # linears sharing X: one search, one s, folded into the norm weight
+            # (in place, so gamma drifts over the steps; the work is the same)
+            res = api.search_scale_group(Xd, Wds, abar, alphas, bits=cfg.bits, zero_point=zp,
+                                         ws=ws_search)
+            api.fold_norm(gamma, res["s_best"])
+        else:
+            res = api.search_scale(Xd, Wds[0], abar, alphas, bits=cfg.bits, zero_point=zp,
+                                   ws=ws_search)
+        for Wd, out in zip(Wds, pack_out):
+            ratio = None
+            if ratios is not None:
+                ratio = api.search_clip(Xd, Wd, res["s_best"], ratios, bits=cfg.bits,
+                                        zero_point=zp, ws=ws_search)["ratio_best"]
+            if cfg.pack:
+                api.quantize_pack(Wd, res["s_best"], ratio, zero_point=zp, ws=ws_pack, out=out)
         return res
 
     for _ in range(args.warmup):
@@ -155,7 +180,7 @@ def main():
     api.profile_enable(False)
 
     elapsed = t1 - t0
-    cands_per_step = cfg.n_alpha + (cfg.n_ratio or 0)
+    cands_per_step = cfg.n_alpha + (cfg.n_ratio or 0)   # clip candidates: per layer, N rows in all
     value = cfg.n_alpha * args.steps / elapsed
     gemm_ms, gemm_n = prof["gemm"]
     gemm_avg_s = gemm_ms / 1e3 / max(gemm_n, 1)
@@ -169,7 +194,7 @@ def main():
     stats_ms, stats_n = prof["stats"]
     stats_gbs = (T * K * X.itemsize) / (stats_ms / 1e3 / max(stats_n, 1)) / 1e9 if stats_n else None
     pack_ms, pack_n = prof["pack"]
-    pack_bytes = N * K * W.itemsize + N * K // 2 + (N * K // 128) * (2 + 0.5) + K * 4
+    pack_bytes = (N * K * X.itemsize + N * K // 2 + (N * K // 128) * (2 + 0.5) + K * 4) / len(Ws)
     pack_gbs = pack_bytes / (pack_ms / 1e3 / max(pack_n, 1)) / 1e9 if pack_n else None
 
     out = {
@@ -188,7 +213,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "T": T, "N": N, "K": K, "group": 128, "bits": cfg.bits,
                    "zero_point": zp, "n_alpha": cfg.n_alpha, "n_ratio": cfg.n_ratio,
-                   "pack": cfg.pack},
+                   "pack": cfg.pack, "layers": list(cfg.layers) or None},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -203,7 +228,7 @@ def main():
         "alpha_best": float(res["alpha_best"]),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, X, W, alphas, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(cfg, X, Ws, alphas, args.cpu_rows)
     print(json.dumps(out), flush=True)
 
 

@@ -11,6 +11,10 @@
  *                      the unquantised product; return the curve and argmin
  *   awq_search_clip    per-output-channel clip ratio search with s fixed
  *   awq_quantize_pack  INT4 codes, packed zeros and fp16 scales
+ *   awq_search_scale_group  the α search for several linears that read the
+ *                      same X and so share one s
+ *   awq_fold_norm, awq_fold_linear  divide the operation that produces X by
+ *                      s, so the scaled weights need no run-time division
  *
  * Sources (page titles and sections):
  *   "AWQ and Activation-Aware Scaling", section "Scaling instead of
@@ -147,6 +151,46 @@ awq_status awq_quantize_pack(const void* W, awq_dtype w_dtype, int64_t N, int64_
                              int32_t* qzeros, uint16_t* scales, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* Steps 2-6 for a group of linears that read the same X (e.g. the query,
+ * key and value projections after one normalisation, or the gate and up
+ * projections). The division by s can go into only one preceding operation,
+ * so the group gets one s ("AWQ and Activation-Aware Scaling", section
+ * "Scaling instead of protecting", the fold into the preceding layer). The
+ * group's output is its layers' outputs side by side, and the error is
+ * averaged over all of them:
+ *   mse[a] = Σ_l Σ_{t,n} (Y_l,a - Y_l)_{tn}² / (T·Σ_l N[l]).
+ * W [host] n_layers device pointers to [N[l], K] weights (16-byte aligned);
+ * N [host] n_layers output-channel counts; 1 <= n_layers <= 16.
+ * row_sums (optional) is [n_alpha, Σ_l N[l]] with the layers' rows in order.
+ * The workspace is sized as for awq_search_scale with N = Σ_l N[l]. Every
+ * other argument and output is as in awq_search_scale, which this equals
+ * when n_layers is 1. Synchronises `stream`. */
+awq_status awq_search_scale_group(const void* X, const void* const* W, const int64_t* N,
+                                  int32_t n_layers, awq_dtype dtype, int64_t T, int64_t K,
+                                  const float* abar, const float* alphas, int32_t n_alpha,
+                                  awq_qconfig qc, float* s_best, float* alpha_best, double* mse,
+                                  double* row_sums, void* ws, size_t ws_bytes, void* stream);
+
+/* The fold into a preceding normalisation ("AWQ and Activation-Aware
+ * Scaling", sections "Scaling instead of protecting" and "When it breaks").
+ * In place: gamma[j] <- gamma[j] / s[j] and, when beta is not NULL,
+ * beta[j] <- beta[j] / s[j], for j < K. Each value is converted to float32,
+ * divided once (IEEE float32) and rounded once, to nearest even, back to
+ * `dtype` (bf16, f16 or f32). gamma, beta: [K] device arrays aligned to
+ * their element size; s: [K] f32 (normally s_best). Does not synchronise. */
+awq_status awq_fold_norm(void* gamma, void* beta, awq_dtype dtype, int64_t K, const float* s,
+                         void* stream);
+
+/* The fold into a preceding linear layer h = x·W_prevᵀ + b_prev whose K
+ * output channels are this layer's K input channels (same sections as
+ * awq_fold_norm). In place: row j of W_prev [K, K_prev] and bias_prev[j]
+ * (when not NULL) are divided by s[j], with the same rounding as
+ * awq_fold_norm. W_prev must be 16-byte aligned with K_prev·element size a
+ * multiple of 16 bytes; bias_prev aligned to its element size.
+ * Does not synchronise. */
+awq_status awq_fold_linear(void* W_prev, void* bias_prev, awq_dtype dtype, int64_t K,
+                           int64_t K_prev, const float* s, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread. */
 const char* awq_last_error(void);
 
@@ -155,9 +199,9 @@ const char* awq_last_error(void);
  * awq_profile_read synchronises those events and returns the summed
  * duration (ms) and launch count of one kernel kind since the last reset.
  * Kinds: 0 stats, 1 scale table, 2 transform (quantise/dequantise
- * candidates), 3 search GEMM, 4 reductions, 5 pack. */
+ * candidates), 3 search GEMM, 4 reductions, 5 pack, 6 fold. */
 enum { AWQ_K_STATS = 0, AWQ_K_SCALE = 1, AWQ_K_TRANSFORM = 2, AWQ_K_GEMM = 3, AWQ_K_REDUCE = 4,
-       AWQ_K_PACK = 5, AWQ_K_COUNT = 6 };
+       AWQ_K_PACK = 5, AWQ_K_FOLD = 6, AWQ_K_COUNT = 7 };
 void awq_profile_enable(int on);
 void awq_profile_reset(void);
 awq_status awq_profile_read(int kind, double* total_ms, int64_t* launches);

@@ -382,7 +382,8 @@ def encode(v32: np.ndarray, dtype: str) -> np.ndarray:
 def _divide_stored(a, dtype, d32):
     """fl32(a / d) elementwise (numpy's float32 division is IEEE's correctly
     rounded quotient), stored back as ``dtype``."""
-    q = decode(a, dtype) / np.asarray(d32, dtype=F32)
+    with np.errstate(over="ignore", under="ignore"):
+        q = decode(a, dtype) / np.asarray(d32, dtype=F32)
     return encode(q.astype(F32), dtype)
 
 

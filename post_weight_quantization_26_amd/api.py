@@ -114,6 +114,72 @@ def search_scale(X: torch.Tensor, W: torch.Tensor, abar: torch.Tensor, alphas: S
                 row_sums=rows)
 
 
+def search_scale_group(X: torch.Tensor, Ws: Sequence[torch.Tensor], abar: torch.Tensor,
+                       alphas: Sequence[float], bits: int = DEFAULT_BITS,
+                       group: int = DEFAULT_GROUP, zero_point: bool = DEFAULT_ZERO_POINT,
+                       want_row_sums: bool = False, ws: Optional[torch.Tensor] = None) -> dict:
+    """One alpha search for linears that read the same X (one shared s): the
+    error is averaged over all their outputs. Same result dict as
+    ``search_scale``; row_sums [n_alpha, sum N] keeps the layers in order."""
+    _dev(X, "X"), _dev(abar, "abar")
+    if not 1 <= len(Ws) <= 16:
+        raise ValueError("a group holds 1 to 16 layers")
+    for i, W in enumerate(Ws):
+        _dev(W, f"Ws[{i}]")
+        if W.dtype != X.dtype or W.shape[1] != X.shape[1]:
+            raise ValueError(f"Ws[{i}] must be [N, K] with X's dtype and K")
+    T, K = X.shape
+    Ns = [int(W.shape[0]) for W in Ws]
+    N = sum(Ns)
+    n = len(alphas)
+    ws = _workspace(ws, workspace_bytes(L.AWQ_OP_SEARCH_SCALE, T, N, K, n, X.dtype), X.device)
+    s_best = torch.empty(K, dtype=torch.float32, device=X.device)
+    rows = torch.empty((n, N), dtype=torch.float64, device=X.device) if want_row_sums else None
+    a_best = ctypes.c_float(0.0)
+    mse = (ctypes.c_double * n)()
+    wptrs = (ctypes.c_void_p * len(Ws))(*[W.data_ptr() for W in Ws])
+    nvals = (ctypes.c_int64 * len(Ws))(*Ns)
+    L.check(L.lib().awq_search_scale_group(_ptr(X), wptrs, nvals, len(Ws), _dtype(X), T, K,
+                                           _ptr(abar), L.float_array(alphas), n,
+                                           qconfig(bits, group, zero_point), _ptr(s_best),
+                                           ctypes.byref(a_best), mse, _ptr(rows), _ptr(ws),
+                                           ws.numel(), _stream()))
+    mse_np = np.array(mse[:], dtype=np.float64)
+    g32 = np.asarray(alphas, dtype=np.float32)
+    idx = int(np.flatnonzero(g32 == np.float32(a_best.value))[0])
+    return dict(alpha_best=np.float32(a_best.value), index=idx, s_best=s_best, mse=mse_np,
+                row_sums=rows)
+
+
+def fold_norm(gamma: torch.Tensor, s: torch.Tensor, beta: Optional[torch.Tensor] = None) -> None:
+    """In place: gamma /= s (and beta /= s) per channel, for the normalisation
+    that produces the searched layer's input."""
+    _dev(gamma, "gamma"), _dev(s, "s")
+    if beta is not None:
+        _dev(beta, "beta")
+        if beta.dtype != gamma.dtype or beta.numel() != gamma.numel():
+            raise ValueError("beta must match gamma")
+    if s.dtype != torch.float32 or s.numel() != gamma.numel():
+        raise ValueError("s must be float32 with one value per channel")
+    L.check(L.lib().awq_fold_norm(_ptr(gamma), _ptr(beta), _dtype(gamma), gamma.numel(), _ptr(s),
+                                  _stream()))
+
+
+def fold_linear(W_prev: torch.Tensor, s: torch.Tensor, bias: Optional[torch.Tensor] = None) -> None:
+    """In place: row j of W_prev [K, K_prev] (and bias[j]) /= s[j], for the
+    linear whose outputs are the searched layer's inputs."""
+    _dev(W_prev, "W_prev"), _dev(s, "s")
+    K, K_prev = W_prev.shape
+    if bias is not None:
+        _dev(bias, "bias")
+        if bias.dtype != W_prev.dtype or bias.numel() != K:
+            raise ValueError("bias must be [K] with W_prev's dtype")
+    if s.dtype != torch.float32 or s.numel() != K:
+        raise ValueError("s must be float32 with one value per output channel of W_prev")
+    L.check(L.lib().awq_fold_linear(_ptr(W_prev), _ptr(bias), _dtype(W_prev), K, K_prev, _ptr(s),
+                                    _stream()))
+
+
 def search_clip(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor, ratios: Sequence[float],
                 bits: int = DEFAULT_BITS, group: int = DEFAULT_GROUP,
                 zero_point: bool = DEFAULT_ZERO_POINT, want_row_sums: bool = False,

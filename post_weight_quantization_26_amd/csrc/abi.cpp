@@ -18,7 +18,8 @@ hipError_t launch_reciprocal(const float* s, int64_t n, float* s_copy, float* in
                              hipStream_t st);
 hipError_t launch_transform(const void* W, int dtype, int64_t N, int64_t K, const float* s_rows,
                             const float* inv_rows, int64_t s_stride, const float* ratios_host,
-                            int nc, int bits, int zero_point, void* E, hipStream_t st);
+                            int nc, int bits, int zero_point, void* E, int64_t cand_stride,
+                            hipStream_t st);
 hipError_t launch_search_gemm(const void* X, int dtype, const void* E, int64_t M, int64_t Nc,
                               int64_t K, float* partials, hipStream_t st);
 hipError_t launch_reduce_rows(const float* partials, int64_t MT, int64_t Nc, double* row_sums,
@@ -31,6 +32,9 @@ hipError_t launch_clip_select(const double* row_sums, int n_ratio, int64_t N,
 hipError_t launch_pack(const void* W, int dtype, int64_t N, int64_t K, const float* s,
                        const float* ratio, int zero_point, int32_t* qweight, int32_t* qzeros,
                        uint16_t* scales, int* overflow, hipStream_t st);
+hipError_t launch_fold_vec(void* v, int dtype, int64_t K, const float* s, hipStream_t st);
+hipError_t launch_fold_rows(void* W, int dtype, int64_t K, int64_t K_prev, const float* s,
+                            hipStream_t st);
 
 namespace {
 
@@ -103,20 +107,32 @@ T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-// Runs transform -> GEMM -> row reduction for candidates [c0, c0+cb).
-awq_status run_batch(const void* X, const void* W, awq_dtype d, int64_t T, int64_t N, int64_t K,
-                     const float* s_rows, const float* inv_rows, int64_t s_stride,
-                     const float* ratios_host, int cb,
-                     awq_qconfig qc, const SearchLayout& L, void* ws, double* row_sums_out,
-                     hipStream_t st) {
+// One layer of a search: its weights and its first row among the N output
+// channels searched together.
+struct Segment {
+  const void* W;
+  int64_t N;
+  int64_t row0;
+};
+
+// Runs transform -> GEMM -> row reduction for candidates [c0, c0+cb). E holds
+// candidate blocks of N rows each; every segment fills its rows of every block.
+awq_status run_batch(const void* X, const Segment* seg, int n_seg, awq_dtype d, int64_t T,
+                     int64_t N, int64_t K, const float* s_rows, const float* inv_rows,
+                     int64_t s_stride, const float* ratios_host, int cb, awq_qconfig qc,
+                     const SearchLayout& L, void* ws, double* row_sums_out, hipStream_t st) {
   void* E = at<void>(ws, L.E);
   float* partials = at<float>(ws, L.partials);
-  AWQ_HIP(timed(AWQ_K_TRANSFORM, st,
-                [&] {
-                  return launch_transform(W, dt(d), N, K, s_rows, inv_rows, s_stride, ratios_host,
-                                          cb, qc.w_bit, qc.zero_point, E, st);
-                }),
-          "transform");
+  for (int l = 0; l < n_seg; ++l) {
+    void* E_l = static_cast<char*>(E) + size_t(seg[l].row0) * size_t(K) * dtype_bytes(d);
+    AWQ_HIP(timed(AWQ_K_TRANSFORM, st,
+                  [&] {
+                    return launch_transform(seg[l].W, dt(d), seg[l].N, K, s_rows, inv_rows,
+                                            s_stride, ratios_host, cb, qc.w_bit, qc.zero_point,
+                                            E_l, N * K, st);
+                  }),
+            "transform");
+  }
   AWQ_HIP(timed(AWQ_K_GEMM, st,
                 [&] { return launch_search_gemm(X, dt(d), E, T, int64_t(cb) * N, K, partials, st); }),
           "search_gemm");
@@ -157,17 +173,15 @@ extern "C" awq_status awq_scale_table(const float* abar, int64_t K, const float*
   return AWQ_OK;
 }
 
-extern "C" awq_status awq_search_scale(const void* X, const void* W, awq_dtype dtype, int64_t T,
-                                       int64_t N, int64_t K, const float* abar,
-                                       const float* alphas, int32_t n_alpha, awq_qconfig qc,
-                                       float* s_best, float* alpha_best, double* mse,
-                                       double* row_sums, void* ws, size_t ws_bytes,
-                                       void* stream) {
-  int32_t nb = 0;
-  awq_status s = check_search(AWQ_OP_SEARCH_SCALE, X, W, dtype, T, N, K, abar, alphas, n_alpha,
-                              qc, s_best, alpha_best, mse, ws, ws_bytes, &nb);
-  if (s != AWQ_OK) return s;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+namespace {
+
+// α search over the layers of `seg` (one layer, or several reading the same
+// X), already validated; N is their total output channels.
+awq_status search_scale_impl(const void* X, const Segment* seg, int n_seg, awq_dtype dtype,
+                             int64_t T, int64_t N, int64_t K, const float* abar,
+                             const float* alphas, int32_t n_alpha, awq_qconfig qc, float* s_best,
+                             float* alpha_best, double* mse, double* row_sums, void* ws,
+                             int32_t nb, hipStream_t st) {
   const SearchLayout L = search_layout(AWQ_OP_SEARCH_SCALE, T, N, K, n_alpha, nb, dtype);
   float* s_table = at<float>(ws, L.s_table);
   float* inv_table = at<float>(ws, L.inv);
@@ -181,8 +195,9 @@ extern "C" awq_status awq_search_scale(const void* X, const void* W, awq_dtype d
           "scale_table");
   for (int c0 = 0; c0 < n_alpha; c0 += nb) {
     const int cb = n_alpha - c0 < nb ? n_alpha - c0 : nb;
-    s = run_batch(X, W, dtype, T, N, K, s_table + int64_t(c0) * K, inv_table + int64_t(c0) * K,
-                  K, nullptr, cb, qc, L, ws, rs + int64_t(c0) * N, st);
+    awq_status s = run_batch(X, seg, n_seg, dtype, T, N, K, s_table + int64_t(c0) * K,
+                             inv_table + int64_t(c0) * K, K, nullptr, cb, qc, L, ws,
+                             rs + int64_t(c0) * N, st);
     if (s != AWQ_OK) return s;
   }
   AWQ_HIP(timed(AWQ_K_REDUCE, st,
@@ -206,6 +221,48 @@ extern "C" awq_status awq_search_scale(const void* X, const void* W, awq_dtype d
   return AWQ_OK;
 }
 
+}  // namespace
+
+extern "C" awq_status awq_search_scale(const void* X, const void* W, awq_dtype dtype, int64_t T,
+                                       int64_t N, int64_t K, const float* abar,
+                                       const float* alphas, int32_t n_alpha, awq_qconfig qc,
+                                       float* s_best, float* alpha_best, double* mse,
+                                       double* row_sums, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  int32_t nb = 0;
+  awq_status s = check_search(AWQ_OP_SEARCH_SCALE, X, W, dtype, T, N, K, abar, alphas, n_alpha,
+                              qc, s_best, alpha_best, mse, ws, ws_bytes, &nb);
+  if (s != AWQ_OK) return s;
+  const Segment seg{W, N, 0};
+  return search_scale_impl(X, &seg, 1, dtype, T, N, K, abar, alphas, n_alpha, qc, s_best,
+                           alpha_best, mse, row_sums, ws, nb, static_cast<hipStream_t>(stream));
+}
+
+extern "C" awq_status awq_search_scale_group(const void* X, const void* const* W,
+                                             const int64_t* N, int32_t n_layers, awq_dtype dtype,
+                                             int64_t T, int64_t K, const float* abar,
+                                             const float* alphas, int32_t n_alpha,
+                                             awq_qconfig qc, float* s_best, float* alpha_best,
+                                             double* mse, double* row_sums, void* ws,
+                                             size_t ws_bytes, void* stream) {
+  int64_t N_total = 0;
+  awq_status s = check_group(W, N, n_layers, &N_total);
+  if (s != AWQ_OK) return s;
+  int32_t nb = 0;
+  s = check_search(AWQ_OP_SEARCH_SCALE, X, W[0], dtype, T, N_total, K, abar, alphas, n_alpha, qc,
+                   s_best, alpha_best, mse, ws, ws_bytes, &nb);
+  if (s != AWQ_OK) return s;
+  Segment seg[kMaxLayers];
+  int64_t row0 = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    seg[l] = Segment{W[l], N[l], row0};
+    row0 += N[l];
+  }
+  return search_scale_impl(X, seg, n_layers, dtype, T, N_total, K, abar, alphas, n_alpha, qc,
+                           s_best, alpha_best, mse, row_sums, ws, nb,
+                           static_cast<hipStream_t>(stream));
+}
+
 extern "C" awq_status awq_search_clip(const void* X, const void* W, awq_dtype dtype, int64_t T,
                                       int64_t N, int64_t K, const float* s, const float* ratios,
                                       int32_t n_ratio, awq_qconfig qc, float* ratio_best,
@@ -222,11 +279,12 @@ extern "C" awq_status awq_search_clip(const void* X, const void* W, awq_dtype dt
   double* mc = at<double>(ws, L.scalar);
   float* inv = at<float>(ws, L.inv);
   float* s_copy = at<float>(ws, L.s_table);
+  const Segment seg{W, N, 0};
   AWQ_HIP(timed(AWQ_K_SCALE, st, [&] { return launch_reciprocal(s, K, s_copy, inv, st); }),
           "reciprocal");
   for (int c0 = 0; c0 < n_ratio; c0 += nb) {
     const int cb = n_ratio - c0 < nb ? n_ratio - c0 : nb;
-    st_ = run_batch(X, W, dtype, T, N, K, s_copy, inv, 0, ratios + c0, cb, qc, L, ws,
+    st_ = run_batch(X, &seg, 1, dtype, T, N, K, s_copy, inv, 0, ratios + c0, cb, qc, L, ws,
                     rs + int64_t(c0) * N, st);
     if (st_ != AWQ_OK) return st_;
   }
@@ -264,6 +322,34 @@ extern "C" awq_status awq_quantize_pack(const void* W, awq_dtype w_dtype, int64_
   AWQ_HIP(hipMemcpyAsync(&host_flag, flag, sizeof(int), hipMemcpyDeviceToHost, st), "copy flag");
   AWQ_HIP(hipStreamSynchronize(st), "synchronize");
   if (host_flag) return set_error(AWQ_E_RANGE, "quantize_pack: a group step overflows fp16");
+  return AWQ_OK;
+}
+
+extern "C" awq_status awq_fold_norm(void* gamma, void* beta, awq_dtype dtype, int64_t K,
+                                    const float* s, void* stream) {
+  awq_status st_ = check_fold_norm(gamma, beta, dtype, K, s);
+  if (st_ != AWQ_OK) return st_;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  AWQ_HIP(timed(AWQ_K_FOLD, st, [&] { return launch_fold_vec(gamma, dt(dtype), K, s, st); }),
+          "fold_norm");
+  if (beta)
+    AWQ_HIP(timed(AWQ_K_FOLD, st, [&] { return launch_fold_vec(beta, dt(dtype), K, s, st); }),
+            "fold_norm bias");
+  return AWQ_OK;
+}
+
+extern "C" awq_status awq_fold_linear(void* W_prev, void* bias_prev, awq_dtype dtype, int64_t K,
+                                      int64_t K_prev, const float* s, void* stream) {
+  awq_status st_ = check_fold_linear(W_prev, bias_prev, dtype, K, K_prev, s);
+  if (st_ != AWQ_OK) return st_;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  AWQ_HIP(timed(AWQ_K_FOLD, st,
+                [&] { return launch_fold_rows(W_prev, dt(dtype), K, K_prev, s, st); }),
+          "fold_linear");
+  if (bias_prev)
+    AWQ_HIP(timed(AWQ_K_FOLD, st,
+                  [&] { return launch_fold_vec(bias_prev, dt(dtype), K, s, st); }),
+            "fold_linear bias");
   return AWQ_OK;
 }
 

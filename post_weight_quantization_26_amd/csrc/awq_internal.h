@@ -12,6 +12,7 @@ namespace awq {
 
 constexpr int kGroup = 128;
 constexpr int kMaxGrid = 64;
+constexpr int kMaxLayers = 16;     // linears searched together on one shared input
 constexpr int kGemmBM_bf16 = 256;  // token rows per search-GEMM tile (bf16 MFMA path)
 constexpr int kGemmBM_f32 = 64;    // token rows per tile on the fp32 path
 constexpr size_t kAlign = 256;
@@ -52,6 +53,13 @@ awq_status check_search(int op, const void* X, const void* W, awq_dtype d, int64
                         int64_t K, const float* vec, const float* grid, int32_t n_grid,
                         awq_qconfig qc, const void* out_dev, const void* out_host,
                         const void* out_host2, const void* ws, size_t ws_bytes, int32_t* nb);
+// Layers of a shared-input group: non-NULL 16-byte aligned weights, sizes
+// >= 1; *N_total receives the summed output channels.
+awq_status check_group(const void* const* W, const int64_t* N, int32_t n_layers, int64_t* N_total);
+awq_status check_fold_norm(const void* gamma, const void* beta, awq_dtype d, int64_t K,
+                           const float* s);
+awq_status check_fold_linear(const void* W_prev, const void* bias, awq_dtype d, int64_t K,
+                             int64_t K_prev, const float* s);
 awq_status check_pack(const void* W, awq_dtype d, int64_t N, int64_t K, const float* s,
                       awq_qconfig qc, const int32_t* qweight, const int32_t* qzeros,
                       const uint16_t* scales, const void* ws, size_t ws_bytes);

@@ -16,10 +16,16 @@ hipError_t launch_reciprocal(const float* s, int64_t n, float* s_copy, float* in
                              hipStream_t st);
 // Candidate error weights E[c] = fold(dequant(quant(W·diag(s_c), r_c))) - W for
 // c in [0, nc): scale rows `s_rows` (s_stride 0 = one shared row) and clip
-// ratios `ratios_host` (NULL = all 1).
+// ratios `ratios_host` (NULL = all 1). Candidate c's [N, K] block starts at
+// element c·cand_stride of E.
 hipError_t launch_transform(const void* W, int dtype, int64_t N, int64_t K, const float* s_rows,
                             const float* inv_rows, int64_t s_stride, const float* ratios_host,
-                            int nc, int bits, int zero_point, void* E, hipStream_t st);
+                            int nc, int bits, int zero_point, void* E, int64_t cand_stride,
+                            hipStream_t st);
+// In-place fold of 1/s: v[j] /= s[j] (j < K); rows of W [K, K_prev] /= s[row].
+hipError_t launch_fold_vec(void* v, int dtype, int64_t K, const float* s, hipStream_t st);
+hipError_t launch_fold_rows(void* W, int dtype, int64_t K, int64_t K_prev, const float* s,
+                            hipStream_t st);
 // partials[mt][c] = Σ_{t in tile mt} (X·Eᵀ)[t][c]² for c in [0, Nc).
 hipError_t launch_search_gemm(const void* X, int dtype, const void* E, int64_t M, int64_t Nc,
                               int64_t K, float* partials, hipStream_t st);

@@ -7,6 +7,10 @@
 // section 3 "The scaling trick" for the fold; section 4 for quantise then
 // measure the output error; "Optional: per-channel clipping" for the ratio).
 //
+// E may hold several layers side by side (linears sharing one input are
+// searched together): candidate c of a layer starts `cand_stride` elements
+// after candidate c-1, and the caller offsets E to the layer's first row.
+//
 // One lane owns 8 consecutive input channels of one row; the 16 lanes of a
 // 128-wide group find its min/max with xor-shuffles, so every lane holds the
 // group's step and zero point. W is read once per batch and each candidate's
@@ -52,7 +56,7 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void transform_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s_rows,
     const float* __restrict__ inv_rows, int64_t s_stride, GridArgs ratios, int has_ratio, int nc,
-    int bits, int zero_point, void* __restrict__ E) {
+    int bits, int zero_point, void* __restrict__ E, int64_t cand_stride) {
 #pragma clang fp contract(off)
   const int64_t NK = N * K;
   const int64_t e0 = (int64_t(blockIdx.x) * kThreads + threadIdx.x) * 8;  // flat n*K + k
@@ -97,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void transform_kernel(
       const float q = quant_code(wp[i], p, rstep);
       e[i] = ((q - p.zero) * p.step) * iv[i] - w[i];
     }
-    if (active) store8<DT>(E, int64_t(c) * NK + e0, e);
+    if (active) store8<DT>(E, int64_t(c) * cand_stride + e0, e);
   }
 }
 
@@ -105,7 +109,8 @@ __global__ __launch_bounds__(kThreads) void transform_kernel(
 
 hipError_t launch_transform(const void* W, int dtype, int64_t N, int64_t K, const float* s_rows,
                             const float* inv_rows, int64_t s_stride, const float* ratios_host,
-                            int nc, int bits, int zero_point, void* E, hipStream_t st) {
+                            int nc, int bits, int zero_point, void* E, int64_t cand_stride,
+                            hipStream_t st) {
   GridArgs g{};
   const int has_ratio = ratios_host != nullptr;
   for (int i = 0; i < nc && i < 64; ++i) g.v[i] = has_ratio ? ratios_host[i] : 1.f;
@@ -113,10 +118,12 @@ hipError_t launch_transform(const void* W, int dtype, int64_t N, int64_t K, cons
   const unsigned blocks = unsigned((lanes + kThreads - 1) / kThreads);
   if (dtype == 1)
     transform_kernel<1><<<blocks, kThreads, 0, st>>>(W, N, K, s_rows, inv_rows, s_stride, g,
-                                                     has_ratio, nc, bits, zero_point, E);
+                                                     has_ratio, nc, bits, zero_point, E,
+                                                     cand_stride);
   else
     transform_kernel<0><<<blocks, kThreads, 0, st>>>(W, N, K, s_rows, inv_rows, s_stride, g,
-                                                     has_ratio, nc, bits, zero_point, E);
+                                                     has_ratio, nc, bits, zero_point, E,
+                                                     cand_stride);
   return hipGetLastError();
 }
 

@@ -143,6 +143,58 @@ awq_status check_search(int op, const void* X, const void* W, awq_dtype d, int64
   return AWQ_OK;
 }
 
+awq_status check_group(const void* const* W, const int64_t* N, int32_t n_layers,
+                       int64_t* N_total) {
+  if (!W || !N) return set_error(AWQ_E_INVALID, "search_scale_group: NULL layer arrays");
+  if (n_layers < 1 || n_layers > kMaxLayers)
+    return set_error(AWQ_E_INVALID, "search_scale_group: n_layers=%d outside 1..%d", n_layers,
+                     kMaxLayers);
+  int64_t tot = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    if (!W[l]) return set_error(AWQ_E_INVALID, "search_scale_group: W[%d] is NULL", l);
+    if (!aligned16(W[l]))
+      return set_error(AWQ_E_INVALID, "search_scale_group: W[%d] must be 16-byte aligned", l);
+    if (N[l] < 1 || N[l] > kMaxDim)
+      return set_error(AWQ_E_INVALID, "search_scale_group: N[%d]=%lld out of range", l,
+                       (long long)N[l]);
+    tot += N[l];
+  }
+  if (tot > kMaxDim)
+    return set_error(AWQ_E_INVALID, "search_scale_group: %lld output channels in total",
+                     (long long)tot);
+  *N_total = tot;
+  return AWQ_OK;
+}
+
+static bool aligned_elem(const void* p, awq_dtype d) {
+  return d == AWQ_F32 ? aligned4(p) : (reinterpret_cast<uintptr_t>(p) & 1u) == 0;
+}
+
+awq_status check_fold_norm(const void* gamma, const void* beta, awq_dtype d, int64_t K,
+                           const float* s) {
+  if (!gamma || !s) return set_error(AWQ_E_INVALID, "fold_norm: NULL gamma or s");
+  if (!dtype_ok(d)) return set_error(AWQ_E_INVALID, "fold_norm: unknown dtype %d", int(d));
+  if (K < 1 || K > kMaxDim) return set_error(AWQ_E_INVALID, "fold_norm: bad K=%lld", (long long)K);
+  if (!aligned_elem(gamma, d) || (beta && !aligned_elem(beta, d)) || !aligned4(s))
+    return set_error(AWQ_E_INVALID, "fold_norm: misaligned pointer");
+  return AWQ_OK;
+}
+
+awq_status check_fold_linear(const void* W_prev, const void* bias, awq_dtype d, int64_t K,
+                             int64_t K_prev, const float* s) {
+  if (!W_prev || !s) return set_error(AWQ_E_INVALID, "fold_linear: NULL W_prev or s");
+  if (!dtype_ok(d)) return set_error(AWQ_E_INVALID, "fold_linear: unknown dtype %d", int(d));
+  if (K < 1 || K_prev < 1 || K > kMaxDim || K_prev > kMaxDim)
+    return set_error(AWQ_E_INVALID, "fold_linear: bad shape K=%lld K_prev=%lld", (long long)K,
+                     (long long)K_prev);
+  if ((K_prev * int64_t(dtype_bytes(d))) % 16)
+    return set_error(AWQ_E_INVALID, "fold_linear: a row of W_prev (K_prev=%lld) must span a "
+                     "multiple of 16 bytes", (long long)K_prev);
+  if (!aligned16(W_prev) || (bias && !aligned_elem(bias, d)) || !aligned4(s))
+    return set_error(AWQ_E_INVALID, "fold_linear: W_prev must be 16-byte aligned");
+  return AWQ_OK;
+}
+
 awq_status check_pack(const void* W, awq_dtype d, int64_t N, int64_t K, const float* s,
                       awq_qconfig qc, const int32_t* qweight, const int32_t* qzeros,
                       const uint16_t* scales, const void* ws, size_t ws_bytes) {

@@ -14,7 +14,8 @@ Gaussian with the stated spreads.
 
 Every array is drawn from numpy's PCG64 keyed by
 ``SeedSequence([seed, config_id, stream])`` with the streams
-0 = W, 1 = X base, 2 = outlier channel indices, 3 = outlier factors, 4 = signs.
+0 = W, 1 = X base, 2 = outlier channel indices, 3 = outlier factors, 4 = signs,
+10 + l = layer l of a group sharing X, 20 / 21 = a normalisation's weight / bias.
 bf16 tensors are produced from float32 draws by one round-to-nearest-even
 conversion and are carried as ``uint16`` bit patterns (numpy has no bf16).
 """
@@ -49,6 +50,7 @@ class LayerConfig:
     n_ratio: int = 0         # 0 = no clip search
     pack: bool = False
     group: int = 128
+    layers: tuple = ()       # output channels of each linear reading the same X (a group)
 
 
 CONFIGS = {
@@ -67,6 +69,11 @@ CONFIGS = {
     # 70B-class MLP layer, asymmetric and symmetric INT4.
     "llama70b_mlp": LayerConfig("llama70b_mlp", 5, 32768, 28672, 8192, "bf16", 0.015, 82,
                                 20.0, 100.0, variants=(True, False), n_ratio=20, pack=True),
+    # Llama-7B query/key/value projections: three 4096x4096 linears on the
+    # same normalised input, searched with one shared s, which is then folded
+    # into the RMSNorm weight; each layer is packed.
+    "llama7b_qkv_group": LayerConfig("llama7b_qkv_group", 6, 65536, 12288, 4096, "bf16", 0.02, 41,
+                                     20.0, 100.0, pack=True, layers=(4096, 4096, 4096)),
 }
 
 BENCH_CONFIG = "llama7b_attn_4096"
@@ -103,9 +110,9 @@ def _encode(a32: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def make_weight(N: int, K: int, w_std: float, dtype: str, seed: int = DEFAULT_SEED,
-                cid: int = 0) -> np.ndarray:
+                cid: int = 0, stream: int = 0) -> np.ndarray:
     """W [N, K] ~ N(0, w_std²), row-major (the out x in layout of a linear layer)."""
-    w = _rng(seed, cid, 0).standard_normal((N, K), dtype=np.float32)
+    w = _rng(seed, cid, stream).standard_normal((N, K), dtype=np.float32)
     w *= np.float32(w_std)
     return _encode(w, dtype)
 
@@ -152,6 +159,32 @@ def make_layer(cfg: LayerConfig, seed: int = DEFAULT_SEED, T: Optional[int] = No
                          cfg.x_kind, seed, cfg.cid)
     W = make_weight(cfg.N, cfg.K, cfg.w_std, cfg.dtype, seed, cfg.cid)
     return X, W
+
+
+def make_group(cfg: LayerConfig, seed: int = DEFAULT_SEED, T: Optional[int] = None):
+    """(X, [W_l]) for a config whose linears share X; layer l's weights come
+    from stream 10 + l."""
+    T = cfg.T if T is None else T
+    X = make_activations(T, cfg.K, cfg.n_outliers, cfg.out_lo, cfg.out_hi, cfg.dtype,
+                         cfg.x_kind, seed, cfg.cid)
+    Ws = [make_weight(n, cfg.K, cfg.w_std, cfg.dtype, seed, cfg.cid, 10 + l)
+          for l, n in enumerate(cfg.layers)]
+    return X, Ws
+
+
+def make_norm_weight(K: int, dtype: str, seed: int = DEFAULT_SEED, cid: int = 0,
+                     with_bias: bool = False):
+    """Per-channel weight γ ~ 1 + 0.1·N(0,1) (and bias β ~ 0.05·N(0,1)) of a
+    normalisation, from streams 20 and 21."""
+    g = (1.0 + 0.1 * _rng(seed, cid, 20).standard_normal(K)).astype(np.float32)
+    b = (0.05 * _rng(seed, cid, 21).standard_normal(K)).astype(np.float32) if with_bias else None
+    return _encode_any(g, dtype), None if b is None else _encode_any(b, dtype)
+
+
+def _encode_any(a32: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f16":
+        return a32.astype(np.float16).view(np.uint16)
+    return _encode(a32, dtype)
 
 
 def make_custom(T: int, N: int, K: int, dtype: str = "bf16", n_out: Optional[int] = None,

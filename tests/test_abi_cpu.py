@@ -178,3 +178,65 @@ def test_autoawq_defaults():
     assert f"DEFAULT_BITS = {gold['w_bit']}" in src
     assert f"DEFAULT_GROUP = {gold['q_group_size']}" in src
     assert f"DEFAULT_ZERO_POINT = {gold['zero_point']}" in src
+
+
+def _group(L, Ws=(FAKE, FAKE), Ns=(256, 128), n_layers=None, ws_bytes=1 << 40, K=256, T=256):
+    lib = L.lib()
+    n = len(Ws) if n_layers is None else n_layers
+    wp = (ctypes.c_void_p * max(len(Ws), 1))(*[w.value if w is not None else None for w in Ws])
+    nv = (ctypes.c_int64 * max(len(Ns), 1))(*Ns)
+    a_best = ctypes.c_float()
+    mse = (ctypes.c_double * 3)()
+    return lib.awq_search_scale_group(FAKE, wp, nv, n, L.AWQ_BF16, T, K, FAKE,
+                                      L.float_array([0.0, 0.5, 1.0]), 3, L.QConfig(4, 128, 1),
+                                      FAKE, ctypes.byref(a_best), mse, None, FAKE, ws_bytes, None)
+
+
+def test_group_search_rejects(L):
+    assert _group(L, n_layers=0) == -1
+    assert _group(L, Ws=(FAKE,) * 17, Ns=(128,) * 17) == -1
+    assert _group(L, Ws=(FAKE, None)) == -1
+    assert _group(L, Ws=(FAKE, MIS)) == -1
+    assert _group(L, Ns=(256, 0)) == -1
+    assert _group(L, K=200) == -1
+    # the workspace is sized for the summed output channels
+    lib = L.lib()
+    one = lib.awq_workspace_bytes_batch(L.AWQ_OP_SEARCH_SCALE, 256, 256, 256, 3, 1, L.AWQ_BF16)
+    both = lib.awq_workspace_bytes_batch(L.AWQ_OP_SEARCH_SCALE, 256, 384, 256, 3, 1, L.AWQ_BF16)
+    assert both > one
+    assert _group(L, ws_bytes=one) == -3
+    assert "workspace" in L.last_error()
+    assert _group(L, Ns=(256, (1 << 31) + 1)) == -1
+    assert "N[1]" in L.last_error()
+    assert _group(L, Ns=(256, 1 << 31)) == -1
+    assert "in total" in L.last_error()
+
+
+def test_fold_rejects(L):
+    lib = L.lib()
+    fn, fl = lib.awq_fold_norm, lib.awq_fold_linear
+    ODD = ctypes.c_void_p(0x10001)
+    assert fn(None, None, L.AWQ_BF16, 64, FAKE, None) == -1
+    assert fn(FAKE, None, L.AWQ_BF16, 0, FAKE, None) == -1
+    assert fn(FAKE, None, 7, 64, FAKE, None) == -1
+    assert fn(FAKE, None, L.AWQ_BF16, 64, None, None) == -1
+    assert fn(ODD, None, L.AWQ_BF16, 64, FAKE, None) == -1
+    assert fn(MIS, None, L.AWQ_F32, 64, FAKE, None) == -1
+    assert fn(FAKE, MIS, L.AWQ_F32, 64, FAKE, None) == -1
+    assert fl(None, None, L.AWQ_BF16, 64, 64, FAKE, None) == -1
+    assert fl(FAKE, None, L.AWQ_BF16, 64, 12, FAKE, None) == -1     # row of 24 bytes
+    assert fl(FAKE, None, L.AWQ_F32, 64, 6, FAKE, None) == -1       # row of 24 bytes
+    assert fl(MIS, None, L.AWQ_BF16, 64, 64, FAKE, None) == -1
+    assert fl(FAKE, ODD, L.AWQ_BF16, 64, 64, FAKE, None) == -1
+    assert fl(FAKE, None, L.AWQ_BF16, 0, 64, FAKE, None) == -1
+    assert fl(FAKE, None, L.AWQ_BF16, 64, 64, None, None) == -1
+    assert "fold_linear" in L.last_error()
+
+
+def test_profile_kinds_match_header(L):
+    src = open(HEADER).read()
+    for name, kind in L.KERNEL_KINDS.items():
+        assert re.search(rf"AWQ_K_{name.upper()}\s*=\s*{kind}\b", src) or \
+            (name == "scale" and re.search(rf"AWQ_K_SCALE\s*=\s*{kind}\b", src)), name
+    count = int(re.search(r"AWQ_K_COUNT\s*=\s*(\d+)", src).group(1))
+    assert count == len(L.KERNEL_KINDS)

@@ -75,7 +75,8 @@ MUTATIONS = [
      "(d_hi == d_lo)", [P.check_encode_bf16_exhaustive]),
     ("bf16 truncated", "up = finite & ((d_hi < d_lo)", "up = finite & ((d_hi < -1.0)",
      [P.check_encode_bf16_exhaustive]),
-    ("fold multiplies by s", "q = decode(a, dtype) / np.asarray(d32", "q = decode(a, dtype) * np.asarray(d32",
+    ("fold multiplies by s", "q = decode(a, dtype) / np.asarray(d32",
+     "q = decode(a, dtype) * np.asarray(d32",
      [P.check_fold_norm, P.check_fold_linear]),
     ("norm bias not folded", "b = None if beta is None else _divide_stored(beta, dtype, s)",
      "b = None if beta is None else np.asarray(beta)", [P.check_fold_norm]),
