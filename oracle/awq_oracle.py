@@ -33,8 +33,9 @@ project's design notes):
     squared difference of the quantised-and-folded layer's output from the
     exact output of the given inputs.
   * Ties in every argmin go to the lowest grid index.
-  * Packing: 8 four-bit codes per 32-bit word along the output dimension,
-    element 8j+i in bits 4i..4i+3; zeros packed the same way; scales fp16.
+  * Packing: codes packed densely along the output dimension from the lowest
+    bit up (4 bits: 8 per 32-bit word, element 8j+i in bits 4i..4i+3; 3 bits:
+    32 per 3 words); zeros packed the same way; scales fp16.
   * Linears that read the same input share one preceding operation, so they
     get one s: their weights are searched as one layer with the outputs
     concatenated, and the error is the mean over all of those outputs.
@@ -285,35 +286,45 @@ def search_clip(X, W, dtype, s32, ratios, bits=4, group=128, zero_point=True, ro
 # Step 8 — quantise and pack
 # ----------------------------------------------------------------------------
 
-def pack_nibbles(codes_kn: np.ndarray) -> np.ndarray:
-    """[R, C] codes in [0, 15] -> [R, C/8] int32; element 8j+i in bits 4i..4i+3."""
-    R, C = codes_kn.shape
-    c = codes_kn.astype(np.uint32).reshape(R, C // 8, 8)
-    word = np.zeros((R, C // 8), dtype=np.uint32)
-    for i in range(8):
-        word |= c[:, :, i] << np.uint32(4 * i)
-    return word.view(np.int32)
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """[R, C] codes of ``bits`` bits -> [R, C·bits/32] int32, packed densely
+    along each row from the lowest bit up: element c occupies bits
+    bits·c .. bits·c + bits - 1 of the row's little-endian bit stream, so a
+    code may straddle two words. For 4 bits this is 8 codes per word, element
+    8j+i in bits 4i..4i+3 of word j, as [roadmap] §5 prints; 3 bits fill
+    3 words with 32 codes."""
+    R, C = codes.shape
+    if (C * bits) % 32:
+        raise ValueError("a row must fill whole 32-bit words")
+    v = codes.astype(np.uint64)
+    out = np.zeros((R, C * bits // 32), dtype=np.uint64)
+    for c in range(C):
+        w, b = divmod(bits * c, 32)
+        out[:, w] |= (v[:, c] << np.uint64(b)) & np.uint64(0xFFFFFFFF)
+        if b + bits > 32:
+            out[:, w + 1] |= v[:, c] >> np.uint64(32 - b)
+    return out.astype(np.uint32).view(np.int32)
 
 
 def quantize_pack(W, dtype, s32, ratio=None, bits=4, group=128, zero_point=True):
-    """Packed 4-bit layer in the AWQ storage layout ([roadmap] §5).
+    """Packed layer in the AWQ storage layout ([roadmap] §5), 4 or 3 bits.
 
-    qweight [K, N/8] int32 (input-major, 8 codes per word along the output
-    dim), qzeros [K/g, N/8] int32 packed the same way, scales [K/g, N] fp16
+    qweight [K, N·b/32] int32 (input-major, codes packed along the output
+    dim), qzeros [K/g, N·b/32] int32 packed the same way, scales [K/g, N] fp16
     bits (RNE of the float32 step). The codes represent W·diag(s), clipped by
     ``ratio`` per row; the caller folds diag(s)^-1 into the preceding
     operation. Returns (qweight, qzeros, scales_u16, overflow_flag).
     """
-    if bits != 4:
-        raise ValueError("packing is defined for 4-bit codes")
+    if bits not in (3, 4):
+        raise ValueError("packing is defined for 3- and 4-bit codes")
     w = decode(W, dtype)
     N, K = w.shape
-    if N % 8:
-        raise ValueError("N must be a multiple of 8")
+    if (N * bits) % 32:
+        raise ValueError("N·bits must be a multiple of 32")
     r = np.ones(N, dtype=F32) if ratio is None else np.asarray(ratio, dtype=F32)
     q, step, zero = quantize(w, s32, r, bits, group, zero_point)
-    qweight = pack_nibbles(np.ascontiguousarray(q.T))
-    qzeros = pack_nibbles(np.ascontiguousarray(zero.astype(np.uint8).T))
+    qweight = pack_codes(np.ascontiguousarray(q.T), bits)
+    qzeros = pack_codes(np.ascontiguousarray(zero.astype(np.uint8).T), bits)
     with np.errstate(over="ignore"):
         sc = step.T.astype(np.float16)
     overflow = bool(~np.isfinite(sc).all())

@@ -134,24 +134,25 @@ def _random_weights(N, K, seed, one_signed_row=True):
 
 def check_codes_nearest_bruteforce(O):
     """Each code is the nearest point of its group's grid {(c - zero)·step}, over
-    every c in [0, 2^b - 1] (exact .5 cases, where RNE decides, are skipped);
+    every c in [0, 2^b - 1], for groups of 32, 64 and 128 channels (exact .5
+    cases, where RNE decides, are skipped);
     codes and zeros stay in range; at r = 1 every scaled weight is within half
     a step of its reconstruction; the step spans the group's range."""
     N, K = 4, 256
     w = _random_weights(N, K, 3)
     s = (np.exp(_rng(4).uniform(-1.5, 1.5, size=K))).astype(F32)
-    for bits, zp, r in itertools.product((3, 4), (True, False), (1.0, 0.7)):
+    for bits, zp, r, gs in itertools.product((3, 4), (True, False), (1.0, 0.7), (32, 64, 128)):
         qmax = 2 ** bits - 1
         ratio = np.full(N, F32(r))
-        q, step, zero = O.quantize(w, s, ratio, bits, 128, zp)
-        assert q.shape == (N, K) and step.shape == (N, K // 128) and zero.shape == step.shape
+        q, step, zero = O.quantize(w, s, ratio, bits, gs, zp)
+        assert q.shape == (N, K) and step.shape == (N, K // gs) and zero.shape == step.shape
         assert q.max() <= qmax and zero.min() >= 0 and zero.max() <= qmax
         wp = (w * s[None, :]).astype(F32).astype(np.float64)
         for n in range(N):
-            for g in range(K // 128):
+            for g in range(K // gs):
                 d, z = float(step[n, g]), float(zero[n, g])
                 grid = (np.arange(qmax + 1) - z) * d
-                blk = wp[n, g * 128:(g + 1) * 128]
+                blk = wp[n, g * gs:(g + 1) * gs]
                 lo = min(0.0, blk.min()) * r
                 hi = max(0.0, blk.max()) * r
                 if zp:
@@ -165,9 +166,9 @@ def check_codes_nearest_bruteforce(O):
                     if abs(pre - math.floor(pre) - 0.5) < 1e-6:
                         continue
                     best = int(np.argmin(np.abs(v - grid)))
-                    assert int(q[n, g * 128 + i]) == best, (bits, zp, r, n, g, i)
+                    assert int(q[n, g * gs + i]) == best, (bits, zp, r, gs, n, g, i)
                     if r == 1.0:
-                        assert abs(v - grid[q[n, g * 128 + i]]) <= d / 2 * (1 + 2 ** -20)
+                        assert abs(v - grid[q[n, g * gs + i]]) <= d / 2 * (1 + 2 ** -20)
 
 
 def check_power_of_two_rescale(O):
@@ -545,6 +546,77 @@ def check_fold_linear(O):
     assert np.array_equal(synth.bf16_bits_to_f32(wb2), synth.bf16_bits_to_f32(wb) * F32(2))
 
 
+# ----------------------------------------------------------------------------
+# 3-bit packing and group sizes
+# ----------------------------------------------------------------------------
+
+def _unpack_bits_python(words_row, bits, count):
+    """Pure-Python reading of a packed row: element c from bits bits·c.. of the
+    little-endian stream of 32-bit words."""
+    stream = 0
+    for i, w in enumerate(words_row):
+        stream |= (int(w) & 0xFFFFFFFF) << (32 * i)
+    return [(stream >> (bits * c)) & ((1 << bits) - 1) for c in range(count)]
+
+
+def check_pack_int3_layout(O):
+    """3-bit codes, worked by hand: 32 codes fill 3 words; element 10 (bits
+    30-32) and element 21 (bits 63-65) straddle words; all-7 codes give three
+    all-ones words. A packed layer unpacks to its codes and zeros, and its
+    storage is 3 + (16 + 3)/g bits per weight."""
+    row = np.zeros((1, 32), np.uint8)
+    row[0, 10] = 0b101
+    assert [int(x) & 0xFFFFFFFF for x in O.pack_codes(row, 3)[0]] == [0x40000000, 0x1, 0x0]
+    row[0, 10] = 0
+    row[0, 21] = 0b011
+    assert [int(x) & 0xFFFFFFFF for x in O.pack_codes(row, 3)[0]] == [0x0, 0x80000000, 0x1]
+    row[:] = 7
+    assert [int(x) & 0xFFFFFFFF for x in O.pack_codes(row, 3)[0]] == [0xFFFFFFFF] * 3
+    row = np.arange(32, dtype=np.uint8)[None, :] % 8          # 0..7 repeated
+    # codes 0..7 then again: bits 0-23 hold 0o76543210 read from the top
+    assert int(O.pack_codes(row, 3)[0, 0]) & 0x00FFFFFF == int("76543210", 8)
+    for gs in (32, 64, 128):
+        N, K = 64, 256
+        W = synth.make_weight(N, K, 0.02, "bf16", seed=60 + gs)
+        w = synth.bf16_bits_to_f32(W)
+        s = (np.exp(_rng(61).uniform(-1, 1, size=K))).astype(F32)
+        ratio = _rng(62).choice(synth.ratio_grid(), size=N).astype(F32)
+        qw, qz, sc, ovf = O.quantize_pack(W, "bf16", s, ratio, 3, gs, True)
+        q, step, zero = O.quantize(w, s, ratio, 3, gs, True)
+        assert qw.shape == (K, N * 3 // 32) and qz.shape == (K // gs, N * 3 // 32)
+        assert sc.shape == (K // gs, N) and not ovf
+        for k in (0, 1, K // 2, K - 1):
+            assert _unpack_bits_python(qw[k], 3, N) == [int(v) for v in q[:, k]]
+        for g in range(K // gs):
+            assert _unpack_bits_python(qz[g], 3, N) == [int(v) for v in zero[:, g]]
+        assert np.array_equal(sc, step.T.astype(np.float16).view(np.uint16))
+        bpw = 8 * (qw.nbytes + qz.nbytes + sc.nbytes) / (N * K)
+        assert bpw == 3 + (16 + 3) / gs == O.storage_bits_per_weight(N, K, 3, gs)
+    # the 4-bit layout through the general packer: element 8j+i in bits 4i..4i+3
+    row4 = np.arange(16, dtype=np.uint8)[None, :]
+    assert [int(x) & 0xFFFFFFFF for x in O.pack_codes(row4, 4)[0]] == [0x76543210, 0xFEDCBA98]
+
+
+def check_group_size_gain(O):
+    """[concept] "When it breaks": smaller groups already absorb part of what
+    the scaling buys, so its gain narrows. Measured as the absolute error
+    reduction mse(α = 0) - min_α mse(α) on an outlier layer, it shrinks from
+    group 128 to 64 to 32, while the best error itself improves with smaller
+    groups. (The relative reduction does not narrow on Gaussian weights; see
+    the design notes.)"""
+    X, W = synth.make_custom(256, 64, 1024, "bf16", n_out=10, seed=1)
+    ab = O.act_stats(X, "bf16")
+    al = synth.alpha_grid(11)
+    gain, best = {}, {}
+    for gs in (32, 64, 128):
+        r = O.search_scale(X, W, "bf16", ab, al, 4, gs, True)
+        gain[gs] = r["mse"][0] - r["mse"].min()
+        best[gs] = r["mse"].min()
+        assert 0 < r["index"] < len(al) - 1
+    assert gain[32] < gain[64] < gain[128], gain
+    assert best[32] < best[64] < best[128], best
+
+
 ALL_CHECKS = [
     check_stats_closed_form, check_stats_exact_sum, check_scale_closed_form,
     check_scale_dead_channel, check_quant_worked_examples, check_codes_nearest_bruteforce,
@@ -552,5 +624,6 @@ ALL_CHECKS = [
     check_gram_identity, check_search_scale_bruteforce, check_search_clip_bruteforce,
     check_monotone_and_separable, check_outlier_behaviour, check_pack_layout,
     check_pack_overflow_flag, check_search_group, check_encode_bf16_exhaustive,
-    check_encode_f16_examples, check_fold_norm, check_fold_linear,
+    check_encode_f16_examples, check_fold_norm, check_fold_linear, check_pack_int3_layout,
+    check_group_size_gain,
 ]

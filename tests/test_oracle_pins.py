@@ -64,10 +64,15 @@ MUTATIONS = [
                                             P.check_monotone_and_separable]),
     ("clip picks the worst ratio", "idx = np.argmin(row_sums, axis=0)",
      "idx = np.argmax(row_sums, axis=0)", [P.check_search_clip_bruteforce]),
-    ("nibbles in reverse order", "word |= c[:, :, i] << np.uint32(4 * i)",
-     "word |= c[:, :, i] << np.uint32(28 - 4 * i)", [P.check_pack_layout]),
-    ("codes packed along the input dim", "pack_nibbles(np.ascontiguousarray(q.T))",
-     "pack_nibbles(np.ascontiguousarray(q))", [P.check_pack_layout]),
+    ("codes packed from the top bit down", "w, b = divmod(bits * c, 32)",
+     "w, b = divmod(bits * c, 32); b = 32 - bits - b if b + bits <= 32 else b",
+     [P.check_pack_layout, P.check_pack_int3_layout]),
+    ("codes packed along the input dim", "qweight = pack_codes(np.ascontiguousarray(q.T), bits)",
+     "qweight = pack_codes(np.ascontiguousarray(q), bits)", [P.check_pack_layout]),
+    ("straddling 3-bit codes lose their high bits", "        if b + bits > 32:\n",
+     "        if False:\n", [P.check_pack_int3_layout]),
+    ("group size ignored by the quantiser", "    G = K // group\n",
+     "    group = 128\n    G = K // group\n", [P.check_codes_nearest_bruteforce]),
     ("group searched on its first layer only",
      "W = np.concatenate([np.asarray(w) for w in Ws], axis=0)", "W = np.asarray(Ws[0])",
      [P.check_search_group]),
