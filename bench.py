@@ -75,8 +75,8 @@ def cpu_baseline(cfg, X, Ws, alphas, rows_n: int):
     t0 = time.perf_counter()
     ab = O.act_stats(X, cfg.dtype)
     t1 = time.perf_counter()
-    res = O.search_scale_group(X, Ws, cfg.dtype, ab, alphas, cfg.bits, 128, cfg.zero_point,
-                               rows=rows)
+    res = O.search_scale_group(X, Ws, cfg.dtype, ab, alphas, cfg.bits, cfg.group,
+                               cfg.zero_point, rows=rows)
     t2 = time.perf_counter()
     if cfg.layers:
         from post_weight_quantization_26_amd import synth
@@ -84,7 +84,8 @@ def cpu_baseline(cfg, X, Ws, alphas, rows_n: int):
                     res["s_best"])
     if cfg.pack:
         for W in Ws:
-            O.quantize_pack(W, cfg.dtype, res["s_best"], None, 4, 128, cfg.zero_point)
+            O.quantize_pack(W, cfg.dtype, res["s_best"], None, cfg.bits, cfg.group,
+                            cfg.zero_point)
     pack_t = time.perf_counter() - t2
     step = (t1 - t0) + (t2 - t1) * cfg.N / len(rows) + pack_t
     return {"value": len(alphas) / step, "unit": "alpha-candidates/s", "cores": int(threads),
@@ -139,9 +140,10 @@ def main():
                             dtype=torch.uint8, device=dev)
     ws_pack = torch.empty(256, dtype=torch.uint8, device=dev)
     abar = torch.empty(K, dtype=torch.float32, device=dev)
-    pack_out = [(torch.empty((K, Wd.shape[0] // 8), dtype=torch.int32, device=dev),
-                 torch.empty((K // 128, Wd.shape[0] // 8), dtype=torch.int32, device=dev),
-                 torch.empty((K // 128, Wd.shape[0]), dtype=torch.float16, device=dev))
+    G = cfg.group
+    pack_out = [(torch.empty((K, Wd.shape[0] * cfg.bits // 32), dtype=torch.int32, device=dev),
+                 torch.empty((K // G, Wd.shape[0] * cfg.bits // 32), dtype=torch.int32, device=dev),
+                 torch.empty((K // G, Wd.shape[0]), dtype=torch.float16, device=dev))
                 for Wd in Wds]
     zp = cfg.zero_point
 
@@ -150,19 +152,20 @@ def main():
         if cfg.layers:
             # linears sharing X: one search, one s, folded into the norm weight
             # (in place, so gamma drifts over the steps; the work is the same)
-            res = api.search_scale_group(Xd, Wds, abar, alphas, bits=cfg.bits, zero_point=zp,
-                                         ws=ws_search)
+            res = api.search_scale_group(Xd, Wds, abar, alphas, bits=cfg.bits, group=G,
+                                         zero_point=zp, ws=ws_search)
             api.fold_norm(gamma, res["s_best"])
         else:
-            res = api.search_scale(Xd, Wds[0], abar, alphas, bits=cfg.bits, zero_point=zp,
-                                   ws=ws_search)
+            res = api.search_scale(Xd, Wds[0], abar, alphas, bits=cfg.bits, group=G,
+                                   zero_point=zp, ws=ws_search)
         for Wd, out in zip(Wds, pack_out):
             ratio = None
             if ratios is not None:
-                ratio = api.search_clip(Xd, Wd, res["s_best"], ratios, bits=cfg.bits,
+                ratio = api.search_clip(Xd, Wd, res["s_best"], ratios, bits=cfg.bits, group=G,
                                         zero_point=zp, ws=ws_search)["ratio_best"]
             if cfg.pack:
-                api.quantize_pack(Wd, res["s_best"], ratio, zero_point=zp, ws=ws_pack, out=out)
+                api.quantize_pack(Wd, res["s_best"], ratio, bits=cfg.bits, group=G, zero_point=zp,
+                                  ws=ws_pack, out=out)
         return res
 
     for _ in range(args.warmup):
@@ -194,7 +197,8 @@ def main():
     stats_ms, stats_n = prof["stats"]
     stats_gbs = (T * K * X.itemsize) / (stats_ms / 1e3 / max(stats_n, 1)) / 1e9 if stats_n else None
     pack_ms, pack_n = prof["pack"]
-    pack_bytes = (N * K * X.itemsize + N * K // 2 + (N * K // 128) * (2 + 0.5) + K * 4) / len(Ws)
+    pack_bytes = (N * K * X.itemsize + N * K * cfg.bits / 8
+                  + (N * K / cfg.group) * (2 + cfg.bits / 8) + K * 4) / len(Ws)
     pack_gbs = pack_bytes / (pack_ms / 1e3 / max(pack_n, 1)) / 1e9 if pack_n else None
 
     out = {
@@ -211,7 +215,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": name, "T": T, "N": N, "K": K, "group": 128, "bits": cfg.bits,
+        "config": {"workload": name, "T": T, "N": N, "K": K, "group": cfg.group, "bits": cfg.bits,
                    "zero_point": zp, "n_alpha": cfg.n_alpha, "n_ratio": cfg.n_ratio,
                    "pack": cfg.pack, "layers": list(cfg.layers) or None},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
@@ -226,6 +230,8 @@ def main():
                 "peak_GBps": HBM_PEAK_GBS},
         "kernels": kernels,
         "alpha_best": float(res["alpha_best"]),
+        "mse_alpha0": float(res["mse"][0]),
+        "mse_best": float(res["mse"].min()),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, X, Ws, alphas, args.cpu_rows)

@@ -10,7 +10,7 @@
  *                      fold diag(s)^-1 back, measure the output MSE against
  *                      the unquantised product; return the curve and argmin
  *   awq_search_clip    per-output-channel clip ratio search with s fixed
- *   awq_quantize_pack  INT4 codes, packed zeros and fp16 scales
+ *   awq_quantize_pack  INT4 or INT3 codes, packed zeros and fp16 scales
  *   awq_search_scale_group  the α search for several linears that read the
  *                      same X and so share one s
  *   awq_fold_norm, awq_fold_linear  divide the operation that produces X by
@@ -38,8 +38,8 @@
  *     outputs synchronise `stream` before returning; the others do not.
  *   - Arguments are validated on the host before anything is enqueued. A
  *     failed check returns a negative status and launches nothing.
- *     X and W must be 16-byte aligned; K must be a multiple of the group
- *     size (128); grids hold 1..64 values.
+ *     X and W must be 16-byte aligned; K must be a multiple of 128 (for
+ *     every group size); grids hold 1..64 values.
  *   - Quantiser arithmetic is IEEE float32 with round-to-nearest-even, one
  *     rounding per operation (no contraction, no flush of denormals):
  *       w' = w·s_j; mx = r·max(0, max_G w'); mn = r·min(0, min_G w')
@@ -47,7 +47,8 @@
  *                   zero = clamp(rint(-mn/step), 0, 2^b-1)
  *       symmetric:  step = max(max(mx,-mn)/(2^(b-1)-1), 1e-5); zero = 2^(b-1)
  *       code = clamp(rint(w'/step) + zero, 0, 2^b-1)
- *     Groups are 128 consecutive input channels of one output row.
+ *     Groups are g consecutive input channels of one output row, g = 32, 64
+ *     or 128 (AutoAWQ's q_group_size; 128 in the pages' configuration).
  *   - Errors never abort: a non-zero status is returned and
  *     awq_last_error() describes it (per calling thread).
  *   - Calls are thread-compatible: concurrent calls must use distinct
@@ -74,7 +75,7 @@ typedef enum {
 
 typedef enum { AWQ_F32 = 0, AWQ_BF16 = 1, AWQ_F16 = 2 } awq_dtype;
 
-/* Quantiser parameters. w_bit: 4 or 3 (packing: 4 only). group_size: 128.
+/* Quantiser parameters. w_bit: 4 or 3. group_size: 32, 64 or 128.
  * zero_point: 1 = asymmetric min-max with an integer zero point,
  * 0 = symmetric (zero point fixed at 2^(w_bit-1)). */
 typedef struct {
@@ -138,11 +139,17 @@ awq_status awq_search_clip(const void* X, const void* W, awq_dtype dtype, int64_
                            awq_qconfig qc, float* ratio_best, double* mse_clip, double* row_sums,
                            void* ws, size_t ws_bytes, void* stream);
 
-/* Step 8 — quantise W·diag(s) (rows clipped by `ratio`, NULL = 1) and pack.
- * W [N, K] (bf16, f16 or f32), N a multiple of 8, w_bit 4.
- * qweight [K, N/8] int32: word (k, j) holds the codes of rows 8j..8j+7 at
- * column k, row 8j+i in bits 4i..4i+3. qzeros [K/128, N/8] int32 packed the
- * same way. scales [K/128, N] IEEE fp16 bits (RNE of the f32 step).
+/* Step 8 — quantise W·diag(s) (rows clipped by `ratio`, NULL = 1) and pack
+ * ("05 — AWQ", section 5 "Bit-level output format").
+ * W [N, K] (bf16, f16 or f32); b = w_bit (4 or 3); g = group_size.
+ * Codes are packed densely along the output dim from the lowest bit up: in
+ * row k of qweight [K, N·b/32] int32, the code of output row n occupies bits
+ * b·n .. b·n+b-1 of the little-endian stream of the row's words. For b = 4
+ * (N a multiple of 8) word (k, j) holds rows 8j..8j+7, row 8j+i in bits
+ * 4i..4i+3, the pages' layout; for b = 3 (N a multiple of 32) 32 rows fill
+ * 3 words and rows 10 and 21 of each 32 straddle two words.
+ * qzeros [K/g, N·b/32] int32 packed the same way. scales [K/g, N] IEEE fp16
+ * bits (RNE of the f32 step).
  * The codes represent W·diag(s); the caller folds diag(s)^-1 into the
  * operation that produces X. ws: at least awq_workspace_bytes(AWQ_OP_PACK,...).
  * Synchronises `stream`; returns AWQ_E_RANGE if a scale overflowed fp16. */

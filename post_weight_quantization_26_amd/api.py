@@ -207,14 +207,17 @@ def quantize_pack(W: torch.Tensor, s: torch.Tensor, ratio: Optional[torch.Tensor
                   bits: int = DEFAULT_BITS, group: int = DEFAULT_GROUP,
                   zero_point: bool = DEFAULT_ZERO_POINT, ws: Optional[torch.Tensor] = None,
                   out=None):
-    """Packed layer: qweight [K, N/8] int32, qzeros [K/g, N/8] int32, scales [K/g, N] float16."""
+    """Packed layer: qweight [K, N·b/32] int32, qzeros [K/g, N·b/32] int32,
+    scales [K/g, N] float16 (b = bits, 4 or 3; codes packed densely along the
+    output dim, lowest bits first)."""
     _dev(W, "W"), _dev(s, "s")
     if ratio is not None:
         _dev(ratio, "ratio")
     N, K = W.shape
     if out is None:
-        qweight = torch.empty((K, N // 8), dtype=torch.int32, device=W.device)
-        qzeros = torch.empty((K // group, N // 8), dtype=torch.int32, device=W.device)
+        nw = N * int(bits) // 32
+        qweight = torch.empty((K, nw), dtype=torch.int32, device=W.device)
+        qzeros = torch.empty((K // group, nw), dtype=torch.int32, device=W.device)
         scales = torch.empty((K // group, N), dtype=torch.float16, device=W.device)
     else:
         qweight, qzeros, scales = out

@@ -18,8 +18,8 @@ hipError_t launch_reciprocal(const float* s, int64_t n, float* s_copy, float* in
                              hipStream_t st);
 hipError_t launch_transform(const void* W, int dtype, int64_t N, int64_t K, const float* s_rows,
                             const float* inv_rows, int64_t s_stride, const float* ratios_host,
-                            int nc, int bits, int zero_point, void* E, int64_t cand_stride,
-                            hipStream_t st);
+                            int nc, int bits, int group, int zero_point, void* E,
+                            int64_t cand_stride, hipStream_t st);
 hipError_t launch_search_gemm(const void* X, int dtype, const void* E, int64_t M, int64_t Nc,
                               int64_t K, float* partials, hipStream_t st);
 hipError_t launch_reduce_rows(const float* partials, int64_t MT, int64_t Nc, double* row_sums,
@@ -30,8 +30,8 @@ hipError_t launch_clip_select(const double* row_sums, int n_ratio, int64_t N,
                               const float* ratios_host, double denom, float* ratio_best,
                               double* best, double* mse_clip, hipStream_t st);
 hipError_t launch_pack(const void* W, int dtype, int64_t N, int64_t K, const float* s,
-                       const float* ratio, int zero_point, int32_t* qweight, int32_t* qzeros,
-                       uint16_t* scales, int* overflow, hipStream_t st);
+                       const float* ratio, int bits, int group, int zero_point, int32_t* qweight,
+                       int32_t* qzeros, uint16_t* scales, int* overflow, hipStream_t st);
 hipError_t launch_fold_vec(void* v, int dtype, int64_t K, const float* s, hipStream_t st);
 hipError_t launch_fold_rows(void* W, int dtype, int64_t K, int64_t K_prev, const float* s,
                             hipStream_t st);
@@ -128,8 +128,8 @@ awq_status run_batch(const void* X, const Segment* seg, int n_seg, awq_dtype d, 
     AWQ_HIP(timed(AWQ_K_TRANSFORM, st,
                   [&] {
                     return launch_transform(seg[l].W, dt(d), seg[l].N, K, s_rows, inv_rows,
-                                            s_stride, ratios_host, cb, qc.w_bit, qc.zero_point,
-                                            E_l, N * K, st);
+                                            s_stride, ratios_host, cb, qc.w_bit, qc.group_size,
+                                            qc.zero_point, E_l, N * K, st);
                   }),
             "transform");
   }
@@ -314,8 +314,8 @@ extern "C" awq_status awq_quantize_pack(const void* W, awq_dtype w_dtype, int64_
   AWQ_HIP(hipMemsetAsync(flag, 0, sizeof(int), st), "clear overflow flag");
   AWQ_HIP(timed(AWQ_K_PACK, st,
                 [&] {
-                  return launch_pack(W, dt(w_dtype), N, K, s, ratio, qc.zero_point, qweight,
-                                     qzeros, scales, flag, st);
+                  return launch_pack(W, dt(w_dtype), N, K, s, ratio, qc.w_bit, qc.group_size,
+                                     qc.zero_point, qweight, qzeros, scales, flag, st);
                 }),
           "pack");
   int host_flag = 0;

@@ -10,7 +10,7 @@
 
 namespace awq {
 
-constexpr int kGroup = 128;
+constexpr int kTileK = 128;   // K must be a multiple of this (search GEMM and pack tiles)
 constexpr int kMaxGrid = 64;
 constexpr int kMaxLayers = 16;     // linears searched together on one shared input
 constexpr int kGemmBM_bf16 = 256;  // token rows per search-GEMM tile (bf16 MFMA path)

@@ -20,8 +20,8 @@ hipError_t launch_reciprocal(const float* s, int64_t n, float* s_copy, float* in
 // element c·cand_stride of E.
 hipError_t launch_transform(const void* W, int dtype, int64_t N, int64_t K, const float* s_rows,
                             const float* inv_rows, int64_t s_stride, const float* ratios_host,
-                            int nc, int bits, int zero_point, void* E, int64_t cand_stride,
-                            hipStream_t st);
+                            int nc, int bits, int group, int zero_point, void* E,
+                            int64_t cand_stride, hipStream_t st);
 // In-place fold of 1/s: v[j] /= s[j] (j < K); rows of W [K, K_prev] /= s[row].
 hipError_t launch_fold_vec(void* v, int dtype, int64_t K, const float* s, hipStream_t st);
 hipError_t launch_fold_rows(void* W, int dtype, int64_t K, int64_t K_prev, const float* s,
@@ -37,8 +37,8 @@ hipError_t launch_clip_select(const double* row_sums, int n_ratio, int64_t N,
                               const float* ratios_host, double denom, float* ratio_best,
                               double* best, double* mse_clip, hipStream_t st);
 hipError_t launch_pack(const void* W, int dtype, int64_t N, int64_t K, const float* s,
-                       const float* ratio, int zero_point, int32_t* qweight, int32_t* qzeros,
-                       uint16_t* scales, int* overflow, hipStream_t st);
+                       const float* ratio, int bits, int group, int zero_point, int32_t* qweight,
+                       int32_t* qzeros, uint16_t* scales, int* overflow, hipStream_t st);
 
 // Grid values travel to kernels by value.
 struct GridArgs {

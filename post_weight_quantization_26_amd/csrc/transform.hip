@@ -51,8 +51,9 @@ __device__ __forceinline__ void store8<0>(void* E, int64_t idx, const float (&e)
   p[1] = make_float4(e[4], e[5], e[6], e[7]);
 }
 
-// DT: 0 = f32 (E in f32), 1 = bf16 (E in bf16).
-template <int DT>
+// DT: 0 = f32 (E in f32), 1 = bf16 (E in bf16). G: group size (32, 64, 128);
+// the G/8 lanes of a group reduce its range.
+template <int DT, int G>
 __global__ __launch_bounds__(kThreads) void transform_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s_rows,
     const float* __restrict__ inv_rows, int64_t s_stride, GridArgs ratios, int has_ratio, int nc,
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void transform_kernel(
 #pragma clang fp contract(off)
   const int64_t NK = N * K;
   const int64_t e0 = (int64_t(blockIdx.x) * kThreads + threadIdx.x) * 8;  // flat n*K + k
-  // NK is a multiple of 128, so the 16 lanes of a group are all in range or all out.
+  // NK is a multiple of 128, so the lanes of a group are all in range or all out.
   const bool active = e0 < NK;
   const int64_t k = active ? e0 % K : 0;
 
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void transform_kernel(
       mn = fminf(mn, wp[i]);
     }
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
+    for (int off = 1; off < G / 8; off <<= 1) {
       mx = fmaxf(mx, __shfl_xor(mx, off));
       mn = fminf(mn, __shfl_xor(mn, off));
     }
@@ -105,26 +106,42 @@ __global__ __launch_bounds__(kThreads) void transform_kernel(
   }
 }
 
+template <int DT>
+hipError_t launch_transform_g(int group, unsigned blocks, hipStream_t st, const void* W, int64_t N,
+                              int64_t K, const float* s_rows, const float* inv_rows,
+                              int64_t s_stride, const GridArgs& g, int has_ratio, int nc,
+                              int bits, int zero_point, void* E, int64_t cand_stride) {
+  if (group == 32)
+    transform_kernel<DT, 32><<<blocks, kThreads, 0, st>>>(W, N, K, s_rows, inv_rows, s_stride, g,
+                                                          has_ratio, nc, bits, zero_point, E,
+                                                          cand_stride);
+  else if (group == 64)
+    transform_kernel<DT, 64><<<blocks, kThreads, 0, st>>>(W, N, K, s_rows, inv_rows, s_stride, g,
+                                                          has_ratio, nc, bits, zero_point, E,
+                                                          cand_stride);
+  else
+    transform_kernel<DT, 128><<<blocks, kThreads, 0, st>>>(W, N, K, s_rows, inv_rows, s_stride,
+                                                           g, has_ratio, nc, bits, zero_point, E,
+                                                           cand_stride);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_transform(const void* W, int dtype, int64_t N, int64_t K, const float* s_rows,
                             const float* inv_rows, int64_t s_stride, const float* ratios_host,
-                            int nc, int bits, int zero_point, void* E, int64_t cand_stride,
-                            hipStream_t st) {
+                            int nc, int bits, int group, int zero_point, void* E,
+                            int64_t cand_stride, hipStream_t st) {
   GridArgs g{};
   const int has_ratio = ratios_host != nullptr;
   for (int i = 0; i < nc && i < 64; ++i) g.v[i] = has_ratio ? ratios_host[i] : 1.f;
   const int64_t lanes = N * K / 8;
   const unsigned blocks = unsigned((lanes + kThreads - 1) / kThreads);
   if (dtype == 1)
-    transform_kernel<1><<<blocks, kThreads, 0, st>>>(W, N, K, s_rows, inv_rows, s_stride, g,
-                                                     has_ratio, nc, bits, zero_point, E,
-                                                     cand_stride);
-  else
-    transform_kernel<0><<<blocks, kThreads, 0, st>>>(W, N, K, s_rows, inv_rows, s_stride, g,
-                                                     has_ratio, nc, bits, zero_point, E,
-                                                     cand_stride);
-  return hipGetLastError();
+    return launch_transform_g<1>(group, blocks, st, W, N, K, s_rows, inv_rows, s_stride, g,
+                                 has_ratio, nc, bits, zero_point, E, cand_stride);
+  return launch_transform_g<0>(group, blocks, st, W, N, K, s_rows, inv_rows, s_stride, g,
+                               has_ratio, nc, bits, zero_point, E, cand_stride);
 }
 
 }  // namespace awq

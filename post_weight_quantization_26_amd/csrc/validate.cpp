@@ -95,12 +95,12 @@ awq_status check_scale_table(const float* abar, int64_t K, const float* alphas, 
   return AWQ_OK;
 }
 
-static awq_status check_qconfig(awq_qconfig qc, bool pack) {
-  if (qc.group_size != kGroup)
-    return set_error(AWQ_E_UNSUPPORTED, "group_size %d not supported (128 only)", qc.group_size);
-  if (pack ? qc.w_bit != 4 : (qc.w_bit != 3 && qc.w_bit != 4))
-    return set_error(AWQ_E_UNSUPPORTED, "w_bit %d not supported here (%s)", qc.w_bit,
-                     pack ? "pack: 4" : "search: 3 or 4");
+static awq_status check_qconfig(awq_qconfig qc) {
+  if (qc.group_size != 32 && qc.group_size != 64 && qc.group_size != 128)
+    return set_error(AWQ_E_UNSUPPORTED, "group_size %d not supported (32, 64 or 128)",
+                     qc.group_size);
+  if (qc.w_bit != 3 && qc.w_bit != 4)
+    return set_error(AWQ_E_UNSUPPORTED, "w_bit %d not supported (3 or 4)", qc.w_bit);
   if (qc.zero_point != 0 && qc.zero_point != 1)
     return set_error(AWQ_E_INVALID, "zero_point must be 0 or 1");
   return AWQ_OK;
@@ -119,11 +119,10 @@ awq_status check_search(int op, const void* X, const void* W, awq_dtype d, int64
   if (T < 1 || N < 1 || K < 1 || T > kMaxDim || N > kMaxDim || K > kMaxDim)
     return set_error(AWQ_E_INVALID, "%s: bad shape T=%lld N=%lld K=%lld", nm, (long long)T,
                      (long long)N, (long long)K);
-  awq_status st = check_qconfig(qc, false);
+  awq_status st = check_qconfig(qc);
   if (st != AWQ_OK) return st;
-  if (K % qc.group_size)
-    return set_error(AWQ_E_INVALID, "%s: K=%lld is not a multiple of the group size", nm,
-                     (long long)K);
+  if (K % kTileK)
+    return set_error(AWQ_E_INVALID, "%s: K=%lld is not a multiple of 128", nm, (long long)K);
   if (n_grid < 1 || n_grid > kMaxGrid)
     return set_error(AWQ_E_INVALID, "%s: grid size %d outside 1..%d", nm, n_grid, kMaxGrid);
   for (int i = 0; i < n_grid; ++i) {
@@ -204,13 +203,14 @@ awq_status check_pack(const void* W, awq_dtype d, int64_t N, int64_t K, const fl
   if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim)
     return set_error(AWQ_E_INVALID, "quantize_pack: bad shape N=%lld K=%lld", (long long)N,
                      (long long)K);
-  awq_status st = check_qconfig(qc, true);
+  awq_status st = check_qconfig(qc);
   if (st != AWQ_OK) return st;
-  if (N % 8) return set_error(AWQ_E_INVALID, "quantize_pack: N=%lld not a multiple of 8",
-                              (long long)N);
-  if (K % qc.group_size)
-    return set_error(AWQ_E_INVALID, "quantize_pack: K=%lld not a multiple of the group size",
-                     (long long)K);
+  const int64_t n_mult = qc.w_bit == 4 ? 8 : 32;   // rows that fill whole 32-bit words
+  if (N % n_mult)
+    return set_error(AWQ_E_INVALID, "quantize_pack: N=%lld not a multiple of %lld for %d-bit codes",
+                     (long long)N, (long long)n_mult, qc.w_bit);
+  if (K % kTileK)
+    return set_error(AWQ_E_INVALID, "quantize_pack: K=%lld not a multiple of 128", (long long)K);
   if (!aligned16(W) || !aligned4(qweight) || !aligned4(qzeros) || !aligned4(scales) ||
       !aligned4(s))
     return set_error(AWQ_E_INVALID, "quantize_pack: W must be 16-byte aligned, outputs 4-byte");

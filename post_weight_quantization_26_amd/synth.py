@@ -62,10 +62,17 @@ CONFIGS = {
     # Llama-7B MLP up projection with the clip search.
     "llama7b_mlp_up": LayerConfig("llama7b_mlp_up", 3, 65536, 11008, 4096, "bf16", 0.02, 41,
                                   20.0, 100.0, n_ratio=20, pack=True),
-    # Llama-7B MLP down projection, heavy-tailed post-activation inputs, INT3.
+    # Llama-7B MLP down projection, heavy-tailed post-activation inputs, INT3,
+    # packed 3-bit.
     "llama7b_mlp_down_int3": LayerConfig("llama7b_mlp_down_int3", 4, 65536, 4096, 11008, "bf16",
                                          0.02, 110, 10.0, 200.0, x_kind="abs_sign", bits=3,
-                                         n_ratio=20),
+                                         n_ratio=20, pack=True),
+    # The attention projection layer at group sizes 32 and 64 (same X and W
+    # as llama7b_attn_4096): the group-size comparison.
+    "llama7b_attn_4096_g64": LayerConfig("llama7b_attn_4096_g64", 2, 65536, 4096, 4096, "bf16",
+                                         0.02, 41, 20.0, 100.0, pack=True, group=64),
+    "llama7b_attn_4096_g32": LayerConfig("llama7b_attn_4096_g32", 2, 65536, 4096, 4096, "bf16",
+                                         0.02, 41, 20.0, 100.0, pack=True, group=32),
     # 70B-class MLP layer, asymmetric and symmetric INT4.
     "llama70b_mlp": LayerConfig("llama70b_mlp", 5, 32768, 28672, 8192, "bf16", 0.015, 82,
                                 20.0, 100.0, variants=(True, False), n_ratio=20, pack=True),

@@ -107,13 +107,13 @@ def _search(L, op, **kw):
 @pytest.mark.parametrize("op", ["scale", "clip"])
 def test_search_rejects(L, kw, status, op):
     if kw.get("qc", 0) is None:
-        kw = dict(kw, qc=L.QConfig(4, 64, 1))
+        kw = dict(kw, qc=L.QConfig(4, 16, 1))          # unsupported group size
     assert _search(L, op, **kw) == status
     assert L.last_error()
 
 
-@pytest.mark.parametrize("qc,status", [((5, 128, 1), -2), ((2, 128, 1), -2), ((4, 32, 1), -2),
-                                       ((4, 128, 2), -1)])
+@pytest.mark.parametrize("qc,status", [((5, 128, 1), -2), ((2, 128, 1), -2), ((4, 16, 1), -2),
+                                       ((4, 256, 1), -2), ((3, 48, 1), -2), ((4, 128, 2), -1)])
 def test_search_rejects_qconfig(L, qc, status):
     assert _search(L, "scale", qc=L.QConfig(*qc)) == status
 
@@ -151,7 +151,11 @@ def test_pack_rejects(L):
                         k.get("wsb", 4096), None]
     assert f(*args(N=12)) == -1                     # N % 8
     assert f(*args(K=200)) == -1                    # K % 128
-    assert f(*args(qc=L.QConfig(3, 128, 1))) == -2  # pack is 4-bit only
+    assert f(*args(K=192, qc=L.QConfig(4, 64, 1))) == -1     # K % 128 for every group size
+    assert f(*args(N=48, qc=L.QConfig(3, 128, 1))) == -1     # 3-bit rows fill words: N % 32
+    assert "multiple of 32" in L.last_error()
+    assert f(*args(qc=L.QConfig(2, 128, 1))) == -2
+    assert f(*args(qc=L.QConfig(4, 16, 1))) == -2
     assert f(*args(W=None)) == -1
     assert f(*args(W=MIS)) == -1
     assert f(*args(wsb=0)) == -3

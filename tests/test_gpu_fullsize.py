@@ -36,17 +36,18 @@ def run_config(api, name, variants=None, pack_check=True):
     rows = sample_rows(cfg.N)
     for zp in (variants or cfg.variants):
         res, ref, Xd, Wd = check_scale_search(api, X, W, cfg.dtype, synth.alpha_grid(cfg.n_alpha),
-                                              cfg.bits, zp, rows=rows)
+                                              cfg.bits, zp, rows=rows, group=cfg.group)
         s = ref["s_table"][res["index"]]
         ratio = None
         if cfg.n_ratio:
             c, cref = check_clip(api, Xd, Wd, X, W, cfg.dtype, s, synth.ratio_grid(cfg.n_ratio),
-                                 cfg.bits, zp, rows=rows)
+                                 cfg.bits, zp, rows=rows, group=cfg.group)
             ratio = c["ratio_best"]
         if cfg.pack and pack_check:
-            qw, qz, sc = api.quantize_pack(Wd, res["s_best"], ratio, zero_point=zp)
+            qw, qz, sc = api.quantize_pack(Wd, res["s_best"], ratio, bits=cfg.bits,
+                                           group=cfg.group, zero_point=zp)
             r_np = None if ratio is None else ratio.cpu().numpy()
-            assert_pack_parity(qw, qz, sc, W, cfg.dtype, s, r_np, zp)
+            assert_pack_parity(qw, qz, sc, W, cfg.dtype, s, r_np, zp, cfg.bits, cfg.group)
         del Xd, Wd
         torch.cuda.empty_cache()
 
@@ -61,8 +62,13 @@ def test_llama7b_mlp_up_full(api):
 
 
 def test_llama7b_mlp_down_int3_full(api):
-    # 4096 x 11008, heavy-tailed inputs, INT3 search and clip (no pack at 3 bits)
+    # 4096 x 11008, heavy-tailed inputs, INT3 search, clip and 3-bit pack
     run_config(api, "llama7b_mlp_down_int3")
+
+
+def test_llama7b_attn_4096_g32_full(api):
+    # the bench layer at group size 32: search and pack
+    run_config(api, "llama7b_attn_4096_g32")
 
 
 def test_llama70b_mlp_full(api):

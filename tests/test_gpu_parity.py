@@ -67,14 +67,14 @@ def assert_alpha_rule(gpu_idx, ref_mse):
         assert gpu_idx in order[:2]
 
 
-def model_E(w32, s32, ratio, bits, zp, dtype):
+def model_E(w32, s32, ratio, bits, zp, dtype, group=128):
     """Error weights as the search GEMM consumes them, from the oracle's codes
     and the kernel's float32 arithmetic: fl32(fl32(fl32((q - zero)·step) ·
     fl32(1/s)) - w), then one RNE rounding to the MFMA operand type (bf16;
     float32 inputs stay float32)."""
-    q, step, zero = O.quantize(w32, s32, ratio, bits, 128, zp)
+    q, step, zero = O.quantize(w32, s32, ratio, bits, group, zp)
     N, K = w32.shape
-    d = ((q.reshape(N, K // 128, 128).astype(np.float32) - zero[:, :, None]) * step[:, :, None])
+    d = ((q.reshape(N, K // group, group).astype(np.float32) - zero[:, :, None]) * step[:, :, None])
     inv_s = (np.float32(1.0) / s32.astype(np.float32)).astype(np.float32)
     e = (d.reshape(N, K) * inv_s[None, :]) - w32
     e = e.astype(np.float32)
@@ -90,7 +90,7 @@ def row_references(X, dtype, w_rows, cands, chunk=4096):
     float32 accumulation bound), each [n_cand, R]."""
     e64 = np.concatenate([O.candidate_weights(w_rows, s, r, *c) - w_rows.astype(np.float64)
                           for (s, r, c) in cands])
-    em = np.concatenate([model_E(w_rows, s, r, c[0], c[2], dtype) for (s, r, c) in cands])
+    em = np.concatenate([model_E(w_rows, s, r, c[0], c[2], dtype, c[1]) for (s, r, c) in cands])
     Rt, K = e64.shape
     M64, Mm, acc, acc2 = (np.zeros(Rt) for _ in range(4))
     aem = np.abs(em).T
@@ -118,14 +118,15 @@ def compare_rows(gpu_rows, M64, Mm, tol, what):
           f"|gpu-oracle|/oracle max {(np.abs(gpu_rows - M64) / M64).max():.2e}")
 
 
-def check_scale_search(api, X, W, dtype, alphas, bits, zp, rows=None, ws=None):
+def check_scale_search(api, X, W, dtype, alphas, bits, zp, rows=None, ws=None, group=128):
     """Runs stats + search on the GPU and the oracle; compares. Returns both results."""
     Xd, Wd = to_dev(X, dtype), to_dev(W, dtype)
     abar = api.act_stats(Xd)
     ref_abar = O.act_stats(X, dtype)
     assert np.array_equal(bits32(abar), ref_abar.view(np.uint32)), "abar differs"
-    res = api.search_scale(Xd, Wd, abar, alphas, bits=bits, zero_point=zp, want_row_sums=True, ws=ws)
-    ref = O.search_scale(X, W, dtype, ref_abar, alphas, bits, 128, zp, rows=rows)
+    res = api.search_scale(Xd, Wd, abar, alphas, bits=bits, group=group, zero_point=zp,
+                           want_row_sums=True, ws=ws)
+    ref = O.search_scale(X, W, dtype, ref_abar, alphas, bits, group, zp, rows=rows)
     T, N = X.shape[0], W.shape[0]
     rs = res["row_sums"].cpu().numpy()
     # the curve is the mean of the per-row sums (any size)
@@ -134,7 +135,7 @@ def check_scale_search(api, X, W, dtype, alphas, bits, zp, rows=None, ws=None):
     assert np.array_equal(bits32(res["s_best"]), ref["s_table"][res["index"]].view(np.uint32))
     sel = slice(None) if rows is None else np.asarray(rows)
     w_rows = O.decode(W, dtype)[sel]
-    cands = [(ref["s_table"][i], 1.0, (bits, 128, zp)) for i in range(len(alphas))]
+    cands = [(ref["s_table"][i], 1.0, (bits, group, zp)) for i in range(len(alphas))]
     M64, Mm, tol = row_references(X, dtype, w_rows, cands)
     assert np.allclose(M64, ref["row_sums"], rtol=1e-10, atol=0)
     compare_rows(rs[:, sel], M64, Mm, tol, "alpha search rows")
@@ -152,17 +153,17 @@ def check_scale_search(api, X, W, dtype, alphas, bits, zp, rows=None, ws=None):
     return res, ref, Xd, Wd
 
 
-def check_clip(api, Xd, Wd, X, W, dtype, s, ratios, bits, zp, rows=None):
+def check_clip(api, Xd, Wd, X, W, dtype, s, ratios, bits, zp, rows=None, group=128):
     T, N = X.shape[0], W.shape[0]
     ratios = np.asarray(ratios, np.float32)
     res = api.search_clip(Xd, Wd, torch.from_numpy(s).to("cuda:0"), ratios, bits=bits,
-                          zero_point=zp, want_row_sums=True)
-    ref = O.search_clip(X, W, dtype, s, ratios, bits, 128, zp, rows=rows)
+                          group=group, zero_point=zp, want_row_sums=True)
+    ref = O.search_clip(X, W, dtype, s, ratios, bits, group, zp, rows=rows)
     rs = res["row_sums"].cpu().numpy()
     sel = slice(None) if rows is None else np.asarray(rows)
     w_rows = O.decode(W, dtype)[sel]
     R = w_rows.shape[0]
-    cands = [(s, np.full(R, r, np.float32), (bits, 128, zp)) for r in ratios]
+    cands = [(s, np.full(R, r, np.float32), (bits, group, zp)) for r in ratios]
     M64, Mm, tol = row_references(X, dtype, w_rows, cands)
     assert np.allclose(M64, ref["row_sums"], rtol=1e-10, atol=0)
     compare_rows(rs[:, sel], M64, Mm, tol, "clip search rows")
@@ -289,17 +290,24 @@ def test_search_clip_small_ragged(api, bits, zp):
 # step 8: pack
 # ---------------------------------------------------------------------------
 
-def unpack_nibbles(words, cols):
-    u = np.ascontiguousarray(words).view(np.uint32)
+def unpack_codes(words, cols, bits):
+    """[R, cols·bits/32] words -> [R, cols] codes; code c at bits bits·c.. of
+    the row's little-endian word stream."""
+    u = np.ascontiguousarray(words).view(np.uint32).astype(np.uint64)
     out = np.zeros((u.shape[0], cols), dtype=np.int64)
-    for i in range(8):
-        out[:, i::8] = (u >> np.uint32(4 * i)) & np.uint32(0xF)
+    mask = np.uint64((1 << bits) - 1)
+    for c in range(cols):
+        w, b = divmod(bits * c, 32)
+        v = u[:, w] >> np.uint64(b)
+        if b + bits > 32:
+            v |= u[:, w + 1] << np.uint64(32 - b)
+        out[:, c] = (v & mask).astype(np.int64)
     return out
 
 
-def assert_pack_parity(qw, qz, sc, W, dtype, s, ratio, zp):
+def assert_pack_parity(qw, qz, sc, W, dtype, s, ratio, zp, bits=4, group=128):
     """GPU packed output against the oracle's; returns the number of near-tie codes."""
-    rqw, rqz, rsc, ovf = O.quantize_pack(W, dtype, s, ratio, 4, 128, zp)
+    rqw, rqz, rsc, ovf = O.quantize_pack(W, dtype, s, ratio, bits, group, zp)
     assert not ovf
     qw, qz, sc = qw.cpu().numpy(), qz.cpu().numpy(), sc.cpu().numpy().view(np.uint16)
     assert np.array_equal(qz, rqz), "qzeros differ"
@@ -307,22 +315,22 @@ def assert_pack_parity(qw, qz, sc, W, dtype, s, ratio, zp):
     if np.array_equal(qw, rqw):
         return 0
     N = W.shape[0]
-    gq, rq = unpack_nibbles(qw, N), unpack_nibbles(rqw, N)      # [K, N]
+    gq, rq = unpack_codes(qw, N, bits), unpack_codes(rqw, N, bits)      # [K, N]
     kk, nn = np.nonzero(gq != rq)
     w32 = O.decode(W, dtype)
     r = np.ones(N, np.float32) if ratio is None else np.asarray(ratio, np.float32)
-    _, step, _ = O.quantize(w32[np.unique(nn)], s, r[np.unique(nn)], 4, 128, zp)
+    _, step, _ = O.quantize(w32[np.unique(nn)], s, r[np.unique(nn)], bits, group, zp)
     row_of = {n: i for i, n in enumerate(np.unique(nn))}
     for k, n in zip(kk, nn):
         wp = np.float32(w32[n, k] * np.float32(s[k]))
-        v = float(np.float32(wp / step[row_of[n], k // 128]))
+        v = float(np.float32(wp / step[row_of[n], k // group]))
         assert abs(v - np.floor(v) - 0.5) < 1e-6, f"code ({k},{n}) differs away from a tie"
         assert abs(int(gq[k, n]) - int(rq[k, n])) == 1
     print(f"pack: {len(kk)} near-tie codes differ")
     return len(kk)
 
 
-def _pack_case(api, N, K, dtype, zp, with_ratio, seed):
+def _pack_case(api, N, K, dtype, zp, with_ratio, seed, bits=4, group=128):
     rng = np.random.default_rng(seed)
     w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
     if dtype == "bf16":
@@ -335,8 +343,10 @@ def _pack_case(api, N, K, dtype, zp, with_ratio, seed):
     ratio = rng.choice(synth.ratio_grid(), size=N).astype(np.float32) if with_ratio else None
     qw, qz, sc = api.quantize_pack(to_dev(W, dtype), torch.from_numpy(s).to("cuda:0"),
                                    None if ratio is None else torch.from_numpy(ratio).to("cuda:0"),
-                                   zero_point=zp)
-    assert_pack_parity(qw, qz, sc, W, dtype, s, ratio, zp)
+                                   bits=bits, group=group, zero_point=zp)
+    assert qw.shape == (K, N * bits // 32) and qz.shape == (K // group, N * bits // 32)
+    assert sc.shape == (K // group, N)
+    assert_pack_parity(qw, qz, sc, W, dtype, s, ratio, zp, bits, group)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
@@ -349,6 +359,36 @@ def test_pack_bitwise(api, dtype, zp, with_ratio):
 @pytest.mark.parametrize("N,K", [(8, 128), (256, 128), (520, 256)])
 def test_pack_bitwise_shapes(api, N, K):
     _pack_case(api, N, K, "bf16", True, True, seed=N + K)
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("group", [32, 64, 128])
+@pytest.mark.parametrize("zp", [True, False])
+def test_pack_bitwise_bits_groups(api, bits, group, zp):
+    # 288 rows: one full 256-row tile and a ragged one (9 x 32 rows for 3 bits)
+    _pack_case(api, 288, 384, "bf16", zp, True, seed=bits * 100 + group, bits=bits, group=group)
+
+
+@pytest.mark.parametrize("N,K", [(32, 128), (544, 256)])
+@pytest.mark.parametrize("dtype", ["f16", "f32"])
+def test_pack_int3_shapes(api, N, K, dtype):
+    _pack_case(api, N, K, dtype, True, False, seed=N * 3 + K, bits=3, group=64)
+
+
+@pytest.mark.parametrize("bits,group,zp", [(4, 32, True), (4, 64, False), (3, 32, True),
+                                           (3, 64, True)])
+def test_search_scale_group_sizes(api, bits, group, zp):
+    X, W = synth.make_custom(700, 300, 384, "bf16", seed=26 + group)
+    check_scale_search(api, X, W, "bf16", synth.alpha_grid(7), bits, zp, group=group)
+
+
+@pytest.mark.parametrize("bits,group", [(4, 32), (3, 64)])
+def test_search_clip_group_sizes(api, bits, group):
+    X, W = synth.make_custom(520, 264, 256, "bf16", seed=27 + group)
+    ab = O.act_stats(X, "bf16")
+    s = O.scale_for_alpha(ab, 0.5)
+    check_clip(api, to_dev(X, "bf16"), to_dev(W, "bf16"), X, W, "bf16", s,
+               synth.ratio_grid(6), bits, True, group=group)
 
 
 def test_pack_overflow_reports_range(api):
