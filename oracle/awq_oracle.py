@@ -331,6 +331,45 @@ def quantize_pack(W, dtype, s32, ratio=None, bits=4, group=128, zero_point=True)
     return qweight, qzeros, np.ascontiguousarray(sc).view(np.uint16), overflow
 
 
+def unpack_codes(words: np.ndarray, count: int, bits: int) -> np.ndarray:
+    """Inverse of ``pack_codes``: [R, W] int32 words -> [R, count] codes, code c
+    read from bits bits·c .. bits·c + bits - 1 of the row's little-endian
+    stream of words."""
+    u = np.ascontiguousarray(words).view(np.uint32).astype(np.uint64)
+    out = np.zeros((u.shape[0], count), dtype=np.int64)
+    mask = np.uint64((1 << bits) - 1)
+    for c in range(count):
+        w, b = divmod(bits * c, 32)
+        v = u[:, w] >> np.uint64(b)
+        if b + bits > 32:
+            v = v | (u[:, w + 1] << np.uint64(32 - b))
+        out[:, c] = (v & mask).astype(np.int64)
+    return out
+
+
+def dequantize_packed(qweight, qzeros, scales_u16, N: int, bits: int = 4, group: int = 128):
+    """Weights a consumer of the packed layout sees, float64 [N, K]:
+    ŵ[n][k] = (q[k][n] - z[k/g][n]) · scale[k/g][n], with the stored fp16
+    scale ([roadmap] §5: qweight, qzeros and fp16 scales; §3: these are the
+    weights of W·diag(s), to be applied to X·diag(s)^-1)."""
+    q = unpack_codes(qweight, N, bits)                        # [K, N]
+    z = unpack_codes(qzeros, N, bits)                         # [K/g, N]
+    sc = np.asarray(scales_u16, dtype=np.uint16).view(np.float16).astype(F64)   # [K/g, N]
+    K = q.shape[0]
+    gidx = np.arange(K) // group
+    return ((q - z[gidx]).astype(F64) * sc[gidx]).T           # [N, K]
+
+
+def w4a16_matmul(Xp, dtype, qweight, qzeros, scales_u16, N: int, bits: int = 4,
+                 group: int = 128) -> np.ndarray:
+    """Y = X'·Ŵᵀ in float64 for activations X' [T, K] (already divided by s,
+    the fold) and a packed layer: what a weight-only-quantised (W4A16) layer
+    computes ([reading] "Key takeaways": weight-only INT4 with 16-bit
+    activations; [roadmap] §5 for the format)."""
+    x = decode(Xp, dtype).astype(F64)
+    return x @ dequantize_packed(qweight, qzeros, scales_u16, N, bits, group).T
+
+
 def storage_bits_per_weight(N: int, K: int, bits: int = 4, group: int = 128) -> float:
     """Bits per weight of the packed layout: codes + fp16 scales + packed zeros."""
     total = N * K * bits + (N * K // group) * (16 + bits)

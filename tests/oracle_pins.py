@@ -617,6 +617,68 @@ def check_group_size_gain(O):
     assert best[32] < best[64] < best[128], best
 
 
+# ----------------------------------------------------------------------------
+# consumer of the packed layout (W4A16)
+# ----------------------------------------------------------------------------
+
+def _exact_groups(N, K, group, rng):
+    """W whose every group quantises exactly at s = 1: group (n, g) spans
+    [-z·2^e, (15 - z)·2^e] with both ends present, values on the 2^e grid."""
+    w = np.zeros((N, K), np.float32)
+    for n in range(N):
+        for g in range(K // group):
+            e = int(rng.integers(-9, -4))
+            z = int(rng.integers(1, 15))
+            codes = rng.integers(0, 16, size=group)
+            codes[0], codes[1] = 0, 15
+            w[n, g * group:(g + 1) * group] = ((codes - z) * 2.0 ** e).astype(np.float32)
+    return w
+
+
+def check_w4a16_exact_layer(O):
+    """A layer that quantises exactly (steps 2^e, integer zero points): the
+    consumer of its packed form reproduces X·Wᵀ, for groups of 32, 64, 128;
+    unpack_codes inverts pack_codes for 3 and 4 bits."""
+    rng = _rng(70)
+    for gs in (32, 64, 128):
+        N, K = 24, 256
+        w = _exact_groups(N, K, gs, rng)
+        qw, qz, sc, ovf = O.quantize_pack(w, "f32", np.ones(K, F32), None, 4, gs, True)
+        assert not ovf
+        q, step, zero = O.quantize(w, np.ones(K, F32), 1.0, 4, gs, True)
+        assert np.all(np.log2(step) == np.round(np.log2(step)))       # steps are powers of 2
+        X = rng.standard_normal((5, K)).astype(F32)
+        Y = O.w4a16_matmul(X, "f32", qw, qz, sc, N, 4, gs)
+        ref = X.astype(np.float64) @ w.astype(np.float64).T
+        assert np.allclose(Y, ref, rtol=1e-12, atol=1e-15), np.abs(Y - ref).max()
+        assert np.array_equal(O.dequantize_packed(qw, qz, sc, N, 4, gs), w.astype(np.float64))
+    for bits in (3, 4):
+        codes = rng.integers(0, 2 ** bits, size=(7, 64))
+        assert np.array_equal(O.unpack_codes(O.pack_codes(codes, bits), 64, bits), codes)
+
+
+def check_w4a16_bruteforce(O):
+    """Tiny packed layer: every output equals a pure-Python sum over k of
+    x[t][k]·(code - zero)·scale, codes and zeros read bit by bit."""
+    rng = _rng(71)
+    N, K, T, gs = 16, 128, 3, 64
+    W = synth.make_weight(N, K, 0.02, "bf16", seed=72)
+    s = np.exp(rng.uniform(-1, 1, size=K)).astype(F32)
+    qw, qz, sc, _ = O.quantize_pack(W, "bf16", s, None, 4, gs, True)
+    X = synth.f32_to_bf16_bits(rng.standard_normal((T, K)).astype(F32))
+    Y = O.w4a16_matmul(X, "bf16", qw, qz, sc, N, 4, gs)
+    x = synth.bf16_bits_to_f32(X).astype(np.float64)
+    scf = sc.view(np.float16).astype(np.float64)
+    for t in range(T):
+        for n in range(N):
+            acc = []
+            for k in range(K):
+                code = _unpack_bits_python(qw[k], 4, N)[n]
+                zero = _unpack_bits_python(qz[k // gs], 4, N)[n]
+                acc.append(float(x[t, k]) * (code - zero) * float(scf[k // gs, n]))
+            assert math.isclose(Y[t, n], math.fsum(acc), rel_tol=1e-12, abs_tol=1e-14)
+
+
 ALL_CHECKS = [
     check_stats_closed_form, check_stats_exact_sum, check_scale_closed_form,
     check_scale_dead_channel, check_quant_worked_examples, check_codes_nearest_bruteforce,
@@ -625,5 +687,5 @@ ALL_CHECKS = [
     check_monotone_and_separable, check_outlier_behaviour, check_pack_layout,
     check_pack_overflow_flag, check_search_group, check_encode_bf16_exhaustive,
     check_encode_f16_examples, check_fold_norm, check_fold_linear, check_pack_int3_layout,
-    check_group_size_gain,
+    check_group_size_gain, check_w4a16_exact_layer, check_w4a16_bruteforce,
 ]

@@ -71,6 +71,14 @@ MUTATIONS = [
      "qweight = pack_codes(np.ascontiguousarray(q), bits)", [P.check_pack_layout]),
     ("straddling 3-bit codes lose their high bits", "        if b + bits > 32:\n",
      "        if False:\n", [P.check_pack_int3_layout]),
+    ("consumer ignores the zero point", "((q - z[gidx]).astype(F64) * sc[gidx]).T",
+     "((q - 0 * z[gidx]).astype(F64) * sc[gidx]).T", [P.check_w4a16_exact_layer]),
+    ("consumer uses the scale of the wrong group", "gidx = np.arange(K) // group",
+     "gidx = np.minimum(np.arange(K) // group + 1, K // group - 1)",
+     [P.check_w4a16_exact_layer, P.check_w4a16_bruteforce]),
+    ("unpacking reads codes from the top bit", "        w, b = divmod(bits * c, 32)\n        v = u",
+     "        w, b = divmod(bits * c, 32)\n        b = 32 - bits - b if b + bits <= 32 else b\n        v = u",
+     [P.check_w4a16_exact_layer]),
     ("group size ignored by the quantiser", "    G = K // group\n",
      "    group = 128\n    G = K // group\n", [P.check_codes_nearest_bruteforce]),
     ("group searched on its first layer only",
