@@ -29,7 +29,6 @@ if ROOT not in sys.path:
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "search_gemm_traffic.json")
-GEMM_SRC = os.path.join(ROOT, "post_weight_quantization_26_amd", "csrc", "gemm.hip")
 
 
 def parse():
@@ -50,8 +49,11 @@ def gemm_traffic(cfg_name: str, launches_per_step: int):
         return None
     with open(TRAFFIC_FILE) as f:
         rec = json.load(f)
-    src_hash = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
-    if rec.get("gemm_source_sha256") != src_hash or rec.get("workload") != cfg_name:
+    h = hashlib.sha256()
+    for rel in rec.get("gemm_sources", []):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    if rec.get("gemm_sources_sha256") != h.hexdigest() or rec.get("workload") != cfg_name:
         return None
     return rec.get("bytes_per_launch")
 

@@ -15,6 +15,7 @@
  *                      same X and so share one s
  *   awq_fold_norm, awq_fold_linear  divide the operation that produces X by
  *                      s, so the scaled weights need no run-time division
+ *   awq_w4a16_matmul   a consumer of the packed layout: Y = X·Ŵᵀ
  *
  * Sources (page titles and sections):
  *   "AWQ and Activation-Aware Scaling", section "Scaling instead of
@@ -198,6 +199,27 @@ awq_status awq_fold_norm(void* gamma, void* beta, awq_dtype dtype, int64_t K, co
 awq_status awq_fold_linear(void* W_prev, void* bias_prev, awq_dtype dtype, int64_t K,
                            int64_t K_prev, const float* s, void* stream);
 
+/* Consumer of the packed layout (W4A16: 4-bit weights, 16-bit activations).
+ * Y[t][n] = Σ_k X[t][k] · Ŵ[n][k] with Ŵ[n][k] = (q[k][n] - z[k/g][n]) ·
+ * scale[k/g][n], reading qweight [K, N/8], qzeros [K/g, N/8] and scales
+ * [K/g, N] (fp16 bits) exactly as awq_quantize_pack writes them at w_bit 4
+ * ("05 — AWQ", section 5 "Bit-level output format"; the AWQ reading note,
+ * "Key takeaways": weight-only INT4 inference with 16-bit activations).
+ * X [T, K] holds the activations already divided by s (the fold), bf16 or
+ * fp16; Y [T, N] is written in the same type. Ŵ is formed exactly in
+ * float32; sums are float32, each output rounded once to nearest even.
+ * T <= 16 runs a fused GEMV (Ŵ never stored); larger T dequantises Ŵ once
+ * into the workspace, rounded to the activation type, and runs an MFMA GEMM.
+ * N a multiple of 8, K of 128; group_size 32, 64 or 128. X and scales
+ * 16-byte aligned, qweight and qzeros 4-byte, Y 2-byte. ws: at least
+ * awq_w4a16_workspace_bytes(T, N, K, dtype), 16-byte aligned.
+ * Does not synchronise. */
+size_t awq_w4a16_workspace_bytes(int64_t T, int64_t N, int64_t K, awq_dtype dtype);
+awq_status awq_w4a16_matmul(const void* X, awq_dtype dtype, int64_t T, int64_t N, int64_t K,
+                            const int32_t* qweight, const int32_t* qzeros,
+                            const uint16_t* scales, int32_t group_size, void* Y, void* ws,
+                            size_t ws_bytes, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread. */
 const char* awq_last_error(void);
 
@@ -206,9 +228,11 @@ const char* awq_last_error(void);
  * awq_profile_read synchronises those events and returns the summed
  * duration (ms) and launch count of one kernel kind since the last reset.
  * Kinds: 0 stats, 1 scale table, 2 transform (quantise/dequantise
- * candidates), 3 search GEMM, 4 reductions, 5 pack, 6 fold. */
+ * candidates), 3 search GEMM, 4 reductions, 5 pack, 6 fold, 7 W4A16
+ * dequantisation, 8 W4A16 GEMM or GEMV, 9 W4A16 GEMV reduction. */
 enum { AWQ_K_STATS = 0, AWQ_K_SCALE = 1, AWQ_K_TRANSFORM = 2, AWQ_K_GEMM = 3, AWQ_K_REDUCE = 4,
-       AWQ_K_PACK = 5, AWQ_K_FOLD = 6, AWQ_K_COUNT = 7 };
+       AWQ_K_PACK = 5, AWQ_K_FOLD = 6, AWQ_K_DEQUANT = 7, AWQ_K_W4A16 = 8,
+       AWQ_K_W4A16_REDUCE = 9, AWQ_K_COUNT = 10 };
 void awq_profile_enable(int on);
 void awq_profile_reset(void);
 awq_status awq_profile_read(int kind, double* total_ms, int64_t* launches);

@@ -20,7 +20,7 @@ STATUS_NAMES = {0: "AWQ_OK", -1: "AWQ_E_INVALID", -2: "AWQ_E_UNSUPPORTED", -3: "
 AWQ_F32, AWQ_BF16, AWQ_F16 = 0, 1, 2
 AWQ_OP_STATS, AWQ_OP_SEARCH_SCALE, AWQ_OP_SEARCH_CLIP, AWQ_OP_PACK = 0, 1, 2, 3
 KERNEL_KINDS = {"stats": 0, "scale": 1, "transform": 2, "gemm": 3, "reduce": 4, "pack": 5,
-                "fold": 6}
+                "fold": 6, "dequant": 7, "w4a16": 8, "w4a16_reduce": 9}
 
 
 class QConfig(ctypes.Structure):
@@ -52,6 +52,9 @@ SIGNATURES = {
                                               c_sz, c_vp]),
     "awq_fold_norm": (ctypes.c_int, [c_vp, c_vp, ctypes.c_int, c_i64, c_vp, c_vp]),
     "awq_fold_linear": (ctypes.c_int, [c_vp, c_vp, ctypes.c_int, c_i64, c_i64, c_vp, c_vp]),
+    "awq_w4a16_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
+    "awq_w4a16_matmul": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp,
+                                        c_i32, c_vp, c_vp, c_sz, c_vp]),
     "awq_last_error": (ctypes.c_char_p, []),
     "awq_profile_enable": (None, [ctypes.c_int]),
     "awq_profile_reset": (None, []),

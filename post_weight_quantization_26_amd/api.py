@@ -228,6 +228,30 @@ def quantize_pack(W: torch.Tensor, s: torch.Tensor, ratio: Optional[torch.Tensor
     return qweight, qzeros, scales
 
 
+def w4a16_workspace_bytes(T: int, N: int, K: int, dtype: torch.dtype) -> int:
+    return int(L.lib().awq_w4a16_workspace_bytes(T, N, K, _DT[dtype]))
+
+
+def w4a16_matmul(X: torch.Tensor, qweight: torch.Tensor, qzeros: torch.Tensor,
+                 scales: torch.Tensor, group: int = DEFAULT_GROUP,
+                 ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """Y = X·Ŵᵀ for a 4-bit packed layer (qweight [K, N/8], qzeros [K/g, N/8],
+    scales [K/g, N] float16) and activations X [T, K] (bf16 or float16,
+    already divided by s). Returns Y [T, N] in X's dtype."""
+    _dev(X, "X"), _dev(qweight, "qweight"), _dev(qzeros, "qzeros"), _dev(scales, "scales")
+    T, K = X.shape
+    N = scales.shape[1]
+    if qweight.shape != (K, N // 8) or qzeros.shape != (K // group, N // 8) or \
+            scales.shape != (K // group, N):
+        raise ValueError("packed layer shapes do not match X and the group size")
+    Y = out if out is not None else torch.empty((T, N), dtype=X.dtype, device=X.device)
+    ws = _workspace(ws, w4a16_workspace_bytes(T, N, K, X.dtype), X.device)
+    L.check(L.lib().awq_w4a16_matmul(_ptr(X), _dtype(X), T, N, K, _ptr(qweight), _ptr(qzeros),
+                                     _ptr(scales), int(group), _ptr(Y), _ptr(ws), ws.numel(),
+                                     _stream()))
+    return Y
+
+
 def profile_enable(on: bool = True) -> None:
     L.lib().awq_profile_enable(1 if on else 0)
 

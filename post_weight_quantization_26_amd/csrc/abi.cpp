@@ -32,6 +32,17 @@ hipError_t launch_clip_select(const double* row_sums, int n_ratio, int64_t N,
 hipError_t launch_pack(const void* W, int dtype, int64_t N, int64_t K, const float* s,
                        const float* ratio, int bits, int group, int zero_point, int32_t* qweight,
                        int32_t* qzeros, uint16_t* scales, int* overflow, hipStream_t st);
+hipError_t launch_w4a16_dequant(const int32_t* qweight, const int32_t* qzeros,
+                                const uint16_t* scales, int64_t N, int64_t K, int group, int f16,
+                                uint16_t* Wd, hipStream_t st);
+hipError_t launch_w4a16_gemm(const uint16_t* X, const uint16_t* Wd, int64_t M, int64_t N,
+                             int64_t K, int f16, uint16_t* Y, hipStream_t st);
+hipError_t launch_w4a16_gemv(const uint16_t* X, int64_t T, int64_t N, int64_t K,
+                             const int32_t* qweight, const int32_t* qzeros,
+                             const uint16_t* scales, int group, int f16, int64_t kpw,
+                             float* partial, hipStream_t st);
+hipError_t launch_w4a16_gemv_reduce(const float* partial, int64_t chunks, int64_t T, int64_t N,
+                                    int f16, uint16_t* Y, hipStream_t st);
 hipError_t launch_fold_vec(void* v, int dtype, int64_t K, const float* s, hipStream_t st);
 hipError_t launch_fold_rows(void* W, int dtype, int64_t K, int64_t K_prev, const float* s,
                             hipStream_t st);
@@ -350,6 +361,47 @@ extern "C" awq_status awq_fold_linear(void* W_prev, void* bias_prev, awq_dtype d
     AWQ_HIP(timed(AWQ_K_FOLD, st,
                   [&] { return launch_fold_vec(bias_prev, dt(dtype), K, s, st); }),
             "fold_linear bias");
+  return AWQ_OK;
+}
+
+extern "C" awq_status awq_w4a16_matmul(const void* X, awq_dtype dtype, int64_t T, int64_t N,
+                                       int64_t K, const int32_t* qweight, const int32_t* qzeros,
+                                       const uint16_t* scales, int32_t group_size, void* Y,
+                                       void* ws, size_t ws_bytes, void* stream) {
+  awq_status st_ = check_w4a16(X, dtype, T, N, K, qweight, qzeros, scales, group_size, Y, ws,
+                               ws_bytes);
+  if (st_ != AWQ_OK) return st_;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int f16 = dtype == AWQ_F16;
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  uint16_t* y = static_cast<uint16_t*>(Y);
+  if (T <= kW4A16GemvMaxT) {
+    float* partial = static_cast<float*>(ws);
+    const int64_t kpw = w4a16_gemv_kpw(N, K);
+    AWQ_HIP(timed(AWQ_K_W4A16, st,
+                  [&] {
+                    return launch_w4a16_gemv(x, T, N, K, qweight, qzeros, scales, group_size, f16,
+                                             kpw, partial, st);
+                  }),
+            "w4a16 gemv");
+    AWQ_HIP(timed(AWQ_K_W4A16_REDUCE, st,
+                  [&] {
+                    return launch_w4a16_gemv_reduce(partial, w4a16_gemv_chunks(N, K), T, N, f16,
+                                                    y, st);
+                  }),
+            "w4a16 gemv reduce");
+    return AWQ_OK;
+  }
+  uint16_t* Wd = static_cast<uint16_t*>(ws);
+  AWQ_HIP(timed(AWQ_K_DEQUANT, st,
+                [&] {
+                  return launch_w4a16_dequant(qweight, qzeros, scales, N, K, group_size, f16, Wd,
+                                              st);
+                }),
+          "w4a16 dequant");
+  AWQ_HIP(timed(AWQ_K_W4A16, st,
+                [&] { return launch_w4a16_gemm(x, Wd, T, N, K, f16, y, st); }),
+          "w4a16 gemm");
   return AWQ_OK;
 }
 

@@ -64,6 +64,16 @@ awq_status check_pack(const void* W, awq_dtype d, int64_t N, int64_t K, const fl
                       awq_qconfig qc, const int32_t* qweight, const int32_t* qzeros,
                       const uint16_t* scales, const void* ws, size_t ws_bytes);
 
+// W4A16 consumer: token rows up to which the fused GEMV path runs; rows of k
+// per wave of the GEMV (the largest of 128, 64, 32 dividing K/4 that still
+// gives >= 1024 workgroups); its number of k chunks.
+constexpr int64_t kW4A16GemvMaxT = 16;
+int64_t w4a16_gemv_kpw(int64_t N, int64_t K);
+inline int64_t w4a16_gemv_chunks(int64_t N, int64_t K) { return K / (4 * w4a16_gemv_kpw(N, K)); }
+awq_status check_w4a16(const void* X, awq_dtype d, int64_t T, int64_t N, int64_t K,
+                       const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                       int32_t group, const void* Y, const void* ws, size_t ws_bytes);
+
 awq_status set_error(awq_status st, const char* fmt, ...);
 
 }  // namespace awq

@@ -1,0 +1,274 @@
+// The MFMA main loop shared by the search GEMM (sums of squares of X·Eᵀ)
+// and the W4A16 consumer GEMM (X·Ŵᵀ stored): a 256x256 output tile per
+// workgroup, A and B both [rows, K] row-major 16-bit operands, K in 32-wide
+// k-tiles through a 4-stage LDS ring filled by buffer_load ... lds.
+//
+//  * 256x256 block tile, four wavefronts (one per SIMD) in a 2x2 arrangement,
+//    each owning 128x128 outputs as 4x4 v_mfma_f32_32x32x16 accumulators
+//    (bf16 or fp16 operands, 256 AGPRs).
+//  * K advances in 32-wide k-tiles through a 4-stage LDS ring (4 x 32 KiB).
+//    Tiles are copied global -> LDS by buffer_load_dwordx4 ... lds (no
+//    staging registers), three k-tiles ahead of the MFMAs. Loads go through a
+//    buffer resource per tile, so rows past the end of A or B read as zero.
+//  * One k-tile per barrier-delimited region; inside it the MFMAs of the
+//    previous k-step run while this k-tile's fragments are read and the DMA
+//    for k-tile kt+3 is issued (sched_group_barrier interleaving).
+//  * LDS rows are 64 bytes (4 chunks of 16 B) with the chunk index XORed by
+//    (row >> 2) & 3: gfx950 serves ds_read_b128 sixteen lanes at a time over
+//    64 banks, and this swizzle keeps both the fragment reads and the DMA
+//    writes free of bank conflicts.
+//  * Each LDS stage is its own __shared__ array and the k-loop is unrolled
+//    over the 4 stages, so the compiler can tell the stage being read from the
+//    stages the DMA writes and does not serialise LDS reads behind the DMA.
+//  * Workgroups are mapped so each XCD runs 4 A tiles x 8 B tiles at a time
+//    while all XCDs share the same 8 B tiles.
+//
+// Output layout of one 32x32 accumulator: lane l holds column l % 32; its
+// register v holds row 8·(v / 4) + 4·(l / 32) + v % 4.
+#pragma once
+
+#include "device_common.h"
+
+namespace awq {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// MFMA operand vector of 8 elements: bf16 or fp16 (F16 = true).
+template <bool F16>
+struct Operand {
+  typedef bf16x8_t type;
+};
+template <>
+struct Operand<true> {
+  typedef f16x8_t type;
+};
+
+#define AWQ_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+constexpr int BM = 256;
+constexpr int BN = 256;
+constexpr int BK = 32;       // k per stage / region
+constexpr int NT = 256;
+constexpr int CH = BK / 8;   // 16-byte chunks per tile row per stage
+constexpr int STAGE = 256 * CH;
+
+__shared__ uint4 sA0[STAGE], sA1[STAGE], sA2[STAGE], sA3[STAGE];
+__shared__ uint4 sB0[STAGE], sB1[STAGE], sB2[STAGE], sB3[STAGE];
+
+template <int S>
+__device__ __forceinline__ uint4* stage_a() {
+  return S == 0 ? sA0 : S == 1 ? sA1 : S == 2 ? sA2 : sA3;
+}
+template <int S>
+__device__ __forceinline__ uint4* stage_b() {
+  return S == 0 ? sB0 : S == 1 ? sB1 : S == 2 ? sB2 : sB3;
+}
+
+// 16-byte slot of (row, chunk) inside a stage.
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * CH + (chunk ^ ((row >> 2) & 3));
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int wait_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int kWaitLgkm0 = 0xF | (3 << 14) | (0x7 << 4);
+
+// Masks for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100;
+
+// Workgroup barrier that neither the compiler nor the scheduler may move a
+// memory operation or any instruction across. Unlike __syncthreads() it adds
+// no vmcnt(0), so DMA copies stay in flight across it.
+__device__ __forceinline__ void region_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Block id -> (token tile, candidate-column tile). Returns false for padding blocks.
+__device__ __forceinline__ bool tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  if (tiles_m >= 32) {
+    const int w = bid >> 8, j = bid & 255;
+    const int xcd = j & 7, i = j >> 3;  // consecutive ids go round-robin over the 8 XCDs
+    const int nwn = (tiles_n + 7) >> 3;
+    const int g = w / nwn, wn = w - g * nwn;
+    tm = 32 * g + 4 * xcd + (i & 3);
+    tn = 8 * wn + (i >> 2);
+  } else {
+    tm = bid % tiles_m;
+    tn = bid / tiles_m;
+  }
+  return tm < tiles_m && tn < tiles_n;
+}
+
+// Buffer resource over `rows` rows of K bf16 starting at `base` (dword 3 =
+// raw 32-bit data format, the gfx9-family default). Offsets past the end
+// read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int64_t rows,
+                                                           int64_t K) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0,
+                                           int(rows * K * 2), 0x00020000);
+}
+
+struct GemmCtx {
+  __amdgpu_buffer_rsrc_t rsA, rsB;
+  int voff[4];  // byte offset (k-tile 0) of the chunk this lane copies in DMA instruction j
+  int wave, KT, oob;
+  int rdA[2], rdB[2];  // fragment slot for k-step 0/1 (sub-tile i adds 128 i)
+};
+
+// Copy k-tile kt into stage S: 4 instructions per operand per wave, each
+// filling 1 KiB (16 rows) of the stage; lane l fills slot base + l. Past the
+// last k-tile the offset leaves the resource, so the copy writes zeros
+// without touching memory and the vmcnt bookkeeping stays uniform.
+template <int S>
+__device__ __forceinline__ void dma_tile(const GemmCtx& c, int kt) {
+  const int kofs = kt < c.KT ? kt * (BK * 2) : c.oob;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsA, AWQ_LDS(stage_a<S>() + (c.wave * 4 + j) * 64),
+                                             16, c.voff[j] + kofs, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsB, AWQ_LDS(stage_b<S>() + (c.wave * 4 + j) * 64),
+                                             16, c.voff[j] + kofs, 0, 0, 0);
+  }
+}
+
+template <int S, class V>
+__device__ __forceinline__ void read_frags(const GemmCtx& c, int ks, V (&fa)[4], V (&fb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    fa[i] = __builtin_bit_cast(V, stage_a<S>()[c.rdA[ks] + i * 128]);
+    fb[i] = __builtin_bit_cast(V, stage_b<S>()[c.rdB[ks] + i * 128]);
+  }
+}
+
+__device__ __forceinline__ floatx16 mfma(bf16x8_t a, bf16x8_t b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx16 mfma(f16x8_t a, f16x8_t b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+template <class V>
+__device__ __forceinline__ void mfma_4x4(floatx16 (&acc)[4][4], const V (&fa)[4],
+                                         const V (&fb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = mfma(fa[i], fb[j], acc[i][j]);
+}
+
+// Region kt (stage S = kt % 4), between two barriers:
+//   DMA of k-tile kt+3 into stage (kt+3) % 4 (last read before this region),
+//   MFMAs of (kt-1, k-step 1) from F1 while F0 <- (kt, k-step 0) is read,
+//   MFMAs of (kt, k-step 0) from F0 while F1 <- (kt, k-step 1) is read,
+//   then wait for this wave's LDS reads and for its DMA of k-tile kt+1
+//   (two k-tiles = 16 copies may stay in flight) and meet at the barrier.
+template <int S, bool PREV, class V>
+__device__ __forceinline__ void region(const GemmCtx& c, int kt, floatx16 (&acc)[4][4],
+                                       V (&f0a)[4], V (&f0b)[4], V (&f1a)[4], V (&f1b)[4]) {
+  dma_tile<(S + 3) & 3>(c, kt + 3);
+  if (PREV) mfma_4x4(acc, f1a, f1b);
+  read_frags<S>(c, 0, f0a, f0b);
+  mfma_4x4(acc, f0a, f0b);
+  read_frags<S>(c, 1, f1a, f1b);
+  // The 8 copies are spread one per two MFMAs over the 16 MFMAs of (kt-1, 1)
+  // so that the LDS writes they cause interleave with the fragment reads
+  // instead of arriving in one burst.
+  if (PREV) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      if (i & 1) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      if (i & 1) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kSgMfma, 8, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_waitcnt(wait_vm(16));
+  region_barrier();
+}
+
+// Sets up the copy offsets and fragment slots of one 256x256 tile whose A
+// rows start at A (rows_a valid rows) and B rows at B (rows_b valid rows).
+__device__ __forceinline__ void gemm_setup(GemmCtx& c, const uint16_t* A, int64_t rows_a,
+                                           const uint16_t* B, int64_t rows_b, int64_t K) {
+  c.rsA = tile_rsrc(A, rows_a, K);
+  c.rsB = tile_rsrc(B, rows_b, K);
+  const int tid = threadIdx.x, lane = tid & 63;
+  c.wave = tid >> 6;
+  c.KT = int(K / BK);
+  c.oob = BM * int(K) * 2;  // beyond every row of the tile
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // Slot p of a stage holds chunk (p & 3) ^ ((row >> 2) & 3) of row p >> 2.
+    const int p = (c.wave * 4 + j) * 64 + lane;
+    const int row = p >> 2;
+    const int chunk = (p & 3) ^ ((row >> 2) & 3);
+    c.voff[j] = (row * int(K) + chunk * 8) * 2;
+  }
+  const int wm = c.wave >> 1, wn = c.wave & 1;
+  const int fr = lane & 31, fh = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    c.rdA[ks] = swz(wm * 128 + fr, 2 * ks + fh);
+    c.rdB[ks] = swz(wn * 128 + fr, 2 * ks + fh);
+  }
+}
+
+// The whole k-loop of one tile: acc[i][j] (wave (wm, wn), sub-tile (i, j))
+// receives Σ_k A·Bᵀ. K must be a multiple of 128 (the number of 32-wide
+// k-tiles a multiple of 4).
+template <bool F16>
+__device__ __forceinline__ void gemm_mainloop(const GemmCtx& c, floatx16 (&acc)[4][4]) {
+  typedef typename Operand<F16>::type V;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  dma_tile<0>(c, 0);
+  dma_tile<1>(c, 1);
+  dma_tile<2>(c, 2);
+  __builtin_amdgcn_s_waitcnt(wait_vm(16));  // k-tile 0 landed; 1 and 2 in flight
+  region_barrier();
+  V f0a[4], f0b[4], f1a[4], f1b[4];
+  region<0, false>(c, 0, acc, f0a, f0b, f1a, f1b);
+  int kt = 1;
+  for (; kt + 4 < c.KT; kt += 4) {
+    region<1, true>(c, kt, acc, f0a, f0b, f1a, f1b);
+    region<2, true>(c, kt + 1, acc, f0a, f0b, f1a, f1b);
+    region<3, true>(c, kt + 2, acc, f0a, f0b, f1a, f1b);
+    region<0, true>(c, kt + 3, acc, f0a, f0b, f1a, f1b);
+  }
+  region<1, true>(c, kt, acc, f0a, f0b, f1a, f1b);
+  region<2, true>(c, kt + 1, acc, f0a, f0b, f1a, f1b);
+  region<3, true>(c, kt + 2, acc, f0a, f0b, f1a, f1b);
+  mfma_4x4(acc, f1a, f1b);
+}
+
+// Number of workgroups the tile_of mapping needs for a tiles_m x tiles_n grid.
+__host__ __device__ inline int64_t gemm_blocks(int tiles_m, int tiles_n) {
+  if (tiles_m >= 32) return int64_t((tiles_m + 31) / 32) * 32 * (int64_t((tiles_n + 7) / 8) * 8);
+  return int64_t(tiles_m) * tiles_n;
+}
+
+}  // namespace
+}  // namespace awq

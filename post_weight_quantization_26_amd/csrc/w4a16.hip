@@ -1,0 +1,339 @@
+// Consumer of the packed layout: a weight-only INT4 linear layer with 16-bit
+// activations (W4A16),
+//
+//   Y[t][n] = Σ_k X'[t][k] · Ŵ[n][k],   Ŵ[n][k] = (q[k][n] - z[k/g][n]) · scale[k/g][n]
+//
+// where X' = X·diag(s)^-1 is what the folded preceding operation produces and
+// (q, z, scale) is the layout the pack kernel writes ("05 — AWQ", section 5
+// "Bit-level output format": qweight [K, N/8], qzeros [K/g, N/8], fp16
+// scales [K/g, N]; the reading note's "Key takeaways": weight-only 4-bit with
+// 16-bit activations). Ŵ is formed exactly in float32 ((q - z) is an integer
+// of at most 4 bits and the scale an fp16 value).
+//
+// Two paths, by the number of token rows T:
+//  * T <= 16 (decode): fused GEMV. A lane owns one qweight word column (8
+//    output channels) and a run of k rows; it dequantises each word in
+//    registers and accumulates T x 8 float32 sums. The 4 waves of a
+//    workgroup take consecutive k runs and meet in LDS; one float32 partial
+//    per (k chunk, t, n) goes to the workspace and a second kernel adds the
+//    chunks in a fixed order and rounds once to the output type. Bound by
+//    HBM reads of qweight (N·K/2 bytes) and by the dequantisation ALU work.
+//  * T > 16 (prefill): the packed layer is dequantised once into [N, K]
+//    16-bit operand rows in the workspace (rounded once, to nearest even, to
+//    the activation type), then the MFMA main loop of the search GEMM
+//    (gemm_core.h) computes X'·Ŵᵀ and the epilogue rounds each float32 sum
+//    once to the output type. At T = 4096 the extra pass moves N·K·2.5 bytes,
+//    a few per cent of the GEMM's time.
+#include "gemm_core.h"
+
+namespace awq {
+namespace {
+
+template <bool F16>
+__device__ __forceinline__ uint16_t to16(float f) {
+  if constexpr (F16) return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+  else return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+template <bool F16>
+__device__ __forceinline__ float from16(uint16_t h) {
+  if constexpr (F16) return f16_to_f32(h);
+  else return bf16_to_f32(h);
+}
+
+// The 8 fp16 scales of output channels 8j..8j+7 in group g (16 bytes) and
+// their 8 zero points (one packed word) as float32.
+__device__ __forceinline__ void group_params(const int32_t* __restrict__ qzeros,
+                                             const uint16_t* __restrict__ scales, int64_t N,
+                                             int64_t g, int64_t j, float (&sc)[8],
+                                             float (&zf)[8]) {
+  const uint4 s4 = *reinterpret_cast<const uint4*>(scales + g * N + 8 * j);
+  const uint32_t sw[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sc[2 * i] = f16_to_f32(uint16_t(sw[i] & 0xFFFFu));
+    sc[2 * i + 1] = f16_to_f32(uint16_t(sw[i] >> 16));
+  }
+  const uint32_t zw = uint32_t(qzeros[g * (N / 8) + j]);
+#pragma unroll
+  for (int r = 0; r < 8; ++r) zf[r] = float((zw >> (4 * r)) & 0xFu);
+}
+
+// ---------------------------------------------------------------------------
+// prefill: dequantise into [N, K] operand rows
+// ---------------------------------------------------------------------------
+
+// Lane (kb, j): k rows 8kb..8kb+7 of word column j -> 8 output rows x 8 k,
+// one 16-byte store per output row (consecutive lanes continue the same row).
+template <bool F16>
+__global__ __launch_bounds__(256) void dequant_kernel(const int32_t* __restrict__ qweight,
+                                                      const int32_t* __restrict__ qzeros,
+                                                      const uint16_t* __restrict__ scales,
+                                                      int64_t N, int64_t K, int group,
+                                                      uint16_t* __restrict__ Wd) {
+#pragma clang fp contract(off)
+  const int64_t K8 = K / 8, N8 = N / 8;
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= K8 * N8) return;
+  const int64_t kb = t % K8, j = t / K8;
+  const int64_t k0 = kb * 8;
+  float sc[8], zf[8];
+  group_params(qzeros, scales, N, k0 / group, j, sc, zf);
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = uint32_t(qweight[(k0 + i) * N8 + j]);
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = (float((w[2 * i] >> (4 * r)) & 0xFu) - zf[r]) * sc[r];
+      const float hi = (float((w[2 * i + 1] >> (4 * r)) & 0xFu) - zf[r]) * sc[r];
+      h[i] = uint32_t(to16<F16>(lo)) | (uint32_t(to16<F16>(hi)) << 16);
+    }
+    *reinterpret_cast<uint4*>(Wd + (8 * j + r) * K + k0) = make_uint4(h[0], h[1], h[2], h[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// prefill: MFMA GEMM with a store epilogue
+// ---------------------------------------------------------------------------
+
+template <bool F16>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void w4a16_gemm_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wd,
+                       int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n,
+                       uint16_t* __restrict__ Y) {
+  int tm, tn;
+  if (!tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
+  const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
+  const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
+  const int64_t rows_b = N - n0 < BN ? N - n0 : BN;
+  GemmCtx c;
+  gemm_setup(c, X + m0 * K, rows_a, Wd + n0 * K, rows_b, K);
+  floatx16 acc[4][4];
+  gemm_mainloop<F16>(c, acc);
+
+  const int lane = threadIdx.x & 63;
+  const int wm = c.wave >> 1, wn = c.wave & 1;
+  const int64_t row0 = m0 + wm * 128 + 4 * (lane >> 5);
+  const int64_t col0 = n0 + wn * 128 + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = col0 + j * 32;
+      if (col >= N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = row0 + i * 32 + 8 * (v >> 2) + (v & 3);
+        if (row < M) Y[row * N + col] = to16<F16>(acc[i][j][v]);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// decode: fused GEMV
+// ---------------------------------------------------------------------------
+
+constexpr int kGemvCols = 64;     // word columns per workgroup (512 outputs)
+constexpr int kGemvWaves = 4;     // k runs per workgroup
+
+// Workgroup (cb, kc): word columns cb·64 .. cb·64+63, k rows kc·(4·kpw) ..;
+// wave w takes rows kc·4·kpw + w·kpw .. + kpw - 1. Lane = word column.
+// TT >= T is the register tile of token rows; rows T..TT-1 are zeros that
+// are neither read from X nor written.
+//
+// Per qweight word (8 output channels at one k): the nibbles are split into
+// bytes (w & 0x0F0F0F0F and (w >> 4) & 0x0F0F0F0F) and converted with the
+// byte-to-float instructions; ŵ = fma(q, scale, -z·scale) is exact (every
+// term is an integer of at most 4 bits times an fp16 value); then one FMA per
+// token row. Activations sit in LDS as [k][TT] so four token rows come in
+// one 16-byte read.
+template <bool F16, int TT>
+__global__ __launch_bounds__(256) void w4a16_gemv_kernel(
+    const uint16_t* __restrict__ X, int64_t T, int64_t N, int64_t K,
+    const int32_t* __restrict__ qweight, const int32_t* __restrict__ qzeros,
+    const uint16_t* __restrict__ scales, int group, int kpw, float* __restrict__ partial) {
+  constexpr int TR = TT < 4 ? TT : 4;            // token rows per cross-wave reduction pass
+  __shared__ float xs[kGemvWaves * 128][TT];
+  __shared__ float red[kGemvWaves - 1][TR][kGemvCols * 8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t N8 = N / 8;
+  const int64_t j = int64_t(blockIdx.x) * kGemvCols + lane;
+  const int64_t kchunk = int64_t(kGemvWaves) * kpw;
+  const int64_t kbase = int64_t(blockIdx.y) * kchunk;
+  // stage this chunk's activations as float32 (rows past T as zeros)
+  for (int e = threadIdx.x; e < TT * kchunk; e += 256) {
+    const int t = e / int(kchunk), kk = e % int(kchunk);
+    xs[kk][t] = t < T ? from16<F16>(X[t * K + kbase + kk]) : 0.f;
+  }
+  __syncthreads();
+
+  float acc[TT][8];
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[t][r] = 0.f;
+
+  if (j < N8) {
+    const int64_t k0 = kbase + int64_t(wave) * kpw;
+    float sc[8], zs[8];
+    int64_t g_cur = -1;
+    for (int kk = 0; kk < kpw; kk += 8) {
+      const int64_t k = k0 + kk;
+      if (k / group != g_cur) {
+        g_cur = k / group;
+        float zf[8];
+        group_params(qzeros, scales, N, g_cur, j, sc, zf);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) zs[r] = -(zf[r] * sc[r]);
+      }
+      uint32_t w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = uint32_t(qweight[(k + i) * N8 + j]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t ev = w[i] & 0x0F0F0F0Fu, od = (w[i] >> 4) & 0x0F0F0F0Fu;
+        float q[8];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          q[2 * b] = float((ev >> (8 * b)) & 0xFFu);
+          q[2 * b + 1] = float((od >> (8 * b)) & 0xFFu);
+        }
+        float xv[TT];
+        const int xk = wave * kpw + kk + i;
+#pragma unroll
+        for (int t = 0; t < TT; ++t) xv[t] = xs[xk][t];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float wv = __builtin_fmaf(q[r], sc[r], zs[r]);
+#pragma unroll
+          for (int t = 0; t < TT; ++t) acc[t][r] = __builtin_fmaf(xv[t], wv, acc[t][r]);
+        }
+      }
+    }
+  }
+  // waves 1..3 hand their sums to wave 0, TR token rows at a time
+#pragma unroll
+  for (int t0 = 0; t0 < TT; t0 += TR) {
+    if (t0 > 0) __syncthreads();
+    if (wave > 0) {
+#pragma unroll
+      for (int t = 0; t < TR; ++t)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) red[wave - 1][t][lane * 8 + r] = acc[t0 + t][r];
+    }
+    __syncthreads();
+    if (wave == 0 && j < N8) {
+#pragma unroll
+      for (int t = 0; t < TR; ++t) {
+        if (t0 + t >= T) break;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float s = ((acc[t0 + t][r] + red[0][t][lane * 8 + r]) + red[1][t][lane * 8 + r]) +
+                          red[2][t][lane * 8 + r];
+          partial[(int64_t(blockIdx.y) * T + t0 + t) * N + 8 * j + r] = s;
+        }
+      }
+    }
+  }
+}
+
+// Y[t][n] = Σ_c partial[c][t][n], chunks added in a fixed order (lane group
+// cl takes chunks cl, cl+4, ...; the four sums are then added in order),
+// rounded once. 64 outputs per workgroup.
+template <bool F16>
+__global__ __launch_bounds__(256) void w4a16_gemv_reduce_kernel(const float* __restrict__ partial,
+                                                                int64_t chunks, int64_t T,
+                                                                int64_t N,
+                                                                uint16_t* __restrict__ Y) {
+  __shared__ float red[4][64];
+  const int o = threadIdx.x & 63, cl = threadIdx.x >> 6;
+  const int64_t e = int64_t(blockIdx.x) * 64 + o;
+  float s = 0.f;
+  if (e < T * N) {
+#pragma unroll 8
+    for (int64_t c = cl; c < chunks; c += 4) s += partial[c * T * N + e];
+  }
+  red[cl][o] = s;
+  __syncthreads();
+  if (cl == 0 && e < T * N) Y[e] = to16<F16>(((red[0][o] + red[1][o]) + red[2][o]) + red[3][o]);
+}
+
+template <bool F16, int TT>
+void launch_gemv_t(dim3 grid, hipStream_t st, const uint16_t* X, int64_t T, int64_t N, int64_t K,
+                   const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                   int group, int kpw, float* partial) {
+  w4a16_gemv_kernel<F16, TT><<<grid, 256, 0, st>>>(X, T, N, K, qweight, qzeros, scales, group,
+                                                   kpw, partial);
+}
+
+template <bool F16>
+void launch_gemv(dim3 grid, hipStream_t st, const uint16_t* X, int64_t T, int64_t N, int64_t K,
+                 const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales, int group,
+                 int kpw, float* partial) {
+  if (T <= 1)
+    launch_gemv_t<F16, 1>(grid, st, X, T, N, K, qweight, qzeros, scales, group, kpw, partial);
+  else if (T <= 2)
+    launch_gemv_t<F16, 2>(grid, st, X, T, N, K, qweight, qzeros, scales, group, kpw, partial);
+  else if (T <= 4)
+    launch_gemv_t<F16, 4>(grid, st, X, T, N, K, qweight, qzeros, scales, group, kpw, partial);
+  else if (T <= 8)
+    launch_gemv_t<F16, 8>(grid, st, X, T, N, K, qweight, qzeros, scales, group, kpw, partial);
+  else
+    launch_gemv_t<F16, 16>(grid, st, X, T, N, K, qweight, qzeros, scales, group, kpw, partial);
+}
+
+}  // namespace
+
+hipError_t launch_w4a16_dequant(const int32_t* qweight, const int32_t* qzeros,
+                                const uint16_t* scales, int64_t N, int64_t K, int group, int f16,
+                                uint16_t* Wd, hipStream_t st) {
+  const int64_t lanes = (K / 8) * (N / 8);
+  const unsigned blocks = unsigned((lanes + 255) / 256);
+  if (f16)
+    dequant_kernel<true><<<blocks, 256, 0, st>>>(qweight, qzeros, scales, N, K, group, Wd);
+  else
+    dequant_kernel<false><<<blocks, 256, 0, st>>>(qweight, qzeros, scales, N, K, group, Wd);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a16_gemm(const uint16_t* X, const uint16_t* Wd, int64_t M, int64_t N,
+                             int64_t K, int f16, uint16_t* Y, hipStream_t st) {
+  if (K % 128) return hipErrorInvalidValue;
+  const int tiles_m = int((M + BM - 1) / BM), tiles_n = int((N + BN - 1) / BN);
+  const unsigned blocks = unsigned(gemm_blocks(tiles_m, tiles_n));
+  if (f16)
+    w4a16_gemm_kernel<true><<<blocks, NT, 0, st>>>(X, Wd, M, N, K, tiles_m, tiles_n, Y);
+  else
+    w4a16_gemm_kernel<false><<<blocks, NT, 0, st>>>(X, Wd, M, N, K, tiles_m, tiles_n, Y);
+  return hipGetLastError();
+}
+
+// 1 <= T <= 16 token rows; kpw in {32, 64, 128} with K a multiple of 4·kpw;
+// partial holds (K / (4·kpw)) x T x N floats.
+hipError_t launch_w4a16_gemv(const uint16_t* X, int64_t T, int64_t N, int64_t K,
+                             const int32_t* qweight, const int32_t* qzeros,
+                             const uint16_t* scales, int group, int f16, int64_t kpw,
+                             float* partial, hipStream_t st) {
+  const int64_t chunks = K / (kGemvWaves * kpw);
+  dim3 grid(unsigned((N / 8 + kGemvCols - 1) / kGemvCols), unsigned(chunks));
+  if (f16)
+    launch_gemv<true>(grid, st, X, T, N, K, qweight, qzeros, scales, group, int(kpw), partial);
+  else
+    launch_gemv<false>(grid, st, X, T, N, K, qweight, qzeros, scales, group, int(kpw), partial);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4a16_gemv_reduce(const float* partial, int64_t chunks, int64_t T, int64_t N,
+                                    int f16, uint16_t* Y, hipStream_t st) {
+  const unsigned rblocks = unsigned((T * N + 63) / 64);
+  if (f16)
+    w4a16_gemv_reduce_kernel<true><<<rblocks, 256, 0, st>>>(partial, chunks, T, N, Y);
+  else
+    w4a16_gemv_reduce_kernel<false><<<rblocks, 256, 0, st>>>(partial, chunks, T, N, Y);
+  return hipGetLastError();
+}
+
+}  // namespace awq

@@ -12,6 +12,14 @@
       times; prints the average kernel time from the library's HIP-event
       timing and the bandwidth it implies (each element read and written once).
 
+  python -m post_weight_quantization_26_amd.profile_run w4a16 [--reps 20]
+      The consumer of the packed layout: the fused GEMV at decode sizes
+      (T = 1 and 16 token rows) and the dequantise + MFMA GEMM path at
+      T = 4096, on the 4096 x 4096 attention projection and the
+      28672 x 8192 70B-class MLP layer (bf16 activations, group 128).
+      Prints one JSON line per case with the library's HIP-event kernel times
+      and the achieved HBM bandwidth (GEMV) or TFLOP/s (GEMM).
+
 The search workload itself is profiled through ``bench.py``.
 """
 from __future__ import annotations
@@ -60,16 +68,70 @@ def fold(reps: int) -> None:
           f"({n // reps} launches), {moved / (rows_ms / 1e3) / 1e9:.0f} GB/s", flush=True)
 
 
+def w4a16(reps: int) -> None:
+    import json
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    if root not in sys.path:
+        sys.path.insert(0, root)
+    import torch
+    from post_weight_quantization_26_amd import api
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    for N, K in ((4096, 4096), (28672, 8192)):
+        W = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        s = torch.ones(K, dtype=torch.float32, device=dev)
+        qw, qz, sc = api.quantize_pack(W, s)
+        del W
+        for T in (1, 16, 4096):
+            X = torch.randn((T, K), generator=g, device=dev).to(torch.bfloat16)
+            ws = torch.empty(api.w4a16_workspace_bytes(T, N, K, torch.bfloat16), dtype=torch.uint8,
+                             device=dev)
+            Y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+            n_rep = reps if T <= 16 else max(3, reps // 4)
+            api.w4a16_matmul(X, qw, qz, sc, ws=ws, out=Y)
+            torch.cuda.synchronize()
+            api.profile_enable(True)
+            api.profile_reset()
+            for _ in range(n_rep):
+                api.w4a16_matmul(X, qw, qz, sc, ws=ws, out=Y)
+            torch.cuda.synchronize()
+            t = {k: api.profile_read(k) for k in ("dequant", "w4a16", "w4a16_reduce")}
+            api.profile_enable(False)
+            main_us = t["w4a16"][0] * 1e3 / n_rep
+            rec = {"N": N, "K": K, "T": T, "main_kernel_us": round(main_us, 2)}
+            packed = N * K // 2 + (N * K // 128) * (2 + 0.5)
+            if T <= 16:
+                chunks = ws.numel() // (T * N * 4)
+                moved = packed + T * K * 2 + chunks * T * N * 4
+                rec.update(path="gemv", reduce_us=round(t["w4a16_reduce"][0] * 1e3 / n_rep, 2),
+                           algorithmic_bytes=int(moved),
+                           GBps=round(moved / (main_us * 1e-6) / 1e9, 1),
+                           frac_of_8TBps=round(moved / (main_us * 1e-6) / 8e12, 4))
+            else:
+                flops = 2.0 * T * N * K
+                rec.update(path="gemm", dequant_us=round(t["dequant"][0] * 1e3 / n_rep, 2),
+                           TFLOPs=round(flops / (main_us * 1e-6) / 1e12, 1),
+                           frac_of_2500=round(flops / (main_us * 1e-6) / 2.5e15, 4))
+            print(json.dumps(rec), flush=True)
+            del X, ws, Y
+        del qw, qz, sc
+        torch.cuda.empty_cache()
+
+
 def main(argv=None) -> int:
     p = argparse.ArgumentParser()
-    p.add_argument("what", choices=["copy", "fold"])
+    p.add_argument("what", choices=["copy", "fold", "w4a16"])
     p.add_argument("--mib", type=int, default=1024)
     p.add_argument("--reps", type=int, default=20)
     a = p.parse_args(argv)
     if a.what == "copy":
         copy(a.mib)
-    else:
+    elif a.what == "fold":
         fold(a.reps)
+    else:
+        w4a16(a.reps)
     return 0
 
 

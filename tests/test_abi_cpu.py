@@ -244,3 +244,39 @@ def test_profile_kinds_match_header(L):
             (name == "scale" and re.search(rf"AWQ_K_SCALE\s*=\s*{kind}\b", src)), name
     count = int(re.search(r"AWQ_K_COUNT\s*=\s*(\d+)", src).group(1))
     assert count == len(L.KERNEL_KINDS)
+
+
+def test_w4a16_workspace_and_rejects(L):
+    lib = L.lib()
+    wsb = lib.awq_w4a16_workspace_bytes
+    # GEMM path (T > 16): the dequantised [N, K] operand rows
+    assert wsb(4096, 4096, 4096, L.AWQ_BF16) == 4096 * 4096 * 2
+    # GEMV path: float32 partials per k chunk, token row and output channel
+    one = wsb(1, 4096, 4096, L.AWQ_BF16)
+    assert one > 0 and one % (4096 * 4) == 0 and one <= 32 * 4096 * 4
+    assert wsb(16, 4096, 4096, L.AWQ_F16) == 16 * one
+    for bad in ((0, 8, 128, 1), (1, 12, 128, 1), (1, 8, 200, 1), (1, 8, 128, 0), (1, 8, 128, 9)):
+        assert wsb(*bad) == 0
+    f = lib.awq_w4a16_matmul
+
+    def call(**k):
+        a = dict(X=FAKE, dt=L.AWQ_BF16, T=4, N=64, K=256, qw=FAKE, qz=FAKE, sc=FAKE, g=128,
+                 Y=FAKE, ws=FAKE, wsb=1 << 30)
+        a.update(k)
+        return f(a["X"], a["dt"], a["T"], a["N"], a["K"], a["qw"], a["qz"], a["sc"], a["g"],
+                 a["Y"], a["ws"], a["wsb"], None)
+
+    assert call(X=None) == -1
+    assert call(Y=None) == -1
+    assert call(dt=L.AWQ_F32) == -2
+    assert call(dt=9) == -1
+    assert call(T=0) == -1
+    assert call(N=12) == -1
+    assert call(K=200) == -1
+    assert call(g=16) == -2
+    assert call(X=MIS) == -1
+    assert call(sc=ctypes.c_void_p(0x10008)) == -1        # scales need 16-byte alignment
+    assert call(Y=ctypes.c_void_p(0x10001)) == -1
+    assert call(wsb=16) == -3
+    assert call(ws=MIS) == -3
+    assert "w4a16_matmul" in L.last_error()
