@@ -39,6 +39,10 @@ def parse():
     p.add_argument("--config", default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=2048)
+    p.add_argument("--method", choices=["direct", "gram"], default="direct",
+                   help="candidate errors as X·Eᵀ (direct) or E·G·Eᵀ with G = XᵀX (gram)")
+    p.add_argument("--no-gram", action="store_true",
+                   help="skip the second measurement through the Gram path")
     return p.parse_args()
 
 
@@ -138,8 +142,16 @@ def main():
     ws_stats = torch.empty(api.workspace_bytes(_lib.AWQ_OP_STATS, T, 1, K, 1, tdt),
                            dtype=torch.uint8, device=dev)
     n_grid = max(cfg.n_alpha, cfg.n_ratio)
-    ws_search = torch.empty(api.workspace_bytes(_lib.AWQ_OP_SEARCH_SCALE, T, N, K, n_grid, tdt),
-                            dtype=torch.uint8, device=dev)
+    method = args.method
+    gram_ok = not cfg.layers and cfg.dtype == "bf16"
+    if method == "gram" and not gram_ok:
+        print(json.dumps({"error": "the Gram path runs single bf16 layers"}))
+        sys.exit(2)
+    ws_need = api.workspace_bytes(_lib.AWQ_OP_SEARCH_SCALE, T, N, K, n_grid, tdt)
+    if gram_ok:
+        ws_need = max(ws_need, api.workspace_bytes(_lib.AWQ_OP_SEARCH_SCALE_GRAM, T, N, K, n_grid,
+                                                   tdt))
+    ws_search = torch.empty(ws_need, dtype=torch.uint8, device=dev)
     ws_pack = torch.empty(256, dtype=torch.uint8, device=dev)
     abar = torch.empty(K, dtype=torch.float32, device=dev)
     G = cfg.group
@@ -148,8 +160,9 @@ def main():
                  torch.empty((K // G, Wd.shape[0]), dtype=torch.float16, device=dev))
                 for Wd in Wds]
     zp = cfg.zero_point
+    cands_per_step = cfg.n_alpha + (cfg.n_ratio or 0)   # clip candidates: per layer, N rows in all
 
-    def step():
+    def step(how):
         api.act_stats(Xd, ws=ws_stats, out=abar)
         if cfg.layers:
             # linears sharing X: one search, one s, folded into the norm weight
@@ -159,43 +172,72 @@ def main():
             api.fold_norm(gamma, res["s_best"])
         else:
             res = api.search_scale(Xd, Wds[0], abar, alphas, bits=cfg.bits, group=G,
-                                   zero_point=zp, ws=ws_search)
+                                   zero_point=zp, ws=ws_search, method=how)
         for Wd, out in zip(Wds, pack_out):
             ratio = None
             if ratios is not None:
                 ratio = api.search_clip(Xd, Wd, res["s_best"], ratios, bits=cfg.bits, group=G,
-                                        zero_point=zp, ws=ws_search)["ratio_best"]
+                                        zero_point=zp, ws=ws_search, method=how)["ratio_best"]
             if cfg.pack:
                 api.quantize_pack(Wd, res["s_best"], ratio, bits=cfg.bits, group=G, zero_point=zp,
                                   ws=ws_pack, out=out)
         return res
 
-    for _ in range(args.warmup):
-        res = step()
-    torch.cuda.synchronize()
-    api.profile_enable(True)
-    api.profile_reset()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        res = step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    prof = {k: api.profile_read(k) for k in _lib.KERNEL_KINDS}
-    api.profile_enable(False)
+    def measure(how):
+        """Warm-up, then exactly args.steps timed steps between synchronisations;
+        kernel times from the library's HIP events on the launch stream."""
+        for _ in range(args.warmup):
+            step(how)
+        torch.cuda.synchronize()
+        api.profile_enable(True)
+        api.profile_reset()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            res = step(how)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        prof = {k: api.profile_read(k) for k in _lib.KERNEL_KINDS}
+        api.profile_enable(False)
+        elapsed = t1 - t0
+        if how == "gram":
+            # [G_hi | G_lo]·Eᵀ: 2·(2K)·K flops per candidate row
+            gemm_ms, gemm_n = prof["gram_search"]
+            flops_per_step = 2.0 * (2 * K) * K * N * cands_per_step
+            kernel_name = "gram_search_kernel"
+        else:
+            gemm_ms, gemm_n = prof["gemm"]
+            flops_per_step = 2.0 * T * N * K * cands_per_step
+            kernel_name = "search_gemm_bf16_kernel"
+        gemm_avg_s = gemm_ms / 1e3 / max(gemm_n, 1)
+        launches_per_step = gemm_n // args.steps if args.steps else 0
+        flops_per_launch = flops_per_step / max(launches_per_step, 1)
+        achieved = flops_per_launch / gemm_avg_s / 1e12
+        traffic = gemm_traffic(name, launches_per_step) if how == "direct" else None
+        roof = {"bound": "mfma", "achieved": round(achieved, 2),
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic, "kernel": kernel_name,
+                "avg_launch_us": round(gemm_avg_s * 1e6, 1),
+                "algorithmic_flops_per_launch": flops_per_launch}
+        kernels = {k: {"avg_us": round(ms * 1e3 / n, 2) if n else None, "launches": n,
+                       "share_of_step": round(ms / (elapsed * 1e3), 4)}
+                   for k, (ms, n) in prof.items() if n}
+        return elapsed, prof, res, roof, kernels
 
-    elapsed = t1 - t0
-    cands_per_step = cfg.n_alpha + (cfg.n_ratio or 0)   # clip candidates: per layer, N rows in all
+    elapsed, prof, res, roofline, kernels = measure(method)
     value = cfg.n_alpha * args.steps / elapsed
-    gemm_ms, gemm_n = prof["gemm"]
-    gemm_avg_s = gemm_ms / 1e3 / max(gemm_n, 1)
-    launches_per_step = gemm_n // args.steps if args.steps else 0
-    flops_per_launch = 2.0 * T * N * K * cands_per_step / max(launches_per_step, 1)
-    achieved = flops_per_launch / gemm_avg_s / 1e12
-    traffic = gemm_traffic(name, launches_per_step)
-    kernels = {k: {"avg_us": round(ms * 1e3 / n, 2) if n else None, "launches": n,
-                   "share_of_step": round(ms / (elapsed * 1e3), 4)}
-               for k, (ms, n) in prof.items()}
+    achieved = roofline["achieved"]
+    other = None
+    if method == "direct" and gram_ok and not args.no_gram:
+        g_el, _, g_res, g_roof, g_kern = measure("gram")
+        other = {"method": "gram", "value": round(cfg.n_alpha * args.steps / g_el, 3),
+                 "all_candidates_per_s": round(cands_per_step * args.steps / g_el, 3),
+                 "ms_per_step": round(g_el / args.steps * 1e3, 3),
+                 "alpha_best": float(g_res["alpha_best"]), "roofline": g_roof,
+                 "kernels": g_kern,
+                 "note": "same candidates through G = X^T X: E.G.E^T per row "
+                         "(2*(2K)*K flops) plus G once per search call (2*T*K^2)"}
     stats_ms, stats_n = prof["stats"]
     stats_gbs = (T * K * X.itemsize) / (stats_ms / 1e3 / max(stats_n, 1)) / 1e9 if stats_n else None
     pack_ms, pack_n = prof["pack"]
@@ -219,13 +261,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "T": T, "N": N, "K": K, "group": cfg.group, "bits": cfg.bits,
                    "zero_point": zp, "n_alpha": cfg.n_alpha, "n_ratio": cfg.n_ratio,
-                   "pack": cfg.pack, "layers": list(cfg.layers) or None},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "search_gemm_bf16_kernel",
-                     "avg_launch_us": round(gemm_avg_s * 1e6, 1),
-                     "algorithmic_flops_per_launch": flops_per_launch},
+                   "pack": cfg.pack, "layers": list(cfg.layers) or None, "method": method},
+        "roofline": roofline,
         "mfma_util_pct": round(100 * achieved / MFMA_BF16_PEAK_TFLOPS, 2),
         "hbm": {"stats_GBps": None if stats_gbs is None else round(stats_gbs, 1),
                 "pack_GBps": None if pack_gbs is None else round(pack_gbs, 1),
@@ -235,6 +272,8 @@ def main():
         "mse_alpha0": float(res["mse"][0]),
         "mse_best": float(res["mse"].min()),
     }
+    if other is not None:
+        out["gram"] = other
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, X, Ws, alphas, args.cpu_rows)
     print(json.dumps(out), flush=True)

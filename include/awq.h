@@ -85,7 +85,8 @@ typedef struct {
   int32_t zero_point;
 } awq_qconfig;
 
-enum { AWQ_OP_STATS = 0, AWQ_OP_SEARCH_SCALE = 1, AWQ_OP_SEARCH_CLIP = 2, AWQ_OP_PACK = 3 };
+enum { AWQ_OP_STATS = 0, AWQ_OP_SEARCH_SCALE = 1, AWQ_OP_SEARCH_CLIP = 2, AWQ_OP_PACK = 3,
+       AWQ_OP_SEARCH_SCALE_GRAM = 4, AWQ_OP_SEARCH_CLIP_GRAM = 5 };
 
 /* Workspace bytes that let `op` process all `n_grid` candidates in one
  * batch (the fastest configuration). Returns 0 for invalid sizes. Pure host
@@ -159,6 +160,29 @@ awq_status awq_quantize_pack(const void* W, awq_dtype w_dtype, int64_t N, int64_
                              int32_t* qzeros, uint16_t* scales, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* The same two searches through the Gram matrix G = XᵀX of the activations:
+ * M_n = Σ_t (X·E_nᵀ)_t² = E_n·G·E_nᵀ, an exact identity of the error measure
+ * ("05 — AWQ", section 4; the identity itself is not on the pages). G is
+ * built once per call (2·T·K² flops, stored as two bf16 halves hi + lo), then
+ * each candidate row costs 2·(2K)·K instead of 2·T·K: T/(2K) times fewer
+ * flops (8x at 64K tokens and K = 4096). The candidates' error weights are
+ * the same bf16 operands as on the direct path; only the float32 rounding
+ * order of the sums differs. Arguments, outputs and synchronisation as in
+ * awq_search_scale / awq_search_clip; bf16 inputs only; T <= 2^22. The
+ * workspace (awq_workspace_bytes with AWQ_OP_SEARCH_SCALE_GRAM /
+ * AWQ_OP_SEARCH_CLIP_GRAM) also holds Xᵀ (K x T, tokens padded to 128) and
+ * the [K, 2K] halves of G. */
+awq_status awq_search_scale_gram(const void* X, const void* W, awq_dtype dtype, int64_t T,
+                                 int64_t N, int64_t K, const float* abar, const float* alphas,
+                                 int32_t n_alpha, awq_qconfig qc, float* s_best,
+                                 float* alpha_best, double* mse, double* row_sums, void* ws,
+                                 size_t ws_bytes, void* stream);
+awq_status awq_search_clip_gram(const void* X, const void* W, awq_dtype dtype, int64_t T,
+                                int64_t N, int64_t K, const float* s, const float* ratios,
+                                int32_t n_ratio, awq_qconfig qc, float* ratio_best,
+                                double* mse_clip, double* row_sums, void* ws, size_t ws_bytes,
+                                void* stream);
+
 /* Steps 2-6 for a group of linears that read the same X (e.g. the query,
  * key and value projections after one normalisation, or the gate and up
  * projections). The division by s can go into only one preceding operation,
@@ -229,10 +253,11 @@ const char* awq_last_error(void);
  * duration (ms) and launch count of one kernel kind since the last reset.
  * Kinds: 0 stats, 1 scale table, 2 transform (quantise/dequantise
  * candidates), 3 search GEMM, 4 reductions, 5 pack, 6 fold, 7 W4A16
- * dequantisation, 8 W4A16 GEMM or GEMV, 9 W4A16 GEMV reduction. */
+ * dequantisation, 8 W4A16 GEMM or GEMV, 9 W4A16 GEMV reduction, 10 Gram
+ * matrix build (transpose + G), 11 Gram-path candidate GEMM. */
 enum { AWQ_K_STATS = 0, AWQ_K_SCALE = 1, AWQ_K_TRANSFORM = 2, AWQ_K_GEMM = 3, AWQ_K_REDUCE = 4,
        AWQ_K_PACK = 5, AWQ_K_FOLD = 6, AWQ_K_DEQUANT = 7, AWQ_K_W4A16 = 8,
-       AWQ_K_W4A16_REDUCE = 9, AWQ_K_COUNT = 10 };
+       AWQ_K_W4A16_REDUCE = 9, AWQ_K_GRAM_BUILD = 10, AWQ_K_GRAM_SEARCH = 11, AWQ_K_COUNT = 12 };
 void awq_profile_enable(int on);
 void awq_profile_reset(void);
 awq_status awq_profile_read(int kind, double* total_ms, int64_t* launches);

@@ -19,8 +19,10 @@ STATUS_NAMES = {0: "AWQ_OK", -1: "AWQ_E_INVALID", -2: "AWQ_E_UNSUPPORTED", -3: "
                 -4: "AWQ_E_RANGE", -5: "AWQ_E_HIP"}
 AWQ_F32, AWQ_BF16, AWQ_F16 = 0, 1, 2
 AWQ_OP_STATS, AWQ_OP_SEARCH_SCALE, AWQ_OP_SEARCH_CLIP, AWQ_OP_PACK = 0, 1, 2, 3
+AWQ_OP_SEARCH_SCALE_GRAM, AWQ_OP_SEARCH_CLIP_GRAM = 4, 5
 KERNEL_KINDS = {"stats": 0, "scale": 1, "transform": 2, "gemm": 3, "reduce": 4, "pack": 5,
-                "fold": 6, "dequant": 7, "w4a16": 8, "w4a16_reduce": 9}
+                "fold": 6, "dequant": 7, "w4a16": 8, "w4a16_reduce": 9, "gram_build": 10,
+                "gram_search": 11}
 
 
 class QConfig(ctypes.Structure):
@@ -46,6 +48,12 @@ SIGNATURES = {
                                        c_i32, QConfig, c_vp, c_dp, c_vp, c_vp, c_sz, c_vp]),
     "awq_quantize_pack": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_vp, c_vp, QConfig,
                                          c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "awq_search_scale_gram": (ctypes.c_int, [c_vp, c_vp, ctypes.c_int, c_i64, c_i64, c_i64, c_vp,
+                                             c_fp, c_i32, QConfig, c_vp, c_fp, c_dp, c_vp, c_vp,
+                                             c_sz, c_vp]),
+    "awq_search_clip_gram": (ctypes.c_int, [c_vp, c_vp, ctypes.c_int, c_i64, c_i64, c_i64, c_vp,
+                                            c_fp, c_i32, QConfig, c_vp, c_dp, c_vp, c_vp, c_sz,
+                                            c_vp]),
     "awq_search_scale_group": (ctypes.c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_i64),
                                               c_i32, ctypes.c_int, c_i64, c_i64, c_vp, c_fp,
                                               c_i32, QConfig, c_vp, c_fp, c_dp, c_vp, c_vp,

@@ -85,28 +85,41 @@ def scale_table(abar: torch.Tensor, alphas: Sequence[float]) -> torch.Tensor:
     return out
 
 
+_METHODS = ("direct", "gram")
+
+
+def _method(method: str) -> bool:
+    if method not in _METHODS:
+        raise ValueError(f"method must be one of {_METHODS}")
+    return method == "gram"
+
+
 def search_scale(X: torch.Tensor, W: torch.Tensor, abar: torch.Tensor, alphas: Sequence[float],
                  bits: int = DEFAULT_BITS, group: int = DEFAULT_GROUP,
                  zero_point: bool = DEFAULT_ZERO_POINT, want_row_sums: bool = False,
-                 ws: Optional[torch.Tensor] = None) -> dict:
+                 ws: Optional[torch.Tensor] = None, method: str = "direct") -> dict:
     """Grid search over alpha. Returns alpha_best, index, s_best [K], mse (numpy
-    [n_alpha]) and, if asked, row_sums [n_alpha, N] float64 on the GPU."""
+    [n_alpha]) and, if asked, row_sums [n_alpha, N] float64 on the GPU.
+    method "direct" measures X·Eᵀ per candidate; "gram" (bf16 only) uses the
+    activations' Gram matrix, E·G·Eᵀ per candidate row."""
+    gram = _method(method)
     _dev(X, "X"), _dev(W, "W"), _dev(abar, "abar")
     if X.dtype != W.dtype:
         raise ValueError("X and W must share a dtype")
     T, K = X.shape
     N = W.shape[0]
     n = len(alphas)
-    ws = _workspace(ws, workspace_bytes(L.AWQ_OP_SEARCH_SCALE, T, N, K, n, X.dtype), X.device)
+    op = L.AWQ_OP_SEARCH_SCALE_GRAM if gram else L.AWQ_OP_SEARCH_SCALE
+    ws = _workspace(ws, workspace_bytes(op, T, N, K, n, X.dtype), X.device)
     s_best = torch.empty(K, dtype=torch.float32, device=X.device)
     rows = torch.empty((n, N), dtype=torch.float64, device=X.device) if want_row_sums else None
     a_best = ctypes.c_float(0.0)
     mse = (ctypes.c_double * n)()
     grid = L.float_array(alphas)
-    L.check(L.lib().awq_search_scale(_ptr(X), _ptr(W), _dtype(X), T, N, K, _ptr(abar), grid, n,
-                                     qconfig(bits, group, zero_point), _ptr(s_best),
-                                     ctypes.byref(a_best), mse, _ptr(rows), _ptr(ws), ws.numel(),
-                                     _stream()))
+    fn = L.lib().awq_search_scale_gram if gram else L.lib().awq_search_scale
+    L.check(fn(_ptr(X), _ptr(W), _dtype(X), T, N, K, _ptr(abar), grid, n,
+               qconfig(bits, group, zero_point), _ptr(s_best), ctypes.byref(a_best), mse,
+               _ptr(rows), _ptr(ws), ws.numel(), _stream()))
     mse_np = np.array(mse[:], dtype=np.float64)
     g32 = np.asarray(alphas, dtype=np.float32)
     idx = int(np.flatnonzero(g32 == np.float32(a_best.value))[0])
@@ -183,23 +196,26 @@ def fold_linear(W_prev: torch.Tensor, s: torch.Tensor, bias: Optional[torch.Tens
 def search_clip(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor, ratios: Sequence[float],
                 bits: int = DEFAULT_BITS, group: int = DEFAULT_GROUP,
                 zero_point: bool = DEFAULT_ZERO_POINT, want_row_sums: bool = False,
-                ws: Optional[torch.Tensor] = None) -> dict:
+                ws: Optional[torch.Tensor] = None, method: str = "direct") -> dict:
     """Per-output-channel clip-ratio search with s fixed. Returns ratio_best [N]
-    (GPU), mse_clip (float) and optionally row_sums [n_ratio, N]."""
+    (GPU), mse_clip (float) and optionally row_sums [n_ratio, N]. method as in
+    search_scale."""
+    gram = _method(method)
     _dev(X, "X"), _dev(W, "W"), _dev(s, "s")
     if X.dtype != W.dtype:
         raise ValueError("X and W must share a dtype")
     T, K = X.shape
     N = W.shape[0]
     n = len(ratios)
-    ws = _workspace(ws, workspace_bytes(L.AWQ_OP_SEARCH_CLIP, T, N, K, n, X.dtype), X.device)
+    op = L.AWQ_OP_SEARCH_CLIP_GRAM if gram else L.AWQ_OP_SEARCH_CLIP
+    ws = _workspace(ws, workspace_bytes(op, T, N, K, n, X.dtype), X.device)
     r_best = torch.empty(N, dtype=torch.float32, device=X.device)
     rows = torch.empty((n, N), dtype=torch.float64, device=X.device) if want_row_sums else None
     mse_clip = ctypes.c_double(0.0)
-    L.check(L.lib().awq_search_clip(_ptr(X), _ptr(W), _dtype(X), T, N, K, _ptr(s),
-                                    L.float_array(ratios), n, qconfig(bits, group, zero_point),
-                                    _ptr(r_best), ctypes.byref(mse_clip), _ptr(rows), _ptr(ws),
-                                    ws.numel(), _stream()))
+    fn = L.lib().awq_search_clip_gram if gram else L.lib().awq_search_clip
+    L.check(fn(_ptr(X), _ptr(W), _dtype(X), T, N, K, _ptr(s), L.float_array(ratios), n,
+               qconfig(bits, group, zero_point), _ptr(r_best), ctypes.byref(mse_clip), _ptr(rows),
+               _ptr(ws), ws.numel(), _stream()))
     return dict(ratio_best=r_best, mse_clip=float(mse_clip.value), row_sums=rows)
 
 

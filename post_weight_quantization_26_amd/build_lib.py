@@ -24,7 +24,8 @@ LIB_NAME = "libawq_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = ["abi.cpp", "validate.cpp", "stats.hip", "scale.hip", "transform.hip", "gemm.hip",
-           "reduce.hip", "pack.hip", "fold.hip", "w4a16.hip"]
+           "reduce.hip", "pack.hip", "fold.hip", "w4a16.hip",
+           "gram.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-ffp-contract=off",
           "-fhip-fp32-correctly-rounded-divide-sqrt",

@@ -43,6 +43,10 @@ hipError_t launch_w4a16_gemv(const uint16_t* X, int64_t T, int64_t N, int64_t K,
                              float* partial, hipStream_t st);
 hipError_t launch_w4a16_gemv_reduce(const float* partial, int64_t chunks, int64_t T, int64_t N,
                                     int f16, uint16_t* Y, hipStream_t st);
+hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, uint16_t* Xt,
+                             uint16_t* Gs, hipStream_t st);
+hipError_t launch_gram_search(const uint16_t* Gs, const void* E, int64_t K, int64_t Nc,
+                              float* partials, hipStream_t st);
 hipError_t launch_fold_vec(void* v, int dtype, int64_t K, const float* s, hipStream_t st);
 hipError_t launch_fold_rows(void* W, int dtype, int64_t K, int64_t K_prev, const float* s,
                             hipStream_t st);
@@ -128,10 +132,13 @@ struct Segment {
 
 // Runs transform -> GEMM -> row reduction for candidates [c0, c0+cb). E holds
 // candidate blocks of N rows each; every segment fills its rows of every block.
+// With Gs (the Gram halves of G) the candidate GEMM is E·G·Eᵀ per row instead
+// of the direct X·Eᵀ.
 awq_status run_batch(const void* X, const Segment* seg, int n_seg, awq_dtype d, int64_t T,
                      int64_t N, int64_t K, const float* s_rows, const float* inv_rows,
                      int64_t s_stride, const float* ratios_host, int cb, awq_qconfig qc,
-                     const SearchLayout& L, void* ws, double* row_sums_out, hipStream_t st) {
+                     const SearchLayout& L, void* ws, double* row_sums_out, hipStream_t st,
+                     const uint16_t* Gs = nullptr) {
   void* E = at<void>(ws, L.E);
   float* partials = at<float>(ws, L.partials);
   for (int l = 0; l < n_seg; ++l) {
@@ -144,9 +151,16 @@ awq_status run_batch(const void* X, const Segment* seg, int n_seg, awq_dtype d, 
                   }),
             "transform");
   }
-  AWQ_HIP(timed(AWQ_K_GEMM, st,
-                [&] { return launch_search_gemm(X, dt(d), E, T, int64_t(cb) * N, K, partials, st); }),
-          "search_gemm");
+  if (Gs)
+    AWQ_HIP(timed(AWQ_K_GRAM_SEARCH, st,
+                  [&] { return launch_gram_search(Gs, E, K, int64_t(cb) * N, partials, st); }),
+            "gram_search");
+  else
+    AWQ_HIP(timed(AWQ_K_GEMM, st,
+                  [&] {
+                    return launch_search_gemm(X, dt(d), E, T, int64_t(cb) * N, K, partials, st);
+                  }),
+            "search_gemm");
   AWQ_HIP(timed(AWQ_K_REDUCE, st,
                 [&] { return launch_reduce_rows(partials, L.MT, int64_t(cb) * N, row_sums_out, st); }),
           "reduce_rows");
@@ -186,14 +200,32 @@ extern "C" awq_status awq_scale_table(const float* abar, int64_t K, const float*
 
 namespace {
 
+// Builds [G_hi | G_lo] of G = XᵀX into the workspace of a Gram search.
+awq_status build_gram(const void* X, int64_t T, int64_t K, const SearchLayout& L, void* ws,
+                      hipStream_t st) {
+  uint16_t* Xt = at<uint16_t>(ws, L.xt);
+  uint16_t* Gs = at<uint16_t>(ws, L.gs);
+  AWQ_HIP(timed(AWQ_K_GRAM_BUILD, st,
+                [&] { return launch_gram_build(X, T, K, L.Tp, Xt, Gs, st); }),
+          "gram_build");
+  return AWQ_OK;
+}
+
 // α search over the layers of `seg` (one layer, or several reading the same
-// X), already validated; N is their total output channels.
-awq_status search_scale_impl(const void* X, const Segment* seg, int n_seg, awq_dtype dtype,
-                             int64_t T, int64_t N, int64_t K, const float* abar,
+// X), already validated; N is their total output channels. op selects the
+// direct or the Gram candidate GEMM.
+awq_status search_scale_impl(int op, const void* X, const Segment* seg, int n_seg,
+                             awq_dtype dtype, int64_t T, int64_t N, int64_t K, const float* abar,
                              const float* alphas, int32_t n_alpha, awq_qconfig qc, float* s_best,
                              float* alpha_best, double* mse, double* row_sums, void* ws,
                              int32_t nb, hipStream_t st) {
-  const SearchLayout L = search_layout(AWQ_OP_SEARCH_SCALE, T, N, K, n_alpha, nb, dtype);
+  const SearchLayout L = search_layout(op, T, N, K, n_alpha, nb, dtype);
+  const uint16_t* Gs = nullptr;
+  if (is_gram_op(op)) {
+    awq_status g = build_gram(X, T, K, L, ws, st);
+    if (g != AWQ_OK) return g;
+    Gs = at<uint16_t>(ws, L.gs);
+  }
   float* s_table = at<float>(ws, L.s_table);
   float* inv_table = at<float>(ws, L.inv);
   double* rs = at<double>(ws, L.row_sums);
@@ -208,7 +240,7 @@ awq_status search_scale_impl(const void* X, const Segment* seg, int n_seg, awq_d
     const int cb = n_alpha - c0 < nb ? n_alpha - c0 : nb;
     awq_status s = run_batch(X, seg, n_seg, dtype, T, N, K, s_table + int64_t(c0) * K,
                              inv_table + int64_t(c0) * K, K, nullptr, cb, qc, L, ws,
-                             rs + int64_t(c0) * N, st);
+                             rs + int64_t(c0) * N, st, Gs);
     if (s != AWQ_OK) return s;
   }
   AWQ_HIP(timed(AWQ_K_REDUCE, st,
@@ -245,8 +277,25 @@ extern "C" awq_status awq_search_scale(const void* X, const void* W, awq_dtype d
                               qc, s_best, alpha_best, mse, ws, ws_bytes, &nb);
   if (s != AWQ_OK) return s;
   const Segment seg{W, N, 0};
-  return search_scale_impl(X, &seg, 1, dtype, T, N, K, abar, alphas, n_alpha, qc, s_best,
-                           alpha_best, mse, row_sums, ws, nb, static_cast<hipStream_t>(stream));
+  return search_scale_impl(AWQ_OP_SEARCH_SCALE, X, &seg, 1, dtype, T, N, K, abar, alphas,
+                           n_alpha, qc, s_best, alpha_best, mse, row_sums, ws, nb,
+                           static_cast<hipStream_t>(stream));
+}
+
+extern "C" awq_status awq_search_scale_gram(const void* X, const void* W, awq_dtype dtype,
+                                            int64_t T, int64_t N, int64_t K, const float* abar,
+                                            const float* alphas, int32_t n_alpha,
+                                            awq_qconfig qc, float* s_best, float* alpha_best,
+                                            double* mse, double* row_sums, void* ws,
+                                            size_t ws_bytes, void* stream) {
+  int32_t nb = 0;
+  awq_status s = check_search(AWQ_OP_SEARCH_SCALE_GRAM, X, W, dtype, T, N, K, abar, alphas,
+                              n_alpha, qc, s_best, alpha_best, mse, ws, ws_bytes, &nb);
+  if (s != AWQ_OK) return s;
+  const Segment seg{W, N, 0};
+  return search_scale_impl(AWQ_OP_SEARCH_SCALE_GRAM, X, &seg, 1, dtype, T, N, K, abar, alphas,
+                           n_alpha, qc, s_best, alpha_best, mse, row_sums, ws, nb,
+                           static_cast<hipStream_t>(stream));
 }
 
 extern "C" awq_status awq_search_scale_group(const void* X, const void* const* W,
@@ -269,34 +318,36 @@ extern "C" awq_status awq_search_scale_group(const void* X, const void* const* W
     seg[l] = Segment{W[l], N[l], row0};
     row0 += N[l];
   }
-  return search_scale_impl(X, seg, n_layers, dtype, T, N_total, K, abar, alphas, n_alpha, qc,
-                           s_best, alpha_best, mse, row_sums, ws, nb,
+  return search_scale_impl(AWQ_OP_SEARCH_SCALE, X, seg, n_layers, dtype, T, N_total, K, abar,
+                           alphas, n_alpha, qc, s_best, alpha_best, mse, row_sums, ws, nb,
                            static_cast<hipStream_t>(stream));
 }
 
-extern "C" awq_status awq_search_clip(const void* X, const void* W, awq_dtype dtype, int64_t T,
-                                      int64_t N, int64_t K, const float* s, const float* ratios,
-                                      int32_t n_ratio, awq_qconfig qc, float* ratio_best,
-                                      double* mse_clip, double* row_sums, void* ws,
-                                      size_t ws_bytes, void* stream) {
-  int32_t nb = 0;
-  awq_status st_ = check_search(AWQ_OP_SEARCH_CLIP, X, W, dtype, T, N, K, s, ratios, n_ratio, qc,
-                                ratio_best, mse_clip, nullptr, ws, ws_bytes, &nb);
-  if (st_ != AWQ_OK) return st_;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const SearchLayout L = search_layout(AWQ_OP_SEARCH_CLIP, T, N, K, n_ratio, nb, dtype);
+namespace {
+
+awq_status search_clip_impl(int op, const void* X, const void* W, awq_dtype dtype, int64_t T,
+                            int64_t N, int64_t K, const float* s, const float* ratios,
+                            int32_t n_ratio, awq_qconfig qc, float* ratio_best, double* mse_clip,
+                            double* row_sums, void* ws, int32_t nb, hipStream_t st) {
+  const SearchLayout L = search_layout(op, T, N, K, n_ratio, nb, dtype);
   double* rs = at<double>(ws, L.row_sums);
   double* best = at<double>(ws, L.best);
   double* mc = at<double>(ws, L.scalar);
   float* inv = at<float>(ws, L.inv);
   float* s_copy = at<float>(ws, L.s_table);
   const Segment seg{W, N, 0};
+  const uint16_t* Gs = nullptr;
+  if (is_gram_op(op)) {
+    awq_status g = build_gram(X, T, K, L, ws, st);
+    if (g != AWQ_OK) return g;
+    Gs = at<uint16_t>(ws, L.gs);
+  }
   AWQ_HIP(timed(AWQ_K_SCALE, st, [&] { return launch_reciprocal(s, K, s_copy, inv, st); }),
           "reciprocal");
   for (int c0 = 0; c0 < n_ratio; c0 += nb) {
     const int cb = n_ratio - c0 < nb ? n_ratio - c0 : nb;
-    st_ = run_batch(X, &seg, 1, dtype, T, N, K, s_copy, inv, 0, ratios + c0, cb, qc, L, ws,
-                    rs + int64_t(c0) * N, st);
+    awq_status st_ = run_batch(X, &seg, 1, dtype, T, N, K, s_copy, inv, 0, ratios + c0, cb, qc,
+                               L, ws, rs + int64_t(c0) * N, st, Gs);
     if (st_ != AWQ_OK) return st_;
   }
   AWQ_HIP(timed(AWQ_K_REDUCE, st,
@@ -312,6 +363,36 @@ extern "C" awq_status awq_search_clip(const void* X, const void* W, awq_dtype dt
   AWQ_HIP(hipMemcpyAsync(mse_clip, mc, sizeof(double), hipMemcpyDeviceToHost, st), "copy mse_clip");
   AWQ_HIP(hipStreamSynchronize(st), "synchronize");
   return AWQ_OK;
+}
+
+}  // namespace
+
+extern "C" awq_status awq_search_clip(const void* X, const void* W, awq_dtype dtype, int64_t T,
+                                      int64_t N, int64_t K, const float* s, const float* ratios,
+                                      int32_t n_ratio, awq_qconfig qc, float* ratio_best,
+                                      double* mse_clip, double* row_sums, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  int32_t nb = 0;
+  awq_status st_ = check_search(AWQ_OP_SEARCH_CLIP, X, W, dtype, T, N, K, s, ratios, n_ratio, qc,
+                                ratio_best, mse_clip, nullptr, ws, ws_bytes, &nb);
+  if (st_ != AWQ_OK) return st_;
+  return search_clip_impl(AWQ_OP_SEARCH_CLIP, X, W, dtype, T, N, K, s, ratios, n_ratio, qc,
+                          ratio_best, mse_clip, row_sums, ws, nb,
+                          static_cast<hipStream_t>(stream));
+}
+
+extern "C" awq_status awq_search_clip_gram(const void* X, const void* W, awq_dtype dtype,
+                                           int64_t T, int64_t N, int64_t K, const float* s,
+                                           const float* ratios, int32_t n_ratio, awq_qconfig qc,
+                                           float* ratio_best, double* mse_clip, double* row_sums,
+                                           void* ws, size_t ws_bytes, void* stream) {
+  int32_t nb = 0;
+  awq_status st_ = check_search(AWQ_OP_SEARCH_CLIP_GRAM, X, W, dtype, T, N, K, s, ratios, n_ratio,
+                                qc, ratio_best, mse_clip, nullptr, ws, ws_bytes, &nb);
+  if (st_ != AWQ_OK) return st_;
+  return search_clip_impl(AWQ_OP_SEARCH_CLIP_GRAM, X, W, dtype, T, N, K, s, ratios, n_ratio, qc,
+                          ratio_best, mse_clip, row_sums, ws, nb,
+                          static_cast<hipStream_t>(stream));
 }
 
 extern "C" awq_status awq_quantize_pack(const void* W, awq_dtype w_dtype, int64_t N, int64_t K,

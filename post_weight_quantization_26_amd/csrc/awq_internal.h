@@ -38,9 +38,15 @@ struct SearchLayout {
   size_t mse;       // [n_grid] f64
   size_t best;      // [N] f64 best per-row sums (clip search)
   size_t scalar;    // [8] f64
+  size_t xt;        // Gram searches: [K, Tp] bf16 transposed, token-padded X
+  size_t gs;        // Gram searches: [K, 2K] bf16 [G_hi | G_lo]
   size_t total;
-  int64_t MT;
+  int64_t MT;       // row tiles of the partials (token tiles; Gram: channel tiles)
+  int64_t Tp;       // Gram searches: tokens padded to a multiple of 128
 };
+
+inline bool is_gram_op(int op) { return op == AWQ_OP_SEARCH_SCALE_GRAM || op == AWQ_OP_SEARCH_CLIP_GRAM; }
+inline bool is_scale_op(int op) { return op == AWQ_OP_SEARCH_SCALE || op == AWQ_OP_SEARCH_SCALE_GRAM; }
 SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_grid, int32_t nb,
                            awq_dtype dtype);
 

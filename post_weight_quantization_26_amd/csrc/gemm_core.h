@@ -138,8 +138,33 @@ __device__ __forceinline__ void dma_tile(const GemmCtx& c, int kt) {
   }
 }
 
-template <int S, class V>
-__device__ __forceinline__ void read_frags(const GemmCtx& c, int ks, V (&fa)[4], V (&fb)[4]) {
+// A and B with their own row strides (in elements); the k-tile index of B
+// wraps every KTb k-tiles (KT = 2·KTb: B's contraction is read twice), so
+// A = [P | Q] against B gives P·Bᵀ + Q·Bᵀ in one k-loop.
+struct GemmCtx2 {
+  __amdgpu_buffer_rsrc_t rsA, rsB;
+  int voffA[4], voffB[4];
+  int wave, KT, KTb, oobA, oobB;
+  int rdA[2], rdB[2];
+};
+
+template <int S>
+__device__ __forceinline__ void dma_tile(const GemmCtx2& c, int kt) {
+  const bool in = kt < c.KT;
+  const int ktb = kt >= c.KTb ? kt - c.KTb : kt;
+  const int kofsA = in ? kt * (BK * 2) : c.oobA;
+  const int kofsB = in ? ktb * (BK * 2) : c.oobB;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsA, AWQ_LDS(stage_a<S>() + (c.wave * 4 + j) * 64),
+                                             16, c.voffA[j] + kofsA, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsB, AWQ_LDS(stage_b<S>() + (c.wave * 4 + j) * 64),
+                                             16, c.voffB[j] + kofsB, 0, 0, 0);
+  }
+}
+
+template <int S, class V, class Ctx>
+__device__ __forceinline__ void read_frags(const Ctx& c, int ks, V (&fa)[4], V (&fb)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     fa[i] = __builtin_bit_cast(V, stage_a<S>()[c.rdA[ks] + i * 128]);
@@ -169,8 +194,8 @@ __device__ __forceinline__ void mfma_4x4(floatx16 (&acc)[4][4], const V (&fa)[4]
 //   MFMAs of (kt, k-step 0) from F0 while F1 <- (kt, k-step 1) is read,
 //   then wait for this wave's LDS reads and for its DMA of k-tile kt+1
 //   (two k-tiles = 16 copies may stay in flight) and meet at the barrier.
-template <int S, bool PREV, class V>
-__device__ __forceinline__ void region(const GemmCtx& c, int kt, floatx16 (&acc)[4][4],
+template <int S, bool PREV, class V, class Ctx>
+__device__ __forceinline__ void region(const Ctx& c, int kt, floatx16 (&acc)[4][4],
                                        V (&f0a)[4], V (&f0b)[4], V (&f1a)[4], V (&f1b)[4]) {
   dma_tile<(S + 3) & 3>(c, kt + 3);
   if (PREV) mfma_4x4(acc, f1a, f1b);
@@ -231,11 +256,42 @@ __device__ __forceinline__ void gemm_setup(GemmCtx& c, const uint16_t* A, int64_
   }
 }
 
+// Setup for GemmCtx2: A rows of lda elements, B rows of ldb elements, the
+// contraction of A is KA elements (a multiple of 128); B's k wraps every
+// KA / 2 elements when wrap_b, else B is read once over KA as well.
+__device__ __forceinline__ void gemm_setup2(GemmCtx2& c, const uint16_t* A, int64_t rows_a,
+                                            int64_t lda, const uint16_t* B, int64_t rows_b,
+                                            int64_t ldb, int64_t KA, bool wrap_b) {
+  c.rsA = tile_rsrc(A, rows_a, lda);
+  c.rsB = tile_rsrc(B, rows_b, ldb);
+  const int tid = threadIdx.x, lane = tid & 63;
+  c.wave = tid >> 6;
+  c.KT = int(KA / BK);
+  c.KTb = wrap_b ? c.KT / 2 : c.KT;
+  c.oobA = BM * int(lda) * 2;
+  c.oobB = BN * int(ldb) * 2;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = (c.wave * 4 + j) * 64 + lane;
+    const int row = p >> 2;
+    const int chunk = (p & 3) ^ ((row >> 2) & 3);
+    c.voffA[j] = (row * int(lda) + chunk * 8) * 2;
+    c.voffB[j] = (row * int(ldb) + chunk * 8) * 2;
+  }
+  const int wm = c.wave >> 1, wn = c.wave & 1;
+  const int fr = lane & 31, fh = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    c.rdA[ks] = swz(wm * 128 + fr, 2 * ks + fh);
+    c.rdB[ks] = swz(wn * 128 + fr, 2 * ks + fh);
+  }
+}
+
 // The whole k-loop of one tile: acc[i][j] (wave (wm, wn), sub-tile (i, j))
 // receives Σ_k A·Bᵀ. K must be a multiple of 128 (the number of 32-wide
 // k-tiles a multiple of 4).
-template <bool F16>
-__device__ __forceinline__ void gemm_mainloop(const GemmCtx& c, floatx16 (&acc)[4][4]) {
+template <bool F16, class Ctx>
+__device__ __forceinline__ void gemm_mainloop(const Ctx& c, floatx16 (&acc)[4][4]) {
   typedef typename Operand<F16>::type V;
 #pragma unroll
   for (int i = 0; i < 4; ++i)

@@ -1,0 +1,190 @@
+// The search's output errors through the Gram matrix of the activations:
+//
+//   M_n = Σ_t (Σ_k X[t][k]·E[n][k])² = E_n · G · E_nᵀ,   G = XᵀX  [K, K]
+//
+// (an exact identity of the error the pages measure: "05 — AWQ: Activation-
+// Aware Weight Scaling", section 4, quantise and measure the output MSE).
+// G costs 2·T·K² once per layer; each candidate row then costs 2·K² instead
+// of 2·T·K, T/K times less (16x at 64K tokens and K = 4096).
+//
+//  1. transpose_pad_kernel: Xt [K, Tp] = Xᵀ with the token dim padded to a
+//     multiple of 128 with zeros (zero rows do not change G).
+//  2. gram_kernel: G = Xt·Xtᵀ on the shared MFMA main loop (gemm_core.h),
+//     float32 sums over all tokens. The epilogue stores G as two bf16
+//     halves, G_hi = bf16(G) and G_lo = bf16(G - G_hi), side by side in
+//     Gs [K, 2K]: hi + lo carries G to about 2^-16 relative, so the bf16
+//     MFMA that follows does not lose G's precision.
+//  3. gram_search_kernel: for a batch of candidate error rows E [Nc, K]
+//     (bf16, the same operands the direct search GEMM uses), one k-loop over
+//     the 2K columns of Gs with E's columns read twice gives
+//     Z[j][n] = Σ_i (G_hi + G_lo)[j][i]·E[n][i] = (G·E_nᵀ)_j in float32. The
+//     epilogue multiplies each Z[j][n] by E[n][j] and sums over the tile's
+//     rows j: partials[tile][n]; the row reduction over tiles gives M_n.
+#include "gemm_core.h"
+
+namespace awq {
+namespace {
+
+// ---------------------------------------------------------------------------
+// 1. Xt = Xᵀ, token dim padded with zeros
+// ---------------------------------------------------------------------------
+
+// Workgroup = 64 tokens x 64 channels through LDS; 16-byte loads and stores.
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ X,
+                                                            int64_t T, int64_t K, int64_t Tp,
+                                                            uint16_t* __restrict__ Xt) {
+  __shared__ uint16_t tile[64][72];
+  const int64_t t0 = int64_t(blockIdx.x) * 64, k0 = int64_t(blockIdx.y) * 64;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + 256 * u;         // 512 chunks of 8 channels
+    const int r = e >> 3, c8 = (e & 7) * 8;
+    const int64_t t = t0 + r;
+    uint4 q = make_uint4(0, 0, 0, 0);
+    if (t < T) q = *reinterpret_cast<const uint4*>(X + t * K + k0 + c8);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tile[r][c8 + 2 * i] = uint16_t(w[i] & 0xFFFFu);
+      tile[r][c8 + 2 * i + 1] = uint16_t(w[i] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + 256 * u;         // 512 chunks of 8 tokens
+    const int kr = e >> 3, t8 = (e & 7) * 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = uint32_t(tile[t8 + 2 * i][kr]) | (uint32_t(tile[t8 + 2 * i + 1][kr]) << 16);
+    if (t0 + t8 < Tp)
+      *reinterpret_cast<uint4*>(Xt + (k0 + kr) * Tp + t0 + t8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. G = Xt·Xtᵀ, stored as [G_hi | G_lo]
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint16_t bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gram_kernel(const uint16_t* __restrict__ Xt, int64_t K, int64_t Tp, int tiles,
+                 uint16_t* __restrict__ Gs) {
+#pragma clang fp contract(off)
+  int tm, tn;
+  if (!tile_of(blockIdx.x, tiles, tiles, tm, tn)) return;
+  const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
+  const int64_t rows_a = K - m0 < BM ? K - m0 : BM;
+  const int64_t rows_b = K - n0 < BN ? K - n0 : BN;
+  GemmCtx c;
+  gemm_setup(c, Xt + m0 * Tp, rows_a, Xt + n0 * Tp, rows_b, Tp);
+  floatx16 acc[4][4];
+  gemm_mainloop<false>(c, acc);
+
+  const int lane = threadIdx.x & 63;
+  const int wm = c.wave >> 1, wn = c.wave & 1;
+  const int64_t row0 = m0 + wm * 128 + 4 * (lane >> 5);
+  const int64_t col0 = n0 + wn * 128 + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = col0 + j * 32;
+      if (col >= K) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = row0 + i * 32 + 8 * (v >> 2) + (v & 3);
+        if (row >= K) continue;
+        const float g = acc[i][j][v];
+        const uint16_t hi = bf16_bits(g);
+        const float rem = g - __uint_as_float(uint32_t(hi) << 16);
+        Gs[row * 2 * K + col] = hi;
+        Gs[row * 2 * K + K + col] = bf16_bits(rem);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. candidates: partials[tm][n] = Σ_{j in row tile tm} (G·E_nᵀ)_j · E[n][j]
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gram_search_kernel(const uint16_t* __restrict__ Gs, const uint16_t* __restrict__ E,
+                        int64_t K, int64_t Nc, int tiles_m, int tiles_n,
+                        float* __restrict__ partials) {
+  int tm, tn;
+  if (!tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
+  const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
+  const int64_t rows_a = K - m0 < BM ? K - m0 : BM;
+  const int64_t rows_b = Nc - n0 < BN ? Nc - n0 : BN;
+  GemmCtx2 c;
+  gemm_setup2(c, Gs + m0 * 2 * K, rows_a, 2 * K, E + n0 * K, rows_b, K, 2 * K, true);
+  floatx16 acc[4][4];
+  gemm_mainloop<false>(c, acc);
+
+  // Epilogue: lane l of sub-tile (i, j) holds column n = ... + l % 32 and
+  // rows 8·(v/4) + 4·(l/32) + v % 4 of the wave's 32-row block i; each group
+  // of 4 consecutive rows takes one 8-byte load of E[n][rows].
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wm = c.wave >> 1, wn = c.wave & 1;
+  const int64_t row0 = m0 + wm * 128 + 4 * (lane >> 5);
+  float* red = reinterpret_cast<float*>(sA0);  // [2][BN]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
+    float s = 0.f;
+    if (n < Nc) {
+      const uint16_t* en = E + n * K;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t r = row0 + i * 32 + 8 * q;      // 4 consecutive rows r..r+3
+          if (r < K) {
+            const uint2 ev = *reinterpret_cast<const uint2*>(en + r);
+            s += acc[i][j][4 * q + 0] * __uint_as_float(ev.x << 16);
+            s += acc[i][j][4 * q + 1] * __uint_as_float(ev.x & 0xFFFF0000u);
+            s += acc[i][j][4 * q + 2] * __uint_as_float(ev.y << 16);
+            s += acc[i][j][4 * q + 3] * __uint_as_float(ev.y & 0xFFFF0000u);
+          }
+        }
+    }
+    s += __shfl_xor(s, 32);
+    if (lane < 32) red[wm * BN + wn * 128 + j * 32 + lane] = s;
+  }
+  __syncthreads();
+  const int64_t col = n0 + tid;
+  if (col < Nc) partials[int64_t(tm) * Nc + col] = red[tid] + red[BN + tid];
+}
+
+}  // namespace
+
+hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, uint16_t* Xt,
+                             uint16_t* Gs, hipStream_t st) {
+  if (K % 128 || Tp % 128 || Tp < T) return hipErrorInvalidValue;
+  dim3 tgrid(unsigned((Tp + 63) / 64), unsigned(K / 64));
+  transpose_pad_kernel<<<tgrid, 256, 0, st>>>(static_cast<const uint16_t*>(X), T, K, Tp, Xt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int tiles = int((K + BM - 1) / BM);
+  gram_kernel<<<unsigned(gemm_blocks(tiles, tiles)), NT, 0, st>>>(Xt, K, Tp, tiles, Gs);
+  return hipGetLastError();
+}
+
+hipError_t launch_gram_search(const uint16_t* Gs, const void* E, int64_t K, int64_t Nc,
+                              float* partials, hipStream_t st) {
+  if (K % 128) return hipErrorInvalidValue;
+  const int tiles_m = int((K + BM - 1) / BM), tiles_n = int((Nc + BN - 1) / BN);
+  gram_search_kernel<<<unsigned(gemm_blocks(tiles_m, tiles_n)), NT, 0, st>>>(
+      Gs, static_cast<const uint16_t*>(E), K, Nc, tiles_m, tiles_n, partials);
+  return hipGetLastError();
+}
+
+}  // namespace awq

@@ -42,12 +42,15 @@ SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_gr
                            awq_dtype dtype) {
   SearchLayout L{};
   const int64_t bm = dtype == AWQ_F32 ? kGemmBM_f32 : kGemmBM_bf16;
-  L.MT = ceil_div(T, bm);
+  const bool gram = is_gram_op(op);
+  L.MT = gram ? ceil_div(K, kGemmBM_bf16) : ceil_div(T, bm);
+  L.Tp = gram ? ceil_div(T, kTileK) * kTileK : 0;
+  const size_t n_tab = is_scale_op(op) ? size_t(n_grid) : 1;
   size_t off = 0;
   L.s_table = off;
-  off += align_up(size_t(op == AWQ_OP_SEARCH_SCALE ? n_grid : 1) * size_t(K) * 4);
+  off += align_up(n_tab * size_t(K) * 4);
   L.inv = off;
-  off += align_up(size_t(op == AWQ_OP_SEARCH_SCALE ? n_grid : 1) * size_t(K) * 4);
+  off += align_up(n_tab * size_t(K) * 4);
   L.E = off;
   off += align_up(size_t(nb) * size_t(N) * size_t(K) * dtype_bytes(dtype));
   L.partials = off;
@@ -60,6 +63,10 @@ SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_gr
   off += align_up(size_t(N) * 8);
   L.scalar = off;
   off += align_up(64);
+  L.xt = off;
+  if (gram) off += align_up(size_t(K) * size_t(L.Tp) * 2);
+  L.gs = off;
+  if (gram) off += align_up(size_t(K) * size_t(2 * K) * 2);
   L.total = off;
   return L;
 }
@@ -110,12 +117,19 @@ awq_status check_search(int op, const void* X, const void* W, awq_dtype d, int64
                         int64_t K, const float* vec, const float* grid, int32_t n_grid,
                         awq_qconfig qc, const void* out_dev, const void* out_host,
                         const void* out_host2, const void* ws, size_t ws_bytes, int32_t* nb) {
-  const char* nm = op == AWQ_OP_SEARCH_SCALE ? "search_scale" : "search_clip";
-  if (!X || !W || !vec || !grid || !out_dev || !out_host || (op == AWQ_OP_SEARCH_SCALE && !out_host2))
+  const char* nm = op == AWQ_OP_SEARCH_SCALE        ? "search_scale"
+                   : op == AWQ_OP_SEARCH_CLIP       ? "search_clip"
+                   : op == AWQ_OP_SEARCH_SCALE_GRAM ? "search_scale_gram"
+                                                    : "search_clip_gram";
+  if (!X || !W || !vec || !grid || !out_dev || !out_host || (is_scale_op(op) && !out_host2))
     return set_error(AWQ_E_INVALID, "%s: NULL pointer argument", nm);
   if (!dtype_ok(d)) return set_error(AWQ_E_INVALID, "%s: unknown dtype %d", nm, int(d));
   if (d == AWQ_F16)
     return set_error(AWQ_E_UNSUPPORTED, "%s: fp16 inputs are not supported (bf16 or f32)", nm);
+  if (is_gram_op(op) && d != AWQ_BF16)
+    return set_error(AWQ_E_UNSUPPORTED, "%s: the Gram path takes bf16 inputs", nm);
+  if (is_gram_op(op) && T > (int64_t(1) << 22))
+    return set_error(AWQ_E_UNSUPPORTED, "%s: at most 2^22 tokens on the Gram path", nm);
   if (T < 1 || N < 1 || K < 1 || T > kMaxDim || N > kMaxDim || K > kMaxDim)
     return set_error(AWQ_E_INVALID, "%s: bad shape T=%lld N=%lld K=%lld", nm, (long long)T,
                      (long long)N, (long long)K);
@@ -127,7 +141,7 @@ awq_status check_search(int op, const void* X, const void* W, awq_dtype d, int64
     return set_error(AWQ_E_INVALID, "%s: grid size %d outside 1..%d", nm, n_grid, kMaxGrid);
   for (int i = 0; i < n_grid; ++i) {
     const float g = grid[i];
-    const bool ok = op == AWQ_OP_SEARCH_SCALE ? (g >= 0.f && g <= 1.f) : (g > 0.f && g <= 1.f);
+    const bool ok = is_scale_op(op) ? (g >= 0.f && g <= 1.f) : (g > 0.f && g <= 1.f);
     if (!ok) return set_error(AWQ_E_INVALID, "%s: grid[%d]=%g out of range", nm, i, double(g));
   }
   if (!aligned16(X) || !aligned16(W) || !aligned4(vec) || !aligned4(out_dev))
@@ -279,6 +293,10 @@ extern "C" size_t awq_workspace_bytes(int op, int64_t T, int64_t N, int64_t K, i
     case AWQ_OP_SEARCH_SCALE:
     case AWQ_OP_SEARCH_CLIP:
       return search_layout(op, T, N, K, n_grid, n_grid, dtype).total;
+    case AWQ_OP_SEARCH_SCALE_GRAM:
+    case AWQ_OP_SEARCH_CLIP_GRAM:
+      if (dtype != AWQ_BF16 || K % kTileK) return 0;
+      return search_layout(op, T, N, K, n_grid, n_grid, dtype).total;
     case AWQ_OP_PACK:
       return kAlign;
     default:
@@ -289,7 +307,7 @@ extern "C" size_t awq_workspace_bytes(int op, int64_t T, int64_t N, int64_t K, i
 extern "C" size_t awq_workspace_bytes_batch(int op, int64_t T, int64_t N, int64_t K,
                                             int32_t n_grid, int32_t batch, awq_dtype dtype) {
   using namespace awq;
-  if (op != AWQ_OP_SEARCH_SCALE && op != AWQ_OP_SEARCH_CLIP) return 0;
+  if (op != AWQ_OP_SEARCH_SCALE && op != AWQ_OP_SEARCH_CLIP && !is_gram_op(op)) return 0;
   if (batch < 1 || batch > n_grid) return 0;
   if (awq_workspace_bytes(op, T, N, K, n_grid, dtype) == 0) return 0;
   return search_layout(op, T, N, K, n_grid, batch, dtype).total;

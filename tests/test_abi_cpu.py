@@ -280,3 +280,38 @@ def test_w4a16_workspace_and_rejects(L):
     assert call(wsb=16) == -3
     assert call(ws=MIS) == -3
     assert "w4a16_matmul" in L.last_error()
+
+
+def test_gram_workspace_and_rejects(L):
+    lib = L.lib()
+    ws = lib.awq_workspace_bytes
+    direct = ws(L.AWQ_OP_SEARCH_SCALE, 65536, 4096, 4096, 20, L.AWQ_BF16)
+    gram = ws(L.AWQ_OP_SEARCH_SCALE_GRAM, 65536, 4096, 4096, 20, L.AWQ_BF16)
+    xt, gs = 4096 * 65536 * 2, 4096 * 8192 * 2
+    # partials shrink to K/256 row tiles; X^T and the G halves are added
+    assert gram > direct - 256 * 20 * 4096 * 4 + xt + gs - (1 << 20)
+    assert gram < direct + xt + gs
+    assert ws(L.AWQ_OP_SEARCH_SCALE_GRAM, 65536, 4096, 4096, 20, L.AWQ_F32) == 0
+    assert ws(L.AWQ_OP_SEARCH_CLIP_GRAM, 700, 300, 384, 5, L.AWQ_BF16) > 384 * 768 * 2 + 384 * 768 * 2
+    assert lib.awq_workspace_bytes_batch(L.AWQ_OP_SEARCH_CLIP_GRAM, 700, 300, 384, 5, 1,
+                                         L.AWQ_BF16) > 0
+    a_best = ctypes.c_float()
+    mse = (ctypes.c_double * 3)()
+    g = L.float_array([0.0, 0.5, 1.0])
+    qc = L.QConfig(4, 128, 1)
+    f = lib.awq_search_scale_gram
+    assert f(FAKE, FAKE, L.AWQ_F32, 256, 256, 256, FAKE, g, 3, qc, FAKE, ctypes.byref(a_best), mse,
+             None, FAKE, 1 << 40, None) == -2
+    assert f(FAKE, FAKE, L.AWQ_BF16, (1 << 22) + 1, 256, 256, FAKE, g, 3, qc, FAKE,
+             ctypes.byref(a_best), mse, None, FAKE, 1 << 40, None) == -2
+    assert f(FAKE, FAKE, L.AWQ_BF16, 256, 256, 200, FAKE, g, 3, qc, FAKE, ctypes.byref(a_best),
+             mse, None, FAKE, 1 << 40, None) == -1
+    need1 = lib.awq_workspace_bytes_batch(L.AWQ_OP_SEARCH_SCALE_GRAM, 256, 256, 256, 3, 1,
+                                          L.AWQ_BF16)
+    assert f(FAKE, FAKE, L.AWQ_BF16, 256, 256, 256, FAKE, g, 3, qc, FAKE, ctypes.byref(a_best),
+             mse, None, FAKE, need1 - 1, None) == -3
+    assert "search_scale_gram" in L.last_error()
+    mc = ctypes.c_double()
+    assert lib.awq_search_clip_gram(FAKE, FAKE, L.AWQ_BF16, 256, 256, 256, FAKE,
+                                    L.float_array([0.0, 1.0]), 2, qc, FAKE, ctypes.byref(mc),
+                                    None, FAKE, 1 << 40, None) == -1      # ratio 0 is invalid

@@ -83,11 +83,12 @@ def model_E(w32, s32, ratio, bits, zp, dtype, group=128):
     return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(e)).astype(np.float64)
 
 
-def row_references(X, dtype, w_rows, cands, chunk=4096):
+def row_references(X, dtype, w_rows, cands, chunk=4096, want_S=False):
     """One pass over X for stacked candidates [(s, ratio), ...] on rows w_rows.
 
     Returns M64 (float64 oracle errors), Mm (model errors) and tol (worst-case
-    float32 accumulation bound), each [n_cand, R]."""
+    float32 accumulation bound of the direct GEMM), each [n_cand, R]; with
+    want_S also S = Σ_t (Σ_k |x_tk|·|e_k|)² per row (= |e|ᵀ(|X|ᵀ|X|)|e|)."""
     e64 = np.concatenate([O.candidate_weights(w_rows, s, r, *c) - w_rows.astype(np.float64)
                           for (s, r, c) in cands])
     em = np.concatenate([model_E(w_rows, s, r, c[0], c[2], dtype, c[1]) for (s, r, c) in cands])
@@ -106,6 +107,8 @@ def row_references(X, dtype, w_rows, cands, chunk=4096):
     g = K * U_F32 / (1 - K * U_F32)
     tol = 2 * g * acc + g * g * acc2 + 300 * U_F32 * Mm
     n = len(cands)
+    if want_S:
+        return M64.reshape(n, -1), Mm.reshape(n, -1), tol.reshape(n, -1), acc2.reshape(n, -1)
     return M64.reshape(n, -1), Mm.reshape(n, -1), tol.reshape(n, -1)
 
 
