@@ -20,6 +20,11 @@
       Prints one JSON line per case with the library's HIP-event kernel times
       and the achieved HBM bandwidth (GEMV) or TFLOP/s (GEMM).
 
+  python -m post_weight_quantization_26_amd.profile_run pack [--reps 20]
+      The INT4 g128 pack of a bf16 W with random scales, 28672 x 8192 (the
+      70B-class MLP layer) and 4096 x 4096, ``reps`` timed launches each;
+      prints the library's HIP-event time and the bandwidth it implies.
+
 The search workload itself is profiled through ``bench.py``.
 """
 from __future__ import annotations
@@ -120,9 +125,40 @@ def w4a16(reps: int) -> None:
         torch.cuda.empty_cache()
 
 
+def pack(reps: int) -> None:
+    import json
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    if root not in sys.path:
+        sys.path.insert(0, root)
+    import torch
+    from post_weight_quantization_26_amd import api
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    for N, K in ((28672, 8192), (4096, 4096)):
+        W = (torch.randn((N, K), generator=g, device=dev) * 0.015).to(torch.bfloat16)
+        s = torch.exp(torch.rand(K, generator=g, device=dev) * 2 - 1)
+        out = api.quantize_pack(W, s)
+        torch.cuda.synchronize()
+        api.profile_enable(True)
+        api.profile_reset()
+        for _ in range(reps):
+            api.quantize_pack(W, s, out=out)
+        torch.cuda.synchronize()
+        ms, n = api.profile_read("pack")
+        api.profile_enable(False)
+        us = ms / n * 1e3
+        moved = N * K * 2 + N * K // 2 + (N * K // 128) * 2.5 + K * 4
+        print(json.dumps({"N": N, "K": K, "pack_us": round(us, 2), "algorithmic_bytes": int(moved),
+                          "GBps": round(moved / (us * 1e-6) / 1e9, 1)}), flush=True)
+        del W, out
+        torch.cuda.empty_cache()
+
+
 def main(argv=None) -> int:
     p = argparse.ArgumentParser()
-    p.add_argument("what", choices=["copy", "fold", "w4a16"])
+    p.add_argument("what", choices=["copy", "fold", "w4a16", "pack"])
     p.add_argument("--mib", type=int, default=1024)
     p.add_argument("--reps", type=int, default=20)
     a = p.parse_args(argv)
@@ -130,6 +166,8 @@ def main(argv=None) -> int:
         copy(a.mib)
     elif a.what == "fold":
         fold(a.reps)
+    elif a.what == "pack":
+        pack(a.reps)
     else:
         w4a16(a.reps)
     return 0
