@@ -143,9 +143,9 @@ def main():
                            dtype=torch.uint8, device=dev)
     n_grid = max(cfg.n_alpha, cfg.n_ratio)
     method = args.method
-    gram_ok = not cfg.layers and cfg.dtype == "bf16"
+    gram_ok = cfg.dtype == "bf16"
     if method == "gram" and not gram_ok:
-        print(json.dumps({"error": "the Gram path runs single bf16 layers"}))
+        print(json.dumps({"error": "the Gram path runs bf16 layers"}))
         sys.exit(2)
     ws_need = api.workspace_bytes(_lib.AWQ_OP_SEARCH_SCALE, T, N, K, n_grid, tdt)
     if gram_ok:
@@ -168,7 +168,7 @@ def main():
             # linears sharing X: one search, one s, folded into the norm weight
             # (in place, so gamma drifts over the steps; the work is the same)
             res = api.search_scale_group(Xd, Wds, abar, alphas, bits=cfg.bits, group=G,
-                                         zero_point=zp, ws=ws_search)
+                                         zero_point=zp, ws=ws_search, method=how)
             api.fold_norm(gamma, res["s_best"])
         else:
             res = api.search_scale(Xd, Wds[0], abar, alphas, bits=cfg.bits, group=G,

@@ -203,6 +203,17 @@ awq_status awq_search_scale_group(const void* X, const void* const* W, const int
                                   awq_qconfig qc, float* s_best, float* alpha_best, double* mse,
                                   double* row_sums, void* ws, size_t ws_bytes, void* stream);
 
+/* The group search through the Gram matrix of the shared X (as
+ * awq_search_scale_gram is to awq_search_scale): one G serves every layer of
+ * the group. Arguments and outputs as in awq_search_scale_group; bf16 inputs
+ * only; workspace sized with AWQ_OP_SEARCH_SCALE_GRAM and N = Σ_l N[l]. */
+awq_status awq_search_scale_group_gram(const void* X, const void* const* W, const int64_t* N,
+                                       int32_t n_layers, awq_dtype dtype, int64_t T, int64_t K,
+                                       const float* abar, const float* alphas, int32_t n_alpha,
+                                       awq_qconfig qc, float* s_best, float* alpha_best,
+                                       double* mse, double* row_sums, void* ws, size_t ws_bytes,
+                                       void* stream);
+
 /* The fold into a preceding normalisation ("AWQ and Activation-Aware
  * Scaling", sections "Scaling instead of protecting" and "When it breaks").
  * In place: gamma[j] <- gamma[j] / s[j] and, when beta is not NULL,

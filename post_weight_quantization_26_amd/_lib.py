@@ -58,6 +58,10 @@ SIGNATURES = {
                                               c_i32, ctypes.c_int, c_i64, c_i64, c_vp, c_fp,
                                               c_i32, QConfig, c_vp, c_fp, c_dp, c_vp, c_vp,
                                               c_sz, c_vp]),
+    "awq_search_scale_group_gram": (ctypes.c_int, [c_vp, ctypes.POINTER(c_vp),
+                                                   ctypes.POINTER(c_i64), c_i32, ctypes.c_int,
+                                                   c_i64, c_i64, c_vp, c_fp, c_i32, QConfig, c_vp,
+                                                   c_fp, c_dp, c_vp, c_vp, c_sz, c_vp]),
     "awq_fold_norm": (ctypes.c_int, [c_vp, c_vp, ctypes.c_int, c_i64, c_vp, c_vp]),
     "awq_fold_linear": (ctypes.c_int, [c_vp, c_vp, ctypes.c_int, c_i64, c_i64, c_vp, c_vp]),
     "awq_w4a16_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),

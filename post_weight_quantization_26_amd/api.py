@@ -130,10 +130,13 @@ def search_scale(X: torch.Tensor, W: torch.Tensor, abar: torch.Tensor, alphas: S
 def search_scale_group(X: torch.Tensor, Ws: Sequence[torch.Tensor], abar: torch.Tensor,
                        alphas: Sequence[float], bits: int = DEFAULT_BITS,
                        group: int = DEFAULT_GROUP, zero_point: bool = DEFAULT_ZERO_POINT,
-                       want_row_sums: bool = False, ws: Optional[torch.Tensor] = None) -> dict:
+                       want_row_sums: bool = False, ws: Optional[torch.Tensor] = None,
+                       method: str = "direct") -> dict:
     """One alpha search for linears that read the same X (one shared s): the
     error is averaged over all their outputs. Same result dict as
-    ``search_scale``; row_sums [n_alpha, sum N] keeps the layers in order."""
+    ``search_scale``; row_sums [n_alpha, sum N] keeps the layers in order.
+    method "gram" (bf16) scores all layers through one G = XᵀX."""
+    gram = _method(method)
     _dev(X, "X"), _dev(abar, "abar")
     if not 1 <= len(Ws) <= 16:
         raise ValueError("a group holds 1 to 16 layers")
@@ -145,18 +148,18 @@ def search_scale_group(X: torch.Tensor, Ws: Sequence[torch.Tensor], abar: torch.
     Ns = [int(W.shape[0]) for W in Ws]
     N = sum(Ns)
     n = len(alphas)
-    ws = _workspace(ws, workspace_bytes(L.AWQ_OP_SEARCH_SCALE, T, N, K, n, X.dtype), X.device)
+    op = L.AWQ_OP_SEARCH_SCALE_GRAM if gram else L.AWQ_OP_SEARCH_SCALE
+    ws = _workspace(ws, workspace_bytes(op, T, N, K, n, X.dtype), X.device)
     s_best = torch.empty(K, dtype=torch.float32, device=X.device)
     rows = torch.empty((n, N), dtype=torch.float64, device=X.device) if want_row_sums else None
     a_best = ctypes.c_float(0.0)
     mse = (ctypes.c_double * n)()
     wptrs = (ctypes.c_void_p * len(Ws))(*[W.data_ptr() for W in Ws])
     nvals = (ctypes.c_int64 * len(Ws))(*Ns)
-    L.check(L.lib().awq_search_scale_group(_ptr(X), wptrs, nvals, len(Ws), _dtype(X), T, K,
-                                           _ptr(abar), L.float_array(alphas), n,
-                                           qconfig(bits, group, zero_point), _ptr(s_best),
-                                           ctypes.byref(a_best), mse, _ptr(rows), _ptr(ws),
-                                           ws.numel(), _stream()))
+    fn = L.lib().awq_search_scale_group_gram if gram else L.lib().awq_search_scale_group
+    L.check(fn(_ptr(X), wptrs, nvals, len(Ws), _dtype(X), T, K, _ptr(abar), L.float_array(alphas),
+               n, qconfig(bits, group, zero_point), _ptr(s_best), ctypes.byref(a_best), mse,
+               _ptr(rows), _ptr(ws), ws.numel(), _stream()))
     mse_np = np.array(mse[:], dtype=np.float64)
     g32 = np.asarray(alphas, dtype=np.float32)
     idx = int(np.flatnonzero(g32 == np.float32(a_best.value))[0])

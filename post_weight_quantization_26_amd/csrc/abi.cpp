@@ -43,8 +43,8 @@ hipError_t launch_w4a16_gemv(const uint16_t* X, int64_t T, int64_t N, int64_t K,
                              float* partial, hipStream_t st);
 hipError_t launch_w4a16_gemv_reduce(const float* partial, int64_t chunks, int64_t T, int64_t N,
                                     int f16, uint16_t* Y, hipStream_t st);
-hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, uint16_t* Xt,
-                             uint16_t* Gs, hipStream_t st);
+hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, int S,
+                             uint16_t* Xt, float* P, uint16_t* Gs, hipStream_t st);
 hipError_t launch_gram_search(const uint16_t* Gs, const void* E, int64_t K, int64_t Nc,
                               float* partials, hipStream_t st);
 hipError_t launch_fold_vec(void* v, int dtype, int64_t K, const float* s, hipStream_t st);
@@ -204,9 +204,10 @@ namespace {
 awq_status build_gram(const void* X, int64_t T, int64_t K, const SearchLayout& L, void* ws,
                       hipStream_t st) {
   uint16_t* Xt = at<uint16_t>(ws, L.xt);
+  float* P = at<float>(ws, L.gp);
   uint16_t* Gs = at<uint16_t>(ws, L.gs);
   AWQ_HIP(timed(AWQ_K_GRAM_BUILD, st,
-                [&] { return launch_gram_build(X, T, K, L.Tp, Xt, Gs, st); }),
+                [&] { return launch_gram_build(X, T, K, L.Tp, L.S, Xt, P, Gs, st); }),
           "gram_build");
   return AWQ_OK;
 }
@@ -298,19 +299,19 @@ extern "C" awq_status awq_search_scale_gram(const void* X, const void* W, awq_dt
                            static_cast<hipStream_t>(stream));
 }
 
-extern "C" awq_status awq_search_scale_group(const void* X, const void* const* W,
-                                             const int64_t* N, int32_t n_layers, awq_dtype dtype,
-                                             int64_t T, int64_t K, const float* abar,
-                                             const float* alphas, int32_t n_alpha,
-                                             awq_qconfig qc, float* s_best, float* alpha_best,
-                                             double* mse, double* row_sums, void* ws,
-                                             size_t ws_bytes, void* stream) {
+namespace {
+
+awq_status search_scale_group_op(int op, const void* X, const void* const* W, const int64_t* N,
+                                 int32_t n_layers, awq_dtype dtype, int64_t T, int64_t K,
+                                 const float* abar, const float* alphas, int32_t n_alpha,
+                                 awq_qconfig qc, float* s_best, float* alpha_best, double* mse,
+                                 double* row_sums, void* ws, size_t ws_bytes, void* stream) {
   int64_t N_total = 0;
   awq_status s = check_group(W, N, n_layers, &N_total);
   if (s != AWQ_OK) return s;
   int32_t nb = 0;
-  s = check_search(AWQ_OP_SEARCH_SCALE, X, W[0], dtype, T, N_total, K, abar, alphas, n_alpha, qc,
-                   s_best, alpha_best, mse, ws, ws_bytes, &nb);
+  s = check_search(op, X, W[0], dtype, T, N_total, K, abar, alphas, n_alpha, qc, s_best,
+                   alpha_best, mse, ws, ws_bytes, &nb);
   if (s != AWQ_OK) return s;
   Segment seg[kMaxLayers];
   int64_t row0 = 0;
@@ -318,9 +319,36 @@ extern "C" awq_status awq_search_scale_group(const void* X, const void* const* W
     seg[l] = Segment{W[l], N[l], row0};
     row0 += N[l];
   }
-  return search_scale_impl(AWQ_OP_SEARCH_SCALE, X, seg, n_layers, dtype, T, N_total, K, abar,
-                           alphas, n_alpha, qc, s_best, alpha_best, mse, row_sums, ws, nb,
+  return search_scale_impl(op, X, seg, n_layers, dtype, T, N_total, K, abar, alphas, n_alpha,
+                           qc, s_best, alpha_best, mse, row_sums, ws, nb,
                            static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" awq_status awq_search_scale_group(const void* X, const void* const* W,
+                                             const int64_t* N, int32_t n_layers, awq_dtype dtype,
+                                             int64_t T, int64_t K, const float* abar,
+                                             const float* alphas, int32_t n_alpha,
+                                             awq_qconfig qc, float* s_best, float* alpha_best,
+                                             double* mse, double* row_sums, void* ws,
+                                             size_t ws_bytes, void* stream) {
+  return search_scale_group_op(AWQ_OP_SEARCH_SCALE, X, W, N, n_layers, dtype, T, K, abar, alphas,
+                               n_alpha, qc, s_best, alpha_best, mse, row_sums, ws, ws_bytes,
+                               stream);
+}
+
+extern "C" awq_status awq_search_scale_group_gram(const void* X, const void* const* W,
+                                                  const int64_t* N, int32_t n_layers,
+                                                  awq_dtype dtype, int64_t T, int64_t K,
+                                                  const float* abar, const float* alphas,
+                                                  int32_t n_alpha, awq_qconfig qc, float* s_best,
+                                                  float* alpha_best, double* mse,
+                                                  double* row_sums, void* ws, size_t ws_bytes,
+                                                  void* stream) {
+  return search_scale_group_op(AWQ_OP_SEARCH_SCALE_GRAM, X, W, N, n_layers, dtype, T, K, abar,
+                               alphas, n_alpha, qc, s_best, alpha_best, mse, row_sums, ws,
+                               ws_bytes, stream);
 }
 
 namespace {

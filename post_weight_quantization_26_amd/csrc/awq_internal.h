@@ -39,11 +39,18 @@ struct SearchLayout {
   size_t best;      // [N] f64 best per-row sums (clip search)
   size_t scalar;    // [8] f64
   size_t xt;        // Gram searches: [K, Tp] bf16 transposed, token-padded X
+  size_t gp;        // Gram searches: [S, U, 256, 256] f32 partial tiles of G
   size_t gs;        // Gram searches: [K, 2K] bf16 [G_hi | G_lo]
   size_t total;
   int64_t MT;       // row tiles of the partials (token tiles; Gram: channel tiles)
   int64_t Tp;       // Gram searches: tokens padded to a multiple of 128
+  int32_t S;        // Gram searches: token slices of the G build
 };
+
+// Token slices of the Gram build: the power of two S <= 16 dividing Tp / 128
+// that finishes the U·S (upper tile, slice) units of work in the fewest
+// rounds of 256 CUs relative to the slice length (ties to the smaller S).
+int32_t gram_slices(int64_t T, int64_t K);
 
 inline bool is_gram_op(int op) { return op == AWQ_OP_SEARCH_SCALE_GRAM || op == AWQ_OP_SEARCH_CLIP_GRAM; }
 inline bool is_scale_op(int op) { return op == AWQ_OP_SEARCH_SCALE || op == AWQ_OP_SEARCH_SCALE_GRAM; }

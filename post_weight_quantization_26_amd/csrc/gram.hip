@@ -9,11 +9,16 @@
 //
 //  1. transpose_pad_kernel: Xt [K, Tp] = Xᵀ with the token dim padded to a
 //     multiple of 128 with zeros (zero rows do not change G).
-//  2. gram_kernel: G = Xt·Xtᵀ on the shared MFMA main loop (gemm_core.h),
-//     float32 sums over all tokens. The epilogue stores G as two bf16
-//     halves, G_hi = bf16(G) and G_lo = bf16(G - G_hi), side by side in
-//     Gs [K, 2K]: hi + lo carries G to about 2^-16 relative, so the bf16
-//     MFMA that follows does not lose G's precision.
+//  2. gram_partial_kernel: G is symmetric, so only its tiles on and above the
+//     diagonal are formed, on the shared MFMA main loop (gemm_core.h). To
+//     keep every CU busy the token range is split into S slices (S chosen on
+//     the host to balance whole rounds of work); each (tile, slice) unit
+//     stores its float32 partial tile.
+//     gram_reduce_kernel adds a tile's S partials in a fixed order and stores
+//     G as two bf16 halves, G_hi = bf16(G) and G_lo = bf16(G - G_hi), side by
+//     side in Gs [K, 2K] (hi + lo carries G to about 2^-16 relative, so the
+//     bf16 MFMA that follows does not lose G's precision), for the tile and,
+//     through an LDS transpose, for its mirror image below the diagonal.
 //  3. gram_search_kernel: for a batch of candidate error rows E [Nc, K]
 //     (bf16, the same operands the direct search GEMM uses), one k-loop over
 //     the 2K columns of Gs with E's columns read twice gives
@@ -65,48 +70,122 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// 2. G = Xt·Xtᵀ, stored as [G_hi | G_lo]
+// 2. G = Xt·Xtᵀ: upper tiles x token slices, then the slice sum as [G_hi | G_lo]
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Upper tile u (row-major over tm <= tn of an nt x nt grid) -> (tm, tn).
+__device__ __forceinline__ void upper_tile(int u, int nt, int& tm, int& tn) {
+  int r = 0, first = 0;
+  while (first + (nt - r) <= u) {
+    first += nt - r;
+    ++r;
+  }
+  tm = r;
+  tn = r + (u - first);
+}
+
+// Block b: slice s = b / U, upper tile u = b % U (units of one token slice run
+// together, so concurrent blocks share that slice's panels of Xt).
+// P[(s·U + u)][256·256]: float32 partial tile, row-major.
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gram_kernel(const uint16_t* __restrict__ Xt, int64_t K, int64_t Tp, int tiles,
-                 uint16_t* __restrict__ Gs) {
-#pragma clang fp contract(off)
+void gram_partial_kernel(const uint16_t* __restrict__ Xt, int64_t K, int64_t Tp, int64_t Ts,
+                         int nt, int U, float* __restrict__ P) {
+  const int s = blockIdx.x / U, u = blockIdx.x % U;
   int tm, tn;
-  if (!tile_of(blockIdx.x, tiles, tiles, tm, tn)) return;
+  upper_tile(u, nt, tm, tn);
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
   const int64_t rows_a = K - m0 < BM ? K - m0 : BM;
   const int64_t rows_b = K - n0 < BN ? K - n0 : BN;
-  GemmCtx c;
-  gemm_setup(c, Xt + m0 * Tp, rows_a, Xt + n0 * Tp, rows_b, Tp);
+  const int64_t t0 = int64_t(s) * Ts;
+  GemmCtx2 c;
+  gemm_setup2(c, Xt + m0 * Tp + t0, rows_a, Tp, Xt + n0 * Tp + t0, rows_b, Tp, Ts, false);
   floatx16 acc[4][4];
   gemm_mainloop<false>(c, acc);
 
   const int lane = threadIdx.x & 63;
   const int wm = c.wave >> 1, wn = c.wave & 1;
-  const int64_t row0 = m0 + wm * 128 + 4 * (lane >> 5);
-  const int64_t col0 = n0 + wn * 128 + (lane & 31);
+  float* tile = P + (int64_t(s) * U + u) * (BM * BN);
+  const int row0 = wm * 128 + 4 * (lane >> 5);
+  const int col0 = wn * 128 + (lane & 31);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = col0 + j * 32;
-      if (col >= K) continue;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = row0 + i * 32 + 8 * (v >> 2) + (v & 3);
-        if (row >= K) continue;
-        const float g = acc[i][j][v];
-        const uint16_t hi = bf16_bits(g);
-        const float rem = g - __uint_as_float(uint32_t(hi) << 16);
-        Gs[row * 2 * K + col] = hi;
-        Gs[row * 2 * K + K + col] = bf16_bits(rem);
-      }
+      for (int v = 0; v < 16; ++v)
+        tile[(row0 + i * 32 + 8 * (v >> 2) + (v & 3)) * BN + col0 + j * 32] = acc[i][j][v];
+}
+
+// Block (u, sb): the 64x64 sub-block sb of upper tile u. Thread t takes row
+// t / 4 and 16 consecutive columns; the S partials are added in slice order.
+__global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restrict__ P, int S,
+                                                          int U, int nt, int64_t K,
+                                                          uint16_t* __restrict__ Gs) {
+#pragma clang fp contract(off)
+  __shared__ uint16_t th[64][66], tl[64][66];
+  const int u = blockIdx.x, sb = blockIdx.y;
+  int tm, tn;
+  upper_tile(u, nt, tm, tn);
+  const int sr = (sb >> 2) * 64, sc = (sb & 3) * 64;
+  const int t = threadIdx.x, r = t >> 2, c0 = (t & 3) * 16;
+  float g[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) g[e] = 0.f;
+  for (int sl = 0; sl < S; ++sl) {
+    const float4* src = reinterpret_cast<const float4*>(
+        P + (int64_t(sl) * U + u) * (BM * BN) + (sr + r) * BN + sc + c0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = src[q];
+      g[4 * q] += v.x; g[4 * q + 1] += v.y; g[4 * q + 2] += v.z; g[4 * q + 3] += v.w;
     }
+  }
+  uint16_t hi[16], lo[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    hi[e] = bf16_bits(g[e]);
+    lo[e] = bf16_bits(g[e] - __uint_as_float(uint32_t(hi[e]) << 16));
+    th[r][c0 + e] = hi[e];
+    tl[r][c0 + e] = lo[e];
+  }
+  const int64_t R = int64_t(tm) * BM + sr + r, C = int64_t(tn) * BN + sc + c0;
+  if (R < K && C < K) {   // K is a multiple of 128, so 16 columns are all in or all out
+    uint32_t wh[8], wl[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      wh[e] = uint32_t(hi[2 * e]) | (uint32_t(hi[2 * e + 1]) << 16);
+      wl[e] = uint32_t(lo[2 * e]) | (uint32_t(lo[2 * e + 1]) << 16);
+    }
+    uint4* dh = reinterpret_cast<uint4*>(Gs + R * 2 * K + C);
+    uint4* dl = reinterpret_cast<uint4*>(Gs + R * 2 * K + K + C);
+    dh[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+    dh[1] = make_uint4(wh[4], wh[5], wh[6], wh[7]);
+    dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+    dl[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
+  }
+  if (tm == tn) return;               // a diagonal tile holds both triangles already
+  __syncthreads();
+  // mirror: element (R, C) also goes to (C, R); thread t writes row c = t / 4
+  // of the transposed sub-block, 16 consecutive rows r of the original.
+  const int64_t Rm = int64_t(tn) * BN + sc + r, Cm = int64_t(tm) * BM + sr + c0;
+  if (Rm < K && Cm < K) {
+    uint32_t wh[8], wl[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      wh[e] = uint32_t(th[c0 + 2 * e][r]) | (uint32_t(th[c0 + 2 * e + 1][r]) << 16);
+      wl[e] = uint32_t(tl[c0 + 2 * e][r]) | (uint32_t(tl[c0 + 2 * e + 1][r]) << 16);
+    }
+    uint4* dh = reinterpret_cast<uint4*>(Gs + Rm * 2 * K + Cm);
+    uint4* dl = reinterpret_cast<uint4*>(Gs + Rm * 2 * K + K + Cm);
+    dh[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+    dh[1] = make_uint4(wh[4], wh[5], wh[6], wh[7]);
+    dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
+    dl[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -166,15 +245,21 @@ void gram_search_kernel(const uint16_t* __restrict__ Gs, const uint16_t* __restr
 
 }  // namespace
 
-hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, uint16_t* Xt,
-                             uint16_t* Gs, hipStream_t st) {
-  if (K % 128 || Tp % 128 || Tp < T) return hipErrorInvalidValue;
+// S token slices of Tp / S tokens each (Tp / S a multiple of 128); P holds
+// S x (upper tiles) float32 partial tiles of 256 x 256.
+hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, int S,
+                             uint16_t* Xt, float* P, uint16_t* Gs, hipStream_t st) {
+  if (K % 128 || Tp % 128 || Tp < T || S < 1 || Tp % (int64_t(S) * 128)) return hipErrorInvalidValue;
   dim3 tgrid(unsigned((Tp + 63) / 64), unsigned(K / 64));
   transpose_pad_kernel<<<tgrid, 256, 0, st>>>(static_cast<const uint16_t*>(X), T, K, Tp, Xt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int tiles = int((K + BM - 1) / BM);
-  gram_kernel<<<unsigned(gemm_blocks(tiles, tiles)), NT, 0, st>>>(Xt, K, Tp, tiles, Gs);
+  const int nt = int((K + BM - 1) / BM);
+  const int U = nt * (nt + 1) / 2;
+  gram_partial_kernel<<<unsigned(int64_t(U) * S), NT, 0, st>>>(Xt, K, Tp, Tp / S, nt, U, P);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  gram_reduce_kernel<<<dim3(unsigned(U), 16), 256, 0, st>>>(P, S, U, nt, K, Gs);
   return hipGetLastError();
 }
 

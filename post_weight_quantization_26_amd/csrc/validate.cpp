@@ -38,6 +38,23 @@ int64_t stats_chunks(int64_t T, int64_t K, awq_dtype d) {
   return chunks;
 }
 
+int32_t gram_slices(int64_t T, int64_t K) {
+  const int64_t Tp = ceil_div(T, kTileK) * kTileK;
+  const int64_t nt = ceil_div(K, kGemmBM_bf16);
+  const int64_t U = nt * (nt + 1) / 2;
+  int32_t best = 1;
+  double best_cost = double(ceil_div(U, 256));
+  for (int32_t S = 2; S <= 16; S *= 2) {
+    if (Tp % (int64_t(S) * kTileK)) break;
+    const double cost = double(ceil_div(U * S, 256)) / S;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = S;
+    }
+  }
+  return best;
+}
+
 SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_grid, int32_t nb,
                            awq_dtype dtype) {
   SearchLayout L{};
@@ -45,6 +62,7 @@ SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_gr
   const bool gram = is_gram_op(op);
   L.MT = gram ? ceil_div(K, kGemmBM_bf16) : ceil_div(T, bm);
   L.Tp = gram ? ceil_div(T, kTileK) * kTileK : 0;
+  L.S = gram ? gram_slices(T, K) : 0;
   const size_t n_tab = is_scale_op(op) ? size_t(n_grid) : 1;
   size_t off = 0;
   L.s_table = off;
@@ -65,6 +83,11 @@ SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_gr
   off += align_up(64);
   L.xt = off;
   if (gram) off += align_up(size_t(K) * size_t(L.Tp) * 2);
+  L.gp = off;
+  if (gram) {
+    const size_t nt = size_t(ceil_div(K, kGemmBM_bf16));
+    off += align_up(size_t(L.S) * (nt * (nt + 1) / 2) * 256 * 256 * 4);
+  }
   L.gs = off;
   if (gram) off += align_up(size_t(K) * size_t(2 * K) * 2);
   L.total = off;

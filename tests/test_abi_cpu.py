@@ -288,9 +288,13 @@ def test_gram_workspace_and_rejects(L):
     direct = ws(L.AWQ_OP_SEARCH_SCALE, 65536, 4096, 4096, 20, L.AWQ_BF16)
     gram = ws(L.AWQ_OP_SEARCH_SCALE_GRAM, 65536, 4096, 4096, 20, L.AWQ_BF16)
     xt, gs = 4096 * 65536 * 2, 4096 * 8192 * 2
-    # partials shrink to K/256 row tiles; X^T and the G halves are added
-    assert gram > direct - 256 * 20 * 4096 * 4 + xt + gs - (1 << 20)
-    assert gram < direct + xt + gs
+    # the build's float32 partial tiles: 16 token slices (the fewest rounds of
+    # 256 CUs per slice length for 136 upper tiles) of 136 tiles of 256x256
+    gp = 16 * 136 * 256 * 256 * 4
+    # partials shrink to K/256 row tiles; X^T, the G build's partial tiles and
+    # the G halves are added
+    assert gram > direct - 256 * 20 * 4096 * 4 + xt + gp + gs - (1 << 20)
+    assert gram < direct + xt + gp + gs
     assert ws(L.AWQ_OP_SEARCH_SCALE_GRAM, 65536, 4096, 4096, 20, L.AWQ_F32) == 0
     assert ws(L.AWQ_OP_SEARCH_CLIP_GRAM, 700, 300, 384, 5, L.AWQ_BF16) > 384 * 768 * 2 + 384 * 768 * 2
     assert lib.awq_workspace_bytes_batch(L.AWQ_OP_SEARCH_CLIP_GRAM, 700, 300, 384, 5, 1,

@@ -97,6 +97,30 @@ def test_group_equals_stacked_single_search(api):
     assert torch.equal(g["row_sums"], b["row_sums"])
 
 
+def test_group_gram_equals_stacked_gram(api):
+    """The group through one G equals the stacked single-layer Gram search bit
+    for bit, and stays within 1e-3 per row of the direct group search."""
+    T, K = 700, 384
+    X, _ = synth.make_custom(T, 8, K, "bf16", seed=44)
+    Ws = [synth.make_weight(n, K, 0.02, "bf16", seed=44, cid=100, stream=10 + l)
+          for l, n in enumerate((200, 72, 136))]
+    Xd = to_dev(X, "bf16")
+    Wds = [to_dev(W, "bf16") for W in Ws]
+    abar = api.act_stats(Xd)
+    alphas = synth.alpha_grid(7)
+    g = api.search_scale_group(Xd, Wds, abar, alphas, want_row_sums=True, method="gram")
+    cat = api.search_scale(Xd, torch.cat(Wds), abar, alphas, want_row_sums=True, method="gram")
+    assert np.array_equal(g["mse"], cat["mse"])
+    assert torch.equal(g["row_sums"], cat["row_sums"])
+    d = api.search_scale_group(Xd, Wds, abar, alphas, want_row_sums=True)
+    rel = (g["row_sums"] - d["row_sums"]).abs() / d["row_sums"]
+    print(f"group gram vs group direct: max rel {rel.max().item():.2e}")
+    assert rel.max().item() <= 1e-3
+    best = d["index"]
+    assert g["index"] == best or \
+        abs(d["mse"][g["index"]] - d["mse"][best]) < 1e-4 * d["mse"][best]
+
+
 # ----------------------------------------------------------------------------
 # the fold
 # ----------------------------------------------------------------------------
