@@ -201,9 +201,12 @@ def main():
         api.profile_enable(False)
         elapsed = t1 - t0
         if how == "gram":
-            # [G_hi | G_lo]·Eᵀ: 2·(2K)·K flops per candidate row
+            # hi and lo halves of G' (diagonal 256-tiles of G, tiles above it
+            # doubled) against each candidate row: row tile tm contracts over
+            # K - 256·tm columns, 2·2·Σ_tm rows_tm·(K - 256·tm) flops per row
             gemm_ms, gemm_n = prof["gram_search"]
-            flops_per_step = 2.0 * (2 * K) * K * N * cands_per_step
+            tri = sum(min(256, K - m0) * (K - m0) for m0 in range(0, K, 256))
+            flops_per_step = 2.0 * 2 * tri * N * cands_per_step
             kernel_name = "gram_search_kernel"
         else:
             gemm_ms, gemm_n = prof["gemm"]
@@ -236,8 +239,10 @@ def main():
                  "ms_per_step": round(g_el / args.steps * 1e3, 3),
                  "alpha_best": float(g_res["alpha_best"]), "roofline": g_roof,
                  "kernels": g_kern,
-                 "note": "same candidates through G = X^T X: E.G.E^T per row "
-                         "(2*(2K)*K flops) plus G once per search call (2*T*K^2)"}
+                 "note": "same candidates through G = X^T X: e.G.e^T per row from the "
+                         "diagonal 256-tiles of G and twice the tiles above them, in bf16 "
+                         "hi + lo halves (4*sum_tm rows_tm*(K-256*tm) flops, about 2.1*K^2 "
+                         "at K=4096), plus G's upper tiles once per search call"}
     stats_ms, stats_n = prof["stats"]
     stats_gbs = (T * K * X.itemsize) / (stats_ms / 1e3 / max(stats_n, 1)) / 1e9 if stats_n else None
     pack_ms, pack_n = prof["pack"]

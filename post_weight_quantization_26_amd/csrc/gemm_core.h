@@ -138,20 +138,22 @@ __device__ __forceinline__ void dma_tile(const GemmCtx& c, int kt) {
   }
 }
 
-// A and B with their own row strides (in elements); the k-tile index of B
-// wraps every KTb k-tiles (KT = 2·KTb: B's contraction is read twice), so
-// A = [P | Q] against B gives P·Bᵀ + Q·Bᵀ in one k-loop.
+// A and B with their own row strides (in elements). With pair_b, A's
+// contraction alternates 128-wide blocks P_0, Q_0, P_1, Q_1, ... and B's
+// k-tile for A's k-tile kt is (kt / 8)·4 + kt % 4, so each 128-wide block of
+// B is read twice in a row and one k-loop gives Σ_c (P_c + Q_c)·B_cᵀ.
 struct GemmCtx2 {
   __amdgpu_buffer_rsrc_t rsA, rsB;
   int voffA[4], voffB[4];
-  int wave, KT, KTb, oobA, oobB;
+  int wave, KT, oobA, oobB;
+  bool pair_b;
   int rdA[2], rdB[2];
 };
 
 template <int S>
 __device__ __forceinline__ void dma_tile(const GemmCtx2& c, int kt) {
   const bool in = kt < c.KT;
-  const int ktb = kt >= c.KTb ? kt - c.KTb : kt;
+  const int ktb = c.pair_b ? ((kt >> 3) << 2) | (kt & 3) : kt;
   const int kofsA = in ? kt * (BK * 2) : c.oobA;
   const int kofsB = in ? ktb * (BK * 2) : c.oobB;
 #pragma unroll
@@ -256,18 +258,18 @@ __device__ __forceinline__ void gemm_setup(GemmCtx& c, const uint16_t* A, int64_
   }
 }
 
-// Setup for GemmCtx2: A rows of lda elements, B rows of ldb elements, the
-// contraction of A is KA elements (a multiple of 128); B's k wraps every
-// KA / 2 elements when wrap_b, else B is read once over KA as well.
+// Setup for GemmCtx2: A rows of lda elements, B rows of ldb elements, A's
+// contraction KA elements (a multiple of 128). B is read over KA as well, or
+// with pair_b (KA a multiple of 256) over KA / 2, each 128-wide block twice.
 __device__ __forceinline__ void gemm_setup2(GemmCtx2& c, const uint16_t* A, int64_t rows_a,
                                             int64_t lda, const uint16_t* B, int64_t rows_b,
-                                            int64_t ldb, int64_t KA, bool wrap_b) {
+                                            int64_t ldb, int64_t KA, bool pair_b) {
   c.rsA = tile_rsrc(A, rows_a, lda);
   c.rsB = tile_rsrc(B, rows_b, ldb);
   const int tid = threadIdx.x, lane = tid & 63;
   c.wave = tid >> 6;
   c.KT = int(KA / BK);
-  c.KTb = wrap_b ? c.KT / 2 : c.KT;
+  c.pair_b = pair_b;
   c.oobA = BM * int(lda) * 2;
   c.oobB = BN * int(ldb) * 2;
 #pragma unroll

@@ -9,22 +9,30 @@
 //
 //  1. transpose_pad_kernel: Xt [K, Tp] = Xᵀ with the token dim padded to a
 //     multiple of 128 with zeros (zero rows do not change G).
-//  2. gram_partial_kernel: G is symmetric, so only its tiles on and above the
-//     diagonal are formed, on the shared MFMA main loop (gemm_core.h). To
-//     keep every CU busy the token range is split into S slices (S chosen on
-//     the host to balance whole rounds of work); each (tile, slice) unit
-//     stores its float32 partial tile.
+//  2. gram_partial_kernel: G is symmetric, so only its 256x256 tiles on and
+//     above the diagonal are formed, on the shared MFMA main loop
+//     (gemm_core.h). To keep every CU busy the token range is split into S
+//     slices (S chosen on the host to balance whole rounds of work); each
+//     (tile, slice) unit stores its float32 partial tile.
 //     gram_reduce_kernel adds a tile's S partials in a fixed order and stores
-//     G as two bf16 halves, G_hi = bf16(G) and G_lo = bf16(G - G_hi), side by
-//     side in Gs [K, 2K] (hi + lo carries G to about 2^-16 relative, so the
-//     bf16 MFMA that follows does not lose G's precision), for the tile and,
-//     through an LDS transpose, for its mirror image below the diagonal.
+//     it as two bf16 halves, hi = bf16(G) and lo = bf16(G - hi) (hi + lo
+//     carries G to about 2^-16 relative, so the bf16 MFMA that follows does
+//     not lose G's precision). Tiles above the diagonal are stored doubled
+//     (exact), and only the upper tiles are stored at all, because
+//       e·G·eᵀ = Σ_tm [ e_tm·G_tm,tm·e_tmᵀ + Σ_{tn > tm} e_tm·(2·G_tm,tn)·e_tnᵀ ]
+//     over the 256-wide index tiles. Row j of Gs [K, 2K] holds, for each
+//     128-wide block c of columns, hi then lo of that block:
+//       Gs[j][256·c + w] = hi(G'[j][128·c + w]), Gs[j][256·c + 128 + w] = lo(...)
+//     so row tile tm's part from its diagonal tile on is one contiguous run.
 //  3. gram_search_kernel: for a batch of candidate error rows E [Nc, K]
-//     (bf16, the same operands the direct search GEMM uses), one k-loop over
-//     the 2K columns of Gs with E's columns read twice gives
-//     Z[j][n] = Σ_i (G_hi + G_lo)[j][i]·E[n][i] = (G·E_nᵀ)_j in float32. The
+//     (bf16, the same operands the direct search GEMM uses), row tile tm
+//     runs one k-loop over Gs columns [512·tm, 2K) with each 128-wide block
+//     of E (from column 256·tm) read twice, once against hi and once
+//     against lo: Z[j][n] = Σ_{i >= 256·tm} G'[j][i]·E[n][i] in float32. The
 //     epilogue multiplies each Z[j][n] by E[n][j] and sums over the tile's
-//     rows j: partials[tile][n]; the row reduction over tiles gives M_n.
+//     rows j: partials[tm][n]; the row reduction over tiles gives M_n. The
+//     k-loop of row tile tm is 2·(K - 256·tm) long, about half the full
+//     product on average.
 #include "gemm_core.h"
 
 namespace awq {
@@ -126,7 +134,6 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
                                                           int U, int nt, int64_t K,
                                                           uint16_t* __restrict__ Gs) {
 #pragma clang fp contract(off)
-  __shared__ uint16_t th[64][66], tl[64][66];
   const int u = blockIdx.x, sb = blockIdx.y;
   int tm, tn;
   upper_tile(u, nt, tm, tn);
@@ -145,12 +152,12 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
     }
   }
   uint16_t hi[16], lo[16];
+  const float w = tm < tn ? 2.f : 1.f;   // tiles above the diagonal count twice (exact)
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    hi[e] = bf16_bits(g[e]);
-    lo[e] = bf16_bits(g[e] - __uint_as_float(uint32_t(hi[e]) << 16));
-    th[r][c0 + e] = hi[e];
-    tl[r][c0 + e] = lo[e];
+    const float f = g[e] * w;
+    hi[e] = bf16_bits(f);
+    lo[e] = bf16_bits(f - __uint_as_float(uint32_t(hi[e]) << 16));
   }
   const int64_t R = int64_t(tm) * BM + sr + r, C = int64_t(tn) * BN + sc + c0;
   if (R < K && C < K) {   // K is a multiple of 128, so 16 columns are all in or all out
@@ -160,27 +167,10 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
       wh[e] = uint32_t(hi[2 * e]) | (uint32_t(hi[2 * e + 1]) << 16);
       wl[e] = uint32_t(lo[2 * e]) | (uint32_t(lo[2 * e + 1]) << 16);
     }
-    uint4* dh = reinterpret_cast<uint4*>(Gs + R * 2 * K + C);
-    uint4* dl = reinterpret_cast<uint4*>(Gs + R * 2 * K + K + C);
-    dh[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
-    dh[1] = make_uint4(wh[4], wh[5], wh[6], wh[7]);
-    dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
-    dl[1] = make_uint4(wl[4], wl[5], wl[6], wl[7]);
-  }
-  if (tm == tn) return;               // a diagonal tile holds both triangles already
-  __syncthreads();
-  // mirror: element (R, C) also goes to (C, R); thread t writes row c = t / 4
-  // of the transposed sub-block, 16 consecutive rows r of the original.
-  const int64_t Rm = int64_t(tn) * BN + sc + r, Cm = int64_t(tm) * BM + sr + c0;
-  if (Rm < K && Cm < K) {
-    uint32_t wh[8], wl[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      wh[e] = uint32_t(th[c0 + 2 * e][r]) | (uint32_t(th[c0 + 2 * e + 1][r]) << 16);
-      wl[e] = uint32_t(tl[c0 + 2 * e][r]) | (uint32_t(tl[c0 + 2 * e + 1][r]) << 16);
-    }
-    uint4* dh = reinterpret_cast<uint4*>(Gs + Rm * 2 * K + Cm);
-    uint4* dl = reinterpret_cast<uint4*>(Gs + Rm * 2 * K + K + Cm);
+    // the 16 columns lie in one 128-wide block (c0 is a multiple of 16)
+    const int64_t col = (C >> 7) * 256 + (C & 127);
+    uint4* dh = reinterpret_cast<uint4*>(Gs + R * 2 * K + col);
+    uint4* dl = reinterpret_cast<uint4*>(Gs + R * 2 * K + col + 128);
     dh[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
     dh[1] = make_uint4(wh[4], wh[5], wh[6], wh[7]);
     dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
@@ -189,20 +179,26 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
 }
 
 // ---------------------------------------------------------------------------
-// 3. candidates: partials[tm][n] = Σ_{j in row tile tm} (G·E_nᵀ)_j · E[n][j]
+// 3. candidates: partials[tm][n] = Σ_{j in row tile tm} Z[j][n] · E[n][j]
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gram_search_kernel(const uint16_t* __restrict__ Gs, const uint16_t* __restrict__ E,
                         int64_t K, int64_t Nc, int tiles_m, int tiles_n,
                         float* __restrict__ partials) {
-  int tm, tn;
-  if (!tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
+  // Groups of 8 candidate tiles, row tiles in increasing order (longest
+  // k-loops first) within a group; consecutive blocks go round-robin over
+  // the 8 XCDs, so each XCD keeps one E tile for all row tiles of a group.
+  const int per = 8 * tiles_m;
+  const int g = int(blockIdx.x) / per, rem = int(blockIdx.x) - g * per;
+  const int tm = rem >> 3, tn = 8 * g + (rem & 7);
+  if (tn >= tiles_n) return;
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
   const int64_t rows_a = K - m0 < BM ? K - m0 : BM;
   const int64_t rows_b = Nc - n0 < BN ? Nc - n0 : BN;
   GemmCtx2 c;
-  gemm_setup2(c, Gs + m0 * 2 * K, rows_a, 2 * K, E + n0 * K, rows_b, K, 2 * K, true);
+  gemm_setup2(c, Gs + m0 * 2 * K + 2 * m0, rows_a, 2 * K, E + n0 * K + m0, rows_b, K,
+              2 * (K - m0), true);
   floatx16 acc[4][4];
   gemm_mainloop<false>(c, acc);
 
@@ -267,7 +263,8 @@ hipError_t launch_gram_search(const uint16_t* Gs, const void* E, int64_t K, int6
                               float* partials, hipStream_t st) {
   if (K % 128) return hipErrorInvalidValue;
   const int tiles_m = int((K + BM - 1) / BM), tiles_n = int((Nc + BN - 1) / BN);
-  gram_search_kernel<<<unsigned(gemm_blocks(tiles_m, tiles_n)), NT, 0, st>>>(
+  const int64_t blocks = int64_t(tiles_m) * 8 * ((tiles_n + 7) / 8);
+  gram_search_kernel<<<unsigned(blocks), NT, 0, st>>>(
       Gs, static_cast<const uint16_t*>(E), K, Nc, tiles_m, tiles_n, partials);
   return hipGetLastError();
 }
