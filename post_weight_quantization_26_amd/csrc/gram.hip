@@ -32,7 +32,8 @@
 //     epilogue multiplies each Z[j][n] by E[n][j] and sums over the tile's
 //     rows j: partials[tm][n]; the row reduction over tiles gives M_n. The
 //     k-loop of row tile tm is 2·(K - 256·tm) long, about half the full
-//     product on average.
+//     product on average; row tiles tm and nt - 1 - tm share a workgroup so
+//     that every workgroup does the same work.
 #include "gemm_core.h"
 
 namespace awq {
@@ -186,57 +187,67 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gram_search_kernel(const uint16_t* __restrict__ Gs, const uint16_t* __restrict__ E,
                         int64_t K, int64_t Nc, int tiles_m, int tiles_n,
                         float* __restrict__ partials) {
-  // Groups of 8 candidate tiles, row tiles in increasing order (longest
-  // k-loops first) within a group; consecutive blocks go round-robin over
-  // the 8 XCDs, so each XCD keeps one E tile for all row tiles of a group.
-  const int per = 8 * tiles_m;
+  // Row tiles p and tiles_m - 1 - p run in one workgroup, one after the
+  // other: their k-loops add up to (tiles_m + 1)·256 columns of K for every
+  // p, so all workgroups take about the same time. Groups of 8 candidate
+  // tiles; consecutive blocks go round-robin over the 8 XCDs, so each XCD
+  // keeps one E tile for all row tiles of a group.
+  const int pairs = (tiles_m + 1) >> 1;
+  const int per = 8 * pairs;
   const int g = int(blockIdx.x) / per, rem = int(blockIdx.x) - g * per;
-  const int tm = rem >> 3, tn = 8 * g + (rem & 7);
+  const int p = rem >> 3, tn = 8 * g + (rem & 7);
   if (tn >= tiles_n) return;
-  const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
-  const int64_t rows_a = K - m0 < BM ? K - m0 : BM;
-  const int64_t rows_b = Nc - n0 < BN ? Nc - n0 : BN;
-  GemmCtx2 c;
-  gemm_setup2(c, Gs + m0 * 2 * K + 2 * m0, rows_a, 2 * K, E + n0 * K + m0, rows_b, K,
-              2 * (K - m0), true);
-  floatx16 acc[4][4];
-  gemm_mainloop<false>(c, acc);
-
-  // Epilogue: lane l of sub-tile (i, j) holds column n = ... + l % 32 and
-  // rows 8·(v/4) + 4·(l/32) + v % 4 of the wave's 32-row block i; each group
-  // of 4 consecutive rows takes one 8-byte load of E[n][rows].
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  const int n_half = (tiles_m - 1 - p == p) ? 1 : 2;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wm = c.wave >> 1, wn = c.wave & 1;
-  const int64_t row0 = m0 + wm * 128 + 4 * (lane >> 5);
+  const int64_t n0 = int64_t(tn) * BN;
+  const int64_t rows_b = Nc - n0 < BN ? Nc - n0 : BN;
   float* red = reinterpret_cast<float*>(sA0);  // [2][BN]
+#pragma nounroll
+  for (int h = 0; h < n_half; ++h) {
+    const int tm = h ? tiles_m - 1 - p : p;
+    const int64_t m0 = int64_t(tm) * BM;
+    const int64_t rows_a = K - m0 < BM ? K - m0 : BM;
+    GemmCtx2 c;
+    gemm_setup2(c, Gs + m0 * 2 * K + 2 * m0, rows_a, 2 * K, E + n0 * K + m0, rows_b, K,
+                2 * (K - m0), true);
+    floatx16 acc[4][4];
+    gemm_mainloop<false>(c, acc);
+
+    // Epilogue: lane l of sub-tile (i, j) holds column n = ... + l % 32 and
+    // rows 8·(v/4) + 4·(l/32) + v % 4 of the wave's 32-row block i; each
+    // group of 4 consecutive rows takes one 8-byte load of E[n][rows].
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int wm = c.wave >> 1, wn = c.wave & 1;
+    const int64_t row0 = m0 + wm * 128 + 4 * (lane >> 5);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
-    float s = 0.f;
-    if (n < Nc) {
-      const uint16_t* en = E + n * K;
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
+      float s = 0.f;
+      if (n < Nc) {
+        const uint16_t* en = E + n * K;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t r = row0 + i * 32 + 8 * q;      // 4 consecutive rows r..r+3
-          if (r < K) {
-            const uint2 ev = *reinterpret_cast<const uint2*>(en + r);
-            s += acc[i][j][4 * q + 0] * __uint_as_float(ev.x << 16);
-            s += acc[i][j][4 * q + 1] * __uint_as_float(ev.x & 0xFFFF0000u);
-            s += acc[i][j][4 * q + 2] * __uint_as_float(ev.y << 16);
-            s += acc[i][j][4 * q + 3] * __uint_as_float(ev.y & 0xFFFF0000u);
+          for (int q = 0; q < 4; ++q) {
+            const int64_t r = row0 + i * 32 + 8 * q;      // 4 consecutive rows r..r+3
+            if (r < K) {
+              const uint2 ev = *reinterpret_cast<const uint2*>(en + r);
+              s += acc[i][j][4 * q + 0] * __uint_as_float(ev.x << 16);
+              s += acc[i][j][4 * q + 1] * __uint_as_float(ev.x & 0xFFFF0000u);
+              s += acc[i][j][4 * q + 2] * __uint_as_float(ev.y << 16);
+              s += acc[i][j][4 * q + 3] * __uint_as_float(ev.y & 0xFFFF0000u);
+            }
           }
-        }
+      }
+      s += __shfl_xor(s, 32);
+      if (lane < 32) red[wm * BN + wn * 128 + j * 32 + lane] = s;
     }
-    s += __shfl_xor(s, 32);
-    if (lane < 32) red[wm * BN + wn * 128 + j * 32 + lane] = s;
+    __syncthreads();
+    const int64_t col = n0 + tid;
+    if (col < Nc) partials[int64_t(tm) * Nc + col] = red[tid] + red[BN + tid];
+    __syncthreads();  // red lives in LDS stage 0, which the next k-loop refills
   }
-  __syncthreads();
-  const int64_t col = n0 + tid;
-  if (col < Nc) partials[int64_t(tm) * Nc + col] = red[tid] + red[BN + tid];
 }
 
 }  // namespace
@@ -263,7 +274,7 @@ hipError_t launch_gram_search(const uint16_t* Gs, const void* E, int64_t K, int6
                               float* partials, hipStream_t st) {
   if (K % 128) return hipErrorInvalidValue;
   const int tiles_m = int((K + BM - 1) / BM), tiles_n = int((Nc + BN - 1) / BN);
-  const int64_t blocks = int64_t(tiles_m) * 8 * ((tiles_n + 7) / 8);
+  const int64_t blocks = int64_t((tiles_m + 1) / 2) * 8 * ((tiles_n + 7) / 8);
   gram_search_kernel<<<unsigned(blocks), NT, 0, st>>>(
       Gs, static_cast<const uint16_t*>(E), K, Nc, tiles_m, tiles_n, partials);
   return hipGetLastError();
