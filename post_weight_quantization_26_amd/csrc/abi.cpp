@@ -43,9 +43,9 @@ hipError_t launch_w4a16_gemv(const uint16_t* X, int64_t T, int64_t N, int64_t K,
                              float* partial, hipStream_t st);
 hipError_t launch_w4a16_gemv_reduce(const float* partial, int64_t chunks, int64_t T, int64_t N,
                                     int f16, uint16_t* Y, hipStream_t st);
-hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, int S,
-                             uint16_t* Xt, float* P, uint16_t* Gs, hipStream_t st);
-hipError_t launch_gram_search(const uint16_t* Gs, const void* E, int64_t K, int64_t Nc,
+hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, int64_t ldx, int S,
+                             uint16_t* Xt, float* P, int64_t ldg, uint16_t* Gs, hipStream_t st);
+hipError_t launch_gram_search(const uint16_t* Gs, int64_t ldg, const void* E, int64_t K, int64_t Nc,
                               float* partials, hipStream_t st);
 hipError_t launch_fold_vec(void* v, int dtype, int64_t K, const float* s, hipStream_t st);
 hipError_t launch_fold_rows(void* W, int dtype, int64_t K, int64_t K_prev, const float* s,
@@ -153,7 +153,7 @@ awq_status run_batch(const void* X, const Segment* seg, int n_seg, awq_dtype d, 
   }
   if (Gs)
     AWQ_HIP(timed(AWQ_K_GRAM_SEARCH, st,
-                  [&] { return launch_gram_search(Gs, E, K, int64_t(cb) * N, partials, st); }),
+                  [&] { return launch_gram_search(Gs, L.ldg, E, K, int64_t(cb) * N, partials, st); }),
             "gram_search");
   else
     AWQ_HIP(timed(AWQ_K_GEMM, st,
@@ -207,7 +207,7 @@ awq_status build_gram(const void* X, int64_t T, int64_t K, const SearchLayout& L
   float* P = at<float>(ws, L.gp);
   uint16_t* Gs = at<uint16_t>(ws, L.gs);
   AWQ_HIP(timed(AWQ_K_GRAM_BUILD, st,
-                [&] { return launch_gram_build(X, T, K, L.Tp, L.S, Xt, P, Gs, st); }),
+                [&] { return launch_gram_build(X, T, K, L.Tp, L.ldx, L.S, Xt, P, L.ldg, Gs, st); }),
           "gram_build");
   return AWQ_OK;
 }

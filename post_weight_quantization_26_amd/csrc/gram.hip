@@ -46,6 +46,7 @@ namespace {
 // Workgroup = 64 tokens x 64 channels through LDS; 16-byte loads and stores.
 __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ X,
                                                             int64_t T, int64_t K, int64_t Tp,
+                                                            int64_t ldx,
                                                             uint16_t* __restrict__ Xt) {
   __shared__ uint16_t tile[64][72];
   const int64_t t0 = int64_t(blockIdx.x) * 64, k0 = int64_t(blockIdx.y) * 64;
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
     for (int i = 0; i < 4; ++i)
       w[i] = uint32_t(tile[t8 + 2 * i][kr]) | (uint32_t(tile[t8 + 2 * i + 1][kr]) << 16);
     if (t0 + t8 < Tp)
-      *reinterpret_cast<uint4*>(Xt + (k0 + kr) * Tp + t0 + t8) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(Xt + (k0 + kr) * ldx + t0 + t8) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -101,7 +102,7 @@ __device__ __forceinline__ void upper_tile(int u, int nt, int& tm, int& tn) {
 // together, so concurrent blocks share that slice's panels of Xt).
 // P[(s·U + u)][256·256]: float32 partial tile, row-major.
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gram_partial_kernel(const uint16_t* __restrict__ Xt, int64_t K, int64_t Tp, int64_t Ts,
+void gram_partial_kernel(const uint16_t* __restrict__ Xt, int64_t K, int64_t ldx, int64_t Ts,
                          int nt, int U, float* __restrict__ P) {
   const int s = blockIdx.x / U, u = blockIdx.x % U;
   int tm, tn;
@@ -111,7 +112,7 @@ void gram_partial_kernel(const uint16_t* __restrict__ Xt, int64_t K, int64_t Tp,
   const int64_t rows_b = K - n0 < BN ? K - n0 : BN;
   const int64_t t0 = int64_t(s) * Ts;
   GemmCtx2 c;
-  gemm_setup2(c, Xt + m0 * Tp + t0, rows_a, Tp, Xt + n0 * Tp + t0, rows_b, Tp, Ts, false);
+  gemm_setup2(c, Xt + m0 * ldx + t0, rows_a, ldx, Xt + n0 * ldx + t0, rows_b, ldx, Ts, false);
   floatx16 acc[4][4];
   gemm_mainloop<false>(c, acc);
 
@@ -132,7 +133,7 @@ void gram_partial_kernel(const uint16_t* __restrict__ Xt, int64_t K, int64_t Tp,
 // Block (u, sb): the 64x64 sub-block sb of upper tile u. Thread t takes row
 // t / 4 and 16 consecutive columns; the S partials are added in slice order.
 __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restrict__ P, int S,
-                                                          int U, int nt, int64_t K,
+                                                          int U, int nt, int64_t K, int64_t ldg,
                                                           uint16_t* __restrict__ Gs) {
 #pragma clang fp contract(off)
   const int u = blockIdx.x, sb = blockIdx.y;
@@ -170,8 +171,8 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
     }
     // the 16 columns lie in one 128-wide block (c0 is a multiple of 16)
     const int64_t col = (C >> 7) * 256 + (C & 127);
-    uint4* dh = reinterpret_cast<uint4*>(Gs + R * 2 * K + col);
-    uint4* dl = reinterpret_cast<uint4*>(Gs + R * 2 * K + col + 128);
+    uint4* dh = reinterpret_cast<uint4*>(Gs + R * ldg + col);
+    uint4* dl = reinterpret_cast<uint4*>(Gs + R * ldg + col + 128);
     dh[0] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
     dh[1] = make_uint4(wh[4], wh[5], wh[6], wh[7]);
     dl[0] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gram_search_kernel(const uint16_t* __restrict__ Gs, const uint16_t* __restrict__ E,
+void gram_search_kernel(const uint16_t* __restrict__ Gs, int64_t ldg, const uint16_t* __restrict__ E,
                         int64_t K, int64_t Nc, int tiles_m, int tiles_n,
                         float* __restrict__ partials) {
   // Row tiles p and tiles_m - 1 - p run in one workgroup, one after the
@@ -208,7 +209,7 @@ void gram_search_kernel(const uint16_t* __restrict__ Gs, const uint16_t* __restr
     const int64_t m0 = int64_t(tm) * BM;
     const int64_t rows_a = K - m0 < BM ? K - m0 : BM;
     GemmCtx2 c;
-    gemm_setup2(c, Gs + m0 * 2 * K + 2 * m0, rows_a, 2 * K, E + n0 * K + m0, rows_b, K,
+    gemm_setup2(c, Gs + m0 * ldg + 2 * m0, rows_a, ldg, E + n0 * K + m0, rows_b, K,
                 2 * (K - m0), true);
     floatx16 acc[4][4];
     gemm_mainloop<false>(c, acc);
@@ -254,29 +255,31 @@ void gram_search_kernel(const uint16_t* __restrict__ Gs, const uint16_t* __restr
 
 // S token slices of Tp / S tokens each (Tp / S a multiple of 128); P holds
 // S x (upper tiles) float32 partial tiles of 256 x 256.
-hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, int S,
-                             uint16_t* Xt, float* P, uint16_t* Gs, hipStream_t st) {
-  if (K % 128 || Tp % 128 || Tp < T || S < 1 || Tp % (int64_t(S) * 128)) return hipErrorInvalidValue;
+hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, int64_t ldx, int S,
+                             uint16_t* Xt, float* P, int64_t ldg, uint16_t* Gs, hipStream_t st) {
+  if (K % 128 || Tp % 128 || Tp < T || S < 1 || Tp % (int64_t(S) * 128) || ldx < Tp ||
+      ldx % 8 || ldg < 2 * K || ldg % 8)
+    return hipErrorInvalidValue;
   dim3 tgrid(unsigned((Tp + 63) / 64), unsigned(K / 64));
-  transpose_pad_kernel<<<tgrid, 256, 0, st>>>(static_cast<const uint16_t*>(X), T, K, Tp, Xt);
+  transpose_pad_kernel<<<tgrid, 256, 0, st>>>(static_cast<const uint16_t*>(X), T, K, Tp, ldx, Xt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nt = int((K + BM - 1) / BM);
   const int U = nt * (nt + 1) / 2;
-  gram_partial_kernel<<<unsigned(int64_t(U) * S), NT, 0, st>>>(Xt, K, Tp, Tp / S, nt, U, P);
+  gram_partial_kernel<<<unsigned(int64_t(U) * S), NT, 0, st>>>(Xt, K, ldx, Tp / S, nt, U, P);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  gram_reduce_kernel<<<dim3(unsigned(U), 16), 256, 0, st>>>(P, S, U, nt, K, Gs);
+  gram_reduce_kernel<<<dim3(unsigned(U), 16), 256, 0, st>>>(P, S, U, nt, K, ldg, Gs);
   return hipGetLastError();
 }
 
-hipError_t launch_gram_search(const uint16_t* Gs, const void* E, int64_t K, int64_t Nc,
+hipError_t launch_gram_search(const uint16_t* Gs, int64_t ldg, const void* E, int64_t K, int64_t Nc,
                               float* partials, hipStream_t st) {
   if (K % 128) return hipErrorInvalidValue;
   const int tiles_m = int((K + BM - 1) / BM), tiles_n = int((Nc + BN - 1) / BN);
   const int64_t blocks = int64_t((tiles_m + 1) / 2) * 8 * ((tiles_n + 7) / 8);
   gram_search_kernel<<<unsigned(blocks), NT, 0, st>>>(
-      Gs, static_cast<const uint16_t*>(E), K, Nc, tiles_m, tiles_n, partials);
+      Gs, ldg, static_cast<const uint16_t*>(E), K, Nc, tiles_m, tiles_n, partials);
   return hipGetLastError();
 }
 

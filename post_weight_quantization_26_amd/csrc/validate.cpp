@@ -63,6 +63,8 @@ SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_gr
   L.MT = gram ? ceil_div(K, kGemmBM_bf16) : ceil_div(T, bm);
   L.Tp = gram ? ceil_div(T, kTileK) * kTileK : 0;
   L.S = gram ? gram_slices(T, K) : 0;
+  L.ldx = gram ? L.Tp + kXtPad : 0;
+  L.ldg = gram ? 2 * K : 0;
   const size_t n_tab = is_scale_op(op) ? size_t(n_grid) : 1;
   size_t off = 0;
   L.s_table = off;
@@ -82,14 +84,14 @@ SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_gr
   L.scalar = off;
   off += align_up(64);
   L.xt = off;
-  if (gram) off += align_up(size_t(K) * size_t(L.Tp) * 2);
+  if (gram) off += align_up(size_t(K) * size_t(L.ldx) * 2);
   L.gp = off;
   if (gram) {
     const size_t nt = size_t(ceil_div(K, kGemmBM_bf16));
     off += align_up(size_t(L.S) * (nt * (nt + 1) / 2) * 256 * 256 * 4);
   }
   L.gs = off;
-  if (gram) off += align_up(size_t(K) * size_t(2 * K) * 2);
+  if (gram) off += align_up(size_t(K) * size_t(L.ldg) * 2);
   L.total = off;
   return L;
 }
