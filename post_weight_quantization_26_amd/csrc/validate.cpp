@@ -64,7 +64,7 @@ SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_gr
   L.Tp = gram ? ceil_div(T, kTileK) * kTileK : 0;
   L.S = gram ? gram_slices(T, K) : 0;
   L.ldx = gram ? L.Tp + kXtPad : 0;
-  L.ldg = gram ? 2 * K : 0;
+  L.ldg = gram ? 2 * K + kGsPad : 0;
   const size_t n_tab = is_scale_op(op) ? size_t(n_grid) : 1;
   size_t off = 0;
   L.s_table = off;
