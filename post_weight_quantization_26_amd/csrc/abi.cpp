@@ -41,6 +41,10 @@ hipError_t launch_w4a16_gemv(const uint16_t* X, int64_t T, int64_t N, int64_t K,
                              const int32_t* qweight, const int32_t* qzeros,
                              const uint16_t* scales, int group, int f16, int64_t kpw,
                              float* partial, hipStream_t st);
+hipError_t launch_w4a16_mgemv(const uint16_t* X, int64_t T, int64_t N, int64_t K,
+                              const int32_t* qweight, const int32_t* qzeros,
+                              const uint16_t* scales, int group, int f16, int64_t kpw,
+                              float* partial, hipStream_t st);
 hipError_t launch_w4a16_gemv_reduce(const float* partial, int64_t chunks, int64_t T, int64_t N,
                                     int f16, uint16_t* Y, hipStream_t st);
 hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, int64_t ldx, int S,
@@ -486,18 +490,19 @@ extern "C" awq_status awq_w4a16_matmul(const void* X, awq_dtype dtype, int64_t T
   uint16_t* y = static_cast<uint16_t*>(Y);
   if (T <= kW4A16GemvMaxT) {
     float* partial = static_cast<float*>(ws);
-    const int64_t kpw = w4a16_gemv_kpw(N, K);
+    const bool mg = w4a16_use_mgemv(N, qweight, qzeros);
+    const int64_t kpw = mg ? w4a16_mgemv_kpw(N, K) : w4a16_gemv_kpw(N, K);
+    const int64_t chunks = mg ? w4a16_mgemv_chunks(N, K) : w4a16_gemv_chunks(N, K);
     AWQ_HIP(timed(AWQ_K_W4A16, st,
                   [&] {
-                    return launch_w4a16_gemv(x, T, N, K, qweight, qzeros, scales, group_size, f16,
-                                             kpw, partial, st);
+                    return mg ? launch_w4a16_mgemv(x, T, N, K, qweight, qzeros, scales,
+                                                   group_size, f16, kpw, partial, st)
+                              : launch_w4a16_gemv(x, T, N, K, qweight, qzeros, scales,
+                                                  group_size, f16, kpw, partial, st);
                   }),
             "w4a16 gemv");
     AWQ_HIP(timed(AWQ_K_W4A16_REDUCE, st,
-                  [&] {
-                    return launch_w4a16_gemv_reduce(partial, w4a16_gemv_chunks(N, K), T, N, f16,
-                                                    y, st);
-                  }),
+                  [&] { return launch_w4a16_gemv_reduce(partial, chunks, T, N, f16, y, st); }),
             "w4a16 gemv reduce");
     return AWQ_OK;
   }

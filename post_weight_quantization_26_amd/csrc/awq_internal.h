@@ -93,6 +93,18 @@ awq_status check_pack(const void* W, awq_dtype d, int64_t N, int64_t K, const fl
 constexpr int64_t kW4A16GemvMaxT = 16;
 int64_t w4a16_gemv_kpw(int64_t N, int64_t K);
 inline int64_t w4a16_gemv_chunks(int64_t N, int64_t K) { return K / (4 * w4a16_gemv_kpw(N, K)); }
+// Decode on the matrix cores: N a multiple of 16 and qweight/qzeros 8-byte
+// aligned (a lane reads two adjacent word columns at once); otherwise the
+// float32 GEMV above.
+inline bool w4a16_use_mgemv(int64_t N, const void* qweight, const void* qzeros) {
+  return N % 16 == 0 && (reinterpret_cast<uintptr_t>(qweight) & 7u) == 0 &&
+         (reinterpret_cast<uintptr_t>(qzeros) & 7u) == 0;
+}
+int64_t w4a16_mgemv_kpw(int64_t N, int64_t K);
+inline int64_t w4a16_mgemv_chunks(int64_t N, int64_t K) {
+  const int64_t span = 4 * w4a16_mgemv_kpw(N, K);
+  return (K + span - 1) / span;
+}
 awq_status check_w4a16(const void* X, awq_dtype d, int64_t T, int64_t N, int64_t K,
                        const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                        int32_t group, const void* Y, const void* ws, size_t ws_bytes);

@@ -1,6 +1,7 @@
 // Argument checks and workspace arithmetic of the C ABI. Plain C++: no HIP
 // headers and no HIP calls, so every rejection path runs on a machine
 // without a GPU.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -266,6 +267,15 @@ int64_t w4a16_gemv_kpw(int64_t N, int64_t K) {
   return kpw;
 }
 
+// k rows per wave of the matrix-core GEMV: the largest of 512, 256, 128 that
+// still gives 384 workgroups (1.5 per CU), else 128.
+int64_t w4a16_mgemv_kpw(int64_t N, int64_t K) {
+  const int64_t col_blocks = ceil_div(N / 8, 32);
+  for (int64_t kpw = 512; kpw > 128; kpw /= 2)
+    if (col_blocks * ceil_div(K, 4 * kpw) >= 384) return kpw;
+  return 128;
+}
+
 awq_status check_w4a16(const void* X, awq_dtype d, int64_t T, int64_t N, int64_t K,
                        const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                        int32_t group, const void* Y, const void* ws, size_t ws_bytes) {
@@ -301,8 +311,12 @@ extern "C" size_t awq_w4a16_workspace_bytes(int64_t T, int64_t N, int64_t K, awq
   if (T < 1 || N < 1 || K < 1 || T > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
   if (dtype != AWQ_BF16 && dtype != AWQ_F16) return 0;
   if (N % 8 || K % kTileK) return 0;
-  if (T <= kW4A16GemvMaxT)
-    return align_up(size_t(w4a16_gemv_chunks(N, K)) * size_t(T) * size_t(N) * 4);
+  if (T <= kW4A16GemvMaxT) {
+    // either decode path, whichever the pointers select
+    const int64_t chunks = N % 16 ? w4a16_gemv_chunks(N, K)
+                                  : std::max(w4a16_gemv_chunks(N, K), w4a16_mgemv_chunks(N, K));
+    return align_up(size_t(chunks) * size_t(T) * size_t(N) * 4);
+  }
   return align_up(size_t(N) * size_t(K) * 2);
 }
 

@@ -10,14 +10,19 @@
 // 16-bit activations). Ŵ is formed exactly in float32 ((q - z) is an integer
 // of at most 4 bits and the scale an fp16 value).
 //
-// Two paths, by the number of token rows T:
-//  * T <= 16 (decode): fused GEMV. A lane owns one qweight word column (8
-//    output channels) and a run of k rows; it dequantises each word in
-//    registers and accumulates T x 8 float32 sums. The 4 waves of a
-//    workgroup take consecutive k runs and meet in LDS; one float32 partial
-//    per (k chunk, t, n) goes to the workspace and a second kernel adds the
-//    chunks in a fixed order and rounds once to the output type. Bound by
-//    HBM reads of qweight (N·K/2 bytes) and by the dequantisation ALU work.
+// Three kernels, by the number of token rows T and the layout:
+//  * T <= 16 (decode), N a multiple of 16: the codes go to the matrix cores
+//    as exact small numbers (B = 1 + q/16) against the activations, 16 token
+//    rows per v_mfma_f32_16x16x32, and the zero points and scales are applied
+//    to the float32 block sums (w4a16_mgemv_kernel, below).
+//  * T <= 16 otherwise: fused float32 GEMV. A lane owns one qweight word
+//    column (8 output channels) and a run of k rows; it dequantises each word
+//    in registers and accumulates T x 8 float32 sums.
+//    In both, the 4 waves of a workgroup take consecutive k runs and meet in
+//    LDS; one float32 partial per (k chunk, t, n) goes to the workspace and a
+//    second kernel adds the chunks in a fixed order and rounds once to the
+//    output type. Bound by HBM reads of qweight (N·K/2 bytes) and by the
+//    unpacking ALU work.
 //  * T > 16 (prefill): the packed layer is dequantised once into [N, K]
 //    16-bit operand rows in the workspace (rounded once, to nearest even, to
 //    the activation type), then the MFMA main loop of the search GEMM
@@ -240,6 +245,225 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// decode on the matrix cores: exact integer codes against the activations
+// ---------------------------------------------------------------------------
+//
+// Per group g of k rows, Σ_k x·ŵ = scale·Σ_k x·(q − z). The codes enter the
+// MFMA as B = 1 + q/16, built from the bits: q goes into the top four
+// mantissa bits of a 16-bit float of exponent 0 (bf16 0x3F80 | q << 3, fp16
+// 0x3C00 | q << 6). Every x·B has at most 16 significant bits, so the
+// v_mfma_f32_16x16x32 products are exact and P'[t][n] = Σ_k x[t][k]·B[k][n]
+// is an ordinary float32 sum. One more MFMA against a column of ones gives
+// S[t] = Σ_k x[t][k], and Σ_k x·(q − z) = 16·P' − (16 + z)·S. At the end of
+// each group a lane adds scale·fma(−(16 + z), S, 16·P') to its float32
+// totals. Token rows past T are zero operands.
+//
+// Operand layout (16x16x32): lane l holds 8 consecutive k (k = 8·(l/16) + e)
+// of row l % 16 of A and of column l % 16 of B, and receives D[4·(l/16) + v]
+// [l % 16] for v = 0..3. The contraction only needs A and B to agree on which
+// k each (lane group, element) holds, so a lane loads k rows 8·(l/16) + e of
+// its qweight words and each nibble position r of a word feeds its own MFMA:
+// MFMA (c, r) covers output channels 8·(wc + c) + r over the 16 lanes' word
+// columns wc. A is read straight from X (16 bytes per lane and k-block).
+//
+// Workgroup (cb, kc): 4 waves, 32 word columns (256 outputs; a lane owns two
+// adjacent word columns, one 8-byte load per k row), k rows kc·4·kpw ..;
+// wave w takes kpw of them (a multiple of 32), and the waves' totals meet in
+// LDS in a fixed order before one float32 partial per (kc, t, n) is stored.
+constexpr int kMgWaves = 4;
+constexpr int kMgCols = 32;       // word columns per workgroup
+constexpr int kMgMfma = 16;       // (c, r): 2 word columns x 8 nibbles per lane
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4 mfma16(bf16x8_t a, bf16x8_t b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mfma16(f16x8_t a, f16x8_t b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// B = 1 + q/16 for nibble r of two qweight words (two consecutive k rows),
+// packed as a pair of 16-bit floats (lo word in the low half). v_perm puts
+// byte r/2 of each word at bits 0-7 and 16-23; one shift moves the nibble to
+// the top four mantissa bits and one and-or masks it and sets the exponent.
+// The other bytes perm and the shift bring along fall outside the mask.
+template <bool F16, int R>
+__device__ __forceinline__ uint32_t code_pair(uint32_t w_lo, uint32_t w_hi) {
+  constexpr uint32_t b = R >> 1;
+  const uint32_t x = __builtin_amdgcn_perm(w_hi, w_lo, 0x0C000C00u | ((4u + b) << 16) | b);
+  // nibble at bits 0-3 (R even) or 4-7 (R odd) of each half -> mantissa top
+  constexpr int kTop = F16 ? 6 : 3;          // lowest bit of the top 4 mantissa bits
+  constexpr int kShift = kTop - 4 * (R & 1);
+  const uint32_t y = kShift >= 0 ? (x << kShift) : (x >> -kShift);
+  constexpr uint32_t kMask = F16 ? 0x03C003C0u : 0x00780078u;
+  constexpr uint32_t kOne = F16 ? 0x3C003C00u : 0x3F803F80u;
+  return (y & kMask) | kOne;
+}
+
+// Registers of one wave: totals per MFMA (c, r); four k-block slots (codes,
+// activations, and the group parameters when the block opens a group: raw
+// fp16 scale pairs and packed zero points), of which three are live at a
+// time (two blocks are prefetched ahead); and the open group's scales and
+// decoded zero points.
+constexpr int kMgSlots = 4;
+
+template <bool F16>
+struct MgState {
+  floatx4 tot[kMgMfma];
+  uint2 w[kMgSlots][8];
+  uint4 a[kMgSlots];
+  uint4 ps0[kMgSlots], ps1[kMgSlots];
+  uint2 pz[kMgSlots];
+  uint4 s0, s1;
+  float zf[kMgMfma];
+};
+
+// Block j (0..3) of a 128-row super-block starting at kb, for groups of G
+// rows (a 128-row super-block holds whole groups, so j's place in its group
+// is known here): at a group's first block take its parameters from the
+// block's slot; prefetch block j + 2 into slot (j + 2) % 4 (with its group's
+// parameters if it opens one); then S = Σ x and, per (c, r), P' = Σ x·B
+// from zero, folded at once: tot += scale·(P' − ((16 + z)/16)·S). That is
+// scale·(16·P' − (16 + z)·S) / 16 with the same rounding; the factor 16 is
+// applied once at the end.
+template <bool F16, int G, int J, class LoadData, class LoadPar>
+__device__ __forceinline__ void mg_block(MgState<F16>& st, int kb, const LoadData& load_data,
+                                         const LoadPar& load_par) {
+  typedef typename Operand<F16>::type V;
+  constexpr int BPG = G / 32;
+  constexpr bool kFirst = J % BPG == 0;
+  constexpr bool kAheadOpens = (J + 2) % BPG == 0;
+  constexpr int B = J & 3, BA = (J + 2) & 3;
+  if constexpr (kFirst) {
+    st.s0 = st.ps0[B];
+    st.s1 = st.ps1[B];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      st.zf[r] = float(16u + ((st.pz[B].x >> (4 * r)) & 0xFu)) * 0.0625f;
+      st.zf[8 + r] = float(16u + ((st.pz[B].y >> (4 * r)) & 0xFu)) * 0.0625f;
+    }
+  }
+  load_data(kb + 32 * (J + 2), st.w[BA], st.a[BA]);
+  if constexpr (kAheadOpens) load_par(kb + 32 * (J + 2), st.ps0[BA], st.ps1[BA], st.pz[BA]);
+
+  const V a = __builtin_bit_cast(V, st.a[B]);
+  const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+  V ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = 1;
+  const floatx4 sx = mfma16(a, ones, zero);
+  const uint32_t sw[8] = {st.s0.x, st.s0.y, st.s0.z, st.s0.w, st.s1.x, st.s1.y, st.s1.z, st.s1.w};
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    uint32_t w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = c ? st.w[B][e].y : st.w[B][e].x;
+#define AWQ_MG_CODE(R)                                                                      \
+  {                                                                                         \
+    constexpr int m = c * 8 + R;                                                            \
+    const V b = __builtin_bit_cast(                                                         \
+        V, make_uint4(code_pair<F16, R>(w[0], w[1]), code_pair<F16, R>(w[2], w[3]),         \
+                      code_pair<F16, R>(w[4], w[5]), code_pair<F16, R>(w[6], w[7])));       \
+    const floatx4 p = mfma16(a, b, zero);                                                   \
+    const float sc = f16_to_f32(uint16_t((sw[m >> 1] >> (16 * (m & 1))) & 0xFFFFu));        \
+    for (int v = 0; v < 4; ++v)                                                             \
+      st.tot[m][v] = __builtin_fmaf(sc, __builtin_fmaf(-st.zf[m], sx[v], p[v]), st.tot[m][v]); \
+  }
+    if (c == 0) {
+      constexpr int c = 0;
+      AWQ_MG_CODE(0) AWQ_MG_CODE(1) AWQ_MG_CODE(2) AWQ_MG_CODE(3)
+      AWQ_MG_CODE(4) AWQ_MG_CODE(5) AWQ_MG_CODE(6) AWQ_MG_CODE(7)
+    } else {
+      constexpr int c = 1;
+      AWQ_MG_CODE(0) AWQ_MG_CODE(1) AWQ_MG_CODE(2) AWQ_MG_CODE(3)
+      AWQ_MG_CODE(4) AWQ_MG_CODE(5) AWQ_MG_CODE(6) AWQ_MG_CODE(7)
+    }
+#undef AWQ_MG_CODE
+  }
+}
+
+template <bool F16, int G>
+__global__ __launch_bounds__(256, 2) void w4a16_mgemv_kernel(
+    const uint16_t* __restrict__ X, int64_t T, int64_t N, int64_t K,
+    const int32_t* __restrict__ qweight, const int32_t* __restrict__ qzeros,
+    const uint16_t* __restrict__ scales, int kpw, float* __restrict__ partial) {
+  __shared__ float red[kMgWaves][16][kMgCols * 8 + 4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int jj = lane & 15, lg = lane >> 4;
+  const int64_t N8 = N / 8;
+  // The lane's two word columns. Lanes past N (N8 is even: both columns or
+  // neither) and token rows past T read column 0 / row 0 instead: every load
+  // stays in bounds and needs no branch, and an MFMA output column depends
+  // only on its own B column (an output row on its own A row), so those
+  // lanes' results, which are never stored, do not reach the others.
+  const int64_t wc = int64_t(blockIdx.x) * kMgCols + 2 * jj;
+  const int64_t wcl = wc < N8 ? wc : 0;
+  // This wave's k rows: kpw (a multiple of 128) from its place in the grid,
+  // cut at K (a multiple of 128); waves past K have none.
+  const int kw0 = (int(blockIdx.y) * kMgWaves + wave) * kpw;
+  const int kw1 = kw0 + kpw < int(K) ? kw0 + kpw : int(K);
+  const uint16_t* xrow = X + int64_t(jj < T ? jj : 0) * K + 8 * lg;
+  const int32_t* qlane = qweight + int64_t(8 * lg) * N8 + wcl;
+
+  MgState<F16> st;
+#pragma unroll
+  for (int m = 0; m < kMgMfma; ++m) st.tot[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  if (kw0 < kw1) {
+    // k-blocks past the wave's last re-read its last block (a harmless
+    // in-bounds prefetch)
+    auto load_data = [&](int kb, uint2 (&w)[8], uint4& a) {
+      const int kc = kb < kw1 ? kb : kw1 - 32;
+      const int32_t* q = qlane + int64_t(kc) * N8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = *reinterpret_cast<const uint2*>(q + e * N8);
+      a = *reinterpret_cast<const uint4*>(xrow + kc);
+    };
+    auto load_par = [&](int kb, uint4& s0, uint4& s1, uint2& z) {
+      const int64_t g = (kb < kw1 ? kb : kw1 - 32) / G;
+      s0 = *reinterpret_cast<const uint4*>(scales + g * N + 8 * wcl);
+      s1 = *reinterpret_cast<const uint4*>(scales + g * N + 8 * wcl + 8);
+      z = *reinterpret_cast<const uint2*>(qzeros + g * N8 + wcl);
+    };
+    load_data(kw0, st.w[0], st.a[0]);
+    load_par(kw0, st.ps0[0], st.ps1[0], st.pz[0]);
+    load_data(kw0 + 32, st.w[1], st.a[1]);
+    if (G == 32) load_par(kw0 + 32, st.ps0[1], st.ps1[1], st.pz[1]);
+    for (int kb = kw0; kb < kw1; kb += 128) {
+      mg_block<F16, G, 0>(st, kb, load_data, load_par);
+      __builtin_amdgcn_sched_barrier(0);
+      mg_block<F16, G, 1>(st, kb, load_data, load_par);
+      __builtin_amdgcn_sched_barrier(0);
+      mg_block<F16, G, 2>(st, kb, load_data, load_par);
+      __builtin_amdgcn_sched_barrier(0);
+      mg_block<F16, G, 3>(st, kb, load_data, load_par);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < kMgMfma; ++m)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) st.tot[m][v] *= 16.f;
+
+  // totals -> LDS [wave][t][n_local], n_local = 8·(2·jj + c) + r
+#pragma unroll
+  for (int m = 0; m < kMgMfma; ++m)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) red[wave][4 * lg + v][16 * jj + m] = st.tot[m][v];
+  __syncthreads();
+  const int nl = threadIdx.x;
+  const int64_t n = int64_t(blockIdx.x) * kMgCols * 8 + nl;
+  if (n < N) {
+    for (int t = 0; t < T; ++t) {
+      const float s = ((red[0][t][nl] + red[1][t][nl]) + red[2][t][nl]) + red[3][t][nl];
+      partial[(int64_t(blockIdx.y) * T + t) * N + n] = s;
+    }
+  }
+}
+
 // Y[t][n] = Σ_c partial[c][t][n], chunks added in a fixed order (lane group
 // cl takes chunks cl, cl+4, ...; the four sums are then added in order),
 // rounded once. 64 outputs per workgroup.
@@ -323,6 +547,40 @@ hipError_t launch_w4a16_gemv(const uint16_t* X, int64_t T, int64_t N, int64_t K,
     launch_gemv<true>(grid, st, X, T, N, K, qweight, qzeros, scales, group, int(kpw), partial);
   else
     launch_gemv<false>(grid, st, X, T, N, K, qweight, qzeros, scales, group, int(kpw), partial);
+  return hipGetLastError();
+}
+
+// 1 <= T <= 16 token rows; N a multiple of 16, qweight and qzeros 8-byte
+// aligned; K a multiple of 128; kpw a multiple of 128; partial holds
+// ceil(K / (4·kpw)) x T x N floats.
+template <bool F16>
+void launch_mgemv_g(int group, dim3 grid, hipStream_t st, const uint16_t* X, int64_t T, int64_t N,
+                    int64_t K, const int32_t* qweight, const int32_t* qzeros,
+                    const uint16_t* scales, int kpw, float* partial) {
+  if (group == 32)
+    w4a16_mgemv_kernel<F16, 32><<<grid, 256, 0, st>>>(X, T, N, K, qweight, qzeros, scales, kpw,
+                                                      partial);
+  else if (group == 64)
+    w4a16_mgemv_kernel<F16, 64><<<grid, 256, 0, st>>>(X, T, N, K, qweight, qzeros, scales, kpw,
+                                                      partial);
+  else
+    w4a16_mgemv_kernel<F16, 128><<<grid, 256, 0, st>>>(X, T, N, K, qweight, qzeros, scales, kpw,
+                                                       partial);
+}
+
+hipError_t launch_w4a16_mgemv(const uint16_t* X, int64_t T, int64_t N, int64_t K,
+                              const int32_t* qweight, const int32_t* qzeros,
+                              const uint16_t* scales, int group, int f16, int64_t kpw,
+                              float* partial, hipStream_t st) {
+  if (T < 1 || T > 16 || N % 16 || K % 128 || kpw < 128 || kpw % 128 || K > (int64_t(1) << 30) ||
+      (group != 32 && group != 64 && group != 128))
+    return hipErrorInvalidValue;
+  const int64_t chunks = (K + kMgWaves * kpw - 1) / (kMgWaves * kpw);
+  dim3 grid(unsigned((N / 8 + kMgCols - 1) / kMgCols), unsigned(chunks));
+  if (f16)
+    launch_mgemv_g<true>(group, grid, st, X, T, N, K, qweight, qzeros, scales, int(kpw), partial);
+  else
+    launch_mgemv_g<false>(group, grid, st, X, T, N, K, qweight, qzeros, scales, int(kpw), partial);
   return hipGetLastError();
 }
 

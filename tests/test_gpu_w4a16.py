@@ -1,16 +1,22 @@
 """GPU parity of the W4A16 consumer of the packed layout, through the C ABI.
 
 Tolerances (derived from the arithmetic, checked per output element):
-  * The kernels form Ŵ = (q - z)·scale exactly in float32. The GEMV path
-    (T <= 16) uses it as is; the GEMM path rounds it once to the activation
-    type (bf16 or fp16) for the MFMA. The test rebuilds exactly that operand
-    ("model") and computes Y_model = X·Ŵ_opᵀ in float64.
-  * GPU and model may differ by float32 accumulation over K and by the one
-    rounding of the output: |Y - Y_model| <= γ_K·Σ_k |x_k ŵ_k| + u·|Y_model|
-    + tiny, with γ_K = K·2^-23 / (1 - K·2^-23) and u = 2^-8 (bf16) or 2^-11
-    (fp16) plus the smallest normal of the output type.
-  * Against the float64 oracle (exact Ŵ) the GEMM path may also differ by
-    the operand rounding: u·Σ_k |x_k ŵ_k|.
+  * Decode (T <= 16) works with the exact Ŵ = (q - z)·scale. The model is
+    Y_model = X·Ŵᵀ in float64. With N a multiple of 16 the matrix cores take
+    B = 1 + q/16 (exact in 16 bits; every product x·B exact in float32) and
+    Σ_k x·(q - z) = 16·Σ x·B - (16 + z)·Σ x per k-block of 32, so float32
+    rounding acts on sums of |x|·(16 + q) and |x|·(16 + z). Bound:
+    γ_{K+4}·Σ_k |x_k|·(32 + q_k + z_k)·scale_k (it also covers the float32
+    GEMV, which rounds sums of |x·ŵ| <= |x|·(q + z)·scale).
+  * Prefill (T > 16) rounds Ŵ once to the activation type (bf16 or fp16) for
+    the MFMA; the test rebuilds exactly that operand and Y_model = X·Ŵ_opᵀ.
+    GPU and model may differ by float32 accumulation over K:
+    γ_K·Σ_k |x_k ŵ_k|.
+  * Both also round the output once: + u·|Y_model| + tiny, with
+    γ_n = n·2^-23 / (1 - n·2^-23), u = 2^-8 (bf16) or 2^-11 (fp16) and tiny
+    the smallest normal of the output type.
+  * Against the float64 oracle (exact Ŵ) the prefill path may also differ
+    by the operand rounding: u·Σ_k |x_k ŵ_k|.
 """
 import numpy as np
 import pytest
@@ -71,8 +77,15 @@ def check_consumer(api, T, N, K, group, dtype, seed):
         w32 = w_exact.astype(np.float32)
         w_op = _dec(_enc(w32, dtype), dtype).astype(np.float64)
     y_model = x @ w_op.T
-    mag = np.abs(x) @ np.abs(w_op).T
-    g = K * U32 / (1 - K * U32)
+    if T <= 16:
+        q = O.unpack_codes(qw, N, 4).astype(np.float64)                  # [K, N]
+        z = np.repeat(O.unpack_codes(qz, N, 4), group, axis=0).astype(np.float64)
+        scl = np.repeat(sc.view(np.float16).astype(np.float64), group, axis=0)
+        mag = np.abs(x) @ ((32.0 + q + z) * scl)
+        g = (K + 4) * U32 / (1 - (K + 4) * U32)
+    else:
+        mag = np.abs(x) @ np.abs(w_op).T
+        g = K * U32 / (1 - K * U32)
     bound = g * mag + UOUT[dtype] * np.abs(y_model) + TINY[dtype]
     err = np.abs(y - y_model)
     worst = (err / bound).max()
@@ -98,6 +111,29 @@ def test_gemv_group_sizes(api, group):
 
 def test_gemv_large(api):
     check_consumer(api, 2, 4096, 4096, 128, "f16", seed=95)
+
+
+# N a multiple of 16: the matrix-core decode path (k runs of 128 rows per
+# wave, 4 waves per chunk). K = 384: one chunk whose fourth wave has no rows;
+# K = 1152: the third chunk has rows for its first wave only; K = 128: one
+# busy wave. N = 272 leaves 2 of the last workgroup's 32 word columns; N =
+# 4112 makes 17 workgroups of columns.
+@pytest.mark.parametrize("T", [1, 3, 8, 16])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_mgemv_path(api, T, dtype):
+    check_consumer(api, T, 272, 1152, 128, dtype, seed=150 + T)
+
+
+@pytest.mark.parametrize("group", [32, 64])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_mgemv_group_sizes(api, group, dtype):
+    check_consumer(api, 5, 4112, 384, group, dtype, seed=160 + group)
+
+
+@pytest.mark.parametrize("K", [128, 2048, 4096])
+def test_mgemv_k_spans(api, K):
+    # K = 2048 and 4096 use several chunks of 4·kpw rows
+    check_consumer(api, 16, 1024, K, 128, "bf16", seed=170 + K // 128)
 
 
 @pytest.mark.parametrize("T", [17, 300])
