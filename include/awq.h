@@ -5,6 +5,7 @@
  * weights, K input channels, N output channels) the library computes:
  *
  *   awq_act_stats      ā_j = mean_t |x_tj|                       (step 1)
+ *   awq_act_stats_accumulate / _finalize   the same over calibration batches
  *   awq_scale_table    s_j(α) = ā_j^α / sqrt(max ā^α · min ā^α)  (step 2)
  *   awq_search_scale   for each α of a grid: quantise W·diag(s) group-wise,
  *                      fold diag(s)^-1 back, measure the output MSE against
@@ -108,6 +109,23 @@ size_t awq_workspace_bytes_batch(int op, int64_t T, int64_t N, int64_t K, int32_
  * Does not synchronise. */
 awq_status awq_act_stats(const void* X, awq_dtype x_dtype, int64_t T, int64_t K, float* abar,
                          void* ws, size_t ws_bytes, void* stream);
+
+/* Step 1 over a calibration set that comes in batches: ā is the mean over
+ * all their tokens (the statistic is a plain mean, so batches add up).
+ * awq_act_stats_accumulate adds Σ_t |x_tj| of one batch X [T, K] (bf16, f16
+ * or f32; K as for awq_act_stats) to sums[j]: sums [K] float64 on the
+ * device, owned by the caller, zeroed by the caller before the first batch.
+ * Batches may differ in T; their order fixes the float64 rounding (a single
+ * batch gives exactly awq_act_stats's sum). Workspace as for awq_act_stats
+ * with this batch's T (awq_workspace_bytes(AWQ_OP_STATS, T, 1, K, 1, dtype)).
+ * awq_act_stats_finalize writes abar_j = fl32(sums_j / count), count = the
+ * total number of tokens (>= 1). Neither synchronises; calls on one stream
+ * run in order. Errors: AWQ_E_INVALID for NULL or misaligned pointers (sums
+ * 8-byte, abar 4-byte) or bad sizes, AWQ_E_WORKSPACE as for awq_act_stats. */
+awq_status awq_act_stats_accumulate(const void* X, awq_dtype x_dtype, int64_t T, int64_t K,
+                                    double* sums, void* ws, size_t ws_bytes, void* stream);
+awq_status awq_act_stats_finalize(const double* sums, int64_t count, int64_t K, float* abar,
+                                  void* stream);
 
 /* Step 2 — scale table s[a][j] = ā_j^α_a / sqrt(max_k ā_k^α_a · min_k ā_k^α_a),
  * computed in float64 and rounded once to f32; ā is floored at 1e-8.

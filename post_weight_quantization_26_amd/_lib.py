@@ -41,6 +41,9 @@ SIGNATURES = {
     "awq_workspace_bytes_batch": (c_sz, [ctypes.c_int, c_i64, c_i64, c_i64, c_i32, c_i32,
                                          ctypes.c_int]),
     "awq_act_stats": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]),
+    "awq_act_stats_accumulate": (ctypes.c_int,
+                                 [c_vp, ctypes.c_int, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]),
+    "awq_act_stats_finalize": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_vp]),
     "awq_scale_table": (ctypes.c_int, [c_vp, c_i64, c_fp, c_i32, c_vp, c_vp]),
     "awq_search_scale": (ctypes.c_int, [c_vp, c_vp, ctypes.c_int, c_i64, c_i64, c_i64, c_vp, c_fp,
                                         c_i32, QConfig, c_vp, c_fp, c_dp, c_vp, c_vp, c_sz, c_vp]),

@@ -75,6 +75,31 @@ def act_stats(X: torch.Tensor, ws: Optional[torch.Tensor] = None,
     return abar
 
 
+def act_stats_accumulate(X: torch.Tensor, sums: torch.Tensor,
+                         ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """sums[j] += Σ_t |x_tj| for one calibration batch X [T, K]; sums is a
+    float64 [K] device tensor the caller zeroes before the first batch."""
+    _dev(X, "X")
+    _dev(sums, "sums")
+    T, K = X.shape
+    if sums.dtype != torch.float64 or sums.numel() != K:
+        raise ValueError("sums must be a float64 tensor of K elements")
+    ws = _workspace(ws, workspace_bytes(L.AWQ_OP_STATS, T, 1, K, 1, X.dtype), X.device)
+    L.check(L.lib().awq_act_stats_accumulate(_ptr(X), _dtype(X), T, K, _ptr(sums), _ptr(ws),
+                                             ws.numel(), _stream()))
+    return sums
+
+
+def act_stats_finalize(sums: torch.Tensor, count: int,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """abar_j = fl32(sums_j / count), count = all calibration tokens."""
+    _dev(sums, "sums")
+    K = sums.numel()
+    abar = out if out is not None else torch.empty(K, dtype=torch.float32, device=sums.device)
+    L.check(L.lib().awq_act_stats_finalize(_ptr(sums), count, K, _ptr(abar), _stream()))
+    return abar
+
+
 def scale_table(abar: torch.Tensor, alphas: Sequence[float]) -> torch.Tensor:
     """s[a][j] = abar_j^alpha_a / sqrt(max abar^alpha_a * min abar^alpha_a), float32."""
     _dev(abar, "abar")

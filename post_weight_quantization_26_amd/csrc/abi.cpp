@@ -47,6 +47,10 @@ hipError_t launch_w4a16_mgemv(const uint16_t* X, int64_t T, int64_t N, int64_t K
                               float* partial, hipStream_t st);
 hipError_t launch_w4a16_gemv_reduce(const float* partial, int64_t chunks, int64_t T, int64_t N,
                                     int f16, uint16_t* Y, hipStream_t st);
+hipError_t launch_stats_accumulate(const void* X, int dtype, int64_t T, int64_t K,
+                                   int64_t chunks, double* partial, double* sums, hipStream_t st);
+hipError_t launch_stats_divide(const double* sums, int64_t count, int64_t K, float* abar,
+                               hipStream_t st);
 hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, int64_t ldx, int S,
                              uint16_t* Xt, float* P, int64_t ldg, uint16_t* Gs, hipStream_t st);
 hipError_t launch_gram_search(const uint16_t* Gs, int64_t ldg, const void* E, int64_t K, int64_t Nc,
@@ -188,6 +192,35 @@ extern "C" awq_status awq_act_stats(const void* X, awq_dtype x_dtype, int64_t T,
                                       st);
                 }),
           "act_stats");
+  return AWQ_OK;
+}
+
+extern "C" awq_status awq_act_stats_accumulate(const void* X, awq_dtype x_dtype, int64_t T,
+                                               int64_t K, double* sums, void* ws,
+                                               size_t ws_bytes, void* stream) {
+  if (!sums) return set_error(AWQ_E_INVALID, "act_stats_accumulate: NULL sums");
+  if (reinterpret_cast<uintptr_t>(sums) & 7u)
+    return set_error(AWQ_E_INVALID, "act_stats_accumulate: sums must be 8-byte aligned");
+  // check_stats wants a non-null abar; the sums stand in for it
+  awq_status s = check_stats(X, x_dtype, T, K, reinterpret_cast<const float*>(sums), ws, ws_bytes);
+  if (s != AWQ_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t chunks = stats_chunks(T, K, x_dtype);
+  AWQ_HIP(timed(AWQ_K_STATS, st,
+                [&] {
+                  return launch_stats_accumulate(X, dt(x_dtype), T, K, chunks,
+                                                 static_cast<double*>(ws), sums, st);
+                }),
+          "act_stats_accumulate");
+  return AWQ_OK;
+}
+
+extern "C" awq_status awq_act_stats_finalize(const double* sums, int64_t count, int64_t K,
+                                             float* abar, void* stream) {
+  awq_status s = check_stats_finalize(sums, count, K, abar);
+  if (s != AWQ_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  AWQ_HIP(launch_stats_divide(sums, count, K, abar, st), "act_stats_finalize");
   return AWQ_OK;
 }
 

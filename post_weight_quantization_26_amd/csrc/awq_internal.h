@@ -68,6 +68,7 @@ SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_gr
                            awq_dtype dtype);
 
 // Host-side argument checks. Return AWQ_OK or an error (message via set_error).
+awq_status check_stats_finalize(const double* sums, int64_t count, int64_t K, const float* abar);
 awq_status check_stats(const void* X, awq_dtype d, int64_t T, int64_t K, const float* abar,
                        const void* ws, size_t ws_bytes);
 awq_status check_scale_table(const float* abar, int64_t K, const float* alphas, int32_t n,

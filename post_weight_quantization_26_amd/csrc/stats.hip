@@ -137,7 +137,59 @@ __global__ __launch_bounds__(256) void stats_finalize_kernel(const double* __res
   if (g == 0 && j < K) abar[j] = float((((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl]) / double(T));
 }
 
+// Calibration in batches: sums[j] += this batch's column sum, formed from the
+// chunk partials exactly as stats_finalize_kernel forms it.
+__global__ __launch_bounds__(256) void stats_accumulate_kernel(const double* __restrict__ partial,
+                                                               int64_t chunks, int64_t K,
+                                                               double* __restrict__ sums) {
+  __shared__ double red[4][64];
+  const int cl = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int64_t j = int64_t(blockIdx.x) * 64 + cl;
+  double s = 0.0;
+  if (j < K) {
+#pragma unroll 4
+    for (int64_t c = g; c < chunks; c += 4) s += partial[c * K + j];
+  }
+  red[g][cl] = s;
+  __syncthreads();
+  if (g == 0 && j < K) sums[j] += ((red[0][cl] + red[1][cl]) + red[2][cl]) + red[3][cl];
+}
+
+__global__ __launch_bounds__(256) void stats_divide_kernel(const double* __restrict__ sums,
+                                                           int64_t count, int64_t K,
+                                                           float* __restrict__ abar) {
+  const int64_t j = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (j < K) abar[j] = float(sums[j] / double(count));
+}
+
 }  // namespace
+
+hipError_t launch_stats_accumulate(const void* X, int dtype, int64_t T, int64_t K,
+                                   int64_t chunks, double* partial, double* sums,
+                                   hipStream_t st) {
+  const int vec = dtype == 0 ? 4 : 8;
+  const int64_t rows_per_chunk = (T + chunks - 1) / chunks;
+  dim3 grid(unsigned((K + int64_t(kColThreads) * vec - 1) / (int64_t(kColThreads) * vec)),
+            unsigned(chunks));
+  dim3 block(kColThreads * kRowLanes);
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  if (dtype == 0)
+    stats_partial_kernel<0><<<grid, block, 0, st>>>(x, T, K, rows_per_chunk, partial);
+  else if (dtype == 1)
+    stats_partial_kernel<1><<<grid, block, 0, st>>>(x, T, K, rows_per_chunk, partial);
+  else
+    stats_partial_kernel<2><<<grid, block, 0, st>>>(x, T, K, rows_per_chunk, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  stats_accumulate_kernel<<<unsigned((K + 63) / 64), 256, 0, st>>>(partial, chunks, K, sums);
+  return hipGetLastError();
+}
+
+hipError_t launch_stats_divide(const double* sums, int64_t count, int64_t K, float* abar,
+                               hipStream_t st) {
+  stats_divide_kernel<<<unsigned((K + 255) / 256), 256, 0, st>>>(sums, count, K, abar);
+  return hipGetLastError();
+}
 
 hipError_t launch_stats(const void* X, int dtype, int64_t T, int64_t K, int64_t chunks,
                         double* partial, float* abar, hipStream_t st) {

@@ -97,6 +97,16 @@ SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_gr
   return L;
 }
 
+awq_status check_stats_finalize(const double* sums, int64_t count, int64_t K, const float* abar) {
+  if (!sums || !abar) return set_error(AWQ_E_INVALID, "act_stats_finalize: NULL sums or abar");
+  if (count < 1 || K < 1 || K > kMaxDim)
+    return set_error(AWQ_E_INVALID, "act_stats_finalize: bad count=%lld or K=%lld",
+                     (long long)count, (long long)K);
+  if ((reinterpret_cast<uintptr_t>(sums) & 7u) || !aligned4(abar))
+    return set_error(AWQ_E_INVALID, "act_stats_finalize: sums must be 8-byte aligned, abar 4");
+  return AWQ_OK;
+}
+
 awq_status check_stats(const void* X, awq_dtype d, int64_t T, int64_t K, const float* abar,
                        const void* ws, size_t ws_bytes) {
   if (!X || !abar) return set_error(AWQ_E_INVALID, "act_stats: NULL X or abar");

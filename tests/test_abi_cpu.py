@@ -135,6 +135,25 @@ def test_stats_rejects(L):
     assert f(FAKE, 9, 16, 64, FAKE, FAKE, 1 << 30, None) == -1
 
 
+def test_stats_batches_rejects(L):
+    lib = L.lib()
+    acc, fin = lib.awq_act_stats_accumulate, lib.awq_act_stats_finalize
+    MIS8 = ctypes.c_void_p(0x10004)       # 4-byte but not 8-byte aligned
+    assert acc(FAKE, 1, 16, 64, None, FAKE, 1 << 30, None) == -1
+    assert acc(FAKE, 1, 16, 64, MIS8, FAKE, 1 << 30, None) == -1
+    assert "8-byte" in L.last_error()
+    assert acc(FAKE, 1, 0, 64, FAKE, FAKE, 1 << 30, None) == -1
+    assert acc(FAKE, 1, 16, 60, FAKE, FAKE, 1 << 30, None) == -1
+    assert acc(MIS, 1, 16, 64, FAKE, FAKE, 1 << 30, None) == -1
+    assert acc(FAKE, 1, 16, 64, FAKE, FAKE, 8, None) == -3
+    assert fin(None, 16, 64, FAKE, None) == -1
+    assert fin(FAKE, 0, 64, FAKE, None) == -1
+    assert fin(FAKE, 16, 0, FAKE, None) == -1
+    assert fin(MIS8, 16, 64, FAKE, None) == -1
+    assert fin(FAKE, 16, 64, MIS, None) == -1
+    assert "act_stats_finalize" in L.last_error()
+
+
 def test_scale_table_rejects(L):
     lib = L.lib()
     assert lib.awq_scale_table(FAKE, 16, L.float_array([0.5, 2.0]), 2, FAKE, None) == -1

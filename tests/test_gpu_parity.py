@@ -207,6 +207,36 @@ def test_act_stats_bitwise(api, dtype, T, K):
     assert np.array_equal(bits32(got), ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_act_stats_one_batch_equals_single_call(api, dtype):
+    """One batch through accumulate + finalize is the single call, bit for bit
+    (same partials, same fixed-order sum, added to zero, same division)."""
+    x = np.random.default_rng(11).standard_normal((3000, 1000)).astype(np.float32) * 4
+    X = {"bf16": synth.f32_to_bf16_bits(x), "f16": x.astype(np.float16).view(np.uint16),
+         "f32": x}[dtype]
+    Xd = to_dev(X, dtype)
+    sums = torch.zeros(1000, dtype=torch.float64, device="cuda:0")
+    api.act_stats_accumulate(Xd, sums)
+    got = api.act_stats_finalize(sums, 3000)
+    assert np.array_equal(bits32(got), bits32(api.act_stats(Xd)))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_act_stats_batches(api, dtype):
+    """Calibration batches of uneven length (one of a single token): the mean
+    over all their tokens, as the oracle computes it on the concatenation."""
+    K = 4096 if dtype == "bf16" else 1000
+    sizes = (300, 1, 5000, 77)
+    batches = [synth.make_activations(T, K, K // 100, 20.0, 100.0, dtype, seed=40 + i)
+               for i, T in enumerate(sizes)]
+    sums = torch.zeros(K, dtype=torch.float64, device="cuda:0")
+    for Xb in batches:
+        api.act_stats_accumulate(to_dev(Xb, dtype), sums)
+    got = api.act_stats_finalize(sums, sum(sizes))
+    ref = O.act_stats(np.concatenate(batches), dtype)
+    assert np.array_equal(bits32(got), ref.view(np.uint32))
+
+
 def test_scale_table_bitwise(api):
     X = synth.make_activations(2048, 4096, 41, 20.0, 100.0, "bf16", seed=3)
     ab = O.act_stats(X, "bf16")
