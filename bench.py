@@ -28,7 +28,8 @@ if ROOT not in sys.path:
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "search_gemm_traffic.json")
+TRAFFIC_FILES = {"direct": os.path.join(ROOT, "profiles", "search_gemm_traffic.json"),
+                 "gram": os.path.join(ROOT, "profiles", "gram_search_traffic.json")}
 
 
 def parse():
@@ -46,12 +47,14 @@ def parse():
     return p.parse_args()
 
 
-def gemm_traffic(cfg_name: str, launches_per_step: int):
-    """HBM bytes per search-GEMM launch from committed rocprofv3 counter runs,
-    or None when the kernel source changed since they were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def gemm_traffic(cfg_name: str, how: str = "direct"):
+    """HBM bytes per launch of the candidate GEMM (search GEMM, or the Gram
+    search) from committed rocprofv3 counter runs, or None when the kernel
+    source changed since they were taken or the workload differs."""
+    path = TRAFFIC_FILES[how]
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         rec = json.load(f)
     h = hashlib.sha256()
     for rel in rec.get("gemm_sources", []):
@@ -216,7 +219,7 @@ def main():
         launches_per_step = gemm_n // args.steps if args.steps else 0
         flops_per_launch = flops_per_step / max(launches_per_step, 1)
         achieved = flops_per_launch / gemm_avg_s / 1e12
-        traffic = gemm_traffic(name, launches_per_step) if how == "direct" else None
+        traffic = gemm_traffic(name, how)
         roof = {"bound": "mfma", "achieved": round(achieved, 2),
                 "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
