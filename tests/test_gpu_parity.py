@@ -112,13 +112,22 @@ def row_references(X, dtype, w_rows, cands, chunk=4096, want_S=False):
     return M64.reshape(n, -1), Mm.reshape(n, -1), tol.reshape(n, -1)
 
 
+def _ratio(num, den):
+    """max of num/den over den > 0 (0 when there is none)."""
+    pos = den > 0
+    return float((num[pos] / den[pos]).max()) if pos.any() else 0.0
+
+
 def compare_rows(gpu_rows, M64, Mm, tol, what):
     err = np.abs(gpu_rows - Mm)
-    worst = (err / tol).max()
+    # a row whose candidate error is exactly zero (an all-zero weight row
+    # quantises exactly) has a zero bound and must come out exactly zero
+    assert np.all(err[tol == 0] == 0), f"{what}: a zero-error row is not zero on the GPU"
+    worst = _ratio(err, tol)
     assert worst <= 1.0, f"{what}: GPU vs model exceeds the float32 bound ({worst:.2f}x)"
-    gap = (np.abs(Mm - M64) / M64).max()
+    gap = _ratio(np.abs(Mm - M64), M64)
     print(f"{what}: |gpu-model|/bound max {worst:.2e}; bf16 operand gap max {gap:.2e}; "
-          f"|gpu-oracle|/oracle max {(np.abs(gpu_rows - M64) / M64).max():.2e}")
+          f"|gpu-oracle|/oracle max {_ratio(np.abs(gpu_rows - M64), M64):.2e}")
 
 
 def check_scale_search(api, X, W, dtype, alphas, bits, zp, rows=None, ws=None, group=128):
@@ -146,13 +155,23 @@ def check_scale_search(api, X, W, dtype, alphas, bits, zp, rows=None, ws=None, g
         # the curve against the model, within the summed float32 bounds (any size)
         assert np.all(np.abs(res["mse"] - Mm.sum(axis=1) / (T * N)) <= tol.sum(axis=1) / (T * N))
         mrel = np.abs(res["mse"] - ref["mse"]) / ref["mse"]
+        m_curve = Mm.sum(axis=1) / (T * N)
+        gap = np.abs(m_curve - ref["mse"])
         if N >= 16:
-            # against the float64 oracle: 1e-3. A layer of a few rows has no
-            # averaging of the bf16 operand rounding across rows; there the
-            # deviation is the model's own gap, already bounded above.
-            assert mrel.max() <= MSE_REL, f"mse rel err {mrel.max():.3e}"
-            assert_alpha_rule(res["index"], ref["mse"])
-        print(f"curve: max rel err vs oracle {mrel.max():.2e}")
+            # against the float64 oracle: 1e-3, plus the model's own gap to it.
+            # The bf16 rounding of the candidate operands averages out over
+            # many rows of similar error; where a few rows dominate the sum
+            # (a layer of a few rows, or one row of much larger weights) it
+            # does not, and the deviation is that gap, bounded above.
+            assert np.all(np.abs(res["mse"] - ref["mse"]) <= MSE_REL * ref["mse"] + gap), \
+                f"mse rel err {mrel.max():.3e}"
+            # the GPU's argmin is the model's (up to float32 ties); it is also
+            # the oracle's whenever the model's gap is below the tie width
+            assert_alpha_rule(res["index"], m_curve)
+            if np.all(gap <= 1e-4 * ref["mse"]):
+                assert_alpha_rule(res["index"], ref["mse"])
+        print(f"curve: max rel err vs oracle {mrel.max():.2e} "
+              f"(model's own gap {(gap / ref['mse']).max():.2e})")
     return res, ref, Xd, Wd
 
 
@@ -271,6 +290,39 @@ def test_search_scale_degenerate_shapes(api):
     res, ref, _, _ = check_scale_search(api, X, W, "bf16", np.array([0.0], np.float32), 4, True)
     assert res["alpha_best"] == 0.0
     assert np.array_equal(bits32(res["s_best"]), np.ones(128, np.float32).view(np.uint32))
+
+
+def degenerate_layer(seed=26):
+    """A 300-token, 288 x 512 layer whose values hit the quantiser's and the
+    scale's floors: an all-zero weight row, a row whose second group is zero,
+    a constant group, a group with a single nonzero, groups far below the
+    1e-5 step floor, a large-magnitude row, and an all-zero activation
+    column (its ā is 0 and is floored at 1e-8 in the scale)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((300, 512)).astype(np.float32)
+    x[:, 7] = 0.0
+    x[:, 100] *= 40.0                                  # an outlier channel
+    w = (rng.standard_normal((288, 512)) * 0.02).astype(np.float32)
+    w[3] = 0.0
+    w[5, 128:256] = 0.0
+    w[8, 0:128] = 0.0125
+    w[9, 256:384] = 0.0
+    w[9, 300] = -0.7
+    w[11, :] = rng.standard_normal(512).astype(np.float32) * 1e-7
+    w[12, 384:] = 3e-6
+    w[13, :] *= 5000.0
+    return synth.f32_to_bf16_bits(x), synth.f32_to_bf16_bits(w)
+
+
+@pytest.mark.parametrize("bits,zp", [(4, True), (3, True), (4, False)])
+def test_degenerate_values_search_and_pack(api, bits, zp):
+    X, W = degenerate_layer()
+    res, ref, Xd, Wd = check_scale_search(api, X, W, "bf16", synth.alpha_grid(7), bits, zp)
+    s = ref["s_table"][res["index"]]
+    check_clip(api, Xd, Wd, X, W, "bf16", s, synth.ratio_grid(6), bits, zp)
+    qw, qz, sc = api.quantize_pack(Wd, torch.from_numpy(s).to("cuda:0"), bits=bits,
+                                   zero_point=zp)
+    assert_pack_parity(qw, qz, sc, W, "bf16", s, None, zp, bits=bits)
 
 
 def test_search_scale_many_token_tiles(api):
