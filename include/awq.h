@@ -71,7 +71,9 @@ typedef enum {
   AWQ_E_INVALID = -1,     /* bad argument: shape, NULL, alignment, grid value */
   AWQ_E_UNSUPPORTED = -2, /* valid but not implemented (dtype, bits, group) */
   AWQ_E_WORKSPACE = -3,   /* workspace smaller than the minimum */
-  AWQ_E_RANGE = -4,       /* an fp16 scale overflowed in awq_quantize_pack */
+  AWQ_E_RANGE = -4,       /* a result is out of range: an fp16 scale overflowed in
+                             awq_quantize_pack, or a search's output error is not
+                             finite (NaN or Inf in its inputs) */
   AWQ_E_HIP = -5          /* a HIP runtime call failed (message in awq_last_error) */
 } awq_status;
 
@@ -142,7 +144,8 @@ awq_status awq_scale_table(const float* abar, int64_t K, const float* alphas, in
  *          Σ_{t,n} (Y_a - Y)_{tn}² / (T·N) where Y_a uses the quantised,
  *          folded weights; row_sums [n_alpha, N] f64 (per output channel
  *          Σ_t, optional: may be NULL). Ties go to the lowest index.
- * Synchronises `stream`. */
+ * Synchronises `stream`. Returns AWQ_E_RANGE if a curve value is not finite
+ * (the curve is written; s_best and alpha_best are not). */
 awq_status awq_search_scale(const void* X, const void* W, awq_dtype dtype, int64_t T, int64_t N,
                             int64_t K, const float* abar, const float* alphas, int32_t n_alpha,
                             awq_qconfig qc, float* s_best, float* alpha_best, double* mse,
@@ -153,7 +156,7 @@ awq_status awq_search_scale(const void* X, const void* W, awq_dtype dtype, int64
  * Every group of row n uses ratio r_n. Outputs: ratio_best [N] f32 (argmin
  * per row, lowest index on ties); mse_clip [host] 1 f64 = Σ_n min_r M_n(r) / (T·N);
  * row_sums [n_ratio, N] f64 = M_n(r) (optional: may be NULL).
- * Synchronises `stream`. */
+ * Synchronises `stream`. Returns AWQ_E_RANGE if mse_clip is not finite. */
 awq_status awq_search_clip(const void* X, const void* W, awq_dtype dtype, int64_t T, int64_t N,
                            int64_t K, const float* s, const float* ratios, int32_t n_ratio,
                            awq_qconfig qc, float* ratio_best, double* mse_clip, double* row_sums,

@@ -1,5 +1,6 @@
 // The C ABI entry points: validate on the host, then enqueue the HIP kernels
 // on the caller's stream. See include/awq.h for the contract of each call.
+#include <cmath>
 #include <hip/hip_runtime_api.h>
 
 #include <cstring>
@@ -287,6 +288,13 @@ awq_status search_scale_impl(int op, const void* X, const Segment* seg, int n_se
   AWQ_HIP(hipMemcpyAsync(mse, mse_dev, sizeof(double) * size_t(n_alpha), hipMemcpyDeviceToHost, st),
           "copy mse");
   AWQ_HIP(hipStreamSynchronize(st), "synchronize");
+  // a NaN or Inf in X, W or abar (or a sum beyond the float range) makes the
+  // curve non-finite and the argmin meaningless: report it, curve written
+  for (int i = 0; i < n_alpha; ++i)
+    if (!std::isfinite(mse[i]))
+      return set_error(AWQ_E_RANGE,
+                       "search_scale: output error of alpha #%d is not finite (NaN or Inf in "
+                       "the inputs?)", i);
   int best = 0;
   for (int i = 1; i < n_alpha; ++i)
     if (mse[i] < mse[best]) best = i;
@@ -427,6 +435,9 @@ awq_status search_clip_impl(int op, const void* X, const void* W, awq_dtype dtyp
             "copy row_sums");
   AWQ_HIP(hipMemcpyAsync(mse_clip, mc, sizeof(double), hipMemcpyDeviceToHost, st), "copy mse_clip");
   AWQ_HIP(hipStreamSynchronize(st), "synchronize");
+  if (!std::isfinite(*mse_clip))
+    return set_error(AWQ_E_RANGE,
+                     "search_clip: output error is not finite (NaN or Inf in the inputs?)");
   return AWQ_OK;
 }
 

@@ -325,6 +325,33 @@ def test_degenerate_values_search_and_pack(api, bits, zp):
     assert_pack_parity(qw, qz, sc, W, "bf16", s, None, zp, bits=bits)
 
 
+def test_non_finite_inputs_are_reported(api):
+    """A NaN in X or an Inf in W makes the output error non-finite: the
+    searches report AWQ_E_RANGE instead of an argmin over NaN, and the pack
+    reports the non-finite fp16 scale the same way."""
+    from post_weight_quantization_26_amd._lib import AwqError
+    X, W = synth.make_custom(300, 264, 256, "bf16", seed=27)
+    Xn = X.copy()
+    Xn[5, 17] = 0x7FC0                                  # bf16 quiet NaN
+    Xd, Wd = to_dev(Xn, "bf16"), to_dev(W, "bf16")
+    abar = api.act_stats(Xd)
+    for method in ("direct", "gram"):
+        with pytest.raises(AwqError, match="not finite"):
+            api.search_scale(Xd, Wd, abar, synth.alpha_grid(3), method=method)
+    Wi = W.copy()
+    Wi[2, 3] = 0x7F80                                   # bf16 +Inf
+    Xd, Wd = to_dev(X, "bf16"), to_dev(Wi, "bf16")
+    s = torch.ones(256, dtype=torch.float32, device="cuda:0")
+    with pytest.raises(AwqError, match="not finite"):
+        api.search_clip(Xd, Wd, s, synth.ratio_grid(3))
+    with pytest.raises(AwqError, match="fp16"):
+        api.quantize_pack(Wd, s)
+    # the library stays usable afterwards
+    Wd = to_dev(W, "bf16")
+    res = api.search_scale(Xd, Wd, api.act_stats(Xd), synth.alpha_grid(3))
+    assert np.all(np.isfinite(res["mse"]))
+
+
 def test_search_scale_many_token_tiles(api):
     # 33 token tiles: exercises the XCD-grouped tile order with padding blocks
     X, W = synth.make_custom(33 * 256 - 5, 520, 256, "bf16", seed=24)
