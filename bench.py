@@ -155,6 +155,11 @@ def main():
         ws_need = max(ws_need, api.workspace_bytes(_lib.AWQ_OP_SEARCH_SCALE_GRAM, T, N, K, n_grid,
                                                    tdt))
     ws_search = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    if gram_ok:
+        # the Gram path builds G once per step and shares it among the searches
+        G_buf = torch.empty(api.gram_bytes(K), dtype=torch.uint8, device=dev)
+        ws_gram = torch.empty(api.workspace_bytes(_lib.AWQ_OP_GRAM_BUILD, T, 1, K, 1, tdt),
+                              dtype=torch.uint8, device=dev)
     ws_pack = torch.empty(256, dtype=torch.uint8, device=dev)
     abar = torch.empty(K, dtype=torch.float32, device=dev)
     G = cfg.group
@@ -167,20 +172,22 @@ def main():
 
     def step(how):
         api.act_stats(Xd, ws=ws_stats, out=abar)
+        Gm = api.gram_build(Xd, ws=ws_gram, out=G_buf) if how == "gram" else None
         if cfg.layers:
             # linears sharing X: one search, one s, folded into the norm weight
             # (in place, so gamma drifts over the steps; the work is the same)
             res = api.search_scale_group(Xd, Wds, abar, alphas, bits=cfg.bits, group=G,
-                                         zero_point=zp, ws=ws_search, method=how)
+                                         zero_point=zp, ws=ws_search, method=how, G=Gm)
             api.fold_norm(gamma, res["s_best"])
         else:
             res = api.search_scale(Xd, Wds[0], abar, alphas, bits=cfg.bits, group=G,
-                                   zero_point=zp, ws=ws_search, method=how)
+                                   zero_point=zp, ws=ws_search, method=how, G=Gm)
         for Wd, out in zip(Wds, pack_out):
             ratio = None
             if ratios is not None:
                 ratio = api.search_clip(Xd, Wd, res["s_best"], ratios, bits=cfg.bits, group=G,
-                                        zero_point=zp, ws=ws_search, method=how)["ratio_best"]
+                                        zero_point=zp, ws=ws_search, method=how,
+                                        G=Gm)["ratio_best"]
             if cfg.pack:
                 api.quantize_pack(Wd, res["s_best"], ratio, bits=cfg.bits, group=G, zero_point=zp,
                                   ws=ws_pack, out=out)
@@ -245,7 +252,8 @@ def main():
                  "note": "same candidates through G = X^T X: e.G.e^T per row from the "
                          "diagonal 256-tiles of G and twice the tiles above them, in bf16 "
                          "hi + lo halves (4*sum_tm rows_tm*(K-256*tm) flops, about 2.1*K^2 "
-                         "at K=4096), plus G's upper tiles once per search call"}
+                         "at K=4096), plus G's upper tiles once per step (gram_build), "
+                         "shared by the scale and clip searches"}
     stats_ms, stats_n = prof["stats"]
     stats_gbs = (T * K * X.itemsize) / (stats_ms / 1e3 / max(stats_n, 1)) / 1e9 if stats_n else None
     pack_ms, pack_n = prof["pack"]

@@ -89,7 +89,9 @@ typedef struct {
 } awq_qconfig;
 
 enum { AWQ_OP_STATS = 0, AWQ_OP_SEARCH_SCALE = 1, AWQ_OP_SEARCH_CLIP = 2, AWQ_OP_PACK = 3,
-       AWQ_OP_SEARCH_SCALE_GRAM = 4, AWQ_OP_SEARCH_CLIP_GRAM = 5 };
+       AWQ_OP_SEARCH_SCALE_GRAM = 4, AWQ_OP_SEARCH_CLIP_GRAM = 5,
+       /* awq_gram_build, and the Gram searches that take a prepared G */
+       AWQ_OP_GRAM_BUILD = 6, AWQ_OP_SEARCH_SCALE_GRAM_G = 7, AWQ_OP_SEARCH_CLIP_GRAM_G = 8 };
 
 /* Workspace bytes that let `op` process all `n_grid` candidates in one
  * batch (the fastest configuration). Returns 0 for invalid sizes. Pure host
@@ -184,9 +186,11 @@ awq_status awq_quantize_pack(const void* W, awq_dtype w_dtype, int64_t N, int64_
 /* The same two searches through the Gram matrix G = XᵀX of the activations:
  * M_n = Σ_t (X·E_nᵀ)_t² = E_n·G·E_nᵀ, an exact identity of the error measure
  * ("05 — AWQ", section 4; the identity itself is not on the pages). G is
- * built once per call (2·T·K² flops, stored as two bf16 halves hi + lo), then
- * each candidate row costs 2·(2K)·K instead of 2·T·K: T/(2K) times fewer
- * flops (8x at 64K tokens and K = 4096). The candidates' error weights are
+ * built once per call (its upper 256x256 tiles, T·K·(K + 256) flops, stored
+ * as two bf16 halves hi + lo), then each candidate row costs about
+ * 2·K·(K + 256) flops (G's diagonal tiles and twice its upper tiles, over hi
+ * and lo) instead of 2·T·K: ~15x fewer at 64K tokens and K = 4096. The
+ * candidates' error weights are
  * the same bf16 operands as on the direct path; only the float32 rounding
  * order of the sums differs. Arguments, outputs and synchronisation as in
  * awq_search_scale / awq_search_clip; bf16 inputs only; T <= 2^22. The
@@ -234,6 +238,40 @@ awq_status awq_search_scale_group_gram(const void* X, const void* const* W, cons
                                        awq_qconfig qc, float* s_best, float* alpha_best,
                                        double* mse, double* row_sums, void* ws, size_t ws_bytes,
                                        void* stream);
+
+/* One Gram matrix for every search of the layers that read the same X: the
+ * scale search, the clip searches that follow it, and group searches.
+ * awq_gram_build writes G of X [T, K] (bf16, K a multiple of 128, T <= 2^22)
+ * into G, a caller-owned device buffer of at least awq_gram_bytes(K) bytes
+ * (16-byte aligned), in the layout the Gram searches read (G's upper tiles as
+ * bf16 hi/lo halves; the rest of the buffer is not written). Workspace:
+ * awq_workspace_bytes(AWQ_OP_GRAM_BUILD, T, 1, K, 1, AWQ_BF16). Does not
+ * synchronise. awq_gram_bytes returns 0 for K not a multiple of 128.
+ * The _g searches take G in place of X and otherwise equal awq_search_scale_gram,
+ * awq_search_clip_gram and awq_search_scale_group_gram, bit for bit; T is
+ * the token count G was built from. Their workspaces
+ * (AWQ_OP_SEARCH_SCALE_GRAM_G, AWQ_OP_SEARCH_CLIP_GRAM_G; N = Σ_l N[l] for
+ * a group) hold no Xᵀ and no G. Errors as for the searches they replace;
+ * AWQ_E_WORKSPACE also when G_bytes < awq_gram_bytes(K). */
+size_t awq_gram_bytes(int64_t K);
+awq_status awq_gram_build(const void* X, awq_dtype dtype, int64_t T, int64_t K, void* G,
+                          size_t G_bytes, void* ws, size_t ws_bytes, void* stream);
+awq_status awq_search_scale_gram_g(const void* G, const void* W, awq_dtype dtype, int64_t T,
+                                   int64_t N, int64_t K, const float* abar, const float* alphas,
+                                   int32_t n_alpha, awq_qconfig qc, float* s_best,
+                                   float* alpha_best, double* mse, double* row_sums, void* ws,
+                                   size_t ws_bytes, void* stream);
+awq_status awq_search_clip_gram_g(const void* G, const void* W, awq_dtype dtype, int64_t T,
+                                  int64_t N, int64_t K, const float* s, const float* ratios,
+                                  int32_t n_ratio, awq_qconfig qc, float* ratio_best,
+                                  double* mse_clip, double* row_sums, void* ws, size_t ws_bytes,
+                                  void* stream);
+awq_status awq_search_scale_group_gram_g(const void* G, const void* const* W, const int64_t* N,
+                                         int32_t n_layers, awq_dtype dtype, int64_t T, int64_t K,
+                                         const float* abar, const float* alphas, int32_t n_alpha,
+                                         awq_qconfig qc, float* s_best, float* alpha_best,
+                                         double* mse, double* row_sums, void* ws,
+                                         size_t ws_bytes, void* stream);
 
 /* The fold into a preceding normalisation ("AWQ and Activation-Aware
  * Scaling", sections "Scaling instead of protecting" and "When it breaks").

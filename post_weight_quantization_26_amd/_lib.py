@@ -20,6 +20,7 @@ STATUS_NAMES = {0: "AWQ_OK", -1: "AWQ_E_INVALID", -2: "AWQ_E_UNSUPPORTED", -3: "
 AWQ_F32, AWQ_BF16, AWQ_F16 = 0, 1, 2
 AWQ_OP_STATS, AWQ_OP_SEARCH_SCALE, AWQ_OP_SEARCH_CLIP, AWQ_OP_PACK = 0, 1, 2, 3
 AWQ_OP_SEARCH_SCALE_GRAM, AWQ_OP_SEARCH_CLIP_GRAM = 4, 5
+AWQ_OP_GRAM_BUILD, AWQ_OP_SEARCH_SCALE_GRAM_G, AWQ_OP_SEARCH_CLIP_GRAM_G = 6, 7, 8
 KERNEL_KINDS = {"stats": 0, "scale": 1, "transform": 2, "gemm": 3, "reduce": 4, "pack": 5,
                 "fold": 6, "dequant": 7, "w4a16": 8, "w4a16_reduce": 9, "gram_build": 10,
                 "gram_search": 11}
@@ -40,6 +41,9 @@ SIGNATURES = {
     "awq_workspace_bytes": (c_sz, [ctypes.c_int, c_i64, c_i64, c_i64, c_i32, ctypes.c_int]),
     "awq_workspace_bytes_batch": (c_sz, [ctypes.c_int, c_i64, c_i64, c_i64, c_i32, c_i32,
                                          ctypes.c_int]),
+    "awq_gram_bytes": (c_sz, [c_i64]),
+    "awq_gram_build": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_vp, c_sz, c_vp, c_sz,
+                                      c_vp]),
     "awq_act_stats": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]),
     "awq_act_stats_accumulate": (ctypes.c_int,
                                  [c_vp, ctypes.c_int, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]),
@@ -54,7 +58,13 @@ SIGNATURES = {
     "awq_search_scale_gram": (ctypes.c_int, [c_vp, c_vp, ctypes.c_int, c_i64, c_i64, c_i64, c_vp,
                                              c_fp, c_i32, QConfig, c_vp, c_fp, c_dp, c_vp, c_vp,
                                              c_sz, c_vp]),
+    "awq_search_scale_gram_g": (ctypes.c_int, [c_vp, c_vp, ctypes.c_int, c_i64, c_i64, c_i64, c_vp,
+                                             c_fp, c_i32, QConfig, c_vp, c_fp, c_dp, c_vp, c_vp,
+                                             c_sz, c_vp]),
     "awq_search_clip_gram": (ctypes.c_int, [c_vp, c_vp, ctypes.c_int, c_i64, c_i64, c_i64, c_vp,
+                                            c_fp, c_i32, QConfig, c_vp, c_dp, c_vp, c_vp, c_sz,
+                                            c_vp]),
+    "awq_search_clip_gram_g": (ctypes.c_int, [c_vp, c_vp, ctypes.c_int, c_i64, c_i64, c_i64, c_vp,
                                             c_fp, c_i32, QConfig, c_vp, c_dp, c_vp, c_vp, c_sz,
                                             c_vp]),
     "awq_search_scale_group": (ctypes.c_int, [c_vp, ctypes.POINTER(c_vp), ctypes.POINTER(c_i64),
@@ -62,6 +72,10 @@ SIGNATURES = {
                                               c_i32, QConfig, c_vp, c_fp, c_dp, c_vp, c_vp,
                                               c_sz, c_vp]),
     "awq_search_scale_group_gram": (ctypes.c_int, [c_vp, ctypes.POINTER(c_vp),
+                                                   ctypes.POINTER(c_i64), c_i32, ctypes.c_int,
+                                                   c_i64, c_i64, c_vp, c_fp, c_i32, QConfig, c_vp,
+                                                   c_fp, c_dp, c_vp, c_vp, c_sz, c_vp]),
+    "awq_search_scale_group_gram_g": (ctypes.c_int, [c_vp, ctypes.POINTER(c_vp),
                                                    ctypes.POINTER(c_i64), c_i32, ctypes.c_int,
                                                    c_i64, c_i64, c_vp, c_fp, c_i32, QConfig, c_vp,
                                                    c_fp, c_dp, c_vp, c_vp, c_sz, c_vp]),

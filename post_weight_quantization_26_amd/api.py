@@ -113,36 +113,64 @@ def scale_table(abar: torch.Tensor, alphas: Sequence[float]) -> torch.Tensor:
 _METHODS = ("direct", "gram")
 
 
-def _method(method: str) -> bool:
+def _method(method: str, G: Optional[torch.Tensor] = None) -> bool:
     if method not in _METHODS:
         raise ValueError(f"method must be one of {_METHODS}")
+    if G is not None:
+        if method != "gram":
+            raise ValueError("a prepared Gram matrix G goes with method='gram'")
+        _dev(G, "G")
     return method == "gram"
+
+
+def gram_bytes(K: int) -> int:
+    return int(L.lib().awq_gram_bytes(K))
+
+
+def gram_build(X: torch.Tensor, ws: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """G = XᵀX of a bf16 layer input [T, K], in the layout the Gram searches
+    read (a uint8 device buffer of gram_bytes(K) bytes). Pass it as ``G=`` to
+    search_scale, search_clip and search_scale_group (method "gram") of every
+    layer that reads X, instead of building it in each search."""
+    _dev(X, "X")
+    T, K = X.shape
+    nbytes = gram_bytes(K)
+    G = out if out is not None else torch.empty(nbytes, dtype=torch.uint8, device=X.device)
+    ws = _workspace(ws, workspace_bytes(L.AWQ_OP_GRAM_BUILD, T, 1, K, 1, X.dtype), X.device)
+    L.check(L.lib().awq_gram_build(_ptr(X), _dtype(X), T, K, _ptr(G), G.numel() * G.element_size(),
+                                   _ptr(ws), ws.numel(), _stream()))
+    return G
 
 
 def search_scale(X: torch.Tensor, W: torch.Tensor, abar: torch.Tensor, alphas: Sequence[float],
                  bits: int = DEFAULT_BITS, group: int = DEFAULT_GROUP,
                  zero_point: bool = DEFAULT_ZERO_POINT, want_row_sums: bool = False,
-                 ws: Optional[torch.Tensor] = None, method: str = "direct") -> dict:
+                 ws: Optional[torch.Tensor] = None, method: str = "direct",
+                 G: Optional[torch.Tensor] = None) -> dict:
     """Grid search over alpha. Returns alpha_best, index, s_best [K], mse (numpy
     [n_alpha]) and, if asked, row_sums [n_alpha, N] float64 on the GPU.
     method "direct" measures X·Eᵀ per candidate; "gram" (bf16 only) uses the
-    activations' Gram matrix, E·G·Eᵀ per candidate row."""
-    gram = _method(method)
+    activations' Gram matrix, E·G·Eᵀ per candidate row, built in the call or
+    taken from ``G`` (gram_build(X))."""
+    gram = _method(method, G)
     _dev(X, "X"), _dev(W, "W"), _dev(abar, "abar")
     if X.dtype != W.dtype:
         raise ValueError("X and W must share a dtype")
     T, K = X.shape
     N = W.shape[0]
     n = len(alphas)
-    op = L.AWQ_OP_SEARCH_SCALE_GRAM if gram else L.AWQ_OP_SEARCH_SCALE
+    op = (L.AWQ_OP_SEARCH_SCALE_GRAM_G if G is not None else
+          L.AWQ_OP_SEARCH_SCALE_GRAM if gram else L.AWQ_OP_SEARCH_SCALE)
     ws = _workspace(ws, workspace_bytes(op, T, N, K, n, X.dtype), X.device)
     s_best = torch.empty(K, dtype=torch.float32, device=X.device)
     rows = torch.empty((n, N), dtype=torch.float64, device=X.device) if want_row_sums else None
     a_best = ctypes.c_float(0.0)
     mse = (ctypes.c_double * n)()
     grid = L.float_array(alphas)
-    fn = L.lib().awq_search_scale_gram if gram else L.lib().awq_search_scale
-    L.check(fn(_ptr(X), _ptr(W), _dtype(X), T, N, K, _ptr(abar), grid, n,
+    fn = (L.lib().awq_search_scale_gram_g if G is not None else
+          L.lib().awq_search_scale_gram if gram else L.lib().awq_search_scale)
+    L.check(fn(_ptr(G if G is not None else X), _ptr(W), _dtype(X), T, N, K, _ptr(abar), grid, n,
                qconfig(bits, group, zero_point), _ptr(s_best), ctypes.byref(a_best), mse,
                _ptr(rows), _ptr(ws), ws.numel(), _stream()))
     mse_np = np.array(mse[:], dtype=np.float64)
@@ -156,12 +184,12 @@ def search_scale_group(X: torch.Tensor, Ws: Sequence[torch.Tensor], abar: torch.
                        alphas: Sequence[float], bits: int = DEFAULT_BITS,
                        group: int = DEFAULT_GROUP, zero_point: bool = DEFAULT_ZERO_POINT,
                        want_row_sums: bool = False, ws: Optional[torch.Tensor] = None,
-                       method: str = "direct") -> dict:
+                       method: str = "direct", G: Optional[torch.Tensor] = None) -> dict:
     """One alpha search for linears that read the same X (one shared s): the
     error is averaged over all their outputs. Same result dict as
     ``search_scale``; row_sums [n_alpha, sum N] keeps the layers in order.
-    method "gram" (bf16) scores all layers through one G = XᵀX."""
-    gram = _method(method)
+    method "gram" (bf16) scores all layers through one G = XᵀX (or ``G``)."""
+    gram = _method(method, G)
     _dev(X, "X"), _dev(abar, "abar")
     if not 1 <= len(Ws) <= 16:
         raise ValueError("a group holds 1 to 16 layers")
@@ -173,7 +201,8 @@ def search_scale_group(X: torch.Tensor, Ws: Sequence[torch.Tensor], abar: torch.
     Ns = [int(W.shape[0]) for W in Ws]
     N = sum(Ns)
     n = len(alphas)
-    op = L.AWQ_OP_SEARCH_SCALE_GRAM if gram else L.AWQ_OP_SEARCH_SCALE
+    op = (L.AWQ_OP_SEARCH_SCALE_GRAM_G if G is not None else
+          L.AWQ_OP_SEARCH_SCALE_GRAM if gram else L.AWQ_OP_SEARCH_SCALE)
     ws = _workspace(ws, workspace_bytes(op, T, N, K, n, X.dtype), X.device)
     s_best = torch.empty(K, dtype=torch.float32, device=X.device)
     rows = torch.empty((n, N), dtype=torch.float64, device=X.device) if want_row_sums else None
@@ -181,8 +210,9 @@ def search_scale_group(X: torch.Tensor, Ws: Sequence[torch.Tensor], abar: torch.
     mse = (ctypes.c_double * n)()
     wptrs = (ctypes.c_void_p * len(Ws))(*[W.data_ptr() for W in Ws])
     nvals = (ctypes.c_int64 * len(Ws))(*Ns)
-    fn = L.lib().awq_search_scale_group_gram if gram else L.lib().awq_search_scale_group
-    L.check(fn(_ptr(X), wptrs, nvals, len(Ws), _dtype(X), T, K, _ptr(abar), L.float_array(alphas),
+    fn = (L.lib().awq_search_scale_group_gram_g if G is not None else
+          L.lib().awq_search_scale_group_gram if gram else L.lib().awq_search_scale_group)
+    L.check(fn(_ptr(G if G is not None else X), wptrs, nvals, len(Ws), _dtype(X), T, K, _ptr(abar), L.float_array(alphas),
                n, qconfig(bits, group, zero_point), _ptr(s_best), ctypes.byref(a_best), mse,
                _ptr(rows), _ptr(ws), ws.numel(), _stream()))
     mse_np = np.array(mse[:], dtype=np.float64)
@@ -224,24 +254,27 @@ def fold_linear(W_prev: torch.Tensor, s: torch.Tensor, bias: Optional[torch.Tens
 def search_clip(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor, ratios: Sequence[float],
                 bits: int = DEFAULT_BITS, group: int = DEFAULT_GROUP,
                 zero_point: bool = DEFAULT_ZERO_POINT, want_row_sums: bool = False,
-                ws: Optional[torch.Tensor] = None, method: str = "direct") -> dict:
+                ws: Optional[torch.Tensor] = None, method: str = "direct",
+                G: Optional[torch.Tensor] = None) -> dict:
     """Per-output-channel clip-ratio search with s fixed. Returns ratio_best [N]
-    (GPU), mse_clip (float) and optionally row_sums [n_ratio, N]. method as in
-    search_scale."""
-    gram = _method(method)
+    (GPU), mse_clip (float) and optionally row_sums [n_ratio, N]. method and G
+    as in search_scale."""
+    gram = _method(method, G)
     _dev(X, "X"), _dev(W, "W"), _dev(s, "s")
     if X.dtype != W.dtype:
         raise ValueError("X and W must share a dtype")
     T, K = X.shape
     N = W.shape[0]
     n = len(ratios)
-    op = L.AWQ_OP_SEARCH_CLIP_GRAM if gram else L.AWQ_OP_SEARCH_CLIP
+    op = (L.AWQ_OP_SEARCH_CLIP_GRAM_G if G is not None else
+          L.AWQ_OP_SEARCH_CLIP_GRAM if gram else L.AWQ_OP_SEARCH_CLIP)
     ws = _workspace(ws, workspace_bytes(op, T, N, K, n, X.dtype), X.device)
     r_best = torch.empty(N, dtype=torch.float32, device=X.device)
     rows = torch.empty((n, N), dtype=torch.float64, device=X.device) if want_row_sums else None
     mse_clip = ctypes.c_double(0.0)
-    fn = L.lib().awq_search_clip_gram if gram else L.lib().awq_search_clip
-    L.check(fn(_ptr(X), _ptr(W), _dtype(X), T, N, K, _ptr(s), L.float_array(ratios), n,
+    fn = (L.lib().awq_search_clip_gram_g if G is not None else
+          L.lib().awq_search_clip_gram if gram else L.lib().awq_search_clip)
+    L.check(fn(_ptr(G if G is not None else X), _ptr(W), _dtype(X), T, N, K, _ptr(s), L.float_array(ratios), n,
                qconfig(bits, group, zero_point), _ptr(r_best), ctypes.byref(mse_clip), _ptr(rows),
                _ptr(ws), ws.numel(), _stream()))
     return dict(ratio_best=r_best, mse_clip=float(mse_clip.value), row_sums=rows)

@@ -236,9 +236,27 @@ extern "C" awq_status awq_scale_table(const float* abar, int64_t K, const float*
   return AWQ_OK;
 }
 
+extern "C" awq_status awq_gram_build(const void* X, awq_dtype dtype, int64_t T, int64_t K,
+                                     void* G, size_t G_bytes, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  awq_status s = check_gram_build(X, dtype, T, K, G, G_bytes, ws, ws_bytes);
+  if (s != AWQ_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const GramBuildLayout B = gram_build_layout(T, K);
+  uint16_t* Xt = at<uint16_t>(ws, B.xt);
+  float* P = at<float>(ws, B.gp);
+  AWQ_HIP(timed(AWQ_K_GRAM_BUILD, st,
+                [&] {
+                  return launch_gram_build(X, T, K, B.Tp, B.ldx, B.S, Xt, P, B.ldg,
+                                           static_cast<uint16_t*>(G), st);
+                }),
+          "gram_build");
+  return AWQ_OK;
+}
+
 namespace {
 
-// Builds [G_hi | G_lo] of G = XᵀX into the workspace of a Gram search.
+// Builds G = XᵀX (upper tiles, hi/lo) into the workspace of a Gram search.
 awq_status build_gram(const void* X, int64_t T, int64_t K, const SearchLayout& L, void* ws,
                       hipStream_t st) {
   uint16_t* Xt = at<uint16_t>(ws, L.xt);
@@ -260,10 +278,12 @@ awq_status search_scale_impl(int op, const void* X, const Segment* seg, int n_se
                              int32_t nb, hipStream_t st) {
   const SearchLayout L = search_layout(op, T, N, K, n_alpha, nb, dtype);
   const uint16_t* Gs = nullptr;
-  if (is_gram_op(op)) {
+  if (builds_gram(op)) {
     awq_status g = build_gram(X, T, K, L, ws, st);
     if (g != AWQ_OK) return g;
     Gs = at<uint16_t>(ws, L.gs);
+  } else if (is_gram_op(op)) {
+    Gs = static_cast<const uint16_t*>(X);   // a prepared G passed in place of X
   }
   float* s_table = at<float>(ws, L.s_table);
   float* inv_table = at<float>(ws, L.inv);
@@ -396,6 +416,35 @@ extern "C" awq_status awq_search_scale_group_gram(const void* X, const void* con
                                ws_bytes, stream);
 }
 
+extern "C" awq_status awq_search_scale_gram_g(const void* G, const void* W, awq_dtype dtype,
+                                              int64_t T, int64_t N, int64_t K, const float* abar,
+                                              const float* alphas, int32_t n_alpha,
+                                              awq_qconfig qc, float* s_best, float* alpha_best,
+                                              double* mse, double* row_sums, void* ws,
+                                              size_t ws_bytes, void* stream) {
+  int32_t nb = 0;
+  awq_status s = check_search(AWQ_OP_SEARCH_SCALE_GRAM_G, G, W, dtype, T, N, K, abar, alphas,
+                              n_alpha, qc, s_best, alpha_best, mse, ws, ws_bytes, &nb);
+  if (s != AWQ_OK) return s;
+  const Segment seg{W, N, 0};
+  return search_scale_impl(AWQ_OP_SEARCH_SCALE_GRAM_G, G, &seg, 1, dtype, T, N, K, abar, alphas,
+                           n_alpha, qc, s_best, alpha_best, mse, row_sums, ws, nb,
+                           static_cast<hipStream_t>(stream));
+}
+
+extern "C" awq_status awq_search_scale_group_gram_g(const void* G, const void* const* W,
+                                                    const int64_t* N, int32_t n_layers,
+                                                    awq_dtype dtype, int64_t T, int64_t K,
+                                                    const float* abar, const float* alphas,
+                                                    int32_t n_alpha, awq_qconfig qc,
+                                                    float* s_best, float* alpha_best, double* mse,
+                                                    double* row_sums, void* ws, size_t ws_bytes,
+                                                    void* stream) {
+  return search_scale_group_op(AWQ_OP_SEARCH_SCALE_GRAM_G, G, W, N, n_layers, dtype, T, K, abar,
+                               alphas, n_alpha, qc, s_best, alpha_best, mse, row_sums, ws,
+                               ws_bytes, stream);
+}
+
 namespace {
 
 awq_status search_clip_impl(int op, const void* X, const void* W, awq_dtype dtype, int64_t T,
@@ -410,10 +459,12 @@ awq_status search_clip_impl(int op, const void* X, const void* W, awq_dtype dtyp
   float* s_copy = at<float>(ws, L.s_table);
   const Segment seg{W, N, 0};
   const uint16_t* Gs = nullptr;
-  if (is_gram_op(op)) {
+  if (builds_gram(op)) {
     awq_status g = build_gram(X, T, K, L, ws, st);
     if (g != AWQ_OK) return g;
     Gs = at<uint16_t>(ws, L.gs);
+  } else if (is_gram_op(op)) {
+    Gs = static_cast<const uint16_t*>(X);   // a prepared G passed in place of X
   }
   AWQ_HIP(timed(AWQ_K_SCALE, st, [&] { return launch_reciprocal(s, K, s_copy, inv, st); }),
           "reciprocal");
@@ -468,6 +519,21 @@ extern "C" awq_status awq_search_clip_gram(const void* X, const void* W, awq_dty
   if (st_ != AWQ_OK) return st_;
   return search_clip_impl(AWQ_OP_SEARCH_CLIP_GRAM, X, W, dtype, T, N, K, s, ratios, n_ratio, qc,
                           ratio_best, mse_clip, row_sums, ws, nb,
+                          static_cast<hipStream_t>(stream));
+}
+
+extern "C" awq_status awq_search_clip_gram_g(const void* G, const void* W, awq_dtype dtype,
+                                             int64_t T, int64_t N, int64_t K, const float* s,
+                                             const float* ratios, int32_t n_ratio,
+                                             awq_qconfig qc, float* ratio_best, double* mse_clip,
+                                             double* row_sums, void* ws, size_t ws_bytes,
+                                             void* stream) {
+  int32_t nb = 0;
+  awq_status st_ = check_search(AWQ_OP_SEARCH_CLIP_GRAM_G, G, W, dtype, T, N, K, s, ratios,
+                                n_ratio, qc, ratio_best, mse_clip, nullptr, ws, ws_bytes, &nb);
+  if (st_ != AWQ_OK) return st_;
+  return search_clip_impl(AWQ_OP_SEARCH_CLIP_GRAM_G, G, W, dtype, T, N, K, s, ratios, n_ratio,
+                          qc, ratio_best, mse_clip, row_sums, ws, nb,
                           static_cast<hipStream_t>(stream));
 }
 

@@ -62,8 +62,29 @@ constexpr int64_t kXtPad = 64, kGsPad = 256;
 // rounds of 256 CUs relative to the slice length (ties to the smaller S).
 int32_t gram_slices(int64_t T, int64_t K);
 
-inline bool is_gram_op(int op) { return op == AWQ_OP_SEARCH_SCALE_GRAM || op == AWQ_OP_SEARCH_CLIP_GRAM; }
-inline bool is_scale_op(int op) { return op == AWQ_OP_SEARCH_SCALE || op == AWQ_OP_SEARCH_SCALE_GRAM; }
+// Gram searches: those that build G in their own workspace, and those that
+// read a prepared G.
+inline bool builds_gram(int op) {
+  return op == AWQ_OP_SEARCH_SCALE_GRAM || op == AWQ_OP_SEARCH_CLIP_GRAM;
+}
+inline bool is_gram_op(int op) {
+  return builds_gram(op) || op == AWQ_OP_SEARCH_SCALE_GRAM_G || op == AWQ_OP_SEARCH_CLIP_GRAM_G;
+}
+inline bool is_scale_op(int op) {
+  return op == AWQ_OP_SEARCH_SCALE || op == AWQ_OP_SEARCH_SCALE_GRAM ||
+         op == AWQ_OP_SEARCH_SCALE_GRAM_G;
+}
+// Xt and the partial tiles of a G build (the first part of a building Gram
+// search's workspace, and the whole workspace of awq_gram_build).
+struct GramBuildLayout {
+  int64_t Tp, ldx, ldg;
+  int32_t S;
+  size_t xt, gp, total;
+};
+GramBuildLayout gram_build_layout(int64_t T, int64_t K);
+size_t gram_g_bytes(int64_t K);
+awq_status check_gram_build(const void* X, awq_dtype d, int64_t T, int64_t K, const void* G,
+                            size_t G_bytes, const void* ws, size_t ws_bytes);
 SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_grid, int32_t nb,
                            awq_dtype dtype);
 

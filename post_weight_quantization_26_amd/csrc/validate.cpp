@@ -56,15 +56,31 @@ int32_t gram_slices(int64_t T, int64_t K) {
   return best;
 }
 
+GramBuildLayout gram_build_layout(int64_t T, int64_t K) {
+  GramBuildLayout B{};
+  B.Tp = ceil_div(T, kTileK) * kTileK;
+  B.S = gram_slices(T, K);
+  B.ldx = B.Tp + kXtPad;
+  B.ldg = 2 * K + kGsPad;
+  const size_t nt = size_t(ceil_div(K, kGemmBM_bf16));
+  B.xt = 0;
+  B.gp = align_up(size_t(K) * size_t(B.ldx) * 2);
+  B.total = B.gp + align_up(size_t(B.S) * (nt * (nt + 1) / 2) * 256 * 256 * 4);
+  return B;
+}
+
+size_t gram_g_bytes(int64_t K) { return align_up(size_t(K) * size_t(2 * K + kGsPad) * 2); }
+
 SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_grid, int32_t nb,
                            awq_dtype dtype) {
   SearchLayout L{};
   const int64_t bm = dtype == AWQ_F32 ? kGemmBM_f32 : kGemmBM_bf16;
-  const bool gram = is_gram_op(op);
+  const bool gram = is_gram_op(op), build = builds_gram(op);
+  const GramBuildLayout B = build ? gram_build_layout(T, K) : GramBuildLayout{};
   L.MT = gram ? ceil_div(K, kGemmBM_bf16) : ceil_div(T, bm);
-  L.Tp = gram ? ceil_div(T, kTileK) * kTileK : 0;
-  L.S = gram ? gram_slices(T, K) : 0;
-  L.ldx = gram ? L.Tp + kXtPad : 0;
+  L.Tp = B.Tp;
+  L.S = B.S;
+  L.ldx = B.ldx;
   L.ldg = gram ? 2 * K + kGsPad : 0;
   const size_t n_tab = is_scale_op(op) ? size_t(n_grid) : 1;
   size_t off = 0;
@@ -84,17 +100,35 @@ SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_gr
   off += align_up(size_t(N) * 8);
   L.scalar = off;
   off += align_up(64);
-  L.xt = off;
-  if (gram) off += align_up(size_t(K) * size_t(L.ldx) * 2);
-  L.gp = off;
-  if (gram) {
-    const size_t nt = size_t(ceil_div(K, kGemmBM_bf16));
-    off += align_up(size_t(L.S) * (nt * (nt + 1) / 2) * 256 * 256 * 4);
-  }
+  // a building Gram search also holds Xt, the partial tiles and G
+  L.xt = off + B.xt;
+  L.gp = off + B.gp;
+  off += B.total;
   L.gs = off;
-  if (gram) off += align_up(size_t(K) * size_t(L.ldg) * 2);
+  if (build) off += gram_g_bytes(K);
   L.total = off;
   return L;
+}
+
+awq_status check_gram_build(const void* X, awq_dtype d, int64_t T, int64_t K, const void* G,
+                            size_t G_bytes, const void* ws, size_t ws_bytes) {
+  if (!X || !G) return set_error(AWQ_E_INVALID, "gram_build: NULL X or G");
+  if (!dtype_ok(d)) return set_error(AWQ_E_INVALID, "gram_build: unknown dtype %d", int(d));
+  if (d != AWQ_BF16) return set_error(AWQ_E_UNSUPPORTED, "gram_build: bf16 inputs only");
+  if (T < 1 || K < 1 || T > (int64_t(1) << 22) || K > kMaxDim)
+    return set_error(AWQ_E_INVALID, "gram_build: bad shape T=%lld K=%lld (T <= 2^22)",
+                     (long long)T, (long long)K);
+  if (K % kTileK)
+    return set_error(AWQ_E_INVALID, "gram_build: K=%lld is not a multiple of 128", (long long)K);
+  if (!aligned16(X) || !aligned16(G))
+    return set_error(AWQ_E_INVALID, "gram_build: X and G must be 16-byte aligned");
+  if (G_bytes < gram_g_bytes(K))
+    return set_error(AWQ_E_WORKSPACE, "gram_build: G needs %zu bytes", gram_g_bytes(K));
+  const size_t need = gram_build_layout(T, K).total;
+  if (!ws || !aligned16(ws) || ws_bytes < need)
+    return set_error(AWQ_E_WORKSPACE, "gram_build: workspace needs %zu bytes (16-byte aligned)",
+                     need);
+  return AWQ_OK;
 }
 
 awq_status check_stats_finalize(const double* sums, int64_t count, int64_t K, const float* abar) {
@@ -153,10 +187,13 @@ awq_status check_search(int op, const void* X, const void* W, awq_dtype d, int64
                         int64_t K, const float* vec, const float* grid, int32_t n_grid,
                         awq_qconfig qc, const void* out_dev, const void* out_host,
                         const void* out_host2, const void* ws, size_t ws_bytes, int32_t* nb) {
-  const char* nm = op == AWQ_OP_SEARCH_SCALE        ? "search_scale"
-                   : op == AWQ_OP_SEARCH_CLIP       ? "search_clip"
-                   : op == AWQ_OP_SEARCH_SCALE_GRAM ? "search_scale_gram"
-                                                    : "search_clip_gram";
+  const char* nm = op == AWQ_OP_SEARCH_SCALE          ? "search_scale"
+                   : op == AWQ_OP_SEARCH_CLIP         ? "search_clip"
+                   : op == AWQ_OP_SEARCH_SCALE_GRAM   ? "search_scale_gram"
+                   : op == AWQ_OP_SEARCH_CLIP_GRAM    ? "search_clip_gram"
+                   : op == AWQ_OP_SEARCH_SCALE_GRAM_G ? "search_scale_gram_g"
+                                                      : "search_clip_gram_g";
+  // X is the prepared G for the _g searches
   if (!X || !W || !vec || !grid || !out_dev || !out_host || (is_scale_op(op) && !out_host2))
     return set_error(AWQ_E_INVALID, "%s: NULL pointer argument", nm);
   if (!dtype_ok(d)) return set_error(AWQ_E_INVALID, "%s: unknown dtype %d", nm, int(d));
@@ -344,8 +381,13 @@ extern "C" size_t awq_workspace_bytes(int op, int64_t T, int64_t N, int64_t K, i
       return search_layout(op, T, N, K, n_grid, n_grid, dtype).total;
     case AWQ_OP_SEARCH_SCALE_GRAM:
     case AWQ_OP_SEARCH_CLIP_GRAM:
+    case AWQ_OP_SEARCH_SCALE_GRAM_G:
+    case AWQ_OP_SEARCH_CLIP_GRAM_G:
       if (dtype != AWQ_BF16 || K % kTileK) return 0;
       return search_layout(op, T, N, K, n_grid, n_grid, dtype).total;
+    case AWQ_OP_GRAM_BUILD:
+      if (dtype != AWQ_BF16 || K % kTileK || T > (int64_t(1) << 22)) return 0;
+      return gram_build_layout(T, K).total;
     case AWQ_OP_PACK:
       return kAlign;
     default:
@@ -360,6 +402,12 @@ extern "C" size_t awq_workspace_bytes_batch(int op, int64_t T, int64_t N, int64_
   if (batch < 1 || batch > n_grid) return 0;
   if (awq_workspace_bytes(op, T, N, K, n_grid, dtype) == 0) return 0;
   return search_layout(op, T, N, K, n_grid, batch, dtype).total;
+}
+
+extern "C" size_t awq_gram_bytes(int64_t K) {
+  using namespace awq;
+  if (K < 1 || K > kMaxDim || K % kTileK) return 0;
+  return gram_g_bytes(K);
 }
 
 extern "C" const char* awq_last_error(void) { return awq::g_err; }

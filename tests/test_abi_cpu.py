@@ -301,6 +301,58 @@ def test_w4a16_workspace_and_rejects(L):
     assert "w4a16_matmul" in L.last_error()
 
 
+def test_prepared_gram_sizes_and_rejects(L):
+    lib = L.lib()
+    ws = lib.awq_workspace_bytes
+    T, K = 65536, 4096
+    gbytes = lib.awq_gram_bytes(K)
+    assert gbytes == K * (2 * K + 256) * 2            # upper tiles' hi/lo rows, padded
+    assert lib.awq_gram_bytes(200) == 0 and lib.awq_gram_bytes(0) == 0
+    build = ws(L.AWQ_OP_GRAM_BUILD, T, 1, K, 1, L.AWQ_BF16)
+    xt = K * (T + 64) * 2
+    gp = 16 * 136 * 256 * 256 * 4
+    assert build == xt + gp
+    assert ws(L.AWQ_OP_GRAM_BUILD, T, 1, K, 1, L.AWQ_F32) == 0
+    for with_g, op in ((L.AWQ_OP_SEARCH_SCALE_GRAM_G, L.AWQ_OP_SEARCH_SCALE_GRAM),
+                       (L.AWQ_OP_SEARCH_CLIP_GRAM_G, L.AWQ_OP_SEARCH_CLIP_GRAM)):
+        # a prepared G: no X^T, partial tiles or G in the search's workspace
+        assert ws(with_g, T, 4096, K, 20, L.AWQ_BF16) == \
+            ws(op, T, 4096, K, 20, L.AWQ_BF16) - build - gbytes
+        assert lib.awq_workspace_bytes_batch(with_g, T, 4096, K, 20, 1, L.AWQ_BF16) > 0
+    f = lib.awq_gram_build
+    big = 1 << 40
+    assert f(FAKE, L.AWQ_BF16, T, K, None, big, FAKE, big, None) == -1
+    assert f(FAKE, L.AWQ_F32, T, K, FAKE, big, FAKE, big, None) == -2
+    assert f(FAKE, L.AWQ_BF16, T, 200, FAKE, big, FAKE, big, None) == -1
+    assert f(FAKE, L.AWQ_BF16, (1 << 22) + 1, K, FAKE, big, FAKE, big, None) == -1
+    assert f(MIS, L.AWQ_BF16, T, K, FAKE, big, FAKE, big, None) == -1
+    assert f(FAKE, L.AWQ_BF16, T, K, FAKE, gbytes - 1, FAKE, big, None) == -3
+    assert f(FAKE, L.AWQ_BF16, T, K, FAKE, gbytes, FAKE, build - 1, None) == -3
+    assert "gram_build" in L.last_error()
+    a_best = ctypes.c_float()
+    mse = (ctypes.c_double * 3)()
+    g = L.float_array([0.0, 0.5, 1.0])
+    qc = L.QConfig(4, 128, 1)
+    sg = lib.awq_search_scale_gram_g
+    assert sg(None, FAKE, L.AWQ_BF16, 256, 256, 256, FAKE, g, 3, qc, FAKE, ctypes.byref(a_best),
+              mse, None, FAKE, big, None) == -1
+    assert sg(FAKE, FAKE, L.AWQ_F32, 256, 256, 256, FAKE, g, 3, qc, FAKE, ctypes.byref(a_best),
+              mse, None, FAKE, big, None) == -2
+    assert "search_scale_gram_g" in L.last_error()
+    mc = ctypes.c_double()
+    cg = lib.awq_search_clip_gram_g
+    r = L.float_array([0.5, 1.0])
+    assert cg(FAKE, FAKE, L.AWQ_BF16, 256, 256, 200, FAKE, r, 2, qc, FAKE, ctypes.byref(mc), None,
+              FAKE, big, None) == -1
+    assert cg(FAKE, FAKE, L.AWQ_BF16, 256, 256, 256, FAKE, r, 2, qc, FAKE, ctypes.byref(mc), None,
+              FAKE, 16, None) == -3
+    gg = lib.awq_search_scale_group_gram_g
+    wp = (ctypes.c_void_p * 2)(FAKE.value, FAKE.value)
+    nv = (ctypes.c_int64 * 2)(256, 128)
+    assert gg(FAKE, wp, nv, 2, L.AWQ_F16, 256, 256, FAKE, g, 3, qc, FAKE, ctypes.byref(a_best),
+              mse, None, FAKE, big, None) == -2
+
+
 def test_gram_workspace_and_rejects(L):
     lib = L.lib()
     ws = lib.awq_workspace_bytes

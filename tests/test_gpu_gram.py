@@ -150,3 +150,52 @@ def test_gram_bench_layer_full(api):
     assert (np.abs(res["mse"] - dref["mse"]) / dref["mse"]).max() <= 1e-4
     del Xd, Wd
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T,N,K", [(700, 300, 384), (2048, 512, 1024)])
+def test_prepared_g_equals_built_in(api, T, N, K):
+    """One G from gram_build serves the scale, clip and group searches; each
+    equals, bit for bit, the search that builds G in its own workspace."""
+    X, W = synth.make_custom(T, N, K, "bf16", seed=150 + K)
+    W2 = synth.make_weight(136, K, 0.02, "bf16", seed=151 + K)
+    Xd, Wd, W2d = to_dev(X, "bf16"), to_dev(W, "bf16"), to_dev(W2, "bf16")
+    abar = api.act_stats(Xd)
+    alphas = synth.alpha_grid(5)
+    G = api.gram_build(Xd)
+    assert G.numel() == api.gram_bytes(K)
+    a = api.search_scale(Xd, Wd, abar, alphas, want_row_sums=True, method="gram")
+    b = api.search_scale(Xd, Wd, abar, alphas, want_row_sums=True, method="gram", G=G)
+    assert np.array_equal(a["mse"], b["mse"]) and a["index"] == b["index"]
+    assert torch.equal(a["row_sums"], b["row_sums"]) and torch.equal(a["s_best"], b["s_best"])
+    ratios = synth.ratio_grid(6)
+    c = api.search_clip(Xd, Wd, a["s_best"], ratios, want_row_sums=True, method="gram")
+    d = api.search_clip(Xd, Wd, a["s_best"], ratios, want_row_sums=True, method="gram", G=G)
+    assert c["mse_clip"] == d["mse_clip"]
+    assert torch.equal(c["ratio_best"], d["ratio_best"]) and torch.equal(c["row_sums"], d["row_sums"])
+    e = api.search_scale_group(Xd, [Wd, W2d], abar, alphas, want_row_sums=True, method="gram")
+    f = api.search_scale_group(Xd, [Wd, W2d], abar, alphas, want_row_sums=True, method="gram",
+                               G=G)
+    assert np.array_equal(e["mse"], f["mse"]) and torch.equal(e["row_sums"], f["row_sums"])
+    # G is only read: a second use gives the same again
+    g = api.search_scale(Xd, Wd, abar, alphas, method="gram", G=G)
+    assert np.array_equal(g["mse"], b["mse"])
+
+
+def test_prepared_g_bench_layer(api):
+    """The 4096x4096, 65,536-token layer: scale and clip searches through one
+    prepared G equal the building searches bit for bit."""
+    cfg = synth.CONFIGS["llama7b_attn_4096"]
+    X, W = synth.make_layer(cfg)
+    Xd, Wd = to_dev(X, "bf16"), to_dev(W, "bf16")
+    abar = api.act_stats(Xd)
+    alphas = synth.alpha_grid(cfg.n_alpha)
+    G = api.gram_build(Xd)
+    a = api.search_scale(Xd, Wd, abar, alphas, method="gram")
+    b = api.search_scale(Xd, Wd, abar, alphas, method="gram", G=G)
+    assert np.array_equal(a["mse"], b["mse"]) and torch.equal(a["s_best"], b["s_best"])
+    ratios = synth.ratio_grid(10)
+    c = api.search_clip(Xd, Wd, a["s_best"], ratios, method="gram")
+    d = api.search_clip(Xd, Wd, a["s_best"], ratios, method="gram", G=G)
+    assert c["mse_clip"] == d["mse_clip"] and torch.equal(c["ratio_best"], d["ratio_best"])
+    del Xd, Wd, G
+    torch.cuda.empty_cache()
