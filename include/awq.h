@@ -239,6 +239,18 @@ awq_status awq_search_scale_group_gram(const void* X, const void* const* W, cons
                                        double* mse, double* row_sums, void* ws, size_t ws_bytes,
                                        void* stream);
 
+/* The consumer of the 3-bit layout (awq_quantize_pack with w_bit = 3): as
+ * awq_w4a16_matmul, with qweight [K, N·3/32] and qzeros [K/g, N·3/32] packed
+ * densely (N a multiple of 32). Ŵ = (q - z)·scale is formed in float32 and
+ * rounded once to the activation type into the workspace (N·K 16-bit values,
+ * awq_w3a16_workspace_bytes), then the MFMA GEMM computes Y for any T.
+ * Errors and synchronisation as for awq_w4a16_matmul. */
+size_t awq_w3a16_workspace_bytes(int64_t T, int64_t N, int64_t K, awq_dtype dtype);
+awq_status awq_w3a16_matmul(const void* X, awq_dtype dtype, int64_t T, int64_t N, int64_t K,
+                            const int32_t* qweight, const int32_t* qzeros,
+                            const uint16_t* scales, int32_t group_size, void* Y, void* ws,
+                            size_t ws_bytes, void* stream);
+
 /* One Gram matrix for every search of the layers that read the same X: the
  * scale search, the clip searches that follow it, and group searches.
  * awq_gram_build writes G of X [T, K] (bf16, K a multiple of 128, T <= 2^22)

@@ -82,7 +82,10 @@ SIGNATURES = {
     "awq_fold_norm": (ctypes.c_int, [c_vp, c_vp, ctypes.c_int, c_i64, c_vp, c_vp]),
     "awq_fold_linear": (ctypes.c_int, [c_vp, c_vp, ctypes.c_int, c_i64, c_i64, c_vp, c_vp]),
     "awq_w4a16_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
+    "awq_w3a16_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, ctypes.c_int]),
     "awq_w4a16_matmul": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp,
+                                        c_i32, c_vp, c_vp, c_sz, c_vp]),
+    "awq_w3a16_matmul": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp,
                                         c_i32, c_vp, c_vp, c_sz, c_vp]),
     "awq_last_error": (ctypes.c_char_p, []),
     "awq_profile_enable": (None, [ctypes.c_int]),

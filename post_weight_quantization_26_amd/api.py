@@ -309,23 +309,35 @@ def w4a16_workspace_bytes(T: int, N: int, K: int, dtype: torch.dtype) -> int:
     return int(L.lib().awq_w4a16_workspace_bytes(T, N, K, _DT[dtype]))
 
 
+def w3a16_workspace_bytes(T: int, N: int, K: int, dtype) -> int:
+    return int(L.lib().awq_w3a16_workspace_bytes(T, N, K, _DT[dtype]))
+
+
 def w4a16_matmul(X: torch.Tensor, qweight: torch.Tensor, qzeros: torch.Tensor,
                  scales: torch.Tensor, group: int = DEFAULT_GROUP,
-                 ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
-    """Y = X·Ŵᵀ for a 4-bit packed layer (qweight [K, N/8], qzeros [K/g, N/8],
-    scales [K/g, N] float16) and activations X [T, K] (bf16 or float16,
-    already divided by s). Returns Y [T, N] in X's dtype."""
+                 ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 bits: int = 4):
+    """Y = X·Ŵᵀ for a packed layer (bits 4: qweight [K, N/8], qzeros
+    [K/g, N/8]; bits 3: [K, 3N/32] and [K/g, 3N/32]; scales [K/g, N] float16)
+    and activations X [T, K] (bf16 or float16, already divided by s). Returns
+    Y [T, N] in X's dtype."""
     _dev(X, "X"), _dev(qweight, "qweight"), _dev(qzeros, "qzeros"), _dev(scales, "scales")
+    if bits not in (3, 4):
+        raise ValueError("bits must be 3 or 4")
     T, K = X.shape
     N = scales.shape[1]
-    if qweight.shape != (K, N // 8) or qzeros.shape != (K // group, N // 8) or \
+    cols = N * bits // 32
+    if qweight.shape != (K, cols) or qzeros.shape != (K // group, cols) or \
             scales.shape != (K // group, N):
         raise ValueError("packed layer shapes do not match X and the group size")
     Y = out if out is not None else torch.empty((T, N), dtype=X.dtype, device=X.device)
-    ws = _workspace(ws, w4a16_workspace_bytes(T, N, K, X.dtype), X.device)
-    L.check(L.lib().awq_w4a16_matmul(_ptr(X), _dtype(X), T, N, K, _ptr(qweight), _ptr(qzeros),
-                                     _ptr(scales), int(group), _ptr(Y), _ptr(ws), ws.numel(),
-                                     _stream()))
+    if bits == 4:
+        fn, need = L.lib().awq_w4a16_matmul, w4a16_workspace_bytes(T, N, K, X.dtype)
+    else:
+        fn, need = L.lib().awq_w3a16_matmul, w3a16_workspace_bytes(T, N, K, X.dtype)
+    ws = _workspace(ws, need, X.device)
+    L.check(fn(_ptr(X), _dtype(X), T, N, K, _ptr(qweight), _ptr(qzeros), _ptr(scales), int(group),
+               _ptr(Y), _ptr(ws), ws.numel(), _stream()))
     return Y
 
 

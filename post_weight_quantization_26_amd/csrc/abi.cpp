@@ -36,6 +36,9 @@ hipError_t launch_pack(const void* W, int dtype, int64_t N, int64_t K, const flo
 hipError_t launch_w4a16_dequant(const int32_t* qweight, const int32_t* qzeros,
                                 const uint16_t* scales, int64_t N, int64_t K, int group, int f16,
                                 uint16_t* Wd, hipStream_t st);
+hipError_t launch_w3a16_dequant(const int32_t* qweight, const int32_t* qzeros,
+                                const uint16_t* scales, int64_t N, int64_t K, int group, int f16,
+                                uint16_t* Wd, hipStream_t st);
 hipError_t launch_w4a16_gemm(const uint16_t* X, const uint16_t* Wd, int64_t M, int64_t N,
                              int64_t K, int f16, uint16_t* Y, hipStream_t st);
 hipError_t launch_w4a16_gemv(const uint16_t* X, int64_t T, int64_t N, int64_t K,
@@ -626,6 +629,31 @@ extern "C" awq_status awq_w4a16_matmul(const void* X, awq_dtype dtype, int64_t T
   AWQ_HIP(timed(AWQ_K_W4A16, st,
                 [&] { return launch_w4a16_gemm(x, Wd, T, N, K, f16, y, st); }),
           "w4a16 gemm");
+  return AWQ_OK;
+}
+
+extern "C" awq_status awq_w3a16_matmul(const void* X, awq_dtype dtype, int64_t T, int64_t N,
+                                       int64_t K, const int32_t* qweight, const int32_t* qzeros,
+                                       const uint16_t* scales, int32_t group_size, void* Y,
+                                       void* ws, size_t ws_bytes, void* stream) {
+  awq_status st_ = check_w3a16(X, dtype, T, N, K, qweight, qzeros, scales, group_size, Y, ws,
+                               ws_bytes);
+  if (st_ != AWQ_OK) return st_;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int f16 = dtype == AWQ_F16;
+  uint16_t* Wd = static_cast<uint16_t*>(ws);
+  AWQ_HIP(timed(AWQ_K_DEQUANT, st,
+                [&] {
+                  return launch_w3a16_dequant(qweight, qzeros, scales, N, K, group_size, f16, Wd,
+                                              st);
+                }),
+          "w3a16 dequant");
+  AWQ_HIP(timed(AWQ_K_W4A16, st,
+                [&] {
+                  return launch_w4a16_gemm(static_cast<const uint16_t*>(X), Wd, T, N, K, f16,
+                                           static_cast<uint16_t*>(Y), st);
+                }),
+          "w3a16 gemm");
   return AWQ_OK;
 }
 

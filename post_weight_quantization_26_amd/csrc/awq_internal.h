@@ -127,6 +127,9 @@ inline int64_t w4a16_mgemv_chunks(int64_t N, int64_t K) {
   const int64_t span = 4 * w4a16_mgemv_kpw(N, K);
   return (K + span - 1) / span;
 }
+awq_status check_w3a16(const void* X, awq_dtype d, int64_t T, int64_t N, int64_t K,
+                       const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                       int32_t group, const void* Y, const void* ws, size_t ws_bytes);
 awq_status check_w4a16(const void* X, awq_dtype d, int64_t T, int64_t N, int64_t K,
                        const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
                        int32_t group, const void* Y, const void* ws, size_t ws_bytes);

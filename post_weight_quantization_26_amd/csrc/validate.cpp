@@ -351,6 +351,35 @@ awq_status check_w4a16(const void* X, awq_dtype d, int64_t T, int64_t N, int64_t
   return AWQ_OK;
 }
 
+
+awq_status check_w3a16(const void* X, awq_dtype d, int64_t T, int64_t N, int64_t K,
+                       const int32_t* qweight, const int32_t* qzeros, const uint16_t* scales,
+                       int32_t group, const void* Y, const void* ws, size_t ws_bytes) {
+  if (!X || !qweight || !qzeros || !scales || !Y)
+    return set_error(AWQ_E_INVALID, "w3a16_matmul: NULL pointer argument");
+  if (!dtype_ok(d)) return set_error(AWQ_E_INVALID, "w3a16_matmul: unknown dtype %d", int(d));
+  if (d == AWQ_F32)
+    return set_error(AWQ_E_UNSUPPORTED, "w3a16_matmul: activations must be bf16 or fp16");
+  if (T < 1 || N < 1 || K < 1 || T > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return set_error(AWQ_E_INVALID, "w3a16_matmul: bad shape T=%lld N=%lld K=%lld",
+                     (long long)T, (long long)N, (long long)K);
+  if (group != 32 && group != 64 && group != 128)
+    return set_error(AWQ_E_UNSUPPORTED, "w3a16_matmul: group_size %d (32, 64 or 128)", group);
+  if (N % 32) return set_error(AWQ_E_INVALID, "w3a16_matmul: N=%lld not a multiple of 32",
+                               (long long)N);
+  if (K % kTileK)
+    return set_error(AWQ_E_INVALID, "w3a16_matmul: K=%lld not a multiple of 128", (long long)K);
+  if (!aligned16(X) || !aligned4(qweight) || !aligned4(qzeros) || !aligned16(scales) ||
+      (reinterpret_cast<uintptr_t>(Y) & 1u))
+    return set_error(AWQ_E_INVALID,
+                     "w3a16_matmul: X and scales must be 16-byte aligned, qweight/qzeros 4, Y 2");
+  const size_t need = awq_w3a16_workspace_bytes(T, N, K, d);
+  if (!ws || !aligned16(ws) || ws_bytes < need)
+    return set_error(AWQ_E_WORKSPACE, "w3a16_matmul: workspace needs %zu bytes (16-byte aligned)",
+                     need);
+  return AWQ_OK;
+}
+
 }  // namespace awq
 
 extern "C" size_t awq_w4a16_workspace_bytes(int64_t T, int64_t N, int64_t K, awq_dtype dtype) {
@@ -364,6 +393,14 @@ extern "C" size_t awq_w4a16_workspace_bytes(int64_t T, int64_t N, int64_t K, awq
                                   : std::max(w4a16_gemv_chunks(N, K), w4a16_mgemv_chunks(N, K));
     return align_up(size_t(chunks) * size_t(T) * size_t(N) * 4);
   }
+  return align_up(size_t(N) * size_t(K) * 2);
+}
+
+extern "C" size_t awq_w3a16_workspace_bytes(int64_t T, int64_t N, int64_t K, awq_dtype dtype) {
+  using namespace awq;
+  if (T < 1 || N < 1 || K < 1 || T > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+  if (dtype != AWQ_BF16 && dtype != AWQ_F16) return 0;
+  if (N % 32 || K % kTileK) return 0;
   return align_up(size_t(N) * size_t(K) * 2);
 }
 

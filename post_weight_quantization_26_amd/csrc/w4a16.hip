@@ -100,6 +100,61 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int32_t* __restrict_
   }
 }
 
+// 3-bit codes: row k of qweight holds the N codes densely, code n in bits
+// 3n .. 3n+2 of the row's little-endian word stream, so 32 codes fill 3 words
+// and codes 10 and 21 of each 32 straddle two words (zero points the same).
+template <int R>
+__device__ __forceinline__ uint32_t code3(const uint32_t (&w)[3]) {
+  constexpr int bit = 3 * R, wi = bit / 32, sh = bit % 32;
+  uint32_t v = w[wi] >> sh;
+  if constexpr (sh > 29) v |= w[wi + 1] << (32 - sh);
+  return v & 7u;
+}
+
+// Lane (kb, j): k rows 8kb..8kb+7 of output rows 32j..32j+31 (3 words per k
+// row); one 16-byte store of 8 k per output row, consecutive lanes continuing
+// the same row. Ŵ = (q - z)·scale in float32, rounded once to the 16-bit type.
+template <bool F16>
+__global__ __launch_bounds__(256) void dequant3_kernel(const int32_t* __restrict__ qweight,
+                                                       const int32_t* __restrict__ qzeros,
+                                                       const uint16_t* __restrict__ scales,
+                                                       int64_t N, int64_t K, int group,
+                                                       uint16_t* __restrict__ Wd) {
+#pragma clang fp contract(off)
+  const int64_t K8 = K / 8, N32 = N / 32, W3 = N / 32 * 3;
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= K8 * N32) return;
+  const int64_t kb = t % K8, j = t / K8;
+  const int64_t k0 = kb * 8, g = k0 / group;
+  uint32_t zw[3], w[8][3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) zw[i] = uint32_t(qzeros[g * W3 + 3 * j + i]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int i = 0; i < 3; ++i) w[e][i] = uint32_t(qweight[(k0 + e) * W3 + 3 * j + i]);
+  const uint16_t* sg = scales + g * N + 32 * j;
+#define AWQ_DQ3_ROW(R)                                                                        \
+  {                                                                                           \
+    const float zf = float(code3<R>(zw));                                                     \
+    const float sc = f16_to_f32(sg[R]);                                                       \
+    uint32_t h[4];                                                                            \
+    for (int i = 0; i < 4; ++i) {                                                             \
+      const float lo = (float(code3<R>(w[2 * i])) - zf) * sc;                                 \
+      const float hi = (float(code3<R>(w[2 * i + 1])) - zf) * sc;                             \
+      h[i] = uint32_t(to16<F16>(lo)) | (uint32_t(to16<F16>(hi)) << 16);                       \
+    }                                                                                         \
+    *reinterpret_cast<uint4*>(Wd + (32 * j + R) * K + k0) = make_uint4(h[0], h[1], h[2], h[3]); \
+  }
+  AWQ_DQ3_ROW(0) AWQ_DQ3_ROW(1) AWQ_DQ3_ROW(2) AWQ_DQ3_ROW(3) AWQ_DQ3_ROW(4) AWQ_DQ3_ROW(5)
+  AWQ_DQ3_ROW(6) AWQ_DQ3_ROW(7) AWQ_DQ3_ROW(8) AWQ_DQ3_ROW(9) AWQ_DQ3_ROW(10) AWQ_DQ3_ROW(11)
+  AWQ_DQ3_ROW(12) AWQ_DQ3_ROW(13) AWQ_DQ3_ROW(14) AWQ_DQ3_ROW(15) AWQ_DQ3_ROW(16)
+  AWQ_DQ3_ROW(17) AWQ_DQ3_ROW(18) AWQ_DQ3_ROW(19) AWQ_DQ3_ROW(20) AWQ_DQ3_ROW(21)
+  AWQ_DQ3_ROW(22) AWQ_DQ3_ROW(23) AWQ_DQ3_ROW(24) AWQ_DQ3_ROW(25) AWQ_DQ3_ROW(26)
+  AWQ_DQ3_ROW(27) AWQ_DQ3_ROW(28) AWQ_DQ3_ROW(29) AWQ_DQ3_ROW(30) AWQ_DQ3_ROW(31)
+#undef AWQ_DQ3_ROW
+}
+
 // ---------------------------------------------------------------------------
 // prefill: MFMA GEMM with a store epilogue
 // ---------------------------------------------------------------------------
@@ -520,6 +575,19 @@ hipError_t launch_w4a16_dequant(const int32_t* qweight, const int32_t* qzeros,
     dequant_kernel<true><<<blocks, 256, 0, st>>>(qweight, qzeros, scales, N, K, group, Wd);
   else
     dequant_kernel<false><<<blocks, 256, 0, st>>>(qweight, qzeros, scales, N, K, group, Wd);
+  return hipGetLastError();
+}
+
+hipError_t launch_w3a16_dequant(const int32_t* qweight, const int32_t* qzeros,
+                                const uint16_t* scales, int64_t N, int64_t K, int group, int f16,
+                                uint16_t* Wd, hipStream_t st) {
+  if (N % 32 || K % 8) return hipErrorInvalidValue;
+  const int64_t lanes = (K / 8) * (N / 32);
+  const unsigned blocks = unsigned((lanes + 255) / 256);
+  if (f16)
+    dequant3_kernel<true><<<blocks, 256, 0, st>>>(qweight, qzeros, scales, N, K, group, Wd);
+  else
+    dequant3_kernel<false><<<blocks, 256, 0, st>>>(qweight, qzeros, scales, N, K, group, Wd);
   return hipGetLastError();
 }
 

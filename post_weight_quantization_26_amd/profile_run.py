@@ -84,30 +84,31 @@ def w4a16(reps: int) -> None:
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
     g.manual_seed(7)
-    for N, K in ((4096, 4096), (28672, 8192)):
+    for N, K, bits in ((4096, 4096, 4), (28672, 8192, 4), (4096, 4096, 3), (28672, 8192, 3)):
         W = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
         s = torch.ones(K, dtype=torch.float32, device=dev)
-        qw, qz, sc = api.quantize_pack(W, s)
+        qw, qz, sc = api.quantize_pack(W, s, bits=bits)
         del W
-        for T in (1, 4, 16, 4096):
+        for T in ((1, 4, 16, 4096) if bits == 4 else (1, 4096)):
             X = torch.randn((T, K), generator=g, device=dev).to(torch.bfloat16)
-            ws = torch.empty(api.w4a16_workspace_bytes(T, N, K, torch.bfloat16), dtype=torch.uint8,
-                             device=dev)
+            need = (api.w4a16_workspace_bytes if bits == 4 else api.w3a16_workspace_bytes)(
+                T, N, K, torch.bfloat16)
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
             Y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
             n_rep = reps if T <= 16 else max(3, reps // 4)
-            api.w4a16_matmul(X, qw, qz, sc, ws=ws, out=Y)
+            api.w4a16_matmul(X, qw, qz, sc, ws=ws, out=Y, bits=bits)
             torch.cuda.synchronize()
             api.profile_enable(True)
             api.profile_reset()
             for _ in range(n_rep):
-                api.w4a16_matmul(X, qw, qz, sc, ws=ws, out=Y)
+                api.w4a16_matmul(X, qw, qz, sc, ws=ws, out=Y, bits=bits)
             torch.cuda.synchronize()
             t = {k: api.profile_read(k) for k in ("dequant", "w4a16", "w4a16_reduce")}
             api.profile_enable(False)
             main_us = t["w4a16"][0] * 1e3 / n_rep
-            rec = {"N": N, "K": K, "T": T, "main_kernel_us": round(main_us, 2)}
-            packed = N * K // 2 + (N * K // 128) * (2 + 0.5)
-            if T <= 16:
+            rec = {"N": N, "K": K, "T": T, "bits": bits, "main_kernel_us": round(main_us, 2)}
+            packed = N * K * bits // 8 + (N * K // 128) * (2 + bits / 8)
+            if T <= 16 and bits == 4:
                 # what any decode kernel must move: the packed layer, X and Y
                 moved = packed + T * K * 2 + T * N * 2
                 rec.update(path="gemv", reduce_us=round(t["w4a16_reduce"][0] * 1e3 / n_rep, 2),

@@ -265,6 +265,28 @@ def test_profile_kinds_match_header(L):
     assert count == len(L.KERNEL_KINDS)
 
 
+def test_w3a16_workspace_and_rejects(L):
+    lib = L.lib()
+    wsb = lib.awq_w3a16_workspace_bytes
+    assert wsb(1, 4096, 4096, L.AWQ_BF16) == 4096 * 4096 * 2      # Ŵ rows for every T
+    assert wsb(4096, 4096, 4096, L.AWQ_F16) == 4096 * 4096 * 2
+    assert wsb(1, 4104, 4096, L.AWQ_BF16) == 0                     # N not a multiple of 32
+    assert wsb(1, 4096, 4096, L.AWQ_F32) == 0
+    f = lib.awq_w3a16_matmul
+    big = 1 << 40
+    call = lambda **k: f(k.get("X", FAKE), k.get("dt", L.AWQ_BF16), k.get("T", 4),
+                         k.get("N", 256), k.get("K", 256), FAKE, FAKE, FAKE, k.get("g", 128),
+                         k.get("Y", FAKE), FAKE, k.get("wsb", big), None)
+    assert call(X=None) == -1
+    assert call(dt=L.AWQ_F32) == -2
+    assert call(N=264) == -1
+    assert "multiple of 32" in L.last_error()
+    assert call(K=200) == -1
+    assert call(g=16) == -2
+    assert call(wsb=16) == -3
+    assert "w3a16_matmul" in L.last_error()
+
+
 def test_w4a16_workspace_and_rejects(L):
     lib = L.lib()
     wsb = lib.awq_w4a16_workspace_bytes

@@ -49,35 +49,39 @@ def _dec(bits, dtype):
     return O.decode(bits, dtype)
 
 
-def packed_layer(N, K, group, seed):
-    """A packed 4-bit layer from the oracle (inputs for the consumer)."""
+def packed_layer(N, K, group, seed, bits=4):
+    """A packed layer from the oracle (inputs for the consumer)."""
     rng = np.random.default_rng(seed)
     W = synth.make_weight(N, K, 0.02, "bf16", seed=seed)
     s = np.exp(rng.uniform(-1, 1, size=K)).astype(np.float32)
-    qw, qz, sc, ovf = O.quantize_pack(W, "bf16", s, None, 4, group, True)
+    qw, qz, sc, ovf = O.quantize_pack(W, "bf16", s, None, bits, group, True)
     assert not ovf
     return qw, qz, sc
 
 
-def check_consumer(api, T, N, K, group, dtype, seed):
-    qw, qz, sc = packed_layer(N, K, group, seed)
+def check_consumer(api, T, N, K, group, dtype, seed, bits=4):
+    """bits 4: exact-Ŵ decode for T <= 16, 16-bit Ŵ GEMM above; bits 3: the
+    16-bit Ŵ GEMM for every T."""
+    qw, qz, sc = packed_layer(N, K, group, seed, bits)
     rng = np.random.default_rng(seed + 1)
     x32 = rng.standard_normal((T, K)).astype(np.float32)
     X = _enc(x32, dtype)
     Xd = to_dev(X, dtype)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
-    Y = api.w4a16_matmul(Xd, dev(qw), dev(qz), dev(sc).view(torch.float16), group=group)
+    Y = api.w4a16_matmul(Xd, dev(qw), dev(qz), dev(sc).view(torch.float16), group=group,
+                         bits=bits)
+    decode = T <= 16 and bits == 4
     torch.cuda.synchronize()
     y = Y.float().cpu().numpy().astype(np.float64)
     x = _dec(X, dtype).astype(np.float64)
-    w_exact = O.dequantize_packed(qw, qz, sc, N, 4, group)          # [N, K] float64
-    if T <= 16:
+    w_exact = O.dequantize_packed(qw, qz, sc, N, bits, group)       # [N, K] float64
+    if decode:
         w_op = w_exact
     else:
         w32 = w_exact.astype(np.float32)
         w_op = _dec(_enc(w32, dtype), dtype).astype(np.float64)
     y_model = x @ w_op.T
-    if T <= 16:
+    if decode:
         q = O.unpack_codes(qw, N, 4).astype(np.float64)                  # [K, N]
         z = np.repeat(O.unpack_codes(qz, N, 4), group, axis=0).astype(np.float64)
         scl = np.repeat(sc.view(np.float16).astype(np.float64), group, axis=0)
@@ -90,11 +94,11 @@ def check_consumer(api, T, N, K, group, dtype, seed):
     err = np.abs(y - y_model)
     worst = (err / bound).max()
     assert worst <= 1.0, f"GPU vs model exceeds the bound ({worst:.2f}x)"
-    y_ref = O.w4a16_matmul(X, dtype, qw, qz, sc, N, 4, group)
-    op_slack = 0.0 if T <= 16 else UOUT[dtype]
+    y_ref = O.w4a16_matmul(X, dtype, qw, qz, sc, N, bits, group)
+    op_slack = 0.0 if decode else UOUT[dtype]
     assert np.all(np.abs(y - y_ref) <= bound + op_slack * (np.abs(x) @ np.abs(w_exact).T))
     rel = np.abs(y - y_ref).max() / np.abs(y_ref).max()
-    print(f"w4a16 T={T} N={N} K={K} g={group} {dtype}: |gpu-model|/bound {worst:.2e}, "
+    print(f"w{bits}a16 T={T} N={N} K={K} g={group} {dtype}: |gpu-model|/bound {worst:.2e}, "
           f"max |gpu-oracle|/max|Y| {rel:.2e}")
 
 
@@ -150,6 +154,37 @@ def test_gemm_group_sizes(api, group):
 def test_gemm_many_tiles(api):
     # 33 token tiles (the XCD-grouped order) and 9 output tiles, last ragged
     check_consumer(api, 33 * 256 - 7, 2056, 256, 128, "bf16", seed=120)
+
+
+# 3-bit layout: codes 10 and 21 of each 32 straddle two words; N = 288 is 9
+# groups of 32 rows and a ragged 256-row GEMM tile
+@pytest.mark.parametrize("T", [1, 16, 300])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_w3a16_consumer(api, T, dtype):
+    check_consumer(api, T, 288, 384, 128, dtype, seed=180 + T, bits=3)
+
+
+@pytest.mark.parametrize("group", [32, 64])
+def test_w3a16_group_sizes(api, group):
+    check_consumer(api, 40, 1024, 512, group, "bf16", seed=190 + group, bits=3)
+
+
+def test_search_pack_consume_end_to_end_int3(api):
+    """INT3: search α, pack 3-bit codes with s*, feed X/s* to the 3-bit
+    consumer; its output error is the error the search reported for α*."""
+    X, W = synth.make_custom(2048, 512, 1024, "bf16", seed=131)
+    Xd, Wd = to_dev(X, "bf16"), to_dev(W, "bf16")
+    abar = api.act_stats(Xd)
+    res = api.search_scale(Xd, Wd, abar, synth.alpha_grid(20), bits=3)
+    qw, qz, sc = api.quantize_pack(Wd, res["s_best"], bits=3)
+    xs = (Xd.float() / res["s_best"][None, :]).to(torch.bfloat16)
+    Y = api.w4a16_matmul(xs, qw, qz, sc, bits=3)
+    y_exact = Xd.double() @ Wd.double().T
+    mse = ((Y.double() - y_exact) ** 2).mean().item()
+    want = float(res["mse"][res["index"]])
+    print(f"end to end INT3: consumer mse {mse:.4e}, search mse at alpha* {want:.4e}")
+    assert abs(mse - want) <= 0.05 * want
+    assert mse < 0.5 * float(res["mse"][0])
 
 
 def test_search_pack_consume_end_to_end(api):
