@@ -100,6 +100,46 @@ __global__ __launch_bounds__(256) void dequant_kernel(const int32_t* __restrict_
   }
 }
 
+// N a multiple of 32: lane (kb, j) takes k rows 8kb..8kb+7 of word columns
+// 4j..4j+3 (output rows 32j..32j+31) with one 16-byte load per k row, so a
+// 128-byte line of qweight feeds 8 lanes instead of 32.
+template <bool F16>
+__global__ __launch_bounds__(256) void dequant4x4_kernel(const int32_t* __restrict__ qweight,
+                                                         const int32_t* __restrict__ qzeros,
+                                                         const uint16_t* __restrict__ scales,
+                                                         int64_t N, int64_t K, int group,
+                                                         uint16_t* __restrict__ Wd) {
+#pragma clang fp contract(off)
+  const int64_t K8 = K / 8, N8 = N / 8, N32 = N / 32;
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= K8 * N32) return;
+  const int64_t kb = t % K8, j = t / K8;
+  const int64_t k0 = kb * 8, g = k0 / group;
+  uint4 w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = *reinterpret_cast<const uint4*>(qweight + (k0 + i) * N8 + 4 * j);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float sc[8], zf[8];
+    group_params(qzeros, scales, N, g, 4 * j + c, sc, zf);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      uint32_t h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t a = c == 0 ? w[2 * i].x : c == 1 ? w[2 * i].y : c == 2 ? w[2 * i].z : w[2 * i].w;
+        const uint32_t b = c == 0 ? w[2 * i + 1].x : c == 1 ? w[2 * i + 1].y
+                         : c == 2 ? w[2 * i + 1].z : w[2 * i + 1].w;
+        const float lo = (float((a >> (4 * r)) & 0xFu) - zf[r]) * sc[r];
+        const float hi = (float((b >> (4 * r)) & 0xFu) - zf[r]) * sc[r];
+        h[i] = uint32_t(to16<F16>(lo)) | (uint32_t(to16<F16>(hi)) << 16);
+      }
+      *reinterpret_cast<uint4*>(Wd + (32 * j + 8 * c + r) * K + k0) =
+          make_uint4(h[0], h[1], h[2], h[3]);
+    }
+  }
+}
+
 // 3-bit codes: row k of qweight holds the N codes densely, code n in bits
 // 3n .. 3n+2 of the row's little-endian word stream, so 32 codes fill 3 words
 // and codes 10 and 21 of each 32 straddle two words (zero points the same).
@@ -569,6 +609,17 @@ void launch_gemv(dim3 grid, hipStream_t st, const uint16_t* X, int64_t T, int64_
 hipError_t launch_w4a16_dequant(const int32_t* qweight, const int32_t* qzeros,
                                 const uint16_t* scales, int64_t N, int64_t K, int group, int f16,
                                 uint16_t* Wd, hipStream_t st) {
+  // 16-byte loads of 4 word columns need N a multiple of 32 and qweight
+  // 16-byte aligned; otherwise one word column per lane
+  if (N % 32 == 0 && (reinterpret_cast<uintptr_t>(qweight) & 15u) == 0) {
+    const int64_t lanes = (K / 8) * (N / 32);
+    const unsigned blocks = unsigned((lanes + 255) / 256);
+    if (f16)
+      dequant4x4_kernel<true><<<blocks, 256, 0, st>>>(qweight, qzeros, scales, N, K, group, Wd);
+    else
+      dequant4x4_kernel<false><<<blocks, 256, 0, st>>>(qweight, qzeros, scales, N, K, group, Wd);
+    return hipGetLastError();
+  }
   const int64_t lanes = (K / 8) * (N / 8);
   const unsigned blocks = unsigned((lanes + 255) / 256);
   if (f16)

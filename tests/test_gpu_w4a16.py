@@ -146,6 +146,13 @@ def test_gemm_path(api, T, dtype):
     check_consumer(api, T, 264, 384, 128, dtype, seed=100 + T)
 
 
+# N a multiple of 32: the dequantisation reads 4 word columns per lane
+@pytest.mark.parametrize("N,group,dtype", [(288, 128, "bf16"), (1056, 32, "f16"),
+                                           (544, 64, "bf16")])
+def test_gemm_path_wide_dequant(api, N, group, dtype):
+    check_consumer(api, 300, N, 512, group, dtype, seed=200 + N)
+
+
 @pytest.mark.parametrize("group", [32, 64])
 def test_gemm_group_sizes(api, group):
     check_consumer(api, 520, 520, 512, group, "f16", seed=110 + group)
