@@ -658,25 +658,26 @@ def check_w4a16_exact_layer(O):
 
 
 def check_w4a16_bruteforce(O):
-    """Tiny packed layer: every output equals a pure-Python sum over k of
-    x[t][k]·(code - zero)·scale, codes and zeros read bit by bit."""
+    """Tiny packed layers of 4 and 3 bits: every output equals a pure-Python
+    sum over k of x[t][k]·(code - zero)·scale, codes and zeros read bit by bit
+    (for 3 bits, 32 outputs so that codes straddle words)."""
     rng = _rng(71)
-    N, K, T, gs = 16, 128, 3, 64
-    W = synth.make_weight(N, K, 0.02, "bf16", seed=72)
-    s = np.exp(rng.uniform(-1, 1, size=K)).astype(F32)
-    qw, qz, sc, _ = O.quantize_pack(W, "bf16", s, None, 4, gs, True)
-    X = synth.f32_to_bf16_bits(rng.standard_normal((T, K)).astype(F32))
-    Y = O.w4a16_matmul(X, "bf16", qw, qz, sc, N, 4, gs)
-    x = synth.bf16_bits_to_f32(X).astype(np.float64)
-    scf = sc.view(np.float16).astype(np.float64)
-    for t in range(T):
-        for n in range(N):
-            acc = []
-            for k in range(K):
-                code = _unpack_bits_python(qw[k], 4, N)[n]
-                zero = _unpack_bits_python(qz[k // gs], 4, N)[n]
-                acc.append(float(x[t, k]) * (code - zero) * float(scf[k // gs, n]))
-            assert math.isclose(Y[t, n], math.fsum(acc), rel_tol=1e-12, abs_tol=1e-14)
+    K, T, gs = 128, 3, 64
+    for bits, N in ((4, 16), (3, 32)):
+        W = synth.make_weight(N, K, 0.02, "bf16", seed=72 + bits)
+        s = np.exp(rng.uniform(-1, 1, size=K)).astype(F32)
+        qw, qz, sc, _ = O.quantize_pack(W, "bf16", s, None, bits, gs, True)
+        X = synth.f32_to_bf16_bits(rng.standard_normal((T, K)).astype(F32))
+        Y = O.w4a16_matmul(X, "bf16", qw, qz, sc, N, bits, gs)
+        x = synth.bf16_bits_to_f32(X).astype(np.float64)
+        scf = sc.view(np.float16).astype(np.float64)
+        codes = [_unpack_bits_python(qw[k], bits, N) for k in range(K)]
+        zeros = [_unpack_bits_python(qz[g], bits, N) for g in range(K // gs)]
+        for t in range(T):
+            for n in range(N):
+                acc = [float(x[t, k]) * (codes[k][n] - zeros[k // gs][n]) * float(scf[k // gs, n])
+                       for k in range(K)]
+                assert math.isclose(Y[t, n], math.fsum(acc), rel_tol=1e-12, abs_tol=1e-14)
 
 
 ALL_CHECKS = [

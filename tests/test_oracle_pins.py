@@ -79,6 +79,9 @@ MUTATIONS = [
     ("unpacking reads codes from the top bit", "        w, b = divmod(bits * c, 32)\n        v = u",
      "        w, b = divmod(bits * c, 32)\n        b = 32 - bits - b if b + bits <= 32 else b\n        v = u",
      [P.check_w4a16_exact_layer]),
+    ("consumer drops the high bits of straddling 3-bit codes",
+     "        if b + bits > 32:\n            v = v | (u[:, w + 1]",
+     "        if False:\n            v = v | (u[:, w + 1]", [P.check_w4a16_bruteforce]),
     ("group size ignored by the quantiser", "    G = K // group\n",
      "    group = 128\n    G = K // group\n", [P.check_codes_nearest_bruteforce]),
     ("group searched on its first layer only",
