@@ -26,7 +26,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 and fp16 MFMA, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published (the float32 search GEMM uses FMAs)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 TRAFFIC_FILES = {"direct": os.path.join(ROOT, "profiles", "search_gemm_traffic.json"),
                  "gram": os.path.join(ROOT, "profiles", "gram_search_traffic.json")}
@@ -129,11 +130,13 @@ def main():
     else:
         X, W = synth.make_layer(cfg)
         Ws = [W]
-    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(cfg.dtype, torch.float32)
 
     def up(a):
         if cfg.dtype == "bf16":
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        if cfg.dtype == "f16":
+            return torch.from_numpy(a.view(np.float16)).to(dev)
         return torch.from_numpy(a).to(dev)
 
     Xd = up(X)
@@ -221,15 +224,18 @@ def main():
         else:
             gemm_ms, gemm_n = prof["gemm"]
             flops_per_step = 2.0 * T * N * K * cands_per_step
-            kernel_name = "search_gemm_bf16_kernel"
+            kernel_name = {"bf16": "search_gemm_bf16_kernel", "f16": "search_gemm_f16_kernel"}.get(
+                cfg.dtype, "search_gemm_f32_kernel")
         gemm_avg_s = gemm_ms / 1e3 / max(gemm_n, 1)
         launches_per_step = gemm_n // args.steps if args.steps else 0
         flops_per_launch = flops_per_step / max(launches_per_step, 1)
         achieved = flops_per_launch / gemm_avg_s / 1e12
         traffic = gemm_traffic(name, how)
-        roof = {"bound": "mfma", "achieved": round(achieved, 2),
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+        f32 = cfg.dtype == "f32"
+        peak = FP32_VECTOR_PEAK_TFLOPS if f32 else MFMA_BF16_PEAK_TFLOPS
+        roof = {"bound": "alu" if f32 else "mfma", "achieved": round(achieved, 2),
+                "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4),
                 "traffic": traffic, "kernel": kernel_name,
                 "avg_launch_us": round(gemm_avg_s * 1e6, 1),
                 "algorithmic_flops_per_launch": flops_per_launch}
@@ -273,13 +279,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "dtype": cfg.dtype,
         "data": "synthetic",
         "config": {"workload": name, "T": T, "N": N, "K": K, "group": cfg.group, "bits": cfg.bits,
                    "zero_point": zp, "n_alpha": cfg.n_alpha, "n_ratio": cfg.n_ratio,
                    "pack": cfg.pack, "layers": list(cfg.layers) or None, "method": method},
         "roofline": roofline,
-        "mfma_util_pct": round(100 * achieved / MFMA_BF16_PEAK_TFLOPS, 2),
+        "mfma_util_pct": round(100 * roofline["frac"], 2),
         "hbm": {"stats_GBps": None if stats_gbs is None else round(stats_gbs, 1),
                 "pack_GBps": None if pack_gbs is None else round(pack_gbs, 1),
                 "peak_GBps": HBM_PEAK_GBS},

@@ -139,7 +139,8 @@ awq_status awq_scale_table(const float* abar, int64_t K, const float* alphas, in
                            float* s_table, void* stream);
 
 /* Steps 2-6 — α grid search for one layer.
- * X [T, K], W [N, K] of `dtype` (bf16 or f32); abar [K] from awq_act_stats;
+ * X [T, K], W [N, K] of `dtype` (bf16, fp16 or f32; the candidates' error
+ * weights go to the GEMM in the same type); abar [K] from awq_act_stats;
  * alphas [host] n_alpha values in [0, 1].
  * Outputs: s_best [K] f32 = the scale row of the best α;
  *          alpha_best [host] 1 f32; mse [host] n_alpha f64, mse[a] =

@@ -21,11 +21,13 @@
 namespace awq {
 namespace {
 
-// K must be a multiple of 128 (so the number of 32-wide k-tiles is a multiple of 4).
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void search_gemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ E,
-                             int64_t M, int64_t Nc, int64_t K, int tiles_m, int tiles_n,
-                             float* __restrict__ partials) {
+// K must be a multiple of 128 (so the number of 32-wide k-tiles is a multiple
+// of 4). F16: fp16 operands instead of bf16 (the same tile, the fp16 MFMA).
+template <bool F16>
+__device__ __forceinline__ void search_gemm_16(const uint16_t* __restrict__ X,
+                                               const uint16_t* __restrict__ E, int64_t M,
+                                               int64_t Nc, int64_t K, int tiles_m, int tiles_n,
+                                               float* __restrict__ partials) {
   int tm, tn;
   if (!tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
@@ -34,7 +36,7 @@ void search_gemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __r
   GemmCtx c;
   gemm_setup(c, X + m0 * K, rows_a, E + n0 * K, rows_b, K);
   floatx16 acc[4][4];
-  gemm_mainloop<false>(c, acc);
+  gemm_mainloop<F16>(c, acc);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wm = c.wave >> 1, wn = c.wave & 1;
 
@@ -56,6 +58,20 @@ void search_gemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __r
   __syncthreads();
   const int64_t col = n0 + tid;
   if (col < Nc) partials[int64_t(tm) * Nc + col] = red[tid] + red[BN + tid];
+}
+
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void search_gemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ E,
+                             int64_t M, int64_t Nc, int64_t K, int tiles_m, int tiles_n,
+                             float* __restrict__ partials) {
+  search_gemm_16<false>(X, E, M, Nc, K, tiles_m, tiles_n, partials);
+}
+
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void search_gemm_f16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ E,
+                            int64_t M, int64_t Nc, int64_t K, int tiles_m, int tiles_n,
+                            float* __restrict__ partials) {
+  search_gemm_16<true>(X, E, M, Nc, K, tiles_m, tiles_n, partials);
 }
 
 // ---------------------------------------------------------------------------
@@ -121,13 +137,18 @@ __global__ __launch_bounds__(256) void search_gemm_f32_kernel(const float* __res
 
 hipError_t launch_search_gemm(const void* X, int dtype, const void* E, int64_t M, int64_t Nc,
                               int64_t K, float* partials, hipStream_t st) {
-  if (dtype == 1) {
+  if (dtype == 1 || dtype == 2) {
     if (K % 128) return hipErrorInvalidValue;
     const int tiles_m = int((M + BM - 1) / BM), tiles_n = int((Nc + BN - 1) / BN);
     const int64_t blocks = gemm_blocks(tiles_m, tiles_n);
-    search_gemm_bf16_kernel<<<unsigned(blocks), NT, 0, st>>>(
-        static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(E), M, Nc, K, tiles_m,
-        tiles_n, partials);
+    if (dtype == 1)
+      search_gemm_bf16_kernel<<<unsigned(blocks), NT, 0, st>>>(
+          static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(E), M, Nc, K, tiles_m,
+          tiles_n, partials);
+    else
+      search_gemm_f16_kernel<<<unsigned(blocks), NT, 0, st>>>(
+          static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(E), M, Nc, K, tiles_m,
+          tiles_n, partials);
   } else {
     const int64_t tiles_m = (M + FB - 1) / FB, tiles_n = (Nc + FB - 1) / FB;
     search_gemm_f32_kernel<<<unsigned(tiles_m * tiles_n), 256, 0, st>>>(

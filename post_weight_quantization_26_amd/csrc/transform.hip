@@ -44,6 +44,20 @@ __device__ __forceinline__ void store8<1>(void* E, int64_t idx, const float (&e)
   *reinterpret_cast<uint4*>(static_cast<uint16_t*>(E) + idx) = q;
 }
 
+// fp16 output: hardware conversion, round-to-nearest-even (subnormals kept).
+template <>
+__device__ __forceinline__ void store8<2>(void* E, int64_t idx, const float (&e)[8]) {
+  uint16_t h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(e[i]));
+  uint4 q;
+  q.x = uint32_t(h[0]) | (uint32_t(h[1]) << 16);
+  q.y = uint32_t(h[2]) | (uint32_t(h[3]) << 16);
+  q.z = uint32_t(h[4]) | (uint32_t(h[5]) << 16);
+  q.w = uint32_t(h[6]) | (uint32_t(h[7]) << 16);
+  *reinterpret_cast<uint4*>(static_cast<uint16_t*>(E) + idx) = q;
+}
+
 template <>
 __device__ __forceinline__ void store8<0>(void* E, int64_t idx, const float (&e)[8]) {
   float4* p = reinterpret_cast<float4*>(static_cast<float*>(E) + idx);
@@ -51,7 +65,8 @@ __device__ __forceinline__ void store8<0>(void* E, int64_t idx, const float (&e)
   p[1] = make_float4(e[4], e[5], e[6], e[7]);
 }
 
-// DT: 0 = f32 (E in f32), 1 = bf16 (E in bf16). G: group size (32, 64, 128);
+// DT: 0 = f32 (E in f32), 1 = bf16 (E in bf16), 2 = fp16 (E in fp16). G:
+// group size (32, 64, 128);
 // the G/8 lanes of a group reduce its range.
 template <int DT, int G>
 __global__ __launch_bounds__(kThreads) void transform_kernel(
@@ -139,6 +154,9 @@ hipError_t launch_transform(const void* W, int dtype, int64_t N, int64_t K, cons
   const unsigned blocks = unsigned((lanes + kThreads - 1) / kThreads);
   if (dtype == 1)
     return launch_transform_g<1>(group, blocks, st, W, N, K, s_rows, inv_rows, s_stride, g,
+                                 has_ratio, nc, bits, zero_point, E, cand_stride);
+  if (dtype == 2)
+    return launch_transform_g<2>(group, blocks, st, W, N, K, s_rows, inv_rows, s_stride, g,
                                  has_ratio, nc, bits, zero_point, E, cand_stride);
   return launch_transform_g<0>(group, blocks, st, W, N, K, s_rows, inv_rows, s_stride, g,
                                has_ratio, nc, bits, zero_point, E, cand_stride);

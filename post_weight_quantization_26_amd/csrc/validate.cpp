@@ -197,8 +197,6 @@ awq_status check_search(int op, const void* X, const void* W, awq_dtype d, int64
   if (!X || !W || !vec || !grid || !out_dev || !out_host || (is_scale_op(op) && !out_host2))
     return set_error(AWQ_E_INVALID, "%s: NULL pointer argument", nm);
   if (!dtype_ok(d)) return set_error(AWQ_E_INVALID, "%s: unknown dtype %d", nm, int(d));
-  if (d == AWQ_F16)
-    return set_error(AWQ_E_UNSUPPORTED, "%s: fp16 inputs are not supported (bf16 or f32)", nm);
   if (is_gram_op(op) && d != AWQ_BF16)
     return set_error(AWQ_E_UNSUPPORTED, "%s: the Gram path takes bf16 inputs", nm);
   if (is_gram_op(op) && T > (int64_t(1) << 22))

@@ -37,7 +37,7 @@ class LayerConfig:
     T: int                   # calibration tokens
     N: int                   # output channels (rows of W)
     K: int                   # input channels
-    dtype: str               # "bf16" or "f32" for both X and W
+    dtype: str               # "bf16", "f16" or "f32" for both X and W
     w_std: float
     n_outliers: int
     out_lo: float
@@ -73,6 +73,10 @@ CONFIGS = {
                                          0.02, 41, 20.0, 100.0, pack=True, group=64),
     "llama7b_attn_4096_g32": LayerConfig("llama7b_attn_4096_g32", 2, 65536, 4096, 4096, "bf16",
                                          0.02, 41, 20.0, 100.0, pack=True, group=32),
+    # The same attention projection held in fp16 (an fp16 model); the same
+    # underlying values as llama7b_attn_4096 (config id 2), stored as fp16.
+    "llama7b_attn_4096_f16": LayerConfig("llama7b_attn_4096_f16", 2, 65536, 4096, 4096, "f16",
+                                         0.02, 41, 20.0, 100.0, pack=True),
     # 70B-class MLP layer, asymmetric and symmetric INT4.
     "llama70b_mlp": LayerConfig("llama70b_mlp", 5, 32768, 28672, 8192, "bf16", 0.015, 82,
                                 20.0, 100.0, variants=(True, False), n_ratio=20, pack=True),
@@ -113,7 +117,12 @@ def _rng(seed: int, cid: int, stream: int) -> np.random.Generator:
 
 
 def _encode(a32: np.ndarray, dtype: str) -> np.ndarray:
-    return f32_to_bf16_bits(a32) if dtype == "bf16" else np.ascontiguousarray(a32, dtype=np.float32)
+    """float32 values stored as bf16 bits (RNE), fp16 bits (numpy's RNE) or float32."""
+    if dtype == "bf16":
+        return f32_to_bf16_bits(a32)
+    if dtype == "f16":
+        return np.ascontiguousarray(a32, dtype=np.float32).astype(np.float16).view(np.uint16)
+    return np.ascontiguousarray(a32, dtype=np.float32)
 
 
 def make_weight(N: int, K: int, w_std: float, dtype: str, seed: int = DEFAULT_SEED,
@@ -140,12 +149,13 @@ def make_activations(T: int, K: int, n_out: int, lo: float, hi: float, dtype: st
     """X [T, K]: N(0,1) (or |N(0,1)|·sign) with ``n_out`` channels scaled up.
 
     Drawn in token chunks so a 65536 x 11008 layer never holds a float64 copy.
-    The outlier factor is applied in float32 before the single bf16 rounding.
+    The outlier factor is applied in float32 before the single rounding to
+    the stored type (bf16 or fp16 bits, or float32).
     """
     idx, fac = outlier_channels(K, n_out, lo, hi, seed, cid)
     g = _rng(seed, cid, 1)
     gs = _rng(seed, cid, 4) if x_kind == "abs_sign" else None
-    out = np.empty((T, K), dtype=np.uint16 if dtype == "bf16" else np.float32)
+    out = np.empty((T, K), dtype=np.uint16 if dtype in ("bf16", "f16") else np.float32)
     for t0 in range(0, T, chunk):
         t1 = min(T, t0 + chunk)
         x = g.standard_normal((t1 - t0, K), dtype=np.float32)
@@ -189,8 +199,6 @@ def make_norm_weight(K: int, dtype: str, seed: int = DEFAULT_SEED, cid: int = 0,
 
 
 def _encode_any(a32: np.ndarray, dtype: str) -> np.ndarray:
-    if dtype == "f16":
-        return a32.astype(np.float16).view(np.uint16)
     return _encode(a32, dtype)
 
 

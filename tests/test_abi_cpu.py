@@ -97,7 +97,7 @@ def _search(L, op, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(X=None), -1), (dict(W=None), -1), (dict(vec=None), -1), (dict(out=None), -1),
     (dict(T=0), -1), (dict(N=-3), -1), (dict(K=200), -1), (dict(K=0), -1),
-    (dict(dtype=7), -1), (dict(dtype=2), -2),
+    (dict(dtype=7), -1),
     (dict(qc=None), -2),
     (dict(grid=[0.5, 1.5]), -1), (dict(grid=[-0.1]), -1), (dict(grid=[float("nan")]), -1),
     (dict(grid=[0.5] * 65), -1), (dict(grid=[]), -1),
@@ -398,6 +398,9 @@ def test_gram_workspace_and_rejects(L):
     qc = L.QConfig(4, 128, 1)
     f = lib.awq_search_scale_gram
     assert f(FAKE, FAKE, L.AWQ_F32, 256, 256, 256, FAKE, g, 3, qc, FAKE, ctypes.byref(a_best), mse,
+             None, FAKE, 1 << 40, None) == -2
+    # fp16 layers go through the direct searches; the Gram path is bf16 only
+    assert f(FAKE, FAKE, L.AWQ_F16, 256, 256, 256, FAKE, g, 3, qc, FAKE, ctypes.byref(a_best), mse,
              None, FAKE, 1 << 40, None) == -2
     assert f(FAKE, FAKE, L.AWQ_BF16, (1 << 22) + 1, 256, 256, FAKE, g, 3, qc, FAKE,
              ctypes.byref(a_best), mse, None, FAKE, 1 << 40, None) == -2

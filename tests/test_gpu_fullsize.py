@@ -56,6 +56,11 @@ def test_llama7b_attn_4096_full(api):
     run_config(api, "llama7b_attn_4096")
 
 
+def test_llama7b_attn_4096_f16_full(api):
+    # the same layer held in fp16: fp16 candidates on the fp16 MFMA, fp16 pack
+    run_config(api, "llama7b_attn_4096_f16")
+
+
 def test_llama7b_mlp_up_full(api):
     # 11008 x 4096, 20 alphas then 20 clip ratios per output channel, then pack
     run_config(api, "llama7b_mlp_up")

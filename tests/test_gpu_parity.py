@@ -70,8 +70,8 @@ def assert_alpha_rule(gpu_idx, ref_mse):
 def model_E(w32, s32, ratio, bits, zp, dtype, group=128):
     """Error weights as the search GEMM consumes them, from the oracle's codes
     and the kernel's float32 arithmetic: fl32(fl32(fl32((q - zero)·step) ·
-    fl32(1/s)) - w), then one RNE rounding to the MFMA operand type (bf16;
-    float32 inputs stay float32)."""
+    fl32(1/s)) - w), then one RNE rounding to the MFMA operand type (bf16 or
+    fp16; float32 inputs stay float32)."""
     q, step, zero = O.quantize(w32, s32, ratio, bits, group, zp)
     N, K = w32.shape
     d = ((q.reshape(N, K // group, group).astype(np.float32) - zero[:, :, None]) * step[:, :, None])
@@ -80,6 +80,8 @@ def model_E(w32, s32, ratio, bits, zp, dtype, group=128):
     e = e.astype(np.float32)
     if dtype == "f32":
         return e.astype(np.float64)
+    if dtype == "f16":
+        return e.astype(np.float16).astype(np.float64)
     return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(e)).astype(np.float64)
 
 
@@ -126,7 +128,7 @@ def compare_rows(gpu_rows, M64, Mm, tol, what):
     worst = _ratio(err, tol)
     assert worst <= 1.0, f"{what}: GPU vs model exceeds the float32 bound ({worst:.2f}x)"
     gap = _ratio(np.abs(Mm - M64), M64)
-    print(f"{what}: |gpu-model|/bound max {worst:.2e}; bf16 operand gap max {gap:.2e}; "
+    print(f"{what}: |gpu-model|/bound max {worst:.2e}; 16-bit operand gap max {gap:.2e}; "
           f"|gpu-oracle|/oracle max {_ratio(np.abs(gpu_rows - M64), M64):.2e}")
 
 
@@ -350,6 +352,31 @@ def test_non_finite_inputs_are_reported(api):
     Wd = to_dev(W, "bf16")
     res = api.search_scale(Xd, Wd, api.act_stats(Xd), synth.alpha_grid(3))
     assert np.all(np.isfinite(res["mse"]))
+
+
+@pytest.mark.parametrize("bits,zp", [(4, True), (3, True), (4, False)])
+def test_search_scale_f16(api, bits, zp):
+    """fp16 layers (fp16 models): the candidates' error weights go to the
+    GEMM as fp16; the model rounds them the same way."""
+    X, W = synth.make_custom(700, 300, 384, "f16", seed=28)
+    res, ref, Xd, Wd = check_scale_search(api, X, W, "f16", synth.alpha_grid(7), bits, zp)
+    s = ref["s_table"][res["index"]]
+    check_clip(api, Xd, Wd, X, W, "f16", s, synth.ratio_grid(6), bits, zp)
+
+
+def test_search_scale_group_f16(api):
+    X, _ = synth.make_custom(600, 8, 256, "f16", seed=29)
+    Ws = [synth.make_weight(n, 256, 0.02, "f16", seed=30 + n) for n in (264, 40)]
+    Xd = to_dev(X, "f16")
+    abar = api.act_stats(Xd)
+    alphas = synth.alpha_grid(5)
+    grp = api.search_scale_group(Xd, [to_dev(w, "f16") for w in Ws], abar, alphas,
+                                 want_row_sums=True)
+    ref = O.search_scale_group(X, Ws, "f16", O.act_stats(X, "f16"), alphas, 4, 128, True)
+    assert np.allclose(grp["mse"], ref["mse"], rtol=MSE_REL, atol=0)
+    stacked = api.search_scale(Xd, to_dev(np.concatenate(Ws), "f16"), abar, alphas,
+                               want_row_sums=True)
+    assert np.array_equal(grp["mse"], stacked["mse"])
 
 
 def test_search_scale_many_token_tiles(api):
