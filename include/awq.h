@@ -196,8 +196,9 @@ awq_status awq_quantize_pack(const void* W, awq_dtype w_dtype, int64_t N, int64_
  * order of the sums differs. Arguments, outputs and synchronisation as in
  * awq_search_scale / awq_search_clip; bf16 inputs only; T <= 2^22. The
  * workspace (awq_workspace_bytes with AWQ_OP_SEARCH_SCALE_GRAM /
- * AWQ_OP_SEARCH_CLIP_GRAM) also holds Xᵀ (K x T, tokens padded to 128) and
- * the [K, 2K] halves of G. */
+ * AWQ_OP_SEARCH_CLIP_GRAM) also holds Xᵀ (K rows of T tokens padded to 128,
+ * plus 64), the build's float32 partial tiles, and G's upper tiles as bf16
+ * hi/lo halves (K x (2K + 256) elements). */
 awq_status awq_search_scale_gram(const void* X, const void* W, awq_dtype dtype, int64_t T,
                                  int64_t N, int64_t K, const float* abar, const float* alphas,
                                  int32_t n_alpha, awq_qconfig qc, float* s_best,

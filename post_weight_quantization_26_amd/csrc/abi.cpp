@@ -107,12 +107,16 @@ hipError_t timed(int kind, hipStream_t st, F&& launch) {
     lk.unlock();
     return launch();
   }
+  // a timing is kept only when both events were created and recorded; the
+  // launch's own status is what the caller sees either way
   hipEvent_t a = take_event(), b = take_event();
-  if (a && b) hipEventRecord(a, st);
+  const bool started = a && b && hipEventRecord(a, st) == hipSuccess;
   hipError_t e = launch();
-  if (a && b) {
-    hipEventRecord(b, st);
+  if (started && hipEventRecord(b, st) == hipSuccess) {
     p.pending.push_back({kind, a, b});
+  } else {
+    if (a) p.spare.push_back(a);
+    if (b) p.spare.push_back(b);
   }
   return e;
 }
@@ -667,7 +671,8 @@ extern "C" void awq_profile_reset(void) {
   Profiler& p = prof();
   std::lock_guard<std::mutex> lk(p.mu);
   for (auto& q : p.pending) {
-    hipEventSynchronize(q.b);
+    // the pending timings are discarded; only wait so the events can be reused
+    (void)hipEventSynchronize(q.b);
     p.spare.push_back(q.a);
     p.spare.push_back(q.b);
   }

@@ -40,7 +40,7 @@ struct SearchLayout {
   size_t scalar;    // [8] f64
   size_t xt;        // Gram searches: [K, Tp] bf16 transposed, token-padded X
   size_t gp;        // Gram searches: [S, U, 256, 256] f32 partial tiles of G
-  size_t gs;        // Gram searches: [K, 2K] bf16 [G_hi | G_lo]
+  size_t gs;        // Gram searches: [K, 2K + 256] bf16, G's upper tiles as hi/lo halves
   size_t total;
   int64_t MT;       // row tiles of the partials (token tiles; Gram: channel tiles)
   int64_t Tp;       // Gram searches: tokens padded to a multiple of 128

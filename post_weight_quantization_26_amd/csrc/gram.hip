@@ -20,7 +20,7 @@
 //     not lose G's precision). Tiles above the diagonal are stored doubled
 //     (exact), and only the upper tiles are stored at all, because
 //       e·G·eᵀ = Σ_tm [ e_tm·G_tm,tm·e_tmᵀ + Σ_{tn > tm} e_tm·(2·G_tm,tn)·e_tnᵀ ]
-//     over the 256-wide index tiles. Row j of Gs [K, 2K] holds, for each
+//     over the 256-wide index tiles. Row j of Gs [K, 2K + 256] holds, for each
 //     128-wide block c of columns, hi then lo of that block:
 //       Gs[j][256·c + w] = hi(G'[j][128·c + w]), Gs[j][256·c + 128 + w] = lo(...)
 //     so row tile tm's part from its diagonal tile on is one contiguous run.
@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// 2. G = Xt·Xtᵀ: upper tiles x token slices, then the slice sum as [G_hi | G_lo]
+// 2. G = Xt·Xtᵀ: upper tiles x token slices, then the slice sum as hi/lo halves
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) {
