@@ -243,10 +243,12 @@ awq_status awq_search_scale_group_gram(const void* X, const void* const* W, cons
 
 /* The consumer of the 3-bit layout (awq_quantize_pack with w_bit = 3): as
  * awq_w4a16_matmul, with qweight [K, N·3/32] and qzeros [K/g, N·3/32] packed
- * densely (N a multiple of 32). Ŵ = (q - z)·scale is formed in float32 and
- * rounded once to the activation type into the workspace (N·K 16-bit values,
- * awq_w3a16_workspace_bytes), then the MFMA GEMM computes Y for any T.
- * Errors and synchronisation as for awq_w4a16_matmul. */
+ * densely (N a multiple of 32). T <= 16: the matrix-core decode of
+ * awq_w4a16_matmul on the exact Ŵ = (q - z)·scale (the workspace holds the
+ * float32 partials). T > 16: Ŵ is formed in float32 and rounded once to the
+ * activation type into the workspace (N·K 16-bit values), then the MFMA GEMM
+ * computes Y. awq_w3a16_workspace_bytes gives the size for each T. Errors and
+ * synchronisation as for awq_w4a16_matmul. */
 size_t awq_w3a16_workspace_bytes(int64_t T, int64_t N, int64_t K, awq_dtype dtype);
 awq_status awq_w3a16_matmul(const void* X, awq_dtype dtype, int64_t T, int64_t N, int64_t K,
                             const int32_t* qweight, const int32_t* qzeros,

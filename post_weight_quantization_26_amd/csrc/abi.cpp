@@ -48,7 +48,7 @@ hipError_t launch_w4a16_gemv(const uint16_t* X, int64_t T, int64_t N, int64_t K,
 hipError_t launch_w4a16_mgemv(const uint16_t* X, int64_t T, int64_t N, int64_t K,
                               const int32_t* qweight, const int32_t* qzeros,
                               const uint16_t* scales, int group, int f16, int64_t kpw,
-                              float* partial, hipStream_t st);
+                              float* partial, hipStream_t st, int bits);
 hipError_t launch_w4a16_gemv_reduce(const float* partial, int64_t chunks, int64_t T, int64_t N,
                                     int f16, uint16_t* Y, hipStream_t st);
 hipError_t launch_stats_accumulate(const void* X, int dtype, int64_t T, int64_t K,
@@ -613,7 +613,7 @@ extern "C" awq_status awq_w4a16_matmul(const void* X, awq_dtype dtype, int64_t T
     AWQ_HIP(timed(AWQ_K_W4A16, st,
                   [&] {
                     return mg ? launch_w4a16_mgemv(x, T, N, K, qweight, qzeros, scales,
-                                                   group_size, f16, kpw, partial, st)
+                                                   group_size, f16, kpw, partial, st, 4)
                               : launch_w4a16_gemv(x, T, N, K, qweight, qzeros, scales,
                                                   group_size, f16, kpw, partial, st);
                   }),
@@ -645,6 +645,24 @@ extern "C" awq_status awq_w3a16_matmul(const void* X, awq_dtype dtype, int64_t T
   if (st_ != AWQ_OK) return st_;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int f16 = dtype == AWQ_F16;
+  if (T <= kW4A16GemvMaxT) {
+    float* partial = static_cast<float*>(ws);
+    const int64_t kpw = w4a16_mgemv_kpw(N, K), chunks = w4a16_mgemv_chunks(N, K);
+    AWQ_HIP(timed(AWQ_K_W4A16, st,
+                  [&] {
+                    return launch_w4a16_mgemv(static_cast<const uint16_t*>(X), T, N, K, qweight,
+                                              qzeros, scales, group_size, f16, kpw, partial, st,
+                                              3);
+                  }),
+            "w3a16 gemv");
+    AWQ_HIP(timed(AWQ_K_W4A16_REDUCE, st,
+                  [&] {
+                    return launch_w4a16_gemv_reduce(partial, chunks, T, N, f16,
+                                                    static_cast<uint16_t*>(Y), st);
+                  }),
+            "w3a16 gemv reduce");
+    return AWQ_OK;
+  }
   uint16_t* Wd = static_cast<uint16_t*>(ws);
   AWQ_HIP(timed(AWQ_K_DEQUANT, st,
                 [&] {

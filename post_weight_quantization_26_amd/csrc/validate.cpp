@@ -399,6 +399,8 @@ extern "C" size_t awq_w3a16_workspace_bytes(int64_t T, int64_t N, int64_t K, awq
   if (T < 1 || N < 1 || K < 1 || T > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
   if (dtype != AWQ_BF16 && dtype != AWQ_F16) return 0;
   if (N % 32 || K % kTileK) return 0;
+  if (T <= kW4A16GemvMaxT)
+    return align_up(size_t(w4a16_mgemv_chunks(N, K)) * size_t(T) * size_t(N) * 4);
   return align_up(size_t(N) * size_t(K) * 2);
 }
 

@@ -14,7 +14,8 @@
 //  * T <= 16 (decode), N a multiple of 16: the codes go to the matrix cores
 //    as exact small numbers (B = 1 + q/16) against the activations, 16 token
 //    rows per v_mfma_f32_16x16x32, and the zero points and scales are applied
-//    to the float32 block sums (w4a16_mgemv_kernel, below).
+//    to the float32 block sums (w4a16_mgemv_kernel, below; also for the
+//    3-bit layout, whose codes a lane pair funnel-shifts into place).
 //  * T <= 16 otherwise: fused float32 GEMV. A lane owns one qweight word
 //    column (8 output channels) and a run of k rows; it dequantises each word
 //    in registers and accumulates T x 8 float32 sums.
@@ -350,9 +351,10 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(
 // 0x3C00 | q << 6). Every x·B has at most 16 significant bits, so the
 // v_mfma_f32_16x16x32 products are exact and P'[t][n] = Σ_k x[t][k]·B[k][n]
 // is an ordinary float32 sum. One more MFMA against a column of ones gives
-// S[t] = Σ_k x[t][k], and Σ_k x·(q − z) = 16·P' − (16 + z)·S. At the end of
-// each group a lane adds scale·fma(−(16 + z), S, 16·P') to its float32
-// totals. Token rows past T are zero operands.
+// S[t] = Σ_k x[t][k], and Σ_k x·(q − z) = 16·P' − (16 + z)·S. After each
+// 32-row k-block a lane adds scale·(P' − ((16 + z)/16)·S) to its float32
+// totals (scaled by 16 once at the end). Token rows past T read row 0 and
+// are never stored.
 //
 // Operand layout (16x16x32): lane l holds 8 consecutive k (k = 8·(l/16) + e)
 // of row l % 16 of A and of column l % 16 of B, and receives D[4·(l/16) + v]
@@ -362,8 +364,9 @@ __global__ __launch_bounds__(256) void w4a16_gemv_kernel(
 // MFMA (c, r) covers output channels 8·(wc + c) + r over the 16 lanes' word
 // columns wc. A is read straight from X (16 bytes per lane and k-block).
 //
-// Workgroup (cb, kc): 4 waves, 32 word columns (256 outputs; a lane owns two
-// adjacent word columns, one 8-byte load per k row), k rows kc·4·kpw ..;
+// Workgroup (cb, kc): 4 waves, 256 outputs (a lane owns 16: two adjacent
+// 4-bit word columns, one 8-byte load per k row, or half of a 3-bit group of
+// 32), k rows kc·4·kpw ..;
 // wave w takes kpw of them (a multiple of 32), and the waves' totals meet in
 // LDS in a fixed order before one float32 partial per (kc, t, n) is stored.
 constexpr int kMgWaves = 4;
@@ -397,6 +400,48 @@ __device__ __forceinline__ uint32_t code_pair(uint32_t w_lo, uint32_t w_hi) {
   return (y & kMask) | kOne;
 }
 
+// The 3-bit layout keeps a 32-row group's codes in 3 words; the two lanes
+// that share a group each load 2 of them (words 0-1 or 1-2) and funnel-shift
+// their 64 bits right by 0 or 16, so that both hold their 16 codes at bits
+// 3r .. 3r+2 of a 48-bit value (lo, hi): codes 0-9 in lo, 11-15 in hi, and
+// code 10 across the two. B = 1 + q/16 for code R of two consecutive k rows,
+// as code_pair: v_perm takes a 2-byte window holding the code from each
+// row's word, one shift puts it at the mantissa bits of q/16 and one and-or
+// masks it and sets the exponent (the bits the shift carries across the
+// halves fall outside the mask).
+template <bool F16, int R>
+__device__ __forceinline__ uint32_t code3_pair(uint32_t lo_a, uint32_t hi_a, uint32_t lo_b,
+                                               uint32_t hi_b, uint32_t one) {
+  constexpr int kLow = F16 ? 6 : 3;          // lowest mantissa bit of q/16
+  constexpr int b = R < 10 ? 3 * R : R > 10 ? 3 * R - 32 : 0;
+  uint32_t wa, wb;
+  if constexpr (R < 10) {
+    wa = lo_a;
+    wb = lo_b;
+  } else if constexpr (R > 10) {
+    wa = hi_a;
+    wb = hi_b;
+  } else {
+    wa = __builtin_amdgcn_alignbit(hi_a, lo_a, 30);
+    wb = __builtin_amdgcn_alignbit(hi_b, lo_b, 30);
+  }
+  constexpr uint32_t B0 = (b >> 3) < 2 ? uint32_t(b >> 3) : 2u;
+  constexpr int kShift = b - 8 * int(B0) - kLow;
+  const uint32_t x =
+      __builtin_amdgcn_perm(wb, wa, B0 | ((B0 + 1u) << 8) | ((B0 + 4u) << 16) | ((B0 + 5u) << 24));
+  const uint32_t y = kShift >= 0 ? (x >> kShift) : (x << -kShift);
+  constexpr uint32_t kMask = (7u << kLow) | (7u << (16 + kLow));
+  return (y & kMask) | one;
+}
+
+// Code r of a lane's aligned 48-bit value (lo, hi), as an integer.
+template <int R>
+__device__ __forceinline__ uint32_t code3_at(uint32_t lo, uint32_t hi) {
+  if constexpr (R < 10) return (lo >> (3 * R)) & 7u;
+  else if constexpr (R > 10) return (hi >> (3 * R - 32)) & 7u;
+  else return __builtin_amdgcn_alignbit(hi, lo, 30) & 7u;
+}
+
 // Registers of one wave: totals per MFMA (c, r); four k-block slots (codes,
 // activations, and the group parameters when the block opens a group: raw
 // fp16 scale pairs and packed zero points), of which three are live at a
@@ -423,21 +468,34 @@ struct MgState {
 // from zero, folded at once: tot += scale·(P' − ((16 + z)/16)·S). That is
 // scale·(16·P' − (16 + z)·S) / 16 with the same rounding; the factor 16 is
 // applied once at the end.
-template <bool F16, int G, int J, class LoadData, class LoadPar>
+template <bool F16, int BITS, int G, int TV, int J, class LoadData, class LoadPar>
 __device__ __forceinline__ void mg_block(MgState<F16>& st, int kb, const LoadData& load_data,
-                                         const LoadPar& load_par) {
+                                         const LoadPar& load_par, uint32_t one) {
   typedef typename Operand<F16>::type V;
   constexpr int BPG = G / 32;
   constexpr bool kFirst = J % BPG == 0;
   constexpr bool kAheadOpens = (J + 2) % BPG == 0;
   constexpr int B = J & 3, BA = (J + 2) & 3;
+  // 3 bits: this lane's funnel shift (0 or 16, by the parity of its group
+  // half)
+  const uint32_t sh3 = (threadIdx.x & 1u) << 4;
   if constexpr (kFirst) {
     st.s0 = st.ps0[B];
     st.s1 = st.ps1[B];
+    if constexpr (BITS == 4) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      st.zf[r] = float(16u + ((st.pz[B].x >> (4 * r)) & 0xFu)) * 0.0625f;
-      st.zf[8 + r] = float(16u + ((st.pz[B].y >> (4 * r)) & 0xFu)) * 0.0625f;
+      for (int r = 0; r < 8; ++r) {
+        st.zf[r] = float(16u + ((st.pz[B].x >> (4 * r)) & 0xFu)) * 0.0625f;
+        st.zf[8 + r] = float(16u + ((st.pz[B].y >> (4 * r)) & 0xFu)) * 0.0625f;
+      }
+    } else {
+      const uint32_t zl = __builtin_amdgcn_alignbit(st.pz[B].y, st.pz[B].x, sh3);
+      const uint32_t zh = st.pz[B].y >> sh3;
+#define AWQ_MG_Z3(R) st.zf[R] = float(16u + code3_at<R>(zl, zh)) * 0.0625f;
+      AWQ_MG_Z3(0) AWQ_MG_Z3(1) AWQ_MG_Z3(2) AWQ_MG_Z3(3) AWQ_MG_Z3(4) AWQ_MG_Z3(5)
+      AWQ_MG_Z3(6) AWQ_MG_Z3(7) AWQ_MG_Z3(8) AWQ_MG_Z3(9) AWQ_MG_Z3(10) AWQ_MG_Z3(11)
+      AWQ_MG_Z3(12) AWQ_MG_Z3(13) AWQ_MG_Z3(14) AWQ_MG_Z3(15)
+#undef AWQ_MG_Z3
     }
   }
   load_data(kb + 32 * (J + 2), st.w[BA], st.a[BA]);
@@ -450,6 +508,31 @@ __device__ __forceinline__ void mg_block(MgState<F16>& st, int kb, const LoadDat
   for (int e = 0; e < 8; ++e) ones[e] = 1;
   const floatx4 sx = mfma16(a, ones, zero);
   const uint32_t sw[8] = {st.s0.x, st.s0.y, st.s0.z, st.s0.w, st.s1.x, st.s1.y, st.s1.z, st.s1.w};
+  if constexpr (BITS == 3) {
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      lo[e] = __builtin_amdgcn_alignbit(st.w[B][e].y, st.w[B][e].x, sh3);
+      hi[e] = st.w[B][e].y >> sh3;
+    }
+#define AWQ_MG_CODE3(R)                                                                     \
+  {                                                                                         \
+    const V b = __builtin_bit_cast(                                                         \
+        V, make_uint4(code3_pair<F16, R>(lo[0], hi[0], lo[1], hi[1], one),                  \
+                      code3_pair<F16, R>(lo[2], hi[2], lo[3], hi[3], one),                  \
+                      code3_pair<F16, R>(lo[4], hi[4], lo[5], hi[5], one),                  \
+                      code3_pair<F16, R>(lo[6], hi[6], lo[7], hi[7], one)));                \
+    const floatx4 p = mfma16(a, b, zero);                                                   \
+    const float sc = f16_to_f32(uint16_t((sw[R >> 1] >> (16 * (R & 1))) & 0xFFFFu));        \
+    for (int v = 0; v < TV; ++v)                                                            \
+      st.tot[R][v] = __builtin_fmaf(sc, __builtin_fmaf(-st.zf[R], sx[v], p[v]), st.tot[R][v]); \
+  }
+    AWQ_MG_CODE3(0) AWQ_MG_CODE3(1) AWQ_MG_CODE3(2) AWQ_MG_CODE3(3)
+    AWQ_MG_CODE3(4) AWQ_MG_CODE3(5) AWQ_MG_CODE3(6) AWQ_MG_CODE3(7)
+    AWQ_MG_CODE3(8) AWQ_MG_CODE3(9) AWQ_MG_CODE3(10) AWQ_MG_CODE3(11)
+    AWQ_MG_CODE3(12) AWQ_MG_CODE3(13) AWQ_MG_CODE3(14) AWQ_MG_CODE3(15)
+#undef AWQ_MG_CODE3
+  } else {
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     uint32_t w[8];
@@ -463,7 +546,7 @@ __device__ __forceinline__ void mg_block(MgState<F16>& st, int kb, const LoadDat
                       code_pair<F16, R>(w[4], w[5]), code_pair<F16, R>(w[6], w[7])));       \
     const floatx4 p = mfma16(a, b, zero);                                                   \
     const float sc = f16_to_f32(uint16_t((sw[m >> 1] >> (16 * (m & 1))) & 0xFFFFu));        \
-    for (int v = 0; v < 4; ++v)                                                             \
+    for (int v = 0; v < TV; ++v)                                                            \
       st.tot[m][v] = __builtin_fmaf(sc, __builtin_fmaf(-st.zf[m], sx[v], p[v]), st.tot[m][v]); \
   }
     if (c == 0) {
@@ -477,9 +560,10 @@ __device__ __forceinline__ void mg_block(MgState<F16>& st, int kb, const LoadDat
     }
 #undef AWQ_MG_CODE
   }
+  }
 }
 
-template <bool F16, int G>
+template <bool F16, int BITS, int G, int TV>
 __global__ __launch_bounds__(256, 2) void w4a16_mgemv_kernel(
     const uint16_t* __restrict__ X, int64_t T, int64_t N, int64_t K,
     const int32_t* __restrict__ qweight, const int32_t* __restrict__ qzeros,
@@ -488,73 +572,102 @@ __global__ __launch_bounds__(256, 2) void w4a16_mgemv_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int jj = lane & 15, lg = lane >> 4;
-  const int64_t N8 = N / 8;
-  // The lane's two word columns. Lanes past N (N8 is even: both columns or
-  // neither) and token rows past T read column 0 / row 0 instead: every load
-  // stays in bounds and needs no branch, and an MFMA output column depends
-  // only on its own B column (an output row on its own A row), so those
-  // lanes' results, which are never stored, do not reach the others.
-  const int64_t wc = int64_t(blockIdx.x) * kMgCols + 2 * jj;
-  const int64_t wcl = wc < N8 ? wc : 0;
+  // Words per k row, and the lane's 16 output rows n0 .. n0 + 15: 4 bits, two
+  // adjacent word columns (one 8-byte load per k row); 3 bits, half of a
+  // 32-row group, words 0-1 (even jj) or 1-2 (odd jj) of its 3 (two 4-byte
+  // loads). Lanes past N (N a multiple of 16, or of 32 for 3 bits: whole
+  // lanes, whole lane pairs) and token rows past T read column 0 / row 0
+  // instead: every load stays in bounds and needs no branch, and an MFMA
+  // output column depends only on its own B column (an output row on its own
+  // A row), so those lanes' results, which are never stored, do not reach the
+  // others.
+  const int64_t RS = BITS == 4 ? N / 8 : N / 32 * 3;
+  // Workgroups are dealt to the 8 XCDs in turn, and each XCD has its own L2.
+  // XCD i takes a contiguous run of (column block, chunk) indices, column
+  // blocks fastest, so neighbouring column blocks, whose qweight row
+  // segments can share cache lines (3 bits: 96 bytes per row and block),
+  // meet in one L2.
+  int bx, by;
+  {
+    const int W = int(gridDim.x) * int(gridDim.y);
+    const int id = int(blockIdx.x) + int(gridDim.x) * int(blockIdx.y);
+    const int q = W / 8, r = W % 8, xi = id % 8;
+    const int L = xi * q + (xi < r ? xi : r) + id / 8;
+    bx = L % int(gridDim.x);
+    by = L / int(gridDim.x);
+  }
+  const int64_t n0 = int64_t(bx) * (kMgCols * 8) + 16 * jj;
+  const bool live = n0 < N;
+  const int64_t nl0 = live ? n0 : 0;
+  const int64_t wq = !live ? 0 : BITS == 4 ? n0 / 8 : 3 * (n0 / 32) + (jj & 1);
   // This wave's k rows: kpw (a multiple of 128) from its place in the grid,
   // cut at K (a multiple of 128); waves past K have none.
-  const int kw0 = (int(blockIdx.y) * kMgWaves + wave) * kpw;
+  const int kw0 = (by * kMgWaves + wave) * kpw;
   const int kw1 = kw0 + kpw < int(K) ? kw0 + kpw : int(K);
   const uint16_t* xrow = X + int64_t(jj < T ? jj : 0) * K + 8 * lg;
-  const int32_t* qlane = qweight + int64_t(8 * lg) * N8 + wcl;
+  const int32_t* qlane = qweight + int64_t(8 * lg) * RS + wq;
+  auto load2 = [](const int32_t* p) {
+    if constexpr (BITS == 4) return *reinterpret_cast<const uint2*>(p);
+    else return make_uint2(uint32_t(p[0]), uint32_t(p[1]));
+  };
 
   MgState<F16> st;
 #pragma unroll
   for (int m = 0; m < kMgMfma; ++m) st.tot[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // The exponent bits of B = 1 + q/16, held in a register so that the 3-bit
+  // operand's mask and or fuse into one instruction.
+  uint32_t one = F16 ? 0x3C003C00u : 0x3F803F80u;
+  asm volatile("" : "+v"(one));
   if (kw0 < kw1) {
     // k-blocks past the wave's last re-read its last block (a harmless
     // in-bounds prefetch)
     auto load_data = [&](int kb, uint2 (&w)[8], uint4& a) {
       const int kc = kb < kw1 ? kb : kw1 - 32;
-      const int32_t* q = qlane + int64_t(kc) * N8;
+      const int32_t* q = qlane + int64_t(kc) * RS;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) w[e] = *reinterpret_cast<const uint2*>(q + e * N8);
+      for (int e = 0; e < 8; ++e) w[e] = load2(q + e * RS);
       a = *reinterpret_cast<const uint4*>(xrow + kc);
     };
     auto load_par = [&](int kb, uint4& s0, uint4& s1, uint2& z) {
       const int64_t g = (kb < kw1 ? kb : kw1 - 32) / G;
-      s0 = *reinterpret_cast<const uint4*>(scales + g * N + 8 * wcl);
-      s1 = *reinterpret_cast<const uint4*>(scales + g * N + 8 * wcl + 8);
-      z = *reinterpret_cast<const uint2*>(qzeros + g * N8 + wcl);
+      s0 = *reinterpret_cast<const uint4*>(scales + g * N + nl0);
+      s1 = *reinterpret_cast<const uint4*>(scales + g * N + nl0 + 8);
+      z = load2(qzeros + g * RS + wq);
     };
     load_data(kw0, st.w[0], st.a[0]);
     load_par(kw0, st.ps0[0], st.ps1[0], st.pz[0]);
     load_data(kw0 + 32, st.w[1], st.a[1]);
     if (G == 32) load_par(kw0 + 32, st.ps0[1], st.ps1[1], st.pz[1]);
     for (int kb = kw0; kb < kw1; kb += 128) {
-      mg_block<F16, G, 0>(st, kb, load_data, load_par);
+      mg_block<F16, BITS, G, TV, 0>(st, kb, load_data, load_par, one);
       __builtin_amdgcn_sched_barrier(0);
-      mg_block<F16, G, 1>(st, kb, load_data, load_par);
+      mg_block<F16, BITS, G, TV, 1>(st, kb, load_data, load_par, one);
       __builtin_amdgcn_sched_barrier(0);
-      mg_block<F16, G, 2>(st, kb, load_data, load_par);
+      mg_block<F16, BITS, G, TV, 2>(st, kb, load_data, load_par, one);
       __builtin_amdgcn_sched_barrier(0);
-      mg_block<F16, G, 3>(st, kb, load_data, load_par);
+      mg_block<F16, BITS, G, TV, 3>(st, kb, load_data, load_par, one);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
   for (int m = 0; m < kMgMfma; ++m)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) st.tot[m][v] *= 16.f;
+    for (int v = 0; v < TV; ++v) st.tot[m][v] *= 16.f;
 
-  // totals -> LDS [wave][t][n_local], n_local = 8·(2·jj + c) + r
+  // totals -> LDS [wave][t][n_local], n_local = 16·jj + m (rows 4·lg + v
+  // for v < TV: with TV < 4, T <= TV and only lane group 0's rows are read)
 #pragma unroll
   for (int m = 0; m < kMgMfma; ++m)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave][4 * lg + v][16 * jj + m] = st.tot[m][v];
+    for (int v = 0; v < TV; ++v) red[wave][4 * lg + v][16 * jj + m] = st.tot[m][v];
   __syncthreads();
   const int nl = threadIdx.x;
-  const int64_t n = int64_t(blockIdx.x) * kMgCols * 8 + nl;
+  const int64_t n = int64_t(bx) * kMgCols * 8 + nl;
   if (n < N) {
     for (int t = 0; t < T; ++t) {
       const float s = ((red[0][t][nl] + red[1][t][nl]) + red[2][t][nl]) + red[3][t][nl];
-      partial[(int64_t(blockIdx.y) * T + t) * N + n] = s;
+      partial[(int64_t(by) * T + t) * N + n] = s;
     }
   }
 }
@@ -669,37 +782,66 @@ hipError_t launch_w4a16_gemv(const uint16_t* X, int64_t T, int64_t N, int64_t K,
   return hipGetLastError();
 }
 
-// 1 <= T <= 16 token rows; N a multiple of 16, qweight and qzeros 8-byte
-// aligned; K a multiple of 128; kpw a multiple of 128; partial holds
-// ceil(K / (4·kpw)) x T x N floats.
-template <bool F16>
+// 1 <= T <= 16 token rows; K a multiple of 128; kpw a multiple of 128;
+// partial holds ceil(K / (4·kpw)) x T x N floats. 4 bits: N a multiple of
+// 16, qweight and qzeros 8-byte aligned; 3 bits: N a multiple of 32.
+template <bool F16, int BITS, int TV>
+void launch_mgemv_tv(int group, dim3 grid, hipStream_t st, const uint16_t* X, int64_t T,
+                     int64_t N, int64_t K, const int32_t* qweight, const int32_t* qzeros,
+                     const uint16_t* scales, int kpw, float* partial) {
+  if (group == 32)
+    w4a16_mgemv_kernel<F16, BITS, 32, TV><<<grid, 256, 0, st>>>(X, T, N, K, qweight, qzeros,
+                                                                scales, kpw, partial);
+  else if (group == 64)
+    w4a16_mgemv_kernel<F16, BITS, 64, TV><<<grid, 256, 0, st>>>(X, T, N, K, qweight, qzeros,
+                                                                scales, kpw, partial);
+  else
+    w4a16_mgemv_kernel<F16, BITS, 128, TV><<<grid, 256, 0, st>>>(X, T, N, K, qweight, qzeros,
+                                                                 scales, kpw, partial);
+}
+
+// The MFMA's output rows are token rows 4·(lane / 16) + v; with T <= 2 only
+// v < T of lane group 0 are stored, so the scale and zero-point fold runs on
+// TV = T rows (else all 4).
+template <bool F16, int BITS>
 void launch_mgemv_g(int group, dim3 grid, hipStream_t st, const uint16_t* X, int64_t T, int64_t N,
                     int64_t K, const int32_t* qweight, const int32_t* qzeros,
                     const uint16_t* scales, int kpw, float* partial) {
-  if (group == 32)
-    w4a16_mgemv_kernel<F16, 32><<<grid, 256, 0, st>>>(X, T, N, K, qweight, qzeros, scales, kpw,
-                                                      partial);
-  else if (group == 64)
-    w4a16_mgemv_kernel<F16, 64><<<grid, 256, 0, st>>>(X, T, N, K, qweight, qzeros, scales, kpw,
-                                                      partial);
+  if (T == 1)
+    launch_mgemv_tv<F16, BITS, 1>(group, grid, st, X, T, N, K, qweight, qzeros, scales, kpw,
+                                  partial);
+  else if (T == 2)
+    launch_mgemv_tv<F16, BITS, 2>(group, grid, st, X, T, N, K, qweight, qzeros, scales, kpw,
+                                  partial);
   else
-    w4a16_mgemv_kernel<F16, 128><<<grid, 256, 0, st>>>(X, T, N, K, qweight, qzeros, scales, kpw,
-                                                       partial);
+    launch_mgemv_tv<F16, BITS, 4>(group, grid, st, X, T, N, K, qweight, qzeros, scales, kpw,
+                                  partial);
 }
 
 hipError_t launch_w4a16_mgemv(const uint16_t* X, int64_t T, int64_t N, int64_t K,
                               const int32_t* qweight, const int32_t* qzeros,
                               const uint16_t* scales, int group, int f16, int64_t kpw,
-                              float* partial, hipStream_t st) {
-  if (T < 1 || T > 16 || N % 16 || K % 128 || kpw < 128 || kpw % 128 || K > (int64_t(1) << 30) ||
-      (group != 32 && group != 64 && group != 128))
+                              float* partial, hipStream_t st, int bits) {
+  if (T < 1 || T > 16 || N % (bits == 3 ? 32 : 16) || K % 128 || kpw < 128 || kpw % 128 ||
+      K > (int64_t(1) << 30) || (group != 32 && group != 64 && group != 128) ||
+      (bits != 3 && bits != 4))
     return hipErrorInvalidValue;
   const int64_t chunks = (K + kMgWaves * kpw - 1) / (kMgWaves * kpw);
-  dim3 grid(unsigned((N / 8 + kMgCols - 1) / kMgCols), unsigned(chunks));
-  if (f16)
-    launch_mgemv_g<true>(group, grid, st, X, T, N, K, qweight, qzeros, scales, int(kpw), partial);
-  else
-    launch_mgemv_g<false>(group, grid, st, X, T, N, K, qweight, qzeros, scales, int(kpw), partial);
+  dim3 grid(unsigned((N + kMgCols * 8 - 1) / (kMgCols * 8)), unsigned(chunks));
+  if (bits == 3) {
+    if (f16)
+      launch_mgemv_g<true, 3>(group, grid, st, X, T, N, K, qweight, qzeros, scales, int(kpw),
+                              partial);
+    else
+      launch_mgemv_g<false, 3>(group, grid, st, X, T, N, K, qweight, qzeros, scales, int(kpw),
+                               partial);
+  } else if (f16) {
+    launch_mgemv_g<true, 4>(group, grid, st, X, T, N, K, qweight, qzeros, scales, int(kpw),
+                            partial);
+  } else {
+    launch_mgemv_g<false, 4>(group, grid, st, X, T, N, K, qweight, qzeros, scales, int(kpw),
+                             partial);
+  }
   return hipGetLastError();
 }
 

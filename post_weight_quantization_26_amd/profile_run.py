@@ -89,7 +89,7 @@ def w4a16(reps: int) -> None:
         s = torch.ones(K, dtype=torch.float32, device=dev)
         qw, qz, sc = api.quantize_pack(W, s, bits=bits)
         del W
-        for T in ((1, 4, 16, 4096) if bits == 4 else (1, 4096)):
+        for T in (1, 4, 16, 4096):
             X = torch.randn((T, K), generator=g, device=dev).to(torch.bfloat16)
             need = (api.w4a16_workspace_bytes if bits == 4 else api.w3a16_workspace_bytes)(
                 T, N, K, torch.bfloat16)
@@ -108,7 +108,7 @@ def w4a16(reps: int) -> None:
             main_us = t["w4a16"][0] * 1e3 / n_rep
             rec = {"N": N, "K": K, "T": T, "bits": bits, "main_kernel_us": round(main_us, 2)}
             packed = N * K * bits // 8 + (N * K // 128) * (2 + bits / 8)
-            if T <= 16 and bits == 4:
+            if T <= 16:
                 # what any decode kernel must move: the packed layer, X and Y
                 moved = packed + T * K * 2 + T * N * 2
                 rec.update(path="gemv", reduce_us=round(t["w4a16_reduce"][0] * 1e3 / n_rep, 2),

@@ -268,7 +268,12 @@ def test_profile_kinds_match_header(L):
 def test_w3a16_workspace_and_rejects(L):
     lib = L.lib()
     wsb = lib.awq_w3a16_workspace_bytes
-    assert wsb(1, 4096, 4096, L.AWQ_BF16) == 4096 * 4096 * 2      # Ŵ rows for every T
+    # decode (T <= 16): float32 partials per k chunk, token row and output row
+    one = wsb(1, 4096, 4096, L.AWQ_BF16)
+    assert one > 0 and one % (4096 * 4) == 0 and one <= 32 * 4096 * 4
+    assert wsb(16, 4096, 4096, L.AWQ_F16) == 16 * one
+    # prefill: the dequantised [N, K] operand rows
+    assert wsb(17, 4096, 4096, L.AWQ_BF16) == 4096 * 4096 * 2
     assert wsb(4096, 4096, 4096, L.AWQ_F16) == 4096 * 4096 * 2
     assert wsb(1, 4104, 4096, L.AWQ_BF16) == 0                     # N not a multiple of 32
     assert wsb(1, 4096, 4096, L.AWQ_F32) == 0

@@ -60,8 +60,7 @@ def packed_layer(N, K, group, seed, bits=4):
 
 
 def check_consumer(api, T, N, K, group, dtype, seed, bits=4):
-    """bits 4: exact-Ŵ decode for T <= 16, 16-bit Ŵ GEMM above; bits 3: the
-    16-bit Ŵ GEMM for every T."""
+    """Exact-Ŵ decode for T <= 16, 16-bit Ŵ GEMM above (both bit widths)."""
     qw, qz, sc = packed_layer(N, K, group, seed, bits)
     rng = np.random.default_rng(seed + 1)
     x32 = rng.standard_normal((T, K)).astype(np.float32)
@@ -70,7 +69,7 @@ def check_consumer(api, T, N, K, group, dtype, seed, bits=4):
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
     Y = api.w4a16_matmul(Xd, dev(qw), dev(qz), dev(sc).view(torch.float16), group=group,
                          bits=bits)
-    decode = T <= 16 and bits == 4
+    decode = T <= 16
     torch.cuda.synchronize()
     y = Y.float().cpu().numpy().astype(np.float64)
     x = _dec(X, dtype).astype(np.float64)
@@ -82,8 +81,8 @@ def check_consumer(api, T, N, K, group, dtype, seed, bits=4):
         w_op = _dec(_enc(w32, dtype), dtype).astype(np.float64)
     y_model = x @ w_op.T
     if decode:
-        q = O.unpack_codes(qw, N, 4).astype(np.float64)                  # [K, N]
-        z = np.repeat(O.unpack_codes(qz, N, 4), group, axis=0).astype(np.float64)
+        q = O.unpack_codes(qw, N, bits).astype(np.float64)               # [K, N]
+        z = np.repeat(O.unpack_codes(qz, N, bits), group, axis=0).astype(np.float64)
         scl = np.repeat(sc.view(np.float16).astype(np.float64), group, axis=0)
         mag = np.abs(x) @ ((32.0 + q + z) * scl)
         g = (K + 4) * U32 / (1 - (K + 4) * U32)
@@ -118,11 +117,12 @@ def test_gemv_large(api):
 
 
 # N a multiple of 16: the matrix-core decode path (k runs of 128 rows per
-# wave, 4 waves per chunk). K = 384: one chunk whose fourth wave has no rows;
+# wave, 4 waves per chunk; T = 1 and 2 fold only the stored token rows). K =
+# 384: one chunk whose fourth wave has no rows;
 # K = 1152: the third chunk has rows for its first wave only; K = 128: one
 # busy wave. N = 272 leaves 2 of the last workgroup's 32 word columns; N =
 # 4112 makes 17 workgroups of columns.
-@pytest.mark.parametrize("T", [1, 3, 8, 16])
+@pytest.mark.parametrize("T", [1, 2, 3, 8, 16])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_mgemv_path(api, T, dtype):
     check_consumer(api, T, 272, 1152, 128, dtype, seed=150 + T)
@@ -164,11 +164,32 @@ def test_gemm_many_tiles(api):
 
 
 # 3-bit layout: codes 10 and 21 of each 32 straddle two words; N = 288 is 9
-# groups of 32 rows and a ragged 256-row GEMM tile
+# groups of 32 rows: a ragged 256-row GEMM tile, and a second decode
+# workgroup with one live lane pair of 8
 @pytest.mark.parametrize("T", [1, 16, 300])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_w3a16_consumer(api, T, dtype):
     check_consumer(api, T, 288, 384, 128, dtype, seed=180 + T, bits=3)
+
+
+# 3-bit decode on the matrix cores: T across 1..16, ragged k chunks (K =
+# 1152: the third chunk has rows for its first wave only), N = 4128 (17
+# workgroups, the last with one group of 32 rows), every group size
+@pytest.mark.parametrize("T", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_w3a16_decode(api, T, dtype):
+    check_consumer(api, T, 4128, 1152, 128, dtype, seed=210 + T, bits=3)
+
+
+@pytest.mark.parametrize("group", [32, 64])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_w3a16_decode_group_sizes(api, group, dtype):
+    check_consumer(api, 5, 544, 384, group, dtype, seed=220 + group, bits=3)
+
+
+@pytest.mark.parametrize("K", [128, 4096])
+def test_w3a16_decode_k_spans(api, K):
+    check_consumer(api, 16, 1024, K, 128, "bf16", seed=230 + K // 128, bits=3)
 
 
 @pytest.mark.parametrize("group", [32, 64])
