@@ -318,12 +318,17 @@ awq_status awq_fold_linear(void* W_prev, void* bias_prev, awq_dtype dtype, int64
  * X [T, K] holds the activations already divided by s (the fold), bf16 or
  * fp16; Y [T, N] is written in the same type. Ŵ is formed exactly in
  * float32; sums are float32, each output rounded once to nearest even.
- * T <= 16 runs a fused GEMV (Ŵ never stored); larger T dequantises Ŵ once
- * into the workspace, rounded to the activation type, and runs an MFMA GEMM.
+ * T <= 16 runs a fused GEMV (Ŵ never stored). Larger T forms Ŵ rounded
+ * once to the activation type for an MFMA GEMM, in one of two ways:
+ *  - with ws_bytes >= awq_w4a16_workspace_bytes(T, N, K, dtype) (N·K 16-bit
+ *    values), Ŵ is dequantised into the workspace first (the faster path);
+ *  - with a smaller workspace (ws may then be NULL and ws_bytes 0) and
+ *    K·N/2 < 2^31, the GEMM dequantises each k-tile on the fly and uses no
+ *    workspace. Both give the same Y bit for bit.
  * N a multiple of 8, K of 128; group_size 32, 64 or 128. X and scales
- * 16-byte aligned, qweight and qzeros 4-byte, Y 2-byte. ws: at least
- * awq_w4a16_workspace_bytes(T, N, K, dtype), 16-byte aligned.
- * Does not synchronise. */
+ * 16-byte aligned, qweight and qzeros 4-byte, Y 2-byte, ws 16-byte.
+ * A workspace too small for T <= 16, or for a layer the on-the-fly GEMM
+ * cannot address: AWQ_E_WORKSPACE. Does not synchronise. */
 size_t awq_w4a16_workspace_bytes(int64_t T, int64_t N, int64_t K, awq_dtype dtype);
 awq_status awq_w4a16_matmul(const void* X, awq_dtype dtype, int64_t T, int64_t N, int64_t K,
                             const int32_t* qweight, const int32_t* qzeros,

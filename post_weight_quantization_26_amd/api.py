@@ -316,11 +316,12 @@ def w3a16_workspace_bytes(T: int, N: int, K: int, dtype) -> int:
 def w4a16_matmul(X: torch.Tensor, qweight: torch.Tensor, qzeros: torch.Tensor,
                  scales: torch.Tensor, group: int = DEFAULT_GROUP,
                  ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                 bits: int = 4):
+                 bits: int = 4, on_the_fly: bool = False):
     """Y = X·Ŵᵀ for a packed layer (bits 4: qweight [K, N/8], qzeros
     [K/g, N/8]; bits 3: [K, 3N/32] and [K/g, 3N/32]; scales [K/g, N] float16)
     and activations X [T, K] (bf16 or float16, already divided by s). Returns
-    Y [T, N] in X's dtype."""
+    Y [T, N] in X's dtype. on_the_fly (4 bits, T > 16): the GEMM dequantises
+    as it goes and takes no workspace (same result, slower)."""
     _dev(X, "X"), _dev(qweight, "qweight"), _dev(qzeros, "qzeros"), _dev(scales, "scales")
     if bits not in (3, 4):
         raise ValueError("bits must be 3 or 4")
@@ -335,6 +336,10 @@ def w4a16_matmul(X: torch.Tensor, qweight: torch.Tensor, qzeros: torch.Tensor,
         fn, need = L.lib().awq_w4a16_matmul, w4a16_workspace_bytes(T, N, K, X.dtype)
     else:
         fn, need = L.lib().awq_w3a16_matmul, w3a16_workspace_bytes(T, N, K, X.dtype)
+    if on_the_fly and bits == 4 and T > 16:
+        L.check(fn(_ptr(X), _dtype(X), T, N, K, _ptr(qweight), _ptr(qzeros), _ptr(scales),
+                   int(group), _ptr(Y), None, 0, _stream()))
+        return Y
     ws = _workspace(ws, need, X.device)
     L.check(fn(_ptr(X), _dtype(X), T, N, K, _ptr(qweight), _ptr(qzeros), _ptr(scales), int(group),
                _ptr(Y), _ptr(ws), ws.numel(), _stream()))

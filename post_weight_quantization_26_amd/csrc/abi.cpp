@@ -49,6 +49,9 @@ hipError_t launch_w4a16_mgemv(const uint16_t* X, int64_t T, int64_t N, int64_t K
                               const int32_t* qweight, const int32_t* qzeros,
                               const uint16_t* scales, int group, int f16, int64_t kpw,
                               float* partial, hipStream_t st, int bits);
+hipError_t launch_w4a16_gemm_q(const uint16_t* X, const int32_t* qweight, const int32_t* qzeros,
+                               const uint16_t* scales, int64_t M, int64_t N, int64_t K,
+                               int group, int f16, uint16_t* Y, hipStream_t st);
 hipError_t launch_w4a16_gemv_reduce(const float* partial, int64_t chunks, int64_t T, int64_t N,
                                     int f16, uint16_t* Y, hipStream_t st);
 hipError_t launch_stats_accumulate(const void* X, int dtype, int64_t T, int64_t K,
@@ -621,6 +624,16 @@ extern "C" awq_status awq_w4a16_matmul(const void* X, awq_dtype dtype, int64_t T
     AWQ_HIP(timed(AWQ_K_W4A16_REDUCE, st,
                   [&] { return launch_w4a16_gemv_reduce(partial, chunks, T, N, f16, y, st); }),
             "w4a16 gemv reduce");
+    return AWQ_OK;
+  }
+  if (ws_bytes < awq_w4a16_workspace_bytes(T, N, K, dtype)) {
+    // (the checks admitted it only where the fused GEMM fits)
+    AWQ_HIP(timed(AWQ_K_W4A16, st,
+                  [&] {
+                    return launch_w4a16_gemm_q(x, qweight, qzeros, scales, T, N, K, group_size,
+                                               f16, y, st);
+                  }),
+            "w4a16 gemm");
     return AWQ_OK;
   }
   uint16_t* Wd = static_cast<uint16_t*>(ws);

@@ -122,6 +122,11 @@ inline bool w4a16_use_mgemv(int64_t N, const void* qweight, const void* qzeros) 
   return N % 16 == 0 && (reinterpret_cast<uintptr_t>(qweight) & 7u) == 0 &&
          (reinterpret_cast<uintptr_t>(qzeros) & 7u) == 0;
 }
+// The prefill GEMM that dequantises on the fly addresses qweight with 32-bit
+// buffer offsets: K·N/2 < 2^31 bytes.
+inline bool w4a16_fused_fits(int64_t N, int64_t K) {
+  return K * (N / 8) * 4 < (int64_t(1) << 31);
+}
 int64_t w4a16_mgemv_kpw(int64_t N, int64_t K);
 inline int64_t w4a16_mgemv_chunks(int64_t N, int64_t K) {
   const int64_t span = 4 * w4a16_mgemv_kpw(N, K);

@@ -77,7 +77,8 @@ constexpr int wait_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) 
 constexpr int kWaitLgkm0 = 0xF | (3 << 14) | (0x7 << 4);
 
 // Masks for __builtin_amdgcn_sched_group_barrier.
-constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100;
+constexpr int kSgValu = 0x002, kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100,
+              kSgDsWrite = 0x200;
 
 // Workgroup barrier that neither the compiler nor the scheduler may move a
 // memory operation or any instruction across. Unlike __syncthreads() it adds

@@ -343,6 +343,8 @@ awq_status check_w4a16(const void* X, awq_dtype d, int64_t T, int64_t N, int64_t
     return set_error(AWQ_E_INVALID,
                      "w4a16_matmul: X and scales must be 16-byte aligned, qweight/qzeros 4, Y 2");
   const size_t need = awq_w4a16_workspace_bytes(T, N, K, d);
+  // prefill with a smaller workspace (or none): the GEMM dequantises on the fly
+  if (T > kW4A16GemvMaxT && ws_bytes < need && w4a16_fused_fits(N, K)) return AWQ_OK;
   if (!ws || !aligned16(ws) || ws_bytes < need)
     return set_error(AWQ_E_WORKSPACE, "w4a16_matmul: workspace needs %zu bytes (16-byte aligned)",
                      need);

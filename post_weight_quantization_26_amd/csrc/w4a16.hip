@@ -234,6 +234,266 @@ void w4a16_gemm_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
+// prefill, dequantising on the fly: X tiles through the LDS-DMA ring, the B
+// tile from the packed layer through registers
+// ---------------------------------------------------------------------------
+//
+// Same tiles, ring, fragment reads and MFMAs as the search GEMM's main loop
+// (gemm_core.h); only the B operand's way into LDS differs. For each 32-wide
+// k-tile a lane loads 4 qweight words (k rows 4·kq .. 4·kq + 3 of the tile,
+// word column c8 of the output tile: outputs n0 + 8·c8 .. + 7), its group's
+// zero-point word and 8 fp16 scales, two k-tiles ahead of use. One region
+// before the MFMAs read the k-tile it forms Ŵ = (q − z)·scale exactly as the
+// dequantisation pass does (fma(q, scale, −z·scale), whose one rounding is
+// that of (q − z)·scale because z·scale is exact), rounds it once to the
+// 16-bit type and writes 4 k x 1 output row per 8-byte LDS store into the
+// ring's swizzled layout. Lanes pair up over word columns (kq = 2·wave +
+// lane % 2, c8 = (lane / 2) % 32), and lane c8 takes its nibbles in the order
+// r + (c8 / 2) (mod 8) (its words and scales rotated by that much), so the
+// 32 lanes that share a store cycle hit 32 different bank pairs.
+struct QLoad {
+  uint32_t w[4];
+  uint32_t z;
+  uint4 s;
+};
+
+struct QCtx {
+  __amdgpu_buffer_rsrc_t rsA, rsQ, rsZ, rsS;
+  int voffA[4];
+  int wave, KT, oobA;
+  int rdA[2], rdB[2];
+  uint32_t qoff, qrow, ktq;  // bytes: lane's word at k-tile 0; per k row; per k-tile
+  uint32_t zoff, soff, zrow, srow;  // bytes: lane's group-0 entries; per group row
+  int gshift;                // k-tiles per group = 1 << gshift
+  uint32_t rot;              // nibble rotation in bits (4·((c8 / 2) % 8))
+  uint32_t oobm;             // 0, or bit 31 for a lane whose word column is past N
+  int wofs[8];               // LDS byte offset within a stage of store r
+};
+
+constexpr uint32_t kQOob = 0x80000000u;  // past every buffer: loads read zero
+
+template <int S>
+__device__ __forceinline__ void dma_a(const QCtx& c, int kt) {
+  const int kofs = kt < c.KT ? kt * (BK * 2) : c.oobA;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsA, AWQ_LDS(stage_a<S>() + (c.wave * 4 + j) * 64),
+                                             16, c.voffA[j] + kofs, 0, 0, 0);
+}
+
+// Packed k-tile kt of this lane. Past the last k-tile the offsets pass the
+// end of each buffer, and lanes past N set bit 31 (c.oobm), so those loads
+// read zeros; they are never used. (No selects on the offsets: the compiler
+// would turn them into branches that split the loop body.)
+__device__ __forceinline__ void load_q(const QCtx& c, int kt, QLoad& q) {
+  const uint32_t base = c.qoff + uint32_t(kt) * c.ktq;
+  const uint32_t g = uint32_t(kt >> c.gshift);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    q.w[i] = __builtin_amdgcn_raw_buffer_load_b32(c.rsQ, (base + i * c.qrow) | c.oobm, 0, 0);
+  q.z = __builtin_amdgcn_raw_buffer_load_b32(c.rsZ, (c.zoff + g * c.zrow) | c.oobm, 0, 0);
+  const auto sv =
+      __builtin_amdgcn_raw_buffer_load_b128(c.rsS, (c.soff + g * c.srow) | c.oobm, 0, 0);
+  q.s = make_uint4(sv[0], sv[1], sv[2], sv[3]);
+}
+
+// Ŵ of one packed k-tile into stage S.
+template <bool F16, int S>
+__device__ __forceinline__ void dq_write(const QCtx& c, const QLoad& q) {
+#pragma clang fp contract(off)
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_alignbit(q.w[i], q.w[i], c.rot);
+  const uint32_t z = __builtin_amdgcn_alignbit(q.z, q.z, c.rot);
+  // the 8 scales rotated by rot / 4 positions: by 2 words, by 1 word, by a half
+  // (selects, not branches: the loop body stays one block for the scheduler)
+  const bool r16 = c.rot & 16u, r8 = c.rot & 8u, r4 = c.rot & 4u;
+  const uint32_t a0 = r16 ? q.s.z : q.s.x, a1 = r16 ? q.s.w : q.s.y;
+  const uint32_t a2 = r16 ? q.s.x : q.s.z, a3 = r16 ? q.s.y : q.s.w;
+  const uint32_t b0 = r8 ? a1 : a0, b1 = r8 ? a2 : a1, b2 = r8 ? a3 : a2, b3 = r8 ? a0 : a3;
+  const uint32_t sw[4] = {r4 ? __builtin_amdgcn_alignbit(b1, b0, 16) : b0,
+                          r4 ? __builtin_amdgcn_alignbit(b2, b1, 16) : b1,
+                          r4 ? __builtin_amdgcn_alignbit(b3, b2, 16) : b2,
+                          r4 ? __builtin_amdgcn_alignbit(b0, b3, 16) : b3};
+  char* stage = reinterpret_cast<char*>(stage_b<S>());
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const float sc = f16_to_f32(uint16_t((sw[r >> 1] >> (16 * (r & 1))) & 0xFFFFu));
+    const float nzs = -float((z >> (4 * r)) & 0xFu) * sc;
+    uint16_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      h[i] = to16<F16>(__builtin_fmaf(float((w[i] >> (4 * r)) & 0xFu), sc, nzs));
+    *reinterpret_cast<uint2*>(stage + c.wofs[r]) =
+        make_uint2(uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16));
+  }
+}
+
+// Region kt (stage S = kt % 4): DMA of X's k-tile kt + 3; MFMAs of (kt - 1,
+// k-step 1) while (kt, 0) is read; Ŵ of k-tile kt + 3 from its slot into
+// stage (S + 3) % 4 (last read in region kt - 1) and the slot refilled with
+// k-tile kt + 5; MFMAs of (kt, 0) while (kt, 1) is read. At the end this
+// wave's LDS traffic is done and X's k-tile kt + 1 has landed: its copies
+// were issued in region kt - 2, and regions kt - 1 and kt issued 10 loads
+// each (whatever order the compiler gives a region's loads).
+template <bool F16, int S, bool PREV, class V>
+__device__ __forceinline__ void region_q(const QCtx& c, int kt, floatx16 (&acc)[4][4],
+                                         V (&f0a)[4], V (&f0b)[4], V (&f1a)[4], V (&f1b)[4],
+                                         QLoad (&slot)[2]) {
+  dma_a<(S + 3) & 3>(c, kt + 3);
+  if (PREV) mfma_4x4(acc, f1a, f1b);
+  read_frags<S>(c, 0, f0a, f0b);
+  dq_write<F16, (S + 3) & 3>(c, slot[(S + 3) & 1]);
+  load_q(c, kt + 5, slot[(S + 3) & 1]);
+  mfma_4x4(acc, f0a, f0b);
+  read_frags<S>(c, 1, f1a, f1b);
+  // The dequantisation's ~190 VALU instructions and 8 LDS stores are spread
+  // over the 32 MFMAs (a few per MFMA) instead of idling the matrix cores in
+  // one block.
+  if (PREV) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgValu, 6, 0);
+      if (i & 1) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgValu, 6, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgValu, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsWrite, 1, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgValu, 4, 0);
+    if (i < 6) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_waitcnt(wait_vm(20));
+  region_barrier();
+}
+
+template <bool F16>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void w4a16_gemm_q_kernel(const uint16_t* __restrict__ X, const int32_t* __restrict__ qweight,
+                         const int32_t* __restrict__ qzeros, const uint16_t* __restrict__ scales,
+                         int64_t M, int64_t N, int64_t K, int gshift, int tiles_m, int tiles_n,
+                         uint16_t* __restrict__ Y) {
+  typedef typename Operand<F16>::type V;
+  int tm, tn;
+  if (!tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
+  const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
+  const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
+  const int tid = threadIdx.x, lane = tid & 63;
+  QCtx c;
+  c.rsA = tile_rsrc(X + m0 * K, rows_a, K);
+  const int64_t N8 = N / 8, G = int64_t(32) << gshift;
+  c.rsQ = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(qweight), 0,
+                                            int(K * N8 * 4), 0x00020000);
+  c.rsZ = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(qzeros), 0,
+                                            int(K / G * N8 * 4), 0x00020000);
+  c.rsS = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0,
+                                            int(K / G * N * 2), 0x00020000);
+  c.wave = tid >> 6;
+  c.KT = int(K / BK);
+  c.oobA = BM * int(K) * 2;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = (c.wave * 4 + j) * 64 + lane;
+    const int row = p >> 2;
+    const int chunk = (p & 3) ^ ((row >> 2) & 3);
+    c.voffA[j] = (row * int(K) + chunk * 8) * 2;
+  }
+  const int wm = c.wave >> 1, wn = c.wave & 1;
+  const int fr = lane & 31, fh = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    c.rdA[ks] = swz(wm * 128 + fr, 2 * ks + fh);
+    c.rdB[ks] = swz(wn * 128 + fr, 2 * ks + fh);
+  }
+  const int kq = 2 * c.wave + (lane & 1), c8 = lane >> 1;
+  const int64_t col = n0 / 8 + c8;  // word column
+  c.oobm = col < N8 ? 0u : kQOob;
+  c.qrow = uint32_t(N8 * 4);
+  c.ktq = c.qrow * BK;
+  c.qoff = uint32_t((int64_t(4 * kq) * N8 + col) * 4);
+  c.zrow = uint32_t(N8 * 4);
+  c.srow = uint32_t(N * 2);
+  c.zoff = uint32_t(col * 4);
+  c.soff = uint32_t(col * 16);
+  c.gshift = gshift;
+  const int rho = (c8 >> 1) & 7;
+  c.rot = uint32_t(4 * rho);
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int row = 8 * c8 + ((r + rho) & 7);
+    c.wofs[r] = swz(row, kq >> 1) * 16 + (kq & 1) * 8;
+  }
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  // prologue: k-tiles 0..2 into stages 0..2, packed k-tiles 3 and 4 in flight
+  dma_a<0>(c, 0);
+  dma_a<1>(c, 1);
+  dma_a<2>(c, 2);
+  QLoad slot[2], t2;
+  load_q(c, 0, slot[0]);
+  load_q(c, 1, slot[1]);
+  load_q(c, 2, t2);
+  dq_write<F16, 0>(c, slot[0]);
+  dq_write<F16, 1>(c, slot[1]);
+  dq_write<F16, 2>(c, t2);
+  load_q(c, 3, slot[1]);
+  load_q(c, 4, slot[0]);
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_waitcnt(wait_vm(12));  // X's k-tiles 0..2 landed
+  region_barrier();
+  V f0a[4], f0b[4], f1a[4], f1b[4];
+  region_q<F16, 0, false>(c, 0, acc, f0a, f0b, f1a, f1b, slot);
+  int kt = 1;
+  for (; kt + 4 < c.KT; kt += 4) {
+    region_q<F16, 1, true>(c, kt, acc, f0a, f0b, f1a, f1b, slot);
+    region_q<F16, 2, true>(c, kt + 1, acc, f0a, f0b, f1a, f1b, slot);
+    region_q<F16, 3, true>(c, kt + 2, acc, f0a, f0b, f1a, f1b, slot);
+    region_q<F16, 0, true>(c, kt + 3, acc, f0a, f0b, f1a, f1b, slot);
+  }
+  region_q<F16, 1, true>(c, kt, acc, f0a, f0b, f1a, f1b, slot);
+  region_q<F16, 2, true>(c, kt + 1, acc, f0a, f0b, f1a, f1b, slot);
+  region_q<F16, 3, true>(c, kt + 2, acc, f0a, f0b, f1a, f1b, slot);
+  mfma_4x4(acc, f1a, f1b);
+
+  const int64_t row0 = m0 + wm * 128 + 4 * (lane >> 5);
+  const int64_t col0 = n0 + wn * 128 + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t cn = col0 + j * 32;
+      if (cn >= N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = row0 + i * 32 + 8 * (v >> 2) + (v & 3);
+        if (row < M) Y[row * N + cn] = to16<F16>(acc[i][j][v]);
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // decode: fused GEMV
 // ---------------------------------------------------------------------------
 
@@ -739,6 +999,26 @@ hipError_t launch_w4a16_dequant(const int32_t* qweight, const int32_t* qzeros,
     dequant_kernel<true><<<blocks, 256, 0, st>>>(qweight, qzeros, scales, N, K, group, Wd);
   else
     dequant_kernel<false><<<blocks, 256, 0, st>>>(qweight, qzeros, scales, N, K, group, Wd);
+  return hipGetLastError();
+}
+
+// Prefill GEMM straight from the packed layer (K·N/2 < 2^31 bytes, K a
+// multiple of 128, group 32, 64 or 128).
+hipError_t launch_w4a16_gemm_q(const uint16_t* X, const int32_t* qweight, const int32_t* qzeros,
+                               const uint16_t* scales, int64_t M, int64_t N, int64_t K,
+                               int group, int f16, uint16_t* Y, hipStream_t st) {
+  if (K % 128 || N % 8 || K * (N / 8) * 4 >= (int64_t(1) << 31) ||
+      (group != 32 && group != 64 && group != 128))
+    return hipErrorInvalidValue;
+  const int gshift = group == 32 ? 0 : group == 64 ? 1 : 2;
+  const int tiles_m = int((M + BM - 1) / BM), tiles_n = int((N + BN - 1) / BN);
+  const unsigned blocks = unsigned(gemm_blocks(tiles_m, tiles_n));
+  if (f16)
+    w4a16_gemm_q_kernel<true><<<blocks, NT, 0, st>>>(X, qweight, qzeros, scales, M, N, K, gshift,
+                                                     tiles_m, tiles_n, Y);
+  else
+    w4a16_gemm_q_kernel<false><<<blocks, NT, 0, st>>>(X, qweight, qzeros, scales, M, N, K,
+                                                      gshift, tiles_m, tiles_n, Y);
   return hipGetLastError();
 }
 

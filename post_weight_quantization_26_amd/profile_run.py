@@ -121,6 +121,22 @@ def w4a16(reps: int) -> None:
                            TFLOPs=round(flops / (main_us * 1e-6) / 1e12, 1),
                            frac_of_2500=round(flops / (main_us * 1e-6) / 2.5e15, 4))
             print(json.dumps(rec), flush=True)
+            if T > 16 and bits == 4:
+                # the GEMM that dequantises on the fly (no workspace)
+                api.w4a16_matmul(X, qw, qz, sc, out=Y, on_the_fly=True)
+                torch.cuda.synchronize()
+                api.profile_enable(True)
+                api.profile_reset()
+                for _ in range(n_rep):
+                    api.w4a16_matmul(X, qw, qz, sc, out=Y, on_the_fly=True)
+                torch.cuda.synchronize()
+                fly_us = api.profile_read("w4a16")[0] * 1e3 / n_rep
+                api.profile_enable(False)
+                print(json.dumps({"N": N, "K": K, "T": T, "bits": bits,
+                                  "main_kernel_us": round(fly_us, 2), "path": "gemm_on_the_fly",
+                                  "TFLOPs": round(flops / (fly_us * 1e-6) / 1e12, 1),
+                                  "frac_of_2500": round(flops / (fly_us * 1e-6) / 2.5e15, 4)}),
+                      flush=True)
             del X, ws, Y
         del qw, qz, sc
         torch.cuda.empty_cache()

@@ -295,7 +295,8 @@ def test_w3a16_workspace_and_rejects(L):
 def test_w4a16_workspace_and_rejects(L):
     lib = L.lib()
     wsb = lib.awq_w4a16_workspace_bytes
-    # GEMM path (T > 16): the dequantised [N, K] operand rows
+    # GEMM path (T > 16): the dequantised [N, K] operand rows (a smaller
+    # workspace selects the on-the-fly GEMM, below)
     assert wsb(4096, 4096, 4096, L.AWQ_BF16) == 4096 * 4096 * 2
     # GEMV path: float32 partials per k chunk, token row and output channel
     one = wsb(1, 4096, 4096, L.AWQ_BF16)
@@ -326,6 +327,10 @@ def test_w4a16_workspace_and_rejects(L):
     assert call(wsb=16) == -3
     assert call(ws=MIS) == -3
     assert "w4a16_matmul" in L.last_error()
+    # prefill with too small a workspace is only for layers the on-the-fly
+    # GEMM can address (K·N/2 < 2^31 bytes)
+    assert call(T=4096, N=65536, K=65536, ws=None, wsb=0) == -3
+    assert call(T=4096, N=65536, K=65536, wsb=16) == -3
 
 
 def test_prepared_gram_sizes_and_rejects(L):

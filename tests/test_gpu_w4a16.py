@@ -59,8 +59,9 @@ def packed_layer(N, K, group, seed, bits=4):
     return qw, qz, sc
 
 
-def check_consumer(api, T, N, K, group, dtype, seed, bits=4):
-    """Exact-Ŵ decode for T <= 16, 16-bit Ŵ GEMM above (both bit widths)."""
+def check_consumer(api, T, N, K, group, dtype, seed, bits=4, on_the_fly=False):
+    """Exact-Ŵ decode for T <= 16, 16-bit Ŵ GEMM above (both bit widths;
+    on_the_fly: the 4-bit GEMM that dequantises as it goes)."""
     qw, qz, sc = packed_layer(N, K, group, seed, bits)
     rng = np.random.default_rng(seed + 1)
     x32 = rng.standard_normal((T, K)).astype(np.float32)
@@ -68,7 +69,7 @@ def check_consumer(api, T, N, K, group, dtype, seed, bits=4):
     Xd = to_dev(X, dtype)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
     Y = api.w4a16_matmul(Xd, dev(qw), dev(qz), dev(sc).view(torch.float16), group=group,
-                         bits=bits)
+                         bits=bits, on_the_fly=on_the_fly)
     decode = T <= 16
     torch.cuda.synchronize()
     y = Y.float().cpu().numpy().astype(np.float64)
@@ -151,6 +152,34 @@ def test_gemm_path(api, T, dtype):
                                            (544, 64, "bf16")])
 def test_gemm_path_wide_dequant(api, N, group, dtype):
     check_consumer(api, 300, N, 512, group, dtype, seed=200 + N)
+
+
+# The GEMM that dequantises on the fly (no workspace): word columns past N in
+# the last output tile (N = 264, 520), ragged token tiles, every group size,
+# a full 4096 x 4096 layer
+@pytest.mark.parametrize("T,N,K,group,dtype", [(300, 288, 512, 128, "bf16"),
+                                               (300, 1056, 512, 32, "f16"),
+                                               (17, 544, 512, 64, "bf16"),
+                                               (520, 264, 384, 128, "f16"),
+                                               (520, 520, 512, 64, "bf16"),
+                                               (300, 4096, 4096, 128, "bf16")])
+def test_gemm_on_the_fly(api, T, N, K, group, dtype):
+    check_consumer(api, T, N, K, group, dtype, seed=240 + N + T, on_the_fly=True)
+
+
+def test_gemm_on_the_fly_equals_two_pass(api):
+    """Both prefill paths form the same rounded Ŵ and run the same MFMA
+    loop over it: identical outputs."""
+    qw, qz, sc = packed_layer(2056, 512, 128, seed=250)
+    rng = np.random.default_rng(251)
+    X = _enc(rng.standard_normal((33 * 256 - 7, 512)).astype(np.float32), "bf16")
+    Xd = to_dev(X, "bf16")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+    args = (Xd, dev(qw), dev(qz), dev(sc).view(torch.float16))
+    y1 = api.w4a16_matmul(*args)
+    y2 = api.w4a16_matmul(*args, on_the_fly=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
 @pytest.mark.parametrize("group", [32, 64])
