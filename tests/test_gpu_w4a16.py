@@ -59,10 +59,13 @@ def packed_layer(N, K, group, seed, bits=4):
     return qw, qz, sc
 
 
-def check_consumer(api, T, N, K, group, dtype, seed, bits=4, on_the_fly=False):
+def check_consumer(api, T, N, K, group, dtype, seed, bits=4, on_the_fly=False, layer=None,
+                   sample=None):
     """Exact-Ŵ decode for T <= 16, 16-bit Ŵ GEMM above (both bit widths;
-    on_the_fly: the 4-bit GEMM that dequantises as it goes)."""
-    qw, qz, sc = packed_layer(N, K, group, seed, bits)
+    on_the_fly: the 4-bit GEMM that dequantises as it goes). layer: a packed
+    layer (qw, qz, sc) built once by the caller. sample: (word columns,
+    output rows) to check instead of all outputs."""
+    qw, qz, sc = layer if layer is not None else packed_layer(N, K, group, seed, bits)
     rng = np.random.default_rng(seed + 1)
     x32 = rng.standard_normal((T, K)).astype(np.float32)
     X = _enc(x32, dtype)
@@ -73,6 +76,10 @@ def check_consumer(api, T, N, K, group, dtype, seed, bits=4, on_the_fly=False):
     decode = T <= 16
     torch.cuda.synchronize()
     y = Y.float().cpu().numpy().astype(np.float64)
+    if sample is not None:
+        wcols, outs = sample
+        qw, qz, sc, N = qw[:, wcols], qz[:, wcols], sc[:, outs], len(outs)
+        y = y[:, outs]
     x = _dec(X, dtype).astype(np.float64)
     w_exact = O.dequantize_packed(qw, qz, sc, N, bits, group)       # [N, K] float64
     if decode:
@@ -263,3 +270,42 @@ def test_search_pack_consume_end_to_end(api):
     assert abs(mse - want) <= 0.05 * want
     # and far below plain rounding (alpha = 0)
     assert mse < 0.5 * float(res["mse"][0])
+
+
+# The 70B-class MLP layer [28672, 8192] at full size, 4 and 3 bits: decode at
+# T = 1 and 16 (the matrix-core GEMV with several k chunks and 112 column
+# blocks) and prefill at T = 64 (both 4-bit paths). The layer is seeded
+# random words, zero points and fp16 scales (any packed layout is a valid
+# input); 4096 outputs spread over every column block, the last included,
+# are checked against the oracle with the same bounds as above.
+def random_packed_layer(N, K, group, bits, seed):
+    rng = np.random.default_rng(seed)
+    cols = N * bits // 32
+    words = lambda rows: rng.integers(0, 1 << 32, size=(rows, cols), dtype=np.uint64).astype(
+        np.uint32).view(np.int32)
+    sc = np.exp(rng.uniform(-7.0, -3.0, size=(K // group, N))).astype(np.float16).view(np.uint16)
+    return words(K), words(K // group), sc
+
+
+def output_sample(N, bits, count):
+    unit_w, unit_n = (1, 8) if bits == 4 else (3, 32)
+    units = N // unit_n
+    pick = np.unique(np.append(np.linspace(0, units - 1, count // unit_n).astype(np.int64),
+                               units - 1))
+    wcols = (pick[:, None] * unit_w + np.arange(unit_w)).ravel()
+    outs = (pick[:, None] * unit_n + np.arange(unit_n)).ravel()
+    return wcols, outs
+
+
+@pytest.fixture(scope="module")
+def layer_70b():
+    return {bits: random_packed_layer(28672, 8192, 128, bits, seed=300 + bits) for bits in (4, 3)}
+
+
+@pytest.mark.parametrize("bits,T,on_the_fly", [(4, 1, False), (4, 16, False), (4, 64, False),
+                                               (4, 64, True), (3, 1, False), (3, 16, False),
+                                               (3, 64, False)])
+def test_consumer_fullsize_70b_layer(api, layer_70b, bits, T, on_the_fly):
+    check_consumer(api, T, 28672, 8192, 128, "bf16", seed=310 + T, bits=bits,
+                   on_the_fly=on_the_fly, layer=layer_70b[bits],
+                   sample=output_sample(28672, bits, 4096))
