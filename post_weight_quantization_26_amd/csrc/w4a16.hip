@@ -712,6 +712,7 @@ constexpr int kMgSlots = 4;
 template <bool F16>
 struct MgState {
   floatx4 tot[kMgMfma];
+  floatx4 pacc[kMgMfma], sacc;  // the open group's MFMA sums P' and S
   uint2 w[kMgSlots][8];
   uint4 a[kMgSlots];
   uint4 ps0[kMgSlots], ps1[kMgSlots];
@@ -766,7 +767,13 @@ __device__ __forceinline__ void mg_block(MgState<F16>& st, int kb, const LoadDat
   V ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = 1;
-  const floatx4 sx = mfma16(a, ones, zero);
+  // At T = 1 the MFMAs accumulate a group's blocks (P' and S over up to 128
+  // rows) and the fold runs once per group; with more token rows the extra
+  // 64 registers would spill, so every block folds.
+  constexpr bool kAccFirst = TV == 1 ? kFirst : true;
+  constexpr bool kAccLast = TV == 1 ? J % BPG == BPG - 1 : true;
+  const floatx4 sx = mfma16(a, ones, kAccFirst ? zero : st.sacc);
+  if constexpr (!kAccLast) st.sacc = sx;
   const uint32_t sw[8] = {st.s0.x, st.s0.y, st.s0.z, st.s0.w, st.s1.x, st.s1.y, st.s1.z, st.s1.w};
   if constexpr (BITS == 3) {
     uint32_t lo[8], hi[8];
@@ -782,10 +789,14 @@ __device__ __forceinline__ void mg_block(MgState<F16>& st, int kb, const LoadDat
                       code3_pair<F16, R>(lo[2], hi[2], lo[3], hi[3], one),                  \
                       code3_pair<F16, R>(lo[4], hi[4], lo[5], hi[5], one),                  \
                       code3_pair<F16, R>(lo[6], hi[6], lo[7], hi[7], one)));                \
-    const floatx4 p = mfma16(a, b, zero);                                                   \
-    const float sc = f16_to_f32(uint16_t((sw[R >> 1] >> (16 * (R & 1))) & 0xFFFFu));        \
-    for (int v = 0; v < TV; ++v)                                                            \
-      st.tot[R][v] = __builtin_fmaf(sc, __builtin_fmaf(-st.zf[R], sx[v], p[v]), st.tot[R][v]); \
+    const floatx4 p = mfma16(a, b, kAccFirst ? zero : st.pacc[R]);                          \
+    if constexpr (kAccLast) {                                                               \
+      const float sc = f16_to_f32(uint16_t((sw[R >> 1] >> (16 * (R & 1))) & 0xFFFFu));      \
+      for (int v = 0; v < TV; ++v)                                                          \
+        st.tot[R][v] = __builtin_fmaf(sc, __builtin_fmaf(-st.zf[R], sx[v], p[v]), st.tot[R][v]); \
+    } else {                                                                                \
+      st.pacc[R] = p;                                                                       \
+    }                                                                                       \
   }
     AWQ_MG_CODE3(0) AWQ_MG_CODE3(1) AWQ_MG_CODE3(2) AWQ_MG_CODE3(3)
     AWQ_MG_CODE3(4) AWQ_MG_CODE3(5) AWQ_MG_CODE3(6) AWQ_MG_CODE3(7)
@@ -804,10 +815,14 @@ __device__ __forceinline__ void mg_block(MgState<F16>& st, int kb, const LoadDat
     const V b = __builtin_bit_cast(                                                         \
         V, make_uint4(code_pair<F16, R>(w[0], w[1]), code_pair<F16, R>(w[2], w[3]),         \
                       code_pair<F16, R>(w[4], w[5]), code_pair<F16, R>(w[6], w[7])));       \
-    const floatx4 p = mfma16(a, b, zero);                                                   \
-    const float sc = f16_to_f32(uint16_t((sw[m >> 1] >> (16 * (m & 1))) & 0xFFFFu));        \
-    for (int v = 0; v < TV; ++v)                                                            \
-      st.tot[m][v] = __builtin_fmaf(sc, __builtin_fmaf(-st.zf[m], sx[v], p[v]), st.tot[m][v]); \
+    const floatx4 p = mfma16(a, b, kAccFirst ? zero : st.pacc[m]);                          \
+    if constexpr (kAccLast) {                                                               \
+      const float sc = f16_to_f32(uint16_t((sw[m >> 1] >> (16 * (m & 1))) & 0xFFFFu));      \
+      for (int v = 0; v < TV; ++v)                                                          \
+        st.tot[m][v] = __builtin_fmaf(sc, __builtin_fmaf(-st.zf[m], sx[v], p[v]), st.tot[m][v]); \
+    } else {                                                                                \
+      st.pacc[m] = p;                                                                       \
+    }                                                                                       \
   }
     if (c == 0) {
       constexpr int c = 0;
