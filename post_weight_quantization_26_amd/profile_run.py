@@ -25,6 +25,15 @@
       70B-class MLP layer) and 4096 x 4096, ``reps`` timed launches each;
       prints the library's HIP-event time and the bandwidth it implies.
 
+  python -m post_weight_quantization_26_amd.profile_run traffic --record R \
+          --fetch FETCH.csv --write WRITE.csv
+      Updates the traffic record R (profiles/search_gemm_traffic.json or
+      profiles/gram_search_traffic.json: kernel, workload, copy calibration
+      and the sources it covers) from two rocprofv3 --pmc runs of one
+      bench.py step (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch): the
+      readings of the record's kernel scaled by the calibration factors give
+      its bytes per launch, stored with the SHA-256 of the sources now.
+
 The search workload itself is profiled through ``bench.py``.
 """
 from __future__ import annotations
@@ -173,13 +182,57 @@ def pack(reps: int) -> None:
         torch.cuda.empty_cache()
 
 
+def traffic(record: str, fetch_csv: str, write_csv: str) -> None:
+    import csv
+    import hashlib
+    import json
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    with open(record) as f:
+        rec = json.load(f)
+
+    def reading(path: str, counter: str) -> float:
+        vals = []
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                name = row["Kernel_Name"]
+                if row["Counter_Name"] == counter and f"::{rec['kernel']}(" in name:
+                    vals.append(float(row["Counter_Value"]))
+        if len(vals) != 1:
+            raise SystemExit(f"{path}: expected one {rec['kernel']} dispatch, found {len(vals)}")
+        return vals[0]
+
+    cal = rec["copy_calibration"]
+    fetch_kb = reading(fetch_csv, "FETCH_SIZE")
+    write_kb = reading(write_csv, "WRITE_SIZE")
+    rec["fetch_size_kb"] = fetch_kb
+    rec["write_size_kb"] = write_kb
+    rec["bytes_per_launch"] = int(round(fetch_kb * 1024 * cal["fetch_factor"]
+                                        + write_kb * 1024 * cal["write_factor"]))
+    h = hashlib.sha256()
+    for rel in rec["gemm_sources"]:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    rec["gemm_sources_sha256"] = h.hexdigest()
+    with open(record, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps({"kernel": rec["kernel"], "fetch_size_kb": fetch_kb, "write_size_kb": write_kb,
+                      "GiB_per_launch": round(rec["bytes_per_launch"] / 2 ** 30, 2)}))
+
+
 def main(argv=None) -> int:
     p = argparse.ArgumentParser()
-    p.add_argument("what", choices=["copy", "fold", "w4a16", "pack"])
+    p.add_argument("what", choices=["copy", "fold", "w4a16", "pack", "traffic"])
     p.add_argument("--mib", type=int, default=1024)
     p.add_argument("--reps", type=int, default=20)
+    p.add_argument("--record")
+    p.add_argument("--fetch")
+    p.add_argument("--write")
     a = p.parse_args(argv)
-    if a.what == "copy":
+    if a.what == "traffic":
+        traffic(a.record, a.fetch, a.write)
+    elif a.what == "copy":
         copy(a.mib)
     elif a.what == "fold":
         fold(a.reps)
