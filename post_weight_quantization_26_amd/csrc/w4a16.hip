@@ -242,9 +242,11 @@ void w4a16_gemm_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
 // (gemm_core.h); only the B operand's way into LDS differs. For each 32-wide
 // k-tile a lane loads 4 qweight words (k rows 4·kq .. 4·kq + 3 of the tile,
 // word column c8 of the output tile: outputs n0 + 8·c8 .. + 7), its group's
-// zero-point word and 8 fp16 scales, two k-tiles ahead of use. One region
-// before the MFMAs read the k-tile it forms Ŵ = (q − z)·scale exactly as the
-// dequantisation pass does (fma(q, scale, −z·scale), whose one rounding is
+// zero-point word and 8 fp16 scales. Region kt (the region whose MFMAs read
+// k-tile kt) loads the packed k-tile kt + 5 and forms the operand of k-tile
+// kt + 3, as the DMA of X's k-tile kt + 3 fills the same ring stage: Ŵ =
+// (q − z)·scale exactly as the dequantisation pass does (fma(q, scale,
+// −z·scale), whose one rounding is
 // that of (q − z)·scale because z·scale is exact), rounds it once to the
 // 16-bit type and writes 4 k x 1 output row per 8-byte LDS store into the
 // ring's swizzled layout. Lanes pair up over word columns (kq = 2·wave +
