@@ -33,10 +33,10 @@ __device__ __forceinline__ void search_gemm_16(const uint16_t* __restrict__ X,
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
   const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
   const int64_t rows_b = Nc - n0 < BN ? Nc - n0 : BN;
-  GemmCtx c;
-  gemm_setup(c, X + m0 * K, rows_a, E + n0 * K, rows_b, K);
+  GemmCtx64 c;
+  gemm_setup64(c, X + m0 * K, rows_a, E + n0 * K, rows_b, K);
   floatx16 acc[4][4];
-  gemm_mainloop<F16>(c, acc);
+  gemm_mainloop64<F16>(c, acc);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wm = c.wave >> 1, wn = c.wave & 1;
 
@@ -44,7 +44,7 @@ __device__ __forceinline__ void search_gemm_16(const uint16_t* __restrict__ X,
   // column j*32 + lane%32 of the wave's range; lanes l and l^32 share it.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  float* red = reinterpret_cast<float*>(sA0);  // [2][BN]
+  float* red = reinterpret_cast<float*>(s64A0);  // [2][BN]
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float s = 0.f;

@@ -1,7 +1,9 @@
-// The MFMA main loop shared by the search GEMM (sums of squares of X·Eᵀ)
-// and the W4A16 consumer GEMM (X·Ŵᵀ stored): a 256x256 output tile per
-// workgroup, A and B both [rows, K] row-major 16-bit operands, K in 32-wide
-// k-tiles through a 4-stage LDS ring filled by buffer_load ... lds.
+// The MFMA main loops of the search GEMM (sums of squares of X·Eᵀ), the
+// W4A16 consumer GEMM (X·Ŵᵀ stored) and the Gram kernels: a 256x256 output
+// tile per workgroup, A and B both [rows, K] row-major 16-bit operands. The
+// loop described here takes K in 32-wide k-tiles through a 4-stage LDS ring
+// filled by buffer_load ... lds; the search GEMM uses the 64-wide, 2-stage
+// form further down (same tile, MFMAs and k order).
 //
 //  * 256x256 block tile, four wavefronts (one per SIMD) in a 2x2 arrangement,
 //    each owning 128x128 outputs as 4x4 v_mfma_f32_32x32x16 accumulators
@@ -320,6 +322,137 @@ __device__ __forceinline__ void gemm_mainloop(const Ctx& c, floatx16 (&acc)[4][4
   region<1, true>(c, kt, acc, f0a, f0b, f1a, f1b);
   region<2, true>(c, kt + 1, acc, f0a, f0b, f1a, f1b);
   region<3, true>(c, kt + 2, acc, f0a, f0b, f1a, f1b);
+  mfma_4x4(acc, f1a, f1b);
+}
+
+// The same tile, wave layout, MFMAs and fragment order with 64-wide k-tiles
+// in a 2-stage ring (2 x 64 KiB): the search GEMM's main loop. Each region
+// (one 64-wide k-tile, 4 k-steps of 16) issues the DMA of k-tile kt + 1
+// into the other stage (last read in region kt - 1), runs the MFMAs of the
+// previous k-step while the next fragments are read, and ends with one wait
+// (this wave's LDS reads and its DMA of kt + 1) and one barrier: half the
+// barriers per k of the 4-stage loop, at one region of copy latency hiding
+// instead of two. LDS rows are 128 bytes (8 chunks of 16 B) with the chunk
+// index XORed by (row / 2) % 8, which keeps a 16-lane fragment read on 16
+// distinct bank groups and lets the DMA fill whole rows. The k order of the
+// MFMAs is the 4-stage loop's, so the sums are bit-identical.
+constexpr int BK64 = 64;
+constexpr int CH64 = 8;
+constexpr int STAGE64 = 256 * CH64;
+__shared__ uint4 s64A0[STAGE64], s64A1[STAGE64], s64B0[STAGE64], s64B1[STAGE64];
+template <int S>
+__device__ __forceinline__ uint4* stage64_a() { return S == 0 ? s64A0 : s64A1; }
+template <int S>
+__device__ __forceinline__ uint4* stage64_b() { return S == 0 ? s64B0 : s64B1; }
+__device__ __forceinline__ int swz64(int row, int chunk) {
+  return row * CH64 + (chunk ^ ((row >> 1) & 7));
+}
+struct GemmCtx64 {
+  __amdgpu_buffer_rsrc_t rsA, rsB;
+  int voff[8];
+  int wave, KT, oob;
+  int rdA[4], rdB[4];
+};
+__device__ __forceinline__ void gemm_setup64(GemmCtx64& c, const uint16_t* A, int64_t rows_a,
+                                             const uint16_t* B, int64_t rows_b, int64_t K) {
+  c.rsA = tile_rsrc(A, rows_a, K);
+  c.rsB = tile_rsrc(B, rows_b, K);
+  const int tid = threadIdx.x, lane = tid & 63;
+  c.wave = tid >> 6;
+  c.KT = int(K / BK64);
+  c.oob = BM * int(K) * 2;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int p = (c.wave * 8 + j) * 64 + lane;
+    const int row = p >> 3;
+    const int chunk = (p & 7) ^ ((row >> 1) & 7);
+    c.voff[j] = (row * int(K) + chunk * 8) * 2;
+  }
+  const int wm = c.wave >> 1, wn = c.wave & 1;
+  const int fr = lane & 31, fh = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    c.rdA[ks] = swz64(wm * 128 + fr, 2 * ks + fh);
+    c.rdB[ks] = swz64(wn * 128 + fr, 2 * ks + fh);
+  }
+}
+template <int S>
+__device__ __forceinline__ void dma64(const GemmCtx64& c, int kt) {
+  const int kofs = kt < c.KT ? kt * (BK64 * 2) : c.oob;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsA, AWQ_LDS(stage64_a<S>() + (c.wave * 8 + j) * 64),
+                                             16, c.voff[j] + kofs, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsB, AWQ_LDS(stage64_b<S>() + (c.wave * 8 + j) * 64),
+                                             16, c.voff[j] + kofs, 0, 0, 0);
+  }
+}
+template <int S, class V>
+__device__ __forceinline__ void read_frags64(const GemmCtx64& c, int ks, V (&fa)[4], V (&fb)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    fa[i] = __builtin_bit_cast(V, stage64_a<S>()[c.rdA[ks] + i * 256]);
+    fb[i] = __builtin_bit_cast(V, stage64_b<S>()[c.rdB[ks] + i * 256]);
+  }
+}
+template <int S, bool PREV, class V>
+__device__ __forceinline__ void region64(const GemmCtx64& c, int kt, floatx16 (&acc)[4][4],
+                                         V (&f0a)[4], V (&f0b)[4], V (&f1a)[4], V (&f1b)[4]) {
+  dma64<S ^ 1>(c, kt + 1);
+  if (PREV) mfma_4x4(acc, f1a, f1b);
+  read_frags64<S>(c, 0, f0a, f0b);
+  mfma_4x4(acc, f0a, f0b);
+  read_frags64<S>(c, 1, f1a, f1b);
+  mfma_4x4(acc, f1a, f1b);
+  read_frags64<S>(c, 2, f0a, f0b);
+  mfma_4x4(acc, f0a, f0b);
+  read_frags64<S>(c, 3, f1a, f1b);
+  if (PREV) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+    }
+  }
+#pragma unroll
+  for (int ph = 0; ph < 3; ++ph) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 8, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  region_barrier();
+}
+template <bool F16>
+__device__ __forceinline__ void gemm_mainloop64(const GemmCtx64& c, floatx16 (&acc)[4][4]) {
+  typedef typename Operand<F16>::type V;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  dma64<0>(c, 0);
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  region_barrier();
+  V f0a[4], f0b[4], f1a[4], f1b[4];
+  region64<0, false>(c, 0, acc, f0a, f0b, f1a, f1b);
+  int kt = 1;
+  for (; kt + 1 < c.KT; kt += 2) {
+    region64<1, true>(c, kt, acc, f0a, f0b, f1a, f1b);
+    region64<0, true>(c, kt + 1, acc, f0a, f0b, f1a, f1b);
+  }
+  region64<1, true>(c, kt, acc, f0a, f0b, f1a, f1b);
   mfma_4x4(acc, f1a, f1b);
 }
 
