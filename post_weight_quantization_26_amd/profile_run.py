@@ -34,6 +34,12 @@
       readings of the record's kernel scaled by the calibration factors give
       its bytes per launch, stored with the SHA-256 of the sources now.
 
+  python -m post_weight_quantization_26_amd.profile_run library_gemm [--reps 5]
+      For comparison only: the vendor library's bf16 GEMM (torch.matmul, i.e.
+      hipBLASLt) on the search GEMM's shape, X [65536, 4096] times the 20
+      candidates' E [81920, 4096] transposed, output [65536, 81920] bf16;
+      prints its time and TFLOP/s (torch events on the current stream).
+
 The search workload itself is profiled through ``bench.py``.
 """
 from __future__ import annotations
@@ -221,9 +227,34 @@ def traffic(record: str, fetch_csv: str, write_csv: str) -> None:
                       "GiB_per_launch": round(rec["bytes_per_launch"] / 2 ** 30, 2)}))
 
 
+def library_gemm(reps: int) -> None:
+    import json
+    import torch
+    T, K, Nc = 65536, 4096, 20 * 4096
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(11)
+    X = torch.randn((T, K), generator=g, device="cuda:0").to(torch.bfloat16)
+    E = (torch.randn((Nc, K), generator=g, device="cuda:0") * 1e-3).to(torch.bfloat16)
+    Y = torch.empty((T, Nc), dtype=torch.bfloat16, device="cuda:0")
+    for _ in range(2):
+        torch.matmul(X, E.t(), out=Y)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        torch.matmul(X, E.t(), out=Y)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    flops = 2.0 * T * Nc * K
+    print(json.dumps({"op": "torch.matmul bf16 X·Eᵀ", "T": T, "Nc": Nc, "K": K, "ms": round(ms, 3),
+                      "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+                      "frac_of_2500": round(flops / (ms * 1e-3) / 2.5e15, 4)}), flush=True)
+
+
 def main(argv=None) -> int:
     p = argparse.ArgumentParser()
-    p.add_argument("what", choices=["copy", "fold", "w4a16", "pack", "traffic"])
+    p.add_argument("what", choices=["copy", "fold", "w4a16", "pack", "traffic", "library_gemm"])
     p.add_argument("--mib", type=int, default=1024)
     p.add_argument("--reps", type=int, default=20)
     p.add_argument("--record")
@@ -232,6 +263,8 @@ def main(argv=None) -> int:
     a = p.parse_args(argv)
     if a.what == "traffic":
         traffic(a.record, a.fetch, a.write)
+    elif a.what == "library_gemm":
+        library_gemm(a.reps)
     elif a.what == "copy":
         copy(a.mib)
     elif a.what == "fold":
