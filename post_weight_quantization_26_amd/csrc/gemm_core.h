@@ -407,27 +407,32 @@ __device__ __forceinline__ void region64(const GemmCtx64& c, int kt, floatx16 (&
   read_frags64<S>(c, 2, f0a, f0b);
   mfma_4x4(acc, f0a, f0b);
   read_frags64<S>(c, 3, f1a, f1b);
+  // each phase: 16 MFMAs with the next k-step's 8 fragment reads one per
+  // two MFMAs; the 16 copies one per two MFMAs over the first two phases
   if (PREV) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
     }
   }
 #pragma unroll
-  for (int ph = 0; ph < 3; ++ph) {
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+  }
+#pragma unroll
+  for (int ph = 0; ph < 2; ++ph) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 8, 0);
   }
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
