@@ -347,27 +347,40 @@ __device__ __forceinline__ uint4* stage64_b() { return S == 0 ? s64B0 : s64B1; }
 __device__ __forceinline__ int swz64(int row, int chunk) {
   return row * CH64 + (chunk ^ ((row >> 1) & 7));
 }
+// A and B with their own row strides (elements); pair_b as in GemmCtx2, at
+// 64-wide k-tiles: A's k-tile kt reads B's k-tile (kt / 4)·2 + kt % 2.
+// Copy j of a wave fills rows 8·j further down than copy 0, so its source
+// offset is a per-lane base (two of them: the swizzle flips by 4 on odd j)
+// plus a uniform step j·8·ld·2 bytes, which goes in the scalar offset.
 struct GemmCtx64 {
   __amdgpu_buffer_rsrc_t rsA, rsB;
-  int voff[8];
-  int wave, KT, oob;
+  int vbaseA[2], vbaseB[2];
+  int stepA, stepB;
+  int wave, KT, oobA, oobB;
+  bool pair_b;
   int rdA[4], rdB[4];
 };
 __device__ __forceinline__ void gemm_setup64(GemmCtx64& c, const uint16_t* A, int64_t rows_a,
-                                             const uint16_t* B, int64_t rows_b, int64_t K) {
-  c.rsA = tile_rsrc(A, rows_a, K);
-  c.rsB = tile_rsrc(B, rows_b, K);
+                                             int64_t lda, const uint16_t* B, int64_t rows_b,
+                                             int64_t ldb, int64_t KA, bool pair_b) {
+  c.rsA = tile_rsrc(A, rows_a, lda);
+  c.rsB = tile_rsrc(B, rows_b, ldb);
   const int tid = threadIdx.x, lane = tid & 63;
   c.wave = tid >> 6;
-  c.KT = int(K / BK64);
-  c.oob = BM * int(K) * 2;
+  c.KT = int(KA / BK64);
+  c.pair_b = pair_b;
+  c.oobA = BM * int(lda) * 2;
+  c.oobB = BN * int(ldb) * 2;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const int p = (c.wave * 8 + j) * 64 + lane;
     const int row = p >> 3;
     const int chunk = (p & 7) ^ ((row >> 1) & 7);
-    c.voff[j] = (row * int(K) + chunk * 8) * 2;
+    c.vbaseA[j] = ((row - 8 * j) * int(lda) + chunk * 8) * 2;
+    c.vbaseB[j] = ((row - 8 * j) * int(ldb) + chunk * 8) * 2;
   }
+  c.stepA = 16 * int(lda);
+  c.stepB = 16 * int(ldb);
   const int wm = c.wave >> 1, wn = c.wave & 1;
   const int fr = lane & 31, fh = lane >> 5;
 #pragma unroll
@@ -376,15 +389,22 @@ __device__ __forceinline__ void gemm_setup64(GemmCtx64& c, const uint16_t* A, in
     c.rdB[ks] = swz64(wn * 128 + fr, 2 * ks + fh);
   }
 }
+__device__ __forceinline__ void gemm_setup64(GemmCtx64& c, const uint16_t* A, int64_t rows_a,
+                                             const uint16_t* B, int64_t rows_b, int64_t K) {
+  gemm_setup64(c, A, rows_a, K, B, rows_b, K, K, false);
+}
 template <int S>
 __device__ __forceinline__ void dma64(const GemmCtx64& c, int kt) {
-  const int kofs = kt < c.KT ? kt * (BK64 * 2) : c.oob;
+  const bool in = kt < c.KT;
+  const int ktb = c.pair_b ? ((kt >> 2) << 1) | (kt & 1) : kt;
+  const int kofsA = in ? kt * (BK64 * 2) : c.oobA;
+  const int kofsB = in ? ktb * (BK64 * 2) : c.oobB;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsA, AWQ_LDS(stage64_a<S>() + (c.wave * 8 + j) * 64),
-                                             16, c.voff[j] + kofs, 0, 0, 0);
+                                             16, c.vbaseA[j & 1] + kofsA, j * c.stepA, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsB, AWQ_LDS(stage64_b<S>() + (c.wave * 8 + j) * 64),
-                                             16, c.voff[j] + kofs, 0, 0, 0);
+                                             16, c.vbaseB[j & 1] + kofsB, j * c.stepB, 0, 0);
   }
 }
 template <int S, class V>

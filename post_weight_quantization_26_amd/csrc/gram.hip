@@ -111,10 +111,10 @@ void gram_partial_kernel(const uint16_t* __restrict__ Xt, int64_t K, int64_t ldx
   const int64_t rows_a = K - m0 < BM ? K - m0 : BM;
   const int64_t rows_b = K - n0 < BN ? K - n0 : BN;
   const int64_t t0 = int64_t(s) * Ts;
-  GemmCtx2 c;
-  gemm_setup2(c, Xt + m0 * ldx + t0, rows_a, ldx, Xt + n0 * ldx + t0, rows_b, ldx, Ts, false);
+  GemmCtx64 c;
+  gemm_setup64(c, Xt + m0 * ldx + t0, rows_a, ldx, Xt + n0 * ldx + t0, rows_b, ldx, Ts, false);
   floatx16 acc[4][4];
-  gemm_mainloop<false>(c, acc);
+  gemm_mainloop64<false>(c, acc);
 
   const int lane = threadIdx.x & 63;
   const int wm = c.wave >> 1, wn = c.wave & 1;
@@ -202,17 +202,17 @@ void gram_search_kernel(const uint16_t* __restrict__ Gs, int64_t ldg, const uint
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t n0 = int64_t(tn) * BN;
   const int64_t rows_b = Nc - n0 < BN ? Nc - n0 : BN;
-  float* red = reinterpret_cast<float*>(sA0);  // [2][BN]
+  float* red = reinterpret_cast<float*>(s64A0);  // [2][BN]
 #pragma nounroll
   for (int h = 0; h < n_half; ++h) {
     const int tm = h ? tiles_m - 1 - p : p;
     const int64_t m0 = int64_t(tm) * BM;
     const int64_t rows_a = K - m0 < BM ? K - m0 : BM;
-    GemmCtx2 c;
-    gemm_setup2(c, Gs + m0 * ldg + 2 * m0, rows_a, ldg, E + n0 * K + m0, rows_b, K,
-                2 * (K - m0), true);
+    GemmCtx64 c;
+    gemm_setup64(c, Gs + m0 * ldg + 2 * m0, rows_a, ldg, E + n0 * K + m0, rows_b, K,
+                 2 * (K - m0), true);
     floatx16 acc[4][4];
-    gemm_mainloop<false>(c, acc);
+    gemm_mainloop64<false>(c, acc);
 
     // Epilogue: lane l of sub-tile (i, j) holds column n = ... + l % 32 and
     // rows 8·(v/4) + 4·(l/32) + v % 4 of the wave's 32-row block i; each
