@@ -210,10 +210,10 @@ void w4a16_gemm_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
   const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
   const int64_t rows_b = N - n0 < BN ? N - n0 : BN;
-  GemmCtx c;
-  gemm_setup(c, X + m0 * K, rows_a, Wd + n0 * K, rows_b, K);
+  GemmCtx64 c;
+  gemm_setup64(c, X + m0 * K, rows_a, Wd + n0 * K, rows_b, K);
   floatx16 acc[4][4];
-  gemm_mainloop<F16>(c, acc);
+  gemm_mainloop64<F16>(c, acc);
 
   const int lane = threadIdx.x & 63;
   const int wm = c.wave >> 1, wn = c.wave & 1;
