@@ -1,29 +1,27 @@
-// The MFMA main loops of the search GEMM (sums of squares of X·Eᵀ), the
-// W4A16 consumer GEMM (X·Ŵᵀ stored) and the Gram kernels: a 256x256 output
-// tile per workgroup, A and B both [rows, K] row-major 16-bit operands. The
-// loop described here takes K in 32-wide k-tiles through a 4-stage LDS ring
-// filled by buffer_load ... lds; the search GEMM uses the 64-wide, 2-stage
-// form further down (same tile, MFMAs and k order).
+// The MFMA main loop of the search GEMM (sums of squares of X·Eᵀ), the
+// Gram build and search, and the W4A16 consumer's prefill GEMM (X·Ŵᵀ
+// stored): a 256x256 output tile per workgroup, A and B both [rows, K]
+// row-major 16-bit operands.
 //
 //  * 256x256 block tile, four wavefronts (one per SIMD) in a 2x2 arrangement,
 //    each owning 128x128 outputs as 4x4 v_mfma_f32_32x32x16 accumulators
 //    (bf16 or fp16 operands, 256 AGPRs).
-//  * K advances in 32-wide k-tiles through a 4-stage LDS ring (4 x 32 KiB).
-//    Tiles are copied global -> LDS by buffer_load_dwordx4 ... lds (no
-//    staging registers), three k-tiles ahead of the MFMAs. Loads go through a
-//    buffer resource per tile, so rows past the end of A or B read as zero.
-//  * One k-tile per barrier-delimited region; inside it the MFMAs of the
-//    previous k-step run while this k-tile's fragments are read and the DMA
-//    for k-tile kt+3 is issued (sched_group_barrier interleaving).
-//  * LDS rows are 64 bytes (4 chunks of 16 B) with the chunk index XORed by
-//    (row >> 2) & 3: gfx950 serves ds_read_b128 sixteen lanes at a time over
-//    64 banks, and this swizzle keeps both the fragment reads and the DMA
-//    writes free of bank conflicts.
+//  * K advances in 64-wide k-tiles through a 2-stage LDS ring (2 x 64 KiB)
+//    filled by buffer_load_dwordx4 ... lds (no staging registers). Loads go
+//    through a buffer resource per tile, so rows past the end of A or B read
+//    as zero. One k-tile per barrier-delimited region (gemm_mainloop64,
+//    below).
 //  * Each LDS stage is its own __shared__ array and the k-loop is unrolled
-//    over the 4 stages, so the compiler can tell the stage being read from the
-//    stages the DMA writes and does not serialise LDS reads behind the DMA.
+//    over the stages, so the compiler can tell the stage being read from the
+//    stage the DMA writes and does not serialise LDS reads behind the DMA.
 //  * Workgroups are mapped so each XCD runs 4 A tiles x 8 B tiles at a time
 //    while all XCDs share the same 8 B tiles.
+//
+// The 32-wide, 4-stage ring (stage_a/stage_b, swz, read_frags) serves the
+// W4A16 GEMM that dequantises on the fly, whose B tile is written into LDS
+// from registers: 32-wide k-tiles with 64-byte LDS rows (4 chunks of 16 B,
+// the chunk index XORed by (row >> 2) & 3, which keeps 16-lane ds_read_b128
+// fragment reads free of bank conflicts).
 //
 // Output layout of one 32x32 accumulator: lane l holds column l % 32; its
 // register v holds row 8·(v / 4) + 4·(l / 32) + v % 4.
@@ -118,56 +116,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base
                                            int(rows * K * 2), 0x00020000);
 }
 
-struct GemmCtx {
-  __amdgpu_buffer_rsrc_t rsA, rsB;
-  int voff[4];  // byte offset (k-tile 0) of the chunk this lane copies in DMA instruction j
-  int wave, KT, oob;
-  int rdA[2], rdB[2];  // fragment slot for k-step 0/1 (sub-tile i adds 128 i)
-};
-
-// Copy k-tile kt into stage S: 4 instructions per operand per wave, each
-// filling 1 KiB (16 rows) of the stage; lane l fills slot base + l. Past the
-// last k-tile the offset leaves the resource, so the copy writes zeros
-// without touching memory and the vmcnt bookkeeping stays uniform.
-template <int S>
-__device__ __forceinline__ void dma_tile(const GemmCtx& c, int kt) {
-  const int kofs = kt < c.KT ? kt * (BK * 2) : c.oob;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsA, AWQ_LDS(stage_a<S>() + (c.wave * 4 + j) * 64),
-                                             16, c.voff[j] + kofs, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsB, AWQ_LDS(stage_b<S>() + (c.wave * 4 + j) * 64),
-                                             16, c.voff[j] + kofs, 0, 0, 0);
-  }
-}
-
-// A and B with their own row strides (in elements). With pair_b, A's
-// contraction alternates 128-wide blocks P_0, Q_0, P_1, Q_1, ... and B's
-// k-tile for A's k-tile kt is (kt / 8)·4 + kt % 4, so each 128-wide block of
-// B is read twice in a row and one k-loop gives Σ_c (P_c + Q_c)·B_cᵀ.
-struct GemmCtx2 {
-  __amdgpu_buffer_rsrc_t rsA, rsB;
-  int voffA[4], voffB[4];
-  int wave, KT, oobA, oobB;
-  bool pair_b;
-  int rdA[2], rdB[2];
-};
-
-template <int S>
-__device__ __forceinline__ void dma_tile(const GemmCtx2& c, int kt) {
-  const bool in = kt < c.KT;
-  const int ktb = c.pair_b ? ((kt >> 3) << 2) | (kt & 3) : kt;
-  const int kofsA = in ? kt * (BK * 2) : c.oobA;
-  const int kofsB = in ? ktb * (BK * 2) : c.oobB;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsA, AWQ_LDS(stage_a<S>() + (c.wave * 4 + j) * 64),
-                                             16, c.voffA[j] + kofsA, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsB, AWQ_LDS(stage_b<S>() + (c.wave * 4 + j) * 64),
-                                             16, c.voffB[j] + kofsB, 0, 0, 0);
-  }
-}
-
 template <int S, class V, class Ctx>
 __device__ __forceinline__ void read_frags(const Ctx& c, int ks, V (&fa)[4], V (&fb)[4]) {
 #pragma unroll
@@ -193,138 +141,6 @@ __device__ __forceinline__ void mfma_4x4(floatx16 (&acc)[4][4], const V (&fa)[4]
     for (int j = 0; j < 4; ++j) acc[i][j] = mfma(fa[i], fb[j], acc[i][j]);
 }
 
-// Region kt (stage S = kt % 4), between two barriers:
-//   DMA of k-tile kt+3 into stage (kt+3) % 4 (last read before this region),
-//   MFMAs of (kt-1, k-step 1) from F1 while F0 <- (kt, k-step 0) is read,
-//   MFMAs of (kt, k-step 0) from F0 while F1 <- (kt, k-step 1) is read,
-//   then wait for this wave's LDS reads and for its DMA of k-tile kt+1
-//   (two k-tiles = 16 copies may stay in flight) and meet at the barrier.
-template <int S, bool PREV, class V, class Ctx>
-__device__ __forceinline__ void region(const Ctx& c, int kt, floatx16 (&acc)[4][4],
-                                       V (&f0a)[4], V (&f0b)[4], V (&f1a)[4], V (&f1b)[4]) {
-  dma_tile<(S + 3) & 3>(c, kt + 3);
-  if (PREV) mfma_4x4(acc, f1a, f1b);
-  read_frags<S>(c, 0, f0a, f0b);
-  mfma_4x4(acc, f0a, f0b);
-  read_frags<S>(c, 1, f1a, f1b);
-  // The 8 copies are spread one per two MFMAs over the 16 MFMAs of (kt-1, 1)
-  // so that the LDS writes they cause interleave with the fragment reads
-  // instead of arriving in one burst.
-  if (PREV) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      if (i & 1) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      if (i & 1) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(kSgMfma, 8, 0);
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  __builtin_amdgcn_s_waitcnt(wait_vm(16));
-  region_barrier();
-}
-
-// Sets up the copy offsets and fragment slots of one 256x256 tile whose A
-// rows start at A (rows_a valid rows) and B rows at B (rows_b valid rows).
-__device__ __forceinline__ void gemm_setup(GemmCtx& c, const uint16_t* A, int64_t rows_a,
-                                           const uint16_t* B, int64_t rows_b, int64_t K) {
-  c.rsA = tile_rsrc(A, rows_a, K);
-  c.rsB = tile_rsrc(B, rows_b, K);
-  const int tid = threadIdx.x, lane = tid & 63;
-  c.wave = tid >> 6;
-  c.KT = int(K / BK);
-  c.oob = BM * int(K) * 2;  // beyond every row of the tile
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // Slot p of a stage holds chunk (p & 3) ^ ((row >> 2) & 3) of row p >> 2.
-    const int p = (c.wave * 4 + j) * 64 + lane;
-    const int row = p >> 2;
-    const int chunk = (p & 3) ^ ((row >> 2) & 3);
-    c.voff[j] = (row * int(K) + chunk * 8) * 2;
-  }
-  const int wm = c.wave >> 1, wn = c.wave & 1;
-  const int fr = lane & 31, fh = lane >> 5;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    c.rdA[ks] = swz(wm * 128 + fr, 2 * ks + fh);
-    c.rdB[ks] = swz(wn * 128 + fr, 2 * ks + fh);
-  }
-}
-
-// Setup for GemmCtx2: A rows of lda elements, B rows of ldb elements, A's
-// contraction KA elements (a multiple of 128). B is read over KA as well, or
-// with pair_b (KA a multiple of 256) over KA / 2, each 128-wide block twice.
-__device__ __forceinline__ void gemm_setup2(GemmCtx2& c, const uint16_t* A, int64_t rows_a,
-                                            int64_t lda, const uint16_t* B, int64_t rows_b,
-                                            int64_t ldb, int64_t KA, bool pair_b) {
-  c.rsA = tile_rsrc(A, rows_a, lda);
-  c.rsB = tile_rsrc(B, rows_b, ldb);
-  const int tid = threadIdx.x, lane = tid & 63;
-  c.wave = tid >> 6;
-  c.KT = int(KA / BK);
-  c.pair_b = pair_b;
-  c.oobA = BM * int(lda) * 2;
-  c.oobB = BN * int(ldb) * 2;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int p = (c.wave * 4 + j) * 64 + lane;
-    const int row = p >> 2;
-    const int chunk = (p & 3) ^ ((row >> 2) & 3);
-    c.voffA[j] = (row * int(lda) + chunk * 8) * 2;
-    c.voffB[j] = (row * int(ldb) + chunk * 8) * 2;
-  }
-  const int wm = c.wave >> 1, wn = c.wave & 1;
-  const int fr = lane & 31, fh = lane >> 5;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    c.rdA[ks] = swz(wm * 128 + fr, 2 * ks + fh);
-    c.rdB[ks] = swz(wn * 128 + fr, 2 * ks + fh);
-  }
-}
-
-// The whole k-loop of one tile: acc[i][j] (wave (wm, wn), sub-tile (i, j))
-// receives Σ_k A·Bᵀ. K must be a multiple of 128 (the number of 32-wide
-// k-tiles a multiple of 4).
-template <bool F16, class Ctx>
-__device__ __forceinline__ void gemm_mainloop(const Ctx& c, floatx16 (&acc)[4][4]) {
-  typedef typename Operand<F16>::type V;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  dma_tile<0>(c, 0);
-  dma_tile<1>(c, 1);
-  dma_tile<2>(c, 2);
-  __builtin_amdgcn_s_waitcnt(wait_vm(16));  // k-tile 0 landed; 1 and 2 in flight
-  region_barrier();
-  V f0a[4], f0b[4], f1a[4], f1b[4];
-  region<0, false>(c, 0, acc, f0a, f0b, f1a, f1b);
-  int kt = 1;
-  for (; kt + 4 < c.KT; kt += 4) {
-    region<1, true>(c, kt, acc, f0a, f0b, f1a, f1b);
-    region<2, true>(c, kt + 1, acc, f0a, f0b, f1a, f1b);
-    region<3, true>(c, kt + 2, acc, f0a, f0b, f1a, f1b);
-    region<0, true>(c, kt + 3, acc, f0a, f0b, f1a, f1b);
-  }
-  region<1, true>(c, kt, acc, f0a, f0b, f1a, f1b);
-  region<2, true>(c, kt + 1, acc, f0a, f0b, f1a, f1b);
-  region<3, true>(c, kt + 2, acc, f0a, f0b, f1a, f1b);
-  mfma_4x4(acc, f1a, f1b);
-}
-
 // The same tile, wave layout, MFMAs and fragment order with 64-wide k-tiles
 // in a 2-stage ring (2 x 64 KiB): the search GEMM's main loop. Each region
 // (one 64-wide k-tile, 4 k-steps of 16) issues the DMA of k-tile kt + 1
@@ -347,8 +163,11 @@ __device__ __forceinline__ uint4* stage64_b() { return S == 0 ? s64B0 : s64B1; }
 __device__ __forceinline__ int swz64(int row, int chunk) {
   return row * CH64 + (chunk ^ ((row >> 1) & 7));
 }
-// A and B with their own row strides (elements); pair_b as in GemmCtx2, at
-// 64-wide k-tiles: A's k-tile kt reads B's k-tile (kt / 4)·2 + kt % 2.
+// A and B with their own row strides (elements). With pair_b, A's
+// contraction alternates 128-wide blocks P_0, Q_0, P_1, Q_1, ... and each
+// 128-wide block of B is read twice in a row, so one k-loop gives
+// Σ_c (P_c + Q_c)·B_cᵀ: A's 64-wide k-tile kt reads B's k-tile
+// (kt / 4)·2 + kt % 2.
 // Copy j of a wave fills rows 8·j further down than copy 0, so its source
 // offset is a per-lane base (two of them: the swizzle flips by 4 on odd j)
 // plus a uniform step j·8·ld·2 bytes, which goes in the scalar offset.
