@@ -9,8 +9,9 @@
 // output tile is ever written: the epilogue squares the fp32 accumulators and
 // sums them per output column.
 //
-// bf16 path: the MFMA main loop of gemm_core.h (256x256 tiles, 4-stage
-// LDS-DMA ring, XCD-aware tile order) with X as the A operand and E as B.
+// bf16 path: the 16x16x32 MFMA main loop of gemm_core.h (256x256 tiles,
+// 2-stage LDS-DMA ring of 64-wide k-tiles, XCD-aware tile order) with X as
+// the A operand and E as B.
 // Each XCD runs 4 token tiles x 8 candidate tiles at a time while all XCDs
 // share the same 8 candidate tiles (one E panel fetch per group of 32 token
 // tiles; X panels stay in the last-level cache).
@@ -21,8 +22,8 @@
 namespace awq {
 namespace {
 
-// K must be a multiple of 128 (so the number of 32-wide k-tiles is a multiple
-// of 4). F16: fp16 operands instead of bf16 (the same tile, the fp16 MFMA).
+// K must be a multiple of 128 (the entry points check it). F16: fp16
+// operands instead of bf16 (the same tile, the fp16 MFMA).
 template <bool F16>
 __device__ __forceinline__ void search_gemm_16(const uint16_t* __restrict__ X,
                                                const uint16_t* __restrict__ E, int64_t M,
@@ -35,25 +36,27 @@ __device__ __forceinline__ void search_gemm_16(const uint16_t* __restrict__ X,
   const int64_t rows_b = Nc - n0 < BN ? Nc - n0 : BN;
   GemmCtx64 c;
   gemm_setup64(c, X + m0 * K, rows_a, E + n0 * K, rows_b, K);
-  floatx16 acc[4][4];
-  gemm_mainloop64<F16>(c, acc);
+  floatx4 acc[8][8];
+  gemm_mainloop16<F16>(c, acc);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wm = c.wave >> 1, wn = c.wave & 1;
 
-  // Epilogue: each lane's 16 accumulators of sub-tile (i, j) all lie in output
-  // column j*32 + lane%32 of the wave's range; lanes l and l^32 share it.
+  // Epilogue: each lane's 4 accumulators of block (i, j) all lie in output
+  // column j*16 + lane%16 of the wave's range; lanes l, l^16, l^32, l^48
+  // share it.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   float* red = reinterpret_cast<float*>(s64A0);  // [2][BN]
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 8; ++j) {
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s += acc[i][j][v] * acc[i][j][v];
+      for (int v = 0; v < 4; ++v) s += acc[i][j][v] * acc[i][j][v];
+    s += __shfl_xor(s, 16);
     s += __shfl_xor(s, 32);
-    if (lane < 32) red[wm * BN + wn * 128 + j * 32 + lane] = s;
+    if (lane < 16) red[wm * BN + wn * 128 + j * 16 + lane] = s;
   }
   __syncthreads();
   const int64_t col = n0 + tid;
