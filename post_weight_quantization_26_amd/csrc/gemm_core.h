@@ -312,13 +312,28 @@ __device__ __forceinline__ void gemm_mainloop64(const GemmCtx64& c, floatx16 (&a
 // makes the register allocator shuttle 4-register tuples inside the loop).
 // The asm is volatile, so LDS reads and copies keep their source order
 // around it: the interleaving below is written out instead of requested
-// with scheduling groups. Callers wait (s_nop) before reading the AGPRs.
+// with scheduling groups. The compiler inserts no hazard waits around asm,
+// so no VALU instruction may touch the accumulators near an MFMA: the first
+// MFMA of each accumulator takes the constant 0 as its addend (no zeroing
+// moves), and the loop ends with an explicit wait tied to every
+// accumulator before anything reads them.
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void mfma16(floatx4& c, const bf16x8_t& a, const bf16x8_t& b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void mfma16(floatx4& c, const f16x8_t& a, const f16x8_t& b) {
   asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16_first(floatx4& c, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16_first(floatx4& c, const f16x8_t& a, const f16x8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
+}
+template <bool FIRST, class V>
+__device__ __forceinline__ void mfma16_acc(floatx4& c, const V& a, const V& b) {
+  if (FIRST) mfma16_first(c, a, b);
+  else mfma16(c, a, b);
 }
 // lane l supplies row l % 16 of a block and k 8·(l / 16) .. +7 of the
 // 32-wide k-step ks (chunk 4·ks + l / 16); block i is 16 rows further on,
@@ -379,14 +394,15 @@ __device__ __forceinline__ void region16(const GemmCtx64& c, const int (&rdA)[2]
 #pragma unroll
     for (int q = 0; q < 16; ++q) frag16<S>(rdA[0], rdB[0], q, f0a, f0b);
   }
+  // without PREV this is the first k-step: each accumulator starts here
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int i = q >> 1, j0 = (q & 1) * 4;
-    mfma16(acc[i][j0], f0a[i], f0b[j0]);
+    mfma16_acc<!PREV>(acc[i][j0], f0a[i], f0b[j0]);
     frag16<S>(rdA[1], rdB[1], q, f1a, f1b);
-    mfma16(acc[i][j0 + 1], f0a[i], f0b[j0 + 1]);
-    mfma16(acc[i][j0 + 2], f0a[i], f0b[j0 + 2]);
-    mfma16(acc[i][j0 + 3], f0a[i], f0b[j0 + 3]);
+    mfma16_acc<!PREV>(acc[i][j0 + 1], f0a[i], f0b[j0 + 1]);
+    mfma16_acc<!PREV>(acc[i][j0 + 2], f0a[i], f0b[j0 + 2]);
+    mfma16_acc<!PREV>(acc[i][j0 + 3], f0a[i], f0b[j0 + 3]);
   }
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
@@ -399,14 +415,11 @@ __device__ __forceinline__ void mfma_8x8(floatx4 (&acc)[8][8], const V (&fa)[8],
 #pragma unroll
     for (int j = 0; j < 8; ++j) mfma16(acc[i][j], fa[i], fb[j]);
 }
-// Ends with the accumulators safe to read (the last MFMAs have drained).
+// Writes every accumulator (no zeroing needed by the caller) and ends with
+// them safe to read (the last MFMAs have drained).
 template <bool F16>
 __device__ __forceinline__ void gemm_mainloop16(const GemmCtx64& c, floatx4 (&acc)[8][8]) {
   typedef typename Operand<F16>::type V;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
   int rdA[2], rdB[2];
   frag_offsets16(c, rdA, rdB);
   dma64<0>(c, 0);

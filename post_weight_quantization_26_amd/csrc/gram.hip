@@ -113,21 +113,22 @@ void gram_partial_kernel(const uint16_t* __restrict__ Xt, int64_t K, int64_t ldx
   const int64_t t0 = int64_t(s) * Ts;
   GemmCtx64 c;
   gemm_setup64(c, Xt + m0 * ldx + t0, rows_a, ldx, Xt + n0 * ldx + t0, rows_b, ldx, Ts, false);
-  floatx16 acc[4][4];
-  gemm_mainloop64<false>(c, acc);
+  floatx4 acc[8][8];
+  gemm_mainloop16<false>(c, acc);
 
+  // lane l of block (i, j) holds column l % 16 and rows 4·(l/16) + v
   const int lane = threadIdx.x & 63;
   const int wm = c.wave >> 1, wn = c.wave & 1;
   float* tile = P + (int64_t(s) * U + u) * (BM * BN);
-  const int row0 = wm * 128 + 4 * (lane >> 5);
-  const int col0 = wn * 128 + (lane & 31);
+  const int row0 = wm * 128 + 4 * (lane >> 4);
+  const int col0 = wn * 128 + (lane & 15);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        tile[(row0 + i * 32 + 8 * (v >> 2) + (v & 3)) * BN + col0 + j * 32] = acc[i][j][v];
+      for (int v = 0; v < 4; ++v)
+        tile[(row0 + i * 16 + v) * BN + col0 + j * 16] = acc[i][j][v];
 }
 
 // Block (u, sb): the 64x64 sub-block sb of upper tile u. Thread t takes row
@@ -211,38 +212,37 @@ void gram_search_kernel(const uint16_t* __restrict__ Gs, int64_t ldg, const uint
     GemmCtx64 c;
     gemm_setup64(c, Gs + m0 * ldg + 2 * m0, rows_a, ldg, E + n0 * K + m0, rows_b, K,
                  2 * (K - m0), true);
-    floatx16 acc[4][4];
-    gemm_mainloop64<false>(c, acc);
+    floatx4 acc[8][8];
+    gemm_mainloop16<false>(c, acc);
 
-    // Epilogue: lane l of sub-tile (i, j) holds column n = ... + l % 32 and
-    // rows 8·(v/4) + 4·(l/32) + v % 4 of the wave's 32-row block i; each
-    // group of 4 consecutive rows takes one 8-byte load of E[n][rows].
+    // Epilogue: lane l of block (i, j) holds column n = ... + l % 16 and
+    // the 4 consecutive rows 4·(l/16) + v of the wave's 16-row block i,
+    // which take one 8-byte load of E[n][rows].
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int wm = c.wave >> 1, wn = c.wave & 1;
-    const int64_t row0 = m0 + wm * 128 + 4 * (lane >> 5);
+    const int64_t row0 = m0 + wm * 128 + 4 * (lane >> 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + wn * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < 8; ++j) {
+      const int64_t n = n0 + wn * 128 + j * 16 + (lane & 15);
       float s = 0.f;
       if (n < Nc) {
         const uint16_t* en = E + n * K;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t r = row0 + i * 32 + 8 * q;      // 4 consecutive rows r..r+3
-            if (r < K) {
-              const uint2 ev = *reinterpret_cast<const uint2*>(en + r);
-              s += acc[i][j][4 * q + 0] * __uint_as_float(ev.x << 16);
-              s += acc[i][j][4 * q + 1] * __uint_as_float(ev.x & 0xFFFF0000u);
-              s += acc[i][j][4 * q + 2] * __uint_as_float(ev.y << 16);
-              s += acc[i][j][4 * q + 3] * __uint_as_float(ev.y & 0xFFFF0000u);
-            }
+        for (int i = 0; i < 8; ++i) {
+          const int64_t r = row0 + i * 16;      // 4 consecutive rows r..r+3
+          if (r < K) {
+            const uint2 ev = *reinterpret_cast<const uint2*>(en + r);
+            s += acc[i][j][0] * __uint_as_float(ev.x << 16);
+            s += acc[i][j][1] * __uint_as_float(ev.x & 0xFFFF0000u);
+            s += acc[i][j][2] * __uint_as_float(ev.y << 16);
+            s += acc[i][j][3] * __uint_as_float(ev.y & 0xFFFF0000u);
           }
+        }
       }
+      s += __shfl_xor(s, 16);
       s += __shfl_xor(s, 32);
-      if (lane < 32) red[wm * BN + wn * 128 + j * 32 + lane] = s;
+      if (lane < 16) red[wm * BN + wn * 128 + j * 16 + lane] = s;
     }
     __syncthreads();
     const int64_t col = n0 + tid;
