@@ -4,34 +4,31 @@
 // row-major 16-bit operands.
 //
 //  * 256x256 block tile, four wavefronts (one per SIMD) in a 2x2 arrangement,
-//    each owning 128x128 outputs as 4x4 v_mfma_f32_32x32x16 accumulators
-//    (bf16 or fp16 operands, 256 AGPRs).
+//    each owning 128x128 outputs as 8x8 blocks of v_mfma_f32_16x16x32
+//    accumulators (bf16 or fp16 operands, 256 AGPRs). On random data the
+//    16x16x32 form sustains a higher rate than 32x32x16 under the chip's
+//    power limit. Its accumulators are pinned to AGPRs through inline asm
+//    (gemm_mainloop16, below).
 //  * K advances in 64-wide k-tiles through a 2-stage LDS ring (2 x 64 KiB)
 //    filled by buffer_load_dwordx4 ... lds (no staging registers). Loads go
 //    through a buffer resource per tile, so rows past the end of A or B read
-//    as zero. One k-tile per barrier-delimited region (gemm_mainloop64,
-//    below).
+//    as zero. One k-tile per barrier-delimited region.
 //  * Each LDS stage is its own __shared__ array and the k-loop is unrolled
 //    over the stages, so the compiler can tell the stage being read from the
 //    stage the DMA writes and does not serialise LDS reads behind the DMA.
 //  * Workgroups are mapped so each XCD runs 4 A tiles x 8 B tiles at a time
 //    while all XCDs share the same 8 B tiles.
-//  * The search GEMM runs the same ring with v_mfma_f32_16x16x32 instead
-//    (gemm_mainloop16: 8x8 blocks of 16x16 per wave, still 256 AGPRs). On
-//    random data the 16x16x32 form sustains a higher rate than 32x32x16
-//    under the chip's power limit, and the loop is ~9% faster end to end.
-//    Its accumulators are pinned to AGPRs through inline asm.
 //
-// The 32-wide, 4-stage ring (stage_a/stage_b, swz, read_frags) serves the
-// W4A16 GEMM that dequantises on the fly, whose B tile is written into LDS
-// from registers: 32-wide k-tiles with 64-byte LDS rows (4 chunks of 16 B,
-// the chunk index XORed by (row >> 2) & 3, which keeps 16-lane ds_read_b128
-// fragment reads free of bank conflicts).
+// The 32-wide, 4-stage ring with 4x4 blocks of v_mfma_f32_32x32x16 per wave
+// (stage_a/stage_b, swz, read_frags, mfma_4x4) serves the W4A16 GEMM that
+// dequantises on the fly, whose B tile is written into LDS from registers:
+// 32-wide k-tiles with 64-byte LDS rows (4 chunks of 16 B, the chunk index
+// XORed by (row >> 2) & 3, which keeps 16-lane ds_read_b128 fragment reads
+// free of bank conflicts).
 //
-// Output layout of one 32x32 accumulator: lane l holds column l % 32; its
-// register v holds row 8·(v / 4) + 4·(l / 32) + v % 4. Of one 16x16
-// accumulator: lane l holds column l % 16; its register v holds row
-// 4·(l / 16) + v.
+// Output layout of one 16x16 accumulator: lane l holds column l % 16; its
+// register v holds row 4·(l / 16) + v. Of one 32x32 accumulator: lane l
+// holds column l % 32; its register v holds row 8·(v / 4) + 4·(l / 32) + v % 4.
 #pragma once
 
 #include "device_common.h"
@@ -148,17 +145,13 @@ __device__ __forceinline__ void mfma_4x4(floatx16 (&acc)[4][4], const V (&fa)[4]
     for (int j = 0; j < 4; ++j) acc[i][j] = mfma(fa[i], fb[j], acc[i][j]);
 }
 
-// The same tile, wave layout, MFMAs and fragment order with 64-wide k-tiles
-// in a 2-stage ring (2 x 64 KiB): the search GEMM's main loop. Each region
-// (one 64-wide k-tile, 4 k-steps of 16) issues the DMA of k-tile kt + 1
-// into the other stage (last read in region kt - 1), runs the MFMAs of the
-// previous k-step while the next fragments are read, and ends with one wait
-// (this wave's LDS reads and its DMA of kt + 1) and one barrier: half the
-// barriers per k of the 4-stage loop, at one region of copy latency hiding
-// instead of two. LDS rows are 128 bytes (8 chunks of 16 B) with the chunk
-// index XORed by (row / 2) % 8, which keeps a 16-lane fragment read on 16
-// distinct bank groups and lets the DMA fill whole rows. The k order of the
-// MFMAs is the 4-stage loop's, so the sums are bit-identical.
+// The 2-stage ring of 64-wide k-tiles (2 x 64 KiB). Each region (one k-tile)
+// issues the DMA of k-tile kt + 1 into the other stage (last read in region
+// kt - 1), runs the MFMAs of the previous k-step while the next fragments
+// are read, and ends with one wait (this wave's LDS reads and its DMA of
+// kt + 1) and one barrier. LDS rows are 128 bytes (8 chunks of 16 B) with
+// the chunk index XORed by (row / 2) % 8, which keeps a 16-lane fragment
+// read on 16 distinct bank groups and lets the DMA fill whole rows.
 constexpr int BK64 = 64;
 constexpr int CH64 = 8;
 constexpr int STAGE64 = 256 * CH64;
@@ -184,7 +177,6 @@ struct GemmCtx64 {
   int stepA, stepB;
   int wave, KT, oobA, oobB;
   bool pair_b;
-  int rdA[4], rdB[4];
 };
 __device__ __forceinline__ void gemm_setup64(GemmCtx64& c, const uint16_t* A, int64_t rows_a,
                                              int64_t lda, const uint16_t* B, int64_t rows_b,
@@ -207,13 +199,6 @@ __device__ __forceinline__ void gemm_setup64(GemmCtx64& c, const uint16_t* A, in
   }
   c.stepA = 16 * int(lda);
   c.stepB = 16 * int(ldb);
-  const int wm = c.wave >> 1, wn = c.wave & 1;
-  const int fr = lane & 31, fh = lane >> 5;
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    c.rdA[ks] = swz64(wm * 128 + fr, 2 * ks + fh);
-    c.rdB[ks] = swz64(wn * 128 + fr, 2 * ks + fh);
-  }
 }
 __device__ __forceinline__ void gemm_setup64(GemmCtx64& c, const uint16_t* A, int64_t rows_a,
                                              const uint16_t* B, int64_t rows_b, int64_t K) {
@@ -233,81 +218,7 @@ __device__ __forceinline__ void dma64(const GemmCtx64& c, int kt) {
                                              16, c.vbaseB[j & 1] + kofsB, j * c.stepB, 0, 0);
   }
 }
-template <int S, class V>
-__device__ __forceinline__ void read_frags64(const GemmCtx64& c, int ks, V (&fa)[4], V (&fb)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    fa[i] = __builtin_bit_cast(V, stage64_a<S>()[c.rdA[ks] + i * 256]);
-    fb[i] = __builtin_bit_cast(V, stage64_b<S>()[c.rdB[ks] + i * 256]);
-  }
-}
-template <int S, bool PREV, class V>
-__device__ __forceinline__ void region64(const GemmCtx64& c, int kt, floatx16 (&acc)[4][4],
-                                         V (&f0a)[4], V (&f0b)[4], V (&f1a)[4], V (&f1b)[4]) {
-  dma64<S ^ 1>(c, kt + 1);
-  if (PREV) mfma_4x4(acc, f1a, f1b);
-  read_frags64<S>(c, 0, f0a, f0b);
-  mfma_4x4(acc, f0a, f0b);
-  read_frags64<S>(c, 1, f1a, f1b);
-  mfma_4x4(acc, f1a, f1b);
-  read_frags64<S>(c, 2, f0a, f0b);
-  mfma_4x4(acc, f0a, f0b);
-  read_frags64<S>(c, 3, f1a, f1b);
-  // each phase: 16 MFMAs with the next k-step's 8 fragment reads one per
-  // two MFMAs; the 16 copies one per two MFMAs over the first two phases
-  if (PREV) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
-  }
-#pragma unroll
-  for (int ph = 0; ph < 2; ++ph) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  __builtin_amdgcn_s_waitcnt(wait_vm(0));
-  region_barrier();
-}
-template <bool F16>
-__device__ __forceinline__ void gemm_mainloop64(const GemmCtx64& c, floatx16 (&acc)[4][4]) {
-  typedef typename Operand<F16>::type V;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  dma64<0>(c, 0);
-  __builtin_amdgcn_s_waitcnt(wait_vm(0));
-  region_barrier();
-  V f0a[4], f0b[4], f1a[4], f1b[4];
-  region64<0, false>(c, 0, acc, f0a, f0b, f1a, f1b);
-  int kt = 1;
-  for (; kt + 1 < c.KT; kt += 2) {
-    region64<1, true>(c, kt, acc, f0a, f0b, f1a, f1b);
-    region64<0, true>(c, kt + 1, acc, f0a, f0b, f1a, f1b);
-  }
-  region64<1, true>(c, kt, acc, f0a, f0b, f1a, f1b);
-  mfma_4x4(acc, f1a, f1b);
-}
-
-// ---- 16x16x32 MFMAs on the same ring: 8x8 blocks of 16x16 per wave ----
+// 8x8 blocks of 16x16x32 MFMAs per wave.
 // The accumulators are pinned to AGPRs through inline asm (the builtin form
 // makes the register allocator shuttle 4-register tuples inside the loop).
 // The asm is volatile, so LDS reads and copies keep their source order

@@ -212,22 +212,23 @@ void w4a16_gemm_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
   const int64_t rows_b = N - n0 < BN ? N - n0 : BN;
   GemmCtx64 c;
   gemm_setup64(c, X + m0 * K, rows_a, Wd + n0 * K, rows_b, K);
-  floatx16 acc[4][4];
-  gemm_mainloop64<F16>(c, acc);
+  floatx4 acc[8][8];
+  gemm_mainloop16<F16>(c, acc);
 
+  // lane l of block (i, j) holds column l % 16 and rows 4·(l/16) + v
   const int lane = threadIdx.x & 63;
   const int wm = c.wave >> 1, wn = c.wave & 1;
-  const int64_t row0 = m0 + wm * 128 + 4 * (lane >> 5);
-  const int64_t col0 = n0 + wn * 128 + (lane & 31);
+  const int64_t row0 = m0 + wm * 128 + 4 * (lane >> 4);
+  const int64_t col0 = n0 + wn * 128 + (lane & 15);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = col0 + j * 32;
+    for (int j = 0; j < 8; ++j) {
+      const int64_t col = col0 + j * 16;
       if (col >= N) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = row0 + i * 32 + 8 * (v >> 2) + (v & 3);
+      for (int v = 0; v < 4; ++v) {
+        const int64_t row = row0 + i * 16 + v;
         if (row < M) Y[row * N + col] = to16<F16>(acc[i][j][v]);
       }
     }
@@ -238,8 +239,9 @@ void w4a16_gemm_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
 // tile from the packed layer through registers
 // ---------------------------------------------------------------------------
 //
-// Same tiles, ring, fragment reads and MFMAs as the search GEMM's main loop
-// (gemm_core.h); only the B operand's way into LDS differs. For each 32-wide
+// The same 256x256 tiles as the GEMM above, on the 32-wide, 4-stage ring of
+// gemm_core.h with 32x32x16 MFMAs; the B operand reaches LDS from registers
+// instead of by DMA. For each 32-wide
 // k-tile a lane loads 4 qweight words (k rows 4·kq .. 4·kq + 3 of the tile,
 // word column c8 of the output tile: outputs n0 + 8·c8 .. + 7), its group's
 // zero-point word and 8 fp16 scales. Region kt (the region whose MFMAs read
