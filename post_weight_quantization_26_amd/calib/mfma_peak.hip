@@ -1,17 +1,28 @@
-// MFMA throughput with the search GEMM's operand pattern: 4 A and 4 B fragments of random
-// bf16 per k-step, 16 accumulators, fragments rotated every k-step (register operands only).
+// Register-only MFMA throughput on random bf16 operands (no memory traffic), the two
+// shapes a 128x128 wave tile can be built from:
+//  * v_mfma_f32_32x32x16_bf16, 4x4 blocks (16 accumulators of 16 registers), builtin;
+//  * v_mfma_f32_16x16x32_bf16, 8x8 blocks (64 accumulators of 4 registers), issued from
+//    inline asm with the accumulators in AGPRs, as the search GEMM does (through the
+//    builtin the register allocator shuffles 4-register accumulators inside the loop).
+// One wave per SIMD, fragments rotated every k-step, launches alternate between the two
+// shapes so both see the same clock and temperature.
 #include <hip/hip_runtime.h>
 #include <cstdio>
 #include <cstdint>
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLaneVecs = 32;   // uint4 operand vectors per lane in the source buffer
+
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k(const uint4* src, float* out, int iters) {
+void mfma32(const uint4* src, float* out, int iters) {
+  const uint4* p = src + (blockIdx.x * 256 + threadIdx.x) * kLaneVecs;
   bf16x8_t a[2][4], b[2][4];
   for (int s = 0; s < 2; ++s)
     for (int i = 0; i < 4; ++i) {
-      a[s][i] = __builtin_bit_cast(bf16x8_t, src[(blockIdx.x * 256 + threadIdx.x) * 16 + s * 8 + i]);
-      b[s][i] = __builtin_bit_cast(bf16x8_t, src[(blockIdx.x * 256 + threadIdx.x) * 16 + s * 8 + 4 + i]);
+      a[s][i] = __builtin_bit_cast(bf16x8_t, p[s * 8 + i]);
+      b[s][i] = __builtin_bit_cast(bf16x8_t, p[s * 8 + 4 + i]);
     }
   floatx16 acc[4][4];
   for (int i = 0; i < 4; ++i) for (int j = 0; j < 4; ++j) for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
@@ -27,6 +38,48 @@ void k(const uint4* src, float* out, int iters) {
   for (int i = 0; i < 4; ++i) for (int j = 0; j < 4; ++j) for (int v = 0; v < 16; ++v) t += acc[i][j][v];
   if (t == 1.2345f) out[0] = t;
 }
+
+__device__ __forceinline__ void mfma16(floatx4& c, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma16_first(floatx4& c, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mfma16x16(const uint4* src, float* out, int iters) {
+  const uint4* p = src + (blockIdx.x * 256 + threadIdx.x) * kLaneVecs;
+  bf16x8_t a[2][8], b[2][8];
+  for (int s = 0; s < 2; ++s)
+    for (int i = 0; i < 8; ++i) {
+      a[s][i] = __builtin_bit_cast(bf16x8_t, p[s * 16 + i]);
+      b[s][i] = __builtin_bit_cast(bf16x8_t, p[s * 16 + 8 + i]);
+    }
+  floatx4 acc[8][8];
+  // the first MFMA of each accumulator adds 0, so no VALU instruction writes the AGPRs
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mfma16_first(acc[i][j], a[0][i], b[0][j]);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mfma16(acc[i][j], a[s][i], b[s][j]);
+  }
+  // the compiler does not see the MFMAs: wait for them, then tie every read to the wait
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+  float t = 0.f;
+  for (int i = 0; i < 8; ++i) for (int j = 0; j < 8; ++j) for (int v = 0; v < 4; ++v) t += acc[i][j][v];
+  if (t == 1.2345f) out[0] = t;
+}
+
 __global__ void fill(uint16_t* p, int64_t n) {
   int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   for (; i < n; i += int64_t(gridDim.x) * blockDim.x) {
@@ -34,16 +87,31 @@ __global__ void fill(uint16_t* p, int64_t n) {
     p[i] = uint16_t(__float_as_uint(float(h & 0xFFFF) / 65536.f - 0.5f) >> 16);
   }
 }
+
 int main() {
-  uint4* src; float* out; hipMalloc(&src, 256 * 256 * 16 * 16); hipMalloc(&out, 4);
-  fill<<<1024, 256>>>((uint16_t*)src, 256LL * 256 * 16 * 8); hipDeviceSynchronize();
-  hipEvent_t e0, e1; hipEventCreate(&e0); hipEventCreate(&e1);
-  const int iters = 10000;
-  for (int pass = 0; pass < 3; ++pass) {
-    hipEventRecord(e0); k<<<256, 256>>>(src, out, iters); hipEventRecord(e1); hipEventSynchronize(e1);
-    float ms; hipEventElapsedTime(&ms, e0, e1);
-    double fl = 256.0 * 4 * iters * 32 * 32768.0;
-    printf("random operands, 1 wave/SIMD: %.1f TFLOP/s (%.1f%% of 2500), %.1f ms\n", fl / ms / 1e9, fl / ms / 1e9 / 25, ms);
+  const int blocks = 256;
+  const size_t n16 = size_t(blocks) * 256 * kLaneVecs * 8;   // bf16 elements
+  uint4* src; float* out;
+  if (hipMalloc(&src, n16 * 2) != hipSuccess || hipMalloc(&out, 4) != hipSuccess) return 1;
+  fill<<<1024, 256>>>((uint16_t*)src, (int64_t)n16);
+  if (hipDeviceSynchronize() != hipSuccess) return 1;
+  hipEvent_t e0, e1;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return 1;
+  // per iteration: 32 MFMAs of 32x32x16 or 128 of 16x16x32; the same 2^20 MACs per lane group
+  const int iters32 = 10000, iters16 = 5000;
+  for (int pass = 0; pass < 4; ++pass) {
+    for (int v = 0; v < 2; ++v) {
+      if (hipEventRecord(e0) != hipSuccess) return 1;
+      if (v == 0) mfma32<<<blocks, 256>>>(src, out, iters32);
+      else mfma16x16<<<blocks, 256>>>(src, out, iters16);
+      if (hipEventRecord(e1) != hipSuccess || hipEventSynchronize(e1) != hipSuccess) return 1;
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess) return 1;
+      const double fl = v == 0 ? double(blocks) * 4 * iters32 * 32 * (2.0 * 32 * 32 * 16)
+                               : double(blocks) * 4 * iters16 * 128 * (2.0 * 16 * 16 * 32);
+      printf("pass %d  %-9s random operands, 1 wave/SIMD: %.1f TFLOP/s (%.1f%% of 2500), %.2f ms\n", pass,
+             v == 0 ? "32x32x16" : "16x16x32", fl / ms / 1e9, fl / ms / 1e9 / 25, ms);
+    }
   }
-  return 0;
+  return hipGetLastError() == hipSuccess ? 0 : 2;
 }
