@@ -11,6 +11,13 @@ Sources (titles of the pages; section names as they appear there):
   [roadmap]  "05 — AWQ: Activation-Aware Weight Scaling" (study roadmap).
   [record]   anthology-of-the-SOTA record SOTA-356, "What to do".
 
+Routes to the output error. ``output_sq_error`` forms X·Eᵀ token block by
+token block (the plain definition). ``gram_matrix`` + ``output_sq_error_gram``
+form G = XᵀX once and then e·G·eᵀ per row: the same sums in another order,
+about T/K times less work for one candidate row, which is what lets the
+oracle produce whole error curves of Llama-class layers. Both are pinned
+(pure-Python sums; each other to 1e-10).
+
 Precision. Activation statistics, the scale table, the dequantised/folded
 weights and every output error are computed in float64. The quantiser itself
 (the arithmetic that decides an integer code) runs in IEEE float32 with
@@ -215,6 +222,49 @@ def output_sq_error(X: np.ndarray, dtype: str, w32: np.ndarray, w_hat: np.ndarra
     return M
 
 
+def gram_matrix(X: np.ndarray, dtype: str, chunk: int = 4096) -> np.ndarray:
+    """G = XᵀX over all calibration tokens, float64 [K, K].
+
+    The output error of step 5 is a quadratic form in the error weights:
+    Σ_t (Σ_j x_tj·e_j)² = Σ_j Σ_k e_j·(Σ_t x_tj·x_tk)·e_k = e·G·eᵀ. G does
+    not depend on the candidate, so it is formed once; token blocks only
+    bound memory. (The identity is exact algebra, not a statement of the
+    pages; it only reorders the sums of [roadmap] §4's output error.)
+    """
+    K = X.shape[1]
+    G = np.zeros((K, K), dtype=F64)
+    for t0 in range(0, X.shape[0], chunk):
+        x = decode(X[t0:t0 + chunk], dtype).astype(F64)
+        G += x.T @ x
+    return G
+
+
+def output_sq_error_gram(G: np.ndarray, w32: np.ndarray, w_hat: np.ndarray,
+                         rows: int = 2048) -> np.ndarray:
+    """M_n = e_n·G·e_nᵀ with e_n = ŵ_n − w_n, for each row n of ``w_hat``
+    (float64): the same per-row output error as ``output_sq_error``, through
+    the Gram matrix of the activations. Row blocks only bound memory."""
+    w_hat = np.asarray(w_hat, dtype=F64)
+    w = np.asarray(w32, dtype=F64)
+    M = np.zeros(w_hat.shape[0], dtype=F64)
+    for r0 in range(0, w_hat.shape[0], rows):
+        E = w_hat[r0:r0 + rows] - w[r0:r0 + rows]
+        M[r0:r0 + rows] = ((E @ G) * E).sum(axis=1)
+    return M
+
+
+def _errors(X, dtype, w, make_candidate, n_cand, G):
+    """[n_cand, R] output errors of the candidates ``make_candidate(i)``
+    (float64 ŵ, [R, K]) on the rows ``w``: the direct route shares one pass
+    over X between all candidates; with G the Gram route takes them one by
+    one."""
+    if G is None:
+        cands = [make_candidate(i) for i in range(n_cand)]
+        M = output_sq_error(X, dtype, np.tile(w, (n_cand, 1)), np.concatenate(cands))
+        return M.reshape(n_cand, w.shape[0])
+    return np.stack([output_sq_error_gram(G, w, make_candidate(i)) for i in range(n_cand)])
+
+
 # ----------------------------------------------------------------------------
 # Steps 2-6 — the α grid search
 # ----------------------------------------------------------------------------
@@ -230,7 +280,8 @@ def candidate_weights(w32, s32, ratio, bits, group, zero_point):
     return fold(dequantize(q, step, zero, group), s32)
 
 
-def search_scale(X, W, dtype, abar, alphas, bits=4, group=128, zero_point=True, rows=None):
+def search_scale(X, W, dtype, abar, alphas, bits=4, group=128, zero_point=True, rows=None,
+                 G=None):
     """Grid search over α ([roadmap] §4; [concept] "Scaling instead of protecting").
 
     For each grid value: scale, quantise, fold back and measure the output
@@ -238,17 +289,18 @@ def search_scale(X, W, dtype, abar, alphas, bits=4, group=128, zero_point=True, 
     the R selected rows, all rows by default), ``mse`` [n_alpha] =
     Σ_n M_n / (T·R), ``index`` (argmin, lowest index on ties), ``alpha_best``,
     ``s_best`` and the whole ``s_table``. With a row subset the curve is that
-    subset's; the chosen α is then the subset's too.
+    subset's; the chosen α is then the subset's too. With ``G`` (the
+    ``gram_matrix`` of X) the errors come from the Gram route; X is then
+    used only for its token count.
     """
     alphas = np.asarray(alphas, dtype=F32)
     T = X.shape[0]
     w = _rows(W, dtype, rows)
     s_tab = scale_table(abar, alphas)
-    cands = [candidate_weights(w, s_tab[i], 1.0, bits, group, zero_point)
-             for i in range(len(alphas))]
     R = w.shape[0]
-    M = output_sq_error(X, dtype, np.tile(w, (len(alphas), 1)), np.concatenate(cands))
-    row_sums = M.reshape(len(alphas), R)
+    row_sums = _errors(X, dtype, w,
+                       lambda i: candidate_weights(w, s_tab[i], 1.0, bits, group, zero_point),
+                       len(alphas), G)
     mse = row_sums.sum(axis=1) / F64(T * R)
     best = int(np.argmin(mse))
     return dict(row_sums=row_sums, mse=mse, index=best, alpha_best=F32(alphas[best]),
@@ -259,7 +311,8 @@ def search_scale(X, W, dtype, abar, alphas, bits=4, group=128, zero_point=True, 
 # Step 7 — per-output-channel clip-ratio search
 # ----------------------------------------------------------------------------
 
-def search_clip(X, W, dtype, s32, ratios, bits=4, group=128, zero_point=True, rows=None):
+def search_clip(X, W, dtype, s32, ratios, bits=4, group=128, zero_point=True, rows=None,
+                G=None):
     """Per-output-channel clip search with s fixed ([roadmap] §4 "Optional:
     per-channel clipping": after α is picked, a clip ratio between 0.5 and
     1.0 of the maximum is searched per channel).
@@ -267,16 +320,17 @@ def search_clip(X, W, dtype, s32, ratios, bits=4, group=128, zero_point=True, ro
     Every group of row n uses that row's ratio. Row n's output error depends
     only on row n, so the per-row argmin is the joint optimum. Returns
     ``row_sums`` [n_ratio, R], ``index`` [R], ``ratio_best`` [R] and
-    ``mse_clip`` = Σ_n M_n(r*_n) / (T·R).
+    ``mse_clip`` = Σ_n M_n(r*_n) / (T·R). ``G`` selects the Gram route, as
+    in ``search_scale``.
     """
     ratios = np.asarray(ratios, dtype=F32)
     T = X.shape[0]
     w = _rows(W, dtype, rows)
     R = w.shape[0]
-    cands = [candidate_weights(w, s32, np.full(R, r, dtype=F32), bits, group, zero_point)
-             for r in ratios]
-    M = output_sq_error(X, dtype, np.tile(w, (len(ratios), 1)), np.concatenate(cands))
-    row_sums = M.reshape(len(ratios), R)
+    row_sums = _errors(X, dtype, w,
+                       lambda i: candidate_weights(w, s32, np.full(R, ratios[i], dtype=F32),
+                                                   bits, group, zero_point),
+                       len(ratios), G)
     idx = np.argmin(row_sums, axis=0)
     mse_clip = row_sums[idx, np.arange(R)].sum() / F64(T * R)
     return dict(row_sums=row_sums, index=idx, ratio_best=ratios[idx], mse_clip=F64(mse_clip))
@@ -384,7 +438,8 @@ def storage_bits_per_weight(N: int, K: int, bits: int = 4, group: int = 128) -> 
 # weights)
 # ----------------------------------------------------------------------------
 
-def search_scale_group(X, Ws, dtype, abar, alphas, bits=4, group=128, zero_point=True, rows=None):
+def search_scale_group(X, Ws, dtype, abar, alphas, bits=4, group=128, zero_point=True, rows=None,
+                       G=None):
     """α search for several linears that read the same X (for example the
     query, key and value projections after one normalisation).
 
@@ -395,7 +450,7 @@ def search_scale_group(X, Ws, dtype, abar, alphas, bits=4, group=128, zero_point
     ``search_scale``.
     """
     W = np.concatenate([np.asarray(w) for w in Ws], axis=0)
-    return search_scale(X, W, dtype, abar, alphas, bits, group, zero_point, rows=rows)
+    return search_scale(X, W, dtype, abar, alphas, bits, group, zero_point, rows=rows, G=G)
 
 
 def encode(v32: np.ndarray, dtype: str) -> np.ndarray:

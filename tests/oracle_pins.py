@@ -254,6 +254,71 @@ def check_gram_identity(O):
     assert np.allclose(M, ref, rtol=1e-10, atol=0)
 
 
+def check_gram_route(O):
+    """The oracle's Gram route (G = XᵀX once, then e·G·eᵀ per row) against
+    exact pure-Python sums on a tiny layer, and against the direct route
+    (pinned by brute force above) to 1e-10 on layers of several token blocks:
+    per row, through both searches (curve, row sums, choices) and for bf16,
+    fp16 and float32 inputs."""
+    r = _rng(12)
+    x = r.standard_normal((7, 128)).astype(F32)
+    x[:, 5] *= F32(30.0)
+    w = (r.standard_normal((3, 128)) * 0.02).astype(F32)
+    w_hat = w.astype(np.float64) + r.standard_normal((3, 128)) * 1e-3
+    G = O.gram_matrix(x, "f32", chunk=3)                   # 3 token blocks, the last ragged
+    assert G.shape == (128, 128) and G.dtype == np.float64
+    ref = _naive_sq_error(x.astype(np.float64), w.astype(np.float64), w_hat)
+    assert np.allclose(O.output_sq_error_gram(G, w, w_hat, rows=2), ref, rtol=1e-10, atol=0)
+    for dtype, (T, N, K) in (("bf16", (300, 40, 256)), ("f16", (260, 24, 384)),
+                             ("f32", (150, 16, 128))):
+        X, W = synth.make_custom(T, N, K, dtype, seed=T + N)
+        G = O.gram_matrix(X, dtype, chunk=64)
+        ab = O.act_stats(X, dtype)
+        alphas = synth.alpha_grid(5)
+        d = O.search_scale(X, W, dtype, ab, alphas, 4, 128, True)
+        g = O.search_scale(X, W, dtype, ab, alphas, 4, 128, True, G=G)
+        assert np.allclose(g["row_sums"], d["row_sums"], rtol=1e-10, atol=0)
+        assert np.allclose(g["mse"], d["mse"], rtol=1e-10, atol=0) and g["index"] == d["index"]
+        ratios = synth.ratio_grid(4)
+        dc = O.search_clip(X, W, dtype, d["s_best"], ratios, 3, 64, True)
+        gc = O.search_clip(X, W, dtype, d["s_best"], ratios, 3, 64, True, G=G)
+        assert np.allclose(gc["row_sums"], dc["row_sums"], rtol=1e-10, atol=0)
+        assert np.allclose(gc["mse_clip"], dc["mse_clip"], rtol=1e-10, atol=0)
+        gw = O.decode(W, dtype)
+        assert np.allclose(O.output_sq_error_gram(G, gw, O.candidate_weights(
+            gw, d["s_best"], 1.0, 4, 128, True), rows=7), d["row_sums"][d["index"]],
+            rtol=1e-10, atol=0)
+
+
+def _f16_value(p):
+    """IEEE binary16 bit pattern -> value, from its fields (pure Python)."""
+    sign = -1.0 if p >> 15 else 1.0
+    e, m = (p >> 10) & 0x1F, p & 0x3FF
+    if e == 0x1F:
+        return sign * math.inf if m == 0 else math.nan
+    if e == 0:
+        return sign * math.ldexp(m, -24)                   # subnormal: m·2^-24
+    return sign * math.ldexp(1024 + m, e - 25)             # (1 + m/1024)·2^(e-15)
+
+
+def check_decode_f16_exhaustive(O):
+    """fp16 inputs: every one of the 65,536 bit patterns decodes to the value
+    its sign, exponent and significand fields give (IEEE binary16), in
+    float32 (which holds every binary16 value exactly); NaN patterns give
+    NaN. The bf16 and float32 decodings are checked on a few hand values."""
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = O.decode(pats, "f16")
+    assert got.dtype == np.float32 and got.shape == (65536,)
+    ref = np.array([_f16_value(int(p)) for p in range(65536)], dtype=np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].astype(np.float64), ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))   # -0 stays -0
+    assert list(O.decode(np.array([0x3F80, 0xC040, 0x0001], np.uint16), "bf16")) == \
+        [1.0, -3.0, math.ldexp(1.0, -133)]
+    assert O.decode(np.array([[0.25]], np.float32), "f32")[0, 0] == 0.25
+
+
 # ----------------------------------------------------------------------------
 # searches
 # ----------------------------------------------------------------------------
@@ -689,4 +754,5 @@ ALL_CHECKS = [
     check_pack_overflow_flag, check_search_group, check_encode_bf16_exhaustive,
     check_encode_f16_examples, check_fold_norm, check_fold_linear, check_pack_int3_layout,
     check_group_size_gain, check_w4a16_exact_layer, check_w4a16_bruteforce,
+    check_gram_route, check_decode_f16_exhaustive,
 ]

@@ -98,6 +98,22 @@ MUTATIONS = [
      "b = None if beta is None else np.asarray(beta)", [P.check_fold_norm]),
     ("previous linear folded along its input dim", "_divide_stored(W_prev, dtype, s[:, None])",
      "_divide_stored(W_prev, dtype, s[None, :])", [P.check_fold_linear]),
+    ("fp16 bits read as bf16", "return np.asarray(a, dtype=np.uint16).view(np.float16).astype(F32)",
+     "return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(F32)",
+     [P.check_decode_f16_exhaustive]),
+    ("fp16 bit patterns converted as integers",
+     "return np.asarray(a, dtype=np.uint16).view(np.float16).astype(F32)",
+     "return np.asarray(a, dtype=np.uint16).astype(np.float16).astype(F32)",
+     [P.check_decode_f16_exhaustive]),
+    ("Gram matrix keeps only the last token block", "        G += x.T @ x", "        G = x.T @ x",
+     [P.check_gram_route]),
+    ("Gram route measures the candidate's weights, not its error",
+     "        E = w_hat[r0:r0 + rows] - w[r0:r0 + rows]", "        E = w_hat[r0:r0 + rows]",
+     [P.check_gram_route]),
+    ("Gram route keeps only G's diagonal", "        M[r0:r0 + rows] = ((E @ G) * E).sum(axis=1)",
+     "        M[r0:r0 + rows] = ((E * np.diag(G)) * E).sum(axis=1)", [P.check_gram_route]),
+    ("Gram route from X·Xᵀ", "        G += x.T @ x", "        G += (x @ x.T)[:K, :K]",
+     [P.check_gram_route]),
 ]
 
 
