@@ -81,17 +81,32 @@ typedef enum { AWQ_F32 = 0, AWQ_BF16 = 1, AWQ_F16 = 2 } awq_dtype;
 
 /* Quantiser parameters. w_bit: 4 or 3. group_size: 32, 64 or 128.
  * zero_point: 1 = asymmetric min-max with an integer zero point,
- * 0 = symmetric (zero point fixed at 2^(w_bit-1)). */
+ * 0 = symmetric (zero point fixed at 2^(w_bit-1)).
+ * flags: 0, or AWQ_SEARCH_SPLIT_E for the direct searches (awq_search_scale,
+ * awq_search_clip, awq_search_scale_group) on bf16 or fp16 layers: each
+ * candidate's error weight e = ŵ - w goes to the matrix cores as two 16-bit
+ * halves, hi = rnd(e) and lo = rnd(e - hi), instead of one rounding. The
+ * per-row output errors then carry only float32 accumulation error (about
+ * 16 significand bits in the operand instead of 8 for bf16 or 11 for fp16),
+ * for twice the search GEMM's work and twice its candidate buffer (size the
+ * workspace with AWQ_OP_SEARCH_SCALE_SPLIT_E / AWQ_OP_SEARCH_CLIP_SPLIT_E).
+ * Float32 layers already use float32 operands and ignore the flag; the Gram
+ * searches reject it (AWQ_E_UNSUPPORTED); awq_quantize_pack ignores it. */
 typedef struct {
   int32_t w_bit;
   int32_t group_size;
   int32_t zero_point;
+  int32_t flags;
 } awq_qconfig;
+
+enum { AWQ_SEARCH_SPLIT_E = 1 };
 
 enum { AWQ_OP_STATS = 0, AWQ_OP_SEARCH_SCALE = 1, AWQ_OP_SEARCH_CLIP = 2, AWQ_OP_PACK = 3,
        AWQ_OP_SEARCH_SCALE_GRAM = 4, AWQ_OP_SEARCH_CLIP_GRAM = 5,
        /* awq_gram_build, and the Gram searches that take a prepared G */
-       AWQ_OP_GRAM_BUILD = 6, AWQ_OP_SEARCH_SCALE_GRAM_G = 7, AWQ_OP_SEARCH_CLIP_GRAM_G = 8 };
+       AWQ_OP_GRAM_BUILD = 6, AWQ_OP_SEARCH_SCALE_GRAM_G = 7, AWQ_OP_SEARCH_CLIP_GRAM_G = 8,
+       /* the direct searches with qc.flags = AWQ_SEARCH_SPLIT_E (bf16, fp16) */
+       AWQ_OP_SEARCH_SCALE_SPLIT_E = 9, AWQ_OP_SEARCH_CLIP_SPLIT_E = 10 };
 
 /* Workspace bytes that let `op` process all `n_grid` candidates in one
  * batch (the fastest configuration). Returns 0 for invalid sizes. Pure host
@@ -99,7 +114,8 @@ enum { AWQ_OP_STATS = 0, AWQ_OP_SEARCH_SCALE = 1, AWQ_OP_SEARCH_CLIP = 2, AWQ_OP
 size_t awq_workspace_bytes(int op, int64_t T, int64_t N, int64_t K, int32_t n_grid,
                            awq_dtype dtype);
 
-/* Workspace bytes for a search (AWQ_OP_SEARCH_SCALE / AWQ_OP_SEARCH_CLIP)
+/* Workspace bytes for a search (AWQ_OP_SEARCH_SCALE / AWQ_OP_SEARCH_CLIP and
+ * their _SPLIT_E and Gram forms)
  * that works through its `n_grid` candidates in batches of at most `batch`
  * (1 <= batch <= n_grid; batch 1 is the minimum any search call accepts).
  * A search call picks the largest batch its workspace allows; results do not

@@ -19,10 +19,10 @@ hipError_t launch_reciprocal(const float* s, int64_t n, float* s_copy, float* in
                              hipStream_t st);
 hipError_t launch_transform(const void* W, int dtype, int64_t N, int64_t K, const float* s_rows,
                             const float* inv_rows, int64_t s_stride, const float* ratios_host,
-                            int nc, int bits, int group, int zero_point, void* E,
+                            int nc, int bits, int group, int zero_point, int split, void* E,
                             int64_t cand_stride, hipStream_t st);
 hipError_t launch_search_gemm(const void* X, int dtype, const void* E, int64_t M, int64_t Nc,
-                              int64_t K, float* partials, hipStream_t st);
+                              int64_t K, int split, float* partials, hipStream_t st);
 hipError_t launch_reduce_rows(const float* partials, int64_t MT, int64_t Nc, double* row_sums,
                               hipStream_t st);
 hipError_t launch_curve(const double* row_sums, int n_cand, int64_t N, double denom,
@@ -160,13 +160,16 @@ awq_status run_batch(const void* X, const Segment* seg, int n_seg, awq_dtype d, 
                      const uint16_t* Gs = nullptr) {
   void* E = at<void>(ws, L.E);
   float* partials = at<float>(ws, L.partials);
+  // split candidates: each row is a hi and a lo half (2K elements)
+  const int split = splits_e(qc, d);
+  const int64_t row_len = split ? 2 * K : K;
   for (int l = 0; l < n_seg; ++l) {
-    void* E_l = static_cast<char*>(E) + size_t(seg[l].row0) * size_t(K) * dtype_bytes(d);
+    void* E_l = static_cast<char*>(E) + size_t(seg[l].row0) * size_t(row_len) * dtype_bytes(d);
     AWQ_HIP(timed(AWQ_K_TRANSFORM, st,
                   [&] {
                     return launch_transform(seg[l].W, dt(d), seg[l].N, K, s_rows, inv_rows,
                                             s_stride, ratios_host, cb, qc.w_bit, qc.group_size,
-                                            qc.zero_point, E_l, N * K, st);
+                                            qc.zero_point, split, E_l, N * row_len, st);
                   }),
             "transform");
   }
@@ -177,7 +180,8 @@ awq_status run_batch(const void* X, const Segment* seg, int n_seg, awq_dtype d, 
   else
     AWQ_HIP(timed(AWQ_K_GEMM, st,
                   [&] {
-                    return launch_search_gemm(X, dt(d), E, T, int64_t(cb) * N, K, partials, st);
+                    return launch_search_gemm(X, dt(d), E, T, int64_t(cb) * N, K, split,
+                                              partials, st);
                   }),
             "search_gemm");
   AWQ_HIP(timed(AWQ_K_REDUCE, st,
@@ -286,7 +290,7 @@ awq_status search_scale_impl(int op, const void* X, const Segment* seg, int n_se
                              const float* alphas, int32_t n_alpha, awq_qconfig qc, float* s_best,
                              float* alpha_best, double* mse, double* row_sums, void* ws,
                              int32_t nb, hipStream_t st) {
-  const SearchLayout L = search_layout(op, T, N, K, n_alpha, nb, dtype);
+  const SearchLayout L = search_layout(layout_op(op, qc, dtype), T, N, K, n_alpha, nb, dtype);
   const uint16_t* Gs = nullptr;
   if (builds_gram(op)) {
     awq_status g = build_gram(X, T, K, L, ws, st);
@@ -461,7 +465,7 @@ awq_status search_clip_impl(int op, const void* X, const void* W, awq_dtype dtyp
                             int64_t N, int64_t K, const float* s, const float* ratios,
                             int32_t n_ratio, awq_qconfig qc, float* ratio_best, double* mse_clip,
                             double* row_sums, void* ws, int32_t nb, hipStream_t st) {
-  const SearchLayout L = search_layout(op, T, N, K, n_ratio, nb, dtype);
+  const SearchLayout L = search_layout(layout_op(op, qc, dtype), T, N, K, n_ratio, nb, dtype);
   double* rs = at<double>(ws, L.row_sums);
   double* best = at<double>(ws, L.best);
   double* mc = at<double>(ws, L.scalar);

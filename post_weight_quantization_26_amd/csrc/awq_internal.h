@@ -32,7 +32,7 @@ int64_t stats_chunks(int64_t T, int64_t K, awq_dtype d);
 struct SearchLayout {
   size_t s_table;   // [n_grid, K] f32 scale table (clip search: aligned copy of s, [K])
   size_t inv;       // [n_grid, K] f32 reciprocal scales (clip search: [K])
-  size_t E;         // [nb, N, K] candidate error weights (bf16 or f32)
+  size_t E;         // [nb, N, K] candidate error weights (bf16, fp16 or f32; split: [nb, N, 2K])
   size_t partials;  // [MT, nb*N] f32 per-tile column sums of squares
   size_t row_sums;  // [n_grid, N] f64
   size_t mse;       // [n_grid] f64
@@ -72,7 +72,29 @@ inline bool is_gram_op(int op) {
 }
 inline bool is_scale_op(int op) {
   return op == AWQ_OP_SEARCH_SCALE || op == AWQ_OP_SEARCH_SCALE_GRAM ||
-         op == AWQ_OP_SEARCH_SCALE_GRAM_G;
+         op == AWQ_OP_SEARCH_SCALE_GRAM_G || op == AWQ_OP_SEARCH_SCALE_SPLIT_E;
+}
+// Direct searches whose candidates are hi/lo halves (rows of 2K elements).
+inline bool is_split_op(int op) {
+  return op == AWQ_OP_SEARCH_SCALE_SPLIT_E || op == AWQ_OP_SEARCH_CLIP_SPLIT_E;
+}
+inline int unsplit_op(int op) {
+  return op == AWQ_OP_SEARCH_SCALE_SPLIT_E ? AWQ_OP_SEARCH_SCALE
+         : op == AWQ_OP_SEARCH_CLIP_SPLIT_E ? AWQ_OP_SEARCH_CLIP
+                                            : op;
+}
+// The search splits the candidates' error weights: asked for, on a 16-bit
+// layer (float32 layers keep float32 operands).
+inline bool splits_e(awq_qconfig qc, awq_dtype d) {
+  return (qc.flags & AWQ_SEARCH_SPLIT_E) && d != AWQ_F32;
+}
+// The op whose workspace layout a search call uses: its split form when the
+// call splits its candidates.
+inline int layout_op(int op, awq_qconfig qc, awq_dtype d) {
+  if (!splits_e(qc, d)) return op;
+  if (op == AWQ_OP_SEARCH_SCALE) return AWQ_OP_SEARCH_SCALE_SPLIT_E;
+  if (op == AWQ_OP_SEARCH_CLIP) return AWQ_OP_SEARCH_CLIP_SPLIT_E;
+  return op;
 }
 // Xt and the partial tiles of a G build (the first part of a building Gram
 // search's workspace, and the whole workspace of awq_gram_build).

@@ -17,18 +17,20 @@ hipError_t launch_reciprocal(const float* s, int64_t n, float* s_copy, float* in
 // Candidate error weights E[c] = fold(dequant(quant(W·diag(s_c), r_c))) - W for
 // c in [0, nc): scale rows `s_rows` (s_stride 0 = one shared row) and clip
 // ratios `ratios_host` (NULL = all 1). Candidate c's [N, K] block starts at
-// element c·cand_stride of E.
+// element c·cand_stride of E. split (16-bit types): rows of 2K elements, hi
+// and lo halves in alternating 128-wide blocks.
 hipError_t launch_transform(const void* W, int dtype, int64_t N, int64_t K, const float* s_rows,
                             const float* inv_rows, int64_t s_stride, const float* ratios_host,
-                            int nc, int bits, int group, int zero_point, void* E,
+                            int nc, int bits, int group, int zero_point, int split, void* E,
                             int64_t cand_stride, hipStream_t st);
 // In-place fold of 1/s: v[j] /= s[j] (j < K); rows of W [K, K_prev] /= s[row].
 hipError_t launch_fold_vec(void* v, int dtype, int64_t K, const float* s, hipStream_t st);
 hipError_t launch_fold_rows(void* W, int dtype, int64_t K, int64_t K_prev, const float* s,
                             hipStream_t st);
-// partials[mt][c] = Σ_{t in tile mt} (X·Eᵀ)[t][c]² for c in [0, Nc).
+// partials[mt][c] = Σ_{t in tile mt} (X·Eᵀ)[t][c]² for c in [0, Nc); with
+// split, E rows are hi/lo halves (2K elements) and the product is X·(hi+lo)ᵀ.
 hipError_t launch_search_gemm(const void* X, int dtype, const void* E, int64_t M, int64_t Nc,
-                              int64_t K, float* partials, hipStream_t st);
+                              int64_t K, int split, float* partials, hipStream_t st);
 hipError_t launch_reduce_rows(const float* partials, int64_t MT, int64_t Nc, double* row_sums,
                               hipStream_t st);
 hipError_t launch_curve(const double* row_sums, int n_cand, int64_t N, double denom,

@@ -16,6 +16,13 @@
 // share the same 8 candidate tiles (one E panel fetch per group of 32 token
 // tiles; X panels stay in the last-level cache).
 //
+// Split operands: E may instead hold each candidate row as two 16-bit halves,
+// hi = rnd(e) and lo = rnd(e - hi), alternating in 128-wide blocks
+// [hi_0 | lo_0 | hi_1 | lo_1 | ...] (row length 2K). The main loop then reads
+// each 128-wide block of X twice (its pair_a mode), so the accumulators hold
+// X·(hi + lo)ᵀ: the candidate operand carries ~16 significand bits instead of
+// 8 (bf16) or 11 (fp16), for twice the MFMA work.
+//
 // fp32 path: a plain LDS-tiled FMA kernel (64x64 tiles) for float32 layers.
 #include "gemm_core.h"
 
@@ -23,8 +30,9 @@ namespace awq {
 namespace {
 
 // K must be a multiple of 128 (the entry points check it). F16: fp16
-// operands instead of bf16 (the same tile, the fp16 MFMA).
-template <bool F16>
+// operands instead of bf16 (the same tile, the fp16 MFMA). SPLIT: E rows are
+// hi/lo halves of length 2K.
+template <bool F16, bool SPLIT>
 __device__ __forceinline__ void search_gemm_16(const uint16_t* __restrict__ X,
                                                const uint16_t* __restrict__ E, int64_t M,
                                                int64_t Nc, int64_t K, int tiles_m, int tiles_n,
@@ -35,7 +43,10 @@ __device__ __forceinline__ void search_gemm_16(const uint16_t* __restrict__ X,
   const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
   const int64_t rows_b = Nc - n0 < BN ? Nc - n0 : BN;
   GemmCtx64 c;
-  gemm_setup64(c, X + m0 * K, rows_a, E + n0 * K, rows_b, K);
+  if (SPLIT)
+    gemm_setup64(c, X + m0 * K, rows_a, K, E + n0 * 2 * K, rows_b, 2 * K, 2 * K, false, true);
+  else
+    gemm_setup64(c, X + m0 * K, rows_a, E + n0 * K, rows_b, K);
   floatx4 acc[8][8];
   gemm_mainloop16<F16>(c, acc);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -67,14 +78,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void search_gemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ E,
                              int64_t M, int64_t Nc, int64_t K, int tiles_m, int tiles_n,
                              float* __restrict__ partials) {
-  search_gemm_16<false>(X, E, M, Nc, K, tiles_m, tiles_n, partials);
+  search_gemm_16<false, false>(X, E, M, Nc, K, tiles_m, tiles_n, partials);
 }
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void search_gemm_f16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ E,
                             int64_t M, int64_t Nc, int64_t K, int tiles_m, int tiles_n,
                             float* __restrict__ partials) {
-  search_gemm_16<true>(X, E, M, Nc, K, tiles_m, tiles_n, partials);
+  search_gemm_16<true, false>(X, E, M, Nc, K, tiles_m, tiles_n, partials);
+}
+
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void search_gemm_bf16_split_kernel(const uint16_t* __restrict__ X,
+                                   const uint16_t* __restrict__ E, int64_t M, int64_t Nc,
+                                   int64_t K, int tiles_m, int tiles_n,
+                                   float* __restrict__ partials) {
+  search_gemm_16<false, true>(X, E, M, Nc, K, tiles_m, tiles_n, partials);
+}
+
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void search_gemm_f16_split_kernel(const uint16_t* __restrict__ X,
+                                  const uint16_t* __restrict__ E, int64_t M, int64_t Nc,
+                                  int64_t K, int tiles_m, int tiles_n,
+                                  float* __restrict__ partials) {
+  search_gemm_16<true, true>(X, E, M, Nc, K, tiles_m, tiles_n, partials);
 }
 
 // ---------------------------------------------------------------------------
@@ -139,19 +166,25 @@ __global__ __launch_bounds__(256) void search_gemm_f32_kernel(const float* __res
 }  // namespace
 
 hipError_t launch_search_gemm(const void* X, int dtype, const void* E, int64_t M, int64_t Nc,
-                              int64_t K, float* partials, hipStream_t st) {
+                              int64_t K, int split, float* partials, hipStream_t st) {
   if (dtype == 1 || dtype == 2) {
     if (K % 128) return hipErrorInvalidValue;
     const int tiles_m = int((M + BM - 1) / BM), tiles_n = int((Nc + BN - 1) / BN);
     const int64_t blocks = gemm_blocks(tiles_m, tiles_n);
-    if (dtype == 1)
-      search_gemm_bf16_kernel<<<unsigned(blocks), NT, 0, st>>>(
-          static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(E), M, Nc, K, tiles_m,
-          tiles_n, partials);
+    const uint16_t* x = static_cast<const uint16_t*>(X);
+    const uint16_t* e = static_cast<const uint16_t*>(E);
+    if (dtype == 1 && split)
+      search_gemm_bf16_split_kernel<<<unsigned(blocks), NT, 0, st>>>(x, e, M, Nc, K, tiles_m,
+                                                                       tiles_n, partials);
+    else if (dtype == 1)
+      search_gemm_bf16_kernel<<<unsigned(blocks), NT, 0, st>>>(x, e, M, Nc, K, tiles_m, tiles_n,
+                                                                 partials);
+    else if (split)
+      search_gemm_f16_split_kernel<<<unsigned(blocks), NT, 0, st>>>(x, e, M, Nc, K, tiles_m,
+                                                                      tiles_n, partials);
     else
-      search_gemm_f16_kernel<<<unsigned(blocks), NT, 0, st>>>(
-          static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(E), M, Nc, K, tiles_m,
-          tiles_n, partials);
+      search_gemm_f16_kernel<<<unsigned(blocks), NT, 0, st>>>(x, e, M, Nc, K, tiles_m, tiles_n,
+                                                                partials);
   } else {
     const int64_t tiles_m = (M + FB - 1) / FB, tiles_n = (Nc + FB - 1) / FB;
     search_gemm_f32_kernel<<<unsigned(tiles_m * tiles_n), 256, 0, st>>>(

@@ -167,7 +167,8 @@ __device__ __forceinline__ int swz64(int row, int chunk) {
 // contraction alternates 128-wide blocks P_0, Q_0, P_1, Q_1, ... and each
 // 128-wide block of B is read twice in a row, so one k-loop gives
 // Σ_c (P_c + Q_c)·B_cᵀ: A's 64-wide k-tile kt reads B's k-tile
-// (kt / 4)·2 + kt % 2.
+// (kt / 4)·2 + kt % 2. pair_a is the same with the roles swapped: B
+// alternates P_c, Q_c and each 128-wide block of A is read twice.
 // Copy j of a wave fills rows 8·j further down than copy 0, so its source
 // offset is a per-lane base (two of them: the swizzle flips by 4 on odd j)
 // plus a uniform step j·8·ld·2 bytes, which goes in the scalar offset.
@@ -176,16 +177,18 @@ struct GemmCtx64 {
   int vbaseA[2], vbaseB[2];
   int stepA, stepB;
   int wave, KT, oobA, oobB;
-  bool pair_b;
+  bool pair_a, pair_b;
 };
 __device__ __forceinline__ void gemm_setup64(GemmCtx64& c, const uint16_t* A, int64_t rows_a,
                                              int64_t lda, const uint16_t* B, int64_t rows_b,
-                                             int64_t ldb, int64_t KA, bool pair_b) {
+                                             int64_t ldb, int64_t KA, bool pair_b,
+                                             bool pair_a = false) {
   c.rsA = tile_rsrc(A, rows_a, lda);
   c.rsB = tile_rsrc(B, rows_b, ldb);
   const int tid = threadIdx.x, lane = tid & 63;
   c.wave = tid >> 6;
   c.KT = int(KA / BK64);
+  c.pair_a = pair_a;
   c.pair_b = pair_b;
   c.oobA = BM * int(lda) * 2;
   c.oobB = BN * int(ldb) * 2;
@@ -207,8 +210,9 @@ __device__ __forceinline__ void gemm_setup64(GemmCtx64& c, const uint16_t* A, in
 template <int S>
 __device__ __forceinline__ void dma64(const GemmCtx64& c, int kt) {
   const bool in = kt < c.KT;
+  const int kta = c.pair_a ? ((kt >> 2) << 1) | (kt & 1) : kt;
   const int ktb = c.pair_b ? ((kt >> 2) << 1) | (kt & 1) : kt;
-  const int kofsA = in ? kt * (BK64 * 2) : c.oobA;
+  const int kofsA = in ? kta * (BK64 * 2) : c.oobA;
   const int kofsB = in ? ktb * (BK64 * 2) : c.oobB;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -271,7 +275,8 @@ __device__ __forceinline__ void copy64(const GemmCtx64& c, int kt, int q) {
   const bool in = kt < c.KT;
   const int j = q & 7;
   if (q < 8) {
-    const int kofsA = in ? kt * (BK64 * 2) : c.oobA;
+    const int kta = c.pair_a ? ((kt >> 2) << 1) | (kt & 1) : kt;
+    const int kofsA = in ? kta * (BK64 * 2) : c.oobA;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsA, AWQ_LDS(stage64_a<S>() + (c.wave * 8 + j) * 64),
                                              16, c.vbaseA[j & 1] + kofsA, j * c.stepA, 0, 0);
   } else {

@@ -20,6 +20,12 @@
 // group's IEEE reciprocal and one FMA correction (quant_code), as in the
 // packed output. The fold multiplies by a precomputed table 1/s instead of
 // dividing by s.
+//
+// Split operands (16-bit types only): each float32 e is stored as two
+// halves hi = rnd(e), lo = rnd(e - hi), both round-to-nearest-even, so hi +
+// lo is e to ~16 significand bits. A row then has length 2K with the halves
+// in alternating 128-wide blocks: channel k's hi at (k / 128)·256 + k % 128,
+// its lo 128 further on (the layout the search GEMM's split kernels read).
 #include "device_common.h"
 
 namespace awq {
@@ -29,6 +35,16 @@ constexpr int kThreads = 256;
 
 template <int DT>
 __device__ __forceinline__ void store8(void* E, int64_t idx, const float (&e)[8]);
+template <int DT>
+__device__ __forceinline__ float rounded(float e);
+template <>
+__device__ __forceinline__ float rounded<1>(float e) {
+  return float(static_cast<__bf16>(e));
+}
+template <>
+__device__ __forceinline__ float rounded<2>(float e) {
+  return float(static_cast<_Float16>(e));
+}
 
 // bf16 output: gfx950 converts float32 to bf16 in hardware with round-to-nearest-even.
 template <>
@@ -67,8 +83,8 @@ __device__ __forceinline__ void store8<0>(void* E, int64_t idx, const float (&e)
 
 // DT: 0 = f32 (E in f32), 1 = bf16 (E in bf16), 2 = fp16 (E in fp16). G:
 // group size (32, 64, 128);
-// the G/8 lanes of a group reduce its range.
-template <int DT, int G>
+// the G/8 lanes of a group reduce its range. SPLIT (DT 1 or 2): hi/lo rows.
+template <int DT, int G, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void transform_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s_rows,
     const float* __restrict__ inv_rows, int64_t s_stride, GridArgs ratios, int has_ratio, int nc,
@@ -117,27 +133,39 @@ __global__ __launch_bounds__(kThreads) void transform_kernel(
       const float q = quant_code(wp[i], p, rstep);
       e[i] = ((q - p.zero) * p.step) * iv[i] - w[i];
     }
-    if (active) store8<DT>(E, int64_t(c) * cand_stride + e0, e);
+    if (!active) continue;
+    if (SPLIT) {
+      // row n = e0 / K; channel k's 128-block b = k / 128 holds hi at 256·b
+      const int64_t o = int64_t(c) * cand_stride + (e0 - k) * 2 + (k >> 7) * 256 + (k & 127);
+      float lo[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float h = rounded<DT>(e[i]);
+        lo[i] = e[i] - h;
+        e[i] = h;
+      }
+      store8<DT>(E, o, e);
+      store8<DT>(E, o + 128, lo);
+    } else {
+      store8<DT>(E, int64_t(c) * cand_stride + e0, e);
+    }
   }
 }
 
-template <int DT>
+template <int DT, bool SPLIT>
 hipError_t launch_transform_g(int group, unsigned blocks, hipStream_t st, const void* W, int64_t N,
                               int64_t K, const float* s_rows, const float* inv_rows,
                               int64_t s_stride, const GridArgs& g, int has_ratio, int nc,
                               int bits, int zero_point, void* E, int64_t cand_stride) {
   if (group == 32)
-    transform_kernel<DT, 32><<<blocks, kThreads, 0, st>>>(W, N, K, s_rows, inv_rows, s_stride, g,
-                                                          has_ratio, nc, bits, zero_point, E,
-                                                          cand_stride);
+    transform_kernel<DT, 32, SPLIT><<<blocks, kThreads, 0, st>>>(
+        W, N, K, s_rows, inv_rows, s_stride, g, has_ratio, nc, bits, zero_point, E, cand_stride);
   else if (group == 64)
-    transform_kernel<DT, 64><<<blocks, kThreads, 0, st>>>(W, N, K, s_rows, inv_rows, s_stride, g,
-                                                          has_ratio, nc, bits, zero_point, E,
-                                                          cand_stride);
+    transform_kernel<DT, 64, SPLIT><<<blocks, kThreads, 0, st>>>(
+        W, N, K, s_rows, inv_rows, s_stride, g, has_ratio, nc, bits, zero_point, E, cand_stride);
   else
-    transform_kernel<DT, 128><<<blocks, kThreads, 0, st>>>(W, N, K, s_rows, inv_rows, s_stride,
-                                                           g, has_ratio, nc, bits, zero_point, E,
-                                                           cand_stride);
+    transform_kernel<DT, 128, SPLIT><<<blocks, kThreads, 0, st>>>(
+        W, N, K, s_rows, inv_rows, s_stride, g, has_ratio, nc, bits, zero_point, E, cand_stride);
   return hipGetLastError();
 }
 
@@ -145,21 +173,27 @@ hipError_t launch_transform_g(int group, unsigned blocks, hipStream_t st, const 
 
 hipError_t launch_transform(const void* W, int dtype, int64_t N, int64_t K, const float* s_rows,
                             const float* inv_rows, int64_t s_stride, const float* ratios_host,
-                            int nc, int bits, int group, int zero_point, void* E,
+                            int nc, int bits, int group, int zero_point, int split, void* E,
                             int64_t cand_stride, hipStream_t st) {
   GridArgs g{};
   const int has_ratio = ratios_host != nullptr;
   for (int i = 0; i < nc && i < 64; ++i) g.v[i] = has_ratio ? ratios_host[i] : 1.f;
   const int64_t lanes = N * K / 8;
   const unsigned blocks = unsigned((lanes + kThreads - 1) / kThreads);
+  if (dtype == 1 && split)
+    return launch_transform_g<1, true>(group, blocks, st, W, N, K, s_rows, inv_rows, s_stride, g,
+                                       has_ratio, nc, bits, zero_point, E, cand_stride);
   if (dtype == 1)
-    return launch_transform_g<1>(group, blocks, st, W, N, K, s_rows, inv_rows, s_stride, g,
-                                 has_ratio, nc, bits, zero_point, E, cand_stride);
+    return launch_transform_g<1, false>(group, blocks, st, W, N, K, s_rows, inv_rows, s_stride, g,
+                                        has_ratio, nc, bits, zero_point, E, cand_stride);
+  if (dtype == 2 && split)
+    return launch_transform_g<2, true>(group, blocks, st, W, N, K, s_rows, inv_rows, s_stride, g,
+                                       has_ratio, nc, bits, zero_point, E, cand_stride);
   if (dtype == 2)
-    return launch_transform_g<2>(group, blocks, st, W, N, K, s_rows, inv_rows, s_stride, g,
-                                 has_ratio, nc, bits, zero_point, E, cand_stride);
-  return launch_transform_g<0>(group, blocks, st, W, N, K, s_rows, inv_rows, s_stride, g,
-                               has_ratio, nc, bits, zero_point, E, cand_stride);
+    return launch_transform_g<2, false>(group, blocks, st, W, N, K, s_rows, inv_rows, s_stride, g,
+                                        has_ratio, nc, bits, zero_point, E, cand_stride);
+  return launch_transform_g<0, false>(group, blocks, st, W, N, K, s_rows, inv_rows, s_stride, g,
+                                      has_ratio, nc, bits, zero_point, E, cand_stride);
 }
 
 }  // namespace awq

@@ -89,7 +89,8 @@ SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_gr
   L.inv = off;
   off += align_up(n_tab * size_t(K) * 4);
   L.E = off;
-  off += align_up(size_t(nb) * size_t(N) * size_t(K) * dtype_bytes(dtype));
+  off += align_up(size_t(nb) * size_t(N) * size_t(K) * dtype_bytes(dtype) *
+                  (is_split_op(op) ? 2 : 1));
   L.partials = off;
   off += align_up(size_t(L.MT) * size_t(nb) * size_t(N) * 4);
   L.row_sums = off;
@@ -180,6 +181,8 @@ static awq_status check_qconfig(awq_qconfig qc) {
     return set_error(AWQ_E_UNSUPPORTED, "w_bit %d not supported (3 or 4)", qc.w_bit);
   if (qc.zero_point != 0 && qc.zero_point != 1)
     return set_error(AWQ_E_INVALID, "zero_point must be 0 or 1");
+  if (qc.flags != 0 && qc.flags != AWQ_SEARCH_SPLIT_E)
+    return set_error(AWQ_E_INVALID, "flags must be 0 or AWQ_SEARCH_SPLIT_E");
   return AWQ_OK;
 }
 
@@ -201,6 +204,8 @@ awq_status check_search(int op, const void* X, const void* W, awq_dtype d, int64
     return set_error(AWQ_E_UNSUPPORTED, "%s: the Gram path takes bf16 inputs", nm);
   if (is_gram_op(op) && T > (int64_t(1) << 22))
     return set_error(AWQ_E_UNSUPPORTED, "%s: at most 2^22 tokens on the Gram path", nm);
+  if (is_gram_op(op) && (qc.flags & AWQ_SEARCH_SPLIT_E))
+    return set_error(AWQ_E_UNSUPPORTED, "%s: split candidates are for the direct searches", nm);
   if (T < 1 || N < 1 || K < 1 || T > kMaxDim || N > kMaxDim || K > kMaxDim)
     return set_error(AWQ_E_INVALID, "%s: bad shape T=%lld N=%lld K=%lld", nm, (long long)T,
                      (long long)N, (long long)K);
@@ -217,12 +222,13 @@ awq_status check_search(int op, const void* X, const void* W, awq_dtype d, int64
   }
   if (!aligned16(X) || !aligned16(W) || !aligned4(vec) || !aligned4(out_dev))
     return set_error(AWQ_E_INVALID, "%s: X and W must be 16-byte aligned", nm);
-  const size_t need1 = search_layout(op, T, N, K, n_grid, 1, d).total;
+  const int lop = layout_op(op, qc, d);
+  const size_t need1 = search_layout(lop, T, N, K, n_grid, 1, d).total;
   if (!ws || !aligned16(ws) || ws_bytes < need1)
     return set_error(AWQ_E_WORKSPACE, "%s: workspace needs at least %zu bytes (16-byte aligned)",
                      nm, need1);
   int32_t b = n_grid;
-  while (b > 1 && search_layout(op, T, N, K, n_grid, b, d).total > ws_bytes) --b;
+  while (b > 1 && search_layout(lop, T, N, K, n_grid, b, d).total > ws_bytes) --b;
   *nb = b;
   return AWQ_OK;
 }
@@ -418,6 +424,11 @@ extern "C" size_t awq_workspace_bytes(int op, int64_t T, int64_t N, int64_t K, i
     case AWQ_OP_SEARCH_SCALE:
     case AWQ_OP_SEARCH_CLIP:
       return search_layout(op, T, N, K, n_grid, n_grid, dtype).total;
+    case AWQ_OP_SEARCH_SCALE_SPLIT_E:
+    case AWQ_OP_SEARCH_CLIP_SPLIT_E:
+      // float32 layers do not split: their searches use the plain layout
+      return search_layout(dtype == AWQ_F32 ? unsplit_op(op) : op, T, N, K, n_grid, n_grid,
+                           dtype).total;
     case AWQ_OP_SEARCH_SCALE_GRAM:
     case AWQ_OP_SEARCH_CLIP_GRAM:
     case AWQ_OP_SEARCH_SCALE_GRAM_G:
@@ -437,9 +448,12 @@ extern "C" size_t awq_workspace_bytes(int op, int64_t T, int64_t N, int64_t K, i
 extern "C" size_t awq_workspace_bytes_batch(int op, int64_t T, int64_t N, int64_t K,
                                             int32_t n_grid, int32_t batch, awq_dtype dtype) {
   using namespace awq;
-  if (op != AWQ_OP_SEARCH_SCALE && op != AWQ_OP_SEARCH_CLIP && !is_gram_op(op)) return 0;
+  if (op != AWQ_OP_SEARCH_SCALE && op != AWQ_OP_SEARCH_CLIP && !is_gram_op(op) &&
+      !is_split_op(op))
+    return 0;
   if (batch < 1 || batch > n_grid) return 0;
   if (awq_workspace_bytes(op, T, N, K, n_grid, dtype) == 0) return 0;
+  if (dtype == AWQ_F32) op = unsplit_op(op);   // float32 layers do not split
   return search_layout(op, T, N, K, n_grid, batch, dtype).total;
 }
 

@@ -66,9 +66,24 @@ def test_workspace_sizes(L):
     assert st == L.AWQ_E_WORKSPACE
     assert ws(L.AWQ_OP_PACK, 1, 4096, 4096, 1, L.AWQ_BF16) > 0
     assert ws(L.AWQ_OP_STATS, 65536, 1, 4096, 1, L.AWQ_BF16) >= 4096 * 8
-    for bad in ((9, 1, 1, 1, 1, 1), (1, 0, 1, 1, 1, 1), (1, 1, 1, 1, 0, 1), (1, 1, 1, 1, 65, 1),
+    for bad in ((11, 1, 1, 1, 1, 1), (1, 0, 1, 1, 1, 1), (1, 1, 1, 1, 0, 1), (1, 1, 1, 1, 65, 1),
                 (1, 1, 1, 1, 1, 7)):
         assert ws(*bad) == 0
+    # split candidates: the candidate buffer doubles; float32 layers do not split
+    for plain, split in ((L.AWQ_OP_SEARCH_SCALE, L.AWQ_OP_SEARCH_SCALE_SPLIT_E),
+                         (L.AWQ_OP_SEARCH_CLIP, L.AWQ_OP_SEARCH_CLIP_SPLIT_E)):
+        for dt in (L.AWQ_BF16, L.AWQ_F16):
+            a, b = ws(plain, 65536, 4096, 4096, 20, dt), ws(split, 65536, 4096, 4096, 20, dt)
+            assert b - a == 20 * 4096 * 4096 * 2
+            a1 = lib.awq_workspace_bytes_batch(plain, 65536, 4096, 4096, 20, 1, dt)
+            b1 = lib.awq_workspace_bytes_batch(split, 65536, 4096, 4096, 20, 1, dt)
+            assert b1 - a1 == 4096 * 4096 * 2
+        assert ws(split, 256, 512, 512, 20, L.AWQ_F32) == ws(plain, 256, 512, 512, 20, L.AWQ_F32)
+    # a split search is refused a workspace sized for the plain one
+    st = lib.awq_search_scale(FAKEW, FAKEW, L.AWQ_BF16, 65536, 4096, 4096, FAKEW,
+                              L.float_array([0.5] * 20), 20, L.QConfig(4, 128, 1, 1), FAKEW,
+                              ctypes.byref(a_best), mse, None, FAKEW, one, None)
+    assert st == L.AWQ_E_WORKSPACE
 
 
 FAKE = ctypes.c_void_p(0x10000)       # aligned, never dereferenced: validation fails first
@@ -103,13 +118,28 @@ def _search(L, op, **kw):
     (dict(grid=[0.5] * 65), -1), (dict(grid=[]), -1),
     (dict(X=MIS), -1), (dict(W=MIS), -1),
     (dict(ws=None), -3), (dict(ws_bytes=1000), -3), (dict(ws=MIS), -3),
+    (dict(flags=2), -1), (dict(flags=-1), -1),
 ])
 @pytest.mark.parametrize("op", ["scale", "clip"])
 def test_search_rejects(L, kw, status, op):
     if kw.get("qc", 0) is None:
         kw = dict(kw, qc=L.QConfig(4, 16, 1))          # unsupported group size
+    if "flags" in kw:
+        kw = dict(qc=L.QConfig(4, 128, 1, kw["flags"]))
     assert _search(L, op, **kw) == status
     assert L.last_error()
+
+
+def test_gram_searches_reject_split(L):
+    lib = L.lib()
+    a_best = ctypes.c_float()
+    mse = (ctypes.c_double * 4)()
+    st = lib.awq_search_scale_gram(FAKE, FAKE, L.AWQ_BF16, 256, 256, 256, FAKE,
+                                   L.float_array([0.5]), 1, L.QConfig(4, 128, 1, 1), FAKE,
+                                   ctypes.byref(a_best), mse, None, FAKE, 1 << 40, None)
+    assert st == L.AWQ_E_UNSUPPORTED and "direct" in L.last_error()
+    # a float32 layer accepts the flag (its candidates are float32 already)
+    assert _search(L, "scale", dtype=L.AWQ_F32, qc=L.QConfig(4, 128, 1, 1), ws_bytes=10) == -3
 
 
 @pytest.mark.parametrize("qc,status", [((5, 128, 1), -2), ((2, 128, 1), -2), ((4, 16, 1), -2),

@@ -27,7 +27,8 @@ import pytest
 from post_weight_quantization_26_amd import build_lib
 
 KERNELS = {
-    "gemm.hip": [r"search_gemm_bf16_kernel", r"search_gemm_f16_kernel"],
+    "gemm.hip": [r"search_gemm_bf16_kernel", r"search_gemm_f16_kernel",
+                 r"search_gemm_bf16_split_kernel", r"search_gemm_f16_split_kernel"],
     "gram.hip": [r"gram_partial_kernel", r"gram_search_kernel"],
     "w4a16.hip": [r"w4a16_gemm_kernelILb0", r"w4a16_gemm_kernelILb1"],
 }

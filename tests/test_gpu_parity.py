@@ -9,6 +9,10 @@ Tolerances:
   * Per-candidate MSE (the curve) against the float64 oracle: 1e-3 relative.
   * Chosen α: identical unless the oracle's two best MSEs are within 1e-4
     relative.
+  * Per-row clip ratio r*_n: the same rule per row (identical unless the
+    oracle's two best errors of that row are within 1e-4 relative). Rows
+    that break it are counted and reported; with split candidate operands
+    (split_e) none may.
   * Per-row output errors M_n: the search GEMM consumes the candidates' error
     weights E = Ŵ - W as bf16 MFMA operands. The test rebuilds exactly those
     operands from the oracle's codes (the kernel's float32 arithmetic, then
@@ -18,9 +22,18 @@ Tolerances:
     row (γ_K = K·2^-23 / (1 - K·2^-23) on Σ_j |x_tj e_nj|, plus 300·2^-23 for
     the sums of squares) and requires |GPU - model| within it. The gap between
     the model and the float64 oracle is the cost of bf16 operands; it is
-    reported, and it is what the 1e-3 curve tolerance absorbs.
+    reported. With split_e the operands are hi + lo halves (the model
+    rebuilds them the same way) and the bound covers 2K products per output.
   * Clip ratio per row: the GPU's pick is optimal for the model up to the
     model tolerance, and its float64 regret is within the row's bf16 gap.
+
+The curve rule and the α rule are asserted exactly as stated above for every
+layer, with one documented exception: a layer whose error is carried by a few
+rows or tokens (one row of much larger weights; one token) does not average
+out the rounding of single 16-bit candidate operands, which leaves up to ~2e-3
+on its curve. Those layers are held to the rules with split_e, and with
+single operands to the per-row float32 bound against the model only
+(``curve_rule=False``, used by the tests that say so).
 """
 import numpy as np
 import pytest
@@ -67,11 +80,19 @@ def assert_alpha_rule(gpu_idx, ref_mse):
         assert gpu_idx in order[:2]
 
 
-def model_E(w32, s32, ratio, bits, zp, dtype, group=128):
+def _round16(e, dtype):
+    """float32 -> the MFMA operand type (RNE), back as float32."""
+    if dtype == "f16":
+        return e.astype(np.float16).astype(np.float32)
+    return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(e))
+
+
+def model_E(w32, s32, ratio, bits, zp, dtype, group=128, split=False, magnitude=False):
     """Error weights as the search GEMM consumes them, from the oracle's codes
     and the kernel's float32 arithmetic: fl32(fl32(fl32((q - zero)·step) ·
     fl32(1/s)) - w), then one RNE rounding to the MFMA operand type (bf16 or
-    fp16; float32 inputs stay float32)."""
+    fp16; float32 inputs stay float32). split: hi = rnd(e), lo = rnd(e - hi)
+    and the operand is hi + lo (magnitude: |hi| + |lo|, for the bound)."""
     q, step, zero = O.quantize(w32, s32, ratio, bits, group, zp)
     N, K = w32.shape
     d = ((q.reshape(N, K // group, group).astype(np.float32) - zero[:, :, None]) * step[:, :, None])
@@ -79,24 +100,31 @@ def model_E(w32, s32, ratio, bits, zp, dtype, group=128):
     e = (d.reshape(N, K) * inv_s[None, :]) - w32
     e = e.astype(np.float32)
     if dtype == "f32":
-        return e.astype(np.float64)
-    if dtype == "f16":
-        return e.astype(np.float16).astype(np.float64)
-    return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(e)).astype(np.float64)
+        return np.abs(e).astype(np.float64) if magnitude else e.astype(np.float64)
+    hi = _round16(e, dtype)
+    if not split:
+        return np.abs(hi).astype(np.float64) if magnitude else hi.astype(np.float64)
+    lo = _round16((e - hi).astype(np.float32), dtype)
+    if magnitude:
+        return np.abs(hi).astype(np.float64) + np.abs(lo).astype(np.float64)
+    return hi.astype(np.float64) + lo.astype(np.float64)
 
 
-def row_references(X, dtype, w_rows, cands, chunk=4096, want_S=False):
+def row_references(X, dtype, w_rows, cands, chunk=4096, want_S=False, split=False):
     """One pass over X for stacked candidates [(s, ratio), ...] on rows w_rows.
 
     Returns M64 (float64 oracle errors), Mm (model errors) and tol (worst-case
     float32 accumulation bound of the direct GEMM), each [n_cand, R]; with
-    want_S also S = Σ_t (Σ_k |x_tk|·|e_k|)² per row (= |e|ᵀ(|X|ᵀ|X|)|e|)."""
+    want_S also S = Σ_t (Σ_k |x_tk|·|e_k|)² per row (= |e|ᵀ(|X|ᵀ|X|)|e|).
+    split: the model's operands are hi + lo halves; the GEMM sums 2K products."""
     e64 = np.concatenate([O.candidate_weights(w_rows, s, r, *c) - w_rows.astype(np.float64)
                           for (s, r, c) in cands])
-    em = np.concatenate([model_E(w_rows, s, r, c[0], c[2], dtype, c[1]) for (s, r, c) in cands])
+    em = np.concatenate([model_E(w_rows, s, r, c[0], c[2], dtype, c[1], split)
+                         for (s, r, c) in cands])
     Rt, K = e64.shape
     M64, Mm, acc, acc2 = (np.zeros(Rt) for _ in range(4))
-    aem = np.abs(em).T
+    aem = np.concatenate([model_E(w_rows, s, r, c[0], c[2], dtype, c[1], split, magnitude=True)
+                          for (s, r, c) in cands]).T
     for t0 in range(0, X.shape[0], chunk):
         x = O.decode(X[t0:t0 + chunk], dtype).astype(np.float64)
         y = x @ e64.T
@@ -106,7 +134,8 @@ def row_references(X, dtype, w_rows, cands, chunk=4096, want_S=False):
         Mm += (ym * ym).sum(axis=0)
         acc += (np.abs(ym) * a).sum(axis=0)
         acc2 += (a * a).sum(axis=0)
-    g = K * U_F32 / (1 - K * U_F32)
+    Ke = 2 * K if split and dtype != "f32" else K
+    g = Ke * U_F32 / (1 - Ke * U_F32)
     tol = 2 * g * acc + g * g * acc2 + 300 * U_F32 * Mm
     n = len(cands)
     if want_S:
@@ -132,14 +161,17 @@ def compare_rows(gpu_rows, M64, Mm, tol, what):
           f"|gpu-oracle|/oracle max {_ratio(np.abs(gpu_rows - M64), M64):.2e}")
 
 
-def check_scale_search(api, X, W, dtype, alphas, bits, zp, rows=None, ws=None, group=128):
-    """Runs stats + search on the GPU and the oracle; compares. Returns both results."""
+def check_scale_search(api, X, W, dtype, alphas, bits, zp, rows=None, ws=None, group=128,
+                       split_e=False, curve_rule=True):
+    """Runs stats + search on the GPU and the oracle; compares. Returns both results.
+    curve_rule=False (only for the layers the module docstring names) keeps
+    every check except the curve and α rules against the float64 oracle."""
     Xd, Wd = to_dev(X, dtype), to_dev(W, dtype)
     abar = api.act_stats(Xd)
     ref_abar = O.act_stats(X, dtype)
     assert np.array_equal(bits32(abar), ref_abar.view(np.uint32)), "abar differs"
     res = api.search_scale(Xd, Wd, abar, alphas, bits=bits, group=group, zero_point=zp,
-                           want_row_sums=True, ws=ws)
+                           want_row_sums=True, ws=ws, split_e=split_e)
     ref = O.search_scale(X, W, dtype, ref_abar, alphas, bits, group, zp, rows=rows)
     T, N = X.shape[0], W.shape[0]
     rs = res["row_sums"].cpu().numpy()
@@ -150,45 +182,52 @@ def check_scale_search(api, X, W, dtype, alphas, bits, zp, rows=None, ws=None, g
     sel = slice(None) if rows is None else np.asarray(rows)
     w_rows = O.decode(W, dtype)[sel]
     cands = [(ref["s_table"][i], 1.0, (bits, group, zp)) for i in range(len(alphas))]
-    M64, Mm, tol = row_references(X, dtype, w_rows, cands)
+    M64, Mm, tol = row_references(X, dtype, w_rows, cands, split=split_e)
     assert np.allclose(M64, ref["row_sums"], rtol=1e-10, atol=0)
     compare_rows(rs[:, sel], M64, Mm, tol, "alpha search rows")
     if rows is None:
         # the curve against the model, within the summed float32 bounds (any size)
         assert np.all(np.abs(res["mse"] - Mm.sum(axis=1) / (T * N)) <= tol.sum(axis=1) / (T * N))
-        mrel = np.abs(res["mse"] - ref["mse"]) / ref["mse"]
-        m_curve = Mm.sum(axis=1) / (T * N)
-        gap = np.abs(m_curve - ref["mse"])
-        if N >= 16:
-            # against the float64 oracle: 1e-3, plus the model's own gap to it.
-            # The bf16 rounding of the candidate operands averages out over
-            # many rows of similar error; where a few rows dominate the sum
-            # (a layer of a few rows, or one row of much larger weights) it
-            # does not, and the deviation is that gap, bounded above.
-            assert np.all(np.abs(res["mse"] - ref["mse"]) <= MSE_REL * ref["mse"] + gap), \
-                f"mse rel err {mrel.max():.3e}"
-            # the GPU's argmin is the model's (up to float32 ties); it is also
-            # the oracle's whenever the model's gap is below the tie width
-            assert_alpha_rule(res["index"], m_curve)
-            if np.all(gap <= 1e-4 * ref["mse"]):
-                assert_alpha_rule(res["index"], ref["mse"])
-        print(f"curve: max rel err vs oracle {mrel.max():.2e} "
-              f"(model's own gap {(gap / ref['mse']).max():.2e})")
+        assert_curve_rules(res["mse"], res["index"], ref["mse"], "alpha curve", curve_rule)
     return res, ref, Xd, Wd
 
 
-def check_clip(api, Xd, Wd, X, W, dtype, s, ratios, bits, zp, rows=None, group=128):
+def assert_curve_rules(gpu_mse, gpu_idx, ref_mse, what, curve_rule=True):
+    """Per-candidate MSE within 1e-3 relative of the float64 oracle, and the
+    oracle's argmin unless its two best values are within 1e-4 relative."""
+    mrel = np.abs(np.asarray(gpu_mse) - ref_mse) / ref_mse
+    print(f"{what}: max rel err vs oracle {mrel.max():.2e}"
+          + ("" if curve_rule else " (rules not asserted: single operands, few rows)"))
+    if curve_rule:
+        assert mrel.max() <= MSE_REL, f"{what}: mse rel err {mrel.max():.3e}"
+        assert_alpha_rule(gpu_idx, ref_mse)
+
+
+def clip_row_rule(gpu_idx, ref_rows):
+    """Rows whose GPU ratio index breaks the α rule applied per row: it differs
+    from the oracle's argmin although the oracle's two best errors of the row
+    are 1e-4 or more apart (relative). Returns their count."""
+    order = np.argsort(ref_rows, axis=0, kind="stable")
+    cols = np.arange(ref_rows.shape[1])
+    best, second = ref_rows[order[0], cols], ref_rows[order[1], cols]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        decided = np.where(best > 0, (second - best) / best, np.inf) >= TIE_REL
+    return int(np.sum(decided & (gpu_idx != order[0])))
+
+
+def check_clip(api, Xd, Wd, X, W, dtype, s, ratios, bits, zp, rows=None, group=128,
+               split_e=False, curve_rule=True):
     T, N = X.shape[0], W.shape[0]
     ratios = np.asarray(ratios, np.float32)
     res = api.search_clip(Xd, Wd, torch.from_numpy(s).to("cuda:0"), ratios, bits=bits,
-                          group=group, zero_point=zp, want_row_sums=True)
+                          group=group, zero_point=zp, want_row_sums=True, split_e=split_e)
     ref = O.search_clip(X, W, dtype, s, ratios, bits, group, zp, rows=rows)
     rs = res["row_sums"].cpu().numpy()
     sel = slice(None) if rows is None else np.asarray(rows)
     w_rows = O.decode(W, dtype)[sel]
     R = w_rows.shape[0]
     cands = [(s, np.full(R, r, np.float32), (bits, group, zp)) for r in ratios]
-    M64, Mm, tol = row_references(X, dtype, w_rows, cands)
+    M64, Mm, tol = row_references(X, dtype, w_rows, cands, split=split_e)
     assert np.allclose(M64, ref["row_sums"], rtol=1e-10, atol=0)
     compare_rows(rs[:, sel], M64, Mm, tol, "clip search rows")
     rb = res["ratio_best"].cpu().numpy()
@@ -201,11 +240,22 @@ def check_clip(api, Xd, Wd, X, W, dtype, s, ratios, bits, zp, rows=None, group=1
     gap = np.abs(Mm - M64)
     assert np.all(M64[gi, cols] - M64.min(axis=0) <=
                   gap[gi, cols] + gap[ref["index"], cols] + tol[gi, cols] + tol[ref["index"], cols])
-    print(f"clip: {np.mean(gi == ref['index']):.1%} of rows pick the oracle's ratio")
+    bad = clip_row_rule(gi, M64)
+    print(f"clip: {np.mean(gi == ref['index']):.1%} of rows pick the oracle's ratio; "
+          f"{bad} of {R} rows break the per-row rule")
+    if split_e:
+        assert bad == 0, f"{bad} rows pick a ratio the oracle rules out"
     best = rs.min(axis=0)
     assert np.isclose(res["mse_clip"], best.sum() / (T * N), rtol=1e-12)
     if rows is None:
-        assert abs(res["mse_clip"] - ref["mse_clip"]) / ref["mse_clip"] <= MSE_REL
+        # the per-ratio curve and mse_clip against the float64 oracle
+        ratio_curve = rs.sum(axis=1) / (T * N)
+        ref_curve = ref["row_sums"].sum(axis=1) / (T * N)
+        rel = abs(res["mse_clip"] - ref["mse_clip"]) / ref["mse_clip"]
+        crel = (np.abs(ratio_curve - ref_curve) / ref_curve).max()
+        print(f"clip: mse_clip rel err {rel:.2e}, ratio curve max rel err {crel:.2e}")
+        if curve_rule:
+            assert rel <= MSE_REL and crel <= MSE_REL
     return res, ref
 
 
@@ -286,10 +336,50 @@ def test_search_scale_tile_aligned(api):
     check_scale_search(api, X, W, "bf16", synth.alpha_grid(5), 4, True)
 
 
-def test_search_scale_degenerate_shapes(api):
-    # one token, one output row, one group, a single α = 0 (plain rounding)
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("bits,zp,group", [(4, True, 128), (3, True, 64), (4, False, 32)])
+def test_search_split_small_ragged(api, dtype, bits, zp, group):
+    """Split candidate operands (hi + lo halves, the main loop's pair mode):
+    the model bound over 2K products per row, the curve rules, and the
+    per-row clip rule with no exception allowed."""
+    X, W = synth.make_custom(700, 300, 384, dtype, seed=91 + bits + group)
+    res, ref, Xd, Wd = check_scale_search(api, X, W, dtype, synth.alpha_grid(7), bits, zp,
+                                          group=group, split_e=True)
+    check_clip(api, Xd, Wd, X, W, dtype, ref["s_table"][res["index"]], synth.ratio_grid(6),
+               bits, zp, group=group, split_e=True)
+
+
+def test_search_split_group_and_batches(api):
+    """A split group search equals the split search of the stacked weights,
+    and a workspace for one candidate at a time gives the same bits."""
+    X, _ = synth.make_custom(600, 8, 256, "bf16", seed=93)
+    Ws = [synth.make_weight(n, 256, 0.02, "bf16", seed=94 + n) for n in (264, 40)]
+    Xd = to_dev(X, "bf16")
+    abar = api.act_stats(Xd)
+    alphas = synth.alpha_grid(5)
+    grp = api.search_scale_group(Xd, [to_dev(w, "bf16") for w in Ws], abar, alphas,
+                                 want_row_sums=True, split_e=True)
+    Wd = to_dev(np.concatenate(Ws), "bf16")
+    stacked = api.search_scale(Xd, Wd, abar, alphas, want_row_sums=True, split_e=True)
+    assert np.array_equal(grp["mse"], stacked["mse"])
+    from post_weight_quantization_26_amd import _lib
+    one = api.workspace_bytes_batch(_lib.AWQ_OP_SEARCH_SCALE_SPLIT_E, 600, 304, 256, 5, 1,
+                                    torch.bfloat16)
+    small = torch.empty(one, dtype=torch.uint8, device="cuda:0")
+    b = api.search_scale(Xd, Wd, abar, alphas, want_row_sums=True, split_e=True, ws=small)
+    assert np.array_equal(b["mse"], stacked["mse"])
+    assert torch.equal(b["row_sums"], stacked["row_sums"])
+    ref = O.search_scale_group(X, Ws, "bf16", O.act_stats(X, "bf16"), alphas)
+    assert_curve_rules(grp["mse"], grp["index"], ref["mse"], "split group curve")
+
+
+@pytest.mark.parametrize("split_e", [True, False])
+def test_search_scale_degenerate_shapes(api, split_e):
+    # one token, one output row, one group, a single α = 0 (plain rounding);
+    # one row of one token: the curve rules hold with split operands
     X, W = synth.make_custom(1, 1, 128, "bf16", n_out=1, seed=23)
-    res, ref, _, _ = check_scale_search(api, X, W, "bf16", np.array([0.0], np.float32), 4, True)
+    res, ref, _, _ = check_scale_search(api, X, W, "bf16", np.array([0.0], np.float32), 4, True,
+                                        split_e=split_e, curve_rule=split_e)
     assert res["alpha_best"] == 0.0
     assert np.array_equal(bits32(res["s_best"]), np.ones(128, np.float32).view(np.uint32))
 
@@ -316,12 +406,19 @@ def degenerate_layer(seed=26):
     return synth.f32_to_bf16_bits(x), synth.f32_to_bf16_bits(w)
 
 
+@pytest.mark.parametrize("split_e", [True, False])
 @pytest.mark.parametrize("bits,zp", [(4, True), (3, True), (4, False)])
-def test_degenerate_values_search_and_pack(api, bits, zp):
+def test_degenerate_values_search_and_pack(api, bits, zp, split_e):
+    """The layer's error is carried by one row of 5000x larger weights, so the
+    rounding of single bf16 candidate operands does not average out over rows
+    (1.9e-3 on its curve): the curve and α rules are asserted with split
+    operands; single operands are held to the per-row float32 bound."""
     X, W = degenerate_layer()
-    res, ref, Xd, Wd = check_scale_search(api, X, W, "bf16", synth.alpha_grid(7), bits, zp)
+    res, ref, Xd, Wd = check_scale_search(api, X, W, "bf16", synth.alpha_grid(7), bits, zp,
+                                          split_e=split_e, curve_rule=split_e)
     s = ref["s_table"][res["index"]]
-    check_clip(api, Xd, Wd, X, W, "bf16", s, synth.ratio_grid(6), bits, zp)
+    check_clip(api, Xd, Wd, X, W, "bf16", s, synth.ratio_grid(6), bits, zp, split_e=split_e,
+               curve_rule=split_e)
     qw, qz, sc = api.quantize_pack(Wd, torch.from_numpy(s).to("cuda:0"), bits=bits,
                                    zero_point=zp)
     assert_pack_parity(qw, qz, sc, W, "bf16", s, None, zp, bits=bits)
