@@ -130,6 +130,21 @@ size_t awq_workspace_bytes_batch(int op, int64_t T, int64_t N, int64_t K, int32_
 awq_status awq_act_stats(const void* X, awq_dtype x_dtype, int64_t T, int64_t K, float* abar,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* awq_act_stats without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). It allocates nothing: the float64 partials go to a
+ * static device array of 2^20 doubles (8 MiB) that each GPU the library runs
+ * on holds until the process ends, found once per device on its first call
+ * there (the current device must be the one `stream` belongs to). Results
+ * equal awq_act_stats bit for bit. Every call on a GPU shares that GPU's
+ * array, so calls that overlap on one GPU (other streams, other threads) race
+ * and must be serialised by the caller. Sizes whose partials need more than
+ * 2^20 doubles (awq_workspace_bytes(AWQ_OP_STATS, ...) > 8 MiB, i.e. K above
+ * about 2^19 for bf16) return AWQ_E_UNSUPPORTED; other argument errors as
+ * for awq_act_stats. Does not synchronise. */
+awq_status awq_act_stats_noalloc(const void* X, awq_dtype x_dtype, int64_t T, int64_t K,
+                                 float* abar, void* stream);
+
 /* Step 1 over a calibration set that comes in batches: ā is the mean over
  * all their tokens (the statistic is a plain mean, so batches add up).
  * awq_act_stats_accumulate adds Σ_t |x_tj| of one batch X [T, K] (bf16, f16

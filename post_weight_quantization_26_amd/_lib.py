@@ -48,6 +48,7 @@ SIGNATURES = {
     "awq_gram_build": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_vp, c_sz, c_vp, c_sz,
                                       c_vp]),
     "awq_act_stats": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]),
+    "awq_act_stats_noalloc": (ctypes.c_int, [c_vp, ctypes.c_int, c_i64, c_i64, c_vp, c_vp]),
     "awq_act_stats_accumulate": (ctypes.c_int,
                                  [c_vp, ctypes.c_int, c_i64, c_i64, c_vp, c_vp, c_sz, c_vp]),
     "awq_act_stats_finalize": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_vp]),

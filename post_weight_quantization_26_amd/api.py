@@ -85,6 +85,18 @@ def act_stats(X: torch.Tensor, ws: Optional[torch.Tensor] = None,
     return abar
 
 
+def act_stats_noalloc(X: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """act_stats through the entry point that allocates nothing (its partials
+    live in a static device array shared by all such calls on a GPU; calls
+    that overlap on one GPU race). ``out`` lets the caller avoid torch's
+    allocation too."""
+    _dev(X, "X")
+    T, K = X.shape
+    abar = out if out is not None else torch.empty(K, dtype=torch.float32, device=X.device)
+    L.check(L.lib().awq_act_stats_noalloc(_ptr(X), _dtype(X), T, K, _ptr(abar), _stream()))
+    return abar
+
+
 def act_stats_accumulate(X: torch.Tensor, sums: torch.Tensor,
                          ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """sums[j] += Σ_t |x_tj| for one calibration batch X [T, K]; sums is a

@@ -13,6 +13,7 @@ namespace awq {
 // Launchers (HIP translation units).
 hipError_t launch_stats(const void* X, int dtype, int64_t T, int64_t K, int64_t chunks,
                         double* partial, float* abar, hipStream_t st);
+hipError_t stats_scratch(double** out);
 hipError_t launch_scale_table(const float* abar, int64_t K, const float* alphas_host, int n,
                               float* s_table, float* inv_table, hipStream_t st);
 hipError_t launch_reciprocal(const float* s, int64_t n, float* s_copy, float* inv,
@@ -207,6 +208,20 @@ extern "C" awq_status awq_act_stats(const void* X, awq_dtype x_dtype, int64_t T,
                                       st);
                 }),
           "act_stats");
+  return AWQ_OK;
+}
+
+extern "C" awq_status awq_act_stats_noalloc(const void* X, awq_dtype x_dtype, int64_t T,
+                                            int64_t K, float* abar, void* stream) {
+  awq_status s = check_stats_noalloc(X, x_dtype, T, K, abar);
+  if (s != AWQ_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  double* partial = nullptr;
+  AWQ_HIP(stats_scratch(&partial), "act_stats_noalloc: scratch address");
+  // the same kernels as awq_act_stats with the static scratch as their
+  // workspace; no profiler events (they would be created on first use)
+  AWQ_HIP(launch_stats(X, dt(x_dtype), T, K, stats_chunks(T, K, x_dtype), partial, abar, st),
+          "act_stats_noalloc");
   return AWQ_OK;
 }
 

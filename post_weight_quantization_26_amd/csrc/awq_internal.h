@@ -114,6 +114,11 @@ SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_gr
 awq_status check_stats_finalize(const double* sums, int64_t count, int64_t K, const float* abar);
 awq_status check_stats(const void* X, awq_dtype d, int64_t T, int64_t K, const float* abar,
                        const void* ws, size_t ws_bytes);
+// awq_act_stats_noalloc: the float64 chunk partials live in a static device
+// array of this many doubles (8 MiB per device); larger calls are refused.
+constexpr int64_t kStatsScratchDoubles = int64_t(1) << 20;
+awq_status check_stats_noalloc(const void* X, awq_dtype d, int64_t T, int64_t K,
+                               const float* abar);
 awq_status check_scale_table(const float* abar, int64_t K, const float* alphas, int32_t n,
                              const float* s_table);
 awq_status check_search(int op, const void* X, const void* W, awq_dtype d, int64_t T, int64_t N,

@@ -12,9 +12,19 @@
 // lanes meet in LDS; one float64 partial per (chunk, column) goes to the
 // workspace, and a finalise pass adds the chunks in a fixed order and rounds
 // once to float32.
+#include <mutex>
+
+#include "awq_internal.h"
 #include "device_common.h"
 
 namespace awq {
+
+// The float64 chunk partials of awq_act_stats_noalloc, for callers that
+// cannot allocate: one copy per device, held until the process ends, shared
+// by every such call on that device. Every entry a launch reads is written
+// by the same launch first, so nothing needs clearing.
+static __device__ __align__(256) double scratch[kStatsScratchDoubles];
+
 namespace {
 
 constexpr int kColThreads = 64;
@@ -189,6 +199,29 @@ hipError_t launch_stats_divide(const double* sums, int64_t count, int64_t K, flo
                                hipStream_t st) {
   stats_divide_kernel<<<unsigned((K + 255) / 256), 256, 0, st>>>(sums, count, K, abar);
   return hipGetLastError();
+}
+
+// Device address of `scratch` on the current device. In host code the
+// array's name is only a stand-in, so its address is looked up once per
+// device (with that device current) and kept.
+hipError_t stats_scratch(double** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptr[dev] = p;
+  }
+  *out = static_cast<double*>(ptr[dev]);
+  return hipSuccess;
 }
 
 hipError_t launch_stats(const void* X, int dtype, int64_t T, int64_t K, int64_t chunks,

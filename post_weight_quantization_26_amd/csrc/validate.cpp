@@ -142,6 +142,28 @@ awq_status check_stats_finalize(const double* sums, int64_t count, int64_t K, co
   return AWQ_OK;
 }
 
+awq_status check_stats_noalloc(const void* X, awq_dtype d, int64_t T, int64_t K,
+                               const float* abar) {
+  if (!X || !abar) return set_error(AWQ_E_INVALID, "act_stats_noalloc: NULL X or abar");
+  if (!dtype_ok(d)) return set_error(AWQ_E_INVALID, "act_stats_noalloc: unknown dtype %d", int(d));
+  if (T < 1 || K < 1 || T > kMaxDim || K > kMaxDim)
+    return set_error(AWQ_E_INVALID, "act_stats_noalloc: bad shape T=%lld K=%lld", (long long)T,
+                     (long long)K);
+  const int64_t vec = 16 / int64_t(dtype_bytes(d));
+  if (K % vec)
+    return set_error(AWQ_E_INVALID, "act_stats_noalloc: K=%lld must be a multiple of %lld",
+                     (long long)K, (long long)vec);
+  if (!aligned16(X) || !aligned4(abar))
+    return set_error(AWQ_E_INVALID, "act_stats_noalloc: X must be 16-byte aligned, abar 4");
+  const int64_t need = stats_chunks(T, K, d) * K;
+  if (need > kStatsScratchDoubles)
+    return set_error(AWQ_E_UNSUPPORTED,
+                     "act_stats_noalloc: %lld float64 partials exceed the static scratch of %lld "
+                     "(use awq_act_stats with a workspace)",
+                     (long long)need, (long long)kStatsScratchDoubles);
+  return AWQ_OK;
+}
+
 awq_status check_stats(const void* X, awq_dtype d, int64_t T, int64_t K, const float* abar,
                        const void* ws, size_t ws_bytes) {
   if (!X || !abar) return set_error(AWQ_E_INVALID, "act_stats: NULL X or abar");

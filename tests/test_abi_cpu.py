@@ -455,3 +455,26 @@ def test_gram_workspace_and_rejects(L):
     assert lib.awq_search_clip_gram(FAKE, FAKE, L.AWQ_BF16, 256, 256, 256, FAKE,
                                     L.float_array([0.0, 1.0]), 2, qc, FAKE, ctypes.byref(mc),
                                     None, FAKE, 1 << 40, None) == -1      # ratio 0 is invalid
+
+
+def test_stats_noalloc_rejects(L):
+    """The allocation-free stats entry point checks its arguments on the host,
+    and refuses sizes whose float64 partials exceed its static 2^20-double
+    scratch (before any device work)."""
+    lib = L.lib()
+    f = lib.awq_act_stats_noalloc
+    assert f(None, L.AWQ_BF16, 64, 4096, FAKE, None) == L.AWQ_E_INVALID
+    assert f(FAKE, L.AWQ_BF16, 64, 4096, None, None) == L.AWQ_E_INVALID
+    assert f(MIS, L.AWQ_BF16, 64, 4096, FAKE, None) == L.AWQ_E_INVALID
+    assert f(FAKE, L.AWQ_BF16, 64, 4100, FAKE, None) == L.AWQ_E_INVALID      # K % 8
+    assert f(FAKE, 9, 64, 4096, FAKE, None) == L.AWQ_E_INVALID
+    assert f(FAKE, L.AWQ_BF16, 0, 4096, FAKE, None) == L.AWQ_E_INVALID
+    # 64 tokens make one chunk: K = 2^20 partials fit exactly, 2^20 + 8 do not
+    assert f(FAKE, L.AWQ_BF16, 64, (1 << 20) + 8, FAKE, None) == L.AWQ_E_UNSUPPORTED
+    assert "static scratch" in L.last_error()
+    ws = lib.awq_workspace_bytes
+    assert ws(L.AWQ_OP_STATS, 64, 1, 1 << 20, 1, L.AWQ_BF16) == 8 << 20
+    # the benchmark layer's partials fit (64K tokens x 4096 channels, bf16 and f32)
+    for dt in (L.AWQ_BF16, L.AWQ_F16, L.AWQ_F32):
+        assert ws(L.AWQ_OP_STATS, 65536, 1, 4096, 1, dt) <= 8 << 20
+        assert ws(L.AWQ_OP_STATS, 65536, 1, 11008, 1, dt) <= 8 << 20
