@@ -41,7 +41,12 @@
  *   - Arguments are validated on the host before anything is enqueued. A
  *     failed check returns a negative status and launches nothing.
  *     X and W must be 16-byte aligned; K must be a multiple of 128 (for
- *     every group size); grids hold 1..64 values.
+ *     every group size); grids hold 1..64 values. Sizes past the kernels'
+ *     32-bit offsets and grids return AWQ_E_UNSUPPORTED: 16-bit searches and
+ *     the consumer need 512·K < 2^31 (split candidates: 512·2K < 2^31),
+ *     weight matrices at most 2^34 elements, and one batch of the candidate
+ *     GEMM fewer than 2^32 work-items (a search takes smaller batches
+ *     where that is what keeps it within the grid).
  *   - Quantiser arithmetic is IEEE float32 with round-to-nearest-even, one
  *     rounding per operation (no contraction, no flush of denormals):
  *       w' = w·s_j; mx = r·max(0, max_G w'); mn = r·min(0, min_G w')
@@ -225,7 +230,9 @@ awq_status awq_quantize_pack(const void* W, awq_dtype w_dtype, int64_t N, int64_
  * candidates' error weights are
  * the same bf16 operands as on the direct path; only the float32 rounding
  * order of the sums differs. Arguments, outputs and synchronisation as in
- * awq_search_scale / awq_search_clip; bf16 inputs only; T <= 2^22. The
+ * awq_search_scale / awq_search_clip; bf16 inputs only; T below about 2^22
+ * (512·(T rounded up to 128, + 64) < 2^31) and K below about 2^21
+ * (512·(2K + 256) < 2^31), else AWQ_E_UNSUPPORTED. The
  * workspace (awq_workspace_bytes with AWQ_OP_SEARCH_SCALE_GRAM /
  * AWQ_OP_SEARCH_CLIP_GRAM) also holds Xᵀ (K rows of T tokens padded to 128,
  * plus 64), the build's float32 partial tiles, and G's upper tiles as bf16
@@ -288,7 +295,8 @@ awq_status awq_w3a16_matmul(const void* X, awq_dtype dtype, int64_t T, int64_t N
 
 /* One Gram matrix for every search of the layers that read the same X: the
  * scale search, the clip searches that follow it, and group searches.
- * awq_gram_build writes G of X [T, K] (bf16, K a multiple of 128, T <= 2^22)
+ * awq_gram_build writes G of X [T, K] (bf16, K a multiple of 128, T and K
+ * within the Gram searches' limits)
  * into G, a caller-owned device buffer of at least awq_gram_bytes(K) bytes
  * (16-byte aligned), in the layout the Gram searches read (G's upper tiles as
  * bf16 hi/lo halves; the rest of the buffer is not written). Workspace:

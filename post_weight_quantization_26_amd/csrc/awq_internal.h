@@ -23,6 +23,34 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 inline size_t dtype_bytes(awq_dtype d) { return d == AWQ_F32 ? 4 : 2; }
 
+// Addressing limits of the kernels, checked on the host before any launch.
+//  * The MFMA main loop reads a 256-row tile of a 16-bit operand through a
+//    buffer resource with 32-bit byte offsets and size: 256 rows times the
+//    row length times 2 bytes must stay below 2^31.
+//  * A launch holds fewer than 2^32 work-items (grids are 32-bit); the
+//    widest element-wise launches (candidate transform, pack, dequantise,
+//    fold) take 8 elements per lane, so their matrices hold at most 2^34
+//    elements.
+constexpr int64_t kMaxMatrixElems = int64_t(1) << 34;
+inline bool tile_rows_fit(int64_t row_elems) {
+  return row_elems >= 0 && row_elems < (int64_t(1) << 22);
+}
+inline bool grid_fits(int64_t blocks, int64_t threads_per_block) {
+  return blocks >= 0 && blocks * threads_per_block < (int64_t(1) << 32);
+}
+// Workgroups of the search GEMM for T token rows and Nc candidate rows
+// (16-bit: 256 x 256 tiles, XCD-grouped; float32: 64 x 64 tiles), and of the
+// Gram search for K channels and Nc candidate rows. 256 threads each.
+inline int64_t search_gemm_blocks(int64_t T, int64_t Nc, awq_dtype d) {
+  if (d == AWQ_F32) return ceil_div(T, 64) * ceil_div(Nc, 64);
+  const int64_t tm = ceil_div(T, 256), tn = ceil_div(Nc, 256);
+  if (tm >= 32) return ceil_div(tm, 32) * 32 * (ceil_div(tn, 8) * 8);
+  return tm * tn;
+}
+inline int64_t gram_search_blocks(int64_t K, int64_t Nc) {
+  return ceil_div(ceil_div(K, 256), 2) * 8 * ceil_div(ceil_div(Nc, 256), 8);
+}
+
 // Number of token chunks the stats kernel splits T into (one float64 partial
 // row per chunk); chosen so the launch has ~1024 workgroups.
 int64_t stats_chunks(int64_t T, int64_t K, awq_dtype d);

@@ -26,8 +26,9 @@ static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3
 
 static bool dtype_ok(awq_dtype d) { return d == AWQ_F32 || d == AWQ_BF16 || d == AWQ_F16; }
 
-// Upper bound on any single dimension; keeps every index product in int64.
-static constexpr int64_t kMaxDim = int64_t(1) << 31;
+// Upper bound on any single dimension: fits an int, keeps every index
+// product in int64.
+static constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 
 int64_t stats_chunks(int64_t T, int64_t K, awq_dtype d) {
   const int64_t vec = 16 / int64_t(dtype_bytes(d));
@@ -70,6 +71,27 @@ GramBuildLayout gram_build_layout(int64_t T, int64_t K) {
 }
 
 size_t gram_g_bytes(int64_t K) { return align_up(size_t(K) * size_t(2 * K + kGsPad) * 2); }
+
+// The Gram build reads 256-row tiles of Xᵀ (rows of Tp + 64 tokens) and the
+// search 256-row tiles of G's halves (rows of 2K + 256): both must fit the
+// main loop's 32-bit tile offsets; its launches must fit the 32-bit grid.
+static awq_status check_gram_limits(const char* nm, int64_t T, int64_t K, bool build) {
+  const int64_t Tp = ceil_div(T, kTileK) * kTileK;
+  if (!tile_rows_fit(Tp + kXtPad))
+    return set_error(AWQ_E_UNSUPPORTED,
+                     "%s: T=%lld tokens exceed the Gram build's 32-bit tile offsets "
+                     "(512 * (T rounded up to 128, + 64) must stay below 2^31)",
+                     nm, (long long)T);
+  if (!tile_rows_fit(2 * K + kGsPad))
+    return set_error(AWQ_E_UNSUPPORTED,
+                     "%s: K=%lld exceeds the Gram search's 32-bit tile offsets "
+                     "(512 * (2K + 256) must stay below 2^31)", nm, (long long)K);
+  const int64_t nt = ceil_div(K, kGemmBM_bf16);
+  if (build && !grid_fits(nt * (nt + 1) / 2 * gram_slices(T, K), 256))
+    return set_error(AWQ_E_UNSUPPORTED, "%s: K=%lld exceeds the Gram build's grid", nm,
+                     (long long)K);
+  return AWQ_OK;
+}
 
 SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_grid, int32_t nb,
                            awq_dtype dtype) {
@@ -116,11 +138,15 @@ awq_status check_gram_build(const void* X, awq_dtype d, int64_t T, int64_t K, co
   if (!X || !G) return set_error(AWQ_E_INVALID, "gram_build: NULL X or G");
   if (!dtype_ok(d)) return set_error(AWQ_E_INVALID, "gram_build: unknown dtype %d", int(d));
   if (d != AWQ_BF16) return set_error(AWQ_E_UNSUPPORTED, "gram_build: bf16 inputs only");
-  if (T < 1 || K < 1 || T > (int64_t(1) << 22) || K > kMaxDim)
-    return set_error(AWQ_E_INVALID, "gram_build: bad shape T=%lld K=%lld (T <= 2^22)",
-                     (long long)T, (long long)K);
+  if (T < 1 || K < 1 || T > kMaxDim || K > kMaxDim)
+    return set_error(AWQ_E_INVALID, "gram_build: bad shape T=%lld K=%lld", (long long)T,
+                     (long long)K);
   if (K % kTileK)
     return set_error(AWQ_E_INVALID, "gram_build: K=%lld is not a multiple of 128", (long long)K);
+  {
+    awq_status st = check_gram_limits("gram_build", T, K, true);
+    if (st != AWQ_OK) return st;
+  }
   if (!aligned16(X) || !aligned16(G))
     return set_error(AWQ_E_INVALID, "gram_build: X and G must be 16-byte aligned");
   if (G_bytes < gram_g_bytes(K))
@@ -224,8 +250,6 @@ awq_status check_search(int op, const void* X, const void* W, awq_dtype d, int64
   if (!dtype_ok(d)) return set_error(AWQ_E_INVALID, "%s: unknown dtype %d", nm, int(d));
   if (is_gram_op(op) && d != AWQ_BF16)
     return set_error(AWQ_E_UNSUPPORTED, "%s: the Gram path takes bf16 inputs", nm);
-  if (is_gram_op(op) && T > (int64_t(1) << 22))
-    return set_error(AWQ_E_UNSUPPORTED, "%s: at most 2^22 tokens on the Gram path", nm);
   if (is_gram_op(op) && (qc.flags & AWQ_SEARCH_SPLIT_E))
     return set_error(AWQ_E_UNSUPPORTED, "%s: split candidates are for the direct searches", nm);
   if (T < 1 || N < 1 || K < 1 || T > kMaxDim || N > kMaxDim || K > kMaxDim)
@@ -235,6 +259,17 @@ awq_status check_search(int op, const void* X, const void* W, awq_dtype d, int64
   if (st != AWQ_OK) return st;
   if (K % kTileK)
     return set_error(AWQ_E_INVALID, "%s: K=%lld is not a multiple of 128", nm, (long long)K);
+  if (N * K > kMaxMatrixElems)
+    return set_error(AWQ_E_UNSUPPORTED, "%s: N*K=%lld weights exceed 2^34 (32-bit grids)", nm,
+                     (long long)(N * K));
+  if (is_gram_op(op)) {
+    st = check_gram_limits(nm, T, K, builds_gram(op));
+    if (st != AWQ_OK) return st;
+  } else if (d != AWQ_F32 && !tile_rows_fit(splits_e(qc, d) ? 2 * K : K)) {
+    return set_error(AWQ_E_UNSUPPORTED,
+                     "%s: K=%lld exceeds the search GEMM's 32-bit tile offsets (512 * K%s must "
+                     "stay below 2^31)", nm, (long long)K, splits_e(qc, d) ? " * 2" : "");
+  }
   if (n_grid < 1 || n_grid > kMaxGrid)
     return set_error(AWQ_E_INVALID, "%s: grid size %d outside 1..%d", nm, n_grid, kMaxGrid);
   for (int i = 0; i < n_grid; ++i) {
@@ -244,13 +279,23 @@ awq_status check_search(int op, const void* X, const void* W, awq_dtype d, int64
   }
   if (!aligned16(X) || !aligned16(W) || !aligned4(vec) || !aligned4(out_dev))
     return set_error(AWQ_E_INVALID, "%s: X and W must be 16-byte aligned", nm);
+  // the candidate GEMM of one batch covers b·N rows: its grid must fit
+  auto blocks = [&](int32_t b) {
+    return is_gram_op(op) ? gram_search_blocks(K, int64_t(b) * N)
+                          : search_gemm_blocks(T, int64_t(b) * N, d);
+  };
+  if (!grid_fits(blocks(1), 256))
+    return set_error(AWQ_E_UNSUPPORTED, "%s: T=%lld tokens x N=%lld rows exceed the 32-bit grid "
+                     "of the candidate GEMM", nm, (long long)T, (long long)N);
   const int lop = layout_op(op, qc, d);
   const size_t need1 = search_layout(lop, T, N, K, n_grid, 1, d).total;
   if (!ws || !aligned16(ws) || ws_bytes < need1)
     return set_error(AWQ_E_WORKSPACE, "%s: workspace needs at least %zu bytes (16-byte aligned)",
                      nm, need1);
   int32_t b = n_grid;
-  while (b > 1 && search_layout(lop, T, N, K, n_grid, b, d).total > ws_bytes) --b;
+  while (b > 1 && (search_layout(lop, T, N, K, n_grid, b, d).total > ws_bytes ||
+                   !grid_fits(blocks(b), 256)))
+    --b;
   *nb = b;
   return AWQ_OK;
 }
@@ -299,6 +344,9 @@ awq_status check_fold_linear(const void* W_prev, const void* bias, awq_dtype d, 
   if (K < 1 || K_prev < 1 || K > kMaxDim || K_prev > kMaxDim)
     return set_error(AWQ_E_INVALID, "fold_linear: bad shape K=%lld K_prev=%lld", (long long)K,
                      (long long)K_prev);
+  if (K * K_prev > kMaxMatrixElems)
+    return set_error(AWQ_E_UNSUPPORTED, "fold_linear: K*K_prev=%lld elements exceed 2^34",
+                     (long long)(K * K_prev));
   if ((K_prev * int64_t(dtype_bytes(d))) % 16)
     return set_error(AWQ_E_INVALID, "fold_linear: a row of W_prev (K_prev=%lld) must span a "
                      "multiple of 16 bytes", (long long)K_prev);
@@ -324,6 +372,9 @@ awq_status check_pack(const void* W, awq_dtype d, int64_t N, int64_t K, const fl
                      (long long)N, (long long)n_mult, qc.w_bit);
   if (K % kTileK)
     return set_error(AWQ_E_INVALID, "quantize_pack: K=%lld not a multiple of 128", (long long)K);
+  if (N * K > kMaxMatrixElems)
+    return set_error(AWQ_E_UNSUPPORTED, "quantize_pack: N*K=%lld weights exceed 2^34",
+                     (long long)(N * K));
   if (!aligned16(W) || !aligned4(qweight) || !aligned4(qzeros) || !aligned4(scales) ||
       !aligned4(s))
     return set_error(AWQ_E_INVALID, "quantize_pack: W must be 16-byte aligned, outputs 4-byte");
@@ -366,6 +417,13 @@ awq_status check_w4a16(const void* X, awq_dtype d, int64_t T, int64_t N, int64_t
                               (long long)N);
   if (K % kTileK)
     return set_error(AWQ_E_INVALID, "w4a16_matmul: K=%lld not a multiple of 128", (long long)K);
+  if (!tile_rows_fit(K) || N * K > kMaxMatrixElems)
+    return set_error(AWQ_E_UNSUPPORTED,
+                     "w4a16_matmul: K=%lld, N=%lld exceed the 32-bit offsets (512 * K must stay "
+                     "below 2^31, N*K at most 2^34)", (long long)K, (long long)N);
+  if (T > kW4A16GemvMaxT && !grid_fits(search_gemm_blocks(T, N, AWQ_BF16), 256))
+    return set_error(AWQ_E_UNSUPPORTED, "w4a16_matmul: T=%lld x N=%lld exceed the GEMM's grid",
+                     (long long)T, (long long)N);
   if (!aligned16(X) || !aligned4(qweight) || !aligned4(qzeros) || !aligned16(scales) ||
       (reinterpret_cast<uintptr_t>(Y) & 1u))
     return set_error(AWQ_E_INVALID,
@@ -397,6 +455,13 @@ awq_status check_w3a16(const void* X, awq_dtype d, int64_t T, int64_t N, int64_t
                                (long long)N);
   if (K % kTileK)
     return set_error(AWQ_E_INVALID, "w3a16_matmul: K=%lld not a multiple of 128", (long long)K);
+  if (!tile_rows_fit(K) || N * K > kMaxMatrixElems)
+    return set_error(AWQ_E_UNSUPPORTED,
+                     "w3a16_matmul: K=%lld, N=%lld exceed the 32-bit offsets (512 * K must stay "
+                     "below 2^31, N*K at most 2^34)", (long long)K, (long long)N);
+  if (T > kW4A16GemvMaxT && !grid_fits(search_gemm_blocks(T, N, AWQ_BF16), 256))
+    return set_error(AWQ_E_UNSUPPORTED, "w3a16_matmul: T=%lld x N=%lld exceed the GEMM's grid",
+                     (long long)T, (long long)N);
   if (!aligned16(X) || !aligned4(qweight) || !aligned4(qzeros) || !aligned16(scales) ||
       (reinterpret_cast<uintptr_t>(Y) & 1u))
     return set_error(AWQ_E_INVALID,
@@ -458,7 +523,9 @@ extern "C" size_t awq_workspace_bytes(int op, int64_t T, int64_t N, int64_t K, i
       if (dtype != AWQ_BF16 || K % kTileK) return 0;
       return search_layout(op, T, N, K, n_grid, n_grid, dtype).total;
     case AWQ_OP_GRAM_BUILD:
-      if (dtype != AWQ_BF16 || K % kTileK || T > (int64_t(1) << 22)) return 0;
+      if (dtype != AWQ_BF16 || K % kTileK ||
+          !tile_rows_fit(ceil_div(T, kTileK) * kTileK + kXtPad))
+        return 0;
       return gram_build_layout(T, K).total;
     case AWQ_OP_PACK:
       return kAlign;

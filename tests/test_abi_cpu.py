@@ -261,7 +261,7 @@ def test_group_search_rejects(L):
     assert "workspace" in L.last_error()
     assert _group(L, Ns=(256, (1 << 31) + 1)) == -1
     assert "N[1]" in L.last_error()
-    assert _group(L, Ns=(256, 1 << 31)) == -1
+    assert _group(L, Ns=(256, (1 << 31) - 1)) == -1
     assert "in total" in L.last_error()
 
 
@@ -386,7 +386,7 @@ def test_prepared_gram_sizes_and_rejects(L):
     assert f(FAKE, L.AWQ_BF16, T, K, None, big, FAKE, big, None) == -1
     assert f(FAKE, L.AWQ_F32, T, K, FAKE, big, FAKE, big, None) == -2
     assert f(FAKE, L.AWQ_BF16, T, 200, FAKE, big, FAKE, big, None) == -1
-    assert f(FAKE, L.AWQ_BF16, (1 << 22) + 1, K, FAKE, big, FAKE, big, None) == -1
+    assert f(FAKE, L.AWQ_BF16, (1 << 22) + 1, K, FAKE, big, FAKE, big, None) == -2
     assert f(MIS, L.AWQ_BF16, T, K, FAKE, big, FAKE, big, None) == -1
     assert f(FAKE, L.AWQ_BF16, T, K, FAKE, gbytes - 1, FAKE, big, None) == -3
     assert f(FAKE, L.AWQ_BF16, T, K, FAKE, gbytes, FAKE, build - 1, None) == -3
@@ -478,3 +478,61 @@ def test_stats_noalloc_rejects(L):
     for dt in (L.AWQ_BF16, L.AWQ_F16, L.AWQ_F32):
         assert ws(L.AWQ_OP_STATS, 65536, 1, 4096, 1, dt) <= 8 << 20
         assert ws(L.AWQ_OP_STATS, 65536, 1, 11008, 1, dt) <= 8 << 20
+
+
+def test_32bit_offset_edges(L):
+    """Sizes at the edges of the kernels' 32-bit tile offsets and grids: the
+    largest accepted size gets past the shape checks (it then fails only on
+    the deliberately small workspace, AWQ_E_WORKSPACE), the next one is
+    refused (AWQ_E_UNSUPPORTED). The search GEMM's 256-row tiles need
+    512·K < 2^31 (split: 512·2K); the Gram build's 512·(T rounded to 128,
+    + 64) and the Gram search's 512·(2K + 256); the consumer GEMM's 512·K;
+    element-wise launches N·K <= 2^34; the candidate GEMM's grid < 2^32
+    work-items."""
+    lib = L.lib()
+    a_best = ctypes.c_float()
+    mse = (ctypes.c_double * 4)()
+    g = L.float_array([0.5])
+    WS, UN = L.AWQ_E_WORKSPACE, L.AWQ_E_UNSUPPORTED
+
+    def scale(fn, T, N, K, dt=L.AWQ_BF16, flags=0, X=FAKE):
+        return fn(X, FAKE, dt, T, N, K, FAKE, g, 1, L.QConfig(4, 128, 1, flags), FAKE,
+                  ctypes.byref(a_best), mse, None, FAKE, 1000, None)
+
+    k22 = 1 << 22
+    assert scale(lib.awq_search_scale, 256, 256, k22 - 128) == WS
+    assert scale(lib.awq_search_scale, 256, 256, k22) == UN
+    assert "32-bit tile offsets" in L.last_error()
+    assert scale(lib.awq_search_scale, 256, 256, k22 // 2 - 128, flags=1) == WS
+    assert scale(lib.awq_search_scale, 256, 256, k22 // 2, flags=1) == UN
+    assert scale(lib.awq_search_scale, 256, 256, k22, dt=L.AWQ_F32) == WS     # 64-bit indices
+    mc = ctypes.c_double()
+    clip = lambda K: lib.awq_search_clip(FAKE, FAKE, L.AWQ_F16, 256, 256, K, FAKE, g, 1,
+                                         L.QConfig(4, 128, 1), FAKE, ctypes.byref(mc), None, FAKE,
+                                         1000, None)
+    assert clip(k22 - 128) == WS and clip(k22) == UN
+    # Gram: tokens padded to 128 plus 64 per X^T row; 2K + 256 per G row
+    assert scale(lib.awq_search_scale_gram, k22 - 128, 256, 256) == WS
+    assert scale(lib.awq_search_scale_gram, k22 - 127, 256, 256) == UN
+    assert scale(lib.awq_search_scale_gram_g, 256, 256, k22 // 2 - 256) == WS
+    assert scale(lib.awq_search_scale_gram_g, 256, 256, k22 // 2 - 128) == UN
+    big = 1 << 40
+    gb = lib.awq_gram_build
+    assert gb(FAKE, L.AWQ_BF16, k22 - 128, 256, FAKE, 0, FAKE, big, None) == WS
+    assert gb(FAKE, L.AWQ_BF16, k22 - 127, 256, FAKE, 0, FAKE, big, None) == UN
+    assert lib.awq_workspace_bytes(L.AWQ_OP_GRAM_BUILD, k22 - 128, 1, 256, 1, L.AWQ_BF16) > 0
+    assert lib.awq_workspace_bytes(L.AWQ_OP_GRAM_BUILD, k22 - 127, 1, 256, 1, L.AWQ_BF16) == 0
+    # the candidate GEMM's grid: 2^31 - 1 tokens x 2^20 rows is past 2^32 work-items
+    assert scale(lib.awq_search_scale, (1 << 31) - 1, 1 << 20, 128) == UN
+    assert "grid" in L.last_error()
+    # element-wise launches: N·K <= 2^34
+    assert scale(lib.awq_search_scale, 256, 1 << 20, 1 << 14) == WS
+    assert scale(lib.awq_search_scale, 256, (1 << 20) + 8, 1 << 14) == UN
+    pk = lambda N, K: lib.awq_quantize_pack(FAKE, L.AWQ_BF16, N, K, FAKE, None,
+                                            L.QConfig(4, 128, 1), FAKE, FAKE, FAKE, FAKE, 0, None)
+    assert pk(1 << 20, 1 << 14) == WS and pk((1 << 20) + 8, 1 << 14) == UN
+    # the consumer: 512·K < 2^31 on every path (T = 1 needs its workspace)
+    wm = lambda K, fn=lib.awq_w4a16_matmul: fn(FAKE, L.AWQ_BF16, 1, 32, K, FAKE, FAKE, FAKE, 128,
+                                               FAKE, FAKE, 0, None)
+    assert wm(k22 - 128) == WS and wm(k22) == UN
+    assert wm(k22 - 128, lib.awq_w3a16_matmul) == WS and wm(k22, lib.awq_w3a16_matmul) == UN
