@@ -66,6 +66,29 @@ def gemm_traffic(cfg_name: str, how: str = "direct"):
     return rec.get("bytes_per_launch")
 
 
+def host_cpu():
+    """The host's CPU model, physical cores and logical CPUs, from lscpu."""
+    import subprocess
+    info = {}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            info[k.strip()] = v.strip()
+    except Exception:  # pragma: no cover
+        pass
+
+    def num(key):
+        try:
+            return int(info.get(key, ""))
+        except ValueError:
+            return None
+    cps, sockets = num("Core(s) per socket"), num("Socket(s)")
+    return {"model": info.get("Model name"),
+            "physical_cores": cps * sockets if cps and sockets else None,
+            "logical_cpus": num("CPU(s)") or os.cpu_count()}
+
+
 def cpu_baseline(cfg, X, Ws, alphas, rows_n: int):
     """The CPU oracle, as it stands, on a bounded sample of one step: stats over
     the full X, the α search over ``rows_n`` evenly spaced output rows (all
@@ -99,7 +122,7 @@ def cpu_baseline(cfg, X, Ws, alphas, rows_n: int):
     pack_t = time.perf_counter() - t2
     step = (t1 - t0) + (t2 - t1) * cfg.N / len(rows) + pack_t
     return {"value": len(alphas) / step, "unit": "alpha-candidates/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "host": host_cpu(),
             "sample": (f"stats over all {cfg.T} tokens; alpha search over {len(rows)} of {cfg.N} "
                        f"output rows (all {len(alphas)} alphas, all tokens) extrapolated x"
                        f"{cfg.N / len(rows):.0f}" + ("; fold into the norm weight" if cfg.layers

@@ -11,22 +11,35 @@
 // that is 8 codes per word, row 8j+i in bits 4i..4i+3 of word j (the page's
 // layout); for 3 bits 32 rows fill 3 words and some codes straddle two.
 //
-// A workgroup owns 256 output rows x one 128-channel tile of the input dim
-// (1, 2 or 4 groups of g = 128, 64 or 32 channels); consecutive workgroups
-// take consecutive tiles of the same rows. Lane (c, jb) takes 8 consecutive
-// channels of two 8-row chunks; 16 lanes cover a row's 128 channels, so
-// every load instruction reads whole 256-byte row segments (non-temporal: W
-// is read once). All 16 rows' loads of a lane are issued before any is used
-// (the kernel is otherwise limited by loads in flight). Per 8-row chunk:
-//   1. scaled weights of all 8 rows in registers; each row's group range by
-//      xor-shuffles over the g/8 lanes of its group;
-//   2. the lanes of a group share the per-row group arithmetic (step, zero
-//      point, reciprocal: three IEEE float32 divisions): lane ℓ of the group
-//      computes it for rows r ≡ ℓ (mod g/8) and the results are broadcast by
-//      shuffles, instead of every lane computing all 8 rows;
-//   3. codes (quotient from the reciprocal with one FMA correction, rint,
-//      clamp) are packed in float arithmetic that is exact (small integers
-//      times powers of two, sums below 2^24): acc = fma(code - zero,
+// A workgroup owns 128·U output rows x one 128-channel tile of the input
+// dim (1, 2 or 4 groups of g = 128, 64 or 32 channels); U = 2 (256 rows) for
+// large layers, U = 1 where that would leave the chip with fewer than four
+// workgroups per CU. Lane (c, jb) takes 8 consecutive channels of U 8-row
+// chunks; 16 lanes cover a row's 128 channels, so every load instruction
+// reads whole 256-byte row segments. Loads are buffer loads (non-temporal: W
+// is read once) from a per-workgroup base: one per-lane offset, the row step
+// in the scalar offset, rows past N read as zero. All of a lane's loads are
+// issued before any is used. Per 8-row chunk:
+//   1. scaled weights w' = w·s of the 8 rows; each lane's partial range of
+//      its 8 channels per row (max3/min3 chains, widened to contain 0);
+//   2. the group ranges through LDS: every lane stores its 16 partials (8
+//      row maxima, 8 negated row minima), lane c reads value c of all 16
+//      lanes and reduces each group's kLanes of them; lanes c and c ^ 8
+//      swap halves, so each lane holds (max, min) of row c % 8 in every
+//      group;
+//   3. each (row, group) pair's step and zero point (IEEE float32 divisions)
+//      on one lane (lanes c and c ^ 8 split the groups; with one group they
+//      duplicate), stored with the reciprocal split in two, 1/step ≈ rh + rl
+//      (rl = fl32((1 - rh·step)·rh), the residual exact by FMA), and the code
+//      bounds; every lane reads back the 8 rows of its group;
+//   4. codes: quotient q = fma(w', rh, w'·rl), the float32 value of
+//      w'·(rh + rl) = w'/step·(1 + O(2^-47)), so it is the correctly rounded
+//      quotient unless the exact one lies within 2^-47 (relative) of a
+//      float32 rounding midpoint; then it is the neighbouring float32, and
+//      rint can differ from the oracle's only when that quotient is within
+//      one ulp (< 1e-6 for codes below 16) of a .5 boundary. rint, clamp to
+//      [-zero, qmax - zero], packed in exact float arithmetic (small
+//      integers times powers of two, sums below 2^24): acc = fma(code - zero,
 //      base^row, acc), the zero points added once per word; 4-bit words use
 //      two 16-bit halves.
 // The partial words are transposed through LDS: for 4 bits each is one
@@ -38,34 +51,9 @@ namespace awq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRows = 256;
 constexpr int kTile = 128;   // input channels per workgroup
 
-__device__ __forceinline__ uint4 load_stream16(const void* p) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(t.x, t.y, t.z, t.w);
-}
-
-// Max / min over the kLanes consecutive lanes of a group (4, 8 or 16 lanes,
-// aligned within a row of 16) with DPP lane swaps: quad_perm [1,0,3,2] and
-// [2,3,0,1] combine within 4 lanes, row_half_mirror pairs the two quads of 8,
-// row_mirror the two halves of 16. Every lane ends with its group's value.
-template <int kCtrl>
-__device__ __forceinline__ void dpp_range_step(float& mx, float& mn) {
-  mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, mx),
-                                                                    kCtrl, 0xF, 0xF, true)));
-  mn = fminf(mn, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, mn),
-                                                                    kCtrl, 0xF, 0xF, true)));
-}
-
-template <int kLanes>
-__device__ __forceinline__ void group_range(float& mx, float& mn) {
-  if constexpr (kLanes >= 2) dpp_range_step<0xB1>(mx, mn);    // quad_perm [1,0,3,2]
-  if constexpr (kLanes >= 4) dpp_range_step<0x4E>(mx, mn);    // quad_perm [2,3,0,1]
-  if constexpr (kLanes >= 8) dpp_range_step<0x141>(mx, mn);   // row_half_mirror
-  if constexpr (kLanes >= 16) dpp_range_step<0x140>(mx, mn);  // row_mirror
-}
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Raw 16-byte pieces of 8 consecutive elements (one piece for 16-bit types,
 // two for float32) and their conversion to float32.
@@ -74,15 +62,9 @@ struct Raw8 {
   uint4 q[DT == 0 ? 2 : 1];
 };
 
-template <int DT>
-__device__ __forceinline__ void raw_load(const void* base, int64_t idx, Raw8<DT>& r) {
-  if constexpr (DT == 0) {
-    const float* p = static_cast<const float*>(base) + idx;
-    r.q[0] = load_stream16(p);
-    r.q[1] = load_stream16(p + 4);
-  } else {
-    r.q[0] = load_stream16(static_cast<const uint16_t*>(base) + idx);
-  }
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+  const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 2 /* nt */);
+  return make_uint4(t.x, t.y, t.z, t.w);
 }
 
 template <int DT>
@@ -107,24 +89,49 @@ __device__ __forceinline__ void raw_to_f32(const Raw8<DT>& r, float (&v)[8]) {
   }
 }
 
-template <int DT, int BITS, int G>
+// Row parameters of one (row, group): reciprocal halves and code bounds.
+struct alignas(16) RowPrm {
+  float rh, rl, lo, hi;   // 1/step ≈ rh + rl; codes - zero in [lo, hi]
+};
+
+// The group ranges and row parameters are exchanged through LDS among the 16
+// lanes of one chunk, which belong to one wavefront: a wavefront's LDS
+// operations complete in issue order, so a fence that keeps the compiler
+// from moving memory operations across it is all the exchange needs.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// LDS slot of partial v (0..7 row maxima, 8..15 negated row minima) written
+// by lane c of chunk jb: the 16 lanes' values of one v are 16 consecutive
+// floats (one 64-byte read), and chunk slices are 272 floats apart so the
+// four chunks of a wave write to different banks.
+constexpr int kRedStride = 272;
+
+template <int DT, int BITS, int G, int U>
 __global__ __launch_bounds__(kThreads) void pack_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s,
     const float* __restrict__ ratio, int zero_point, int32_t* __restrict__ qweight,
     int32_t* __restrict__ qzeros, uint16_t* __restrict__ scales, int* __restrict__ overflow) {
 #pragma clang fp contract(off)
-  constexpr int kGroups = kTile / G;     // groups per tile
-  constexpr int kLanes = G / 8;          // lanes per group
+  constexpr int kGroups = kTile / G;       // groups per tile
+  constexpr int kLanes = G / 8;            // lanes per group
   constexpr int kHalves = BITS == 4 ? 2 : 1;
-  __shared__ uint32_t words[kTile][33];
+  constexpr int kRows = 128 * U;           // output rows per workgroup
+  constexpr int kChunks = 16 * U;          // 8-row chunks per workgroup
+  constexpr int kMine = kGroups >= 2 ? kGroups / 2 : 1;   // (row, group) pairs per lane
+  constexpr int ESZ = DT == 0 ? 4 : 2;
+  __shared__ uint32_t words[kTile][kChunks + 1];
   __shared__ uint16_t sc_lds[kGroups][kRows];
   __shared__ uint8_t z_lds[kGroups][kRows];
+  __shared__ __attribute__((aligned(16))) float red[16 * kRedStride];
+  __shared__ RowPrm prm[16][kGroups][8];
 
   const int tid = threadIdx.x;
   const int c = tid & 15, jb = tid >> 4;
   const int gi = c / kLanes;                       // this lane's group within the tile
-  const int gl = c % kLanes;                       // this lane's index within the group
-  const int glane0 = (tid & 48) + gi * kLanes;    // wave lane of the group's first lane
   const int64_t n0 = int64_t(blockIdx.y) * kRows;
   const int64_t tile = blockIdx.x;
   const int64_t k = tile * kTile + c * 8;
@@ -133,68 +140,105 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(
 #pragma unroll
   for (int i = 0; i < 8; ++i) sv[i] = s[k + i];
 
-  // Every load of both 8-row chunks is issued before any is used.
-  Raw8<DT> raw[2][8];
+  // W rows n0 .. n0 + kRows - 1 from this workgroup's base; rows past N read
+  // as zero. Offsets stay below 2^31 (the host checks 512·K < 2^31).
+  const int64_t rows_here = N - n0 < kRows ? N - n0 : kRows;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(W) + n0 * K * ESZ), 0,
+      int(rows_here * K * ESZ), 0x00020000);
+  const int row_bytes = int(K) * ESZ;
+  const int voff = (8 * jb * row_bytes) + int(k) * ESZ;
+
+  // Every load of every chunk is issued before any is used.
+  Raw8<DT> raw[U][8];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < U; ++u)
 #pragma unroll
     for (int r8 = 0; r8 < 8; ++r8) {
-      const int64_t n = n0 + 8 * (jb + 16 * u) + r8;
-      if (n < N) {
-        raw_load<DT>(W, n * K + k, raw[u][r8]);
-      } else {
+      const int soff = (128 * u + r8) * row_bytes;   // uniform: the scalar offset
 #pragma unroll
-        for (int q = 0; q < (DT == 0 ? 2 : 1); ++q) raw[u][r8].q[q] = make_uint4(0, 0, 0, 0);
-      }
+      for (int q = 0; q < (DT == 0 ? 2 : 1); ++q)
+        raw[u][r8].q[q] = buf_load16(rs, voff + 16 * q, soff);
     }
 
+  const float qmax = float((1 << BITS) - 1);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int j = jb + 16 * u;                     // 8-row chunk, 0..31
-    // 1. scaled weights and each row's 0-widened group range
-    float wp[8][8], mx[8], mn[8];
+  for (int u = 0; u < U; ++u) {
+    const int j = jb + 16 * u;                     // 8-row chunk, 0 .. kChunks - 1
+    // 1. scaled weights and this lane's partial ranges
+    float wp[8][8], mx[8], nmn[8];
 #pragma unroll
     for (int r8 = 0; r8 < 8; ++r8) {
       float w[8];
       raw_to_f32<DT>(raw[u][r8], w);
-      mx[r8] = 0.f;
-      mn[r8] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        wp[r8][i] = w[i] * sv[i];
-        mx[r8] = fmaxf(mx[r8], wp[r8][i]);
-        mn[r8] = fminf(mn[r8], wp[r8][i]);
+      for (int i = 0; i < 8; ++i) wp[r8][i] = w[i] * sv[i];
+      float a = fmaxf(fmaxf(0.f, wp[r8][0]), wp[r8][1]);
+      float b = fminf(fminf(0.f, wp[r8][0]), wp[r8][1]);
+#pragma unroll
+      for (int i = 2; i < 8; i += 2) {
+        a = fmaxf(fmaxf(a, wp[r8][i]), wp[r8][i + 1]);
+        b = fminf(fminf(b, wp[r8][i]), wp[r8][i + 1]);
+      }
+      mx[r8] = a;
+      nmn[r8] = -b;
+    }
+    // 2. group ranges through LDS
+    float* my = red + jb * kRedStride + c;
+#pragma unroll
+    for (int r8 = 0; r8 < 8; ++r8) {
+      my[16 * r8] = mx[r8];
+      my[16 * (8 + r8)] = nmn[r8];
+    }
+    wave_lds_sync();
+    // lane c reduces value c of the 16 lanes, kLanes at a time (one group
+    // per run of kLanes lanes)
+    float gm[kGroups];
+    {
+      const float4* rd = reinterpret_cast<const float4*>(red + jb * kRedStride + 16 * c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 t = rd[q];
+        const int g = 4 * q / kLanes;
+        const float m4 = fmaxf(fmaxf(t.x, t.y), fmaxf(t.z, t.w));
+        if constexpr (kLanes == 4) {
+          gm[g] = m4;
+        } else {
+          gm[g] = (4 * q) % kLanes == 0 ? m4 : fmaxf(gm[g], m4);
+        }
       }
     }
+    float gmx[kGroups], gmn[kGroups];
 #pragma unroll
-    for (int r8 = 0; r8 < 8; ++r8) group_range<kLanes>(mx[r8], mn[r8]);
-    // 2. group arithmetic of rows r ≡ gl (mod kLanes), then broadcast
-    constexpr int kMine = kLanes >= 8 ? 1 : 8 / kLanes;   // rows this lane computes
-    float my_step[kMine], my_zero[kMine], my_rstep[kMine];
+    for (int g = 0; g < kGroups; ++g) {
+      const float m = gm[g];
+      // lanes c and c ^ 8 hold the max and the negated min of row c % 8
+      const float o = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+          __builtin_bit_cast(int, m), 0x128 /* row_ror:8 */, 0xF, 0xF, true));
+      gmx[g] = c < 8 ? m : o;
+      gmn[g] = -(c < 8 ? o : m);
+    }
+    // 3. the step, zero point and reciprocal halves of this lane's pairs
+    const int r8 = c & 7;
+    const int64_t n = n0 + 8 * j + r8;
+    const bool valid = n < N;
+    const float rr = (ratio != nullptr && valid) ? ratio[n] : 1.f;
 #pragma unroll
     for (int m = 0; m < kMine; ++m) {
-      const int r8 = kLanes >= 8 ? (gl & 7) : gl + kLanes * m;
-      float mxr = mx[0], mnr = mn[0];
-#pragma unroll
-      for (int q = 1; q < 8; ++q)
-        if (q == r8) { mxr = mx[q]; mnr = mn[q]; }
-      const int64_t n = n0 + 8 * j + r8;
-      const bool valid = n < N;
-      const float r = (ratio != nullptr && valid) ? ratio[n] : 1.f;
-      const QParams p = group_qparams(mxr, mnr, r, BITS, zero_point);
-      my_step[m] = p.step;
-      my_zero[m] = p.zero;
-      my_rstep[m] = 1.0f / p.step;
-      if (gl == r8 % kLanes && gl < 8) {
-        const _Float16 hf = _Float16(p.step);
-        const uint16_t hb = __builtin_bit_cast(uint16_t, hf);
-        sc_lds[gi][8 * j + r8] = hb;
-        z_lds[gi][8 * j + r8] = uint8_t(p.zero);
+      const int g = kGroups >= 2 ? (c >> 3) + 2 * m : 0;
+      const QParams p = group_qparams(gmx[g], gmn[g], rr, BITS, zero_point);
+      const float rh = 1.0f / p.step;
+      const float rl = __builtin_fmaf(-rh, p.step, 1.0f) * rh;
+      if (kGroups >= 2 || c < 8) {
+        prm[jb][g][r8] = RowPrm{rh, rl, -p.zero, qmax - p.zero};
+        const uint16_t hb = __builtin_bit_cast(uint16_t, _Float16(p.step));
+        sc_lds[g][8 * j + r8] = hb;
+        z_lds[g][8 * j + r8] = uint8_t(p.zero);
         if (valid && (hb & 0x7FFFu) >= 0x7C00u) *overflow = 1;
       }
     }
-    // 3. codes, packed exactly in float
-    const float qmax = float((1 << BITS) - 1);
+    wave_lds_sync();
+    // 4. codes of the 8 rows, packed exactly in float
     float acc[kHalves][8], zacc[kHalves];
 #pragma unroll
     for (int h = 0; h < kHalves; ++h) {
@@ -203,23 +247,17 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(
       for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
     }
 #pragma unroll
-    for (int r8 = 0; r8 < 8; ++r8) {
-      const int src = glane0 + (r8 % kLanes);
-      const int m = kLanes >= 8 ? 0 : r8 / kLanes;
-      const float step = __shfl(my_step[m], src);
-      const float zero = __shfl(my_zero[m], src);
-      const float rstep = __shfl(my_rstep[m], src);
-      const int h = kHalves == 2 ? (r8 >> 2) : 0;
-      const float pw = float(1 << (BITS * (kHalves == 2 ? (r8 & 3) : r8)));
-      const float lo = -zero, hi = qmax - zero;
+    for (int q8 = 0; q8 < 8; ++q8) {
+      const RowPrm pr = prm[jb][gi][q8];
+      const int h = kHalves == 2 ? (q8 >> 2) : 0;
+      const float pw = float(1 << (BITS * (kHalves == 2 ? (q8 & 3) : q8)));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float q0 = wp[r8][i] * rstep;
-        const float quo = __builtin_fmaf(__builtin_fmaf(-q0, step, wp[r8][i]), rstep, q0);
-        const float cd = __builtin_amdgcn_fmed3f(__builtin_rintf(quo), lo, hi);
+        const float quo = __builtin_fmaf(wp[q8][i], pr.rh, wp[q8][i] * pr.rl);
+        const float cd = __builtin_amdgcn_fmed3f(__builtin_rintf(quo), pr.lo, pr.hi);
         acc[h][i] = __builtin_fmaf(cd, pw, acc[h][i]);
       }
-      zacc[h] = __builtin_fmaf(zero, pw, zacc[h]);
+      zacc[h] = __builtin_fmaf(-pr.lo, pw, zacc[h]);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -233,16 +271,16 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(
   const int64_t g0 = tile * kGroups;               // first group row of this tile
   if constexpr (BITS == 4) {
     const int64_t N8 = N / 8;
-    const int jj = tid & 31;
+    const int jj = tid % kChunks;
     const int64_t jcol = n0 / 8 + jj;
     if (jcol < N8) {
 #pragma unroll 4
-      for (int v = 0; v < 16; ++v) {
-        const int kk = (tid >> 5) + 8 * v;
+      for (int v = 0; v < kChunks / 2; ++v) {
+        const int kk = tid / kChunks + (kThreads / kChunks) * v;
         qweight[(tile * kTile + kk) * N8 + jcol] = int32_t(words[kk][jj]);
       }
     }
-    const int zg = tid >> 5;
+    const int zg = tid / kChunks;
     if (zg < kGroups && jcol < N8) {
       uint32_t zw = 0;
 #pragma unroll
@@ -251,13 +289,14 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(
     }
   } else {
     // 3 bits: four 24-bit partial words (rows 32q .. 32q+31) -> three words.
+    constexpr int kQ = kChunks / 4;              // 32-row column blocks per workgroup
     const int64_t N32 = N / 32, N3 = N32 * 3;
-    const int q = tid & 7;
+    const int q = tid % kQ;
     const int64_t qcol = n0 / 32 + q;
     if (qcol < N32) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int kk = (tid >> 3) + 32 * v;
+      for (int v = 0; v < kTile * kQ / kThreads; ++v) {
+        const int kk = tid / kQ + (kThreads / kQ) * v;
         const uint32_t a = words[kk][4 * q], b = words[kk][4 * q + 1];
         const uint32_t cc = words[kk][4 * q + 2], d = words[kk][4 * q + 3];
         int32_t* dst = qweight + (tile * kTile + kk) * N3 + 3 * qcol;
@@ -266,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(
         dst[2] = int32_t((cc >> 16) | (d << 8));
       }
     }
-    const int zg = tid >> 3;
+    const int zg = tid / kQ;
     if (zg < kGroups && qcol < N32) {
       uint32_t z3[3] = {0, 0, 0};
 #pragma unroll
@@ -282,36 +321,39 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(
       dst[2] = int32_t(z3[2]);
     }
   }
+  if (tid < kRows) {
 #pragma unroll
-  for (int zg = 0; zg < kGroups; ++zg)
-    if (n0 + tid < N) scales[(g0 + zg) * N + n0 + tid] = sc_lds[zg][tid];
+    for (int zg = 0; zg < kGroups; ++zg)
+      if (n0 + tid < N) scales[(g0 + zg) * N + n0 + tid] = sc_lds[zg][tid];
+  }
 }
 
-template <int DT, int BITS>
+template <int DT, int BITS, int U>
 hipError_t launch_pack_g(int group, dim3 grid, hipStream_t st, const void* W, int64_t N,
                          int64_t K, const float* s, const float* ratio, int zero_point,
                          int32_t* qweight, int32_t* qzeros, uint16_t* scales, int* overflow) {
   if (group == 32)
-    pack_kernel<DT, BITS, 32><<<grid, kThreads, 0, st>>>(W, N, K, s, ratio, zero_point, qweight,
-                                                         qzeros, scales, overflow);
+    pack_kernel<DT, BITS, 32, U><<<grid, kThreads, 0, st>>>(W, N, K, s, ratio, zero_point,
+                                                            qweight, qzeros, scales, overflow);
   else if (group == 64)
-    pack_kernel<DT, BITS, 64><<<grid, kThreads, 0, st>>>(W, N, K, s, ratio, zero_point, qweight,
-                                                         qzeros, scales, overflow);
+    pack_kernel<DT, BITS, 64, U><<<grid, kThreads, 0, st>>>(W, N, K, s, ratio, zero_point,
+                                                            qweight, qzeros, scales, overflow);
   else
-    pack_kernel<DT, BITS, 128><<<grid, kThreads, 0, st>>>(W, N, K, s, ratio, zero_point, qweight,
-                                                          qzeros, scales, overflow);
+    pack_kernel<DT, BITS, 128, U><<<grid, kThreads, 0, st>>>(W, N, K, s, ratio, zero_point,
+                                                             qweight, qzeros, scales, overflow);
   return hipGetLastError();
 }
 
-template <int DT>
-hipError_t launch_pack_b(int bits, int group, dim3 grid, hipStream_t st, const void* W,
-                         int64_t N, int64_t K, const float* s, const float* ratio, int zero_point,
+template <int DT, int U>
+hipError_t launch_pack_b(int bits, int group, hipStream_t st, const void* W, int64_t N,
+                         int64_t K, const float* s, const float* ratio, int zero_point,
                          int32_t* qweight, int32_t* qzeros, uint16_t* scales, int* overflow) {
+  const dim3 grid(unsigned(K / kTile), unsigned((N + 128 * U - 1) / (128 * U)));
   if (bits == 3)
-    return launch_pack_g<DT, 3>(group, grid, st, W, N, K, s, ratio, zero_point, qweight, qzeros,
-                                scales, overflow);
-  return launch_pack_g<DT, 4>(group, grid, st, W, N, K, s, ratio, zero_point, qweight, qzeros,
-                              scales, overflow);
+    return launch_pack_g<DT, 3, U>(group, grid, st, W, N, K, s, ratio, zero_point, qweight,
+                                   qzeros, scales, overflow);
+  return launch_pack_g<DT, 4, U>(group, grid, st, W, N, K, s, ratio, zero_point, qweight, qzeros,
+                                 scales, overflow);
 }
 
 }  // namespace
@@ -319,15 +361,22 @@ hipError_t launch_pack_b(int bits, int group, dim3 grid, hipStream_t st, const v
 hipError_t launch_pack(const void* W, int dtype, int64_t N, int64_t K, const float* s,
                        const float* ratio, int bits, int group, int zero_point, int32_t* qweight,
                        int32_t* qzeros, uint16_t* scales, int* overflow, hipStream_t st) {
-  dim3 grid(unsigned(K / kTile), unsigned((N + kRows - 1) / kRows));
+  // 256-row tiles unless that leaves fewer than 1024 workgroups (four per
+  // CU); float32 inputs always take 128 rows (their loads fill twice the
+  // registers)
+  const bool wide = dtype != 0 && (K / kTile) * ((N + 255) / 256) >= 1024;
   if (dtype == 1)
-    return launch_pack_b<1>(bits, group, grid, st, W, N, K, s, ratio, zero_point, qweight, qzeros,
-                            scales, overflow);
+    return wide ? launch_pack_b<1, 2>(bits, group, st, W, N, K, s, ratio, zero_point, qweight,
+                                      qzeros, scales, overflow)
+                : launch_pack_b<1, 1>(bits, group, st, W, N, K, s, ratio, zero_point, qweight,
+                                      qzeros, scales, overflow);
   if (dtype == 2)
-    return launch_pack_b<2>(bits, group, grid, st, W, N, K, s, ratio, zero_point, qweight, qzeros,
-                            scales, overflow);
-  return launch_pack_b<0>(bits, group, grid, st, W, N, K, s, ratio, zero_point, qweight, qzeros,
-                          scales, overflow);
+    return wide ? launch_pack_b<2, 2>(bits, group, st, W, N, K, s, ratio, zero_point, qweight,
+                                      qzeros, scales, overflow)
+                : launch_pack_b<2, 1>(bits, group, st, W, N, K, s, ratio, zero_point, qweight,
+                                      qzeros, scales, overflow);
+  return launch_pack_b<0, 1>(bits, group, st, W, N, K, s, ratio, zero_point, qweight, qzeros,
+                             scales, overflow);
 }
 
 }  // namespace awq

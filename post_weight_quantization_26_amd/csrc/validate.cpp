@@ -372,9 +372,10 @@ awq_status check_pack(const void* W, awq_dtype d, int64_t N, int64_t K, const fl
                      (long long)N, (long long)n_mult, qc.w_bit);
   if (K % kTileK)
     return set_error(AWQ_E_INVALID, "quantize_pack: K=%lld not a multiple of 128", (long long)K);
-  if (N * K > kMaxMatrixElems)
-    return set_error(AWQ_E_UNSUPPORTED, "quantize_pack: N*K=%lld weights exceed 2^34",
-                     (long long)(N * K));
+  if (N * K > kMaxMatrixElems || !tile_rows_fit(K))
+    return set_error(AWQ_E_UNSUPPORTED,
+                     "quantize_pack: N*K=%lld weights exceed 2^34, or K=%lld its 32-bit tile "
+                     "offsets (512 * K must stay below 2^31)", (long long)(N * K), (long long)K);
   if (!aligned16(W) || !aligned4(qweight) || !aligned4(qzeros) || !aligned4(scales) ||
       !aligned4(s))
     return set_error(AWQ_E_INVALID, "quantize_pack: W must be 16-byte aligned, outputs 4-byte");

@@ -531,6 +531,7 @@ def test_32bit_offset_edges(L):
     pk = lambda N, K: lib.awq_quantize_pack(FAKE, L.AWQ_BF16, N, K, FAKE, None,
                                             L.QConfig(4, 128, 1), FAKE, FAKE, FAKE, FAKE, 0, None)
     assert pk(1 << 20, 1 << 14) == WS and pk((1 << 20) + 8, 1 << 14) == UN
+    assert pk(8, k22 - 128) == WS and pk(8, k22) == UN
     # the consumer: 512·K < 2^31 on every path (T = 1 needs its workspace)
     wm = lambda K, fn=lib.awq_w4a16_matmul: fn(FAKE, L.AWQ_BF16, 1, 32, K, FAKE, FAKE, FAKE, 128,
                                                FAKE, FAKE, 0, None)
