@@ -31,6 +31,8 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published (the float32 se
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 TRAFFIC_FILES = {"direct": os.path.join(ROOT, "profiles", "search_gemm_traffic.json"),
                  "gram": os.path.join(ROOT, "profiles", "gram_search_traffic.json")}
+COUNTER_FILES = {"direct": os.path.join(ROOT, "profiles", "search_gemm_counters.json"),
+                 "gram": os.path.join(ROOT, "profiles", "gram_search_counters.json")}
 
 
 def parse():
@@ -48,11 +50,9 @@ def parse():
     return p.parse_args()
 
 
-def gemm_traffic(cfg_name: str, how: str = "direct"):
-    """HBM bytes per launch of the candidate GEMM (search GEMM, or the Gram
-    search) from committed rocprofv3 counter runs, or None when the kernel
-    source changed since they were taken or the workload differs."""
-    path = TRAFFIC_FILES[how]
+def _current_record(path: str, cfg_name: str):
+    """A committed counter record, or None when the kernel source changed
+    since its counters were taken or it covers another workload."""
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -63,7 +63,27 @@ def gemm_traffic(cfg_name: str, how: str = "direct"):
             h.update(f.read())
     if rec.get("gemm_sources_sha256") != h.hexdigest() or rec.get("workload") != cfg_name:
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def gemm_traffic(cfg_name: str, how: str = "direct"):
+    """HBM bytes per launch of the candidate GEMM (search GEMM, or the Gram
+    search) from committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs, or None."""
+    rec = _current_record(TRAFFIC_FILES[how], cfg_name)
+    return None if rec is None else rec.get("bytes_per_launch")
+
+
+def gemm_mfma_util(cfg_name: str, how: str = "direct"):
+    """Matrix-core utilisation of the candidate GEMM from a committed rocprofv3
+    counter run (SQ_VALU_MFMA_BUSY_CYCLES per SIMD over GRBM_GUI_ACTIVE per
+    XCD, in that run's own dispatch), with the shader clock it ran at; None
+    when stale."""
+    rec = _current_record(COUNTER_FILES[how], cfg_name)
+    if rec is None:
+        return None
+    return {"frac": rec["mfma_busy_frac"], "clock_ghz": rec["clock_ghz"],
+            "dispatch_us_under_counters": rec["dispatch_us_under_counters"],
+            "source": os.path.relpath(COUNTER_FILES[how], ROOT)}
 
 
 def host_cpu():
@@ -261,7 +281,8 @@ def main():
                 "frac": round(achieved / peak, 4),
                 "traffic": traffic, "kernel": kernel_name,
                 "avg_launch_us": round(gemm_avg_s * 1e6, 1),
-                "algorithmic_flops_per_launch": flops_per_launch}
+                "algorithmic_flops_per_launch": flops_per_launch,
+                "mfma_util_counters": None if f32 else gemm_mfma_util(name, how)}
         kernels = {k: {"avg_us": round(ms * 1e3 / n, 2) if n else None, "launches": n,
                        "share_of_step": round(ms / (elapsed * 1e3), 4)}
                    for k, (ms, n) in prof.items() if n}
@@ -308,7 +329,8 @@ def main():
                    "zero_point": zp, "n_alpha": cfg.n_alpha, "n_ratio": cfg.n_ratio,
                    "pack": cfg.pack, "layers": list(cfg.layers) or None, "method": method},
         "roofline": roofline,
-        "mfma_util_pct": round(100 * roofline["frac"], 2),
+        "mfma_util_pct": (None if roofline["mfma_util_counters"] is None
+                          else round(100 * roofline["mfma_util_counters"]["frac"], 1)),
         "hbm": {"stats_GBps": None if stats_gbs is None else round(stats_gbs, 1),
                 "pack_GBps": None if pack_gbs is None else round(pack_gbs, 1),
                 "peak_GBps": HBM_PEAK_GBS},

@@ -34,6 +34,16 @@
       readings of the record's kernel scaled by the calibration factors give
       its bytes per launch, stored with the SHA-256 of the sources now.
 
+  python -m post_weight_quantization_26_amd.profile_run counters --record R --pmc PMC.csv
+      Updates the counter record R (profiles/search_gemm_counters.json or
+      profiles/gram_search_counters.json) from one rocprofv3 --pmc run of one
+      bench.py step with GRBM_GUI_ACTIVE, SQ_BUSY_CYCLES,
+      SQ_VALU_MFMA_BUSY_CYCLES, SQ_LDS_BANK_CONFLICT and SQ_WAVES: the
+      record's kernel's readings, its dispatch time under the counters, the
+      shader clock they imply (GRBM_GUI_ACTIVE per XCD over the dispatch) and
+      the matrix-core utilisation (SQ_VALU_MFMA_BUSY_CYCLES per SIMD over
+      GRBM_GUI_ACTIVE per XCD), stored with the SHA-256 of the sources now.
+
   python -m post_weight_quantization_26_amd.profile_run library_gemm [--reps 5]
       For comparison only: the vendor library's bf16 GEMM (torch.matmul, i.e.
       hipBLASLt) on the search GEMM's shape, X [65536, 4096] times the 20
@@ -227,6 +237,46 @@ def traffic(record: str, fetch_csv: str, write_csv: str) -> None:
                       "GiB_per_launch": round(rec["bytes_per_launch"] / 2 ** 30, 2)}))
 
 
+XCDS, SIMDS = 8, 1024   # MI355X: 8 XCDs, 256 CUs of 4 SIMDs
+
+
+def counters(record: str, pmc_csv: str) -> None:
+    import csv
+    import hashlib
+    import json
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    with open(record) as f:
+        rec = json.load(f)
+    vals, span = {}, None
+    with open(pmc_csv) as f:
+        for row in csv.DictReader(f):
+            if f"::{rec['kernel']}(" not in row["Kernel_Name"]:
+                continue
+            key = (row["Dispatch_Id"], row["Counter_Name"])
+            vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+            span = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-9
+    dispatches = {d for d, _ in vals}
+    if len(dispatches) != 1:
+        raise SystemExit(f"{pmc_csv}: expected one {rec['kernel']} dispatch, found {len(dispatches)}")
+    rd = {c: v for (_, c), v in vals.items()}
+    gui = rd["GRBM_GUI_ACTIVE"] / XCDS
+    rec["counters"] = rd
+    rec["dispatch_us_under_counters"] = round(span * 1e6, 1)
+    rec["clock_ghz"] = round(gui / span / 1e9, 3)
+    rec["mfma_busy_frac"] = round(rd["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS / gui, 4)
+    h = hashlib.sha256()
+    for rel in rec["gemm_sources"]:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    rec["gemm_sources_sha256"] = h.hexdigest()
+    with open(record, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps({"kernel": rec["kernel"], "clock_ghz": rec["clock_ghz"],
+                      "mfma_busy_frac": rec["mfma_busy_frac"]}))
+
+
 def library_gemm(reps: int) -> None:
     import json
     import torch
@@ -254,7 +304,9 @@ def library_gemm(reps: int) -> None:
 
 def main(argv=None) -> int:
     p = argparse.ArgumentParser()
-    p.add_argument("what", choices=["copy", "fold", "w4a16", "pack", "traffic", "library_gemm"])
+    p.add_argument("what", choices=["copy", "fold", "w4a16", "pack", "traffic", "counters",
+                                    "library_gemm"])
+    p.add_argument("--pmc")
     p.add_argument("--mib", type=int, default=1024)
     p.add_argument("--reps", type=int, default=20)
     p.add_argument("--record")
@@ -263,6 +315,8 @@ def main(argv=None) -> int:
     a = p.parse_args(argv)
     if a.what == "traffic":
         traffic(a.record, a.fetch, a.write)
+    elif a.what == "counters":
+        counters(a.record, a.pmc)
     elif a.what == "library_gemm":
         library_gemm(a.reps)
     elif a.what == "copy":
