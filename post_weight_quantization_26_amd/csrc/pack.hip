@@ -11,15 +11,15 @@
 // that is 8 codes per word, row 8j+i in bits 4i..4i+3 of word j (the page's
 // layout); for 3 bits 32 rows fill 3 words and some codes straddle two.
 //
-// A workgroup owns 128·U output rows x one 128-channel tile of the input
-// dim (1, 2 or 4 groups of g = 128, 64 or 32 channels); U = 2 (256 rows) for
-// large layers, U = 1 where that would leave the chip with fewer than four
-// workgroups per CU. Lane (c, jb) takes 8 consecutive channels of U 8-row
-// chunks; 16 lanes cover a row's 128 channels, so every load instruction
-// reads whole 256-byte row segments. Loads are buffer loads (non-temporal: W
-// is read once) from a per-workgroup base: one per-lane offset, the row step
-// in the scalar offset, rows past N read as zero. All of a lane's loads are
-// issued before any is used. Per 8-row chunk:
+// A workgroup owns 128 output rows x one 128-channel tile of the input dim
+// (1, 2 or 4 groups of g = 128, 64 or 32 channels): on the 70B-class layer
+// 128-row tiles ran faster than 256-row ones (more resident waves per SIMD,
+// a shorter tail of the grid). Lane (c, jb) takes 8 consecutive channels of
+// one 8-row chunk; 16 lanes cover a row's 128 channels, so every load
+// instruction reads whole 256-byte row segments. Loads are buffer loads
+// (non-temporal: W is read once) from a per-workgroup base: one per-lane
+// offset, the row step in the scalar offset, rows past N read as zero. All
+// of a lane's loads are issued before any is used. Per 8-row chunk:
 //   1. scaled weights w' = w·s of the 8 rows; each lane's partial range of
 //      its 8 channels per row (max3/min3 chains, widened to contain 0);
 //   2. the group ranges through LDS: every lane stores its 16 partials (8
@@ -110,7 +110,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 // four chunks of a wave write to different banks.
 constexpr int kRedStride = 272;
 
-template <int DT, int BITS, int G, int U>
+template <int DT, int BITS, int G>
 __global__ __launch_bounds__(kThreads) void pack_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s,
     const float* __restrict__ ratio, int zero_point, int32_t* __restrict__ qweight,
@@ -119,8 +119,8 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(
   constexpr int kGroups = kTile / G;       // groups per tile
   constexpr int kLanes = G / 8;            // lanes per group
   constexpr int kHalves = BITS == 4 ? 2 : 1;
-  constexpr int kRows = 128 * U;           // output rows per workgroup
-  constexpr int kChunks = 16 * U;          // 8-row chunks per workgroup
+  constexpr int kRows = 128;               // output rows per workgroup
+  constexpr int kChunks = 16;              // 8-row chunks per workgroup
   constexpr int kMine = kGroups >= 2 ? kGroups / 2 : 1;   // (row, group) pairs per lane
   constexpr int ESZ = DT == 0 ? 4 : 2;
   __shared__ uint32_t words[kTile][kChunks + 1];
@@ -149,28 +149,25 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(
   const int row_bytes = int(K) * ESZ;
   const int voff = (8 * jb * row_bytes) + int(k) * ESZ;
 
-  // Every load of every chunk is issued before any is used.
-  Raw8<DT> raw[U][8];
+  // Every load is issued before any is used.
+  Raw8<DT> raw[8];
 #pragma unroll
-  for (int u = 0; u < U; ++u)
+  for (int r8 = 0; r8 < 8; ++r8) {
+    const int soff = r8 * row_bytes;               // uniform: the scalar offset
 #pragma unroll
-    for (int r8 = 0; r8 < 8; ++r8) {
-      const int soff = (128 * u + r8) * row_bytes;   // uniform: the scalar offset
-#pragma unroll
-      for (int q = 0; q < (DT == 0 ? 2 : 1); ++q)
-        raw[u][r8].q[q] = buf_load16(rs, voff + 16 * q, soff);
-    }
+    for (int q = 0; q < (DT == 0 ? 2 : 1); ++q)
+      raw[r8].q[q] = buf_load16(rs, voff + 16 * q, soff);
+  }
 
   const float qmax = float((1 << BITS) - 1);
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int j = jb + 16 * u;                     // 8-row chunk, 0 .. kChunks - 1
+  {
+    const int j = jb;                              // this lane's 8-row chunk
     // 1. scaled weights and this lane's partial ranges
     float wp[8][8], mx[8], nmn[8];
 #pragma unroll
     for (int r8 = 0; r8 < 8; ++r8) {
       float w[8];
-      raw_to_f32<DT>(raw[u][r8], w);
+      raw_to_f32<DT>(raw[r8], w);
 #pragma unroll
       for (int i = 0; i < 8; ++i) wp[r8][i] = w[i] * sv[i];
       float a = fmaxf(fmaxf(0.f, wp[r8][0]), wp[r8][1]);
@@ -328,32 +325,31 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(
   }
 }
 
-template <int DT, int BITS, int U>
+template <int DT, int BITS>
 hipError_t launch_pack_g(int group, dim3 grid, hipStream_t st, const void* W, int64_t N,
                          int64_t K, const float* s, const float* ratio, int zero_point,
                          int32_t* qweight, int32_t* qzeros, uint16_t* scales, int* overflow) {
   if (group == 32)
-    pack_kernel<DT, BITS, 32, U><<<grid, kThreads, 0, st>>>(W, N, K, s, ratio, zero_point,
-                                                            qweight, qzeros, scales, overflow);
+    pack_kernel<DT, BITS, 32><<<grid, kThreads, 0, st>>>(W, N, K, s, ratio, zero_point, qweight,
+                                                         qzeros, scales, overflow);
   else if (group == 64)
-    pack_kernel<DT, BITS, 64, U><<<grid, kThreads, 0, st>>>(W, N, K, s, ratio, zero_point,
-                                                            qweight, qzeros, scales, overflow);
+    pack_kernel<DT, BITS, 64><<<grid, kThreads, 0, st>>>(W, N, K, s, ratio, zero_point, qweight,
+                                                         qzeros, scales, overflow);
   else
-    pack_kernel<DT, BITS, 128, U><<<grid, kThreads, 0, st>>>(W, N, K, s, ratio, zero_point,
-                                                             qweight, qzeros, scales, overflow);
+    pack_kernel<DT, BITS, 128><<<grid, kThreads, 0, st>>>(W, N, K, s, ratio, zero_point, qweight,
+                                                          qzeros, scales, overflow);
   return hipGetLastError();
 }
 
-template <int DT, int U>
-hipError_t launch_pack_b(int bits, int group, hipStream_t st, const void* W, int64_t N,
-                         int64_t K, const float* s, const float* ratio, int zero_point,
+template <int DT>
+hipError_t launch_pack_b(int bits, int group, dim3 grid, hipStream_t st, const void* W,
+                         int64_t N, int64_t K, const float* s, const float* ratio, int zero_point,
                          int32_t* qweight, int32_t* qzeros, uint16_t* scales, int* overflow) {
-  const dim3 grid(unsigned(K / kTile), unsigned((N + 128 * U - 1) / (128 * U)));
   if (bits == 3)
-    return launch_pack_g<DT, 3, U>(group, grid, st, W, N, K, s, ratio, zero_point, qweight,
-                                   qzeros, scales, overflow);
-  return launch_pack_g<DT, 4, U>(group, grid, st, W, N, K, s, ratio, zero_point, qweight, qzeros,
-                                 scales, overflow);
+    return launch_pack_g<DT, 3>(group, grid, st, W, N, K, s, ratio, zero_point, qweight, qzeros,
+                                scales, overflow);
+  return launch_pack_g<DT, 4>(group, grid, st, W, N, K, s, ratio, zero_point, qweight, qzeros,
+                              scales, overflow);
 }
 
 }  // namespace
@@ -361,22 +357,15 @@ hipError_t launch_pack_b(int bits, int group, hipStream_t st, const void* W, int
 hipError_t launch_pack(const void* W, int dtype, int64_t N, int64_t K, const float* s,
                        const float* ratio, int bits, int group, int zero_point, int32_t* qweight,
                        int32_t* qzeros, uint16_t* scales, int* overflow, hipStream_t st) {
-  // 256-row tiles unless that leaves fewer than 1024 workgroups (four per
-  // CU); float32 inputs always take 128 rows (their loads fill twice the
-  // registers)
-  const bool wide = dtype != 0 && (K / kTile) * ((N + 255) / 256) >= 1024;
+  dim3 grid(unsigned(K / kTile), unsigned((N + 127) / 128));
   if (dtype == 1)
-    return wide ? launch_pack_b<1, 2>(bits, group, st, W, N, K, s, ratio, zero_point, qweight,
-                                      qzeros, scales, overflow)
-                : launch_pack_b<1, 1>(bits, group, st, W, N, K, s, ratio, zero_point, qweight,
-                                      qzeros, scales, overflow);
+    return launch_pack_b<1>(bits, group, grid, st, W, N, K, s, ratio, zero_point, qweight, qzeros,
+                            scales, overflow);
   if (dtype == 2)
-    return wide ? launch_pack_b<2, 2>(bits, group, st, W, N, K, s, ratio, zero_point, qweight,
-                                      qzeros, scales, overflow)
-                : launch_pack_b<2, 1>(bits, group, st, W, N, K, s, ratio, zero_point, qweight,
-                                      qzeros, scales, overflow);
-  return launch_pack_b<0, 1>(bits, group, st, W, N, K, s, ratio, zero_point, qweight, qzeros,
-                             scales, overflow);
+    return launch_pack_b<2>(bits, group, grid, st, W, N, K, s, ratio, zero_point, qweight, qzeros,
+                            scales, overflow);
+  return launch_pack_b<0>(bits, group, grid, st, W, N, K, s, ratio, zero_point, qweight, qzeros,
+                          scales, overflow);
 }
 
 }  // namespace awq
