@@ -19,16 +19,8 @@
 //  * Workgroups are mapped so each XCD runs 4 A tiles x 8 B tiles at a time
 //    while all XCDs share the same 8 B tiles.
 //
-// The 32-wide, 4-stage ring with 4x4 blocks of v_mfma_f32_32x32x16 per wave
-// (stage_a/stage_b, swz, read_frags, mfma_4x4) serves the W4A16 GEMM that
-// dequantises on the fly, whose B tile is written into LDS from registers:
-// 32-wide k-tiles with 64-byte LDS rows (4 chunks of 16 B, the chunk index
-// XORed by (row >> 2) & 3, which keeps 16-lane ds_read_b128 fragment reads
-// free of bank conflicts).
-//
 // Output layout of one 16x16 accumulator: lane l holds column l % 16; its
-// register v holds row 4·(l / 16) + v. Of one 32x32 accumulator: lane l
-// holds column l % 32; its register v holds row 8·(v / 4) + 4·(l / 32) + v % 4.
+// register v holds row 4·(l / 16) + v.
 #pragma once
 
 #include "device_common.h"
@@ -38,7 +30,6 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 // MFMA operand vector of 8 elements: bf16 or fp16 (F16 = true).
 template <bool F16>
@@ -54,27 +45,7 @@ struct Operand<true> {
 
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 32;       // k per stage / region
 constexpr int NT = 256;
-constexpr int CH = BK / 8;   // 16-byte chunks per tile row per stage
-constexpr int STAGE = 256 * CH;
-
-__shared__ uint4 sA0[STAGE], sA1[STAGE], sA2[STAGE], sA3[STAGE];
-__shared__ uint4 sB0[STAGE], sB1[STAGE], sB2[STAGE], sB3[STAGE];
-
-template <int S>
-__device__ __forceinline__ uint4* stage_a() {
-  return S == 0 ? sA0 : S == 1 ? sA1 : S == 2 ? sA2 : sA3;
-}
-template <int S>
-__device__ __forceinline__ uint4* stage_b() {
-  return S == 0 ? sB0 : S == 1 ? sB1 : S == 2 ? sB2 : sB3;
-}
-
-// 16-byte slot of (row, chunk) inside a stage.
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * CH + (chunk ^ ((row >> 2) & 3));
-}
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int wait_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
@@ -118,31 +89,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base
                                                            int64_t K) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0,
                                            int(rows * K * 2), 0x00020000);
-}
-
-template <int S, class V, class Ctx>
-__device__ __forceinline__ void read_frags(const Ctx& c, int ks, V (&fa)[4], V (&fb)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    fa[i] = __builtin_bit_cast(V, stage_a<S>()[c.rdA[ks] + i * 128]);
-    fb[i] = __builtin_bit_cast(V, stage_b<S>()[c.rdB[ks] + i * 128]);
-  }
-}
-
-__device__ __forceinline__ floatx16 mfma(bf16x8_t a, bf16x8_t b, floatx16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ floatx16 mfma(f16x8_t a, f16x8_t b, floatx16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-template <class V>
-__device__ __forceinline__ void mfma_4x4(floatx16 (&acc)[4][4], const V (&fa)[4],
-                                         const V (&fb)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = mfma(fa[i], fb[j], acc[i][j]);
 }
 
 // The 2-stage ring of 64-wide k-tiles (2 x 64 KiB). Each region (one k-tile)
@@ -285,6 +231,13 @@ __device__ __forceinline__ void copy64(const GemmCtx64& c, int kt, int q) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsB, AWQ_LDS(stage64_b<S>() + (c.wave * 8 + j) * 64),
                                              16, c.vbaseB[j & 1] + kofsB, j * c.stepB, 0, 0);
   }
+}
+// Only A's copies of k-tile kt (for loops whose B operand is formed in
+// registers).
+template <int S>
+__device__ __forceinline__ void dma64_a(const GemmCtx64& c, int kt) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) copy64<S>(c, kt, q);
 }
 // One k-tile: the previous k-step's 64 MFMAs (f1) carry k-step 0's 16
 // fragment reads and the next k-tile's 16 copies, one each per four MFMAs;

@@ -10,7 +10,7 @@
 // 16-bit activations). Ŵ is formed exactly in float32 ((q - z) is an integer
 // of at most 4 bits and the scale an fp16 value).
 //
-// Three kernels, by the number of token rows T and the layout:
+// Four kernels, by the number of token rows T and the layout:
 //  * T <= 16 (decode), N a multiple of 16: the codes go to the matrix cores
 //    as exact small numbers (B = 1 + q/16) against the activations, 16 token
 //    rows per v_mfma_f32_16x16x32, and the zero points and scales are applied
@@ -30,6 +30,14 @@
 //    (gemm_core.h) computes X'·Ŵᵀ and the epilogue rounds each float32 sum
 //    once to the output type. At T = 4096 the extra pass moves N·K·2.5 bytes,
 //    a few per cent of the GEMM's time.
+//  * T > 16, 4 bits, on request: the same main loop with the B operand
+//    formed from the packed layer in registers (w4a16_gemm_q_kernel, no
+//    workspace), bit for bit the operand of the dequantisation pass. One
+//    wave both feeds its matrix core and does the unpacking, so its VALU
+//    work sits between the MFMAs; at T = 4096 it runs behind the two-pass
+//    path.
+#include <utility>
+
 #include "gemm_core.h"
 
 namespace awq {
@@ -236,153 +244,334 @@ void w4a16_gemm_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
 
 // ---------------------------------------------------------------------------
 // prefill, dequantising on the fly: X tiles through the LDS-DMA ring, the B
-// tile from the packed layer through registers
+// tile formed from the packed layer in registers
 // ---------------------------------------------------------------------------
 //
-// The same 256x256 tiles as the GEMM above, on the 32-wide, 4-stage ring of
-// gemm_core.h with 32x32x16 MFMAs; the B operand reaches LDS from registers
-// instead of by DMA. For each 32-wide
-// k-tile a lane loads 4 qweight words (k rows 4·kq .. 4·kq + 3 of the tile,
-// word column c8 of the output tile: outputs n0 + 8·c8 .. + 7), its group's
-// zero-point word and 8 fp16 scales. Region kt (the region whose MFMAs read
-// k-tile kt) loads the packed k-tile kt + 5 and forms the operand of k-tile
-// kt + 3, as the DMA of X's k-tile kt + 3 fills the same ring stage: Ŵ =
-// (q − z)·scale exactly as the dequantisation pass does (fma(q, scale,
-// −z·scale), whose one rounding is
-// that of (q − z)·scale because z·scale is exact), rounds it once to the
-// 16-bit type and writes 4 k x 1 output row per 8-byte LDS store into the
-// ring's swizzled layout. Lanes pair up over word columns (kq = 2·wave +
-// lane % 2, c8 = (lane / 2) % 32), and lane c8 takes its nibbles in the order
-// r + (c8 / 2) (mod 8) (its words and scales rotated by that much), so the
-// 32 lanes that share a store cycle hit 32 different bank pairs.
-struct QLoad {
-  uint32_t w[4];
-  uint32_t z;
-  uint4 s;
+// The same 256x256 tiles and 16x16x32 main loop as the GEMM above (the
+// 64-wide, 2-stage ring of gemm_core.h); only the B operand reaches LDS from
+// registers instead of by DMA. Lane (j, kc) = (tid % 32, tid / 32) owns word
+// column j of the output tile (outputs n0 + 8j .. + 7) and k rows 8kc .. 8kc + 7
+// of each 64-wide k-tile: 8 qweight words, its group's zero-point word and the
+// 8 fp16 scales (32 lanes read 128 consecutive bytes of a qweight row). Region
+// kt (whose MFMAs read k-tile kt) loads the packed k-tile kt + 2 into the slot
+// k-tile kt used and forms the operand of k-tile kt + 1, as the DMA of X's
+// k-tile kt + 1 fills the same ring stage. Each output row's 8 k values are
+// one 16-byte LDS store. An LDS write serves 8 lanes at a time, which must
+// hit 8 different 16-byte bank groups (chunk slots modulo 8); lane j takes
+// its rows in the order i + 2t (mod 8), t = (j / 2) % 4, which puts the 8
+// lanes j = 8b .. 8b + 7 on 8 distinct slots of the swizzled layout. That is
+// a rotation of the words by whole bytes (so the nibble classes below keep
+// their parity) and of the scales by whole words.
+//
+// Ŵ = (q − z)·scale as the dequantisation pass rounds it, with one
+// v_fma_mix_f32 per value: the code enters as an fp16 number B + q whose low
+// mantissa bits are the nibble (B = 1024 for a nibble at bits 0..3 of a
+// 16-bit half, 0x6400 | q; B = 64 for one at bits 4..7, 0x5400 | q << 4),
+// made by one and-or of the word (or of the word shifted right by 8); the
+// scale enters as its fp16 half; the addend is −(B + z)·scale, formed the
+// same way from the zero-point word. (B + q)·scale and (B + z)·scale have at
+// most 22 significant bits, so the fused result is (q − z)·scale rounded once
+// to float32, the value the dequantisation pass forms, and the operand equals
+// that pass's bit for bit.
+struct Q16Slot {
+  uint32_t w[8];   // qweight words of k rows 8kc .. 8kc + 7
+  uint32_t z;      // zero-point word
+  uint4 s;         // 8 fp16 scales
 };
 
-struct QCtx {
-  __amdgpu_buffer_rsrc_t rsA, rsQ, rsZ, rsS;
-  int voffA[4];
-  int wave, KT, oobA;
-  int rdA[2], rdB[2];
+struct Q16Ctx {
+  __amdgpu_buffer_rsrc_t rsQ, rsZ, rsS;
   uint32_t qoff, qrow, ktq;  // bytes: lane's word at k-tile 0; per k row; per k-tile
   uint32_t zoff, soff, zrow, srow;  // bytes: lane's group-0 entries; per group row
-  int gshift;                // k-tiles per group = 1 << gshift
-  uint32_t rot;              // nibble rotation in bits (4·((c8 / 2) % 8))
+  uint32_t kc8;              // 8·kc: the lane's first k row within a k-tile
+  int gshift;                // log2 of the group size
   uint32_t oobm;             // 0, or bit 31 for a lane whose word column is past N
-  int wofs[8];               // LDS byte offset within a stage of store r
+  uint32_t rot;              // 8t: the words' rotation in bits
+  bool t2, t1;               // t & 2, t & 1: the scale words' rotation
+  int lds[8];                // LDS byte offset within a stage of the lane's row i
+  uint32_t mag[2];           // 0x64006400 and 0x54005400, kept in vector registers
 };
 
 constexpr uint32_t kQOob = 0x80000000u;  // past every buffer: loads read zero
 
-template <int S>
-__device__ __forceinline__ void dma_a(const QCtx& c, int kt) {
-  const int kofs = kt < c.KT ? kt * (BK * 2) : c.oobA;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsA, AWQ_LDS(stage_a<S>() + (c.wave * 4 + j) * 64),
-                                             16, c.voffA[j] + kofs, 0, 0, 0);
-}
-
 // Packed k-tile kt of this lane. Past the last k-tile the offsets pass the
 // end of each buffer, and lanes past N set bit 31 (c.oobm), so those loads
-// read zeros; they are never used. (No selects on the offsets: the compiler
-// would turn them into branches that split the loop body.)
-__device__ __forceinline__ void load_q(const QCtx& c, int kt, QLoad& q) {
-  const uint32_t base = c.qoff + uint32_t(kt) * c.ktq;
-  const uint32_t g = uint32_t(kt >> c.gshift);
+// read zeros; they are never used.
+__device__ __forceinline__ void q16_load(const Q16Ctx& q, int kt, Q16Slot& sl) {
+  const uint32_t base = (q.qoff + uint32_t(kt) * q.ktq) | q.oobm;
+  const uint32_t g = (uint32_t(kt) * 64 + q.kc8) >> q.gshift;
+  // the k-row step is uniform: it goes in the scalar offset
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    q.w[i] = __builtin_amdgcn_raw_buffer_load_b32(c.rsQ, (base + i * c.qrow) | c.oobm, 0, 0);
-  q.z = __builtin_amdgcn_raw_buffer_load_b32(c.rsZ, (c.zoff + g * c.zrow) | c.oobm, 0, 0);
-  const auto sv =
-      __builtin_amdgcn_raw_buffer_load_b128(c.rsS, (c.soff + g * c.srow) | c.oobm, 0, 0);
-  q.s = make_uint4(sv[0], sv[1], sv[2], sv[3]);
+  for (int r = 0; r < 8; ++r)
+    sl.w[r] = __builtin_amdgcn_raw_buffer_load_b32(q.rsQ, base, int(r * q.qrow), 0);
+  sl.z = __builtin_amdgcn_raw_buffer_load_b32(q.rsZ, (q.zoff + g * q.zrow) | q.oobm, 0, 0);
+  const auto sv = __builtin_amdgcn_raw_buffer_load_b128(q.rsS, (q.soff + g * q.srow) | q.oobm,
+                                                        0, 0);
+  sl.s = make_uint4(sv[0], sv[1], sv[2], sv[3]);
 }
 
-// Ŵ of one packed k-tile into stage S.
+// fp16 numbers B + nibble in both 16-bit halves of a word (see above): NIB = 0
+// takes the nibbles at bits 0..3 of each half (B = 1024), NIB = 1 those at
+// bits 4..7 (B = 64). One v_and_or_b32: the mask comes from a scalar
+// register and the exponent bits from a vector register that q.mag holds
+// (two literals cannot share one instruction here).
+template <int NIB>
+__device__ __forceinline__ uint32_t magic16(const Q16Ctx& q, uint32_t x) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3"
+      : "=v"(r)
+      : "v"(x), "s"(NIB == 0 ? 0x000F000Fu : 0x00F000F0u), "v"(q.mag[NIB]));
+  return r;
+}
+
+// float32 a·b + c with a and b the fp16 halves HA / HB of their words (NA
+// negates a): one v_fma_mix_f32, whose fp16 inputs are exact in float32
+template <int HA, int HB, bool NA>
+__device__ __forceinline__ float fma_mix16(uint32_t a, uint32_t b, float c) {
+  float r;
+  if constexpr (NA) {
+    if constexpr (HA == 0 && HB == 0)
+      asm("v_fma_mix_f32 %0, -%1, %2, %3 op_sel_hi:[1,1,0]" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    else if constexpr (HA == 0)
+      asm("v_fma_mix_f32 %0, -%1, %2, %3 op_sel:[0,1,0] op_sel_hi:[1,1,0]"
+          : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    else if constexpr (HB == 0)
+      asm("v_fma_mix_f32 %0, -%1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,1,0]"
+          : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    else
+      asm("v_fma_mix_f32 %0, -%1, %2, %3 op_sel:[1,1,0] op_sel_hi:[1,1,0]"
+          : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  } else {
+    if constexpr (HA == 0 && HB == 0)
+      asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,1,0]" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    else if constexpr (HA == 0)
+      asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[1,1,0]"
+          : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    else if constexpr (HB == 0)
+      asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,1,0]"
+          : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    else
+      asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,1,0] op_sel_hi:[1,1,0]"
+          : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  }
+  return r;
+}
+
+// two float32 values rounded to nearest even into one packed 16-bit pair
+// (low half first), the conversion the dequantisation pass applies to each
+template <bool F16>
+__device__ __forceinline__ uint32_t pack16(float a, float b) {
+  uint32_t r;
+  if constexpr (F16) asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  else asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// Forming one k-tile's operand: the lane's row i (output row 8j + (i + 2t)
+// % 8) takes nibble i of each rotated word (bits 4i .. 4i + 3), so nibble
+// class c = i % 4 (the and-or on the rotated word for c < 2, on it shifted
+// right by 8 for c >= 2; low nibbles for even c) holds rows c and c + 4 in
+// its two halves. Operations, at most two VALU instructions each (what a
+// 16x16x32 MFMA hides), none reading what the one just before it wrote:
+//  * C a: X's DMA copy a of the next k-tile;
+//  * RA h, RB h: the scale words rotated by 2 words, then by 1 (h = which
+//    pair of the four);
+//  * ZR, ZA, ZT, ZB: the zero-point word rotated, its classes 0 and 1, its
+//    shift, classes 2 and 3;
+//  * N c: −(B + z)·scale of rows c and c + 4;
+//  * X p: words 2p and 2p + 1 rotated;  T p: those shifted right by 8;
+//  * M c p: class c of words 2p and 2p + 1;
+//  * V c p h: the values of row c (h = 0) or c + 4 (h = 1) at k rows 2p and
+//    2p + 1;
+//  * P c p: those values packed, for both rows;
+//  * D c: the 16-byte LDS stores of rows c and c + 4.
+struct Q16Work {
+  uint32_t x[8];     // rotated words
+  uint32_t a[4], sw[4], zx;   // scale words rotated by 2 words, then by t; rotated zero word
+  uint32_t t[8];     // rotated words shifted right by 8
+  uint32_t m[8];     // the current class of each word
+  uint32_t zm[4], zt;
+  float nzs[8];
+  float v[4];        // the values of pair p: row c at 2p, 2p + 1; row c + 4 at 2p, 2p + 1
+  uint32_t h[2][4];  // packed k pairs of rows c and c + 4
+};
+
+constexpr int kQ16Copy = 1, kQ16RA = 2, kQ16RB = 3, kQ16ZR = 4, kQ16ZA = 5, kQ16ZT = 6,
+              kQ16ZB = 7, kQ16N = 8, kQ16X = 9, kQ16T = 10, kQ16M = 11, kQ16V = 12,
+              kQ16P = 13;
+constexpr int q16_code(int kind, int a = 0, int b = 0) { return kind * 100 + a * 10 + b; }
+
+// The schedule of a region's 128 MFMA slots: slot s runs q16_op_at(s) (0 =
+// none) after MFMA s, and the stores q16_store_at(s) (−1 = none).
+//  slots 0..31: copies, then X 0..3, then T 0..3 in the even slots; RA, RB,
+//  the zero-point word and N 0..3 in the odd;
+//  slots 32..95: the classes in order 0..3, 16 slots each (M c p, V c p 0,
+//  V c p 1, P c p for p = 0..3); each class's stores go in the slot after
+//  its last pack.
+constexpr int kQ16Classes = 32;   // first slot of class 0; class c starts 16c later
+constexpr int q16_op_at(int s) {
+  if (s < 32) {
+    if (s % 2 == 0) {
+      const int e = s / 2;
+      return e < 8 ? q16_code(kQ16Copy, e) : e < 12 ? q16_code(kQ16X, e - 8)
+                                                     : q16_code(kQ16T, e - 12);
+    }
+    constexpr int odd[16] = {q16_code(kQ16RA, 0), q16_code(kQ16RA, 1), q16_code(kQ16ZR),
+                             q16_code(kQ16RB, 0), q16_code(kQ16RB, 1), q16_code(kQ16ZA),
+                             q16_code(kQ16ZT),    q16_code(kQ16ZB),    q16_code(kQ16N, 0),
+                             q16_code(kQ16N, 1),  q16_code(kQ16N, 2),  q16_code(kQ16N, 3),
+                             0, 0, 0, 0};
+    return odd[s / 2];
+  }
+  const int d = s - kQ16Classes;
+  if (d < 64) {
+    const int c = d / 16, p = (d % 16) / 4, e = d % 4;
+    return e == 0 ? q16_code(kQ16M, c, p)
+         : e == 3 ? q16_code(kQ16P, c, p)
+                  : q16_code(kQ16V, c, 2 * p + (e - 1));
+  }
+  return 0;
+}
+constexpr int q16_store_at(int s) {
+  const int d = s - kQ16Classes - 16;
+  return d >= 0 && d < 64 && d % 16 == 0 ? d / 16 : -1;
+}
+
+template <bool F16, int S, int OP, bool COPY = true>
+__device__ __forceinline__ void q16_op(const GemmCtx64& c, const Q16Ctx& q, const Q16Slot& sl,
+                                       Q16Work& w, int kt) {
+  constexpr int kind = OP / 100, A = (OP / 10) % 10, B = OP % 10;
+  if constexpr (kind == kQ16Copy) {
+    if constexpr (COPY) copy64<S>(c, kt + 1, A);
+  } else if constexpr (kind == kQ16RA) {
+    // scale word k of the result is word (k + t) % 4 of the slot's (selects,
+    // not branches: the loop body stays one block)
+    if constexpr (A == 0) {
+      w.a[0] = q.t2 ? sl.s.z : sl.s.x;
+      w.a[1] = q.t2 ? sl.s.w : sl.s.y;
+    } else {
+      w.a[2] = q.t2 ? sl.s.x : sl.s.z;
+      w.a[3] = q.t2 ? sl.s.y : sl.s.w;
+    }
+  } else if constexpr (kind == kQ16RB) {
+    w.sw[2 * A] = q.t1 ? w.a[2 * A + 1] : w.a[2 * A];
+    w.sw[2 * A + 1] = q.t1 ? w.a[(2 * A + 2) % 4] : w.a[2 * A + 1];
+  } else if constexpr (kind == kQ16ZR) {
+    w.zx = __builtin_amdgcn_alignbit(sl.z, sl.z, q.rot);
+  } else if constexpr (kind == kQ16ZA) {
+    w.zm[0] = magic16<0>(q, w.zx);
+    w.zm[1] = magic16<1>(q, w.zx);
+  } else if constexpr (kind == kQ16ZT) {
+    w.zt = w.zx >> 8;
+  } else if constexpr (kind == kQ16ZB) {
+    w.zm[2] = magic16<0>(q, w.zt);
+    w.zm[3] = magic16<1>(q, w.zt);
+  } else if constexpr (kind == kQ16N) {
+    // rows A and A + 4: scales in rotated words A / 2 and 2 + A / 2, half A % 2
+    w.nzs[A] = fma_mix16<0, A % 2, true>(w.zm[A], w.sw[A / 2], 0.0f);
+    w.nzs[A + 4] = fma_mix16<1, A % 2, true>(w.zm[A], w.sw[2 + A / 2], 0.0f);
+  } else if constexpr (kind == kQ16X) {
+    w.x[2 * A] = __builtin_amdgcn_alignbit(sl.w[2 * A], sl.w[2 * A], q.rot);
+    w.x[2 * A + 1] = __builtin_amdgcn_alignbit(sl.w[2 * A + 1], sl.w[2 * A + 1], q.rot);
+  } else if constexpr (kind == kQ16T) {
+    w.t[2 * A] = w.x[2 * A] >> 8;
+    w.t[2 * A + 1] = w.x[2 * A + 1] >> 8;
+  } else if constexpr (kind == kQ16M) {
+    const uint32_t x0 = A < 2 ? w.x[2 * B] : w.t[2 * B];
+    const uint32_t x1 = A < 2 ? w.x[2 * B + 1] : w.t[2 * B + 1];
+    w.m[2 * B] = magic16<A % 2>(q, x0);
+    w.m[2 * B + 1] = magic16<A % 2>(q, x1);
+  } else if constexpr (kind == kQ16V) {
+    constexpr int p = B / 2, h = B % 2;   // row A + 4h, k rows 2p and 2p + 1
+    const uint32_t s = w.sw[2 * h + A / 2];
+    w.v[2 * h] = fma_mix16<h, A % 2, false>(w.m[2 * p], s, w.nzs[A + 4 * h]);
+    w.v[2 * h + 1] = fma_mix16<h, A % 2, false>(w.m[2 * p + 1], s, w.nzs[A + 4 * h]);
+  } else if constexpr (kind == kQ16P) {
+    w.h[0][B] = pack16<F16>(w.v[0], w.v[1]);
+    w.h[1][B] = pack16<F16>(w.v[2], w.v[3]);
+  }
+}
+
+// the 16-byte stores of rows c and c + 4 into stage S
+template <int S, int C>
+__device__ __forceinline__ void q16_store(const Q16Ctx& q, const Q16Work& w) {
+  char* base = reinterpret_cast<char*>(stage64_b<S>());
+  *reinterpret_cast<uint4*>(base + q.lds[C]) =
+      make_uint4(w.h[0][0], w.h[0][1], w.h[0][2], w.h[0][3]);
+  *reinterpret_cast<uint4*>(base + q.lds[C + 4]) =
+      make_uint4(w.h[1][0], w.h[1][1], w.h[1][2], w.h[1][3]);
+}
+
+// All of one slot's operand into stage S (the prologue; copies left out).
+template <bool F16, int S, int... Ss>
+__device__ __forceinline__ void q16_form_seq(const GemmCtx64& c, const Q16Ctx& q,
+                                             const Q16Slot& sl, Q16Work& w,
+                                             std::integer_sequence<int, Ss...>) {
+  (([&] {
+     q16_op<F16, S, q16_op_at(Ss), false>(c, q, sl, w, 0);
+     if constexpr (q16_store_at(Ss) >= 0) q16_store<S, q16_store_at(Ss)>(q, w);
+   }()),
+   ...);
+}
 template <bool F16, int S>
-__device__ __forceinline__ void dq_write(const QCtx& c, const QLoad& q) {
-#pragma clang fp contract(off)
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = __builtin_amdgcn_alignbit(q.w[i], q.w[i], c.rot);
-  const uint32_t z = __builtin_amdgcn_alignbit(q.z, q.z, c.rot);
-  // the 8 scales rotated by rot / 4 positions: by 2 words, by 1 word, by a half
-  // (selects, not branches: the loop body stays one block for the scheduler)
-  const bool r16 = c.rot & 16u, r8 = c.rot & 8u, r4 = c.rot & 4u;
-  const uint32_t a0 = r16 ? q.s.z : q.s.x, a1 = r16 ? q.s.w : q.s.y;
-  const uint32_t a2 = r16 ? q.s.x : q.s.z, a3 = r16 ? q.s.y : q.s.w;
-  const uint32_t b0 = r8 ? a1 : a0, b1 = r8 ? a2 : a1, b2 = r8 ? a3 : a2, b3 = r8 ? a0 : a3;
-  const uint32_t sw[4] = {r4 ? __builtin_amdgcn_alignbit(b1, b0, 16) : b0,
-                          r4 ? __builtin_amdgcn_alignbit(b2, b1, 16) : b1,
-                          r4 ? __builtin_amdgcn_alignbit(b3, b2, 16) : b2,
-                          r4 ? __builtin_amdgcn_alignbit(b0, b3, 16) : b3};
-  char* stage = reinterpret_cast<char*>(stage_b<S>());
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const float sc = f16_to_f32(uint16_t((sw[r >> 1] >> (16 * (r & 1))) & 0xFFFFu));
-    const float nzs = -float((z >> (4 * r)) & 0xFu) * sc;
-    uint16_t h[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      h[i] = to16<F16>(__builtin_fmaf(float((w[i] >> (4 * r)) & 0xFu), sc, nzs));
-    *reinterpret_cast<uint2*>(stage + c.wofs[r]) =
-        make_uint2(uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16));
+__device__ __forceinline__ void q16_form_all(const GemmCtx64& c, const Q16Ctx& q,
+                                             const Q16Slot& sl) {
+  Q16Work w;
+  q16_form_seq<F16, S>(c, q, sl, w, std::make_integer_sequence<int, 128>{});
+}
+
+// MFMA m of region kt (stage S = kt % 2) and what follows it. MFMAs 0..63
+// finish the previous k-step (fragments f1; none in the first region) and
+// read k-step 0's fragments f0 after every fourth; MFMAs 64..127 run k-step
+// 0 and read k-step 1's into f1. Then slot m's operation for the operand of
+// k-tile kt + 1 (into stage S ^ 1), pinned there.
+template <bool F16, int S, bool PREV, int M, class V>
+__device__ __forceinline__ void q16_slot(const GemmCtx64& c, const Q16Ctx& q,
+                                         const int (&rdA)[2], const int (&rdB)[2], int kt,
+                                         floatx4 (&acc)[8][8], V (&f0a)[8], V (&f0b)[8],
+                                         V (&f1a)[8], V (&f1b)[8], const Q16Slot& sl,
+                                         Q16Work& w) {
+  constexpr int u = (M % 64) / 4, t = M % 4, i = u >> 1, j = (u & 1) * 4 + t;
+  if constexpr (M < 64) {
+    if constexpr (PREV) mfma16(acc[i][j], f1a[i], f1b[j]);
+    if constexpr (t == 0) frag16<S>(rdA[0], rdB[0], u, f0a, f0b);
+  } else {
+    mfma16_acc<!PREV>(acc[i][j], f0a[i], f0b[j]);
+    if constexpr (t == 0) frag16<S>(rdA[1], rdB[1], u, f1a, f1b);
+  }
+  constexpr int op = q16_op_at(M), st = q16_store_at(M);
+  if constexpr (op != 0 || st >= 0) {
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (st >= 0) q16_store<S ^ 1, st>(q, w);
+    if constexpr (op != 0) q16_op<F16, S ^ 1, op>(c, q, sl, w, kt);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Region kt (stage S = kt % 4): DMA of X's k-tile kt + 3; MFMAs of (kt - 1,
-// k-step 1) while (kt, 0) is read; Ŵ of k-tile kt + 3 from its slot into
-// stage (S + 3) % 4 (last read in region kt - 1) and the slot refilled with
-// k-tile kt + 5; MFMAs of (kt, 0) while (kt, 1) is read. At the end this
-// wave's LDS traffic is done and X's k-tile kt + 1 has landed: its copies
-// were issued in region kt - 2, and regions kt - 1 and kt issued 10 loads
-// each (whatever order the compiler gives a region's loads).
+template <bool F16, int S, bool PREV, class V, int... Ms>
+__device__ __forceinline__ void q16_slots(const GemmCtx64& c, const Q16Ctx& q,
+                                          const int (&rdA)[2], const int (&rdB)[2], int kt,
+                                          floatx4 (&acc)[8][8], V (&f0a)[8], V (&f0b)[8],
+                                          V (&f1a)[8], V (&f1b)[8], const Q16Slot& sl,
+                                          Q16Work& w, std::integer_sequence<int, Ms...>) {
+  (q16_slot<F16, S, PREV, Ms>(c, q, rdA, rdB, kt, acc, f0a, f0b, f1a, f1b, sl, w), ...);
+}
+
+// Region kt (stage S = kt % 2): the packed loads of k-tile kt + 2 go out
+// first, into the slot k-tile kt was formed from; the 128 MFMA slots follow;
+// the region ends, as in gemm_core.h, with one wait and one barrier.
 template <bool F16, int S, bool PREV, class V>
-__device__ __forceinline__ void region_q(const QCtx& c, int kt, floatx16 (&acc)[4][4],
-                                         V (&f0a)[4], V (&f0b)[4], V (&f1a)[4], V (&f1b)[4],
-                                         QLoad (&slot)[2]) {
-  dma_a<(S + 3) & 3>(c, kt + 3);
-  if (PREV) mfma_4x4(acc, f1a, f1b);
-  read_frags<S>(c, 0, f0a, f0b);
-  dq_write<F16, (S + 3) & 3>(c, slot[(S + 3) & 1]);
-  load_q(c, kt + 5, slot[(S + 3) & 1]);
-  mfma_4x4(acc, f0a, f0b);
-  read_frags<S>(c, 1, f1a, f1b);
-  // The dequantisation's ~190 VALU instructions and 8 LDS stores are spread
-  // over the 32 MFMAs (a few per MFMA) instead of idling the matrix cores in
-  // one block.
-  if (PREV) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgValu, 6, 0);
-      if (i & 1) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgValu, 6, 0);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgValu, 6, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgDsWrite, 1, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgValu, 4, 0);
-    if (i < 6) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
-  }
+__device__ __forceinline__ void region16q(const GemmCtx64& c, const Q16Ctx& q,
+                                          const int (&rdA)[2], const int (&rdB)[2], int kt,
+                                          floatx4 (&acc)[8][8], V (&f0a)[8], V (&f0b)[8],
+                                          V (&f1a)[8], V (&f1b)[8], Q16Slot (&slot)[2]) {
+  Q16Work w;
+  q16_load(q, kt + 2, slot[S]);
+  __builtin_amdgcn_sched_barrier(0);
+  q16_slots<F16, S, PREV>(c, q, rdA, rdB, kt, acc, f0a, f0b, f1a, f1b, slot[S ^ 1], w,
+                          std::make_integer_sequence<int, 128>{});
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  __builtin_amdgcn_s_waitcnt(wait_vm(20));
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
   region_barrier();
 }
 
@@ -397,102 +586,85 @@ void w4a16_gemm_q_kernel(const uint16_t* __restrict__ X, const int32_t* __restri
   if (!tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
   const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
-  const int tid = threadIdx.x, lane = tid & 63;
-  QCtx c;
-  c.rsA = tile_rsrc(X + m0 * K, rows_a, K);
-  const int64_t N8 = N / 8, G = int64_t(32) << gshift;
-  c.rsQ = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(qweight), 0,
+  const int tid = threadIdx.x;
+  // X through the ring (B's half of the context is unused: B is formed here)
+  GemmCtx64 c;
+  gemm_setup64(c, X + m0 * K, rows_a, X + m0 * K, rows_a, K);
+  Q16Ctx q;
+  const int64_t N8 = N / 8, G = int64_t(1) << gshift;
+  q.rsQ = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(qweight), 0,
                                             int(K * N8 * 4), 0x00020000);
-  c.rsZ = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(qzeros), 0,
+  q.rsZ = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(qzeros), 0,
                                             int(K / G * N8 * 4), 0x00020000);
-  c.rsS = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0,
+  q.rsS = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(scales), 0,
                                             int(K / G * N * 2), 0x00020000);
-  c.wave = tid >> 6;
-  c.KT = int(K / BK);
-  c.oobA = BM * int(K) * 2;
+  const int j = tid & 31, kc = tid >> 5;
+  const int64_t col = n0 / 8 + j;  // word column
+  q.oobm = col < N8 ? 0u : kQOob;
+  q.qrow = uint32_t(N8 * 4);
+  q.ktq = q.qrow * 64;
+  q.kc8 = uint32_t(8 * kc);
+  q.qoff = uint32_t((int64_t(8 * kc) * N8 + col) * 4);
+  q.zrow = uint32_t(N8 * 4);
+  q.srow = uint32_t(N * 2);
+  q.zoff = uint32_t(col * 4);
+  q.soff = uint32_t(col * 16);
+  q.gshift = gshift;
+  const int t = (j >> 1) & 3;
+  q.rot = uint32_t(8 * t);
+  q.t2 = t & 2;
+  q.t1 = t & 1;
+  // row m = (i + 2t) % 8 of the lane's 8 sits at swz64(8j + m, kc)·16
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int p = (c.wave * 4 + j) * 64 + lane;
-    const int row = p >> 2;
-    const int chunk = (p & 3) ^ ((row >> 2) & 3);
-    c.voffA[j] = (row * int(K) + chunk * 8) * 2;
-  }
-  const int wm = c.wave >> 1, wn = c.wave & 1;
-  const int fr = lane & 31, fh = lane >> 5;
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    c.rdA[ks] = swz(wm * 128 + fr, 2 * ks + fh);
-    c.rdB[ks] = swz(wn * 128 + fr, 2 * ks + fh);
-  }
-  const int kq = 2 * c.wave + (lane & 1), c8 = lane >> 1;
-  const int64_t col = n0 / 8 + c8;  // word column
-  c.oobm = col < N8 ? 0u : kQOob;
-  c.qrow = uint32_t(N8 * 4);
-  c.ktq = c.qrow * BK;
-  c.qoff = uint32_t((int64_t(4 * kq) * N8 + col) * 4);
-  c.zrow = uint32_t(N8 * 4);
-  c.srow = uint32_t(N * 2);
-  c.zoff = uint32_t(col * 4);
-  c.soff = uint32_t(col * 16);
-  c.gshift = gshift;
-  const int rho = (c8 >> 1) & 7;
-  c.rot = uint32_t(4 * rho);
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int row = 8 * c8 + ((r + rho) & 7);
-    c.wofs[r] = swz(row, kq >> 1) * 16 + (kq & 1) * 8;
-  }
+  for (int i = 0; i < 8; ++i) q.lds[i] = swz64(8 * j + ((i + 2 * t) & 7), kc) * 16;
+  // opaque to the compiler, so it keeps them in registers instead of
+  // re-materialising them at every use
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(q.mag[0]));
+  asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(q.mag[1]));
 
-  floatx16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  // prologue: k-tiles 0..2 into stages 0..2, packed k-tiles 3 and 4 in flight
-  dma_a<0>(c, 0);
-  dma_a<1>(c, 1);
-  dma_a<2>(c, 2);
-  QLoad slot[2], t2;
-  load_q(c, 0, slot[0]);
-  load_q(c, 1, slot[1]);
-  load_q(c, 2, t2);
-  dq_write<F16, 0>(c, slot[0]);
-  dq_write<F16, 1>(c, slot[1]);
-  dq_write<F16, 2>(c, t2);
-  load_q(c, 3, slot[1]);
-  load_q(c, 4, slot[0]);
+  int rdA[2], rdB[2];
+  frag_offsets16(c, rdA, rdB);
+  floatx4 acc[8][8];
+  // prologue: k-tile 0 of X and of the operand in stage 0; packed k-tile 1
+  // in slot 1, which region 0 forms from
+  Q16Slot slot[2];
+  q16_load(q, 0, slot[0]);
+  q16_load(q, 1, slot[1]);
+  dma64_a<0>(c, 0);
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  q16_form_all<F16, 0>(c, q, slot[0]);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  __builtin_amdgcn_s_waitcnt(wait_vm(12));  // X's k-tiles 0..2 landed
   region_barrier();
-  V f0a[4], f0b[4], f1a[4], f1b[4];
-  region_q<F16, 0, false>(c, 0, acc, f0a, f0b, f1a, f1b, slot);
+  V f0a[8], f0b[8], f1a[8], f1b[8];
+  region16q<F16, 0, false>(c, q, rdA, rdB, 0, acc, f0a, f0b, f1a, f1b, slot);
   int kt = 1;
-  for (; kt + 4 < c.KT; kt += 4) {
-    region_q<F16, 1, true>(c, kt, acc, f0a, f0b, f1a, f1b, slot);
-    region_q<F16, 2, true>(c, kt + 1, acc, f0a, f0b, f1a, f1b, slot);
-    region_q<F16, 3, true>(c, kt + 2, acc, f0a, f0b, f1a, f1b, slot);
-    region_q<F16, 0, true>(c, kt + 3, acc, f0a, f0b, f1a, f1b, slot);
+  for (; kt + 1 < c.KT; kt += 2) {
+    region16q<F16, 1, true>(c, q, rdA, rdB, kt, acc, f0a, f0b, f1a, f1b, slot);
+    region16q<F16, 0, true>(c, q, rdA, rdB, kt + 1, acc, f0a, f0b, f1a, f1b, slot);
   }
-  region_q<F16, 1, true>(c, kt, acc, f0a, f0b, f1a, f1b, slot);
-  region_q<F16, 2, true>(c, kt + 1, acc, f0a, f0b, f1a, f1b, slot);
-  region_q<F16, 3, true>(c, kt + 2, acc, f0a, f0b, f1a, f1b, slot);
-  mfma_4x4(acc, f1a, f1b);
+  if (kt < c.KT) region16q<F16, 1, true>(c, q, rdA, rdB, kt, acc, f0a, f0b, f1a, f1b, slot);
+  mfma_8x8(acc, f1a, f1b);
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) asm volatile("" : "+a"(acc[i][jj]));
 
-  const int64_t row0 = m0 + wm * 128 + 4 * (lane >> 5);
-  const int64_t col0 = n0 + wn * 128 + (lane & 31);
+  // lane l of block (i, j) holds column l % 16 and rows 4·(l/16) + v
+  const int lane = tid & 63;
+  const int wm = c.wave >> 1, wn = c.wave & 1;
+  const int64_t row0 = m0 + wm * 128 + 4 * (lane >> 4);
+  const int64_t col0 = n0 + wn * 128 + (lane & 15);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t cn = col0 + j * 32;
+    for (int jj = 0; jj < 8; ++jj) {
+      const int64_t cn = col0 + jj * 16;
       if (cn >= N) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = row0 + i * 32 + 8 * (v >> 2) + (v & 3);
-        if (row < M) Y[row * N + cn] = to16<F16>(acc[i][j][v]);
+      for (int v = 0; v < 4; ++v) {
+        const int64_t row = row0 + i * 16 + v;
+        if (row < M) Y[row * N + cn] = to16<F16>(acc[i][jj][v]);
       }
     }
 }
@@ -1029,7 +1201,7 @@ hipError_t launch_w4a16_gemm_q(const uint16_t* X, const int32_t* qweight, const 
   if (K % 128 || N % 8 || K * (N / 8) * 4 >= (int64_t(1) << 31) ||
       (group != 32 && group != 64 && group != 128))
     return hipErrorInvalidValue;
-  const int gshift = group == 32 ? 0 : group == 64 ? 1 : 2;
+  const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;   // log2 of the group size
   const int tiles_m = int((M + BM - 1) / BM), tiles_n = int((N + BN - 1) / BN);
   const unsigned blocks = unsigned(gemm_blocks(tiles_m, tiles_n));
   if (f16)

@@ -30,7 +30,8 @@ KERNELS = {
     "gemm.hip": [r"search_gemm_bf16_kernel", r"search_gemm_f16_kernel",
                  r"search_gemm_bf16_split_kernel", r"search_gemm_f16_split_kernel"],
     "gram.hip": [r"gram_partial_kernel", r"gram_search_kernel"],
-    "w4a16.hip": [r"w4a16_gemm_kernelILb0", r"w4a16_gemm_kernelILb1"],
+    "w4a16.hip": [r"w4a16_gemm_kernelILb0", r"w4a16_gemm_kernelILb1", r"w4a16_gemm_q_kernelILb0",
+                  r"w4a16_gemm_q_kernelILb1"],
 }
 
 
@@ -130,7 +131,10 @@ def test_asm_mfma_kernel_isa(assembly, src, kernel):
                     assert not (_regs(ops[0]) & (src_regs | dst)), \
                         f"{kernel}: VALU write {states} states before MFMA: {p} -> {ins[k]}"
 
-    # 4. LDS read results waited for before an MFMA reads them
+    # 4. LDS read results waited for before an MFMA reads them. lgkmcnt
+    # counts every LDS and scalar-memory operation in issue order (a loop
+    # that forms an operand in registers stores it to LDS among the reads),
+    # so all of them enter the queue; only reads carry registers.
     pending = []
     for s in ins:
         if s.startswith("s_waitcnt"):
@@ -141,6 +145,8 @@ def test_asm_mfma_kernel_isa(assembly, src, kernel):
             continue
         if s.startswith("ds_read"):
             pending.append(_regs(_operands(s)[0]))
+        elif s.startswith(("ds_write", "s_load", "s_buffer_load")):
+            pending.append(set())
         elif s.startswith("v_mfma"):
             _, src_regs = _mfma_regs(s)
             assert not any(p & src_regs for p in pending), f"{kernel}: MFMA reads an LDS result in flight: {s}"
