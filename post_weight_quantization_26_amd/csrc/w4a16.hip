@@ -281,11 +281,14 @@ struct Q16Slot {
 
 struct Q16Ctx {
   __amdgpu_buffer_rsrc_t rsQ, rsZ, rsS;
-  uint32_t qoff, qrow, ktq;  // bytes: lane's word at k-tile 0; per k row; per k-tile
-  uint32_t zoff, soff, zrow, srow;  // bytes: lane's group-0 entries; per group row
-  uint32_t kc8;              // 8·kc: the lane's first k row within a k-tile
+  // Vector offsets (bytes, bit 31 set for a lane whose word column is past
+  // N, so its loads read zero): the lane's qweight word at k row 8kc of
+  // k-tile 0, and its zero-point word and scales in the group that k row
+  // 64·kt + 8kc falls in, less the part common to the wave (g0(kt) group rows)
+  uint32_t qoff, zoff, soff;
+  uint32_t qrow, ktq, zrow, srow;   // bytes per k row, per k-tile, per group row (two)
+  int kt_last;               // the last k-tile
   int gshift;                // log2 of the group size
-  uint32_t oobm;             // 0, or bit 31 for a lane whose word column is past N
   uint32_t rot;              // 8t: the words' rotation in bits
   bool t2, t1;               // t & 2, t & 1: the scale words' rotation
   int lds[8];                // LDS byte offset within a stage of the lane's row i
@@ -294,19 +297,24 @@ struct Q16Ctx {
 
 constexpr uint32_t kQOob = 0x80000000u;  // past every buffer: loads read zero
 
-// Packed k-tile kt of this lane. Past the last k-tile the offsets pass the
-// end of each buffer, and lanes past N set bit 31 (c.oobm), so those loads
-// read zeros; they are never used.
+// The wave's first group row of k-tile kt: k rows 64·kt .. + 63 hold groups
+// 2kt and 2kt + 1 at group size 32 (the lane's share is in q.zoff, q.soff),
+// group kt at 64 and kt / 2 at 128.
+__device__ __forceinline__ uint32_t q16_group0(const Q16Ctx& q, int kt) {
+  return q.gshift == 5 ? uint32_t(2 * kt) : uint32_t(kt) >> (q.gshift - 6);
+}
+
+// Packed k-tile kt of this lane. The k-tile's and the group's steps are
+// common to the wave, so they go in the scalar offsets; k-tiles past the
+// last one (loaded ahead, never used) read the last one again.
 __device__ __forceinline__ void q16_load(const Q16Ctx& q, int kt, Q16Slot& sl) {
-  const uint32_t base = (q.qoff + uint32_t(kt) * q.ktq) | q.oobm;
-  const uint32_t g = (uint32_t(kt) * 64 + q.kc8) >> q.gshift;
-  // the k-row step is uniform: it goes in the scalar offset
+  const int k = kt < q.kt_last ? kt : q.kt_last;
+  const uint32_t sq = uint32_t(k) * q.ktq, g = q16_group0(q, k);
 #pragma unroll
   for (int r = 0; r < 8; ++r)
-    sl.w[r] = __builtin_amdgcn_raw_buffer_load_b32(q.rsQ, base, int(r * q.qrow), 0);
-  sl.z = __builtin_amdgcn_raw_buffer_load_b32(q.rsZ, (q.zoff + g * q.zrow) | q.oobm, 0, 0);
-  const auto sv = __builtin_amdgcn_raw_buffer_load_b128(q.rsS, (q.soff + g * q.srow) | q.oobm,
-                                                        0, 0);
+    sl.w[r] = __builtin_amdgcn_raw_buffer_load_b32(q.rsQ, q.qoff, int(sq + r * q.qrow), 0);
+  sl.z = __builtin_amdgcn_raw_buffer_load_b32(q.rsZ, q.zoff, int(g * q.zrow), 0);
+  const auto sv = __builtin_amdgcn_raw_buffer_load_b128(q.rsS, q.soff, int(g * q.srow), 0);
   sl.s = make_uint4(sv[0], sv[1], sv[2], sv[3]);
 }
 
@@ -402,12 +410,14 @@ constexpr int kQ16Copy = 1, kQ16RA = 2, kQ16RB = 3, kQ16ZR = 4, kQ16ZA = 5, kQ16
 constexpr int q16_code(int kind, int a = 0, int b = 0) { return kind * 100 + a * 10 + b; }
 
 // The schedule of a region's 128 MFMA slots: slot s runs q16_op_at(s) (0 =
-// none) after MFMA s, and the stores q16_store_at(s) (−1 = none).
+// none) after MFMA s, and the stores q16_store_at(s) (−1 = none). Every
+// operation is at least two slots after those it reads.
 //  slots 0..31: copies, then X 0..3, then T 0..3 in the even slots; RA, RB,
 //  the zero-point word and N 0..3 in the odd;
-//  slots 32..95: the classes in order 0..3, 16 slots each (M c p, V c p 0,
-//  V c p 1, P c p for p = 0..3); each class's stores go in the slot after
-//  its last pack.
+//  slots 32..97: the classes in order 0..3, 16 slots each, pair p of class
+//  c taking slots 4p .. 4p + 3 of it for M c p, P c (p − 1) (the previous
+//  class's last pack at p = 0), V c p 0 and V c p 1; class c's stores go
+//  two slots after its last pack.
 constexpr int kQ16Classes = 32;   // first slot of class 0; class c starts 16c later
 constexpr int q16_op_at(int s) {
   if (s < 32) {
@@ -424,17 +434,18 @@ constexpr int q16_op_at(int s) {
     return odd[s / 2];
   }
   const int d = s - kQ16Classes;
+  if (d == 65) return q16_code(kQ16P, 3, 3);
   if (d < 64) {
     const int c = d / 16, p = (d % 16) / 4, e = d % 4;
-    return e == 0 ? q16_code(kQ16M, c, p)
-         : e == 3 ? q16_code(kQ16P, c, p)
-                  : q16_code(kQ16V, c, 2 * p + (e - 1));
+    if (e == 0) return q16_code(kQ16M, c, p);
+    if (e == 1) return p > 0 ? q16_code(kQ16P, c, p - 1) : c > 0 ? q16_code(kQ16P, c - 1, 3) : 0;
+    return q16_code(kQ16V, c, 2 * p + (e - 2));
   }
   return 0;
 }
 constexpr int q16_store_at(int s) {
-  const int d = s - kQ16Classes - 16;
-  return d >= 0 && d < 64 && d % 16 == 0 ? d / 16 : -1;
+  const int d = s - kQ16Classes - 16 - 3;   // two slots after class c's last pack
+  return d >= 0 && d <= 48 && d % 16 == 0 ? d / 16 : -1;
 }
 
 template <bool F16, int S, int OP, bool COPY = true>
@@ -600,16 +611,19 @@ void w4a16_gemm_q_kernel(const uint16_t* __restrict__ X, const int32_t* __restri
                                             int(K / G * N * 2), 0x00020000);
   const int j = tid & 31, kc = tid >> 5;
   const int64_t col = n0 / 8 + j;  // word column
-  q.oobm = col < N8 ? 0u : kQOob;
+  const uint32_t oobm = col < N8 ? 0u : kQOob;
   q.qrow = uint32_t(N8 * 4);
   q.ktq = q.qrow * 64;
-  q.kc8 = uint32_t(8 * kc);
-  q.qoff = uint32_t((int64_t(8 * kc) * N8 + col) * 4);
   q.zrow = uint32_t(N8 * 4);
   q.srow = uint32_t(N * 2);
-  q.zoff = uint32_t(col * 4);
-  q.soff = uint32_t(col * 16);
+  q.kt_last = int(K / 64) - 1;
   q.gshift = gshift;
+  // at group size 32 the lane's k rows 8kc .. 8kc + 7 sit in the k-tile's
+  // second group for kc >= 4
+  const uint32_t gl = gshift == 5 ? uint32_t(kc >> 2) : 0u;
+  q.qoff = uint32_t((int64_t(8 * kc) * N8 + col) * 4) | oobm;
+  q.zoff = (uint32_t(col * 4) + gl * q.zrow) | oobm;
+  q.soff = (uint32_t(col * 16) + gl * q.srow) | oobm;
   const int t = (j >> 1) & 3;
   q.rot = uint32_t(8 * t);
   q.t2 = t & 2;
