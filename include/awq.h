@@ -96,7 +96,19 @@ typedef enum { AWQ_F32 = 0, AWQ_BF16 = 1, AWQ_F16 = 2 } awq_dtype;
  * for twice the search GEMM's work and twice its candidate buffer (size the
  * workspace with AWQ_OP_SEARCH_SCALE_SPLIT_E / AWQ_OP_SEARCH_CLIP_SPLIT_E).
  * Float32 layers already use float32 operands and ignore the flag; the Gram
- * searches reject it (AWQ_E_UNSUPPORTED); awq_quantize_pack ignores it. */
+ * searches reject it (AWQ_E_UNSUPPORTED); awq_quantize_pack ignores it.
+ * Or AWQ_SEARCH_FUSED for awq_search_scale and awq_search_clip on bf16 or
+ * fp16 layers with N a multiple of 256 ("05 — AWQ" section 4, the scale /
+ * quantise / measure steps in one pass): no candidate buffer is written;
+ * a parameter pass stores each (candidate, row, group)'s step, zero point
+ * and reciprocal, and the search GEMM forms the candidates' error weights
+ * while it stages its operand. The results equal those of flags = 0 bit for
+ * bit. The candidate buffer shrinks from 2K to K/2 bytes per candidate row
+ * (size the workspace with AWQ_OP_SEARCH_SCALE_FUSED /
+ * AWQ_OP_SEARCH_CLIP_FUSED; the plain ops' larger sizes work too); the
+ * search GEMM runs about 2.2 times as long. Every other search, float32
+ * layers, other N and the combination with AWQ_SEARCH_SPLIT_E are rejected
+ * (AWQ_E_UNSUPPORTED). */
 typedef struct {
   int32_t w_bit;
   int32_t group_size;
@@ -104,14 +116,16 @@ typedef struct {
   int32_t flags;
 } awq_qconfig;
 
-enum { AWQ_SEARCH_SPLIT_E = 1 };
+enum { AWQ_SEARCH_SPLIT_E = 1, AWQ_SEARCH_FUSED = 2 };
 
 enum { AWQ_OP_STATS = 0, AWQ_OP_SEARCH_SCALE = 1, AWQ_OP_SEARCH_CLIP = 2, AWQ_OP_PACK = 3,
        AWQ_OP_SEARCH_SCALE_GRAM = 4, AWQ_OP_SEARCH_CLIP_GRAM = 5,
        /* awq_gram_build, and the Gram searches that take a prepared G */
        AWQ_OP_GRAM_BUILD = 6, AWQ_OP_SEARCH_SCALE_GRAM_G = 7, AWQ_OP_SEARCH_CLIP_GRAM_G = 8,
        /* the direct searches with qc.flags = AWQ_SEARCH_SPLIT_E (bf16, fp16) */
-       AWQ_OP_SEARCH_SCALE_SPLIT_E = 9, AWQ_OP_SEARCH_CLIP_SPLIT_E = 10 };
+       AWQ_OP_SEARCH_SCALE_SPLIT_E = 9, AWQ_OP_SEARCH_CLIP_SPLIT_E = 10,
+       /* the direct searches with qc.flags = AWQ_SEARCH_FUSED (bf16, fp16) */
+       AWQ_OP_SEARCH_SCALE_FUSED = 11, AWQ_OP_SEARCH_CLIP_FUSED = 12 };
 
 /* Workspace bytes that let `op` process all `n_grid` candidates in one
  * batch (the fastest configuration). Returns 0 for invalid sizes. Pure host
@@ -120,7 +134,7 @@ size_t awq_workspace_bytes(int op, int64_t T, int64_t N, int64_t K, int32_t n_gr
                            awq_dtype dtype);
 
 /* Workspace bytes for a search (AWQ_OP_SEARCH_SCALE / AWQ_OP_SEARCH_CLIP and
- * their _SPLIT_E and Gram forms)
+ * their _SPLIT_E, _FUSED and Gram forms)
  * that works through its `n_grid` candidates in batches of at most `batch`
  * (1 <= batch <= n_grid; batch 1 is the minimum any search call accepts).
  * A search call picks the largest batch its workspace allows; results do not

@@ -22,7 +22,9 @@ AWQ_OP_STATS, AWQ_OP_SEARCH_SCALE, AWQ_OP_SEARCH_CLIP, AWQ_OP_PACK = 0, 1, 2, 3
 AWQ_OP_SEARCH_SCALE_GRAM, AWQ_OP_SEARCH_CLIP_GRAM = 4, 5
 AWQ_OP_GRAM_BUILD, AWQ_OP_SEARCH_SCALE_GRAM_G, AWQ_OP_SEARCH_CLIP_GRAM_G = 6, 7, 8
 AWQ_OP_SEARCH_SCALE_SPLIT_E, AWQ_OP_SEARCH_CLIP_SPLIT_E = 9, 10
+AWQ_OP_SEARCH_SCALE_FUSED, AWQ_OP_SEARCH_CLIP_FUSED = 11, 12
 AWQ_SEARCH_SPLIT_E = 1
+AWQ_SEARCH_FUSED = 2
 KERNEL_KINDS = {"stats": 0, "scale": 1, "transform": 2, "gemm": 3, "reduce": 4, "pack": 5,
                 "fold": 6, "dequant": 7, "w4a16": 8, "w4a16_reduce": 9, "gram_build": 10,
                 "gram_search": 11}

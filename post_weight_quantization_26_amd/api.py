@@ -60,13 +60,17 @@ def _workspace(ws: Optional[torch.Tensor], need: int, device) -> torch.Tensor:
 
 
 def qconfig(bits=DEFAULT_BITS, group=DEFAULT_GROUP, zero_point=DEFAULT_ZERO_POINT,
-            split_e=False) -> L.QConfig:
+            split_e=False, fused=False) -> L.QConfig:
     return L.QConfig(int(bits), int(group), int(bool(zero_point)),
-                     L.AWQ_SEARCH_SPLIT_E if split_e else 0)
+                     (L.AWQ_SEARCH_SPLIT_E if split_e else 0) |
+                     (L.AWQ_SEARCH_FUSED if fused else 0))
 
 
-def _direct_op(op: int, split_e: bool) -> int:
-    """The workspace op of a direct search, in its split form when asked."""
+def _direct_op(op: int, split_e: bool, fused: bool = False) -> int:
+    """The workspace op of a direct search, in its split or fused form when asked."""
+    if fused:
+        return {L.AWQ_OP_SEARCH_SCALE: L.AWQ_OP_SEARCH_SCALE_FUSED,
+                L.AWQ_OP_SEARCH_CLIP: L.AWQ_OP_SEARCH_CLIP_FUSED}.get(op, op)
     if not split_e:
         return op
     return {L.AWQ_OP_SEARCH_SCALE: L.AWQ_OP_SEARCH_SCALE_SPLIT_E,
@@ -169,13 +173,16 @@ def search_scale(X: torch.Tensor, W: torch.Tensor, abar: torch.Tensor, alphas: S
                  bits: int = DEFAULT_BITS, group: int = DEFAULT_GROUP,
                  zero_point: bool = DEFAULT_ZERO_POINT, want_row_sums: bool = False,
                  ws: Optional[torch.Tensor] = None, method: str = "direct",
-                 G: Optional[torch.Tensor] = None, split_e: bool = False) -> dict:
+                 G: Optional[torch.Tensor] = None, split_e: bool = False,
+                 fused: bool = False) -> dict:
     """Grid search over alpha. Returns alpha_best, index, s_best [K], mse (numpy
     [n_alpha]) and, if asked, row_sums [n_alpha, N] float64 on the GPU.
     method "direct" measures X·Eᵀ per candidate; "gram" (bf16 only) uses the
     activations' Gram matrix, E·G·Eᵀ per candidate row, built in the call or
     taken from ``G`` (gram_build(X)). split_e (direct method): candidates go
-    to the matrix cores as hi + lo 16-bit halves (twice the GEMM work)."""
+    to the matrix cores as hi + lo 16-bit halves (twice the GEMM work).
+    fused (direct method, 16-bit, N a multiple of 256): the search GEMM forms
+    the candidates itself from W and per-group parameters; same results."""
     gram = _method(method, G)
     _dev(X, "X"), _dev(W, "W"), _dev(abar, "abar")
     if X.dtype != W.dtype:
@@ -184,7 +191,8 @@ def search_scale(X: torch.Tensor, W: torch.Tensor, abar: torch.Tensor, alphas: S
     N = W.shape[0]
     n = len(alphas)
     op = (L.AWQ_OP_SEARCH_SCALE_GRAM_G if G is not None else
-          L.AWQ_OP_SEARCH_SCALE_GRAM if gram else _direct_op(L.AWQ_OP_SEARCH_SCALE, split_e))
+          L.AWQ_OP_SEARCH_SCALE_GRAM if gram else
+          _direct_op(L.AWQ_OP_SEARCH_SCALE, split_e, fused))
     ws = _workspace(ws, workspace_bytes(op, T, N, K, n, X.dtype), X.device)
     s_best = torch.empty(K, dtype=torch.float32, device=X.device)
     rows = torch.empty((n, N), dtype=torch.float64, device=X.device) if want_row_sums else None
@@ -194,8 +202,8 @@ def search_scale(X: torch.Tensor, W: torch.Tensor, abar: torch.Tensor, alphas: S
     fn = (L.lib().awq_search_scale_gram_g if G is not None else
           L.lib().awq_search_scale_gram if gram else L.lib().awq_search_scale)
     L.check(fn(_ptr(G if G is not None else X), _ptr(W), _dtype(X), T, N, K, _ptr(abar), grid, n,
-               qconfig(bits, group, zero_point, split_e), _ptr(s_best), ctypes.byref(a_best), mse,
-               _ptr(rows), _ptr(ws), ws.numel(), _stream()))
+               qconfig(bits, group, zero_point, split_e, fused), _ptr(s_best),
+               ctypes.byref(a_best), mse, _ptr(rows), _ptr(ws), ws.numel(), _stream()))
     mse_np = np.array(mse[:], dtype=np.float64)
     g32 = np.asarray(alphas, dtype=np.float32)
     idx = int(np.flatnonzero(g32 == np.float32(a_best.value))[0])
@@ -280,10 +288,11 @@ def search_clip(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor, ratios: Seque
                 bits: int = DEFAULT_BITS, group: int = DEFAULT_GROUP,
                 zero_point: bool = DEFAULT_ZERO_POINT, want_row_sums: bool = False,
                 ws: Optional[torch.Tensor] = None, method: str = "direct",
-                G: Optional[torch.Tensor] = None, split_e: bool = False) -> dict:
+                G: Optional[torch.Tensor] = None, split_e: bool = False,
+                fused: bool = False) -> dict:
     """Per-output-channel clip-ratio search with s fixed. Returns ratio_best [N]
-    (GPU), mse_clip (float) and optionally row_sums [n_ratio, N]. method, G
-    and split_e as in search_scale."""
+    (GPU), mse_clip (float) and optionally row_sums [n_ratio, N]. method, G,
+    split_e and fused as in search_scale."""
     gram = _method(method, G)
     _dev(X, "X"), _dev(W, "W"), _dev(s, "s")
     if X.dtype != W.dtype:
@@ -292,7 +301,8 @@ def search_clip(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor, ratios: Seque
     N = W.shape[0]
     n = len(ratios)
     op = (L.AWQ_OP_SEARCH_CLIP_GRAM_G if G is not None else
-          L.AWQ_OP_SEARCH_CLIP_GRAM if gram else _direct_op(L.AWQ_OP_SEARCH_CLIP, split_e))
+          L.AWQ_OP_SEARCH_CLIP_GRAM if gram else
+          _direct_op(L.AWQ_OP_SEARCH_CLIP, split_e, fused))
     ws = _workspace(ws, workspace_bytes(op, T, N, K, n, X.dtype), X.device)
     r_best = torch.empty(N, dtype=torch.float32, device=X.device)
     rows = torch.empty((n, N), dtype=torch.float64, device=X.device) if want_row_sums else None
@@ -300,7 +310,8 @@ def search_clip(X: torch.Tensor, W: torch.Tensor, s: torch.Tensor, ratios: Seque
     fn = (L.lib().awq_search_clip_gram_g if G is not None else
           L.lib().awq_search_clip_gram if gram else L.lib().awq_search_clip)
     L.check(fn(_ptr(G if G is not None else X), _ptr(W), _dtype(X), T, N, K, _ptr(s), L.float_array(ratios), n,
-               qconfig(bits, group, zero_point, split_e), _ptr(r_best), ctypes.byref(mse_clip),
+               qconfig(bits, group, zero_point, split_e, fused), _ptr(r_best),
+               ctypes.byref(mse_clip),
                _ptr(rows),
                _ptr(ws), ws.numel(), _stream()))
     return dict(ratio_best=r_best, mse_clip=float(mse_clip.value), row_sums=rows)

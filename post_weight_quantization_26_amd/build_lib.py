@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = ["abi.cpp", "validate.cpp", "stats.hip", "scale.hip", "transform.hip", "gemm.hip",
            "reduce.hip", "pack.hip", "fold.hip", "w4a16.hip",
-           "gram.hip"]
+           "gram.hip", "fused.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-ffp-contract=off",
           "-fhip-fp32-correctly-rounded-divide-sqrt",

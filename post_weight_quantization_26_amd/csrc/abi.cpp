@@ -24,6 +24,14 @@ hipError_t launch_transform(const void* W, int dtype, int64_t N, int64_t K, cons
                             int64_t cand_stride, hipStream_t st);
 hipError_t launch_search_gemm(const void* X, int dtype, const void* E, int64_t M, int64_t Nc,
                               int64_t K, int split, float* partials, hipStream_t st);
+hipError_t launch_group_params(const void* W, int dtype, int64_t N, int64_t K,
+                               const float* s_rows, int64_t s_stride, const float* ratios_host,
+                               int nc, int bits, int group, int zero_point, float* P,
+                               int64_t cand_stride, hipStream_t st);
+hipError_t launch_search_fused(const void* X, int dtype, const void* W, const float* P,
+                               const float* s_rows, const float* inv_rows, int64_t s_stride,
+                               int64_t M, int64_t N, int64_t K, int nc, int group, int bits,
+                               float* partials, hipStream_t st);
 hipError_t launch_reduce_rows(const float* partials, int64_t MT, int64_t Nc, double* row_sums,
                               hipStream_t st);
 hipError_t launch_curve(const double* row_sums, int n_cand, int64_t N, double denom,
@@ -161,6 +169,32 @@ awq_status run_batch(const void* X, const Segment* seg, int n_seg, awq_dtype d, 
                      const uint16_t* Gs = nullptr) {
   void* E = at<void>(ws, L.E);
   float* partials = at<float>(ws, L.partials);
+  if (qc.flags & AWQ_SEARCH_FUSED) {
+    // one layer (checked): its group parameters go where E would, and the
+    // search GEMM forms the candidates from W
+    float* P = static_cast<float*>(E);
+    const int64_t pstride = N * (K / qc.group_size);
+    AWQ_HIP(timed(AWQ_K_TRANSFORM, st,
+                  [&] {
+                    return launch_group_params(seg[0].W, dt(d), N, K, s_rows, s_stride,
+                                               ratios_host, cb, qc.w_bit, qc.group_size,
+                                               qc.zero_point, P, pstride, st);
+                  }),
+            "group_params");
+    AWQ_HIP(timed(AWQ_K_GEMM, st,
+                  [&] {
+                    return launch_search_fused(X, dt(d), seg[0].W, P, s_rows, inv_rows, s_stride,
+                                               T, N, K, cb, qc.group_size, qc.w_bit, partials,
+                                               st);
+                  }),
+            "search_fused");
+    AWQ_HIP(timed(AWQ_K_REDUCE, st,
+                  [&] {
+                    return launch_reduce_rows(partials, L.MT, int64_t(cb) * N, row_sums_out, st);
+                  }),
+            "reduce_rows");
+    return AWQ_OK;
+  }
   // split candidates: each row is a hi and a lo half (2K elements)
   const int split = splits_e(qc, d);
   const int64_t row_len = split ? 2 * K : K;
@@ -403,6 +437,9 @@ awq_status search_scale_group_op(int op, const void* X, const void* const* W, co
   int64_t N_total = 0;
   awq_status s = check_group(W, N, n_layers, &N_total);
   if (s != AWQ_OK) return s;
+  if (qc.flags & AWQ_SEARCH_FUSED)
+    return set_error(AWQ_E_UNSUPPORTED,
+                     "search_scale_group: the fused search covers single-layer searches");
   int32_t nb = 0;
   s = check_search(op, X, W[0], dtype, T, N_total, K, abar, alphas, n_alpha, qc, s_best,
                    alpha_best, mse, ws, ws_bytes, &nb);

@@ -100,7 +100,13 @@ inline bool is_gram_op(int op) {
 }
 inline bool is_scale_op(int op) {
   return op == AWQ_OP_SEARCH_SCALE || op == AWQ_OP_SEARCH_SCALE_GRAM ||
-         op == AWQ_OP_SEARCH_SCALE_GRAM_G || op == AWQ_OP_SEARCH_SCALE_SPLIT_E;
+         op == AWQ_OP_SEARCH_SCALE_GRAM_G || op == AWQ_OP_SEARCH_SCALE_SPLIT_E ||
+         op == AWQ_OP_SEARCH_SCALE_FUSED;
+}
+// Direct searches that form the candidates in the search GEMM: their
+// candidate region holds float4 group parameters, at most K/2 bytes a row.
+inline bool is_fused_op(int op) {
+  return op == AWQ_OP_SEARCH_SCALE_FUSED || op == AWQ_OP_SEARCH_CLIP_FUSED;
 }
 // Direct searches whose candidates are hi/lo halves (rows of 2K elements).
 inline bool is_split_op(int op) {
@@ -116,9 +122,14 @@ inline int unsplit_op(int op) {
 inline bool splits_e(awq_qconfig qc, awq_dtype d) {
   return (qc.flags & AWQ_SEARCH_SPLIT_E) && d != AWQ_F32;
 }
-// The op whose workspace layout a search call uses: its split form when the
-// call splits its candidates.
+// The op whose workspace layout a search call uses: its split or fused form
+// when the call splits or fuses its candidates.
 inline int layout_op(int op, awq_qconfig qc, awq_dtype d) {
+  if ((qc.flags & AWQ_SEARCH_FUSED) && d != AWQ_F32) {
+    if (op == AWQ_OP_SEARCH_SCALE) return AWQ_OP_SEARCH_SCALE_FUSED;
+    if (op == AWQ_OP_SEARCH_CLIP) return AWQ_OP_SEARCH_CLIP_FUSED;
+    return op;
+  }
   if (!splits_e(qc, d)) return op;
   if (op == AWQ_OP_SEARCH_SCALE) return AWQ_OP_SEARCH_SCALE_SPLIT_E;
   if (op == AWQ_OP_SEARCH_CLIP) return AWQ_OP_SEARCH_CLIP_SPLIT_E;

@@ -12,14 +12,15 @@
 // after candidate c-1, and the caller offsets E to the layer's first row.
 //
 // One lane owns 8 consecutive input channels of one row; the 16 lanes of a
-// 128-wide group find its min/max with xor-shuffles, so every lane holds the
-// group's step and zero point. W is read once per batch and each candidate's
-// E row segment is written with one 16-byte store per lane.
+// 128-wide group find its min/max with xor-shuffles. W is read once per
+// batch and each candidate's E row segment is written with one 16-byte store
+// per lane.
 //
 // Arithmetic per element: w' = w·s; the code quotient w'/step comes from the
 // group's IEEE reciprocal and one FMA correction (quant_code), as in the
 // packed output. The fold multiplies by a precomputed table 1/s instead of
-// dividing by s.
+// dividing by s. A group's step, zero point and reciprocal are formed by one
+// lane per candidate and shared by shuffles.
 //
 // Split operands (16-bit types only): each float32 e is stored as two
 // halves hi = rnd(e), lo = rnd(e - hi), both round-to-nearest-even, so hi +
@@ -81,20 +82,42 @@ __device__ __forceinline__ void store8<0>(void* E, int64_t idx, const float (&e)
   p[1] = make_float4(e[4], e[5], e[6], e[7]);
 }
 
+// 8 consecutive float32 scale (or reciprocal) entries of candidate row c
+__device__ __forceinline__ void load_row8(const float* rows, int64_t stride, int c, int64_t k,
+                                          float (&v)[8]) {
+  // 16-byte aligned rows (k is a multiple of 8)
+  const float4* p = reinterpret_cast<const float4*>(rows + int64_t(c) * stride + k);
+  const float4 a = p[0], b = p[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
 // DT: 0 = f32 (E in f32), 1 = bf16 (E in bf16), 2 = fp16 (E in fp16). G:
-// group size (32, 64, 128);
-// the G/8 lanes of a group reduce its range. SPLIT (DT 1 or 2): hi/lo rows.
-template <int DT, int G, bool SPLIT>
+// group size (32, 64, 128); the L = G/8 lanes of a group reduce its range.
+// SPLIT (DT 1 or 2): hi/lo rows. PARAMS: instead of E, write each (candidate,
+// row, group)'s {step, zero, 1/step, 0} to E as float4, entry
+// c·cand_stride + n·(K/G) + k/G.
+//
+// The candidates go in chunks of L: first every lane forms the group ranges
+// of the chunk's candidates (shuffles over the group's lanes), and lane i of
+// the group keeps candidate i's; then each lane forms the step and zero point
+// of its own candidate (the IEEE divisions, once per group and candidate
+// instead of once per lane); then, candidate by candidate, the group's lanes
+// take them from lane i by shuffle and quantise their 8 channels.
+template <int DT, int G, bool SPLIT, bool PARAMS>
 __global__ __launch_bounds__(kThreads) void transform_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s_rows,
     const float* __restrict__ inv_rows, int64_t s_stride, GridArgs ratios, int has_ratio, int nc,
     int bits, int zero_point, void* __restrict__ E, int64_t cand_stride) {
 #pragma clang fp contract(off)
+  constexpr int L = G / 8;
   const int64_t NK = N * K;
   const int64_t e0 = (int64_t(blockIdx.x) * kThreads + threadIdx.x) * 8;  // flat n*K + k
   // NK is a multiple of 128, so the lanes of a group are all in range or all out.
   const bool active = e0 < NK;
   const int64_t k = active ? e0 % K : 0;
+  const int lig = threadIdx.x & (L - 1);                 // lane within the group
+  const int lbase = (threadIdx.x & 63) & ~(L - 1);       // the group's first lane in the wave
 
   float w[8];
   if (active) {
@@ -104,67 +127,90 @@ __global__ __launch_bounds__(kThreads) void transform_kernel(
     for (int i = 0; i < 8; ++i) w[i] = 0.f;
   }
 
-  for (int c = 0; c < nc; ++c) {
-    // 16-byte aligned rows (k is a multiple of 8); idle lanes read column 0.
-    const float4* s4 = reinterpret_cast<const float4*>(s_rows + int64_t(c) * s_stride + k);
-    const float4* i4 = reinterpret_cast<const float4*>(inv_rows + int64_t(c) * s_stride + k);
-    const float4 sa = s4[0], sb = s4[1], ia = i4[0], ib = i4[1];
-    const float sv[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
-    const float iv[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
-    float wp[8];
-    float mx = 0.f, mn = 0.f;  // range widened to contain 0
+  for (int c0 = 0; c0 < nc; c0 += L) {
+    const int nl = nc - c0 < L ? nc - c0 : L;
+    // ranges of the chunk's candidates; lane i of the group keeps candidate c0 + i's
+    float kmx = 0.f, kmn = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      wp[i] = w[i] * sv[i];
-      mx = fmaxf(mx, wp[i]);
-      mn = fminf(mn, wp[i]);
-    }
+    for (int i = 0; i < L; ++i) {
+      if (i < nl) {   // the same for every lane
+        float sv[8];
+        load_row8(s_rows, s_stride, c0 + i, k, sv);
+        float mx = 0.f, mn = 0.f;  // range widened to contain 0
 #pragma unroll
-    for (int off = 1; off < G / 8; off <<= 1) {
-      mx = fmaxf(mx, __shfl_xor(mx, off));
-      mn = fminf(mn, __shfl_xor(mn, off));
-    }
-    const float r = has_ratio ? ratios.v[c] : 1.f;
-    const QParams p = group_qparams(mx, mn, r, bits, zero_point);
-    const float rstep = 1.0f / p.step;
-    float e[8];
+        for (int t = 0; t < 8; ++t) {
+          const float wp = w[t] * sv[t];
+          mx = fmaxf(mx, wp);
+          mn = fminf(mn, wp);
+        }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float q = quant_code(wp[i], p, rstep);
-      e[i] = ((q - p.zero) * p.step) * iv[i] - w[i];
-    }
-    if (!active) continue;
-    if (SPLIT) {
-      // row n = e0 / K; channel k's 128-block b = k / 128 holds hi at 256·b
-      const int64_t o = int64_t(c) * cand_stride + (e0 - k) * 2 + (k >> 7) * 256 + (k & 127);
-      float lo[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float h = rounded<DT>(e[i]);
-        lo[i] = e[i] - h;
-        e[i] = h;
+        for (int off = 1; off < L; off <<= 1) {
+          mx = fmaxf(mx, __shfl_xor(mx, off));
+          mn = fminf(mn, __shfl_xor(mn, off));
+        }
+        kmx = lig == i ? mx : kmx;
+        kmn = lig == i ? mn : kmn;
       }
-      store8<DT>(E, o, e);
-      store8<DT>(E, o + 128, lo);
+    }
+    // this lane's candidate: step, zero point and reciprocal
+    const int cl = c0 + (lig < nl ? lig : 0);
+    const float r = has_ratio ? ratios.v[cl] : 1.f;
+    const QParams p = group_qparams(kmx, kmn, r, bits, zero_point);
+    const float rstep = 1.0f / p.step;
+    if constexpr (PARAMS) {
+      if (active && lig < nl) {
+        const int64_t n = e0 / K;
+        reinterpret_cast<float4*>(E)[int64_t(cl) * cand_stride + n * (K / G) + k / G] =
+            make_float4(p.step, p.zero, rstep, 0.f);
+      }
     } else {
-      store8<DT>(E, int64_t(c) * cand_stride + e0, e);
+      for (int i = 0; i < nl; ++i) {
+        const int c = c0 + i;
+        const QParams pc{__shfl(p.step, lbase + i), __shfl(p.zero, lbase + i), p.qmax};
+        const float rc = __shfl(rstep, lbase + i);
+        float sv[8], iv[8];
+        load_row8(s_rows, s_stride, c, k, sv);
+        load_row8(inv_rows, s_stride, c, k, iv);
+        float e[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float q = quant_code(w[t] * sv[t], pc, rc);
+          e[t] = ((q - pc.zero) * pc.step) * iv[t] - w[t];
+        }
+        if (!active) continue;
+        if constexpr (SPLIT) {
+          // row n = e0 / K; channel k's 128-block b = k / 128 holds hi at 256·b
+          const int64_t o = int64_t(c) * cand_stride + (e0 - k) * 2 + (k >> 7) * 256 + (k & 127);
+          float lo[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const float h = rounded<DT>(e[t]);
+            lo[t] = e[t] - h;
+            e[t] = h;
+          }
+          store8<DT>(E, o, e);
+          store8<DT>(E, o + 128, lo);
+        } else {
+          store8<DT>(E, int64_t(c) * cand_stride + e0, e);
+        }
+      }
     }
   }
 }
 
-template <int DT, bool SPLIT>
+template <int DT, bool SPLIT, bool PARAMS>
 hipError_t launch_transform_g(int group, unsigned blocks, hipStream_t st, const void* W, int64_t N,
                               int64_t K, const float* s_rows, const float* inv_rows,
                               int64_t s_stride, const GridArgs& g, int has_ratio, int nc,
                               int bits, int zero_point, void* E, int64_t cand_stride) {
   if (group == 32)
-    transform_kernel<DT, 32, SPLIT><<<blocks, kThreads, 0, st>>>(
+    transform_kernel<DT, 32, SPLIT, PARAMS><<<blocks, kThreads, 0, st>>>(
         W, N, K, s_rows, inv_rows, s_stride, g, has_ratio, nc, bits, zero_point, E, cand_stride);
   else if (group == 64)
-    transform_kernel<DT, 64, SPLIT><<<blocks, kThreads, 0, st>>>(
+    transform_kernel<DT, 64, SPLIT, PARAMS><<<blocks, kThreads, 0, st>>>(
         W, N, K, s_rows, inv_rows, s_stride, g, has_ratio, nc, bits, zero_point, E, cand_stride);
   else
-    transform_kernel<DT, 128, SPLIT><<<blocks, kThreads, 0, st>>>(
+    transform_kernel<DT, 128, SPLIT, PARAMS><<<blocks, kThreads, 0, st>>>(
         W, N, K, s_rows, inv_rows, s_stride, g, has_ratio, nc, bits, zero_point, E, cand_stride);
   return hipGetLastError();
 }
@@ -181,19 +227,47 @@ hipError_t launch_transform(const void* W, int dtype, int64_t N, int64_t K, cons
   const int64_t lanes = N * K / 8;
   const unsigned blocks = unsigned((lanes + kThreads - 1) / kThreads);
   if (dtype == 1 && split)
-    return launch_transform_g<1, true>(group, blocks, st, W, N, K, s_rows, inv_rows, s_stride, g,
-                                       has_ratio, nc, bits, zero_point, E, cand_stride);
+    return launch_transform_g<1, true, false>(group, blocks, st, W, N, K, s_rows, inv_rows,
+                                              s_stride, g, has_ratio, nc, bits, zero_point, E,
+                                              cand_stride);
   if (dtype == 1)
-    return launch_transform_g<1, false>(group, blocks, st, W, N, K, s_rows, inv_rows, s_stride, g,
-                                        has_ratio, nc, bits, zero_point, E, cand_stride);
+    return launch_transform_g<1, false, false>(group, blocks, st, W, N, K, s_rows, inv_rows,
+                                               s_stride, g, has_ratio, nc, bits, zero_point, E,
+                                               cand_stride);
   if (dtype == 2 && split)
-    return launch_transform_g<2, true>(group, blocks, st, W, N, K, s_rows, inv_rows, s_stride, g,
-                                       has_ratio, nc, bits, zero_point, E, cand_stride);
+    return launch_transform_g<2, true, false>(group, blocks, st, W, N, K, s_rows, inv_rows,
+                                              s_stride, g, has_ratio, nc, bits, zero_point, E,
+                                              cand_stride);
   if (dtype == 2)
-    return launch_transform_g<2, false>(group, blocks, st, W, N, K, s_rows, inv_rows, s_stride, g,
-                                        has_ratio, nc, bits, zero_point, E, cand_stride);
-  return launch_transform_g<0, false>(group, blocks, st, W, N, K, s_rows, inv_rows, s_stride, g,
-                                      has_ratio, nc, bits, zero_point, E, cand_stride);
+    return launch_transform_g<2, false, false>(group, blocks, st, W, N, K, s_rows, inv_rows,
+                                               s_stride, g, has_ratio, nc, bits, zero_point, E,
+                                               cand_stride);
+  return launch_transform_g<0, false, false>(group, blocks, st, W, N, K, s_rows, inv_rows,
+                                             s_stride, g, has_ratio, nc, bits, zero_point, E,
+                                             cand_stride);
+}
+
+// The group parameters of every (candidate, row, group) as float4 {step,
+// zero, 1/step, 0}: candidate c's N·K/G entries start c·cand_stride entries
+// into P (the fused search's table).
+hipError_t launch_group_params(const void* W, int dtype, int64_t N, int64_t K,
+                               const float* s_rows, int64_t s_stride, const float* ratios_host,
+                               int nc, int bits, int group, int zero_point, float* P,
+                               int64_t cand_stride, hipStream_t st) {
+  GridArgs g{};
+  const int has_ratio = ratios_host != nullptr;
+  for (int i = 0; i < nc && i < 64; ++i) g.v[i] = has_ratio ? ratios_host[i] : 1.f;
+  const int64_t lanes = N * K / 8;
+  const unsigned blocks = unsigned((lanes + kThreads - 1) / kThreads);
+  if (dtype == 1)
+    return launch_transform_g<1, false, true>(group, blocks, st, W, N, K, s_rows, s_rows,
+                                              s_stride, g, has_ratio, nc, bits, zero_point, P,
+                                              cand_stride);
+  if (dtype == 2)
+    return launch_transform_g<2, false, true>(group, blocks, st, W, N, K, s_rows, s_rows,
+                                              s_stride, g, has_ratio, nc, bits, zero_point, P,
+                                              cand_stride);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace awq

@@ -111,8 +111,11 @@ SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_gr
   L.inv = off;
   off += align_up(n_tab * size_t(K) * 4);
   L.E = off;
-  off += align_up(size_t(nb) * size_t(N) * size_t(K) * dtype_bytes(dtype) *
-                  (is_split_op(op) ? 2 : 1));
+  // fused searches: (step, zero, 1/step) per row and group of at least 32
+  // channels, 16 bytes each
+  off += align_up(is_fused_op(op) ? size_t(nb) * size_t(N) * size_t(K / 32) * 16
+                                  : size_t(nb) * size_t(N) * size_t(K) * dtype_bytes(dtype) *
+                                        (is_split_op(op) ? 2 : 1));
   L.partials = off;
   off += align_up(size_t(L.MT) * size_t(nb) * size_t(N) * 4);
   L.row_sums = off;
@@ -229,8 +232,8 @@ static awq_status check_qconfig(awq_qconfig qc) {
     return set_error(AWQ_E_UNSUPPORTED, "w_bit %d not supported (3 or 4)", qc.w_bit);
   if (qc.zero_point != 0 && qc.zero_point != 1)
     return set_error(AWQ_E_INVALID, "zero_point must be 0 or 1");
-  if (qc.flags != 0 && qc.flags != AWQ_SEARCH_SPLIT_E)
-    return set_error(AWQ_E_INVALID, "flags must be 0 or AWQ_SEARCH_SPLIT_E");
+  if (qc.flags != 0 && qc.flags != AWQ_SEARCH_SPLIT_E && qc.flags != AWQ_SEARCH_FUSED)
+    return set_error(AWQ_E_INVALID, "flags must be 0, AWQ_SEARCH_SPLIT_E or AWQ_SEARCH_FUSED");
   return AWQ_OK;
 }
 
@@ -252,6 +255,12 @@ awq_status check_search(int op, const void* X, const void* W, awq_dtype d, int64
     return set_error(AWQ_E_UNSUPPORTED, "%s: the Gram path takes bf16 inputs", nm);
   if (is_gram_op(op) && (qc.flags & AWQ_SEARCH_SPLIT_E))
     return set_error(AWQ_E_UNSUPPORTED, "%s: split candidates are for the direct searches", nm);
+  if ((qc.flags & AWQ_SEARCH_FUSED) && (is_gram_op(op) || d == AWQ_F32))
+    return set_error(AWQ_E_UNSUPPORTED,
+                     "%s: the fused search is for the direct searches of bf16 and fp16 layers", nm);
+  if ((qc.flags & AWQ_SEARCH_FUSED) && N % 256)
+    return set_error(AWQ_E_UNSUPPORTED, "%s: the fused search needs N a multiple of 256 (N=%lld)",
+                     nm, (long long)N);
   if (T < 1 || N < 1 || K < 1 || T > kMaxDim || N > kMaxDim || K > kMaxDim)
     return set_error(AWQ_E_INVALID, "%s: bad shape T=%lld N=%lld K=%lld", nm, (long long)T,
                      (long long)N, (long long)K);
@@ -517,6 +526,10 @@ extern "C" size_t awq_workspace_bytes(int op, int64_t T, int64_t N, int64_t K, i
       // float32 layers do not split: their searches use the plain layout
       return search_layout(dtype == AWQ_F32 ? unsplit_op(op) : op, T, N, K, n_grid, n_grid,
                            dtype).total;
+    case AWQ_OP_SEARCH_SCALE_FUSED:
+    case AWQ_OP_SEARCH_CLIP_FUSED:
+      if (dtype == AWQ_F32 || K % kTileK) return 0;   // 16-bit layers only
+      return search_layout(op, T, N, K, n_grid, n_grid, dtype).total;
     case AWQ_OP_SEARCH_SCALE_GRAM:
     case AWQ_OP_SEARCH_CLIP_GRAM:
     case AWQ_OP_SEARCH_SCALE_GRAM_G:
@@ -539,7 +552,7 @@ extern "C" size_t awq_workspace_bytes_batch(int op, int64_t T, int64_t N, int64_
                                             int32_t n_grid, int32_t batch, awq_dtype dtype) {
   using namespace awq;
   if (op != AWQ_OP_SEARCH_SCALE && op != AWQ_OP_SEARCH_CLIP && !is_gram_op(op) &&
-      !is_split_op(op))
+      !is_split_op(op) && !is_fused_op(op))
     return 0;
   if (batch < 1 || batch > n_grid) return 0;
   if (awq_workspace_bytes(op, T, N, K, n_grid, dtype) == 0) return 0;

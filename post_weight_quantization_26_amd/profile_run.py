@@ -44,6 +44,14 @@
       the matrix-core utilisation (SQ_VALU_MFMA_BUSY_CYCLES per SIMD over
       GRBM_GUI_ACTIVE per XCD), stored with the SHA-256 of the sources now.
 
+  python -m post_weight_quantization_26_amd.profile_run fused [--reps 3]
+      The α search of the 4096 x 4096 bf16 layer over 65,536 tokens and 20
+      candidates (INT4, group 128), two-pass (transform writes every
+      candidate's E, then the search GEMM) and fused (a parameter pass, then
+      the search GEMM forming E itself), ``reps`` timed calls each after one
+      warm-up; prints the library's HIP-event kernel times per call and the
+      whole call's time, and checks that both curves are identical.
+
   python -m post_weight_quantization_26_amd.profile_run library_gemm [--reps 5]
       For comparison only: the vendor library's bf16 GEMM (torch.matmul, i.e.
       hipBLASLt) on the search GEMM's shape, X [65536, 4096] times the 20
@@ -302,10 +310,57 @@ def library_gemm(reps: int) -> None:
                       "frac_of_2500": round(flops / (ms * 1e-3) / 2.5e15, 4)}), flush=True)
 
 
+def fused(reps: int) -> None:
+    import json
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    if root not in sys.path:
+        sys.path.insert(0, root)
+    import numpy as np
+    import torch
+    from post_weight_quantization_26_amd import api
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    T, N, K = 65536, 4096, 4096
+    X = torch.randn((T, K), generator=g, device=dev)
+    X[:, :41] *= 20.0   # a few large input channels
+    X = X.to(torch.bfloat16)
+    W = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    abar = api.act_stats(X)
+    alphas = [i / 20 for i in range(20)]
+    ws = torch.empty(api.workspace_bytes(api.L.AWQ_OP_SEARCH_SCALE, T, N, K, 20, X.dtype),
+                     dtype=torch.uint8, device=dev)
+    curves = {}
+    for fz in (False, True):
+        api.search_scale(X, W, abar, alphas, ws=ws, fused=fz)
+        torch.cuda.synchronize()
+        api.profile_enable(True)
+        api.profile_reset()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            r = api.search_scale(X, W, abar, alphas, ws=ws, fused=fz)
+        b.record()
+        torch.cuda.synchronize()
+        t = {k: api.profile_read(k)[0] / reps for k in ("transform", "gemm", "reduce")}
+        api.profile_enable(False)
+        curves[fz] = r["mse"]
+        flops = 2.0 * T * 20 * N * K
+        print(json.dumps({"path": "fused" if fz else "two-pass",
+                          "transform_or_params_ms": round(t["transform"], 3),
+                          "gemm_ms": round(t["gemm"], 3), "reduce_ms": round(t["reduce"], 3),
+                          "call_ms": round(a.elapsed_time(b) / reps, 3),
+                          "gemm_frac_of_2500": round(flops / (t["gemm"] * 1e-3) / 2.5e15, 4)}),
+              flush=True)
+    print(json.dumps({"curves_identical": bool(np.array_equal(curves[False], curves[True]))}),
+          flush=True)
+
+
 def main(argv=None) -> int:
     p = argparse.ArgumentParser()
     p.add_argument("what", choices=["copy", "fold", "w4a16", "pack", "traffic", "counters",
-                                    "library_gemm"])
+                                    "library_gemm", "fused"])
     p.add_argument("--pmc")
     p.add_argument("--mib", type=int, default=1024)
     p.add_argument("--reps", type=int, default=20)
@@ -319,6 +374,8 @@ def main(argv=None) -> int:
         counters(a.record, a.pmc)
     elif a.what == "library_gemm":
         library_gemm(a.reps)
+    elif a.what == "fused":
+        fused(a.reps if a.reps != 20 else 3)
     elif a.what == "copy":
         copy(a.mib)
     elif a.what == "fold":

@@ -66,7 +66,7 @@ def test_workspace_sizes(L):
     assert st == L.AWQ_E_WORKSPACE
     assert ws(L.AWQ_OP_PACK, 1, 4096, 4096, 1, L.AWQ_BF16) > 0
     assert ws(L.AWQ_OP_STATS, 65536, 1, 4096, 1, L.AWQ_BF16) >= 4096 * 8
-    for bad in ((11, 1, 1, 1, 1, 1), (1, 0, 1, 1, 1, 1), (1, 1, 1, 1, 0, 1), (1, 1, 1, 1, 65, 1),
+    for bad in ((13, 1, 1, 1, 1, 1), (1, 0, 1, 1, 1, 1), (1, 1, 1, 1, 0, 1), (1, 1, 1, 1, 65, 1),
                 (1, 1, 1, 1, 1, 7)):
         assert ws(*bad) == 0
     # split candidates: the candidate buffer doubles; float32 layers do not split
@@ -83,6 +83,29 @@ def test_workspace_sizes(L):
     st = lib.awq_search_scale(FAKEW, FAKEW, L.AWQ_BF16, 65536, 4096, 4096, FAKEW,
                               L.float_array([0.5] * 20), 20, L.QConfig(4, 128, 1, 1), FAKEW,
                               ctypes.byref(a_best), mse, None, FAKEW, one, None)
+    assert st == L.AWQ_E_WORKSPACE
+    # fused searches: K/2 bytes per candidate row instead of 2K; 16-bit layers only
+    for plain, fused in ((L.AWQ_OP_SEARCH_SCALE, L.AWQ_OP_SEARCH_SCALE_FUSED),
+                         (L.AWQ_OP_SEARCH_CLIP, L.AWQ_OP_SEARCH_CLIP_FUSED)):
+        for dt in (L.AWQ_BF16, L.AWQ_F16):
+            a, b = ws(plain, 65536, 4096, 4096, 20, dt), ws(fused, 65536, 4096, 4096, 20, dt)
+            assert a - b == 20 * 4096 * (4096 * 2 - 4096 // 2)
+            a1 = lib.awq_workspace_bytes_batch(plain, 65536, 4096, 4096, 20, 1, dt)
+            b1 = lib.awq_workspace_bytes_batch(fused, 65536, 4096, 4096, 20, 1, dt)
+            assert a1 - b1 == 4096 * (4096 * 2 - 4096 // 2)
+        assert ws(fused, 256, 512, 512, 20, L.AWQ_F32) == 0
+        assert lib.awq_workspace_bytes_batch(fused, 256, 512, 512, 20, 2, L.AWQ_F32) == 0
+    # a fused search takes its own (smaller) size; the unfused search does not
+    fz = L.QConfig(4, 128, 1, L.AWQ_SEARCH_FUSED)
+    f1 = lib.awq_workspace_bytes_batch(L.AWQ_OP_SEARCH_SCALE_FUSED, 65536, 4096, 4096, 20, 1,
+                                       L.AWQ_BF16)
+    st = lib.awq_search_scale(FAKEW, FAKEW, L.AWQ_BF16, 65536, 4096, 4096, FAKEW,
+                              L.float_array([0.5] * 20), 20, fz, FAKEW,
+                              ctypes.byref(a_best), mse, None, FAKEW, f1 - 1, None)
+    assert st == L.AWQ_E_WORKSPACE
+    st = lib.awq_search_scale(FAKEW, FAKEW, L.AWQ_BF16, 65536, 4096, 4096, FAKEW,
+                              L.float_array([0.5] * 20), 20, L.QConfig(4, 128, 1), FAKEW,
+                              ctypes.byref(a_best), mse, None, FAKEW, f1, None)
     assert st == L.AWQ_E_WORKSPACE
 
 
@@ -118,7 +141,7 @@ def _search(L, op, **kw):
     (dict(grid=[0.5] * 65), -1), (dict(grid=[]), -1),
     (dict(X=MIS), -1), (dict(W=MIS), -1),
     (dict(ws=None), -3), (dict(ws_bytes=1000), -3), (dict(ws=MIS), -3),
-    (dict(flags=2), -1), (dict(flags=-1), -1),
+    (dict(flags=3), -1), (dict(flags=4), -1), (dict(flags=-1), -1),
 ])
 @pytest.mark.parametrize("op", ["scale", "clip"])
 def test_search_rejects(L, kw, status, op):
@@ -140,6 +163,40 @@ def test_gram_searches_reject_split(L):
     assert st == L.AWQ_E_UNSUPPORTED and "direct" in L.last_error()
     # a float32 layer accepts the flag (its candidates are float32 already)
     assert _search(L, "scale", dtype=L.AWQ_F32, qc=L.QConfig(4, 128, 1, 1), ws_bytes=10) == -3
+
+
+@pytest.mark.parametrize("op", ["scale", "clip"])
+def test_fused_search_limits(L, op):
+    fused = L.QConfig(4, 128, 1, L.AWQ_SEARCH_FUSED)
+    # a bf16 layer with N a multiple of 256 passes every check before the workspace one
+    assert _search(L, op, qc=fused, ws_bytes=10) == L.AWQ_E_WORKSPACE
+    assert _search(L, op, qc=L.QConfig(4, 64, 0, L.AWQ_SEARCH_FUSED), dtype=L.AWQ_F16, N=512,
+                   ws_bytes=10) == L.AWQ_E_WORKSPACE
+    # N not a multiple of 256, float32 layers
+    assert _search(L, op, qc=fused, N=384) == L.AWQ_E_UNSUPPORTED
+    assert "multiple of 256" in L.last_error()
+    assert _search(L, op, qc=fused, dtype=L.AWQ_F32) == L.AWQ_E_UNSUPPORTED
+    # the parameter table fits the fused workspace's candidate region at every group size
+    for fused in (L.AWQ_OP_SEARCH_SCALE_FUSED, L.AWQ_OP_SEARCH_CLIP_FUSED):
+        one = L.lib().awq_workspace_bytes_batch(fused, 4096, 4096, 4096, 20, 1, L.AWQ_BF16)
+        assert one > 4096 * (4096 // 32) * 16
+
+
+def test_fused_search_rejected_elsewhere(L):
+    lib = L.lib()
+    a_best = ctypes.c_float()
+    mse = (ctypes.c_double * 4)()
+    fused = L.QConfig(4, 128, 1, L.AWQ_SEARCH_FUSED)
+    st = lib.awq_search_scale_gram(FAKE, FAKE, L.AWQ_BF16, 256, 256, 256, FAKE,
+                                   L.float_array([0.5]), 1, fused, FAKE, ctypes.byref(a_best),
+                                   mse, None, FAKE, 1 << 40, None)
+    assert st == L.AWQ_E_UNSUPPORTED and "direct" in L.last_error()
+    W = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    N = (ctypes.c_int64 * 2)(256, 256)
+    st = lib.awq_search_scale_group(FAKE, W, N, 2, L.AWQ_BF16, 256, 256, FAKE,
+                                    L.float_array([0.5]), 1, fused, FAKE, ctypes.byref(a_best),
+                                    mse, None, FAKE, 1 << 40, None)
+    assert st == L.AWQ_E_UNSUPPORTED and "single-layer" in L.last_error()
 
 
 @pytest.mark.parametrize("qc,status", [((5, 128, 1), -2), ((2, 128, 1), -2), ((4, 16, 1), -2),

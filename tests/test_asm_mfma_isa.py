@@ -32,6 +32,7 @@ KERNELS = {
     "gram.hip": [r"gram_partial_kernel", r"gram_search_kernel"],
     "w4a16.hip": [r"w4a16_gemm_kernelILb0", r"w4a16_gemm_kernelILb1", r"w4a16_gemm_q_kernelILb0",
                   r"w4a16_gemm_q_kernelILb1"],
+    "fused.hip": [r"search_fused_kernelILb0", r"search_fused_kernelILb1"],
 }
 
 
