@@ -27,6 +27,8 @@
 // lo is e to ~16 significand bits. A row then has length 2K with the halves
 // in alternating 128-wide blocks: channel k's hi at (k / 128)·256 + k % 128,
 // its lo 128 further on (the layout the search GEMM's split kernels read).
+#include <utility>
+
 #include "device_common.h"
 
 namespace awq {
@@ -82,6 +84,43 @@ __device__ __forceinline__ void store8<0>(void* E, int64_t idx, const float (&e)
   p[1] = make_float4(e[4], e[5], e[6], e[7]);
 }
 
+// Cross-lane moves inside a group of L = 4, 8 or 16 lanes (aligned runs of
+// a 16-lane DPP row), as VALU instructions instead of LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// every lane of the group gets the group's max (MAX) or min: lanes xor 1 and
+// xor 2 within a quad, then the half-row mirror (lane i and 7 - i: the other
+// quad of 8 lanes), then the row mirror (lane i and 15 - i: the other half)
+template <int L, bool MAX>
+__device__ __forceinline__ float group_reduce(float v) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+  v = op(v, dpp<0xB1>(v));                    // quad_perm [1, 0, 3, 2]
+  v = op(v, dpp<0x4E>(v));                    // quad_perm [2, 3, 0, 1]
+  if constexpr (L >= 8) v = op(v, dpp<0x141>(v));   // row_half_mirror
+  if constexpr (L >= 16) v = op(v, dpp<0x140>(v));  // row_mirror
+  return v;
+}
+// lane I of the group, for every lane of the group
+template <int L, int I>
+__device__ __forceinline__ float group_bcast(float v) {
+  if constexpr (L == 16) {
+    return dpp<0x150 + I>(v);                 // row_newbcast: lane I of the row
+  } else if constexpr (L == 8) {
+    const float a = dpp<0x150 + I>(v), b = dpp<0x158 + I>(v);
+    return (threadIdx.x & 8) ? b : a;
+  } else {
+    return dpp<I | (I << 2) | (I << 4) | (I << 6)>(v);   // quad_perm [I, I, I, I]
+  }
+}
+
+// f(integral_constant<I>) for I = 0 .. n - 1 (n <= the sequence's length)
+template <class F, int... Is>
+__device__ __forceinline__ void first_n(F& f, int n, std::integer_sequence<int, Is...>) {
+  ((Is < n ? f(std::integral_constant<int, Is>{}) : void()), ...);
+}
+
 // 8 consecutive float32 scale (or reciprocal) entries of candidate row c
 __device__ __forceinline__ void load_row8(const float* rows, int64_t stride, int c, int64_t k,
                                           float (&v)[8]) {
@@ -99,11 +138,12 @@ __device__ __forceinline__ void load_row8(const float* rows, int64_t stride, int
 // c·cand_stride + n·(K/G) + k/G.
 //
 // The candidates go in chunks of L: first every lane forms the group ranges
-// of the chunk's candidates (shuffles over the group's lanes), and lane i of
-// the group keeps candidate i's; then each lane forms the step and zero point
-// of its own candidate (the IEEE divisions, once per group and candidate
-// instead of once per lane); then, candidate by candidate, the group's lanes
-// take them from lane i by shuffle and quantise their 8 channels.
+// of the chunk's candidates (DPP reductions over the group's lanes), and lane
+// i of the group keeps candidate i's; then each lane forms the step and zero
+// point of its own candidate (the IEEE divisions, once per group and
+// candidate instead of once per lane); then, candidate by candidate, the
+// group's lanes take them from lane i by DPP broadcast and quantise their 8
+// channels.
 template <int DT, int G, bool SPLIT, bool PARAMS>
 __global__ __launch_bounds__(kThreads) void transform_kernel(
     const void* __restrict__ W, int64_t N, int64_t K, const float* __restrict__ s_rows,
@@ -117,7 +157,6 @@ __global__ __launch_bounds__(kThreads) void transform_kernel(
   const bool active = e0 < NK;
   const int64_t k = active ? e0 % K : 0;
   const int lig = threadIdx.x & (L - 1);                 // lane within the group
-  const int lbase = (threadIdx.x & 63) & ~(L - 1);       // the group's first lane in the wave
 
   float w[8];
   if (active) {
@@ -143,11 +182,8 @@ __global__ __launch_bounds__(kThreads) void transform_kernel(
           mx = fmaxf(mx, wp);
           mn = fminf(mn, wp);
         }
-#pragma unroll
-        for (int off = 1; off < L; off <<= 1) {
-          mx = fmaxf(mx, __shfl_xor(mx, off));
-          mn = fminf(mn, __shfl_xor(mn, off));
-        }
+        mx = group_reduce<L, true>(mx);
+        mn = group_reduce<L, false>(mn);
         kmx = lig == i ? mx : kmx;
         kmn = lig == i ? mn : kmn;
       }
@@ -164,10 +200,11 @@ __global__ __launch_bounds__(kThreads) void transform_kernel(
             make_float4(p.step, p.zero, rstep, 0.f);
       }
     } else {
-      for (int i = 0; i < nl; ++i) {
+      auto one = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
         const int c = c0 + i;
-        const QParams pc{__shfl(p.step, lbase + i), __shfl(p.zero, lbase + i), p.qmax};
-        const float rc = __shfl(rstep, lbase + i);
+        const QParams pc{group_bcast<L, i>(p.step), group_bcast<L, i>(p.zero), p.qmax};
+        const float rc = group_bcast<L, i>(rstep);
         float sv[8], iv[8];
         load_row8(s_rows, s_stride, c, k, sv);
         load_row8(inv_rows, s_stride, c, k, iv);
@@ -177,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void transform_kernel(
           const float q = quant_code(w[t] * sv[t], pc, rc);
           e[t] = ((q - pc.zero) * pc.step) * iv[t] - w[t];
         }
-        if (!active) continue;
+        if (!active) return;
         if constexpr (SPLIT) {
           // row n = e0 / K; channel k's 128-block b = k / 128 holds hi at 256·b
           const int64_t o = int64_t(c) * cand_stride + (e0 - k) * 2 + (k >> 7) * 256 + (k & 127);
@@ -193,7 +230,9 @@ __global__ __launch_bounds__(kThreads) void transform_kernel(
         } else {
           store8<DT>(E, int64_t(c) * cand_stride + e0, e);
         }
-      }
+      };
+      // candidates c0 .. c0 + nl - 1, each with its lane's parameters
+      first_n(one, nl, std::make_integer_sequence<int, L>{});
     }
   }
 }
