@@ -106,7 +106,7 @@ typedef enum { AWQ_F32 = 0, AWQ_BF16 = 1, AWQ_F16 = 2 } awq_dtype;
  * bit. The candidate buffer shrinks from 2K to K/2 bytes per candidate row
  * (size the workspace with AWQ_OP_SEARCH_SCALE_FUSED /
  * AWQ_OP_SEARCH_CLIP_FUSED; the plain ops' larger sizes work too); the
- * search GEMM runs about 2.2 times as long. Every other search, float32
+ * search GEMM runs about 1.9 times as long. Every other search, float32
  * layers, other N and the combination with AWQ_SEARCH_SPLIT_E are rejected
  * (AWQ_E_UNSUPPORTED). */
 typedef struct {

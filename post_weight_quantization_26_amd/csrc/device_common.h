@@ -124,15 +124,18 @@ __device__ __forceinline__ QParams group_qparams(float mx, float mn, float ratio
   return p;
 }
 
-// Code of a scaled weight. The quotient w'/step comes from the group's IEEE
-// reciprocal `rstep` = 1/step and one FMA correction step, which gives the
-// correctly rounded quotient up to at most one ulp in rare cases; a code can
-// differ from exact division only when the quotient lies within one ulp of a
-// .5 rounding boundary.
-__device__ __forceinline__ float quant_code(float wp, const QParams& p, float rstep) {
+// Code of a scaled weight, less its zero point: q - zero with q =
+// clamp(rint(w'/step) + zero, 0, qmax). The quotient w'/step comes from the
+// group's IEEE reciprocal `rstep` = 1/step and one FMA correction step, which
+// gives the correctly rounded quotient up to at most one ulp in rare cases; a
+// code can differ from exact division only when the quotient lies within one
+// ulp of a .5 rounding boundary. rint(quotient), zero and qmax are integers
+// held exactly in float32, so clamping rint(quotient) to [-zero, qmax - zero]
+// (one med3) is the clamp of the code and the subtraction of the zero point.
+__device__ __forceinline__ float quant_code_centered(float wp, const QParams& p, float rstep) {
   const float q0 = wp * rstep;
   const float quo = __builtin_fmaf(__builtin_fmaf(-q0, p.step, wp), rstep, q0);
-  return fminf(fmaxf(__builtin_rintf(quo) + p.zero, 0.f), p.qmax);
+  return __builtin_amdgcn_fmed3f(__builtin_rintf(quo), -p.zero, p.qmax - p.zero);
 }
 
 }  // namespace awq

@@ -113,8 +113,8 @@ __device__ __forceinline__ void fu_form(const FuCtx& f, const FuHalf& h, const f
   for (int t = 0; t < 4; ++t) {
     const int kk = 4 * HH + t;
     const float w = fu_w<F16>(t < 2 ? wa : wb, t & 1);
-    const float q = quant_code(w * sv[kk], p, h.rstep[r]);
-    e[t] = ((q - p.zero) * p.step) * iv[kk] - w;
+    const float qc = quant_code_centered(w * sv[kk], p, h.rstep[r]);
+    e[t] = (qc * p.step) * iv[kk] - w;
   }
   // two values per packed conversion, each rounded to nearest even as the
   // transform's per-value conversion rounds it

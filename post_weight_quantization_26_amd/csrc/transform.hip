@@ -17,10 +17,11 @@
 // per lane.
 //
 // Arithmetic per element: w' = w·s; the code quotient w'/step comes from the
-// group's IEEE reciprocal and one FMA correction (quant_code), as in the
+// group's IEEE reciprocal and one FMA correction (quant_code_centered, which
+// also clamps the code and takes off the zero point in one med3), as in the
 // packed output. The fold multiplies by a precomputed table 1/s instead of
 // dividing by s. A group's step, zero point and reciprocal are formed by one
-// lane per candidate and shared by shuffles.
+// lane per candidate and shared by DPP broadcasts.
 //
 // Split operands (16-bit types only): each float32 e is stored as two
 // halves hi = rnd(e), lo = rnd(e - hi), both round-to-nearest-even, so hi +
@@ -211,8 +212,8 @@ __global__ __launch_bounds__(kThreads) void transform_kernel(
         float e[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const float q = quant_code(w[t] * sv[t], pc, rc);
-          e[t] = ((q - pc.zero) * pc.step) * iv[t] - w[t];
+          const float qc = quant_code_centered(w[t] * sv[t], pc, rc);
+          e[t] = (qc * pc.step) * iv[t] - w[t];
         }
         if (!active) return;
         if constexpr (SPLIT) {
