@@ -39,6 +39,8 @@ CASES = [
     (257, 768, 256, 32, 3, True, "bf16"),
     (700, 1024, 640, 32, 4, True, "f16"),
     (4096, 4096, 4096, 128, 4, True, "bf16"),
+    (129, 256, 128, 32, 4, True, "bf16"),     # K = 128: two k-tiles
+    (64, 512, 128, 128, 3, False, "f16"),
 ]
 
 

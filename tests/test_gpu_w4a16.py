@@ -169,22 +169,29 @@ def test_gemm_path_wide_dequant(api, N, group, dtype):
                                                (17, 544, 512, 64, "bf16"),
                                                (520, 264, 384, 128, "f16"),
                                                (520, 520, 512, 64, "bf16"),
-                                               (300, 4096, 4096, 128, "bf16")])
+                                               (300, 4096, 4096, 128, "bf16"),
+                                               # K = 128: two k-tiles, every load
+                                               # ahead of the end reads the last one
+                                               (129, 256, 128, 32, "bf16"),
+                                               (64, 520, 128, 128, "f16")])
 def test_gemm_on_the_fly(api, T, N, K, group, dtype):
     check_consumer(api, T, N, K, group, dtype, seed=240 + N + T, on_the_fly=True)
 
 
-def test_gemm_on_the_fly_equals_two_pass(api):
+@pytest.mark.parametrize("N,K,group,dtype,T", [(2056, 512, 128, "bf16", 33 * 256 - 7),
+                                               (1032, 640, 32, "f16", 700),
+                                               (512, 384, 64, "bf16", 257)])
+def test_gemm_on_the_fly_equals_two_pass(api, N, K, group, dtype, T):
     """Both prefill paths form the same rounded Ŵ and run the same MFMA
     loop over it: identical outputs."""
-    qw, qz, sc = packed_layer(2056, 512, 128, seed=250)
-    rng = np.random.default_rng(251)
-    X = _enc(rng.standard_normal((33 * 256 - 7, 512)).astype(np.float32), "bf16")
-    Xd = to_dev(X, "bf16")
+    qw, qz, sc = packed_layer(N, K, group, seed=250 + N)
+    rng = np.random.default_rng(251 + N)
+    X = _enc(rng.standard_normal((T, K)).astype(np.float32), dtype)
+    Xd = to_dev(X, dtype)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
     args = (Xd, dev(qw), dev(qz), dev(sc).view(torch.float16))
-    y1 = api.w4a16_matmul(*args)
-    y2 = api.w4a16_matmul(*args, on_the_fly=True)
+    y1 = api.w4a16_matmul(*args, group=group)
+    y2 = api.w4a16_matmul(*args, group=group, on_the_fly=True)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
