@@ -118,12 +118,16 @@ __device__ __forceinline__ int swz64(int row, int chunk) {
 // Copy j of a wave fills rows 8·j further down than copy 0, so its source
 // offset is a per-lane base (two of them: the swizzle flips by 4 on odd j)
 // plus a uniform step j·8·ld·2 bytes, which goes in the scalar offset.
+// rev: the k-loop visits the k-tiles from the last to the first (the
+// accumulation order changes, the pairing does not), so that loops of
+// different lengths over the same operand's tail read the same k-tiles at
+// the same time.
 struct GemmCtx64 {
   __amdgpu_buffer_rsrc_t rsA, rsB;
   int vbaseA[2], vbaseB[2];
   int stepA, stepB;
   int wave, KT, oobA, oobB;
-  bool pair_a, pair_b;
+  bool pair_a, pair_b, rev;
 };
 __device__ __forceinline__ void gemm_setup64(GemmCtx64& c, const uint16_t* A, int64_t rows_a,
                                              int64_t lda, const uint16_t* B, int64_t rows_b,
@@ -136,6 +140,7 @@ __device__ __forceinline__ void gemm_setup64(GemmCtx64& c, const uint16_t* A, in
   c.KT = int(KA / BK64);
   c.pair_a = pair_a;
   c.pair_b = pair_b;
+  c.rev = false;
   c.oobA = BM * int(lda) * 2;
   c.oobB = BN * int(ldb) * 2;
 #pragma unroll
@@ -156,6 +161,7 @@ __device__ __forceinline__ void gemm_setup64(GemmCtx64& c, const uint16_t* A, in
 template <int S>
 __device__ __forceinline__ void dma64(const GemmCtx64& c, int kt) {
   const bool in = kt < c.KT;
+  if (c.rev && in) kt = c.KT - 1 - kt;
   const int kta = c.pair_a ? ((kt >> 2) << 1) | (kt & 1) : kt;
   const int ktb = c.pair_b ? ((kt >> 2) << 1) | (kt & 1) : kt;
   const int kofsA = in ? kta * (BK64 * 2) : c.oobA;
@@ -219,6 +225,7 @@ template <int S>
 __device__ __forceinline__ void copy64(const GemmCtx64& c, int kt, int q) {
   // copy q of the 16 a wave issues per k-tile: A rows for q < 8, then B
   const bool in = kt < c.KT;
+  if (c.rev && in) kt = c.KT - 1 - kt;
   const int j = q & 7;
   if (q < 8) {
     const int kta = c.pair_a ? ((kt >> 2) << 1) | (kt & 1) : kt;

@@ -212,6 +212,10 @@ void gram_search_kernel(const uint16_t* __restrict__ Gs, int64_t ldg, const uint
     GemmCtx64 c;
     gemm_setup64(c, Gs + m0 * ldg + 2 * m0, rows_a, ldg, E + n0 * K + m0, rows_b, K,
                  2 * (K - m0), true);
+    // from the last k-tile down: the row tiles of one candidate tile start at
+    // different columns (256·tm) but end at the same one, so run this way
+    // the workgroups of an XCD read the same E k-tiles at the same time
+    c.rev = true;
     floatx4 acc[8][8];
     gemm_mainloop16<false>(c, acc);
 
