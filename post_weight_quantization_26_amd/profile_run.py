@@ -1,10 +1,13 @@
 """Small, fixed workloads to run under rocprofv3.
 
-  python -m post_weight_quantization_26_amd.profile_run copy [--mib 1024]
+  python -m post_weight_quantization_26_amd.profile_run copy [--mib 1024] [--reps R]
       One device-to-device copy of a known size (torch's copy kernel). Its
       FETCH_SIZE / WRITE_SIZE counters calibrate what those counters report
       per byte actually moved, so the search kernels' counter readings can be
-      converted to HBM bytes.
+      converted to HBM bytes. With --reps R > 1: R timed copies back to back,
+      cycling over enough buffers that no source stays in the last-level
+      cache; prints the time per copy (the practical rate of a transfer of
+      that size).
 
   python -m post_weight_quantization_26_amd.profile_run fold [--reps 20]
       The fold of 1/s into a preceding linear layer at the Llama-7B MLP up
@@ -66,15 +69,37 @@ import argparse
 import sys
 
 
-def copy(mib: int) -> None:
+def copy(mib: int, reps: int = 1) -> None:
     import torch
     n = mib * (1 << 20) // 2
-    src = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
-    dst = torch.empty_like(src)
+    if reps <= 1:
+        src = torch.empty(n, dtype=torch.bfloat16, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copied {mib} MiB device-to-device", flush=True)
+        return
+    # timed copies cycling over enough buffers (at least 512 MiB of sources)
+    # that no source stays in the 256 MB last-level cache between its uses
+    import json
+    nbuf = max(2, -(-512 // mib))
+    bufs = [(torch.empty(n, dtype=torch.bfloat16, device="cuda:0").fill_(1.0),
+             torch.empty(n, dtype=torch.bfloat16, device="cuda:0")) for _ in range(nbuf)]
+    for s_, d_ in bufs:
+        d_.copy_(s_)
     torch.cuda.synchronize()
-    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(reps):
+        s_, d_ = bufs[i % nbuf]
+        d_.copy_(s_)
+    b.record()
     torch.cuda.synchronize()
-    print(f"copied {mib} MiB device-to-device", flush=True)
+    us = a.elapsed_time(b) * 1e3 / reps
+    moved = 2 * n * 2
+    print(json.dumps({"copy_mib": mib, "reps": reps, "buffers": nbuf, "us_per_copy": round(us, 2),
+                      "GBps_read_plus_write": round(moved / (us * 1e-6) / 1e9, 1)}), flush=True)
 
 
 def fold(reps: int) -> None:
@@ -377,7 +402,7 @@ def main(argv=None) -> int:
     elif a.what == "fused":
         fused(a.reps if a.reps != 20 else 3)
     elif a.what == "copy":
-        copy(a.mib)
+        copy(a.mib, a.reps if a.reps != 20 else 1)
     elif a.what == "fold":
         fold(a.reps)
     elif a.what == "pack":
