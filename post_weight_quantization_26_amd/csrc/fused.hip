@@ -291,17 +291,7 @@ void search_fused_kernel(const uint16_t* __restrict__ X, const uint16_t* __restr
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   float* red = reinterpret_cast<float*>(s64A0);  // [2][BN]
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) s += acc[i][jj][v] * acc[i][jj][v];
-    s += __shfl_xor(s, 16);
-    s += __shfl_xor(s, 32);
-    if (lane < 16) red[wm * BN + wn * 128 + jj * 16 + lane] = s;
-  }
+  column_square_sums(acc, red, wm, wn, lane);
   __syncthreads();
   const int64_t Nc = int64_t(tiles_n) * BN;
   partials[int64_t(tm) * Nc + n0 + tid] = red[tid] + red[BN + tid];

@@ -11,7 +11,8 @@
 //
 // bf16 path: the 16x16x32 MFMA main loop of gemm_core.h (256x256 tiles,
 // 2-stage LDS-DMA ring of 64-wide k-tiles, XCD-aware tile order) with X as
-// the A operand and E as B.
+// the A operand and E as B, in a persistent grid of one workgroup per CU
+// whose tiles follow one another through the ring.
 // Each XCD runs 4 token tiles x 8 candidate tiles at a time while all XCDs
 // share the same 8 candidate tiles (one E panel fetch per group of 32 token
 // tiles; X panels stay in the last-level cache).
@@ -29,79 +30,106 @@
 namespace awq {
 namespace {
 
-// K must be a multiple of 128 (the entry points check it). F16: fp16
-// operands instead of bf16 (the same tile, the fp16 MFMA). SPLIT: E rows are
-// hi/lo halves of length 2K.
-template <bool F16, bool SPLIT>
-__device__ __forceinline__ void search_gemm_16(const uint16_t* __restrict__ X,
-                                               const uint16_t* __restrict__ E, int64_t M,
-                                               int64_t Nc, int64_t K, int tiles_m, int tiles_n,
-                                               float* __restrict__ partials) {
-  int tm, tn;
-  if (!tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
+// The epilogue's column sums of the two wave rows (not aliased with the
+// k-tile ring, which already holds the next tile's first k-tile).
+__shared__ float sRed[2 * BN];
+
+// Operand contexts of output tile (tm, tn).
+template <bool SPLIT>
+__device__ __forceinline__ void search_tile_setup(GemmCtx64& c, const uint16_t* X,
+                                                  const uint16_t* E, int64_t M, int64_t Nc,
+                                                  int64_t K, int tm, int tn) {
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
   const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
   const int64_t rows_b = Nc - n0 < BN ? Nc - n0 : BN;
-  GemmCtx64 c;
   if (SPLIT)
     gemm_setup64(c, X + m0 * K, rows_a, K, E + n0 * 2 * K, rows_b, 2 * K, 2 * K, false, true);
   else
     gemm_setup64(c, X + m0 * K, rows_a, E + n0 * K, rows_b, K);
-  floatx4 acc[8][8];
-  gemm_mainloop16<F16>(c, acc);
+}
+
+// First block id at or after bid, in steps of the grid size, that maps to a
+// tile; nblocks if none.
+__device__ __forceinline__ int64_t next_tile(int64_t bid, int64_t nblocks, int tiles_m,
+                                             int tiles_n, int& tm, int& tn) {
+  for (; bid < nblocks; bid += gridDim.x)
+    if (tile_of(int(bid), tiles_m, tiles_n, tm, tn)) break;
+  return bid;
+}
+
+// K must be a multiple of 128 (the entry points check it), so every tile's
+// k-loop has an even number of 64-wide k-tiles. F16: fp16 operands instead
+// of bf16 (the same tile, the fp16 MFMA). SPLIT: E rows are hi/lo halves of
+// length 2K.
+//
+// Persistent: workgroup b takes block ids b, b + grid, b + 2·grid, ... of the
+// tile_of order (with a grid of 256 that keeps each block id's XCD). Each
+// tile's last k-tile region copies the first k-tile of the workgroup's next
+// tile, so only the first tile waits for its operands.
+template <bool F16, bool SPLIT>
+__device__ __forceinline__ void search_gemm_16(const uint16_t* __restrict__ X,
+                                               const uint16_t* __restrict__ E, int64_t M,
+                                               int64_t Nc, int64_t K, int tiles_m, int tiles_n,
+                                               int64_t nblocks, float* __restrict__ partials) {
+  int tm = 0, tn = 0;
+  int64_t bid = next_tile(blockIdx.x, nblocks, tiles_m, tiles_n, tm, tn);
+  if (bid >= nblocks) return;
+  GemmCtx64 c;
+  search_tile_setup<SPLIT>(c, X, E, M, Nc, K, tm, tn);
+  dma64<0>(c, 0);
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  region_barrier();
   const int tid = threadIdx.x, lane = tid & 63;
   const int wm = c.wave >> 1, wn = c.wave & 1;
-
-  // Epilogue: each lane's 4 accumulators of block (i, j) all lie in output
-  // column j*16 + lane%16 of the wave's range; lanes l, l^16, l^32, l^48
-  // share it.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(s64A0);  // [2][BN]
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) s += acc[i][j][v] * acc[i][j][v];
-    s += __shfl_xor(s, 16);
-    s += __shfl_xor(s, 32);
-    if (lane < 16) red[wm * BN + wn * 128 + j * 16 + lane] = s;
+  for (;;) {
+    int ntm = tm, ntn = tn;
+    const int64_t nbid = next_tile(bid + gridDim.x, nblocks, tiles_m, tiles_n, ntm, ntn);
+    const bool more = nbid < nblocks;
+    // after the last tile the copies re-read this tile's first k-tile (unused)
+    GemmCtx64 cn = c;
+    if (more) search_tile_setup<SPLIT>(cn, X, E, M, Nc, K, ntm, ntn);
+    floatx4 acc[8][8];
+    gemm_mainloop16_chain<F16>(c, cn, acc);
+    column_square_sums(acc, sRed, wm, wn, lane);
+    __syncthreads();
+    const int64_t col = int64_t(tn) * BN + tid;
+    if (col < Nc) partials[int64_t(tm) * Nc + col] = sRed[tid] + sRed[BN + tid];
+    if (!more) break;
+    bid = nbid;
+    tm = ntm;
+    tn = ntn;
+    c = cn;
   }
-  __syncthreads();
-  const int64_t col = n0 + tid;
-  if (col < Nc) partials[int64_t(tm) * Nc + col] = red[tid] + red[BN + tid];
 }
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void search_gemm_bf16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ E,
                              int64_t M, int64_t Nc, int64_t K, int tiles_m, int tiles_n,
-                             float* __restrict__ partials) {
-  search_gemm_16<false, false>(X, E, M, Nc, K, tiles_m, tiles_n, partials);
+                             int64_t nblocks, float* __restrict__ partials) {
+  search_gemm_16<false, false>(X, E, M, Nc, K, tiles_m, tiles_n, nblocks, partials);
 }
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void search_gemm_f16_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ E,
                             int64_t M, int64_t Nc, int64_t K, int tiles_m, int tiles_n,
-                            float* __restrict__ partials) {
-  search_gemm_16<true, false>(X, E, M, Nc, K, tiles_m, tiles_n, partials);
+                            int64_t nblocks, float* __restrict__ partials) {
+  search_gemm_16<true, false>(X, E, M, Nc, K, tiles_m, tiles_n, nblocks, partials);
 }
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void search_gemm_bf16_split_kernel(const uint16_t* __restrict__ X,
                                    const uint16_t* __restrict__ E, int64_t M, int64_t Nc,
-                                   int64_t K, int tiles_m, int tiles_n,
+                                   int64_t K, int tiles_m, int tiles_n, int64_t nblocks,
                                    float* __restrict__ partials) {
-  search_gemm_16<false, true>(X, E, M, Nc, K, tiles_m, tiles_n, partials);
+  search_gemm_16<false, true>(X, E, M, Nc, K, tiles_m, tiles_n, nblocks, partials);
 }
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void search_gemm_f16_split_kernel(const uint16_t* __restrict__ X,
                                   const uint16_t* __restrict__ E, int64_t M, int64_t Nc,
-                                  int64_t K, int tiles_m, int tiles_n,
+                                  int64_t K, int tiles_m, int tiles_n, int64_t nblocks,
                                   float* __restrict__ partials) {
-  search_gemm_16<true, true>(X, E, M, Nc, K, tiles_m, tiles_n, partials);
+  search_gemm_16<true, true>(X, E, M, Nc, K, tiles_m, tiles_n, nblocks, partials);
 }
 
 // ---------------------------------------------------------------------------
@@ -165,26 +193,32 @@ __global__ __launch_bounds__(256) void search_gemm_f32_kernel(const float* __res
 
 }  // namespace
 
+// Workgroups of the persistent search GEMM: 256, a multiple of the 8 XCDs,
+// so workgroup b runs on the XCD that block ids b + 256·i are mapped for.
+constexpr int64_t kSearchGrid = 256;
+
 hipError_t launch_search_gemm(const void* X, int dtype, const void* E, int64_t M, int64_t Nc,
                               int64_t K, int split, float* partials, hipStream_t st) {
   if (dtype == 1 || dtype == 2) {
     if (K % 128) return hipErrorInvalidValue;
     const int tiles_m = int((M + BM - 1) / BM), tiles_n = int((Nc + BN - 1) / BN);
     const int64_t blocks = gemm_blocks(tiles_m, tiles_n);
+    // one workgroup per CU of a 256-CU part, each looping over its tiles
+    const unsigned grid = unsigned(blocks < kSearchGrid ? blocks : kSearchGrid);
     const uint16_t* x = static_cast<const uint16_t*>(X);
     const uint16_t* e = static_cast<const uint16_t*>(E);
     if (dtype == 1 && split)
-      search_gemm_bf16_split_kernel<<<unsigned(blocks), NT, 0, st>>>(x, e, M, Nc, K, tiles_m,
-                                                                       tiles_n, partials);
+      search_gemm_bf16_split_kernel<<<grid, NT, 0, st>>>(x, e, M, Nc, K, tiles_m, tiles_n, blocks,
+                                                         partials);
     else if (dtype == 1)
-      search_gemm_bf16_kernel<<<unsigned(blocks), NT, 0, st>>>(x, e, M, Nc, K, tiles_m, tiles_n,
-                                                                 partials);
+      search_gemm_bf16_kernel<<<grid, NT, 0, st>>>(x, e, M, Nc, K, tiles_m, tiles_n, blocks,
+                                                   partials);
     else if (split)
-      search_gemm_f16_split_kernel<<<unsigned(blocks), NT, 0, st>>>(x, e, M, Nc, K, tiles_m,
-                                                                      tiles_n, partials);
+      search_gemm_f16_split_kernel<<<grid, NT, 0, st>>>(x, e, M, Nc, K, tiles_m, tiles_n, blocks,
+                                                        partials);
     else
-      search_gemm_f16_kernel<<<unsigned(blocks), NT, 0, st>>>(x, e, M, Nc, K, tiles_m, tiles_n,
-                                                                partials);
+      search_gemm_f16_kernel<<<grid, NT, 0, st>>>(x, e, M, Nc, K, tiles_m, tiles_n, blocks,
+                                                  partials);
   } else {
     const int64_t tiles_m = (M + FB - 1) / FB, tiles_n = (Nc + FB - 1) / FB;
     search_gemm_f32_kernel<<<unsigned(tiles_m * tiles_n), 256, 0, st>>>(

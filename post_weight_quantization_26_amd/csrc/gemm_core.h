@@ -249,10 +249,14 @@ __device__ __forceinline__ void dma64_a(const GemmCtx64& c, int kt) {
 // One k-tile: the previous k-step's 64 MFMAs (f1) carry k-step 0's 16
 // fragment reads and the next k-tile's 16 copies, one each per four MFMAs;
 // k-step 0's MFMAs (f0) carry k-step 1's reads, one per four MFMAs.
-template <int S, bool PREV, class V>
+// NEXT: the copies fetch k-tile 0 of another tile (context cn) instead of
+// k-tile kt + 1 of this one.
+template <int S, bool PREV, bool NEXT = false, class V>
 __device__ __forceinline__ void region16(const GemmCtx64& c, const int (&rdA)[2], const int (&rdB)[2],
                                          int kt, floatx4 (&acc)[8][8], V (&f0a)[8], V (&f0b)[8],
-                                         V (&f1a)[8], V (&f1b)[8]) {
+                                         V (&f1a)[8], V (&f1b)[8], const GemmCtx64* cn = nullptr) {
+  const GemmCtx64& cc = NEXT ? *cn : c;
+  const int ktc = NEXT ? 0 : kt + 1;
   if (PREV) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
@@ -261,12 +265,12 @@ __device__ __forceinline__ void region16(const GemmCtx64& c, const int (&rdA)[2]
       frag16<S>(rdA[0], rdB[0], q, f0a, f0b);
       mfma16(acc[i][j0 + 1], f1a[i], f1b[j0 + 1]);
       mfma16(acc[i][j0 + 2], f1a[i], f1b[j0 + 2]);
-      copy64<S ^ 1>(c, kt + 1, q);
+      copy64<S ^ 1>(cc, ktc, q);
       mfma16(acc[i][j0 + 3], f1a[i], f1b[j0 + 3]);
     }
   } else {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) copy64<S ^ 1>(c, kt + 1, q);
+    for (int q = 0; q < 16; ++q) copy64<S ^ 1>(cc, ktc, q);
 #pragma unroll
     for (int q = 0; q < 16; ++q) frag16<S>(rdA[0], rdB[0], q, f0a, f0b);
   }
@@ -319,6 +323,53 @@ __device__ __forceinline__ void gemm_mainloop16(const GemmCtx64& c, floatx4 (&ac
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
+
+// The k-loop of one tile in a chain of tiles: k-tile 0 is already in stage
+// 0 (copied by the previous tile's last region, or by the caller before the
+// first tile), KT is even and at least 2, and the last region copies k-tile
+// 0 of the next tile (context cn) into stage 0. Same accumulator contract
+// as gemm_mainloop16.
+template <bool F16>
+__device__ __forceinline__ void gemm_mainloop16_chain(const GemmCtx64& c, const GemmCtx64& cn,
+                                                      floatx4 (&acc)[8][8]) {
+  typedef typename Operand<F16>::type V;
+  int rdA[2], rdB[2];
+  frag_offsets16(c, rdA, rdB);
+  V f0a[8], f0b[8], f1a[8], f1b[8];
+  region16<0, false>(c, rdA, rdB, 0, acc, f0a, f0b, f1a, f1b);
+  int kt = 1;
+  for (; kt + 2 < c.KT; kt += 2) {
+    region16<1, true>(c, rdA, rdB, kt, acc, f0a, f0b, f1a, f1b);
+    region16<0, true>(c, rdA, rdB, kt + 1, acc, f0a, f0b, f1a, f1b);
+  }
+  region16<1, true, true>(c, rdA, rdB, kt, acc, f0a, f0b, f1a, f1b, &cn);
+  mfma_8x8(acc, f1a, f1b);
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
+
+// Epilogue of the search GEMMs: each lane's 4 accumulators of block (i, j)
+// lie in output column j·16 + lane % 16 of the wave's 128 columns, and lanes
+// l, l^16, l^32, l^48 share that column. The squares are summed over the
+// wave's 128 rows (one FMA each, rows in block order) and the result goes to
+// red[wm·BN + wn·128 + column].
+__device__ __forceinline__ void column_square_sums(const floatx4 (&acc)[8][8], float* red, int wm,
+                                                   int wn, int lane) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s = __builtin_fmaf(acc[i][j][v], acc[i][j][v], s);
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    if (lane < 16) red[wm * BN + wn * 128 + j * 16 + lane] = s;
+  }
 }
 
 // Number of workgroups the tile_of mapping needs for a tiles_m x tiles_n grid.
