@@ -185,6 +185,14 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
 // 3. candidates: partials[tm][n] = Σ_{j in row tile tm} Z[j][n] · E[n][j]
 // ---------------------------------------------------------------------------
 
+// The epilogue's block of E, E[n0 .. n0 + 255][m0 .. m0 + 255], in four
+// 64-column quarters, each laid out like a B k-tile (swz64 rows of 128 bytes)
+// in one of the k-tile ring's four arrays; and its column sums.
+__device__ __forceinline__ uint4* e_quarter(int q) {
+  return q == 0 ? s64A0 : q == 1 ? s64A1 : q == 2 ? s64B0 : s64B1;
+}
+__shared__ float sRedG[2 * BN];
+
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gram_search_kernel(const uint16_t* __restrict__ Gs, int64_t ldg, const uint16_t* __restrict__ E,
                         int64_t K, int64_t Nc, int tiles_m, int tiles_n,
@@ -203,7 +211,6 @@ void gram_search_kernel(const uint16_t* __restrict__ Gs, int64_t ldg, const uint
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t n0 = int64_t(tn) * BN;
   const int64_t rows_b = Nc - n0 < BN ? Nc - n0 : BN;
-  float* red = reinterpret_cast<float*>(s64A0);  // [2][BN]
 #pragma nounroll
   for (int h = 0; h < n_half; ++h) {
     const int tm = h ? tiles_m - 1 - p : p;
@@ -219,39 +226,62 @@ void gram_search_kernel(const uint16_t* __restrict__ Gs, int64_t ldg, const uint
     floatx4 acc[8][8];
     gemm_mainloop16<false>(c, acc);
 
-    // Epilogue: lane l of block (i, j) holds column n = ... + l % 16 and
-    // the 4 consecutive rows 4·(l/16) + v of the wave's 16-row block i,
-    // which take one 8-byte load of E[n][rows].
-    __builtin_amdgcn_s_waitcnt(0);
+    // Epilogue. The k-loop's reads and copies are complete (its last region
+    // waited for them before its barrier), so the ring is free: copy the E
+    // block into it, through a resource that ends at the tile's last valid
+    // element (rows_a is 128 or 256, so whole quarters are valid or not).
+    const __amdgpu_buffer_rsrc_t rsE = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(E + n0 * K + m0), 0, int(((rows_b - 1) * K + rows_a) * 2),
+        0x00020000);
+    const int nq = int(rows_a >> 6);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q < nq) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsE, AWQ_LDS(e_quarter(q) + (c.wave * 8 + j) * 64),
+                                                   16, c.vbaseB[j & 1] + 128 * q, j * c.stepB, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
     __syncthreads();
-    const int wm = c.wave >> 1, wn = c.wave & 1;
-    const int64_t row0 = m0 + wm * 128 + 4 * (lane >> 4);
+    // lane l of block (i, j) holds column n = wn·128 + 16·j + l % 16 of the
+    // tile and the 4 consecutive rows 4·(l/16) + v of the wave's 16-row block
+    // i, whose E values are one 8-byte LDS read: quarter 2·wm + i/4, chunk
+    // 2·(i % 4) + (l/16)/2 of row n, half (l/16) % 2 of it. Rows past K
+    // (rows_a = 128) are skipped; columns past Nc read zeros.
+    const int wm = __builtin_amdgcn_readfirstlane(c.wave >> 1), wn = c.wave & 1;
+    const int lq = lane >> 4;
+    // rows_a is 128 or 256: with 128 the upper wave row lies past K. Its
+    // quarters were not copied, so its sums are dropped, not its reads.
+    const bool rows_ok = wm == 0 || rows_a == BM;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int64_t n = n0 + wn * 128 + j * 16 + (lane & 15);
+      const int nl = wn * 128 + j * 16 + (lane & 15);
       float s = 0.f;
-      if (n < Nc) {
-        const uint16_t* en = E + n * K;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int64_t r = row0 + i * 16;      // 4 consecutive rows r..r+3
-          if (r < K) {
-            const uint2 ev = *reinterpret_cast<const uint2*>(en + r);
-            s += acc[i][j][0] * __uint_as_float(ev.x << 16);
-            s += acc[i][j][1] * __uint_as_float(ev.x & 0xFFFF0000u);
-            s += acc[i][j][2] * __uint_as_float(ev.y << 16);
-            s += acc[i][j][3] * __uint_as_float(ev.y & 0xFFFF0000u);
-          }
-        }
+      for (int i = 0; i < 8; ++i) {
+        const uint4* qa = e_quarter(2 * wm + (i >> 2));
+        const uint2 ev = *reinterpret_cast<const uint2*>(
+            reinterpret_cast<const char*>(qa + swz64(nl, 2 * (i & 3) + (lq >> 1))) + 8 * (lq & 1));
+        s = __builtin_fmaf(acc[i][j][0], __uint_as_float(ev.x << 16), s);
+        s = __builtin_fmaf(acc[i][j][1], __uint_as_float(ev.x & 0xFFFF0000u), s);
+        s = __builtin_fmaf(acc[i][j][2], __uint_as_float(ev.y << 16), s);
+        s = __builtin_fmaf(acc[i][j][3], __uint_as_float(ev.y & 0xFFFF0000u), s);
       }
+      s = rows_ok ? s : 0.f;
       s += __shfl_xor(s, 16);
       s += __shfl_xor(s, 32);
-      if (lane < 16) red[wm * BN + wn * 128 + j * 16 + lane] = s;
+      if (lane < 16) sRedG[wm * BN + wn * 128 + j * 16 + lane] = s;
+      // one column block at a time: keeps the LDS reads from being hoisted
+      // past the VGPR budget
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // every wave's E reads come before its column sums, so past this
+    // barrier the next k-loop may refill the ring
     __syncthreads();
     const int64_t col = n0 + tid;
-    if (col < Nc) partials[int64_t(tm) * Nc + col] = red[tid] + red[BN + tid];
-    __syncthreads();  // red lives in LDS stage 0, which the next k-loop refills
+    if (col < Nc) partials[int64_t(tm) * Nc + col] = sRedG[tid] + sRedG[BN + tid];
   }
 }
 
