@@ -85,9 +85,10 @@ struct SearchLayout {
 // K = 4096).
 constexpr int64_t kXtPad = 64, kGsPad = 256;
 
-// Token slices of the Gram build: the power of two S <= 16 dividing Tp / 128
-// that finishes the U·S (upper tile, slice) units of work in the fewest
-// rounds of 256 CUs relative to the slice length (ties to the smaller S).
+// Token slices of the Gram build: the S <= 16 (slices of at least two
+// 64-token k-tiles, lengths differing by at most one k-tile) that finishes
+// the U·S (upper tile, slice) units of work in the fewest rounds of 256 CUs
+// relative to the slice length (ties to the smaller S).
 int32_t gram_slices(int64_t T, int64_t K);
 
 // Gram searches: those that build G in their own workspace, and those that

@@ -12,8 +12,11 @@
 //  2. gram_partial_kernel: G is symmetric, so only its 256x256 tiles on and
 //     above the diagonal are formed, on the shared MFMA main loop
 //     (gemm_core.h). To keep every CU busy the token range is split into S
-//     slices (S chosen on the host to balance whole rounds of work); each
-//     (tile, slice) unit stores its float32 partial tile.
+//     slices of whole 64-token k-tiles, slice s taking k-tiles
+//     [s·KT/S, (s+1)·KT/S) (S chosen on the host to balance whole rounds of
+//     work: at 64K tokens and K = 4096, 15 slices of 68 or 69 k-tiles make
+//     2040 units, 8 rounds of 256 CUs); each (tile, slice) unit stores its
+//     float32 partial tile.
 //     gram_reduce_kernel adds a tile's S partials in a fixed order and stores
 //     it as two bf16 halves, hi = bf16(G) and lo = bf16(G - hi) (hi + lo
 //     carries G to about 2^-16 relative, so the bf16 MFMA that follows does
@@ -102,15 +105,16 @@ __device__ __forceinline__ void upper_tile(int u, int nt, int& tm, int& tn) {
 // together, so concurrent blocks share that slice's panels of Xt).
 // P[(s·U + u)][256·256]: float32 partial tile, row-major.
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gram_partial_kernel(const uint16_t* __restrict__ Xt, int64_t K, int64_t ldx, int64_t Ts,
-                         int nt, int U, float* __restrict__ P) {
+void gram_partial_kernel(const uint16_t* __restrict__ Xt, int64_t K, int64_t ldx, int64_t KT,
+                         int S, int nt, int U, float* __restrict__ P) {
   const int s = blockIdx.x / U, u = blockIdx.x % U;
   int tm, tn;
   upper_tile(u, nt, tm, tn);
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
   const int64_t rows_a = K - m0 < BM ? K - m0 : BM;
   const int64_t rows_b = K - n0 < BN ? K - n0 : BN;
-  const int64_t t0 = int64_t(s) * Ts;
+  const int64_t k0 = int64_t(s) * KT / S, k1 = int64_t(s + 1) * KT / S;
+  const int64_t t0 = k0 * BK64, Ts = (k1 - k0) * BK64;
   GemmCtx64 c;
   gemm_setup64(c, Xt + m0 * ldx + t0, rows_a, ldx, Xt + n0 * ldx + t0, rows_b, ldx, Ts, false);
   floatx4 acc[8][8];
@@ -287,11 +291,11 @@ void gram_search_kernel(const uint16_t* __restrict__ Gs, int64_t ldg, const uint
 
 }  // namespace
 
-// S token slices of Tp / S tokens each (Tp / S a multiple of 128); P holds
+// S token slices of whole 64-token k-tiles (at least one each); P holds
 // S x (upper tiles) float32 partial tiles of 256 x 256.
 hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, int64_t ldx, int S,
                              uint16_t* Xt, float* P, int64_t ldg, uint16_t* Gs, hipStream_t st) {
-  if (K % 128 || Tp % 128 || Tp < T || S < 1 || Tp % (int64_t(S) * 128) || ldx < Tp ||
+  if (K % 128 || Tp % 128 || Tp < T || S < 1 || int64_t(S) * 64 > Tp || ldx < Tp ||
       ldx % 8 || ldg < 2 * K || ldg % 8)
     return hipErrorInvalidValue;
   dim3 tgrid(unsigned((Tp + 63) / 64), unsigned(K / 64));
@@ -300,7 +304,7 @@ hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, in
   if (e != hipSuccess) return e;
   const int nt = int((K + BM - 1) / BM);
   const int U = nt * (nt + 1) / 2;
-  gram_partial_kernel<<<unsigned(int64_t(U) * S), NT, 0, st>>>(Xt, K, ldx, Tp / S, nt, U, P);
+  gram_partial_kernel<<<unsigned(int64_t(U) * S), NT, 0, st>>>(Xt, K, ldx, Tp / BK64, S, nt, U, P);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   gram_reduce_kernel<<<dim3(unsigned(U), 16), 256, 0, st>>>(P, S, U, nt, K, ldg, Gs);

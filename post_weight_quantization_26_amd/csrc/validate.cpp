@@ -44,10 +44,10 @@ int32_t gram_slices(int64_t T, int64_t K) {
   const int64_t Tp = ceil_div(T, kTileK) * kTileK;
   const int64_t nt = ceil_div(K, kGemmBM_bf16);
   const int64_t U = nt * (nt + 1) / 2;
+  const int64_t ktiles = Tp / 64;
   int32_t best = 1;
   double best_cost = double(ceil_div(U, 256));
-  for (int32_t S = 2; S <= 16; S *= 2) {
-    if (Tp % (int64_t(S) * kTileK)) break;
+  for (int32_t S = 2; S <= 16 && 2 * S <= ktiles; ++S) {
     const double cost = double(ceil_div(U * S, 256)) / S;
     if (cost < best_cost) {
       best_cost = cost;

@@ -429,7 +429,7 @@ def test_prepared_gram_sizes_and_rejects(L):
     assert lib.awq_gram_bytes(200) == 0 and lib.awq_gram_bytes(0) == 0
     build = ws(L.AWQ_OP_GRAM_BUILD, T, 1, K, 1, L.AWQ_BF16)
     xt = K * (T + 64) * 2
-    gp = 16 * 136 * 256 * 256 * 4
+    gp = 15 * 136 * 256 * 256 * 4                     # 15 token slices x 136 upper tiles
     assert build == xt + gp
     assert ws(L.AWQ_OP_GRAM_BUILD, T, 1, K, 1, L.AWQ_F32) == 0
     for with_g, op in ((L.AWQ_OP_SEARCH_SCALE_GRAM_G, L.AWQ_OP_SEARCH_SCALE_GRAM),
@@ -478,9 +478,10 @@ def test_gram_workspace_and_rejects(L):
     direct = ws(L.AWQ_OP_SEARCH_SCALE, 65536, 4096, 4096, 20, L.AWQ_BF16)
     gram = ws(L.AWQ_OP_SEARCH_SCALE_GRAM, 65536, 4096, 4096, 20, L.AWQ_BF16)
     xt, gs = 4096 * 65536 * 2, 4096 * 8192 * 2
-    # the build's float32 partial tiles: 16 token slices (the fewest rounds of
-    # 256 CUs per slice length for 136 upper tiles) of 136 tiles of 256x256
-    gp = 16 * 136 * 256 * 256 * 4
+    # the build's float32 partial tiles: 15 token slices (136 upper tiles x 15
+    # slices = 2040 units, 8 rounds of 256 CUs: the fewest rounds per slice
+    # length for S <= 16) of 136 tiles of 256x256
+    gp = 15 * 136 * 256 * 256 * 4
     # partials shrink to K/256 row tiles; X^T, the G build's partial tiles and
     # the G halves are added
     assert gram > direct - 256 * 20 * 4096 * 4 + xt + gp + gs - (1 << 20)
