@@ -102,6 +102,25 @@ def copy(mib: int, reps: int = 1) -> None:
                       "GBps_read_plus_write": round(moved / (us * 1e-6) / 1e9, 1)}), flush=True)
 
 
+def fill(mib: int, reps: int) -> None:
+    """Write-only rate: torch's fill of a mib-MiB bf16 buffer, reps times."""
+    import json
+    import torch
+    x = torch.empty(mib * (1 << 20) // 2, dtype=torch.bfloat16, device="cuda:0")
+    for _ in range(3):
+        x.fill_(1.0)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        x.fill_(1.0)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    print(json.dumps({"fill_mib": mib, "reps": reps, "us_per_fill": round(us, 2),
+                      "GBps_written": round(mib * (1 << 20) / (us * 1e-6) / 1e9, 1)}), flush=True)
+
+
 def fold(reps: int) -> None:
     import os
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -384,8 +403,8 @@ def fused(reps: int) -> None:
 
 def main(argv=None) -> int:
     p = argparse.ArgumentParser()
-    p.add_argument("what", choices=["copy", "fold", "w4a16", "pack", "traffic", "counters",
-                                    "library_gemm", "fused"])
+    p.add_argument("what", choices=["copy", "fill", "fold", "w4a16", "pack", "traffic",
+                                    "counters", "library_gemm", "fused"])
     p.add_argument("--pmc")
     p.add_argument("--mib", type=int, default=1024)
     p.add_argument("--reps", type=int, default=20)
@@ -403,6 +422,8 @@ def main(argv=None) -> int:
         fused(a.reps if a.reps != 20 else 3)
     elif a.what == "copy":
         copy(a.mib, a.reps if a.reps != 20 else 1)
+    elif a.what == "fill":
+        fill(a.mib, a.reps)
     elif a.what == "fold":
         fold(a.reps)
     elif a.what == "pack":
