@@ -101,15 +101,44 @@ __device__ __forceinline__ void upper_tile(int u, int nt, int& tm, int& tn) {
   tn = r + (u - first);
 }
 
-// Block b: slice s = b / U, upper tile u = b % U (units of one token slice run
-// together, so concurrent blocks share that slice's panels of Xt).
-// P[(s·U + u)][256·256]: float32 partial tile, row-major.
+// Upper tile q in row-pair order -> (tm, tn): pair p is row p (tiles p ..
+// nt - 1) then row nt - 1 - p (its nt - p .. nt - 1 tiles follow), nt + 1
+// tiles a pair; a pair needs only the panels from row p up.
+__device__ __forceinline__ void pair_tile(int q, int nt, int& tm, int& tn) {
+  const int p = q / (nt + 1), r = q - p * (nt + 1);
+  if (r < nt - p) {
+    tm = p;
+    tn = p + r;
+  } else {
+    tm = nt - 1 - p;
+    tn = tm + (r - (nt - p));
+  }
+}
+
+// Units v = s·U + q (slice s, upper tile q). With compact (from 1024 units
+// on), runs of 32 consecutive units go to one XCD (consecutive block ids go
+// round-robin over the 8 XCDs: block b runs on XCD b % 8, the i-th there
+// for i = b / 8) and tiles follow the row-pair order, so an XCD's 32
+// concurrent tiles draw on ~15 panels of one slice instead of 32 panel-slices
+// of two (at K = 4096); otherwise block v is unit v in row-major tile order.
+// P[(s·U + u)][256·256]: float32 partial tile of row-major upper tile u.
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gram_partial_kernel(const uint16_t* __restrict__ Xt, int64_t K, int64_t ldx, int64_t KT,
-                         int S, int nt, int U, float* __restrict__ P) {
-  const int s = blockIdx.x / U, u = blockIdx.x % U;
-  int tm, tn;
-  upper_tile(u, nt, tm, tn);
+                         int S, int nt, int U, int compact, float* __restrict__ P) {
+  int64_t v = blockIdx.x;
+  if (compact) {
+    const int b = int(blockIdx.x), x = b & 7, i = b >> 3;
+    v = int64_t(i >> 5) * 256 + 32 * x + (i & 31);
+    if (v >= int64_t(U) * S) return;
+  }
+  const int s = int(v / U), q = int(v % U);
+  int tm, tn, u = q;
+  if (compact) {
+    pair_tile(q, nt, tm, tn);
+    u = tm * nt - tm * (tm - 1) / 2 + (tn - tm);   // its row-major index
+  } else {
+    upper_tile(q, nt, tm, tn);
+  }
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
   const int64_t rows_a = K - m0 < BM ? K - m0 : BM;
   const int64_t rows_b = K - n0 < BN ? K - n0 : BN;
@@ -304,7 +333,11 @@ hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, in
   if (e != hipSuccess) return e;
   const int nt = int((K + BM - 1) / BM);
   const int U = nt * (nt + 1) / 2;
-  gram_partial_kernel<<<unsigned(int64_t(U) * S), NT, 0, st>>>(Xt, K, ldx, Tp / BK64, S, nt, U, P);
+  const int64_t units = int64_t(U) * S;
+  const int compact = units >= 1024;
+  const int64_t pblocks = compact ? (units + 255) / 256 * 256 : units;
+  gram_partial_kernel<<<unsigned(pblocks), NT, 0, st>>>(Xt, K, ldx, Tp / BK64, S, nt, U, compact,
+                                                        P);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   gram_reduce_kernel<<<dim3(unsigned(U), 16), 256, 0, st>>>(P, S, U, nt, K, ldg, Gs);
