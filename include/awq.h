@@ -244,13 +244,13 @@ awq_status awq_quantize_pack(const void* W, awq_dtype w_dtype, int64_t N, int64_
  * candidates' error weights are
  * the same bf16 operands as on the direct path; only the float32 rounding
  * order of the sums differs. Arguments, outputs and synchronisation as in
- * awq_search_scale / awq_search_clip; bf16 inputs only; T below about 2^22
- * (512·(T rounded up to 128, + 64) < 2^31) and K below about 2^21
- * (512·(2K + 256) < 2^31), else AWQ_E_UNSUPPORTED. The
- * workspace (awq_workspace_bytes with AWQ_OP_SEARCH_SCALE_GRAM /
- * AWQ_OP_SEARCH_CLIP_GRAM) also holds Xᵀ (K rows of T tokens padded to 128,
- * plus 64), the build's float32 partial tiles, and G's upper tiles as bf16
- * hi/lo halves (K x (2K + 256) elements). */
+ * awq_search_scale / awq_search_clip; bf16 inputs only; K below about 2^21
+ * (512·(2K + 256) < 2^31), else AWQ_E_UNSUPPORTED. The build reads X as it
+ * is (no transposed copy). The workspace (awq_workspace_bytes with
+ * AWQ_OP_SEARCH_SCALE_GRAM / AWQ_OP_SEARCH_CLIP_GRAM) also holds the
+ * build's float32 partial tiles (up to 16 token slices of G's upper 256x256
+ * tiles) and G's upper tiles as bf16 hi/lo halves (K x (2K + 256)
+ * elements). */
 awq_status awq_search_scale_gram(const void* X, const void* W, awq_dtype dtype, int64_t T,
                                  int64_t N, int64_t K, const float* abar, const float* alphas,
                                  int32_t n_alpha, awq_qconfig qc, float* s_best,
@@ -320,7 +320,7 @@ awq_status awq_w3a16_matmul(const void* X, awq_dtype dtype, int64_t T, int64_t N
  * awq_search_clip_gram and awq_search_scale_group_gram, bit for bit; T is
  * the token count G was built from. Their workspaces
  * (AWQ_OP_SEARCH_SCALE_GRAM_G, AWQ_OP_SEARCH_CLIP_GRAM_G; N = Σ_l N[l] for
- * a group) hold no Xᵀ and no G. Errors as for the searches they replace;
+ * a group) hold no partial tiles and no G. Errors as for the searches they replace;
  * AWQ_E_WORKSPACE also when G_bytes < awq_gram_bytes(K). */
 size_t awq_gram_bytes(int64_t K);
 awq_status awq_gram_build(const void* X, awq_dtype dtype, int64_t T, int64_t K, void* G,

@@ -67,8 +67,8 @@ hipError_t launch_stats_accumulate(const void* X, int dtype, int64_t T, int64_t 
                                    int64_t chunks, double* partial, double* sums, hipStream_t st);
 hipError_t launch_stats_divide(const double* sums, int64_t count, int64_t K, float* abar,
                                hipStream_t st);
-hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, int64_t ldx, int S,
-                             uint16_t* Xt, float* P, int64_t ldg, uint16_t* Gs, hipStream_t st);
+hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, int S, float* P,
+                             int64_t ldg, uint16_t* Gs, hipStream_t st);
 hipError_t launch_gram_search(const uint16_t* Gs, int64_t ldg, const void* E, int64_t K, int64_t Nc,
                               float* partials, hipStream_t st);
 hipError_t launch_fold_vec(void* v, int dtype, int64_t K, const float* s, hipStream_t st);
@@ -306,12 +306,11 @@ extern "C" awq_status awq_gram_build(const void* X, awq_dtype dtype, int64_t T, 
   if (s != AWQ_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const GramBuildLayout B = gram_build_layout(T, K);
-  uint16_t* Xt = at<uint16_t>(ws, B.xt);
   float* P = at<float>(ws, B.gp);
   AWQ_HIP(timed(AWQ_K_GRAM_BUILD, st,
                 [&] {
-                  return launch_gram_build(X, T, K, B.Tp, B.ldx, B.S, Xt, P, B.ldg,
-                                           static_cast<uint16_t*>(G), st);
+                  return launch_gram_build(X, T, K, B.Tp, B.S, P, B.ldg, static_cast<uint16_t*>(G),
+                                           st);
                 }),
           "gram_build");
   return AWQ_OK;
@@ -322,11 +321,10 @@ namespace {
 // Builds G = XᵀX (upper tiles, hi/lo) into the workspace of a Gram search.
 awq_status build_gram(const void* X, int64_t T, int64_t K, const SearchLayout& L, void* ws,
                       hipStream_t st) {
-  uint16_t* Xt = at<uint16_t>(ws, L.xt);
   float* P = at<float>(ws, L.gp);
   uint16_t* Gs = at<uint16_t>(ws, L.gs);
   AWQ_HIP(timed(AWQ_K_GRAM_BUILD, st,
-                [&] { return launch_gram_build(X, T, K, L.Tp, L.ldx, L.S, Xt, P, L.ldg, Gs, st); }),
+                [&] { return launch_gram_build(X, T, K, L.Tp, L.S, P, L.ldg, Gs, st); }),
           "gram_build");
   return AWQ_OK;
 }

@@ -66,24 +66,20 @@ struct SearchLayout {
   size_t mse;       // [n_grid] f64
   size_t best;      // [N] f64 best per-row sums (clip search)
   size_t scalar;    // [8] f64
-  size_t xt;        // Gram searches: [K, Tp] bf16 transposed, token-padded X
   size_t gp;        // Gram searches: [S, U, 256, 256] f32 partial tiles of G
   size_t gs;        // Gram searches: [K, 2K + 256] bf16, G's upper tiles as hi/lo halves
   size_t total;
   int64_t MT;       // row tiles of the partials (token tiles; Gram: channel tiles)
   int64_t Tp;       // Gram searches: tokens padded to a multiple of 128
-  int64_t ldx;      // Gram searches: row stride of Xt in elements (>= Tp)
   int64_t ldg;      // Gram searches: row stride of Gs in elements (>= 2K)
   int32_t S;        // Gram searches: token slices of the G build
 };
 
-// Row padding of Xt and Gs (elements). Unpadded, their row strides are
-// powers of two at typical sizes (Xt: 128 KiB at 64K tokens; Gs: 32 KiB at
-// K = 8192), so the 256 rows of one k-tile fall on few cache sets and memory
-// channels. Measured: 64 more elements per Xt row cut the G build by ~14% at
-// 64K tokens; 256 more per Gs row cut the K = 8192 search by ~8% (neutral at
-// K = 4096).
-constexpr int64_t kXtPad = 64, kGsPad = 256;
+// Row padding of Gs (elements). Unpadded, its row stride is a power of two
+// at typical sizes (32 KiB at K = 8192), so the 256 rows of one k-tile fall
+// on few cache sets and memory channels. Measured: 256 more elements per row
+// cut the K = 8192 search by ~8% (neutral at K = 4096).
+constexpr int64_t kGsPad = 256;
 
 // Token slices of the Gram build: the S <= 16 (slices of at least two
 // 64-token k-tiles, lengths differing by at most one k-tile) that finishes
@@ -136,12 +132,12 @@ inline int layout_op(int op, awq_qconfig qc, awq_dtype d) {
   if (op == AWQ_OP_SEARCH_CLIP) return AWQ_OP_SEARCH_CLIP_SPLIT_E;
   return op;
 }
-// Xt and the partial tiles of a G build (the first part of a building Gram
-// search's workspace, and the whole workspace of awq_gram_build).
+// The partial tiles of a G build (the first part of a building Gram search's
+// workspace, and the whole workspace of awq_gram_build).
 struct GramBuildLayout {
-  int64_t Tp, ldx, ldg;
+  int64_t Tp, ldg;
   int32_t S;
-  size_t xt, gp, total;
+  size_t gp, total;
 };
 GramBuildLayout gram_build_layout(int64_t T, int64_t K);
 size_t gram_g_bytes(int64_t K);

@@ -7,16 +7,16 @@
 // G costs 2·T·K² once per layer; each candidate row then costs 2·K² instead
 // of 2·T·K, T/K times less (16x at 64K tokens and K = 4096).
 //
-//  1. transpose_pad_kernel: Xt [K, Tp] = Xᵀ with the token dim padded to a
-//     multiple of 128 with zeros (zero rows do not change G).
-//  2. gram_partial_kernel: G is symmetric, so only its 256x256 tiles on and
-//     above the diagonal are formed, on the shared MFMA main loop
-//     (gemm_core.h). To keep every CU busy the token range is split into S
-//     slices of whole 64-token k-tiles, slice s taking k-tiles
-//     [s·KT/S, (s+1)·KT/S) (S chosen on the host to balance whole rounds of
-//     work: at 64K tokens and K = 4096, 15 slices of 68 or 69 k-tiles make
-//     2040 units, 8 rounds of 256 CUs); each (tile, slice) unit stores its
-//     float32 partial tile.
+//  1. gram_partial_kernel: G is symmetric, so only its 256x256 tiles on and
+//     above the diagonal are formed, on the MFMA schedule of gemm_core.h
+//     with its operands read from X itself: k-tiles of 64 tokens x 256
+//     channels go to LDS as they are, and transposing LDS reads
+//     (ds_read_b64_tr_b16) hand each lane its channel's 8 consecutive tokens.
+//     To keep every CU busy the token range is split into S slices of whole
+//     64-token k-tiles, slice s taking k-tiles [s·KT/S, (s+1)·KT/S) (S chosen
+//     on the host to balance whole rounds of work: at 64K tokens and
+//     K = 4096, 15 slices of 68 or 69 k-tiles make 2040 units, 8 rounds of
+//     256 CUs); each (tile, slice) unit stores its float32 partial tile.
 //     gram_reduce_kernel adds a tile's S partials in a fixed order and stores
 //     it as two bf16 halves, hi = bf16(G) and lo = bf16(G - hi) (hi + lo
 //     carries G to about 2^-16 relative, so the bf16 MFMA that follows does
@@ -27,7 +27,7 @@
 //     128-wide block c of columns, hi then lo of that block:
 //       Gs[j][256·c + w] = hi(G'[j][128·c + w]), Gs[j][256·c + 128 + w] = lo(...)
 //     so row tile tm's part from its diagonal tile on is one contiguous run.
-//  3. gram_search_kernel: for a batch of candidate error rows E [Nc, K]
+//  2. gram_search_kernel: for a batch of candidate error rows E [Nc, K]
 //     (bf16, the same operands the direct search GEMM uses), row tile tm
 //     runs one k-loop over Gs columns [512·tm, 2K) with each 128-wide block
 //     of E (from column 256·tm) read twice, once against hi and once
@@ -43,47 +43,7 @@ namespace awq {
 namespace {
 
 // ---------------------------------------------------------------------------
-// 1. Xt = Xᵀ, token dim padded with zeros
-// ---------------------------------------------------------------------------
-
-// Workgroup = 64 tokens x 64 channels through LDS; 16-byte loads and stores.
-__global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ X,
-                                                            int64_t T, int64_t K, int64_t Tp,
-                                                            int64_t ldx,
-                                                            uint16_t* __restrict__ Xt) {
-  __shared__ uint16_t tile[64][72];
-  const int64_t t0 = int64_t(blockIdx.x) * 64, k0 = int64_t(blockIdx.y) * 64;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = tid + 256 * u;         // 512 chunks of 8 channels
-    const int r = e >> 3, c8 = (e & 7) * 8;
-    const int64_t t = t0 + r;
-    uint4 q = make_uint4(0, 0, 0, 0);
-    if (t < T) q = *reinterpret_cast<const uint4*>(X + t * K + k0 + c8);
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tile[r][c8 + 2 * i] = uint16_t(w[i] & 0xFFFFu);
-      tile[r][c8 + 2 * i + 1] = uint16_t(w[i] >> 16);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = tid + 256 * u;         // 512 chunks of 8 tokens
-    const int kr = e >> 3, t8 = (e & 7) * 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = uint32_t(tile[t8 + 2 * i][kr]) | (uint32_t(tile[t8 + 2 * i + 1][kr]) << 16);
-    if (t0 + t8 < Tp)
-      *reinterpret_cast<uint4*>(Xt + (k0 + kr) * ldx + t0 + t8) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 2. G = Xt·Xtᵀ: upper tiles x token slices, then the slice sum as hi/lo halves
+// 2. G = XᵀX: upper tiles x token slices, then the slice sum as hi/lo halves
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ uint16_t bf16_bits(float f) {
@@ -115,6 +75,157 @@ __device__ __forceinline__ void pair_tile(int q, int nt, int& tm, int& tn) {
   }
 }
 
+// An operand k-tile is 64 tokens x 256 channels of X, 64 rows of 512 bytes
+// (32 chunks of 16 bytes) in one ring array, chunk c of token row r at c ^
+// hx(r). One ds_read_b64_tr_b16 returns lane l (of each 16-lane group) the
+// l-th of the 16 elements that the group's quad e (lanes 4e .. 4e+3, 8 bytes
+// each) points at, for e = 0..3: four token rows of one channel. An MFMA
+// operand (8 tokens of one channel per lane) is two such reads. The 16 rows
+// one read touches (4 per group, the groups 8 rows apart) differ in bits 0,
+// 1, 3 and 4, so hx takes those bits: their 32-byte runs land on 16
+// distinct chunk pairs.
+__device__ __forceinline__ int hx(int r) { return 2 * ((r & 3) | ((r >> 1) & 12)); }
+constexpr int kXOob = 0x40000000;   // a byte offset past any k-tile's records
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // one MFMA operand
+
+struct XCtx {
+  const uint16_t* a;   // X + t0·K + m0: row-side channels
+  const uint16_t* b;   // X + t0·K + n0: column-side channels
+  int64_t K;           // X's row length (elements)
+  int tokens;          // tokens from t0 to the end of X
+  int ca, cb;          // valid channels from m0 and from n0 (128 or 256)
+  int KT;              // k-tiles of the slice
+  int wave;
+  int vbA[2], vbB[2];  // copy j's per-lane byte offset within its k-tile, by j & 1
+  int rdA[8], rdB[8];  // fragment block i's per-lane LDS byte offset (k-step 0, rows 0-3)
+};
+
+// Buffer resource over k-tile kt of one operand: 64 token rows from
+// base + 64·kt·K, ending at the last valid channel of the last valid token
+// (nothing past it, and nothing at all past X's last token).
+// (Every input is the same on all lanes; readfirstlane says so to the
+// compiler, which otherwise wraps each copy in a loop over distinct values.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t xtile_rsrc(const uint16_t* base, int64_t K,
+                                                             int tokens, int chans, int kt) {
+  int rows = tokens - 64 * kt;
+  rows = rows < 0 ? 0 : rows > 64 ? 64 : rows;
+  const int rec = __builtin_amdgcn_readfirstlane(int(rows ? (int64_t(rows - 1) * K + chans) * 2 : 0));
+  const uint64_t p = reinterpret_cast<uint64_t>(base + int64_t(64) * kt * K);
+  const uint64_t pu = (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(int(p >> 32)))) << 32) |
+                      uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(p))));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<uint16_t*>(pu), 0, rec, 0x00020000);
+}
+
+__device__ __forceinline__ void xctx_setup(XCtx& c) {
+  const int lane = threadIdx.x & 63;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: LDS targets in SGPRs
+  // copy j of wave w fills token rows r0 = 8w + 32·(j / 4) + 2·(j % 4) and
+  // r0 + 1 (lane / 32), physical chunk lane % 32; hx of those rows depends
+  // on j only through j & 1
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const int r = 8 * c.wave + 2 * jj + (lane >> 5);
+    const int ch = (lane & 31) ^ hx(r);               // logical chunk: channels 8·ch ..
+    const int64_t row_bytes = int64_t(8 * c.wave + (lane >> 5)) * c.K * 2;
+    c.vbA[jj] = 8 * ch < c.ca ? int(row_bytes) + 16 * ch : kXOob;
+    c.vbB[jj] = 8 * ch < c.cb ? int(row_bytes) + 16 * ch : kXOob;
+  }
+  // fragment reads: group g = lane / 16 takes tokens 8g .. 8g+7 of a k-step,
+  // quad q = (lane / 4) % 4 the rows 8g + q (and + 4), lane j4 = lane % 4 the
+  // channels 4·j4 .. +3 of the block's 16
+  const int g = lane >> 4, q = (lane >> 2) & 3, j4 = lane & 3;
+  const int h = 2 * (q | (g << 2));
+  const int wm = c.wave >> 1, wn = c.wave & 1;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    c.rdA[i] = (8 * g + q) * 512 + (((16 * wm + 2 * i) ^ h) + (j4 >> 1)) * 16 + (j4 & 1) * 8;
+    c.rdB[i] = (8 * g + q) * 512 + (((16 * wn + 2 * i) ^ h) + (j4 >> 1)) * 16 + (j4 & 1) * 8;
+  }
+}
+
+template <int S>
+__device__ __forceinline__ void xcopy(const XCtx& c, __amdgpu_buffer_rsrc_t rsA,
+                                      __amdgpu_buffer_rsrc_t rsB, int q) {
+  // copy q of the 16 a wave issues per k-tile: A's 8, then B's 8
+  const int j = q & 7;
+  const int r0 = 8 * c.wave + 32 * (j >> 2) + 2 * (j & 3);
+  const int soff = int((32 * (j >> 2) + 2 * (j & 3)) * c.K * 2);
+  if (q < 8)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, AWQ_LDS(stage64_a<S>() + r0 * 32), 16,
+                                             c.vbA[j & 1], soff, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, AWQ_LDS(stage64_b<S>() + r0 * 32), 16,
+                                             c.vbB[j & 1], soff, 0, 0);
+}
+
+__device__ __forceinline__ u32x2 tr_read(const uint4* stage, int byte_off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(reinterpret_cast<const char*>(stage) + byte_off)));
+}
+// half-read r (0..31) of k-step ks: fragment r / 2 (B blocks 0..7, then A
+// blocks), token rows + 4·(r % 2)
+template <int S>
+__device__ __forceinline__ void xfrag(const XCtx& c, int ks, int r, u32x4 (&fa)[8], u32x4 (&fb)[8]) {
+  const int f = r >> 1, hh = r & 1;
+  const int row_off = (32 * ks + 4 * hh) * 512;
+  // tokens 0-3 of the lane's 8 go to words 0-1, tokens 4-7 to words 2-3
+  auto put = [hh](u32x4& dst, u32x2 v) {
+    const u32x4 w = __builtin_shufflevector(v, v, 0, 1, 0, 1);
+    dst = hh ? __builtin_shufflevector(dst, w, 0, 1, 6, 7) : __builtin_shufflevector(dst, w, 4, 5, 2, 3);
+  };
+  if (f < 8)
+    put(fb[f], tr_read(stage64_b<S>(), c.rdB[f] + row_off));
+  else
+    put(fa[f - 8], tr_read(stage64_a<S>(), c.rdA[f - 8] + row_off));
+}
+__device__ __forceinline__ bf16x8_t as_bf16(const u32x4& v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// One 64-token k-tile, the schedule of region16 with two half-reads where it
+// has one read: the previous k-step's 64 MFMAs carry k-step 0's 32
+// half-reads and the next k-tile's 16 copies; k-step 0's carry k-step 1's.
+template <int S, bool PREV>
+__device__ __forceinline__ void xregion(const XCtx& c, int kt, floatx4 (&acc)[8][8],
+                                        u32x4 (&f0a)[8], u32x4 (&f0b)[8], u32x4 (&f1a)[8],
+                                        u32x4 (&f1b)[8]) {
+  const bool more = kt + 1 < c.KT;
+  const __amdgpu_buffer_rsrc_t rsA = xtile_rsrc(c.a, c.K, more ? c.tokens : 0, c.ca, kt + 1);
+  const __amdgpu_buffer_rsrc_t rsB = xtile_rsrc(c.b, c.K, more ? c.tokens : 0, c.cb, kt + 1);
+  if (PREV) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int i = q >> 1, j0 = (q & 1) * 4;
+      mfma16(acc[i][j0], as_bf16(f1a[i]), as_bf16(f1b[j0]));
+      xfrag<S>(c, 0, 2 * q, f0a, f0b);
+      mfma16(acc[i][j0 + 1], as_bf16(f1a[i]), as_bf16(f1b[j0 + 1]));
+      xfrag<S>(c, 0, 2 * q + 1, f0a, f0b);
+      mfma16(acc[i][j0 + 2], as_bf16(f1a[i]), as_bf16(f1b[j0 + 2]));
+      xcopy<S ^ 1>(c, rsA, rsB, q);
+      mfma16(acc[i][j0 + 3], as_bf16(f1a[i]), as_bf16(f1b[j0 + 3]));
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) xcopy<S ^ 1>(c, rsA, rsB, q);
+#pragma unroll
+    for (int r = 0; r < 32; ++r) xfrag<S>(c, 0, r, f0a, f0b);
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int i = q >> 1, j0 = (q & 1) * 4;
+    mfma16_acc<!PREV>(acc[i][j0], as_bf16(f0a[i]), as_bf16(f0b[j0]));
+    xfrag<S>(c, 1, 2 * q, f1a, f1b);
+    mfma16_acc<!PREV>(acc[i][j0 + 1], as_bf16(f0a[i]), as_bf16(f0b[j0 + 1]));
+    xfrag<S>(c, 1, 2 * q + 1, f1a, f1b);
+    mfma16_acc<!PREV>(acc[i][j0 + 2], as_bf16(f0a[i]), as_bf16(f0b[j0 + 2]));
+    mfma16_acc<!PREV>(acc[i][j0 + 3], as_bf16(f0a[i]), as_bf16(f0b[j0 + 3]));
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  region_barrier();
+}
+
 // Units v = s·U + q (slice s, upper tile q). With compact (from 1024 units
 // on), runs of 32 consecutive units go to one XCD (consecutive block ids go
 // round-robin over the 8 XCDs: block b runs on XCD b % 8, the i-th there
@@ -122,9 +233,10 @@ __device__ __forceinline__ void pair_tile(int q, int nt, int& tm, int& tn) {
 // concurrent tiles draw on ~15 panels of one slice instead of 32 panel-slices
 // of two (at K = 4096); otherwise block v is unit v in row-major tile order.
 // P[(s·U + u)][256·256]: float32 partial tile of row-major upper tile u.
+// X [T, K] row-major; tokens past T read as zero.
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gram_partial_kernel(const uint16_t* __restrict__ Xt, int64_t K, int64_t ldx, int64_t KT,
-                         int S, int nt, int U, int compact, float* __restrict__ P) {
+void gram_partial_kernel(const uint16_t* __restrict__ X, int64_t T, int64_t K, int64_t KT,
+                           int S, int nt, int U, int compact, float* __restrict__ P) {
   int64_t v = blockIdx.x;
   if (compact) {
     const int b = int(blockIdx.x), x = b & 7, i = b >> 3;
@@ -135,19 +247,50 @@ void gram_partial_kernel(const uint16_t* __restrict__ Xt, int64_t K, int64_t ldx
   int tm, tn, u = q;
   if (compact) {
     pair_tile(q, nt, tm, tn);
-    u = tm * nt - tm * (tm - 1) / 2 + (tn - tm);   // its row-major index
+    u = tm * nt - tm * (tm - 1) / 2 + (tn - tm);
   } else {
     upper_tile(q, nt, tm, tn);
   }
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
-  const int64_t rows_a = K - m0 < BM ? K - m0 : BM;
-  const int64_t rows_b = K - n0 < BN ? K - n0 : BN;
   const int64_t k0 = int64_t(s) * KT / S, k1 = int64_t(s + 1) * KT / S;
-  const int64_t t0 = k0 * BK64, Ts = (k1 - k0) * BK64;
-  GemmCtx64 c;
-  gemm_setup64(c, Xt + m0 * ldx + t0, rows_a, ldx, Xt + n0 * ldx + t0, rows_b, ldx, Ts, false);
+  const int64_t t0 = k0 * BK64;
+  XCtx c;
+  c.K = K;
+  c.a = X + t0 * K + m0;
+  c.b = X + t0 * K + n0;
+  c.tokens = int(T - t0 < int64_t(1) << 30 ? T - t0 : int64_t(1) << 30);
+  c.ca = int(K - m0 < BM ? K - m0 : BM);
+  c.cb = int(K - n0 < BN ? K - n0 : BN);
+  c.KT = int(k1 - k0);
+  xctx_setup(c);
+
+  // k-tile 0 into stage 0
+  {
+    const __amdgpu_buffer_rsrc_t rsA = xtile_rsrc(c.a, K, c.tokens, c.ca, 0);
+    const __amdgpu_buffer_rsrc_t rsB = xtile_rsrc(c.b, K, c.tokens, c.cb, 0);
+#pragma unroll
+    for (int qq = 0; qq < 16; ++qq) xcopy<0>(c, rsA, rsB, qq);
+  }
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  region_barrier();
   floatx4 acc[8][8];
-  gemm_mainloop16<false>(c, acc);
+  u32x4 f0a[8], f0b[8], f1a[8], f1b[8];
+  xregion<0, false>(c, 0, acc, f0a, f0b, f1a, f1b);
+  int kt = 1;
+  for (; kt + 1 < c.KT; kt += 2) {
+    xregion<1, true>(c, kt, acc, f0a, f0b, f1a, f1b);
+    xregion<0, true>(c, kt + 1, acc, f0a, f0b, f1a, f1b);
+  }
+  if (kt < c.KT) xregion<1, true>(c, kt, acc, f0a, f0b, f1a, f1b);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mfma16(acc[i][j], as_bf16(f1a[i]), as_bf16(f1b[j]));
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
 
   // lane l of block (i, j) holds column l % 16 and rows 4·(l/16) + v
   const int lane = threadIdx.x & 63;
@@ -160,8 +303,8 @@ void gram_partial_kernel(const uint16_t* __restrict__ Xt, int64_t K, int64_t ldx
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        tile[(row0 + i * 16 + v) * BN + col0 + j * 16] = acc[i][j][v];
+      for (int vv = 0; vv < 4; ++vv)
+        tile[(row0 + i * 16 + vv) * BN + col0 + j * 16] = acc[i][j][vv];
 }
 
 // Block (u, sb): the 64x64 sub-block sb of upper tile u. Thread t takes row
@@ -320,24 +463,21 @@ void gram_search_kernel(const uint16_t* __restrict__ Gs, int64_t ldg, const uint
 
 }  // namespace
 
-// S token slices of whole 64-token k-tiles (at least one each); P holds
-// S x (upper tiles) float32 partial tiles of 256 x 256.
-hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, int64_t ldx, int S,
-                             uint16_t* Xt, float* P, int64_t ldg, uint16_t* Gs, hipStream_t st) {
-  if (K % 128 || Tp % 128 || Tp < T || S < 1 || int64_t(S) * 64 > Tp || ldx < Tp ||
-      ldx % 8 || ldg < 2 * K || ldg % 8)
+// S token slices of whole 64-token k-tiles (at least one each) of the Tp
+// tokens (T rounded up to 128; those past T read as zero); P holds S x
+// (upper tiles) float32 partial tiles of 256 x 256.
+hipError_t launch_gram_build(const void* X, int64_t T, int64_t K, int64_t Tp, int S, float* P,
+                             int64_t ldg, uint16_t* Gs, hipStream_t st) {
+  if (K % 128 || Tp % 128 || Tp < T || S < 1 || int64_t(S) * 64 > Tp || ldg < 2 * K || ldg % 8)
     return hipErrorInvalidValue;
-  dim3 tgrid(unsigned((Tp + 63) / 64), unsigned(K / 64));
-  transpose_pad_kernel<<<tgrid, 256, 0, st>>>(static_cast<const uint16_t*>(X), T, K, Tp, ldx, Xt);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int nt = int((K + BM - 1) / BM);
   const int U = nt * (nt + 1) / 2;
   const int64_t units = int64_t(U) * S;
   const int compact = units >= 1024;
   const int64_t pblocks = compact ? (units + 255) / 256 * 256 : units;
-  gram_partial_kernel<<<unsigned(pblocks), NT, 0, st>>>(Xt, K, ldx, Tp / BK64, S, nt, U, compact,
-                                                        P);
+  gram_partial_kernel<<<unsigned(pblocks), NT, 0, st>>>(static_cast<const uint16_t*>(X), T, K,
+                                                        Tp / BK64, S, nt, U, compact, P);
+  hipError_t e;
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   gram_reduce_kernel<<<dim3(unsigned(U), 16), 256, 0, st>>>(P, S, U, nt, K, ldg, Gs);

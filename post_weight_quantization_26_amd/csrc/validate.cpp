@@ -61,33 +61,27 @@ GramBuildLayout gram_build_layout(int64_t T, int64_t K) {
   GramBuildLayout B{};
   B.Tp = ceil_div(T, kTileK) * kTileK;
   B.S = gram_slices(T, K);
-  B.ldx = B.Tp + kXtPad;
   B.ldg = 2 * K + kGsPad;
   const size_t nt = size_t(ceil_div(K, kGemmBM_bf16));
-  B.xt = 0;
-  B.gp = align_up(size_t(K) * size_t(B.ldx) * 2);
-  B.total = B.gp + align_up(size_t(B.S) * (nt * (nt + 1) / 2) * 256 * 256 * 4);
+  B.gp = 0;
+  B.total = align_up(size_t(B.S) * (nt * (nt + 1) / 2) * 256 * 256 * 4);
   return B;
 }
 
 size_t gram_g_bytes(int64_t K) { return align_up(size_t(K) * size_t(2 * K + kGsPad) * 2); }
 
-// The Gram build reads 256-row tiles of Xᵀ (rows of Tp + 64 tokens) and the
-// search 256-row tiles of G's halves (rows of 2K + 256): both must fit the
-// main loop's 32-bit tile offsets; its launches must fit the 32-bit grid.
+// The Gram search reads 256-row tiles of G's halves (rows of 2K + 256): they
+// must fit the main loop's 32-bit tile offsets; the build's launch must fit
+// the 32-bit grid. (The build reads X one 64-token k-tile at a time, so T
+// needs no limit of its own.)
 static awq_status check_gram_limits(const char* nm, int64_t T, int64_t K, bool build) {
-  const int64_t Tp = ceil_div(T, kTileK) * kTileK;
-  if (!tile_rows_fit(Tp + kXtPad))
-    return set_error(AWQ_E_UNSUPPORTED,
-                     "%s: T=%lld tokens exceed the Gram build's 32-bit tile offsets "
-                     "(512 * (T rounded up to 128, + 64) must stay below 2^31)",
-                     nm, (long long)T);
   if (!tile_rows_fit(2 * K + kGsPad))
     return set_error(AWQ_E_UNSUPPORTED,
                      "%s: K=%lld exceeds the Gram search's 32-bit tile offsets "
                      "(512 * (2K + 256) must stay below 2^31)", nm, (long long)K);
   const int64_t nt = ceil_div(K, kGemmBM_bf16);
-  if (build && !grid_fits(nt * (nt + 1) / 2 * gram_slices(T, K), 256))
+  // (the build's grid is its units rounded up to a multiple of 256)
+  if (build && !grid_fits(ceil_div(nt * (nt + 1) / 2 * gram_slices(T, K), 256) * 256, 256))
     return set_error(AWQ_E_UNSUPPORTED, "%s: K=%lld exceeds the Gram build's grid", nm,
                      (long long)K);
   return AWQ_OK;
@@ -102,7 +96,6 @@ SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_gr
   L.MT = gram ? ceil_div(K, kGemmBM_bf16) : ceil_div(T, bm);
   L.Tp = B.Tp;
   L.S = B.S;
-  L.ldx = B.ldx;
   L.ldg = gram ? 2 * K + kGsPad : 0;
   const size_t n_tab = is_scale_op(op) ? size_t(n_grid) : 1;
   size_t off = 0;
@@ -126,8 +119,7 @@ SearchLayout search_layout(int op, int64_t T, int64_t N, int64_t K, int32_t n_gr
   off += align_up(size_t(N) * 8);
   L.scalar = off;
   off += align_up(64);
-  // a building Gram search also holds Xt, the partial tiles and G
-  L.xt = off + B.xt;
+  // a building Gram search also holds the partial tiles and G
   L.gp = off + B.gp;
   off += B.total;
   L.gs = off;
@@ -537,9 +529,7 @@ extern "C" size_t awq_workspace_bytes(int op, int64_t T, int64_t N, int64_t K, i
       if (dtype != AWQ_BF16 || K % kTileK) return 0;
       return search_layout(op, T, N, K, n_grid, n_grid, dtype).total;
     case AWQ_OP_GRAM_BUILD:
-      if (dtype != AWQ_BF16 || K % kTileK ||
-          !tile_rows_fit(ceil_div(T, kTileK) * kTileK + kXtPad))
-        return 0;
+      if (dtype != AWQ_BF16 || K % kTileK) return 0;
       return gram_build_layout(T, K).total;
     case AWQ_OP_PACK:
       return kAlign;

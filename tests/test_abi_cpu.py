@@ -428,13 +428,12 @@ def test_prepared_gram_sizes_and_rejects(L):
     assert gbytes == K * (2 * K + 256) * 2            # upper tiles' hi/lo rows, padded
     assert lib.awq_gram_bytes(200) == 0 and lib.awq_gram_bytes(0) == 0
     build = ws(L.AWQ_OP_GRAM_BUILD, T, 1, K, 1, L.AWQ_BF16)
-    xt = K * (T + 64) * 2
     gp = 15 * 136 * 256 * 256 * 4                     # 15 token slices x 136 upper tiles
-    assert build == xt + gp
+    assert build == gp                                # X is read in place: no X^T
     assert ws(L.AWQ_OP_GRAM_BUILD, T, 1, K, 1, L.AWQ_F32) == 0
     for with_g, op in ((L.AWQ_OP_SEARCH_SCALE_GRAM_G, L.AWQ_OP_SEARCH_SCALE_GRAM),
                        (L.AWQ_OP_SEARCH_CLIP_GRAM_G, L.AWQ_OP_SEARCH_CLIP_GRAM)):
-        # a prepared G: no X^T, partial tiles or G in the search's workspace
+        # a prepared G: no partial tiles or G in the search's workspace
         assert ws(with_g, T, 4096, K, 20, L.AWQ_BF16) == \
             ws(op, T, 4096, K, 20, L.AWQ_BF16) - build - gbytes
         assert lib.awq_workspace_bytes_batch(with_g, T, 4096, K, 20, 1, L.AWQ_BF16) > 0
@@ -443,7 +442,7 @@ def test_prepared_gram_sizes_and_rejects(L):
     assert f(FAKE, L.AWQ_BF16, T, K, None, big, FAKE, big, None) == -1
     assert f(FAKE, L.AWQ_F32, T, K, FAKE, big, FAKE, big, None) == -2
     assert f(FAKE, L.AWQ_BF16, T, 200, FAKE, big, FAKE, big, None) == -1
-    assert f(FAKE, L.AWQ_BF16, (1 << 22) + 1, K, FAKE, big, FAKE, big, None) == -2
+    assert f(FAKE, L.AWQ_BF16, 1 << 31, K, FAKE, big, FAKE, big, None) == -1   # past 2^31 - 1
     assert f(MIS, L.AWQ_BF16, T, K, FAKE, big, FAKE, big, None) == -1
     assert f(FAKE, L.AWQ_BF16, T, K, FAKE, gbytes - 1, FAKE, big, None) == -3
     assert f(FAKE, L.AWQ_BF16, T, K, FAKE, gbytes, FAKE, build - 1, None) == -3
@@ -477,15 +476,15 @@ def test_gram_workspace_and_rejects(L):
     ws = lib.awq_workspace_bytes
     direct = ws(L.AWQ_OP_SEARCH_SCALE, 65536, 4096, 4096, 20, L.AWQ_BF16)
     gram = ws(L.AWQ_OP_SEARCH_SCALE_GRAM, 65536, 4096, 4096, 20, L.AWQ_BF16)
-    xt, gs = 4096 * 65536 * 2, 4096 * 8192 * 2
+    gs = 4096 * 8192 * 2
     # the build's float32 partial tiles: 15 token slices (136 upper tiles x 15
     # slices = 2040 units, 8 rounds of 256 CUs: the fewest rounds per slice
     # length for S <= 16) of 136 tiles of 256x256
     gp = 15 * 136 * 256 * 256 * 4
-    # partials shrink to K/256 row tiles; X^T, the G build's partial tiles and
-    # the G halves are added
-    assert gram > direct - 256 * 20 * 4096 * 4 + xt + gp + gs - (1 << 20)
-    assert gram < direct + xt + gp + gs
+    # partials shrink to K/256 row tiles; the G build's partial tiles and the
+    # G halves are added (X is read in place)
+    assert gram > direct - 256 * 20 * 4096 * 4 + gp + gs - (1 << 20)
+    assert gram < direct + gp + gs
     assert ws(L.AWQ_OP_SEARCH_SCALE_GRAM, 65536, 4096, 4096, 20, L.AWQ_F32) == 0
     assert ws(L.AWQ_OP_SEARCH_CLIP_GRAM, 700, 300, 384, 5, L.AWQ_BF16) > 384 * 768 * 2 + 384 * 768 * 2
     assert lib.awq_workspace_bytes_batch(L.AWQ_OP_SEARCH_CLIP_GRAM, 700, 300, 384, 5, 1,
@@ -500,8 +499,8 @@ def test_gram_workspace_and_rejects(L):
     # fp16 layers go through the direct searches; the Gram path is bf16 only
     assert f(FAKE, FAKE, L.AWQ_F16, 256, 256, 256, FAKE, g, 3, qc, FAKE, ctypes.byref(a_best), mse,
              None, FAKE, 1 << 40, None) == -2
-    assert f(FAKE, FAKE, L.AWQ_BF16, (1 << 22) + 1, 256, 256, FAKE, g, 3, qc, FAKE,
-             ctypes.byref(a_best), mse, None, FAKE, 1 << 40, None) == -2
+    assert f(FAKE, FAKE, L.AWQ_BF16, 1 << 31, 256, 256, FAKE, g, 3, qc, FAKE,
+             ctypes.byref(a_best), mse, None, FAKE, 1 << 40, None) == -1
     assert f(FAKE, FAKE, L.AWQ_BF16, 256, 256, 200, FAKE, g, 3, qc, FAKE, ctypes.byref(a_best),
              mse, None, FAKE, 1 << 40, None) == -1
     need1 = lib.awq_workspace_bytes_batch(L.AWQ_OP_SEARCH_SCALE_GRAM, 256, 256, 256, 3, 1,
@@ -543,8 +542,9 @@ def test_32bit_offset_edges(L):
     largest accepted size gets past the shape checks (it then fails only on
     the deliberately small workspace, AWQ_E_WORKSPACE), the next one is
     refused (AWQ_E_UNSUPPORTED). The search GEMM's 256-row tiles need
-    512·K < 2^31 (split: 512·2K); the Gram build's 512·(T rounded to 128,
-    + 64) and the Gram search's 512·(2K + 256); the consumer GEMM's 512·K;
+    512·K < 2^31 (split: 512·2K); the Gram search's 512·(2K + 256) (the
+    Gram build reads X one 64-token k-tile at a time and takes any token
+    count); the consumer GEMM's 512·K;
     element-wise launches N·K <= 2^34; the candidate GEMM's grid < 2^32
     work-items."""
     lib = L.lib()
@@ -569,17 +569,16 @@ def test_32bit_offset_edges(L):
                                          L.QConfig(4, 128, 1), FAKE, ctypes.byref(mc), None, FAKE,
                                          1000, None)
     assert clip(k22 - 128) == WS and clip(k22) == UN
-    # Gram: tokens padded to 128 plus 64 per X^T row; 2K + 256 per G row
-    assert scale(lib.awq_search_scale_gram, k22 - 128, 256, 256) == WS
-    assert scale(lib.awq_search_scale_gram, k22 - 127, 256, 256) == UN
+    # Gram: 2K + 256 per G row; any token count up to the shape limit 2^31 - 1
+    t_max = (1 << 31) - 1
+    assert scale(lib.awq_search_scale_gram, t_max, 256, 256) == WS
     assert scale(lib.awq_search_scale_gram_g, 256, 256, k22 // 2 - 256) == WS
     assert scale(lib.awq_search_scale_gram_g, 256, 256, k22 // 2 - 128) == UN
     big = 1 << 40
     gb = lib.awq_gram_build
-    assert gb(FAKE, L.AWQ_BF16, k22 - 128, 256, FAKE, 0, FAKE, big, None) == WS
-    assert gb(FAKE, L.AWQ_BF16, k22 - 127, 256, FAKE, 0, FAKE, big, None) == UN
-    assert lib.awq_workspace_bytes(L.AWQ_OP_GRAM_BUILD, k22 - 128, 1, 256, 1, L.AWQ_BF16) > 0
-    assert lib.awq_workspace_bytes(L.AWQ_OP_GRAM_BUILD, k22 - 127, 1, 256, 1, L.AWQ_BF16) == 0
+    assert gb(FAKE, L.AWQ_BF16, t_max, 256, FAKE, 0, FAKE, big, None) == WS
+    assert gb(FAKE, L.AWQ_BF16, 256, k22 // 2 - 128, FAKE, 0, FAKE, big, None) == UN
+    assert lib.awq_workspace_bytes(L.AWQ_OP_GRAM_BUILD, t_max, 1, 256, 1, L.AWQ_BF16) > 0
     # the candidate GEMM's grid: 2^31 - 1 tokens x 2^20 rows is past 2^32 work-items
     assert scale(lib.awq_search_scale, (1 << 31) - 1, 1 << 20, 128) == UN
     assert "grid" in L.last_error()

@@ -65,7 +65,9 @@ def assembly(tmp_path_factory):
 def _kernel_body(asm, name):
     m = re.search(r"^(_Z\S*" + name + r"\S*):[ \t]*(;.*)?$", asm, re.M)
     assert m, f"kernel {name} not found in the assembly"
-    end = asm.index("s_endpgm", m.end())
+    # the whole function: a kernel may end early on some paths (padding blocks)
+    fe = asm.find(".Lfunc_end", m.end())
+    end = fe if fe >= 0 else asm.index("s_endpgm", m.end())
     lines = asm[m.end():end].split("\n")
     return [ln.strip() for ln in lines
             if ln.strip() and not ln.strip().startswith((";", ".", "#"))]
