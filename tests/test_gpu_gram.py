@@ -88,6 +88,48 @@ def check_gram_scale(api, X, W, alphas, bits, zp, rows=None, group=128, curve_ru
     return res, dref, Xd, Wd
 
 
+def g_prime_from_gs(Gs_bytes, K):
+    """G' (G on diagonal 256-tiles, 2G above them; NaN below) decoded from
+    the hi/lo layout: row j, column c of its row tile's part holds hi at
+    256·(c // 128) + c % 128 and lo 128 further on."""
+    gs = Gs_bytes.view(np.uint16).reshape(K, 2 * K + 256)
+    f = lambda h: (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    c = np.arange(K)
+    hi = f(gs[:, 256 * (c // 128) + c % 128])
+    lo = f(gs[:, 256 * (c // 128) + 128 + c % 128])
+    G = hi + lo
+    tile = np.arange(K) // 256
+    G[tile[:, None] > tile[None, :]] = np.nan
+    return G
+
+
+@pytest.mark.parametrize("T,K", [(700, 384), (1000, 640), (65, 128), (4160, 1152), (1100, 4096)])
+def test_gram_matrix_elementwise(api, T, K):
+    """G from X in place (transposing LDS reads, token slices, the XCD order
+    from 1024 units on: 1100 tokens at K = 4096 make 9 slices x 136 tiles)
+    against the float64 G of the oracle, every stored entry: within
+    γ_T·(|X|ᵀ|X|) for the float32 sums plus 2^-16 for the hi/lo split,
+    doubled above the diagonal tiles. Ragged T and a 128-channel last tile
+    included."""
+    X, _ = synth.make_custom(T, 8, K, "bf16", seed=300 + T + K)
+    G = api.gram_build(to_dev(X, "bf16"))
+    torch.cuda.synchronize()
+    Gd = g_prime_from_gs(G.cpu().numpy(), K)
+    G64 = O.gram_matrix(X, "bf16")
+    xa = np.abs(O.decode(X, "bf16").astype(np.float64))
+    A = xa.T @ xa
+    tile = np.arange(K) // 256
+    w = np.where(tile[:, None] < tile[None, :], 2.0, 1.0)
+    upper = tile[:, None] <= tile[None, :]
+    ref = w * G64
+    bound = w * (gamma(T) * A + 2.0 ** -16 * np.abs(G64)) * 1.01
+    err = np.abs(Gd - ref)
+    worst = (err[upper] / np.maximum(bound[upper], 1e-300)).max()
+    print(f"G {T}x{K}: max |err|/bound {worst:.2e}")
+    assert np.all(np.isfinite(Gd[upper]))
+    assert worst <= 1.0
+
+
 @pytest.mark.parametrize("bits,zp", [(4, True), (3, True), (4, False)])
 def test_gram_scale_small_ragged(api, bits, zp):
     # 700 tokens (padded to 768), 384 channels (two 256-row tiles of G, one
