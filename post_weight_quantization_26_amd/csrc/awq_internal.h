@@ -45,6 +45,7 @@ inline int64_t search_gemm_blocks(int64_t T, int64_t Nc, awq_dtype d) {
   if (d == AWQ_F32) return ceil_div(T, 64) * ceil_div(Nc, 64);
   const int64_t tm = ceil_div(T, 256), tn = ceil_div(Nc, 256);
   if (tm >= 32) return ceil_div(tm, 32) * 32 * (ceil_div(tn, 8) * 8);
+  if (tm == 16 || tm == 8 || tm == 4) return ceil_div(tn, 64 / (tm / 4)) * 256;
   return tm * tn;
 }
 inline int64_t gram_search_blocks(int64_t K, int64_t Nc) {

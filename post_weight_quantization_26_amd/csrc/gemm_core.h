@@ -66,15 +66,27 @@ __device__ __forceinline__ void region_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Block id -> (token tile, candidate-column tile). Returns false for padding blocks.
+// Block id -> (token tile, candidate-column tile). Returns false for padding
+// blocks. Every 256 consecutive ids give each XCD 4 token tiles x 8 column
+// tiles (consecutive ids go round-robin over the 8 XCDs). From 32 token tiles
+// on, all XCDs take the same 8 column tiles and 32 token tiles between them;
+// with 16, 8 or 4 token tiles (4096, 2048, 1024 tokens) the 8 XCDs split
+// into 4, 2 or 1 token groups x 2, 4 or 8 column groups.
 __device__ __forceinline__ bool tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
   if (tiles_m >= 32) {
     const int w = bid >> 8, j = bid & 255;
-    const int xcd = j & 7, i = j >> 3;  // consecutive ids go round-robin over the 8 XCDs
+    const int xcd = j & 7, i = j >> 3;
     const int nwn = (tiles_n + 7) >> 3;
     const int g = w / nwn, wn = w - g * nwn;
     tm = 32 * g + 4 * xcd + (i & 3);
     tn = 8 * wn + (i >> 2);
+  } else if (tiles_m == 16 || tiles_m == 8 || tiles_m == 4) {
+    const int w = bid >> 8, j = bid & 255;
+    const int xcd = j & 7, i = j >> 3;
+    const int nag = tiles_m >> 2;                 // token groups of 4 tiles
+    const int ag = xcd & (nag - 1), bg = (8 / nag) * w + xcd / nag;
+    tm = 4 * ag + (i & 3);
+    tn = 8 * bg + (i >> 2);
   } else {
     tm = bid % tiles_m;
     tn = bid / tiles_m;
@@ -375,6 +387,10 @@ __device__ __forceinline__ void column_square_sums(const floatx4 (&acc)[8][8], f
 // Number of workgroups the tile_of mapping needs for a tiles_m x tiles_n grid.
 __host__ __device__ inline int64_t gemm_blocks(int tiles_m, int tiles_n) {
   if (tiles_m >= 32) return int64_t((tiles_m + 31) / 32) * 32 * (int64_t((tiles_n + 7) / 8) * 8);
+  if (tiles_m == 16 || tiles_m == 8 || tiles_m == 4) {
+    const int per = 64 / (tiles_m >> 2);           // column tiles per 256 ids
+    return int64_t((tiles_n + per - 1) / per) * 256;
+  }
   return int64_t(tiles_m) * tiles_n;
 }
 

@@ -482,6 +482,14 @@ def test_search_scale_many_token_tiles(api):
     check_scale_search(api, X, W, "bf16", synth.alpha_grid(3), 4, True)
 
 
+@pytest.mark.parametrize("T", [4000, 2000, 1000])
+def test_search_scale_4_8_16_token_tiles(api, T):
+    # 16, 8 and 4 token tiles: the XCD-grouped order for few token tiles
+    # (token groups x column groups), 7 column tiles with padding blocks
+    X, W = synth.make_custom(T, 520, 256, "bf16", seed=T)
+    check_scale_search(api, X, W, "bf16", synth.alpha_grid(3), 4, True)
+
+
 def test_search_is_deterministic_and_batch_invariant(api):
     X, W = synth.make_custom(600, 264, 256, "bf16", seed=25)
     Xd, Wd = to_dev(X, "bf16"), to_dev(W, "bf16")
