@@ -273,6 +273,24 @@ void w4a16_gemm_kernel(const uint16_t* __restrict__ X, const uint16_t* __restric
 // most 22 significant bits, so the fused result is (q − z)·scale rounded once
 // to float32, the value the dequantisation pass forms, and the operand equals
 // that pass's bit for bit.
+
+// Tile order of this kernel: from 32 token tiles on the shared XCD-grouped
+// order; below that, column tile by column tile with the token tile fastest,
+// so consecutive ids (one per XCD in turn) spread each column tile's packed
+// words over the XCDs. The grouped order for 4-16 token tiles suits the
+// two-pass GEMM, whose B tiles are as large as its A tiles; here B is a
+// quarter of the bytes and the grouped order measured slower.
+__device__ __forceinline__ bool q_tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  if (tiles_m >= 32) return tile_of(bid, tiles_m, tiles_n, tm, tn);
+  tm = bid % tiles_m;
+  tn = bid / tiles_m;
+  return tn < tiles_n;
+}
+
+inline int64_t q_gemm_blocks(int tiles_m, int tiles_n) {
+  return tiles_m >= 32 ? gemm_blocks(tiles_m, tiles_n) : int64_t(tiles_m) * tiles_n;
+}
+
 struct Q16Slot {
   uint32_t w[8];   // qweight words of k rows 8kc .. 8kc + 7
   uint32_t z;      // zero-point word
@@ -594,7 +612,7 @@ void w4a16_gemm_q_kernel(const uint16_t* __restrict__ X, const int32_t* __restri
                          uint16_t* __restrict__ Y) {
   typedef typename Operand<F16>::type V;
   int tm, tn;
-  if (!tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
+  if (!q_tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn)) return;
   const int64_t m0 = int64_t(tm) * BM, n0 = int64_t(tn) * BN;
   const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
   const int tid = threadIdx.x;
@@ -1217,7 +1235,7 @@ hipError_t launch_w4a16_gemm_q(const uint16_t* X, const int32_t* qweight, const 
     return hipErrorInvalidValue;
   const int gshift = group == 32 ? 5 : group == 64 ? 6 : 7;   // log2 of the group size
   const int tiles_m = int((M + BM - 1) / BM), tiles_n = int((N + BN - 1) / BN);
-  const unsigned blocks = unsigned(gemm_blocks(tiles_m, tiles_n));
+  const unsigned blocks = unsigned(q_gemm_blocks(tiles_m, tiles_n));
   if (f16)
     w4a16_gemm_q_kernel<true><<<blocks, NT, 0, st>>>(X, qweight, qzeros, scales, M, N, K, gshift,
                                                      tiles_m, tiles_n, Y);
