@@ -333,7 +333,10 @@ def main():
                           else round(100 * roofline["mfma_util_counters"]["frac"], 1)),
         "hbm": {"stats_GBps": None if stats_gbs is None else round(stats_gbs, 1),
                 "pack_GBps": None if pack_gbs is None else round(pack_gbs, 1),
-                "peak_GBps": HBM_PEAK_GBS},
+                "peak_GBps": HBM_PEAK_GBS,
+                "timing": "HIP events around each launch; they include the launch's own "
+                          "few microseconds, a large part of a 4096x4096 pack (about 11 us "
+                          "of kernel time in a kernel trace)"},
         "kernels": kernels,
         "alpha_best": float(res["alpha_best"]),
         "mse_alpha0": float(res["mse"][0]),
