@@ -292,19 +292,41 @@ void gram_partial_kernel(const uint16_t* __restrict__ X, int64_t T, int64_t K, i
 #pragma unroll
     for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
 
-  // lane l of block (i, j) holds column l % 16 and rows 4·(l/16) + v
+  // Store through LDS: lane l of block (i, j) holds column 16·j + l % 16
+  // and rows 16·i + 4·(l/16) + v of the wave's 128 x 128, scattered over
+  // half-lines if stored as they lie. The k-loop left the ring idle (its
+  // last region ended on a barrier after its reads and copies), so each
+  // wave takes one of its four 32 KiB arrays, writes 64 of its columns
+  // there as 128 rows of 64 floats, reads them back 4 consecutive floats
+  // per lane and stores whole 256-byte row runs; twice. Column c of row r
+  // sits at c ^ (16·((r / 4) % 4)): the 64 lanes of a 4-byte write (4 rows
+  // 4 apart, 16 columns) land on 64 distinct banks, and the 4 floats a
+  // 16-byte read takes stay consecutive. Only the wave itself touches its
+  // array, and a wave's LDS operations take effect in order.
   const int lane = threadIdx.x & 63;
   const int wm = c.wave >> 1, wn = c.wave & 1;
-  float* tile = P + (int64_t(s) * U + u) * (BM * BN);
-  const int row0 = wm * 128 + 4 * (lane >> 4);
-  const int col0 = wn * 128 + (lane & 15);
+  float* stg = reinterpret_cast<float*>(c.wave == 0 ? s64A0 : c.wave == 1 ? s64A1
+                                        : c.wave == 2 ? s64B0 : s64B1);
+  float* tile = P + (int64_t(s) * U + u) * (BM * BN) + int64_t(wm) * 128 * BN + wn * 128;
+  const int rq = lane >> 4, cl = lane & 15;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int p = 0; p < 2; ++p) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int vv = 0; vv < 4; ++vv)
-        tile[(row0 + i * 16 + vv) * BN + col0 + j * 16] = acc[i][j][vv];
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) {
+          const int r = 16 * i + 4 * rq + vv;
+          stg[r * 64 + ((16 * j + cl) ^ (16 * rq))] = acc[i][4 * p + j][vv];
+        }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int r = 4 * k + rq;
+      const float4 v4 = *reinterpret_cast<const float4*>(stg + r * 64 + ((4 * cl) ^ (16 * (k & 3))));
+      *reinterpret_cast<float4*>(tile + int64_t(r) * BN + 64 * p + 4 * cl) = v4;
+    }
+  }
 }
 
 // Block (u, sb): the 64x64 sub-block sb of upper tile u. Thread t takes row
