@@ -95,8 +95,11 @@ def g_prime_from_gs(Gs_bytes, K):
     gs = Gs_bytes.view(np.uint16).reshape(K, 2 * K + 256)
     f = lambda h: (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     c = np.arange(K)
-    hi = f(gs[:, 256 * (c // 128) + c % 128])
-    lo = f(gs[:, 256 * (c // 128) + 128 + c % 128])
+    # tiles below the diagonal are never written and may hold signalling NaN
+    # bit patterns, whose widening raises numpy's invalid-value warning
+    with np.errstate(invalid="ignore"):
+        hi = f(gs[:, 256 * (c // 128) + c % 128])
+        lo = f(gs[:, 256 * (c // 128) + 128 + c % 128])
     G = hi + lo
     tile = np.arange(K) // 256
     G[tile[:, None] > tile[None, :]] = np.nan
