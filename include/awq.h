@@ -228,6 +228,7 @@ awq_status awq_search_clip(const void* X, const void* W, awq_dtype dtype, int64_
  * bits (RNE of the f32 step).
  * The codes represent W·diag(s); the caller folds diag(s)^-1 into the
  * operation that produces X. ws: at least awq_workspace_bytes(AWQ_OP_PACK,...).
+ * N must keep 64·N below 2^31 (AWQ_E_UNSUPPORTED otherwise).
  * Synchronises `stream`; returns AWQ_E_RANGE if a scale overflowed fp16. */
 awq_status awq_quantize_pack(const void* W, awq_dtype w_dtype, int64_t N, int64_t K,
                              const float* s, const float* ratio, awq_qconfig qc, int32_t* qweight,

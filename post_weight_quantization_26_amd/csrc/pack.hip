@@ -39,12 +39,14 @@
 //      rint can differ from the oracle's only when that quotient is within
 //      one ulp (< 1e-6 for codes below 16) of a .5 boundary. rint, clamp to
 //      [-zero, qmax - zero], packed in exact float arithmetic (small
-//      integers times powers of two, sums below 2^24): acc = fma(code - zero,
-//      base^row, acc), the zero points added once per word; 4-bit words use
-//      two 16-bit halves.
+//      integers times powers of two, sums below 2^24): each word starts from
+//      its rows' zero points Σ zero·base^row (read from LDS before the codes)
+//      and takes acc = fma(code - zero, base^row, acc) row by row; 4-bit
+//      words use two 16-bit halves.
 // The partial words are transposed through LDS: for 4 bits each is one
 // qweight word; for 3 bits four of them (32 rows) make three words. qweight
-// rows are written with consecutive stores.
+// rows are written with consecutive stores (4 bits: buffer stores from the
+// tile's first row, the row step in the scalar offset).
 #include "device_common.h"
 
 namespace awq {
@@ -128,6 +130,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(
   __shared__ uint8_t z_lds[kGroups][kRows];
   __shared__ __attribute__((aligned(16))) float red[16 * kRedStride];
   __shared__ RowPrm prm[16][kGroups][8];
+  __shared__ __attribute__((aligned(16))) float zlo[16][kGroups][8];   // -zero per row
 
   const int tid = threadIdx.x;
   const int c = tid & 15, jb = tid >> 4;
@@ -228,6 +231,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(
       const float rl = __builtin_fmaf(-rh, p.step, 1.0f) * rh;
       if (kGroups >= 2 || c < 8) {
         prm[jb][g][r8] = RowPrm{rh, rl, -p.zero, qmax - p.zero};
+        zlo[jb][g][r8] = -p.zero;
         const uint16_t hb = __builtin_bit_cast(uint16_t, _Float16(p.step));
         sc_lds[g][8 * j + r8] = hb;
         z_lds[g][8 * j + r8] = uint8_t(p.zero);
@@ -235,31 +239,43 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(
       }
     }
     wave_lds_sync();
-    // 4. codes of the 8 rows, packed exactly in float
-    float acc[kHalves][8], zacc[kHalves];
+    // 4. codes of the 8 rows, packed exactly in float. Each word (half
+    //    word for 4 bits) starts from its rows' zero points, zacc =
+    //    Σ_r zero_r·base^r, and adds (code_r - zero_r)·base^r row by row:
+    //    every partial sum is an integer in [0, 2^24), so the order of the
+    //    additions does not change the result.
+    float zacc[kHalves];
+    {
+      const float4* zl = reinterpret_cast<const float4*>(&zlo[jb][gi][0]);
+      const float4 za = zl[0], zb = zl[1];
+      const float nz[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
 #pragma unroll
-    for (int h = 0; h < kHalves; ++h) {
-      zacc[h] = 0.f;
+      for (int h = 0; h < kHalves; ++h) zacc[h] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
+      for (int q8 = 0; q8 < 8; ++q8) {
+        const int h = kHalves == 2 ? (q8 >> 2) : 0;
+        const float pw = float(1 << (BITS * (kHalves == 2 ? (q8 & 3) : q8)));
+        zacc[h] = __builtin_fmaf(-nz[q8], pw, zacc[h]);
+      }
     }
+    float acc[kHalves][8];
 #pragma unroll
     for (int q8 = 0; q8 < 8; ++q8) {
       const RowPrm pr = prm[jb][gi][q8];
       const int h = kHalves == 2 ? (q8 >> 2) : 0;
-      const float pw = float(1 << (BITS * (kHalves == 2 ? (q8 & 3) : q8)));
+      const int r = kHalves == 2 ? (q8 & 3) : q8;
+      const float pw = float(1 << (BITS * r));
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float quo = __builtin_fmaf(wp[q8][i], pr.rh, wp[q8][i] * pr.rl);
         const float cd = __builtin_amdgcn_fmed3f(__builtin_rintf(quo), pr.lo, pr.hi);
-        acc[h][i] = __builtin_fmaf(cd, pw, acc[h][i]);
+        acc[h][i] = r == 0 ? cd + zacc[h] : __builtin_fmaf(cd, pw, acc[h][i]);
       }
-      zacc[h] = __builtin_fmaf(-pr.lo, pw, zacc[h]);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      uint32_t wd = uint32_t(acc[0][i] + zacc[0]);
-      if constexpr (kHalves == 2) wd |= uint32_t(acc[1][i] + zacc[1]) << 16;
+      uint32_t wd = uint32_t(acc[0][i]);
+      if constexpr (kHalves == 2) wd |= uint32_t(acc[1][i]) << 16;
       words[c * 8 + i][j] = wd;
     }
   }
@@ -271,10 +287,17 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(
     const int jj = tid % kChunks;
     const int64_t jcol = n0 / 8 + jj;
     if (jcol < N8) {
-#pragma unroll 4
+      // from this tile's first qweight row; row steps go in the scalar
+      // offset (the host checks that 4·K·N/8 stays below 2^31 bytes)
+      const __amdgpu_buffer_rsrc_t qs = __builtin_amdgcn_make_buffer_rsrc(
+          qweight + tile * kTile * N8, 0, int(kTile * N8 * 4), 0x00020000);
+      const int kk0 = tid / kChunks;
+      const int qoff = int((kk0 * N8 + jcol) * 4);
+#pragma unroll
       for (int v = 0; v < kChunks / 2; ++v) {
-        const int kk = tid / kChunks + (kThreads / kChunks) * v;
-        qweight[(tile * kTile + kk) * N8 + jcol] = int32_t(words[kk][jj]);
+        const int kk = kk0 + (kThreads / kChunks) * v;
+        __builtin_amdgcn_raw_buffer_store_b32(words[kk][jj], qs, qoff,
+                                              int((kThreads / kChunks) * v * N8 * 4), 0);
       }
     }
     const int zg = tid / kChunks;

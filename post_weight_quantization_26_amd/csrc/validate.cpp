@@ -377,6 +377,10 @@ awq_status check_pack(const void* W, awq_dtype d, int64_t N, int64_t K, const fl
     return set_error(AWQ_E_UNSUPPORTED,
                      "quantize_pack: N*K=%lld weights exceed 2^34, or K=%lld its 32-bit tile "
                      "offsets (512 * K must stay below 2^31)", (long long)(N * K), (long long)K);
+  if (N * 64 >= (int64_t(1) << 31))   // 128 qweight rows of N/8 words per workgroup
+    return set_error(AWQ_E_UNSUPPORTED,
+                     "quantize_pack: N=%lld exceeds the 32-bit offsets of a workgroup's qweight "
+                     "rows (64 * N must stay below 2^31)", (long long)N);
   if (!aligned16(W) || !aligned4(qweight) || !aligned4(qzeros) || !aligned4(scales) ||
       !aligned4(s))
     return set_error(AWQ_E_INVALID, "quantize_pack: W must be 16-byte aligned, outputs 4-byte");

@@ -589,6 +589,8 @@ def test_32bit_offset_edges(L):
                                             L.QConfig(4, 128, 1), FAKE, FAKE, FAKE, FAKE, 0, None)
     assert pk(1 << 20, 1 << 14) == WS and pk((1 << 20) + 8, 1 << 14) == UN
     assert pk(8, k22 - 128) == WS and pk(8, k22) == UN
+    # a workgroup's 128 qweight rows of N/8 words: 64·N < 2^31
+    assert pk((1 << 25) - 8, 128) == WS and pk(1 << 25, 128) == UN
     # the consumer: 512·K < 2^31 on every path (T = 1 needs its workspace)
     wm = lambda K, fn=lib.awq_w4a16_matmul: fn(FAKE, L.AWQ_BF16, 1, 32, K, FAKE, FAKE, FAKE, 128,
                                                FAKE, FAKE, 0, None)
