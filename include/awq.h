@@ -159,7 +159,7 @@ awq_status awq_act_stats(const void* X, awq_dtype x_dtype, int64_t T, int64_t K,
  * array, so calls that overlap on one GPU (other streams, other threads) race
  * and must be serialised by the caller. Sizes whose partials need more than
  * 2^20 doubles (awq_workspace_bytes(AWQ_OP_STATS, ...) > 8 MiB, i.e. K above
- * about 2^19 for bf16) return AWQ_E_UNSUPPORTED; other argument errors as
+ * 2^20) return AWQ_E_UNSUPPORTED; other argument errors as
  * for awq_act_stats. Does not synchronise. */
 awq_status awq_act_stats_noalloc(const void* X, awq_dtype x_dtype, int64_t T, int64_t K,
                                  float* abar, void* stream);

@@ -53,7 +53,7 @@ inline int64_t gram_search_blocks(int64_t K, int64_t Nc) {
 }
 
 // Number of token chunks the stats kernel splits T into (one float64 partial
-// row per chunk); chosen so the launch has ~1024 workgroups.
+// row per chunk); chosen so the launch has at most 512 workgroups, 2 per CU.
 int64_t stats_chunks(int64_t T, int64_t K, awq_dtype d);
 
 // Byte offsets of the regions of a search workspace for a batch of `nb`

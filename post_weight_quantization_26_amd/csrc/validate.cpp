@@ -33,7 +33,10 @@ static constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 int64_t stats_chunks(int64_t T, int64_t K, awq_dtype d) {
   const int64_t vec = 16 / int64_t(dtype_bytes(d));
   const int64_t col_blocks = ceil_div(K, 64 * vec);
-  int64_t chunks = ceil_div(1024, col_blocks);
+  // at most 512 workgroups, 2 per CU (a third on some CUs left others idle
+  // at the end: 11008 channels in 22 strips x 24 chunks ran 14% slower than
+  // x 23), each with 4 loads in flight per lane: 32 KiB per CU in flight
+  int64_t chunks = 512 / col_blocks;
   const int64_t max_chunks = ceil_div(T, 64);  // at least 64 rows (16 per row lane) per chunk
   if (chunks > max_chunks) chunks = max_chunks;
   if (chunks < 1) chunks = 1;
