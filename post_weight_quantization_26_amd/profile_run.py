@@ -28,6 +28,13 @@
       70B-class MLP layer) and 4096 x 4096, ``reps`` timed launches each;
       prints the library's HIP-event time and the bandwidth it implies.
 
+  python -m post_weight_quantization_26_amd.profile_run stats [--reps 20]
+      The activation statistics (column sums of |x|, then the mean) of a bf16
+      X at 65,536 x 4096 (the Llama-7B attention input) and 65,536 x 11,008
+      (the MLP down-projection input), ``reps`` timed calls each; prints the
+      library's HIP-event time per call and the bandwidth it implies (X read
+      once).
+
   python -m post_weight_quantization_26_amd.profile_run traffic --record R \
           --fetch FETCH.csv --write WRITE.csv
       Updates the traffic record R (profiles/search_gemm_traffic.json or
@@ -250,6 +257,38 @@ def pack(reps: int) -> None:
         torch.cuda.empty_cache()
 
 
+def stats(reps: int) -> None:
+    import json
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    if root not in sys.path:
+        sys.path.insert(0, root)
+    import torch
+    from post_weight_quantization_26_amd import _lib, api
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    for T, K in ((65536, 4096), (65536, 11008)):
+        X = torch.randn((T, K), generator=g, device=dev).to(torch.bfloat16)
+        ws = torch.empty(api.workspace_bytes(_lib.AWQ_OP_STATS, T, 1, K, 1, X.dtype),
+                         dtype=torch.uint8, device=dev)
+        out = api.act_stats(X, ws=ws)
+        torch.cuda.synchronize()
+        api.profile_enable(True)
+        api.profile_reset()
+        for _ in range(reps):
+            api.act_stats(X, ws=ws, out=out)
+        torch.cuda.synchronize()
+        ms, n = api.profile_read("stats")
+        api.profile_enable(False)
+        us = ms / n * 1e3
+        moved = T * K * 2
+        print(json.dumps({"T": T, "K": K, "stats_us": round(us, 2), "algorithmic_bytes": moved,
+                          "GBps": round(moved / (us * 1e-6) / 1e9, 1)}), flush=True)
+        del X, ws, out
+        torch.cuda.empty_cache()
+
+
 def traffic(record: str, fetch_csv: str, write_csv: str) -> None:
     import csv
     import hashlib
@@ -403,7 +442,7 @@ def fused(reps: int) -> None:
 
 def main(argv=None) -> int:
     p = argparse.ArgumentParser()
-    p.add_argument("what", choices=["copy", "fill", "fold", "w4a16", "pack", "traffic",
+    p.add_argument("what", choices=["copy", "fill", "fold", "w4a16", "pack", "stats", "traffic",
                                     "counters", "library_gemm", "fused"])
     p.add_argument("--pmc")
     p.add_argument("--mib", type=int, default=1024)
@@ -428,6 +467,8 @@ def main(argv=None) -> int:
         fold(a.reps)
     elif a.what == "pack":
         pack(a.reps)
+    elif a.what == "stats":
+        stats(a.reps)
     else:
         w4a16(a.reps)
     return 0
